@@ -1,0 +1,288 @@
+"""ctypes declarations of include/vc.h and thin wrappers taking torch tensors."""
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvc.so")
+
+VC_OK, VC_ERR_INVALID_ARG, VC_ERR_UNSUPPORTED, VC_ERR_WORKSPACE, VC_ERR_HIP = range(5)
+VC_F32, VC_BF16 = 0, 1
+VC_QUANT_KIVI, VC_DROP_TOPK = 1, 2
+
+_STATUS = {1: "VC_ERR_INVALID_ARG", 2: "VC_ERR_UNSUPPORTED", 3: "VC_ERR_WORKSPACE", 4: "VC_ERR_HIP"}
+
+
+class VcError(RuntimeError):
+    def __init__(self, status, fn, msg):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first (python -m lossy_kv_draft_amd.build)")
+lib = ctypes.CDLL(LIB_PATH)
+
+c_i32, c_i64, c_f32, c_sz, c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+
+class vc_ckv(ctypes.Structure):
+    _fields_ = [("method", c_i32), ("k_bits", c_i32), ("v_bits", c_i32), ("group", c_i32),
+                ("param_dtype", c_i32), ("kv_dtype", c_i32), ("keep_ratio", c_f32),
+                ("B", c_i32), ("Hkv", c_i32), ("d", c_i32), ("capacity", c_i64), ("n_main", c_i64),
+                ("k_codes", c_p), ("v_codes", c_p), ("k_scale", c_p), ("k_zero", c_p),
+                ("v_scale", c_p), ("v_zero", c_p), ("k_kept", c_p), ("v_kept", c_p),
+                ("kept_idx", c_p), ("tail_k", c_p), ("tail_v", c_p),
+                ("tail_cap", c_i64), ("tail_len", c_i64)]
+
+
+_P = ctypes.POINTER(vc_ckv)
+# name -> (restype, argtypes); every symbol declared in include/vc.h
+_DECLS = {
+    "vc_compress": (c_i32, [_P, c_p, c_p, c_i64, c_i64, c_i64, c_i64, c_p, c_i32, c_f32, c_p, c_sz, c_p]),
+    "vc_compress_workspace_bytes": (c_sz, [_P, c_i64, c_i32]),
+    "vc_drop_keep_count": (c_i64, [c_f32, c_i64]),
+    "vc_drop_scores": (c_i32, [c_p, c_i32, c_p, c_i32, c_i32, c_i64, c_i32, c_i32, c_f32, c_p, c_p, c_sz, c_p]),
+    "vc_drop_scores_workspace_bytes": (c_sz, [c_i32, c_i32, c_i64, c_i32]),
+    "vc_drop_select": (c_i32, [c_p, c_i32, c_i32, c_i64, c_i64, c_p, c_p, c_sz, c_p]),
+    "vc_drop_select_workspace_bytes": (c_sz, [c_i32, c_i32, c_i64]),
+    "vc_gather_rows": (c_i32, [c_p, c_i32, c_i32, c_i32, c_i64, c_i32, c_p, c_i64, c_p, c_i64, c_p]),
+    "vc_decode_attn_compressed": (c_i32, [_P, c_p, c_i32, c_f32, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
+    "vc_decode_workspace_bytes": (c_sz, [_P, c_i32]),
+    "vc_verify_attn_full": (c_i32, [c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, c_i64, c_p,
+                                    c_i32, c_f32, c_p, c_p, c_p, c_sz, c_p]),
+    "vc_verify_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, c_i32]),
+    "vc_verify_split_tokens": (c_i32, [c_i32, c_i32]),
+    "vc_head_mean": (c_i32, [c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, c_i64, c_i64, c_p, c_p]),
+    "vc_logits_argmax": (c_i32, [c_p, c_i32, c_i64, c_i32, c_p, c_i32, c_i32, c_p, c_p, c_sz, c_p]),
+    "vc_logits_workspace_bytes": (c_sz, [c_i64, c_i32]),
+    "vc_accept": (c_i32, [c_p, c_p, c_i32, c_i32, c_p, c_p, c_p, c_p]),
+    "vc_stage_full_kv": (c_i32, [c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i64, c_i64, c_i64, c_i64,
+                                 c_p, c_p]),
+    "vc_stage_full_kv_d2h": (c_i32, [c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i64, c_i64, c_i64, c_i64,
+                                     c_p, c_p]),
+    "vc_last_error": (ctypes.c_char_p, []),
+}
+EXPORTS = tuple(_DECLS)
+for _n, (_r, _a) in _DECLS.items():
+    _f = getattr(lib, _n)
+    _f.restype, _f.argtypes = _r, _a
+
+
+def vc_last_error() -> str:
+    return lib.vc_last_error().decode()
+
+
+def _check(status, fn):
+    if status != VC_OK:
+        raise VcError(status, fn, vc_last_error())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        return torch.cuda.current_stream().cuda_stream
+    return s.cuda_stream if hasattr(s, "cuda_stream") else s
+
+
+def _dt(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return VC_F32
+    if t == torch.bfloat16:
+        return VC_BF16
+    raise TypeError(f"unsupported dtype {t}")
+
+
+_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """Zero-filled device workspace (the library restores the parts that must be zero)."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+class Ckv:
+    """Device storage of one layer's compressed KV cache plus its vc_ckv descriptor.
+
+    method "quant": packed codes and group parameters; method "drop": kept rows and
+    their source positions.  Both carry a full-precision tail of tail_cap rows."""
+
+    def __init__(self, method, B, Hkv, d, capacity, *, k_bits=4, v_bits=4, group=32, param_dtype="bf16",
+                 kv_dtype="bf16", keep_ratio=1.0, tail_cap=0, device="cuda"):
+        self.method = {"quant": VC_QUANT_KIVI, "drop": VC_DROP_TOPK}[method]
+        self.B, self.Hkv, self.d, self.capacity = B, Hkv, d, capacity
+        self.k_bits, self.v_bits, self.group = k_bits, v_bits, group
+        self.param_dtype, self.kv_dtype, self.keep_ratio = param_dtype, kv_dtype, keep_ratio
+        self.tail_cap = tail_cap
+        self.n_main = 0
+        self.tail_len = 0
+        kvt, pt = _TORCH[kv_dtype], _TORCH[param_dtype]
+        z = dict(device=device)
+        self.k_codes = self.v_codes = self.k_scale = self.k_zero = self.v_scale = self.v_zero = None
+        self.k_kept = self.v_kept = self.kept_idx = None
+        if self.method == VC_QUANT_KIVI:
+            self.k_codes = torch.zeros(B, Hkv, capacity, d * k_bits // 32, dtype=torch.int32, **z)
+            self.v_codes = torch.zeros(B, Hkv, capacity, d * v_bits // 32, dtype=torch.int32, **z)
+            self.k_scale = torch.zeros(B, Hkv, capacity // group, d, dtype=pt, **z)
+            self.k_zero = torch.zeros(B, Hkv, capacity // group, d, dtype=pt, **z)
+            self.v_scale = torch.zeros(B, Hkv, capacity, d // group, dtype=pt, **z)
+            self.v_zero = torch.zeros(B, Hkv, capacity, d // group, dtype=pt, **z)
+        else:
+            self.k_kept = torch.zeros(B, Hkv, capacity, d, dtype=kvt, **z)
+            self.v_kept = torch.zeros(B, Hkv, capacity, d, dtype=kvt, **z)
+            self.kept_idx = torch.zeros(B, Hkv, capacity, dtype=torch.int32, **z)
+        self.tail_k = torch.zeros(B, Hkv, tail_cap, d, dtype=kvt, **z) if tail_cap else None
+        self.tail_v = torch.zeros(B, Hkv, tail_cap, d, dtype=kvt, **z) if tail_cap else None
+
+    def struct(self) -> vc_ckv:
+        return vc_ckv(self.method, self.k_bits, self.v_bits, self.group,
+                      VC_F32 if self.param_dtype == "f32" else VC_BF16,
+                      VC_F32 if self.kv_dtype == "f32" else VC_BF16, self.keep_ratio,
+                      self.B, self.Hkv, self.d, self.capacity, self.n_main,
+                      _ptr(self.k_codes), _ptr(self.v_codes), _ptr(self.k_scale), _ptr(self.k_zero),
+                      _ptr(self.v_scale), _ptr(self.v_zero), _ptr(self.k_kept), _ptr(self.v_kept),
+                      _ptr(self.kept_idx), _ptr(self.tail_k), _ptr(self.tail_v), self.tail_cap, self.tail_len)
+
+    def stored_bytes(self, n_main=None) -> int:
+        """Bytes of the compressed rows [0, n_main) over all sequences and heads."""
+        n = self.n_main if n_main is None else n_main
+        bh = self.B * self.Hkv
+        if self.method == VC_QUANT_KIVI:
+            pb = 4 if self.param_dtype == "f32" else 2
+            codes = bh * n * self.d * (self.k_bits + self.v_bits) // 8
+            params = bh * (n // self.group) * self.d * 2 * pb + bh * n * (self.d // self.group) * 2 * pb
+            return codes + params
+        eb = 4 if self.kv_dtype == "f32" else 2
+        return bh * n * self.d * 2 * eb
+
+
+def vc_compress_workspace_bytes(ckv: Ckv, n_tokens: int, n_probes: int) -> int:
+    return lib.vc_compress_workspace_bytes(ctypes.byref(ckv.struct()), n_tokens, n_probes)
+
+
+def vc_compress(ckv: Ckv, k_src, v_src, *, src_begin=0, n_tokens=None, dst_begin=0, probes=None,
+                sm_scale=None, ws=None, stream=None):
+    src_rows = k_src.shape[2]
+    n = src_rows - src_begin if n_tokens is None else n_tokens
+    P = 0 if probes is None else probes.shape[1]
+    scale = (ckv.d ** -0.5) if sm_scale is None else sm_scale
+    c = ckv.struct()
+    if ws is None:
+        ws = workspace(lib.vc_compress_workspace_bytes(ctypes.byref(c), n, P), k_src.device)
+    _check(lib.vc_compress(ctypes.byref(c), _ptr(k_src), _ptr(v_src), src_rows, src_begin, n, dst_begin,
+                           _ptr(probes), P, scale, _ptr(ws), ws.numel(), _stream(stream)), "vc_compress")
+
+
+def vc_drop_keep_count(keep_ratio: float, N: int) -> int:
+    return lib.vc_drop_keep_count(keep_ratio, N)
+
+
+def vc_drop_scores_workspace_bytes(B, Hkv, N, n_probes) -> int:
+    return lib.vc_drop_scores_workspace_bytes(B, Hkv, N, n_probes)
+
+
+def vc_drop_scores(k, probes, scores, *, sm_scale=None, ws=None, stream=None):
+    B, Hkv, N, d = k.shape
+    P = probes.shape[1]
+    if ws is None:
+        ws = workspace(lib.vc_drop_scores_workspace_bytes(B, Hkv, N, P), k.device)
+    _check(lib.vc_drop_scores(_ptr(k), _dt(k.dtype), _ptr(probes), B, Hkv, N, d, P,
+                              d ** -0.5 if sm_scale is None else sm_scale, _ptr(scores), _ptr(ws), ws.numel(),
+                              _stream(stream)), "vc_drop_scores")
+
+
+def vc_drop_select(scores, n_keep, kept_idx, *, stream=None):
+    B, Hkv, N = scores.shape
+    _check(lib.vc_drop_select(_ptr(scores), B, Hkv, N, n_keep, _ptr(kept_idx), None, 0, _stream(stream)),
+           "vc_drop_select")
+
+
+def vc_gather_rows(src, idx, n, dst, *, stream=None):
+    B, Hkv, src_rows, d = src.shape
+    _check(lib.vc_gather_rows(_ptr(src), _dt(src.dtype), B, Hkv, src_rows, d, _ptr(idx), n, _ptr(dst),
+                              dst.shape[2], _stream(stream)), "vc_gather_rows")
+
+
+def vc_decode_workspace_bytes(ckv: Ckv, Hq: int) -> int:
+    return lib.vc_decode_workspace_bytes(ctypes.byref(ckv.struct()), Hq)
+
+
+def vc_decode_attn_compressed(ckv: Ckv, q, out, *, lse=None, sm_scale=None, main_lens=None, tail_lens=None,
+                              ws=None, stream=None):
+    B, Hq, d = q.shape
+    c = ckv.struct()
+    if ws is None:
+        ws = workspace(lib.vc_decode_workspace_bytes(ctypes.byref(c), Hq), q.device)
+    _check(lib.vc_decode_attn_compressed(ctypes.byref(c), _ptr(q), Hq, d ** -0.5 if sm_scale is None else sm_scale,
+                                         _ptr(main_lens), _ptr(tail_lens), _ptr(out), _ptr(lse), _ptr(ws),
+                                         ws.numel(), _stream(stream)), "vc_decode_attn_compressed")
+
+
+def vc_verify_split_tokens(B: int, Hkv: int) -> int:
+    return lib.vc_verify_split_tokens(B, Hkv)
+
+
+def vc_verify_workspace_bytes(B, Hq, Hkv, d, k, max_len, split_tokens=0) -> int:
+    return lib.vc_verify_workspace_bytes(B, Hq, Hkv, d, k, max_len, split_tokens)
+
+
+def vc_verify_attn_full(q, k_cache, v_cache, ctx_len, out, *, lse=None, ctx_lens=None, split_tokens=0,
+                        sm_scale=None, ws=None, stream=None):
+    B, Hq, k, d = q.shape
+    Hkv, rows = k_cache.shape[1], k_cache.shape[2]
+    if ws is None:
+        ws = workspace(lib.vc_verify_workspace_bytes(B, Hq, Hkv, d, k, ctx_len, split_tokens), q.device)
+    _check(lib.vc_verify_attn_full(_ptr(q), _ptr(k_cache), _ptr(v_cache), _dt(q.dtype), B, Hq, Hkv, d, k, rows,
+                                   ctx_len, _ptr(ctx_lens), split_tokens,
+                                   d ** -0.5 if sm_scale is None else sm_scale, _ptr(out), _ptr(lse), _ptr(ws),
+                                   ws.numel(), _stream(stream)), "vc_verify_attn_full")
+
+
+def vc_head_mean(o, u, *, k=None, stream=None):
+    """o: [B, Hq, k, d] (verify layout) or [B, Hq, d] (decode layout) -> u float32 [B*k, d]."""
+    if o.dim() == 3:
+        B, Hq, d = o.shape
+        kk, sb, sh, si = 1, o.stride(0), o.stride(1), 0
+    else:
+        B, Hq, kk, d = o.shape
+        sb, sh, si = o.stride(0), o.stride(1), o.stride(2)
+    _check(lib.vc_head_mean(_ptr(o), _dt(o.dtype), B, Hq, kk, d, sb, sh, si, _ptr(u), _stream(stream)),
+           "vc_head_mean")
+
+
+def vc_logits_workspace_bytes(R, V) -> int:
+    return lib.vc_logits_workspace_bytes(R, V)
+
+
+def vc_logits_argmax(u, W, tokens, *, ws=None, stream=None):
+    R, K = u.shape
+    V = W.shape[0]
+    if ws is None:
+        ws = workspace(lib.vc_logits_workspace_bytes(R, V), u.device)
+    _check(lib.vc_logits_argmax(_ptr(u), _dt(u.dtype), R, K, _ptr(W), _dt(W.dtype), V, _ptr(tokens), _ptr(ws),
+                                ws.numel(), _stream(stream)), "vc_logits_argmax")
+
+
+def vc_accept(draft, target, accept_len, n_commit, commit, *, stream=None):
+    B, k = draft.shape
+    _check(lib.vc_accept(_ptr(draft), _ptr(target), B, k, _ptr(accept_len), _ptr(n_commit), _ptr(commit),
+                         _stream(stream)), "vc_accept")
+
+
+def vc_stage_full_kv(host_k, host_v, dev_k, dev_v, tok_begin, tok_end, *, copy_stream=None, done=None):
+    B, Hkv, host_rows, d = host_k.shape
+    _check(lib.vc_stage_full_kv(_ptr(host_k), _ptr(host_v), _ptr(dev_k), _ptr(dev_v), B, Hkv, d,
+                                host_k.element_size(), host_rows, dev_k.shape[2], tok_begin, tok_end,
+                                _stream(copy_stream), None if done is None else done.cuda_event),
+           "vc_stage_full_kv")
+
+
+def vc_stage_full_kv_d2h(dev_k, dev_v, host_k, host_v, tok_begin, tok_end, *, copy_stream=None, done=None):
+    B, Hkv, host_rows, d = host_k.shape
+    _check(lib.vc_stage_full_kv_d2h(_ptr(dev_k), _ptr(dev_v), _ptr(host_k), _ptr(host_v), B, Hkv, d,
+                                    host_k.element_size(), host_rows, dev_k.shape[2], tok_begin, tok_end,
+                                    _stream(copy_stream), None if done is None else done.cuda_event),
+           "vc_stage_full_kv_d2h")

@@ -1,0 +1,131 @@
+// Entry points that only dispatch (compression) or drive the copy engines (full-KV
+// staging), and the thread-local error message.
+//
+// Staging follows the abstract of "VeriCache: Turning Lossy KV Cache into Lossless
+// LLM Inference" (neuraltrendhub.com summary, "Original abstract"): the full KV
+// cache stays out of GPU memory and is swapped in for verification, overlapped with
+// compressed-KV drafting because one is bound by HBM and the other by PCIe.  The
+// rows of every (sequence, kv-head) are one strided 2-D copy per tensor, issued as
+// hipMemcpy2DAsync on the caller's copy stream so the DMA engines move them while
+// the compute queues draft.
+
+#include "common.h"
+
+namespace vc {
+
+static thread_local char g_err[512];
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+vc_status compress_quant(const vc_ckv* c, const void* k_src, const void* v_src, int64_t src_rows, int64_t src_begin,
+                         int64_t n_tokens, int64_t dst_begin, hipStream_t stream);
+vc_status drop_scores_impl(const void* k, int32_t kv_dtype, const void* probes, int32_t B, int32_t Hkv, int64_t N,
+                           int32_t d, int32_t P, float sm_scale, float* scores, void* ws, size_t ws_bytes,
+                           hipStream_t s);
+vc_status drop_select_impl(const float* scores, int32_t B, int32_t Hkv, int64_t N, int64_t n_keep, int32_t* kept,
+                           int64_t kept_pitch, hipStream_t s);
+vc_status gather_impl(const void* src, int32_t kv_dtype, int32_t B, int32_t Hkv, int64_t src_rows, int32_t d,
+                      const int32_t* idx, int64_t n, int64_t idx_pitch, void* dst, int64_t dst_rows, hipStream_t s);
+
+static vc_status stage_rows(const void* src_k, const void* src_v, void* dst_k, void* dst_v, int32_t B, int32_t Hkv,
+                            int32_t d, int32_t elem_bytes, int64_t src_rows, int64_t dst_rows, int64_t tok_begin,
+                            int64_t tok_end, hipMemcpyKind kind, void* copy_stream, void* done) {
+  VC_REQUIRE(src_k && src_v && dst_k && dst_v, "NULL pointer argument");
+  VC_REQUIRE(B > 0 && Hkv > 0 && d > 0, "bad B/Hkv/d");
+  VC_REQUIRE(elem_bytes == 1 || elem_bytes == 2 || elem_bytes == 4 || elem_bytes == 8, "bad elem_bytes %d",
+             elem_bytes);
+  VC_REQUIRE(tok_begin >= 0 && tok_begin <= tok_end && tok_end <= src_rows && tok_end <= dst_rows,
+             "rows [%lld, %lld) do not fit host_rows %lld / dev_rows %lld", (long long)tok_begin, (long long)tok_end,
+             (long long)(kind == hipMemcpyHostToDevice ? src_rows : dst_rows),
+             (long long)(kind == hipMemcpyHostToDevice ? dst_rows : src_rows));
+  hipStream_t s = as_stream(copy_stream);
+  const size_t row = static_cast<size_t>(d) * elem_bytes;
+  const size_t width = static_cast<size_t>(tok_end - tok_begin) * row;
+  if (width > 0) {
+    const size_t spitch = static_cast<size_t>(src_rows) * row, dpitch = static_cast<size_t>(dst_rows) * row;
+    const size_t off_s = static_cast<size_t>(tok_begin) * row, off_d = off_s;
+    const size_t height = static_cast<size_t>(B) * Hkv;
+    VC_HIP(hipMemcpy2DAsync(static_cast<char*>(dst_k) + off_d, dpitch, static_cast<const char*>(src_k) + off_s, spitch,
+                            width, height, kind, s));
+    VC_HIP(hipMemcpy2DAsync(static_cast<char*>(dst_v) + off_d, dpitch, static_cast<const char*>(src_v) + off_s, spitch,
+                            width, height, kind, s));
+  }
+  if (done) VC_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(done), s));
+  return VC_OK;
+}
+
+}  // namespace vc
+
+using namespace vc;
+
+extern "C" const char* vc_last_error(void) { return g_err; }
+
+extern "C" size_t vc_compress_workspace_bytes(const vc_ckv* c, int64_t n_tokens, int32_t n_probes) {
+  if (!c || c->method != VC_DROP_TOPK || n_tokens <= 0 || n_probes <= 0 || c->B <= 0 || c->Hkv <= 0) return 0;
+  size_t scores = align_up(static_cast<size_t>(c->B) * c->Hkv * n_tokens * sizeof(float), 256);
+  return scores + vc_drop_scores_workspace_bytes(c->B, c->Hkv, n_tokens, n_probes);
+}
+
+extern "C" vc_status vc_compress(const vc_ckv* c, const void* k_src, const void* v_src, int64_t src_rows,
+                                 int64_t src_begin, int64_t n_tokens, int64_t dst_begin, const void* probes,
+                                 int32_t n_probes, float sm_scale, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  VC_REQUIRE(c != nullptr, "ckv is NULL");
+  hipStream_t s = as_stream(stream);
+  if (c->method == VC_QUANT_KIVI) {
+    VC_REQUIRE(probes == nullptr && n_probes == 0, "probes must be NULL for quantization");
+    return compress_quant(c, k_src, v_src, src_rows, src_begin, n_tokens, dst_begin, s);
+  }
+  VC_REQUIRE(c->method == VC_DROP_TOPK, "unknown ckv.method %d", c->method);
+  VC_REQUIRE(src_begin == 0 && dst_begin == 0, "token dropping compresses whole sequences (src_begin = dst_begin = 0)");
+  VC_REQUIRE(k_src && v_src && probes, "k_src / v_src / probes is NULL");
+  VC_REQUIRE(c->B > 0 && c->Hkv > 0 && c->d > 0, "bad B/Hkv/d");
+  VC_REQUIRE(valid_dtype(c->kv_dtype), "bad kv_dtype");
+  VC_REQUIRE(n_tokens > 0 && n_tokens <= src_rows, "n_tokens must be in [1, src_rows]");
+  VC_REQUIRE(src_rows == n_tokens, "token dropping needs src_rows == n_tokens");
+  VC_REQUIRE(c->keep_ratio > 0.f && c->keep_ratio <= 1.f, "keep_ratio must be in (0, 1]");
+  const int64_t keep = vc_drop_keep_count(c->keep_ratio, n_tokens);
+  VC_REQUIRE(keep <= c->capacity, "n_keep %lld exceeds capacity %lld", (long long)keep, (long long)c->capacity);
+  VC_REQUIRE(c->k_kept && c->v_kept && c->kept_idx, "kept arrays are NULL");
+  size_t need = vc_compress_workspace_bytes(c, n_tokens, n_probes);
+  if (!ws || ws_bytes < need) {
+    set_error("compress workspace needs %zu bytes (got %zu)", need, ws_bytes);
+    return VC_ERR_WORKSPACE;
+  }
+  float* scores = static_cast<float*>(ws);
+  size_t sb = align_up(static_cast<size_t>(c->B) * c->Hkv * n_tokens * sizeof(float), 256);
+  vc_status st = drop_scores_impl(k_src, c->kv_dtype, probes, c->B, c->Hkv, n_tokens, c->d, n_probes, sm_scale,
+                                  scores, static_cast<char*>(ws) + sb, ws_bytes - sb, s);
+  if (st != VC_OK) return st;
+  st = drop_select_impl(scores, c->B, c->Hkv, n_tokens, keep, c->kept_idx, c->capacity, s);
+  if (st != VC_OK) return st;
+  st = gather_impl(k_src, c->kv_dtype, c->B, c->Hkv, src_rows, c->d, c->kept_idx, keep, c->capacity, c->k_kept,
+                   c->capacity, s);
+  if (st != VC_OK) return st;
+  return gather_impl(v_src, c->kv_dtype, c->B, c->Hkv, src_rows, c->d, c->kept_idx, keep, c->capacity, c->v_kept,
+                     c->capacity, s);
+}
+
+extern "C" vc_status vc_stage_full_kv(const void* host_k, const void* host_v, void* dev_k, void* dev_v, int32_t B,
+                                      int32_t Hkv, int32_t d, int32_t elem_bytes, int64_t host_rows, int64_t dev_rows,
+                                      int64_t tok_begin, int64_t tok_end, void* copy_stream, void* done) {
+  clear_error();
+  return stage_rows(host_k, host_v, dev_k, dev_v, B, Hkv, d, elem_bytes, host_rows, dev_rows, tok_begin, tok_end,
+                    hipMemcpyHostToDevice, copy_stream, done);
+}
+
+extern "C" vc_status vc_stage_full_kv_d2h(const void* dev_k, const void* dev_v, void* host_k, void* host_v, int32_t B,
+                                          int32_t Hkv, int32_t d, int32_t elem_bytes, int64_t host_rows,
+                                          int64_t dev_rows, int64_t tok_begin, int64_t tok_end, void* copy_stream,
+                                          void* done) {
+  clear_error();
+  return stage_rows(dev_k, dev_v, host_k, host_v, B, Hkv, d, elem_bytes, dev_rows, host_rows, tok_begin, tok_end,
+                    hipMemcpyDeviceToHost, copy_stream, done);
+}

@@ -1,0 +1,96 @@
+// Internal helpers shared by the library's HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+#include <stdarg.h>
+
+#include "../../include/vc.h"
+
+namespace vc {
+
+// ---------------------------------------------------------------- errors
+void set_error(const char* fmt, ...);
+void clear_error();
+
+#define VC_REQUIRE(cond, ...)                        \
+  do {                                               \
+    if (!(cond)) {                                   \
+      ::vc::set_error(__VA_ARGS__);                  \
+      return VC_ERR_INVALID_ARG;                     \
+    }                                                \
+  } while (0)
+
+#define VC_UNSUPPORTED(cond, ...)                    \
+  do {                                               \
+    if (!(cond)) {                                   \
+      ::vc::set_error(__VA_ARGS__);                  \
+      return VC_ERR_UNSUPPORTED;                     \
+    }                                                \
+  } while (0)
+
+#define VC_HIP(expr)                                                              \
+  do {                                                                            \
+    hipError_t e_ = (expr);                                                       \
+    if (e_ != hipSuccess) {                                                       \
+      ::vc::set_error("%s failed: %s", #expr, hipGetErrorString(e_));             \
+      return VC_ERR_HIP;                                                          \
+    }                                                                             \
+  } while (0)
+
+#define VC_LAUNCHED(name)                                                         \
+  do {                                                                            \
+    hipError_t e_ = hipGetLastError();                                            \
+    if (e_ != hipSuccess) {                                                       \
+      ::vc::set_error("launch of %s failed: %s", name, hipGetErrorString(e_));    \
+      return VC_ERR_HIP;                                                          \
+    }                                                                             \
+  } while (0)
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline bool valid_dtype(int32_t t) { return t == VC_F32 || t == VC_BF16; }
+inline size_t dtype_bytes(int32_t t) { return t == VC_F32 ? 4 : 2; }
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- device types
+typedef uint16_t bf16_t;  // raw bfloat16 storage
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest, ties to even (inputs are finite in this library).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  static __device__ __forceinline__ void store(bf16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+__device__ __forceinline__ float warp_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float warp_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+}  // namespace vc

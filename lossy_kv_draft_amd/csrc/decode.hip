@@ -1,0 +1,356 @@
+// Draft-side single-token decode attention over the compressed KV cache.
+//
+// Summary page "VeriCache: Turning Lossy KV Cache into Lossless LLM Inference",
+// "What the paper found": drafting runs the target model on the compressed KV
+// cache and is HBM-bandwidth-bound.  Keys/values are either KIVI-quantized packed
+// codes (dequantized in registers as z + code * s) or token-dropped rows kept in
+// full precision, followed by a short full-precision tail.
+//
+// Generic kernel (any bit width, float32 or bf16 storage, d <= 256):
+//   grid = (splits, B*Hkv); one workgroup streams one contiguous range of token
+//   positions of one (sequence, kv-head) and serves all Hq/Hkv q-heads that read
+//   that kv-head, so each packed row is fetched from HBM once.  Per 32-token tile:
+//   dequantize K and V into LDS (float32), scores per (head, token), online
+//   softmax per head (base-2, scale folded into q), then P.V accumulated in
+//   registers per (head, channel).  Each split writes (m, l, o) partials to the
+//   workspace; the last split of a (sequence, kv-head) to finish -- found with an
+//   atomic counter -- merges all splits in split order (deterministic) and writes
+//   the normalized output and the log-sum-exp, then resets its counter to zero.
+
+#include "common.h"
+
+namespace vc {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecTile = 32;
+constexpr int kDecMaxAcc = 16;     // (H * d) / kDecThreads accumulators per thread
+constexpr int kDecMaxSplits = 64;
+constexpr int kDecTargetBlocks = 2048;
+
+struct DecodeArgs {
+  // compressed cache
+  const uint32_t* k_codes;
+  const uint32_t* v_codes;
+  const void* k_scale;
+  const void* k_zero;
+  const void* v_scale;
+  const void* v_zero;
+  const void* k_kept;
+  const void* v_kept;
+  const void* tail_k;
+  const void* tail_v;
+  int64_t capacity, tail_cap, n_main, tail_len;
+  const int32_t* main_lens;
+  const int32_t* tail_lens;
+  int k_bits, v_bits, G;
+  // problem
+  const void* q;
+  void* out;
+  float* lse;
+  int Hkv, H, d;
+  float qscale;  // sm_scale * log2(e)
+  int splits;
+  int64_t chunk;
+  // workspace
+  float* part_o;   // [B*Hkv][splits][H][d]
+  float* part_ml;  // [B*Hkv][splits][H][2]
+  int* counters;   // [B*Hkv]
+};
+
+template <typename P>
+__device__ __forceinline__ float load_param(const void* p, int64_t i) {
+  return Elem<P>::load(static_cast<const P*>(p), i);
+}
+
+__device__ __forceinline__ uint32_t extract_code(const uint32_t* row, int c, int bits) {
+  int pos = c * bits;
+  int w = pos >> 5, off = pos & 31;
+  uint32_t x = row[w] >> off;
+  if (off + bits > 32) x |= row[w + 1] << (32 - off);
+  return x & ((1u << bits) - 1u);
+}
+
+// QUANT = true: packed codes; false: kept (dense) rows.
+template <typename T, typename P, bool QUANT>
+__global__ void __launch_bounds__(kDecThreads) decode_generic_kernel(DecodeArgs a) {
+  extern __shared__ float smem[];
+  const int d = a.d, H = a.H;
+  const int kpitch = d + 1;
+  float* qs = smem;                          // [H][d]
+  float* kt = qs + H * d;                    // [kDecTile][d+1]
+  float* vt = kt + kDecTile * kpitch;        // [kDecTile][d]
+  float* sc = vt + kDecTile * d;             // [H][kDecTile]
+  float* alpha = sc + H * kDecTile;          // [H]
+  float* mrun = alpha + H;                   // [H]
+  float* lrun = mrun + H;                    // [H]
+  __shared__ int is_last;
+
+  const int split = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / a.Hkv;
+  const int hk = bh % a.Hkv;
+  const int tid = threadIdx.x;
+
+  const int64_t main_len = a.main_lens ? a.main_lens[b] : a.n_main;
+  const int64_t tail_len = a.tail_lens ? a.tail_lens[b] : a.tail_len;
+  const int64_t total = main_len + tail_len;
+  const int64_t start = static_cast<int64_t>(split) * a.chunk;
+  const int64_t end = min(total, start + a.chunk);
+
+  const T* q = static_cast<const T*>(a.q);
+  for (int i = tid; i < H * d; i += kDecThreads) {
+    int h = i / d, c = i % d;
+    qs[i] = Elem<T>::load(q, (static_cast<int64_t>(b) * a.Hkv * H + hk * H + h) * d + c) * a.qscale;
+  }
+  for (int h = tid; h < H; h += kDecThreads) {
+    mrun[h] = -INFINITY;
+    lrun[h] = 0.f;
+  }
+  float acc[kDecMaxAcc];
+#pragma unroll
+  for (int j = 0; j < kDecMaxAcc; ++j) acc[j] = 0.f;
+  __syncthreads();
+
+  const int kw = d * a.k_bits / 32, vw = d * a.v_bits / 32;
+  const int vgroups = d / a.G;
+  for (int64_t t0 = start; t0 < end; t0 += kDecTile) {
+    // ---- stage dequantized K and V of the tile
+    for (int i = tid; i < kDecTile * d; i += kDecThreads) {
+      int t = i / d, c = i % d;
+      int64_t pos = t0 + t;
+      float kv = 0.f, vv = 0.f;
+      if (pos < end) {
+        if (pos < main_len) {
+          if constexpr (QUANT) {
+            const uint32_t* krow = a.k_codes + (static_cast<int64_t>(bh) * a.capacity + pos) * kw;
+            const uint32_t* vrow = a.v_codes + (static_cast<int64_t>(bh) * a.capacity + pos) * vw;
+            int64_t kp = (static_cast<int64_t>(bh) * (a.capacity / a.G) + pos / a.G) * d + c;
+            int64_t vp = (static_cast<int64_t>(bh) * a.capacity + pos) * vgroups + c / a.G;
+            kv = load_param<P>(a.k_zero, kp) + static_cast<float>(extract_code(krow, c, a.k_bits)) * load_param<P>(a.k_scale, kp);
+            vv = load_param<P>(a.v_zero, vp) + static_cast<float>(extract_code(vrow, c, a.v_bits)) * load_param<P>(a.v_scale, vp);
+          } else {
+            int64_t e = (static_cast<int64_t>(bh) * a.capacity + pos) * d + c;
+            kv = Elem<T>::load(static_cast<const T*>(a.k_kept), e);
+            vv = Elem<T>::load(static_cast<const T*>(a.v_kept), e);
+          }
+        } else {
+          int64_t e = (static_cast<int64_t>(bh) * a.tail_cap + (pos - main_len)) * d + c;
+          kv = Elem<T>::load(static_cast<const T*>(a.tail_k), e);
+          vv = Elem<T>::load(static_cast<const T*>(a.tail_v), e);
+        }
+      }
+      kt[t * kpitch + c] = kv;
+      vt[t * d + c] = vv;
+    }
+    __syncthreads();
+    // ---- scores
+    for (int j = tid; j < H * kDecTile; j += kDecThreads) {
+      int h = j / kDecTile, t = j % kDecTile;
+      float s = -INFINITY;
+      if (t0 + t < end) {
+        const float* kr = kt + t * kpitch;
+        const float* qr = qs + h * d;
+        float x = 0.f;
+        for (int c = 0; c < d; ++c) x = fmaf(qr[c], kr[c], x);
+        s = x;
+      }
+      sc[j] = s;
+    }
+    __syncthreads();
+    // ---- online softmax, one thread per head
+    for (int h = tid; h < H; h += kDecThreads) {
+      float mt = -INFINITY;
+      for (int t = 0; t < kDecTile; ++t) mt = fmaxf(mt, sc[h * kDecTile + t]);
+      float mn = fmaxf(mrun[h], mt);
+      float l = 0.f;
+      for (int t = 0; t < kDecTile; ++t) {
+        float p = exp2f(sc[h * kDecTile + t] - mn);
+        sc[h * kDecTile + t] = p;
+        l += p;
+      }
+      float al = exp2f(mrun[h] - mn);
+      alpha[h] = al;
+      lrun[h] = lrun[h] * al + l;
+      mrun[h] = mn;
+    }
+    __syncthreads();
+    // ---- P.V
+#pragma unroll
+    for (int j = 0; j < kDecMaxAcc; ++j) {
+      int i = tid + j * kDecThreads;
+      if (i < H * d) {
+        int h = i / d, c = i % d;
+        float x = acc[j] * alpha[h];
+        const float* pr = sc + h * kDecTile;
+        for (int t = 0; t < kDecTile; ++t) x = fmaf(pr[t], vt[t * d + c], x);
+        acc[j] = x;
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- partials
+  const int64_t pbase = static_cast<int64_t>(bh) * a.splits + split;
+#pragma unroll
+  for (int j = 0; j < kDecMaxAcc; ++j) {
+    int i = tid + j * kDecThreads;
+    if (i < H * d) a.part_o[pbase * H * d + i] = acc[j];
+  }
+  for (int h = tid; h < H; h += kDecThreads) {
+    a.part_ml[(pbase * H + h) * 2 + 0] = mrun[h];
+    a.part_ml[(pbase * H + h) * 2 + 1] = lrun[h];
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    int prev = atomicAdd(a.counters + bh, 1);
+    is_last = (prev == a.splits - 1);
+  }
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+
+  // ---- merge all splits in split order
+  T* out = static_cast<T*>(a.out);
+  for (int i = tid; i < H * d; i += kDecThreads) {
+    int h = i / d;
+    float M = -INFINITY;
+    for (int s = 0; s < a.splits; ++s)
+      M = fmaxf(M, a.part_ml[((static_cast<int64_t>(bh) * a.splits + s) * H + h) * 2]);
+    float L = 0.f, O = 0.f;
+    for (int s = 0; s < a.splits; ++s) {
+      int64_t ps = static_cast<int64_t>(bh) * a.splits + s;
+      float m = a.part_ml[(ps * H + h) * 2];
+      float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+      L += a.part_ml[(ps * H + h) * 2 + 1] * w;
+      O += a.part_o[ps * H * d + i] * w;
+    }
+    float o = L > 0.f ? O / L : 0.f;
+    int64_t oi = (static_cast<int64_t>(b) * a.Hkv * H + hk * H) * d + i;
+    Elem<T>::store(out, oi, o);
+    if (a.lse && (i % d) == 0)
+      a.lse[static_cast<int64_t>(b) * a.Hkv * H + hk * H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  }
+  if (tid == 0) a.counters[bh] = 0;
+}
+
+// ------------------------------------------------------------------ host side
+
+vc_status validate_quant_ckv(const vc_ckv* c);
+
+static int decode_splits(const vc_ckv* c) {
+  int bh = c->B * c->Hkv;
+  int s = static_cast<int>(cdiv(kDecTargetBlocks, bh));
+  return s < 1 ? 1 : (s > kDecMaxSplits ? kDecMaxSplits : s);
+}
+
+static vc_status validate_decode_ckv(const vc_ckv* c) {
+  VC_REQUIRE(c != nullptr, "ckv is NULL");
+  if (c->method == VC_QUANT_KIVI) return validate_quant_ckv(c);
+  VC_REQUIRE(c->method == VC_DROP_TOPK, "unknown ckv.method %d", c->method);
+  VC_REQUIRE(c->B > 0 && c->Hkv > 0 && c->d > 0, "bad B/Hkv/d");
+  VC_REQUIRE(valid_dtype(c->kv_dtype), "bad kv_dtype");
+  VC_REQUIRE(c->n_main >= 0 && c->n_main <= c->capacity, "n_main must be in [0, capacity]");
+  VC_REQUIRE(c->n_main == 0 || (c->k_kept && c->v_kept), "kept arrays are NULL");
+  VC_REQUIRE(c->tail_len >= 0 && c->tail_len <= c->tail_cap, "tail_len must be in [0, tail_cap]");
+  VC_REQUIRE(c->tail_len == 0 || (c->tail_k && c->tail_v), "tail arrays are NULL");
+  return VC_OK;
+}
+
+}  // namespace vc
+
+using namespace vc;
+
+extern "C" size_t vc_decode_workspace_bytes(const vc_ckv* c, int32_t Hq) {
+  if (!c || c->B <= 0 || c->Hkv <= 0 || c->d <= 0 || Hq <= 0) return 0;
+  size_t bh = static_cast<size_t>(c->B) * c->Hkv;
+  size_t S = decode_splits(c);
+  size_t H = Hq / c->Hkv;
+  size_t bytes = align_up(bh * S * H * c->d * sizeof(float), 256);
+  bytes += align_up(bh * S * H * 2 * sizeof(float), 256);
+  bytes += align_up(bh * sizeof(int), 256);
+  return bytes;
+}
+
+extern "C" vc_status vc_decode_attn_compressed(const vc_ckv* c, const void* q, int32_t Hq, float sm_scale,
+                                               const int32_t* main_lens, const int32_t* tail_lens, void* out,
+                                               float* lse, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  vc_status st = validate_decode_ckv(c);
+  if (st != VC_OK) return st;
+  VC_REQUIRE(q && out, "q / out is NULL");
+  VC_REQUIRE(Hq > 0 && Hq % c->Hkv == 0, "Hq %d must be a positive multiple of Hkv %d", Hq, c->Hkv);
+  VC_REQUIRE(sm_scale > 0.f && sm_scale < INFINITY, "sm_scale must be positive and finite");
+  const int H = Hq / c->Hkv;
+  VC_UNSUPPORTED(c->d % 32 == 0 && c->d <= 256, "d must be a multiple of 32 and at most 256 (got %d)", c->d);
+  VC_UNSUPPORTED(H * c->d <= kDecMaxAcc * kDecThreads, "Hq/Hkv * d = %d exceeds %d", H * c->d,
+                 kDecMaxAcc * kDecThreads);
+  size_t need = vc_decode_workspace_bytes(c, Hq);
+  if (!ws || ws_bytes < need) {
+    set_error("decode workspace needs %zu bytes (got %zu)", need, ws_bytes);
+    return VC_ERR_WORKSPACE;
+  }
+  DecodeArgs a{};
+  a.k_codes = c->k_codes;
+  a.v_codes = c->v_codes;
+  a.k_scale = c->k_scale;
+  a.k_zero = c->k_zero;
+  a.v_scale = c->v_scale;
+  a.v_zero = c->v_zero;
+  a.k_kept = c->k_kept;
+  a.v_kept = c->v_kept;
+  a.tail_k = c->tail_k;
+  a.tail_v = c->tail_v;
+  a.capacity = c->capacity;
+  a.tail_cap = c->tail_cap;
+  a.n_main = c->n_main;
+  a.tail_len = c->tail_len;
+  a.main_lens = main_lens;
+  a.tail_lens = tail_lens;
+  a.k_bits = c->k_bits;
+  a.v_bits = c->v_bits;
+  a.G = c->method == VC_QUANT_KIVI ? c->group : 1;
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.Hkv = c->Hkv;
+  a.H = H;
+  a.d = c->d;
+  a.qscale = sm_scale * kLog2e;
+  int S = decode_splits(c);
+  int64_t total = c->n_main + c->tail_len;
+  a.chunk = cdiv(cdiv(total > 0 ? total : 1, S), kDecTile) * kDecTile;
+  a.splits = S;
+  size_t bh = static_cast<size_t>(c->B) * c->Hkv;
+  char* w = static_cast<char*>(ws);
+  a.part_o = reinterpret_cast<float*>(w);
+  w += align_up(bh * S * H * c->d * sizeof(float), 256);
+  a.part_ml = reinterpret_cast<float*>(w);
+  w += align_up(bh * S * H * 2 * sizeof(float), 256);
+  a.counters = reinterpret_cast<int*>(w);
+
+  dim3 grid(S, static_cast<unsigned>(bh));
+  size_t lds = (static_cast<size_t>(H) * c->d + kDecTile * (c->d + 1) + kDecTile * c->d + H * kDecTile + 3 * H) *
+               sizeof(float);
+  hipStream_t s = as_stream(stream);
+  const bool quant = c->method == VC_QUANT_KIVI;
+  const bool bf = c->kv_dtype == VC_BF16;
+  const bool pbf = c->param_dtype == VC_BF16;
+  if (quant) {
+    if (bf && pbf)
+      hipLaunchKernelGGL((decode_generic_kernel<bf16_t, bf16_t, true>), grid, dim3(kDecThreads), lds, s, a);
+    else if (bf)
+      hipLaunchKernelGGL((decode_generic_kernel<bf16_t, float, true>), grid, dim3(kDecThreads), lds, s, a);
+    else if (pbf)
+      hipLaunchKernelGGL((decode_generic_kernel<float, bf16_t, true>), grid, dim3(kDecThreads), lds, s, a);
+    else
+      hipLaunchKernelGGL((decode_generic_kernel<float, float, true>), grid, dim3(kDecThreads), lds, s, a);
+  } else {
+    if (bf)
+      hipLaunchKernelGGL((decode_generic_kernel<bf16_t, float, false>), grid, dim3(kDecThreads), lds, s, a);
+    else
+      hipLaunchKernelGGL((decode_generic_kernel<float, float, false>), grid, dim3(kDecThreads), lds, s, a);
+  }
+  VC_LAUNCHED("decode_generic_kernel");
+  return VC_OK;
+}

@@ -1,0 +1,411 @@
+// Token dropping by accumulated attention (compression of the draft cache).
+//
+// Episode page "VeriCache: Lossless LLM Inference from Lossy KV Caches", source 3
+// (H2O, heavy-hitter tokens collect most of the attention); summary page
+// "VeriCache: Turning Lossy KV Cache into Lossless LLM Inference", "Original
+// abstract" (token dropping is one of the compressor families).
+//
+// score_n = sum_p softmax_n(P_p . K_n * sm_scale) over n_probes probe queries,
+// per (sequence, kv-head); the n_keep highest scores are kept (equal scores: lower
+// position first), their positions stored ascending and their K/V rows copied.
+//
+// Scoring runs on matrix cores (v_mfma_f32_16x16x32_bf16: K and probes are bf16,
+// products exact, float32 accumulation) in two passes over K:
+//   pass 1 (grid = chunks x B*Hkv): per chunk and probe the running max and sum of
+//           exp2 of the scaled scores;
+//   pass 2: every block merges the per-chunk statistics of its (sequence, head)
+//           in chunk order, recomputes the scores of its chunk and sums the
+//           probabilities over the probes (fixed butterfly order).
+// Selection: one workgroup per (sequence, kv-head) finds the n_keep-th largest
+// score by a 4 x 8-bit radix select on the float bits (scores are >= 0, so their
+// bit patterns order like their values), then compacts in position order the
+// positions with a larger score plus the lowest-positioned equal ones.
+
+#include "common.h"
+
+namespace vc {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kDropChunk = 2048;
+constexpr int kDropMaxProbes = 64;
+
+union DP16 {
+  uint4 u;
+  bf16x8_t v;
+};
+
+template <int D>
+__device__ __forceinline__ void load_probes(const bf16_t* probes, int hk, int P, int l16, int kb,
+                                            bf16x8_t (&pf)[4][D / 32]) {
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    int p = ct * 16 + l16;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      DP16 x;
+      x.u = make_uint4(0, 0, 0, 0);
+      if (p < P)
+        x.u = *reinterpret_cast<const uint4*>(probes + (static_cast<int64_t>(hk) * P + p) * D + 32 * ks + 8 * kb);
+      pf[ct][ks] = x.v;
+    }
+  }
+}
+
+// s[ct][r] = score(token tok0 + 4 kb + r, probe 16 ct + l16), unscaled
+template <int D, typename T>
+__device__ __forceinline__ void tile_scores(const T* krows, int64_t tok0, int64_t N, int l16, int kb,
+                                            const bf16x8_t (&pf)[4][D / 32], f32x4_t (&s)[4]) {
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) s[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int64_t tok = tok0 + l16;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    DP16 a;
+    a.u = make_uint4(0, 0, 0, 0);
+    if (tok < N) {
+      if constexpr (sizeof(T) == 2) {
+        a.u = *reinterpret_cast<const uint4*>(krows + tok * D + 32 * ks + 8 * kb);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a.v[j] = static_cast<__bf16>(krows[tok * D + 32 * ks + 8 * kb + j]);
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) s[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, pf[ct][ks], s[ct], 0, 0, 0);
+  }
+}
+
+template <int D, typename T>
+__global__ void __launch_bounds__(256) drop_stats_kernel(const T* k, const bf16_t* probes, int Hkv, int64_t N, int P,
+                                                         float qscale, int nchunks, float* stat_m, float* stat_l) {
+  __shared__ float sm[4][kDropMaxProbes], sl[4][kDropMaxProbes];
+  const int chunk = blockIdx.x, bh = blockIdx.y, hk = bh % Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, kb = lane >> 4;
+  bf16x8_t pf[4][D / 32];
+  load_probes<D>(probes, hk, P, l16, kb, pf);
+  const T* krows = k + static_cast<int64_t>(bh) * N * D;
+  float m[4], l[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) { m[ct] = -INFINITY; l[ct] = 0.f; }
+  const int64_t c0 = static_cast<int64_t>(chunk) * kDropChunk;
+  const int64_t c1 = min(N, c0 + kDropChunk);
+  for (int64_t t0 = c0 + wave * 16; t0 < c1; t0 += 64) {
+    f32x4_t s[4];
+    tile_scores<D, T>(krows, t0, N, l16, kb, pf, s);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = (t0 + 4 * kb + r < c1) ? s[ct][r] * qscale : -INFINITY;
+        s[ct][r] = v;
+        mt = fmaxf(mt, v);
+      }
+      float mn = fmaxf(m[ct], mt);
+      if (mn == -INFINITY) continue;
+      float acc = l[ct] * exp2f(m[ct] - mn);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc += exp2f(s[ct][r] - mn);
+      l[ct] = acc;
+      m[ct] = mn;
+    }
+  }
+  // combine the 4 lane groups (same probe), then the 4 waves
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      float om = __shfl_xor(m[ct], o), ol = __shfl_xor(l[ct], o);
+      float mn = fmaxf(m[ct], om);
+      if (mn != -INFINITY) {
+        l[ct] = l[ct] * exp2f(m[ct] - mn) + ol * exp2f(om - mn);
+        m[ct] = mn;
+      }
+    }
+    if (kb == 0) { sm[wave][ct * 16 + l16] = m[ct]; sl[wave][ct * 16 + l16] = l[ct]; }
+  }
+  __syncthreads();
+  if (tid < P) {
+    float mm = sm[0][tid], ll = sl[0][tid];
+    for (int w = 1; w < 4; ++w) {
+      float om = sm[w][tid], ol = sl[w][tid];
+      float mn = fmaxf(mm, om);
+      if (mn != -INFINITY) {
+        ll = ll * exp2f(mm - mn) + ol * exp2f(om - mn);
+        mm = mn;
+      }
+    }
+    stat_m[(static_cast<int64_t>(bh) * nchunks + chunk) * P + tid] = mm;
+    stat_l[(static_cast<int64_t>(bh) * nchunks + chunk) * P + tid] = ll;
+  }
+}
+
+template <int D, typename T>
+__global__ void __launch_bounds__(256) drop_scores_kernel(const T* k, const bf16_t* probes, int Hkv, int64_t N, int P,
+                                                          float qscale, int nchunks, const float* stat_m,
+                                                          const float* stat_l, float* scores) {
+  __shared__ float gm[kDropMaxProbes], ginv[kDropMaxProbes];
+  const int chunk = blockIdx.x, bh = blockIdx.y, hk = bh % Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, kb = lane >> 4;
+  if (tid < P) {
+    float mm = -INFINITY, ll = 0.f;
+    for (int c = 0; c < nchunks; ++c) {
+      float om = stat_m[(static_cast<int64_t>(bh) * nchunks + c) * P + tid];
+      float ol = stat_l[(static_cast<int64_t>(bh) * nchunks + c) * P + tid];
+      float mn = fmaxf(mm, om);
+      if (mn != -INFINITY) {
+        ll = ll * exp2f(mm - mn) + ol * exp2f(om - mn);
+        mm = mn;
+      }
+    }
+    gm[tid] = mm;
+    ginv[tid] = 1.f / ll;
+  }
+  __syncthreads();
+  bf16x8_t pf[4][D / 32];
+  load_probes<D>(probes, hk, P, l16, kb, pf);
+  float pm[4], pinv[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    int p = ct * 16 + l16;
+    pm[ct] = p < P ? gm[p] : 0.f;
+    pinv[ct] = p < P ? ginv[p] : 0.f;
+  }
+  const T* krows = k + static_cast<int64_t>(bh) * N * D;
+  const int64_t c0 = static_cast<int64_t>(chunk) * kDropChunk;
+  const int64_t c1 = min(N, c0 + kDropChunk);
+  for (int64_t t0 = c0 + wave * 16; t0 < c1; t0 += 64) {
+    f32x4_t s[4];
+    tile_scores<D, T>(krows, t0, N, l16, kb, pf, s);
+    float acc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) x += exp2f(s[ct][r] * qscale - pm[ct]) * pinv[ct];
+      acc[r] = x;
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] += __shfl_xor(acc[r], o);
+    if (l16 == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int64_t tok = t0 + 4 * kb + r;
+        if (tok < c1) scores[static_cast<int64_t>(bh) * N + tok] = acc[r];
+      }
+    }
+  }
+}
+
+// ---- top-k selection: one block per (sequence, kv-head)
+constexpr int kSelThreads = 1024;
+
+__global__ void __launch_bounds__(kSelThreads) drop_select_kernel(const float* scores, int64_t N, int64_t n_keep,
+                                                                  int32_t* kept, int64_t kept_pitch) {
+  __shared__ unsigned hist[256];
+  __shared__ uint32_t s_prefix;
+  __shared__ int64_t s_remain;
+  __shared__ int64_t s_need_eq;
+  __shared__ int64_t s_base;
+  __shared__ int64_t s_eqbase;
+  __shared__ unsigned wsum[kSelThreads / 64][2];
+  const int bh = blockIdx.x;
+  const float* sc = scores + static_cast<int64_t>(bh) * N;
+  int32_t* out = kept + static_cast<int64_t>(bh) * kept_pitch;
+  const int tid = threadIdx.x;
+
+  if (tid == 0) { s_prefix = 0; s_remain = n_keep; }
+  __syncthreads();
+  // radix select of the n_keep-th largest key, most significant digit first
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+    const uint32_t prefix = s_prefix;
+    const uint32_t pmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    for (int64_t n = tid; n < N; n += kSelThreads) {
+      uint32_t key = __float_as_uint(sc[n]);
+      if ((key & pmask) == (prefix & pmask)) atomicAdd(&hist[(key >> shift) & 0xFF], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int64_t rem = s_remain;
+      int bin = 255;
+      for (; bin > 0; --bin) {
+        if (static_cast<int64_t>(hist[bin]) >= rem) break;
+        rem -= hist[bin];
+      }
+      s_prefix = prefix | (static_cast<uint32_t>(bin) << shift);
+      s_remain = rem;
+    }
+    __syncthreads();
+  }
+  const uint32_t thr = s_prefix;  // key of the n_keep-th largest score
+  if (tid == 0) { s_need_eq = s_remain; s_base = 0; s_eqbase = 0; }
+  __syncthreads();
+  const int64_t need_eq = s_need_eq;
+  // compaction in position order
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int64_t n0 = 0; n0 < N; n0 += kSelThreads) {
+    int64_t n = n0 + tid;
+    uint32_t key = n < N ? __float_as_uint(sc[n]) : 0u;
+    bool gt = n < N && key > thr;
+    bool eq = n < N && key == thr;
+    unsigned long long bgt = __ballot(gt), beq = __ballot(eq);
+    unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    unsigned gt_before = __popcll(bgt & below), eq_before = __popcll(beq & below);
+    if (lane == 0) { wsum[wave][0] = __popcll(bgt); wsum[wave][1] = __popcll(beq); }
+    __syncthreads();
+    unsigned wgt = 0, weq = 0, tgt = 0, teq = 0;
+    for (int w = 0; w < kSelThreads / 64; ++w) {
+      if (w < wave) { wgt += wsum[w][0]; weq += wsum[w][1]; }
+      tgt += wsum[w][0];
+      teq += wsum[w][1];
+    }
+    int64_t eq_rank = s_eqbase + weq + eq_before;
+    bool take_eq = eq && eq_rank < need_eq;
+    // positions taken before this thread: all gt before + equal ones before (capped)
+    int64_t eq_taken_before = min<int64_t>(eq_rank, need_eq);
+    int64_t slot = s_base + wgt + gt_before + (eq_taken_before - min<int64_t>(s_eqbase, need_eq));
+    if ((gt || take_eq) && slot < n_keep) out[slot] = static_cast<int32_t>(n);
+    __syncthreads();
+    if (tid == 0) {
+      int64_t eq_taken = min<int64_t>(s_eqbase + teq, need_eq) - min<int64_t>(s_eqbase, need_eq);
+      s_base += tgt + eq_taken;
+      s_eqbase += teq;
+    }
+    __syncthreads();
+  }
+}
+
+template <int VEC>
+__global__ void __launch_bounds__(256) gather_rows_kernel(const uint4* src, int64_t src_rows, int row_vecs,
+                                                          const int32_t* idx, int64_t n, int64_t idx_pitch,
+                                                          uint4* dst, int64_t dst_rows) {
+  const int bh = blockIdx.y;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= n * row_vecs) return;
+  const int64_t j = e / row_vecs;
+  const int c = static_cast<int>(e % row_vecs);
+  const int64_t s = idx[static_cast<int64_t>(bh) * idx_pitch + j];
+  if (s < 0 || s >= src_rows) return;  // out-of-range index: row left untouched
+  dst[(static_cast<int64_t>(bh) * dst_rows + j) * row_vecs + c] = src[(static_cast<int64_t>(bh) * src_rows + s) * row_vecs + c];
+}
+
+static int drop_chunks(int64_t N) { return static_cast<int>(cdiv(N, kDropChunk)); }
+
+static size_t scores_ws_bytes(int32_t B, int32_t Hkv, int64_t N, int32_t P) {
+  size_t n = static_cast<size_t>(B) * Hkv * drop_chunks(N) * P;
+  return 2 * align_up(n * sizeof(float), 256);
+}
+
+vc_status drop_scores_impl(const void* k, int32_t kv_dtype, const void* probes, int32_t B, int32_t Hkv, int64_t N,
+                           int32_t d, int32_t P, float sm_scale, float* scores, void* ws, size_t ws_bytes,
+                           hipStream_t s) {
+  VC_REQUIRE(k && probes && scores, "k / probes / scores is NULL");
+  VC_REQUIRE(valid_dtype(kv_dtype), "bad kv_dtype");
+  VC_REQUIRE(B > 0 && Hkv > 0 && N > 0, "bad shape");
+  VC_REQUIRE(P >= 1 && P <= kDropMaxProbes, "n_probes must be in [1, %d] (got %d)", kDropMaxProbes, P);
+  VC_REQUIRE(sm_scale > 0.f && sm_scale < INFINITY, "sm_scale must be positive and finite");
+  VC_UNSUPPORTED(d == 64 || d == 128, "token-drop scoring supports d = 64 or 128 (got %d)", d);
+  size_t need = scores_ws_bytes(B, Hkv, N, P);
+  if (!ws || ws_bytes < need) {
+    set_error("drop-score workspace needs %zu bytes (got %zu)", need, ws_bytes);
+    return VC_ERR_WORKSPACE;
+  }
+  int nch = drop_chunks(N);
+  size_t n = static_cast<size_t>(B) * Hkv * nch * P;
+  float* sm = static_cast<float*>(ws);
+  float* sl = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(n * sizeof(float), 256));
+  dim3 grid(nch, static_cast<unsigned>(B * Hkv));
+  float qs = sm_scale * kLog2e;
+  const bf16_t* pr = static_cast<const bf16_t*>(probes);
+#define VC_DS(D_, T_)                                                                                               \
+  do {                                                                                                              \
+    hipLaunchKernelGGL((drop_stats_kernel<D_, T_>), grid, dim3(256), 0, s, static_cast<const T_*>(k), pr, Hkv, N, P, \
+                       qs, nch, sm, sl);                                                                            \
+    hipLaunchKernelGGL((drop_scores_kernel<D_, T_>), grid, dim3(256), 0, s, static_cast<const T_*>(k), pr, Hkv, N,  \
+                       P, qs, nch, sm, sl, scores);                                                                 \
+  } while (0)
+  if (kv_dtype == VC_BF16) {
+    if (d == 128) VC_DS(128, bf16_t); else VC_DS(64, bf16_t);
+  } else {
+    if (d == 128) VC_DS(128, float); else VC_DS(64, float);
+  }
+#undef VC_DS
+  VC_LAUNCHED("drop_scores_kernel");
+  return VC_OK;
+}
+
+vc_status drop_select_impl(const float* scores, int32_t B, int32_t Hkv, int64_t N, int64_t n_keep, int32_t* kept,
+                           int64_t kept_pitch, hipStream_t s) {
+  VC_REQUIRE(scores && kept, "scores / kept_idx is NULL");
+  VC_REQUIRE(B > 0 && Hkv > 0 && N > 0, "bad shape");
+  VC_REQUIRE(n_keep >= 1 && n_keep <= N, "n_keep must be in [1, N] (got %lld, N %lld)", (long long)n_keep,
+             (long long)N);
+  VC_REQUIRE(N <= 0x7fffffffLL, "N too large for int32 indices");
+  hipLaunchKernelGGL(drop_select_kernel, dim3(static_cast<unsigned>(B * Hkv)), dim3(kSelThreads), 0, s, scores, N,
+                     n_keep, kept, kept_pitch);
+  VC_LAUNCHED("drop_select_kernel");
+  return VC_OK;
+}
+
+vc_status gather_impl(const void* src, int32_t kv_dtype, int32_t B, int32_t Hkv, int64_t src_rows, int32_t d,
+                      const int32_t* idx, int64_t n, int64_t idx_pitch, void* dst, int64_t dst_rows, hipStream_t s) {
+  VC_REQUIRE(src && idx && dst, "NULL pointer argument");
+  VC_REQUIRE(valid_dtype(kv_dtype), "bad kv_dtype");
+  VC_REQUIRE(B > 0 && Hkv > 0 && d > 0 && n >= 0 && n <= dst_rows, "bad shape");
+  size_t row_bytes = static_cast<size_t>(d) * dtype_bytes(kv_dtype);
+  VC_UNSUPPORTED(row_bytes % 16 == 0, "row size must be a multiple of 16 bytes");
+  if (n == 0) return VC_OK;
+  int rv = static_cast<int>(row_bytes / 16);
+  dim3 grid(static_cast<unsigned>(cdiv(n * rv, 256)), static_cast<unsigned>(B * Hkv));
+  hipLaunchKernelGGL(gather_rows_kernel<1>, grid, dim3(256), 0, s, static_cast<const uint4*>(src), src_rows, rv, idx, n,
+                     idx_pitch, static_cast<uint4*>(dst), dst_rows);
+  VC_LAUNCHED("gather_rows_kernel");
+  return VC_OK;
+}
+
+}  // namespace vc
+
+using namespace vc;
+
+extern "C" int64_t vc_drop_keep_count(float keep_ratio, int64_t N) {
+  if (N <= 0 || !(keep_ratio > 0.f)) return 0;
+  double x = static_cast<double>(keep_ratio) * static_cast<double>(N);
+  int64_t n = static_cast<int64_t>(ceil(x - 1e-9));
+  if (n < 1) n = 1;
+  if (n > N) n = N;
+  return n;
+}
+
+extern "C" size_t vc_drop_scores_workspace_bytes(int32_t B, int32_t Hkv, int64_t N, int32_t n_probes) {
+  if (B <= 0 || Hkv <= 0 || N <= 0 || n_probes <= 0) return 0;
+  return scores_ws_bytes(B, Hkv, N, n_probes);
+}
+
+extern "C" vc_status vc_drop_scores(const void* k, int32_t kv_dtype, const void* probes, int32_t B, int32_t Hkv,
+                                    int64_t N, int32_t d, int32_t n_probes, float sm_scale, float* scores, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  clear_error();
+  return drop_scores_impl(k, kv_dtype, probes, B, Hkv, N, d, n_probes, sm_scale, scores, ws, ws_bytes,
+                          as_stream(stream));
+}
+
+extern "C" size_t vc_drop_select_workspace_bytes(int32_t, int32_t, int64_t) { return 0; }
+
+extern "C" vc_status vc_drop_select(const float* scores, int32_t B, int32_t Hkv, int64_t N, int64_t n_keep,
+                                    int32_t* kept_idx, void*, size_t, void* stream) {
+  clear_error();
+  return drop_select_impl(scores, B, Hkv, N, n_keep, kept_idx, n_keep, as_stream(stream));
+}
+
+extern "C" vc_status vc_gather_rows(const void* src, int32_t kv_dtype, int32_t B, int32_t Hkv, int64_t src_rows,
+                                    int32_t d, const int32_t* idx, int64_t n, void* dst, int64_t dst_rows,
+                                    void* stream) {
+  clear_error();
+  return gather_impl(src, kv_dtype, B, Hkv, src_rows, d, idx, n, n, dst, dst_rows, as_stream(stream));
+}

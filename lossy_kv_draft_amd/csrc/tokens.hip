@@ -1,0 +1,283 @@
+// Greedy tokens and prefix acceptance.
+//
+// Summary page "VeriCache: Turning Lossy KV Cache into Lossless LLM Inference",
+// "What the paper found": greedy-decoding output identical to full-KV inference;
+// episode page "VeriCache: Lossless LLM Inference from Lossy KV Caches", source 2
+// (speculative decoding): the longest prefix on which draft and target agree is
+// accepted and the target's token at the first disagreement is committed.
+//
+// vc_head_mean: mean over q-heads of an attention output row (float32).
+// vc_logits_argmax: tokens = argmax_v (u . W_v), ties to the lowest v.
+//   bf16 W (matrix cores): u is float32, split exactly into u_hi + u_lo with both
+//   parts bf16, and W (u_hi + u_lo) is accumulated in float32 on
+//   v_mfma_f32_16x16x32_bf16 (each product is exact; u keeps ~16 significant bits).
+//   A workgroup owns 128 vocabulary rows (32 per wave, held as A operands in
+//   registers) and sweeps every input row in 16-row tiles, so W is read from HBM
+//   once; per tile it reduces (max, lowest index) over its 128 rows and writes one
+//   partial per (row, block); a second kernel reduces the blocks in order.
+//   float32 W or other shapes: one workgroup per row, float32 dot products.
+// vc_accept: one thread per sequence.
+
+#include "common.h"
+
+namespace vc {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__global__ void head_mean_kernel(const T* o, int B, int Hq, int k, int d, int64_t sb, int64_t sh, int64_t si,
+                                 float* u) {
+  int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= static_cast<int64_t>(B) * k * d) return;
+  int c = static_cast<int>(e % d);
+  int64_t r = e / d;
+  int b = static_cast<int>(r / k), i = static_cast<int>(r % k);
+  float s = 0.f;
+  for (int h = 0; h < Hq; ++h) s += Elem<T>::load(o, b * sb + h * sh + i * si + c);
+  u[e] = s / static_cast<float>(Hq);
+}
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+// ---- float32 / generic path: one block per row
+template <typename TU, typename TW>
+__global__ void __launch_bounds__(256) argmax_rowwise_kernel(const TU* u, const TW* W, int K, int V, int32_t* tok) {
+  __shared__ float su[1024];
+  __shared__ float bv_s[4];
+  __shared__ int bi_s[4];
+  const int64_t r = blockIdx.x;
+  for (int c = threadIdx.x; c < K; c += 256) su[c] = Elem<TU>::load(u, r * K + c);
+  __syncthreads();
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int v = threadIdx.x; v < V; v += 256) {
+    float x = 0.f;
+    for (int c = 0; c < K; ++c) x = fmaf(su[c], Elem<TW>::load(W, static_cast<int64_t>(v) * K + c), x);
+    if (better(x, v, bv, bi)) { bv = x; bi = v; }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    float ov = __shfl_xor(bv, o);
+    int oi = __shfl_xor(bi, o);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  if ((threadIdx.x & 63) == 0) { bv_s[threadIdx.x >> 6] = bv; bi_s[threadIdx.x >> 6] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (better(bv_s[w], bi_s[w], bv, bi)) { bv = bv_s[w]; bi = bi_s[w]; }
+    // NaN-free inputs always find an index; keep 0 otherwise
+    tok[r] = bi == 0x7fffffff ? 0 : bi;
+  }
+}
+
+// ---- bf16 W on matrix cores
+constexpr int kLgVBlock = 128;
+
+template <int KD, typename TU>
+__global__ void __launch_bounds__(256) argmax_mfma_kernel(const TU* u, const bf16_t* W, int64_t R, int V,
+                                                          float* part_v, int* part_i, int nvb) {
+  constexpr int KS = KD / 32;
+  __shared__ float wv[4][16];
+  __shared__ int wi[4][16];
+  const int vb = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, kb = lane >> 4;
+  const int v0 = vb * kLgVBlock + wave * 32;
+  union P16 { uint4 u; bf16x8_t v; };
+  bf16x8_t wa[2][KS];
+#pragma unroll
+  for (int vt = 0; vt < 2; ++vt) {
+    int v = v0 + vt * 16 + l16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      P16 p;
+      p.u = make_uint4(0, 0, 0, 0);
+      if (v < V) p.u = *reinterpret_cast<const uint4*>(W + static_cast<int64_t>(v) * KD + 32 * ks + 8 * kb);
+      wa[vt][ks] = p.v;
+    }
+  }
+  for (int64_t r0 = 0; r0 < R; r0 += 16) {
+    const int64_t r = r0 + l16;
+    f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8_t hi, lo;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float x = r < R ? Elem<TU>::load(u, r * KD + 32 * ks + 8 * kb + j) : 0.f;
+        __bf16 h = static_cast<__bf16>(x);
+        hi[j] = h;
+        lo[j] = static_cast<__bf16>(x - static_cast<float>(h));
+      }
+#pragma unroll
+      for (int vt = 0; vt < 2; ++vt) {
+        acc[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[vt][ks], hi, acc[vt], 0, 0, 0);
+        acc[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[vt][ks], lo, acc[vt], 0, 0, 0);
+      }
+    }
+    // acc[vt][i] = logit(vocab v0 + 16 vt + 4 kb + i, row r)
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int v = v0 + vt * 16 + 4 * kb + i;
+        if (v < V && better(acc[vt][i], v, bv, bi)) { bv = acc[vt][i]; bi = v; }
+      }
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      float ov = __shfl_xor(bv, o);
+      int oi = __shfl_xor(bi, o);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    if (kb == 0) { wv[wave][l16] = bv; wi[wave][l16] = bi; }
+    __syncthreads();
+    if (tid < 16 && r0 + tid < R) {
+      float b2 = wv[0][tid];
+      int i2 = wi[0][tid];
+      for (int w = 1; w < 4; ++w)
+        if (better(wv[w][tid], wi[w][tid], b2, i2)) { b2 = wv[w][tid]; i2 = wi[w][tid]; }
+      part_v[(r0 + tid) * nvb + vb] = b2;
+      part_i[(r0 + tid) * nvb + vb] = i2;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void __launch_bounds__(256) argmax_reduce_kernel(const float* part_v, const int* part_i, int nvb,
+                                                            int32_t* tok) {
+  const int64_t r = blockIdx.x;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int j = threadIdx.x; j < nvb; j += 256) {
+    float v = part_v[r * nvb + j];
+    int i = part_i[r * nvb + j];
+    if (better(v, i, bv, bi)) { bv = v; bi = i; }
+  }
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  for (int o = 32; o > 0; o >>= 1) {
+    float ov = __shfl_xor(bv, o);
+    int oi = __shfl_xor(bi, o);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = bv; si[threadIdx.x >> 6] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (better(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
+    tok[r] = bi == 0x7fffffff ? 0 : bi;
+  }
+}
+
+__global__ void accept_kernel(const int32_t* draft, const int32_t* target, int B, int k, int32_t* acc,
+                              int32_t* nc, int32_t* commit) {
+  int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int32_t* d = draft + static_cast<int64_t>(b) * k;
+  const int32_t* t = target + static_cast<int64_t>(b) * k;
+  int32_t* c = commit + static_cast<int64_t>(b) * k;
+  int a = 0;
+  while (a < k && d[a] == t[a]) {
+    c[a] = d[a];
+    ++a;
+  }
+  int n = a;
+  if (a < k) c[n++] = t[a];
+  for (int j = n; j < k; ++j) c[j] = -1;
+  acc[b] = a;
+  nc[b] = n;
+}
+
+static bool use_mfma_argmax(int32_t w_dtype, int32_t K) { return w_dtype == VC_BF16 && (K == 64 || K == 128); }
+
+}  // namespace vc
+
+using namespace vc;
+
+extern "C" vc_status vc_head_mean(const void* o, int32_t kv_dtype, int32_t B, int32_t Hq, int32_t k, int32_t d,
+                                  int64_t stride_b, int64_t stride_h, int64_t stride_i, float* u, void* stream) {
+  clear_error();
+  VC_REQUIRE(o && u, "o / u is NULL");
+  VC_REQUIRE(valid_dtype(kv_dtype), "bad kv_dtype");
+  VC_REQUIRE(B > 0 && Hq > 0 && k > 0 && d > 0, "bad shape");
+  int64_t n = static_cast<int64_t>(B) * k * d;
+  dim3 grid(static_cast<unsigned>(cdiv(n, 256)));
+  if (kv_dtype == VC_F32)
+    hipLaunchKernelGGL(head_mean_kernel<float>, grid, dim3(256), 0, as_stream(stream), static_cast<const float*>(o),
+                       B, Hq, k, d, stride_b, stride_h, stride_i, u);
+  else
+    hipLaunchKernelGGL(head_mean_kernel<bf16_t>, grid, dim3(256), 0, as_stream(stream),
+                       static_cast<const bf16_t*>(o), B, Hq, k, d, stride_b, stride_h, stride_i, u);
+  VC_LAUNCHED("head_mean_kernel");
+  return VC_OK;
+}
+
+extern "C" size_t vc_logits_workspace_bytes(int64_t R, int32_t V) {
+  if (R <= 0 || V <= 0) return 0;
+  size_t nvb = static_cast<size_t>(cdiv(V, kLgVBlock));
+  return align_up(R * nvb * sizeof(float), 256) + align_up(R * nvb * sizeof(int), 256);
+}
+
+extern "C" vc_status vc_logits_argmax(const void* u, int32_t u_dtype, int64_t R, int32_t K, const void* W,
+                                      int32_t w_dtype, int32_t V, int32_t* tokens, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  clear_error();
+  VC_REQUIRE(u && W && tokens, "u / W / tokens is NULL");
+  VC_REQUIRE(valid_dtype(u_dtype) && valid_dtype(w_dtype), "bad dtype");
+  VC_REQUIRE(R > 0 && K > 0 && V > 0, "bad shape (R %lld, K %d, V %d)", (long long)R, K, V);
+  hipStream_t s = as_stream(stream);
+  if (use_mfma_argmax(w_dtype, K)) {
+    size_t need = vc_logits_workspace_bytes(R, V);
+    if (!ws || ws_bytes < need) {
+      set_error("logits workspace needs %zu bytes (got %zu)", need, ws_bytes);
+      return VC_ERR_WORKSPACE;
+    }
+    int nvb = static_cast<int>(cdiv(V, kLgVBlock));
+    float* pv = static_cast<float*>(ws);
+    int* pi = reinterpret_cast<int*>(static_cast<char*>(ws) + align_up(R * nvb * sizeof(float), 256));
+    const bf16_t* w = static_cast<const bf16_t*>(W);
+    if (K == 128) {
+      if (u_dtype == VC_F32)
+        hipLaunchKernelGGL((argmax_mfma_kernel<128, float>), dim3(nvb), dim3(256), 0, s, static_cast<const float*>(u), w, R, V, pv, pi, nvb);
+      else
+        hipLaunchKernelGGL((argmax_mfma_kernel<128, bf16_t>), dim3(nvb), dim3(256), 0, s, static_cast<const bf16_t*>(u), w, R, V, pv, pi, nvb);
+    } else {
+      if (u_dtype == VC_F32)
+        hipLaunchKernelGGL((argmax_mfma_kernel<64, float>), dim3(nvb), dim3(256), 0, s, static_cast<const float*>(u), w, R, V, pv, pi, nvb);
+      else
+        hipLaunchKernelGGL((argmax_mfma_kernel<64, bf16_t>), dim3(nvb), dim3(256), 0, s, static_cast<const bf16_t*>(u), w, R, V, pv, pi, nvb);
+    }
+    VC_LAUNCHED("argmax_mfma_kernel");
+    hipLaunchKernelGGL(argmax_reduce_kernel, dim3(static_cast<unsigned>(R)), dim3(256), 0, s, pv, pi, nvb, tokens);
+    VC_LAUNCHED("argmax_reduce_kernel");
+    return VC_OK;
+  }
+  VC_UNSUPPORTED(K <= 1024, "K must be at most 1024 on the float32 path (got %d)", K);
+  dim3 grid(static_cast<unsigned>(R));
+#define VC_AM(TU, TW) \
+  hipLaunchKernelGGL((argmax_rowwise_kernel<TU, TW>), grid, dim3(256), 0, s, static_cast<const TU*>(u), static_cast<const TW*>(W), K, V, tokens)
+  if (u_dtype == VC_F32 && w_dtype == VC_F32) VC_AM(float, float);
+  else if (u_dtype == VC_F32) VC_AM(float, bf16_t);
+  else if (w_dtype == VC_F32) VC_AM(bf16_t, float);
+  else VC_AM(bf16_t, bf16_t);
+#undef VC_AM
+  VC_LAUNCHED("argmax_rowwise_kernel");
+  return VC_OK;
+}
+
+extern "C" vc_status vc_accept(const int32_t* draft, const int32_t* target, int32_t B, int32_t k, int32_t* accept_len,
+                               int32_t* n_commit, int32_t* commit, void* stream) {
+  clear_error();
+  VC_REQUIRE(draft && target && accept_len && n_commit && commit, "NULL pointer argument");
+  VC_REQUIRE(B > 0, "B must be positive");
+  VC_REQUIRE(k >= 1 && k <= 1024, "k must be in [1, 1024] (got %d)", k);
+  hipLaunchKernelGGL(accept_kernel, dim3(static_cast<unsigned>(cdiv(B, 64))), dim3(64), 0, as_stream(stream), draft,
+                     target, B, k, accept_len, n_commit, commit);
+  VC_LAUNCHED("accept_kernel");
+  return VC_OK;
+}

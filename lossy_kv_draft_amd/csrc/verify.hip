@@ -1,0 +1,440 @@
+// Verification: causal attention of the k-row draft window over the full KV cache.
+//
+// Summary page "VeriCache: Turning Lossy KV Cache into Lossless LLM Inference",
+// "What the paper found" and "Original abstract": drafted tokens are verified
+// against the full KV cache so that the output equals full-KV greedy decoding.
+// Row i of a sequence with context length L attends to cache rows [0, L + i] (the
+// window's own keys/values are already written at rows [L, L + k)).
+//
+// bf16 path (matrix cores, v_mfma_f32_16x16x32_bf16, float32 accumulation):
+//   grid = (splits, row blocks, B*Hkv).  The rows of all Hq/Hkv q-heads that read
+//   one kv-head are stacked (M = (Hq/Hkv) * k rows) so every K/V tile is read from
+//   HBM once per row block.  Each of the 4 waves owns 16*RT rows.  Per 64-token
+//   tile: K is staged in LDS as [token][d] and V transposed as [d][token]; the
+//   wave computes S^T = K Q^T (tokens x rows), masks positions beyond each row's
+//   limit, runs an online softmax per row (base 2), rounds P to bf16 and
+//   accumulates O^T += V^T P^T.  The probabilities stay in the lanes that produced
+//   them: the S^T output layout of a pair of 16-token tiles is exactly the
+//   B-operand layout of the P.V product once the 32 token indices of that product
+//   are enumerated in the same (permuted) order on both operands.
+//   The global loads of the next tile are issued before the current tile is
+//   computed (register prefetch).
+//
+// float32 path: one wave per (row, split), lanes over d, float32 throughout.
+//
+// Splits are cut at absolute cache positions (multiples of split_tokens); every row
+// is reduced over the same tiles in the same order whatever k, its window position
+// or the neighbouring rows are (tiles and splits past a row's limit contribute
+// exact zeros), and the merge kernel combines splits in split order.  So row i of a
+// k-row call equals bit for bit the 1-row call with context L + i.  All sources in
+// this file are compiled without floating-point contraction so that every
+// instantiation performs the same roundings.
+
+#include "common.h"
+
+namespace vc {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kVerThreads = 256;
+constexpr int kVerTile = 64;
+
+struct VerifyArgs {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  int Hq, Hkv, H, d, k;
+  int64_t cache_rows, ctx_len;
+  const int32_t* ctx_lens;
+  int64_t C;      // split size in positions
+  int splits;
+  int rows_per_block;
+  float qscale;   // sm_scale * log2(e)
+  float* part_o;  // [B*Hkv][splits][M][d]
+  float* part_ml; // [B*Hkv][splits][M][2]
+};
+
+union Pack16 {
+  uint4 u;
+  bf16x8_t v;
+  bf16_t h[8];
+};
+
+template <int D, int RT>
+__global__ void __launch_bounds__(kVerThreads) verify_mfma_kernel(VerifyArgs a) {
+  constexpr int KP = D + 8;          // K tile row pitch (bf16 elements)
+  constexpr int VP = kVerTile + 8;   // V^T row pitch
+  constexpr int KS = D / 32;         // k-steps of the score product
+  constexpr int DT = D / 16;         // 16-channel tiles of the output
+  constexpr int KCH = kVerTile * D / 8 / kVerThreads;   // 16-byte K chunks per thread
+  constexpr int VCH = kVerTile * D / 16 / kVerThreads;  // (2 tokens x 8 channels) V items per thread
+  __shared__ __attribute__((aligned(16))) bf16_t k_lds[kVerTile * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t vt_lds[D * VP];
+
+  const int split = blockIdx.x, rblk = blockIdx.y, bh = blockIdx.z;
+  const int b = bh / a.Hkv, hk = bh % a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, kb = lane >> 4;
+  const int M = a.H * a.k;
+  const int row0 = rblk * a.rows_per_block + wave * 16 * RT;
+  const int64_t L = a.ctx_lens ? a.ctx_lens[b] : a.ctx_len;
+  const int64_t limit = L + a.k;  // readable positions [0, limit)
+  const int64_t s_begin = static_cast<int64_t>(split) * a.C;
+  const int64_t s_end = min(s_begin + a.C, limit);
+
+  const bf16_t* q = static_cast<const bf16_t*>(a.q) + (static_cast<int64_t>(b) * a.Hq + hk * a.H) * a.k * D;
+  const bf16_t* kc = static_cast<const bf16_t*>(a.kc) + static_cast<int64_t>(bh) * a.cache_rows * D;
+  const bf16_t* vc = static_cast<const bf16_t*>(a.vc) + static_cast<int64_t>(bh) * a.cache_rows * D;
+
+  bf16x8_t qf[RT][KS];
+  int64_t rlim[RT];  // last position row may see (inclusive); -1 for padding rows
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    int row = row0 + rt * 16 + l16;
+    rlim[rt] = row < M ? L + (row % a.k) : -1;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      Pack16 p;
+      p.u = make_uint4(0, 0, 0, 0);
+      if (row < M) p.u = *reinterpret_cast<const uint4*>(q + static_cast<int64_t>(row) * D + 32 * ks + 8 * kb);
+      qf[rt][ks] = p.v;
+    }
+  }
+
+  f32x4_t o[DT][RT];
+  float m[RT], lsum[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m[rt] = -INFINITY;
+    lsum[rt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  uint4 kreg[KCH];
+  uint4 vreg[VCH][2];
+  auto gload = [&](int64_t t0) {
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      int id = tid + j * kVerThreads;
+      int t = id / (D / 8), c8 = id % (D / 8);
+      int64_t pos = t0 + t;
+      kreg[j] = pos < limit ? *reinterpret_cast<const uint4*>(kc + pos * D + c8 * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < VCH; ++j) {
+      int id = tid + j * kVerThreads;
+      int tp = id / (D / 8), c8 = id % (D / 8);
+      int64_t pos = t0 + 2 * tp;
+      vreg[j][0] = pos < limit ? *reinterpret_cast<const uint4*>(vc + pos * D + c8 * 8) : make_uint4(0, 0, 0, 0);
+      vreg[j][1] = pos + 1 < limit ? *reinterpret_cast<const uint4*>(vc + (pos + 1) * D + c8 * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      int id = tid + j * kVerThreads;
+      int t = id / (D / 8), c8 = id % (D / 8);
+      *reinterpret_cast<uint4*>(k_lds + t * KP + c8 * 8) = kreg[j];
+    }
+#pragma unroll
+    for (int j = 0; j < VCH; ++j) {
+      int id = tid + j * kVerThreads;
+      int tp = id / (D / 8), c8 = id % (D / 8);
+      Pack16 x0, x1;
+      x0.u = vreg[j][0];
+      x1.u = vreg[j][1];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t w = static_cast<uint32_t>(x0.h[e]) | (static_cast<uint32_t>(x1.h[e]) << 16);
+        *reinterpret_cast<uint32_t*>(vt_lds + (c8 * 8 + e) * VP + 2 * tp) = w;
+      }
+    }
+  };
+
+  if (s_begin < s_end) gload(s_begin);
+  for (int64_t t0 = s_begin; t0 < s_end; t0 += kVerTile) {
+    __syncthreads();
+    lstore();
+    __syncthreads();
+    if (t0 + kVerTile < s_end) gload(t0 + kVerTile);
+    if (row0 >= M) continue;  // padding wave: only helps staging
+
+    // ---- S^T = K Q^T : s[tt][rt][r] = score(token t0 + 16 tt + 4 kb + r, row row0 + 16 rt + l16)
+    f32x4_t s[4][RT];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) s[tt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        Pack16 ka;
+        ka.u = *reinterpret_cast<const uint4*>(k_lds + (tt * 16 + l16) * KP + 32 * ks + 8 * kb);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          s[tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.v, qf[rt][ks], s[tt][rt], 0, 0, 0);
+      }
+    }
+
+    // ---- online softmax per row; P^T operand built in place
+    bf16x8_t pb[RT][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int64_t pos = t0 + tt * 16 + 4 * kb + r;
+          float v = pos <= rlim[rt] ? s[tt][rt][r] * a.qscale : -INFINITY;
+          s[tt][rt][r] = v;
+          mt = fmaxf(mt, v);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      float mnew = fmaxf(m[rt], mt);
+      float alpha = mnew == -INFINITY ? 1.f : exp2f(m[rt] - mnew);
+      m[rt] = mnew;
+      lsum[rt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
+      Pack16 p0, p1;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float p = mnew == -INFINITY ? 0.f : exp2f(s[tt][rt][r] - mnew);
+          __bf16 pbv = static_cast<__bf16>(p);
+          lsum[rt] += static_cast<float>(pbv);
+          Pack16& dst = (tt < 2) ? p0 : p1;
+          dst.v[(tt & 1) * 4 + r] = pbv;
+        }
+      pb[rt][0] = p0.v;
+      pb[rt][1] = p1.v;
+    }
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16_t* vr = vt_lds + (dt * 16 + l16) * VP + 32 * ks2 + 4 * kb;
+        uint2 lo = *reinterpret_cast<const uint2*>(vr);
+        uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
+        Pack16 va;
+        va.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pb[rt][ks2], o[dt][rt], 0, 0, 0);
+      }
+    }
+  }
+
+  if (row0 >= M) return;
+  // ---- partials: o[dt][rt][r] = O^T[d = 16 dt + 4 kb + r][row = row0 + 16 rt + l16]
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float l = lsum[rt];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    int row = row0 + rt * 16 + l16;
+    if (row >= M) continue;
+    int64_t pr = (static_cast<int64_t>(bh) * a.splits + split) * M + row;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<f32x4_t*>(a.part_o + pr * D + dt * 16 + 4 * kb) = o[dt][rt];
+    if (kb == 0) {
+      a.part_ml[pr * 2] = m[rt];
+      a.part_ml[pr * 2 + 1] = l;
+    }
+  }
+}
+
+// float32 path: one 64-lane wave per (row, split); lanes cover d (d <= 256).
+template <typename T>
+__global__ void __launch_bounds__(256) verify_f32_kernel(VerifyArgs a) {
+  const int split = blockIdx.x, bh = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.y * 4 + wave;
+  const int b = bh / a.Hkv, hk = bh % a.Hkv;
+  const int M = a.H * a.k, d = a.d;
+  if (row >= M) return;
+  const int64_t L = a.ctx_lens ? a.ctx_lens[b] : a.ctx_len;
+  const int64_t last = L + (row % a.k);
+  const int64_t s_begin = static_cast<int64_t>(split) * a.C;
+  const int64_t s_end = min(s_begin + a.C, last + 1);
+  const T* q = static_cast<const T*>(a.q) + ((static_cast<int64_t>(b) * a.Hq + hk * a.H) * a.k + row) * d;
+  const T* kc = static_cast<const T*>(a.kc) + static_cast<int64_t>(bh) * a.cache_rows * d;
+  const T* vc = static_cast<const T*>(a.vc) + static_cast<int64_t>(bh) * a.cache_rows * d;
+  float qv[4], ov[4];
+  for (int j = 0; j < 4; ++j) {
+    int c = lane + 64 * j;
+    qv[j] = c < d ? Elem<T>::load(q, c) : 0.f;
+    ov[j] = 0.f;
+  }
+  float mrun = -INFINITY, lrun = 0.f;
+  for (int64_t pos = s_begin; pos < s_end; ++pos) {
+    float x = 0.f;
+    for (int j = 0; j < 4; ++j) {
+      int c = lane + 64 * j;
+      if (c < d) x = fmaf(qv[j], Elem<T>::load(kc, pos * d + c), x);
+    }
+    x = warp_sum(x) * a.qscale;
+    float mnew = fmaxf(mrun, x);
+    float al = exp2f(mrun - mnew);
+    float p = exp2f(x - mnew);
+    lrun = lrun * al + p;
+    mrun = mnew;
+    for (int j = 0; j < 4; ++j) {
+      int c = lane + 64 * j;
+      if (c < d) ov[j] = fmaf(p, Elem<T>::load(vc, pos * d + c), ov[j] * al);
+    }
+  }
+  int64_t pr = (static_cast<int64_t>(bh) * a.splits + split) * M + row;
+  for (int j = 0; j < 4; ++j) {
+    int c = lane + 64 * j;
+    if (c < d) a.part_o[pr * d + c] = ov[j];
+  }
+  if (lane == 0) {
+    a.part_ml[pr * 2] = mrun;
+    a.part_ml[pr * 2 + 1] = lrun;
+  }
+}
+
+// Merge of the split partials in split order; one thread per (row, channel).
+template <typename T>
+__global__ void __launch_bounds__(256) verify_merge_kernel(VerifyArgs a, void* out, float* lse) {
+  const int bh = blockIdx.y;
+  const int M = a.H * a.k, d = a.d;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= static_cast<int64_t>(M) * d) return;
+  const int row = static_cast<int>(e / d), c = static_cast<int>(e % d);
+  const int b = bh / a.Hkv, hk = bh % a.Hkv;
+  float Mx = -INFINITY;
+  for (int s = 0; s < a.splits; ++s)
+    Mx = fmaxf(Mx, a.part_ml[((static_cast<int64_t>(bh) * a.splits + s) * M + row) * 2]);
+  float Lsum = 0.f, O = 0.f;
+  for (int s = 0; s < a.splits; ++s) {
+    int64_t pr = (static_cast<int64_t>(bh) * a.splits + s) * M + row;
+    float mv = a.part_ml[pr * 2];
+    float w = mv == -INFINITY ? 0.f : exp2f(mv - Mx);
+    Lsum = fmaf(a.part_ml[pr * 2 + 1], w, Lsum);
+    O = fmaf(a.part_o[pr * d + c], w, O);
+  }
+  int64_t orow = (static_cast<int64_t>(b) * a.Hq + hk * a.H) * a.k + row;
+  Elem<T>::store(static_cast<T*>(out), orow * d + c, Lsum > 0.f ? O / Lsum : 0.f);
+  if (lse && c == 0) lse[orow] = Lsum > 0.f ? (Mx + log2f(Lsum)) * kLn2 : -INFINITY;
+}
+
+// Row tiling of the bf16 kernel: RT 16-row tiles per wave, 4 waves per block.
+static void verify_tiling(int M, int& RT, int& nblk) {
+  nblk = static_cast<int>(cdiv(M, 256));
+  int per = static_cast<int>(cdiv(M, nblk));
+  RT = static_cast<int>(cdiv(per, 64));
+  if (RT < 1) RT = 1;
+  if (RT > 4) RT = 4;
+  nblk = static_cast<int>(cdiv(M, 64 * RT));
+}
+
+}  // namespace vc
+
+using namespace vc;
+
+extern "C" int32_t vc_verify_split_tokens(int32_t B, int32_t Hkv) {
+  int64_t bh = static_cast<int64_t>(B > 0 ? B : 1) * (Hkv > 0 ? Hkv : 1);
+  int64_t c = 1024;
+  while (c < 64 * bh && c < 16384) c *= 2;
+  return static_cast<int32_t>(c);
+}
+
+extern "C" size_t vc_verify_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t k,
+                                            int64_t max_len, int32_t split_tokens) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || k <= 0 || max_len < 0) return 0;
+  int64_t C = split_tokens > 0 ? split_tokens : vc_verify_split_tokens(B, Hkv);
+  int64_t S = cdiv(max_len + k, C);
+  if (S < 1) S = 1;
+  size_t M = static_cast<size_t>(Hq / Hkv) * k;
+  size_t bh = static_cast<size_t>(B) * Hkv;
+  return align_up(bh * S * M * d * sizeof(float), 256) + align_up(bh * S * M * 2 * sizeof(float), 256);
+}
+
+extern "C" vc_status vc_verify_attn_full(const void* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                                         int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t k,
+                                         int64_t cache_rows, int64_t ctx_len, const int32_t* ctx_lens,
+                                         int32_t split_tokens, float sm_scale, void* out, float* lse, void* ws,
+                                         size_t ws_bytes, void* stream) {
+  clear_error();
+  VC_REQUIRE(q && k_cache && v_cache && out, "q / k_cache / v_cache / out is NULL");
+  VC_REQUIRE(valid_dtype(kv_dtype), "bad kv_dtype %d", kv_dtype);
+  VC_REQUIRE(B > 0 && Hkv > 0 && Hq > 0 && Hq % Hkv == 0, "bad B/Hq/Hkv (%d, %d, %d)", B, Hq, Hkv);
+  VC_REQUIRE(k >= 1 && k <= 1024, "k must be in [1, 1024] (got %d)", k);
+  VC_REQUIRE(d > 0, "bad d");
+  VC_REQUIRE(ctx_len >= 0 && ctx_len + k <= cache_rows, "ctx_len + k (%lld) exceeds cache_rows %lld",
+             (long long)(ctx_len + k), (long long)cache_rows);
+  VC_REQUIRE(sm_scale > 0.f && sm_scale < INFINITY, "sm_scale must be positive and finite");
+  VC_REQUIRE(split_tokens >= 0 && split_tokens % kVerTile == 0, "split_tokens must be a multiple of %d", kVerTile);
+  if (kv_dtype == VC_BF16)
+    VC_UNSUPPORTED(d == 64 || d == 128, "bf16 verify supports d = 64 or 128 (got %d)", d);
+  else
+    VC_UNSUPPORTED(d <= 256, "f32 verify supports d <= 256 (got %d)", d);
+  const int64_t C = split_tokens > 0 ? split_tokens : vc_verify_split_tokens(B, Hkv);
+  size_t need = vc_verify_workspace_bytes(B, Hq, Hkv, d, k, ctx_len, static_cast<int32_t>(C));
+  if (!ws || ws_bytes < need) {
+    set_error("verify workspace needs %zu bytes (got %zu)", need, ws_bytes);
+    return VC_ERR_WORKSPACE;
+  }
+  VerifyArgs a{};
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.H = Hq / Hkv;
+  a.d = d;
+  a.k = k;
+  a.cache_rows = cache_rows;
+  a.ctx_len = ctx_len;
+  a.ctx_lens = ctx_lens;
+  a.C = C;
+  a.splits = static_cast<int>(cdiv(ctx_len + k, C));
+  a.qscale = sm_scale * kLog2e;
+  const int M = a.H * k;
+  size_t bh = static_cast<size_t>(B) * Hkv;
+  a.part_o = static_cast<float*>(ws);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(bh * a.splits * M * d * sizeof(float), 256));
+  hipStream_t s = as_stream(stream);
+  if (kv_dtype == VC_BF16) {
+    int RT, nblk;
+    verify_tiling(M, RT, nblk);
+    a.rows_per_block = 64 * RT;
+    dim3 grid(a.splits, nblk, static_cast<unsigned>(bh));
+#define VC_VER_LAUNCH(D_, RT_) \
+  hipLaunchKernelGGL((verify_mfma_kernel<D_, RT_>), grid, dim3(kVerThreads), 0, s, a)
+    if (d == 128) {
+      if (RT == 1) VC_VER_LAUNCH(128, 1);
+      else if (RT == 2) VC_VER_LAUNCH(128, 2);
+      else if (RT == 3) VC_VER_LAUNCH(128, 3);
+      else VC_VER_LAUNCH(128, 4);
+    } else {
+      if (RT == 1) VC_VER_LAUNCH(64, 1);
+      else if (RT == 2) VC_VER_LAUNCH(64, 2);
+      else if (RT == 3) VC_VER_LAUNCH(64, 3);
+      else VC_VER_LAUNCH(64, 4);
+    }
+#undef VC_VER_LAUNCH
+    VC_LAUNCHED("verify_mfma_kernel");
+    dim3 mgrid(static_cast<unsigned>(cdiv(static_cast<int64_t>(M) * d, 256)), static_cast<unsigned>(bh));
+    hipLaunchKernelGGL(verify_merge_kernel<bf16_t>, mgrid, dim3(256), 0, s, a, out, lse);
+  } else {
+    dim3 grid(a.splits, static_cast<unsigned>(cdiv(M, 4)), static_cast<unsigned>(bh));
+    hipLaunchKernelGGL(verify_f32_kernel<float>, grid, dim3(256), 0, s, a);
+    VC_LAUNCHED("verify_f32_kernel");
+    dim3 mgrid(static_cast<unsigned>(cdiv(static_cast<int64_t>(M) * d, 256)), static_cast<unsigned>(bh));
+    hipLaunchKernelGGL(verify_merge_kernel<float>, mgrid, dim3(256), 0, s, a, out, lse);
+  }
+  VC_LAUNCHED("verify_merge_kernel");
+  return VC_OK;
+}

@@ -1,0 +1,105 @@
+"""The C-ABI library: it loads without a GPU, exports every entry point declared in
+include/vc.h, and rejects bad arguments on the host before anything is enqueued
+(these calls never reach a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import lossy_kv_draft_amd as L
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "vc.h")
+
+
+def declared():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(vc_\w+)\s*\(", text))
+
+
+def test_header_and_binding_agree():
+    assert declared() == set(L.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for name in declared():
+        assert hasattr(lib, name), name
+
+
+def test_keep_count_and_split_tokens():
+    assert L.vc_drop_keep_count(0.25, 131072) == 32768
+    assert L.vc_drop_keep_count(0.25, 10) == 3
+    assert L.vc_drop_keep_count(1.0, 7) == 7
+    for B, H in [(1, 2), (4, 4), (8, 8), (16, 4), (4, 8)]:
+        c = L.vc_verify_split_tokens(B, H)
+        assert c % 64 == 0 and 1024 <= c <= 16384
+
+
+def _ckv(**kw):
+    a = dict(k_bits=2, v_bits=2, group=32, param_dtype="f32", kv_dtype="f32", tail_cap=4, device="cpu")
+    a.update(kw)
+    return L.Ckv("quant", 1, 2, 64, 512, **a)
+
+
+def _bad(fn, *a, status=L._lib.VC_ERR_INVALID_ARG, **k):
+    with pytest.raises(L.VcError) as e:
+        fn(*a, **k)
+    assert e.value.status == status, str(e.value)
+    assert L.vc_last_error() != ""
+    return str(e.value)
+
+
+def test_decode_rejects_bad_arguments():
+    q = torch.zeros(1, 8, 64)
+    out = torch.zeros(1, 8, 64)
+    ws = torch.zeros(1 << 20, dtype=torch.uint8)
+    c = _ckv(k_bits=5)
+    assert "bits" in _bad(L.vc_decode_attn_compressed, c, q, out, ws=ws, stream=0)
+    c = _ckv()
+    c.n_main = 100  # not a multiple of the group
+    _bad(L.vc_decode_attn_compressed, c, q, out, ws=ws, stream=0)
+    c = _ckv()
+    c.n_main = 512
+    _bad(L.vc_decode_attn_compressed, c, torch.zeros(1, 7, 64), torch.zeros(1, 7, 64), ws=ws, stream=0)
+    _bad(L.vc_decode_attn_compressed, c, q, out, ws=torch.zeros(8, dtype=torch.uint8), stream=0,
+         status=L._lib.VC_ERR_WORKSPACE)
+    c.tail_len = 5  # beyond tail_cap
+    _bad(L.vc_decode_attn_compressed, c, q, out, ws=ws, stream=0)
+
+
+def test_compress_rejects_misaligned_rows():
+    c = _ckv()
+    k = torch.zeros(1, 2, 512, 64)
+    _bad(L.vc_compress, c, k, k, src_begin=16, n_tokens=32, stream=0)
+    _bad(L.vc_compress, c, k, k, n_tokens=48, stream=0)
+    _bad(L.vc_compress, c, k, k, dst_begin=512, n_tokens=32, stream=0)
+
+
+def test_verify_accept_stage_reject_bad_arguments():
+    q = torch.zeros(1, 8, 4, 64, dtype=torch.bfloat16)
+    kc = torch.zeros(1, 2, 100, 64, dtype=torch.bfloat16)
+    out = torch.zeros_like(q)
+    ws = torch.zeros(1 << 20, dtype=torch.uint8)
+    _bad(L.vc_verify_attn_full, q, kc, kc, 97, out, ws=ws, stream=0)          # ctx + k > rows
+    _bad(L.vc_verify_attn_full, q, kc, kc, 10, out, ws=ws, split_tokens=100, stream=0)
+    _bad(L.vc_verify_attn_full, q.float(), kc.float(), kc.float(), 10, out.float(), ws=ws, stream=0,
+         sm_scale=-1.0)
+    _bad(L.vc_verify_attn_full, torch.zeros(1, 8, 4, 96, dtype=torch.bfloat16),
+         torch.zeros(1, 2, 100, 96, dtype=torch.bfloat16), torch.zeros(1, 2, 100, 96, dtype=torch.bfloat16), 10,
+         torch.zeros(1, 8, 4, 96, dtype=torch.bfloat16), ws=ws, stream=0, status=L._lib.VC_ERR_UNSUPPORTED)
+    d = torch.zeros(2, 2000, dtype=torch.int32)
+    _bad(L.vc_accept, d, d, d[:, 0], d[:, 0], d, stream=0)                    # k > 1024
+    hk = torch.zeros(1, 2, 8, 4)
+    _bad(L.vc_stage_full_kv, hk, hk, torch.zeros(1, 2, 4, 4), torch.zeros(1, 2, 4, 4), 0, 8, copy_stream=0)
+
+
+def test_drop_rejects_bad_arguments():
+    s = torch.zeros(1, 2, 10)
+    _bad(L.vc_drop_select, s, 11, torch.zeros(1, 2, 11, dtype=torch.int32), stream=0)
+    _bad(L.vc_drop_select, s, 0, torch.zeros(1, 2, 1, dtype=torch.int32), stream=0)
+    k = torch.zeros(1, 2, 10, 64, dtype=torch.bfloat16)
+    _bad(L.vc_drop_scores, k, torch.zeros(2, 65, 64, dtype=torch.bfloat16), torch.zeros(1, 2, 10),
+         ws=torch.zeros(1 << 16, dtype=torch.uint8), stream=0)

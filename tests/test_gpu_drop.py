@@ -1,0 +1,114 @@
+"""GPU parity: token-drop scoring (tolerance), top-k selection (bit exact on the
+same float32 scores; on GPU-computed scores exact outside the near-threshold band),
+row gather (bit exact) and decode over the kept rows, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import lossy_kv_draft_amd as L
+from workloads import configs as C, gen as G
+from oracle import drop as OD, attention as OA
+from gpu_util import T, np32, say, TOL
+
+pytestmark = pytest.mark.gpu
+
+SMALL = C.small(C.DROP, N=5000)   # 3 scoring chunks, ragged last chunk
+
+
+def _scores_oracle(w, K, P):
+    return np.stack([np.stack([OD.scores(K[b, h], P[h], w.d ** -0.5) for h in range(w.Hkv)]) for b in range(w.B)])
+
+
+def test_drop_scores_match_oracle():
+    w = SMALL
+    K = G.full_kv(w, "k")
+    P = G.full_probes(w)
+    sc = torch.empty(w.B, w.Hkv, w.N, device="cuda")
+    L.vc_drop_scores(T(K, torch.bfloat16), T(P, torch.bfloat16), sc)
+    torch.cuda.synchronize()
+    ref = _scores_oracle(w, K, P)
+    got = np32(sc)
+    assert np.abs(got - ref).max() <= 1e-5 * ref.max() + 1e-9
+    assert np.allclose(got.sum(axis=-1), w.n_probes, rtol=1e-4)
+
+
+@pytest.mark.parametrize("N,keep", [(5000, 1250), (4096, 1024), (777, 1), (777, 777), (300, 299)])
+def test_drop_select_bit_exact_on_same_scores(N, keep):
+    """The oracle's scores, rounded to float32 and coarsened to force many exact ties,
+    are the input of both selections."""
+    w = SMALL.with_(N=N)
+    rng = np.random.default_rng(N + keep)
+    s = rng.gamma(2.0, 1.0, size=(w.B, w.Hkv, N)).astype(np.float32)
+    s = np.round(s * 8) / 8                     # many ties
+    s = s.astype(np.float32)
+    kept = torch.empty(w.B, w.Hkv, keep, dtype=torch.int32, device="cuda")
+    L.vc_drop_select(T(s), keep, kept)
+    torch.cuda.synchronize()
+    got = kept.cpu().numpy()
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            assert np.array_equal(got[b, h], OD.select(s[b, h], keep)), (b, h)
+
+
+def test_gather_rows_bit_exact():
+    w = SMALL
+    K = G.full_kv(w, "k")
+    idx = np.sort(np.random.default_rng(1).choice(w.N, size=(w.B, w.Hkv, 100), replace=True), axis=-1)
+    dst = torch.zeros(w.B, w.Hkv, 128, w.d, dtype=torch.bfloat16, device="cuda")
+    L.vc_gather_rows(T(K, torch.bfloat16), T(idx, torch.int32), 100, dst)
+    torch.cuda.synchronize()
+    got = np32(dst)
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            assert np.array_equal(got[b, h, :100], OD.gather(K[b, h], idx[b, h]))
+            assert np.all(got[b, h, 100:] == 0)
+
+
+def test_compress_drop_end_to_end_and_decode():
+    w = SMALL
+    say(f"[drop] B{w.B} Hkv{w.Hkv} N{w.N} keep {w.keep_ratio}")
+    K, V = G.full_kv(w, "k"), G.full_kv(w, "v")
+    P = G.full_probes(w)
+    keep = OD.n_keep(w.N, w.keep_ratio)
+    assert L.vc_drop_keep_count(w.keep_ratio, w.N) == keep
+    ckv = L.Ckv("drop", w.B, w.Hkv, w.d, keep, keep_ratio=w.keep_ratio, kv_dtype="bf16")
+    Kd, Vd = T(K, torch.bfloat16), T(V, torch.bfloat16)
+    L.vc_compress(ckv, Kd, Vd, probes=T(P, torch.bfloat16))
+    ckv.n_main = keep
+    torch.cuda.synchronize()
+    ref_scores = _scores_oracle(w, K, P)
+    idx = ckv.kept_idx.cpu().numpy()
+    kk, vk = np32(ckv.k_kept), np32(ckv.v_kept)
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            ref = OD.select(ref_scores[b, h], keep)
+            s = ref_scores[b, h]
+            thr = np.sort(s)[::-1][keep - 1]
+            band = np.abs(s - thr) <= 1e-6 * s.max()
+            # outside the near-threshold band both selections agree exactly
+            g, r = np.zeros(w.N, bool), np.zeros(w.N, bool)
+            g[idx[b, h]] = True
+            r[ref] = True
+            assert np.array_equal(g[~band], r[~band])
+            assert np.all(np.diff(idx[b, h]) > 0) and g.sum() == keep
+            assert np.array_equal(kk[b, h], K[b, h, idx[b, h]]) and np.array_equal(vk[b, h], V[b, h, idx[b, h]])
+    # decode over the kept rows
+    Q = G.full_window_q(w)[:, :, 0]
+    out = torch.empty(w.B, w.Hq, w.d, device="cuda", dtype=torch.bfloat16)
+    L.vc_decode_attn_compressed(ckv, T(Q, torch.bfloat16), out)
+    torch.cuda.synchronize()
+    for b in range(w.B):
+        o, _ = OA.decode(Q[b], kk[b], vk[b], w.d ** -0.5)
+        assert np.abs(np32(out[b]) - o).max() <= TOL["bf16"]
+
+
+def test_keep_all_decode_equals_dense_decode():
+    w = SMALL.with_(N=1000, keep_ratio=1.0)
+    K, V = G.full_kv(w, "k"), G.full_kv(w, "v")
+    P = G.full_probes(w)
+    ckv = L.Ckv("drop", w.B, w.Hkv, w.d, w.N, keep_ratio=1.0, kv_dtype="bf16")
+    L.vc_compress(ckv, T(K, torch.bfloat16), T(V, torch.bfloat16), probes=T(P, torch.bfloat16))
+    ckv.n_main = w.N
+    torch.cuda.synchronize()
+    assert np.array_equal(ckv.kept_idx.cpu().numpy(), np.broadcast_to(np.arange(w.N), (w.B, w.Hkv, w.N)))
+    assert torch.equal(ckv.k_kept, T(K, torch.bfloat16))

@@ -1,0 +1,194 @@
+"""GPU parity: quantize-and-pack (bit exact) and compressed decode attention
+(within the stated tolerance) against the oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import lossy_kv_draft_amd as L
+from workloads import configs as C, gen as G
+from oracle import quant as OQ, attention as OA
+from gpu_util import T, np32, tdtype, oracle_compress, oracle_dequant, upload_quant, inputs, TOL, LSE_TOL, say
+
+pytestmark = pytest.mark.gpu
+
+# reduced copies of the quantized workloads; N spans several 32-token tiles and
+# several splits and is not a multiple of the split length
+SMALL = {
+    "tiny_fp32": C.TINY,
+    "llama8b_4bit": C.small(C.LLAMA8B, N=64 * 37),
+    "qwen30b_k4v3": C.small(C.QWEN30B, N=32 * 45),
+    "e2e_2bit": C.small(C.E2E, N=32 * 41),
+    "k8v16_f32": C.TINY.with_(name="k8v16", k_bits=8, v_bits=16, N=32 * 9),
+    "k16v8_bf16": C.small(C.LLAMA8B, N=64 * 5, k_bits=16, v_bits=8, scale_dtype="f32"),
+    "k3v2_g16": C.small(C.E2E, N=16 * 13, k_bits=3, v_bits=2, group=16),
+}
+
+
+def _ckv(w, N, tail_cap=0):
+    return L.Ckv("quant", w.B, w.Hkv, w.d, N, k_bits=w.k_bits, v_bits=w.v_bits, group=w.group,
+                 param_dtype=w.scale_dtype, kv_dtype=w.dtype, tail_cap=tail_cap)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_compress_quant_bit_exact(name):
+    w = SMALL[name]
+    say(f"[quant] {name} B{w.B} Hkv{w.Hkv} N{w.N} d{w.d} k{w.k_bits} v{w.v_bits} G{w.group}")
+    K, V = G.full_kv(w, "k"), G.full_kv(w, "v")
+    ckv = _ckv(w, w.N)
+    L.vc_compress(ckv, T(K, tdtype(w.dtype)), T(V, tdtype(w.dtype)))
+    torch.cuda.synchronize()
+    ref = oracle_compress(w, K, V)
+    assert np.array_equal(ckv.k_codes.cpu().numpy().view(np.uint32), ref["k_codes"])
+    assert np.array_equal(ckv.v_codes.cpu().numpy().view(np.uint32), ref["v_codes"])
+    for key in ("k_scale", "k_zero", "v_scale", "v_zero"):
+        assert np.array_equal(np32(getattr(ckv, key)), ref[key]), key
+
+
+def test_compress_quant_row_offsets():
+    """Rows [2G, 5G) of a source written at rows [G, 4G) of the cache; other rows untouched."""
+    w = SMALL["e2e_2bit"]
+    G_ = w.group
+    K, V = G.full_kv(w, "k"), G.full_kv(w, "v")
+    ckv = _ckv(w, 8 * G_)
+    ckv.k_codes.fill_(-1)
+    L.vc_compress(ckv, T(K, torch.bfloat16), T(V, torch.bfloat16), src_begin=2 * G_, n_tokens=3 * G_, dst_begin=G_)
+    torch.cuda.synchronize()
+    ref = oracle_compress(w, K[:, :, 2 * G_:5 * G_], V[:, :, 2 * G_:5 * G_])
+    got = ckv.k_codes.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got[:, :, G_:4 * G_], ref["k_codes"])
+    assert np.all(got[:, :, :G_] == 0xFFFFFFFF) and np.all(got[:, :, 4 * G_:] == 0xFFFFFFFF)
+    assert np.array_equal(np32(ckv.v_scale)[:, :, G_:4 * G_], ref["v_scale"])
+    assert np.array_equal(np32(ckv.k_zero)[:, :, 1:4], ref["k_zero"])
+
+
+def test_compress_constant_groups_give_zero_scale():
+    w = SMALL["llama8b_4bit"].with_(N=128)
+    K = np.full((w.B, w.Hkv, 128, w.d), 1.5, np.float32)
+    ckv = _ckv(w, 128)
+    L.vc_compress(ckv, T(K, torch.bfloat16), T(K, torch.bfloat16))
+    torch.cuda.synchronize()
+    assert int(ckv.k_codes.abs().sum()) == 0 and float(ckv.k_scale.float().abs().sum()) == 0.0
+    assert torch.all(ckv.k_zero.float() == 1.5)
+
+
+def _decode_case(w, tail, seed_row=None):
+    """Decode each sequence's window query `tail-1` over the compressed context plus
+    window rows [0, tail) (the draft step of that row)."""
+    K, V, Q, Kw, Vw = inputs(w)
+    comp = oracle_compress(w, K, V)
+    dt = tdtype(w.dtype)
+    ckv = _ckv(w, w.N, tail_cap=max(tail, 1))
+    upload_quant(ckv, comp, w.N)
+    ckv.n_main = w.N
+    ckv.tail_len = tail
+    if tail:
+        ckv.tail_k[:, :, :tail] = T(Kw[:, :, :tail], dt)
+        ckv.tail_v[:, :, :tail] = T(Vw[:, :, :tail], dt)
+    i = max(tail - 1, 0)
+    q = T(Q[:, :, i], dt)
+    out = torch.empty(w.B, w.Hq, w.d, device="cuda", dtype=dt)
+    lse = torch.empty(w.B, w.Hq, device="cuda", dtype=torch.float32)
+    L.vc_decode_attn_compressed(ckv, q, out, lse=lse)
+    torch.cuda.synchronize()
+    kh, vh = oracle_dequant(w, comp)
+    sc = w.d ** -0.5
+    for b in range(w.B):
+        o, l = OA.decode(Q[b, :, i], kh[b], vh[b], sc, Kw[b, :, :tail], Vw[b, :, :tail])
+        err = np.abs(np32(out[b]) - o).max()
+        lerr = np.abs(np32(lse[b]) - l).max()
+        assert err <= TOL[w.dtype], f"b={b} max-abs {err}"
+        assert lerr <= LSE_TOL[w.dtype], f"b={b} lse error {lerr}"
+    return ckv, out
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("tail", [0, 5])
+def test_decode_quant_matches_oracle(name, tail):
+    w = SMALL[name]
+    say(f"[decode] {name} tail={tail}")
+    _decode_case(w, tail)
+
+
+def test_decode_ragged_lengths_and_empty_sequence():
+    w = C.small(C.E2E, B=3, N=32 * 20)
+    K, V, Q, Kw, Vw = inputs(w)
+    comp = oracle_compress(w, K, V)
+    ckv = _ckv(w, w.N, tail_cap=8)
+    upload_quant(ckv, comp, w.N)
+    ckv.n_main, ckv.tail_len = w.N, 8
+    ckv.tail_k[:] = T(Kw[:, :, :8], torch.bfloat16)
+    ckv.tail_v[:] = T(Vw[:, :, :8], torch.bfloat16)
+    main = [w.N, 32 * 7, 0]
+    tl = [3, 0, 0]
+    out = torch.empty(w.B, w.Hq, w.d, device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty(w.B, w.Hq, device="cuda")
+    L.vc_decode_attn_compressed(ckv, T(Q[:, :, 0], torch.bfloat16), out, lse=lse,
+                                main_lens=torch.tensor(main, dtype=torch.int32, device="cuda"),
+                                tail_lens=torch.tensor(tl, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    kh, vh = oracle_dequant(w, comp)
+    for b in range(2):
+        o, l = OA.decode(Q[b, :, 0], kh[b, :, :main[b]], vh[b, :, :main[b]], w.d ** -0.5,
+                         Kw[b, :, :tl[b]], Vw[b, :, :tl[b]])
+        assert np.abs(np32(out[b]) - o).max() <= TOL["bf16"]
+        assert np.abs(np32(lse[b]) - l).max() <= LSE_TOL["bf16"]
+    assert torch.all(out[2] == 0) and torch.all(torch.isneginf(lse[2]))
+
+
+def test_decode_is_deterministic_and_reuses_workspace():
+    w = SMALL["llama8b_4bit"]
+    K, V, Q, Kw, Vw = inputs(w)
+    comp = oracle_compress(w, K, V)
+    ckv = _ckv(w, w.N)
+    upload_quant(ckv, comp, w.N)
+    ckv.n_main = w.N
+    ws = L.workspace(L.vc_decode_workspace_bytes(ckv, w.Hq))
+    outs = []
+    for _ in range(3):
+        o = torch.empty(w.B, w.Hq, w.d, device="cuda", dtype=torch.bfloat16)
+        L.vc_decode_attn_compressed(ckv, T(Q[:, :, 0], torch.bfloat16), o, ws=ws)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("wname", ["llama8b", "qwen30b"])
+def test_full_size_compress_and_decode_sampled(wname):
+    """Full-size workload in the launch configuration the benchmark times: compress
+    the whole cache on the GPU, decode draft row 0, and compare sampled slices
+    (codes bit exact, outputs within tolerance) with the oracle."""
+    w = {"llama8b": C.LLAMA8B, "qwen30b": C.QWEN30B}[wname]
+    say(f"[full] {w.name}: generating inputs")
+    dt = torch.bfloat16
+    Kd = torch.empty(w.B, w.Hkv, w.N, w.d, dtype=dt, device="cuda")
+    Vd = torch.empty_like(Kd)
+    for b in range(w.B):
+        Kd[b] = T(np.stack([G.kv_slice(w, "k", b, h) for h in range(w.Hkv)]), dt)
+        Vd[b] = T(np.stack([G.kv_slice(w, "v", b, h) for h in range(w.Hkv)]), dt)
+    ckv = _ckv(w, w.N, tail_cap=1)
+    L.vc_compress(ckv, Kd, Vd)
+    ckv.n_main, ckv.tail_len = w.N, 1
+    Q0 = np.stack([np.stack([G.window_q(w, b, h)[0] for h in range(w.Hq)]) for b in range(w.B)])
+    Kw0 = np.stack([np.stack([G.window_kv(w, "k", b, h)[:1] for h in range(w.Hkv)]) for b in range(w.B)])
+    Vw0 = np.stack([np.stack([G.window_kv(w, "v", b, h)[:1] for h in range(w.Hkv)]) for b in range(w.B)])
+    ckv.tail_k[:] = T(Kw0, dt)
+    ckv.tail_v[:] = T(Vw0, dt)
+    out = torch.empty(w.B, w.Hq, w.d, device="cuda", dtype=dt)
+    L.vc_decode_attn_compressed(ckv, T(Q0, dt), out)
+    torch.cuda.synchronize()
+    del Kd, Vd
+    rng = np.random.default_rng(7)
+    grp = w.Hq // w.Hkv
+    for b, h in {(int(rng.integers(w.B)), int(rng.integers(w.Hkv))) for _ in range(3)} | {(w.B - 1, w.Hkv - 1)}:
+        say(f"[full] {w.name}: checking slice b={b} h={h}")
+        k, v = G.kv_slice(w, "k", b, h), G.kv_slice(w, "v", b, h)
+        c = OQ.compress_slice(k, v, w.k_bits, w.v_bits, w.group, w.scale_dtype)
+        assert np.array_equal(ckv.k_codes[b, h].cpu().numpy().view(np.uint32), c["k_codes"])
+        assert np.array_equal(ckv.v_codes[b, h].cpu().numpy().view(np.uint32), c["v_codes"])
+        assert np.array_equal(np32(ckv.k_scale[b, h]), c["k_scale"])
+        assert np.array_equal(np32(ckv.v_zero[b, h]), c["v_zero"])
+        kh, vh = OQ.dequantize_slice(c, w.d, w.k_bits, w.v_bits, w.group)
+        o, _ = OA.decode(Q0[b, h * grp:(h + 1) * grp], kh[None], vh[None], w.d ** -0.5, Kw0[b, h:h + 1],
+                         Vw0[b, h:h + 1])
+        err = np.abs(np32(out[b, h * grp:(h + 1) * grp]) - o).max()
+        assert err <= TOL["bf16"], f"b={b} h={h} max-abs {err}"

@@ -81,12 +81,12 @@ def test_argmax_ties_go_to_lowest_index():
 def test_tokens_from_outputs_uses_head_mean():
     rng = np.random.default_rng(5)
     o = rng.standard_normal((2, 4, 3, 8))
-    W = rng.standard_normal((8, 20))
+    W = rng.standard_normal((20, 8))
     t = LG.tokens_from_outputs(o, W)
     for b in range(2):
         for i in range(3):
             u = sum(o[b, h, i] for h in range(4)) / 4
-            assert t[b, i] == int(np.argmax(u @ W))
+            assert t[b, i] == int(np.argmax(W @ u))
 
 
 def test_accept_brute_force_all_short_strings():
