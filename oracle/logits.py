@@ -6,10 +6,11 @@ TEST INFRASTRUCTURE (see the package header).
 Source: neuraltrendhub.com summary "What the paper found" (greedy decoding output
 must equal full-KV inference).  For the attention-only workloads there is no model,
 so the token of a row is read from its attention output through a fixed random
-projection W [d, V] (a reading; the pages do not describe one):
+projection W [V, d], one row per vocabulary entry (a reading; the pages do not
+describe one):
 
 * u = mean over the Hq q-heads of the row's attention output (float64);
-* logits = u @ W; token = argmax, equal logits going to the lowest index.
+* logits_v = u . W_v; token = argmax, equal logits going to the lowest index.
 
 Parity: pinned by planted ties (lowest index wins) and by np.argmax's documented
 first-occurrence rule.
@@ -23,7 +24,8 @@ def head_mean(o: np.ndarray) -> np.ndarray:
 
 
 def logits(u: np.ndarray, W: np.ndarray) -> np.ndarray:
-    return np.asarray(u, np.float64) @ np.asarray(W, np.float64)
+    """u [..., d], W [V, d] -> [..., V] (float64)."""
+    return np.asarray(u, np.float64) @ np.asarray(W, np.float64).T
 
 
 def argmax_lowest(x: np.ndarray) -> np.ndarray:

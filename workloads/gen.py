@@ -84,8 +84,8 @@ def probes(w: Workload, h: int) -> np.ndarray:
 
 
 def projection(w: Workload) -> np.ndarray:
-    """Random vocabulary projection W: [d, vocab]."""
-    return to_storage(_normal(_rng(w, _W), (w.d, w.vocab)), w.w_dtype)
+    """Random vocabulary projection W: [vocab, d] (one row per vocabulary entry)."""
+    return to_storage(_normal(_rng(w, _W), (w.vocab, w.d)), w.w_dtype)
 
 
 def _stack(fn, outer, inner, threads=8):
