@@ -1,0 +1,344 @@
+"""Benchmark of the VeriCache draft-and-verify hot path on one MI355X.
+
+One step = one kernel-level draft-and-verify round over one batch of synthetic
+inputs resident in HBM:
+  draft   k single-token decode-attention calls over the compressed cache (draft
+          step i attends to the compressed context plus window rows 0..i),
+  verify  causal window attention of the k rows over the full bf16 cache,
+  tokens  head mean + greedy argmax through a fixed random vocabulary projection
+          for the draft and the verify rows, then longest-prefix acceptance.
+Staging of the full KV from pinned host memory (PCIe) and compression are measured
+separately (they are not part of `value`).
+
+value = compressed decode-attention HBM GB/s (algorithmic bytes of the k decode
+calls / their time).  verify TFLOP/s and accepted tokens/s of the round are reported
+beside it.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compressed decode-attn HBM GB/s; verify-attn TFLOP/s; accepted tok/s @32k ctx"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="llama8b", choices=["llama8b", "qwen30b", "drop", "tiny"])
+    p.add_argument("--copies", type=int, default=3, help="compressed-cache copies rotated across draft calls")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-stage", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def decode_bytes(w, n_ctx, tail):
+    """Algorithmic bytes of one decode call: the compressed rows it must read (codes
+    and group parameters, or the kept bf16 rows), the tail rows, the queries and the
+    outputs."""
+    bh = w.B * w.Hkv
+    eb = 4 if w.dtype == "f32" else 2
+    if w.method == "quant":
+        pb = 4 if w.scale_dtype == "f32" else 2
+        main = bh * n_ctx * w.d * (w.k_bits + w.v_bits) // 8
+        main += bh * (n_ctx // w.group) * w.d * 2 * pb + bh * n_ctx * (w.d // w.group) * 2 * pb
+    else:
+        main = bh * n_ctx * w.d * 2 * eb
+    return main + bh * tail * w.d * 2 * eb + 2 * w.B * w.Hq * w.d * eb
+
+
+def verify_flops(w, n_ctx):
+    """4 * B * Hq * d * sum_i (N + i + 1): QK^T and PV over the visible keys."""
+    return 4.0 * w.B * w.Hq * w.d * sum(n_ctx + i + 1 for i in range(w.k))
+
+
+def verify_bytes(w, n_ctx):
+    eb = 4 if w.dtype == "f32" else 2
+    return w.B * w.Hkv * (n_ctx + w.k) * w.d * 2 * eb + 2 * w.B * w.Hq * w.k * w.d * eb
+
+
+def workload(name):
+    from workloads import configs as C
+    w = {"llama8b": C.LLAMA8B, "qwen30b": C.QWEN30B, "drop": C.DROP, "tiny": C.TINY}[name]
+    # A projection for the greedy tokens: the Llama-3-8B-shaped and token-dropping
+    # layers name none, so they use a Llama-3 sized vocabulary (128256).
+    if w.vocab == 0:
+        w = w.with_(vocab=128256, w_dtype="bf16")
+    return w
+
+
+def setup(w, copies):
+    import torch
+    import lossy_kv_draft_amd as L
+    from workloads import gen as G
+    dev = "cuda"
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    rows = w.N + w.k
+    t0 = time.time()
+    kc = torch.empty(w.B, w.Hkv, rows, w.d, dtype=dt, device=dev)
+    vc = torch.empty_like(kc)
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(8) as ex:
+        for b in range(w.B):
+            for which, dst in (("k", kc), ("v", vc)):
+                rows_b = list(ex.map(lambda h: G.kv_slice(w, which, b, h), range(w.Hkv)))
+                dst[b, :, :w.N] = torch.from_numpy(np.stack(rows_b)).to(dev, dt)
+    kc[:, :, w.N:] = torch.from_numpy(G.full_window_kv(w, "k")).to(dev, dt)
+    vc[:, :, w.N:] = torch.from_numpy(G.full_window_kv(w, "v")).to(dev, dt)
+    q = torch.from_numpy(G.full_window_q(w)).to(dev, dt)
+    Wp = torch.from_numpy(G.projection(w)).to(dev, torch.float32 if w.w_dtype == "f32" else torch.bfloat16)
+    print(f"[bench] inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    ckvs = []
+    comp_ms = None
+    for c in range(copies):
+        if w.method == "quant":
+            ckv = L.Ckv("quant", w.B, w.Hkv, w.d, w.N, k_bits=w.k_bits, v_bits=w.v_bits, group=w.group,
+                        param_dtype=w.scale_dtype, kv_dtype=w.dtype, tail_cap=w.k)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            L.vc_compress(ckv, kc, vc, n_tokens=w.N)
+            e1.record()
+            torch.cuda.synchronize()
+            comp_ms = e0.elapsed_time(e1)
+            ckv.n_main = w.N
+        else:
+            keep = L.vc_drop_keep_count(w.keep_ratio, w.N)
+            ckv = L.Ckv("drop", w.B, w.Hkv, w.d, keep, keep_ratio=w.keep_ratio, kv_dtype=w.dtype, tail_cap=w.k)
+            probes = torch.from_numpy(G.full_probes(w)).to(dev, torch.bfloat16)
+            ksrc = kc[:, :, :w.N].contiguous()
+            vsrc = vc[:, :, :w.N].contiguous()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            L.vc_compress(ckv, ksrc, vsrc, probes=probes)
+            e1.record()
+            torch.cuda.synchronize()
+            comp_ms = e0.elapsed_time(e1)
+            del ksrc, vsrc
+            ckv.n_main = keep
+        ckv.tail_k.copy_(kc[:, :, w.N:])
+        ckv.tail_v.copy_(vc[:, :, w.N:])
+        ckvs.append(ckv)
+    st = dict(w=w, kc=kc, vc=vc, q=q, W=Wp, ckvs=ckvs, dt=dt, comp_ms=comp_ms)
+    st["dec_ws"] = L.workspace(L.vc_decode_workspace_bytes(ckvs[0], w.Hq))
+    st["ver_ws"] = L.workspace(L.vc_verify_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, w.k, w.N))
+    R = w.B * w.k
+    st["lg_ws"] = L.workspace(L.vc_logits_workspace_bytes(R, w.vocab))
+    st["qrows"] = [q[:, :, i].contiguous() for i in range(w.k)]
+    # draft outputs [k, B, Hq, d]: step i writes slice i; read as [B, Hq, k, d] by stride
+    st["dec_all"] = torch.empty(w.k, w.B, w.Hq, w.d, dtype=dt, device=dev)
+    st["dec_out"] = [st["dec_all"][i] for i in range(w.k)]
+    st["out_v"] = torch.empty(w.B, w.Hq, w.k, w.d, dtype=dt, device=dev)
+    st["u_d"] = torch.empty(R, w.d, device=dev)
+    st["u_v"] = torch.empty(R, w.d, device=dev)
+    st["tok_d"] = torch.empty(R, dtype=torch.int32, device=dev)
+    st["tok_v"] = torch.empty(R, dtype=torch.int32, device=dev)
+    st["acc"] = torch.empty(w.B, dtype=torch.int32, device=dev)
+    st["nc"] = torch.empty(w.B, dtype=torch.int32, device=dev)
+    st["com"] = torch.empty(w.B, w.k, dtype=torch.int32, device=dev)
+    return st
+
+
+def run_step(st, ev=None, dec_ev=None):
+    """One round.  ev: 4 events (start, after draft, after verify, after tokens);
+    dec_ev: list of (start, end) event pairs around each decode launch."""
+    import lossy_kv_draft_amd as L
+    w = st["w"]
+    if ev:
+        ev[0].record()
+    for i in range(w.k):
+        ckv = st["ckvs"][i % len(st["ckvs"])]
+        ckv.tail_len = i + 1
+        if dec_ev:
+            dec_ev[i][0].record()
+        L.vc_decode_attn_compressed(ckv, st["qrows"][i], st["dec_out"][i], ws=st["dec_ws"])
+        if dec_ev:
+            dec_ev[i][1].record()
+    if ev:
+        ev[1].record()
+    L.vc_verify_attn_full(st["q"], st["kc"], st["vc"], w.N, st["out_v"], ws=st["ver_ws"])
+    if ev:
+        ev[2].record()
+    L.vc_head_mean(st["dec_all"].permute(1, 2, 0, 3), st["u_d"])
+    L.vc_head_mean(st["out_v"], st["u_v"])
+    L.vc_logits_argmax(st["u_d"], st["W"], st["tok_d"], ws=st["lg_ws"])
+    L.vc_logits_argmax(st["u_v"], st["W"], st["tok_v"], ws=st["lg_ws"])
+    L.vc_accept(st["tok_d"].view(w.B, w.k), st["tok_v"].view(w.B, w.k), st["acc"], st["nc"], st["com"])
+    if ev:
+        ev[3].record()
+
+
+def measure_stage(st):
+    """Full-KV swap-in: H2D copy of the whole context of one layer from pinned host
+    memory on a side stream, alone and overlapped with the k draft decodes."""
+    import torch
+    import lossy_kv_draft_amd as L
+    w = st["w"]
+    hk = torch.empty(st["kc"].shape, dtype=st["dt"], pin_memory=True)
+    hv = torch.empty(st["vc"].shape, dtype=st["dt"], pin_memory=True)
+    hk.copy_(st["kc"])
+    hv.copy_(st["vc"])
+    dk = torch.empty_like(st["kc"])
+    dv = torch.empty_like(st["vc"])
+    side = torch.cuda.Stream()
+    nbytes = 2 * w.B * w.Hkv * w.N * w.d * hk.element_size()
+    done = torch.cuda.Event()
+
+    def stage():
+        L.vc_stage_full_kv(hk, hv, dk, dv, 0, w.N, copy_stream=side, done=done)
+
+    def draft():
+        for i in range(w.k):
+            ckv = st["ckvs"][i % len(st["ckvs"])]
+            ckv.tail_len = i + 1
+            L.vc_decode_attn_compressed(ckv, st["qrows"][i], st["dec_out"][i], ws=st["dec_ws"])
+
+    res = {}
+    for name, fn in (("stage_alone", lambda: (stage(), done.synchronize())),
+                     ("draft_alone", lambda: (draft(), torch.cuda.synchronize())),
+                     ("overlapped", lambda: (stage(), draft(), torch.cuda.current_stream().wait_event(done),
+                                             torch.cuda.synchronize()))):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        res[name] = min(ts) * 1e3
+    ok = torch.equal(dk[:, :, :w.N], st["kc"][:, :, :w.N])
+    return {"bytes": nbytes, "h2d_GBps": round(nbytes / (res["stage_alone"] * 1e-3) / 1e9, 2),
+            "stage_ms": round(res["stage_alone"], 3), "draft_ms": round(res["draft_alone"], 3),
+            "overlapped_ms": round(res["overlapped"], 3),
+            "overlap_hidden_frac": round((res["stage_alone"] + res["draft_alone"] - res["overlapped"]) /
+                                         min(res["stage_alone"], res["draft_alone"]), 3),
+            "copy_exact": bool(ok)}
+
+
+def cpu_baseline(w, seconds):
+    """The oracle (numpy, float64 attention) timed on the host for a bounded sample:
+    whole (sequence, kv-head) slices of the same workload -- dequantize the slice's
+    compressed rows and decode one draft query of each of its q-heads -- repeated
+    until about `seconds` of work; scaled to GB/s of the same algorithmic bytes."""
+    from workloads import gen as G
+    from oracle import quant as OQ, attention as OA, drop as OD
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    grp = w.Hq // w.Hkv
+    per_slice = decode_bytes(w, w.N, 1) / (w.B * w.Hkv)
+    done, t_total, b, h = 0, 0.0, 0, 0
+    # inputs and their compression are prepared outside the timed region
+    while t_total < seconds and done < w.B * w.Hkv:
+        k, v = G.kv_slice(w, "k", b, h), G.kv_slice(w, "v", b, h)
+        q = np.stack([G.window_q(w, b, h * grp + j)[0] for j in range(grp)])
+        kw, vw = G.window_kv(w, "k", b, h)[:1], G.window_kv(w, "v", b, h)[:1]
+        if w.method == "quant":
+            c = OQ.compress_slice(k, v, w.k_bits, w.v_bits, w.group, w.scale_dtype)
+            t0 = time.perf_counter()
+            kh, vh = OQ.dequantize_slice(c, w.d, w.k_bits, w.v_bits, w.group)
+            OA.decode(q, kh[None], vh[None], w.d ** -0.5, kw[None], vw[None])
+        else:
+            t0 = time.perf_counter()
+            nk = OD.n_keep(w.N, w.keep_ratio)   # same work as decoding the kept rows
+            OA.decode(q, k[None, :nk], v[None, :nk], w.d ** -0.5, kw[None], vw[None])
+        t_total += time.perf_counter() - t0
+        done += 1
+        h += 1
+        if h == w.Hkv:
+            h, b = 0, b + 1
+    return {"value": round(done * per_slice / t_total / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} of {w.B * w.Hkv} (sequence, kv-head) slices: {'dequantize + ' if w.method == 'quant' else ''}decode of "
+                      f"{grp} q-heads over {w.N} tokens, {t_total:.1f}s of CPU time, "
+                      f"{len(os.sched_getaffinity(0))} cores visible"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: the hot path is measured on a single MI355X "
+              "(per-(sequence, kv-head) sharding needs no collectives; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    w = workload(a.workload)
+    torch.cuda.set_device(0)
+    st = setup(w, a.copies)
+    for _ in range(a.warmup):
+        run_step(st)
+    torch.cuda.synchronize()
+
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [[mk() for _ in range(4)] for _ in range(a.steps)]
+    dec = [[(mk(), mk()) for _ in range(w.k)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(a.steps):
+        run_step(st, evs[s], dec[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    draft_ms = sum(e[0].elapsed_time(e[1]) for e in evs)
+    verify_ms = sum(e[1].elapsed_time(e[2]) for e in evs)
+    tok_ms = sum(e[2].elapsed_time(e[3]) for e in evs)
+    step_ms = sum(e[0].elapsed_time(e[3]) for e in evs) / a.steps
+    dec_launch_ms = [p[0].elapsed_time(p[1]) for d in dec for p in d]
+    dec_avg_ms = float(np.mean(dec_launch_ms))
+
+    # algorithmic work: draft step i reads the compressed context plus i + 1 tail rows
+    n_ctx = st["ckvs"][0].n_main
+    dbytes = sum(decode_bytes(w, n_ctx, i + 1) for i in range(w.k))
+    decode_gbs = dbytes * a.steps / (draft_ms * 1e-3) / 1e9
+    per_launch = dbytes / w.k
+    achieved = per_launch / (dec_avg_ms * 1e-3) / 1e9
+    vflops = verify_flops(w, w.N)
+    verify_tflops = vflops * a.steps / (verify_ms * 1e-3) / 1e12
+    verify_gbs = verify_bytes(w, w.N) * a.steps / (verify_ms * 1e-3) / 1e9
+    accepted = int(st["nc"].sum().item())
+    acc_len = st["acc"].float().mean().item()
+
+    line = {
+        "metric": METRIC, "value": round(decode_gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "global_batch": w.B, "seq_len": w.N, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.d, "draft_window": w.k, "compressor": (
+                       f"KIVI-style K{w.k_bits}/V{w.v_bits} group {w.group}" if w.method == "quant"
+                       else f"top-{w.keep_ratio:g} accumulated attention, {w.n_probes} probes"),
+                   "parallelism": "none (1 GPU)", "cache_copies_rotated": a.copies},
+        "verify_attn_tflops": round(verify_tflops, 2),
+        "verify_attn_hbm_gbs": round(verify_gbs, 1),
+        "verify_mfma_frac": round(verify_tflops / BF16_PEAK_TFLOPS, 4),
+        "accepted_tok_per_s": round(accepted / (step_ms * 1e-3), 1),
+        "mean_accept_len": round(acc_len, 3),
+        "phase_ms": {"draft": round(draft_ms / a.steps, 4), "verify": round(verify_ms / a.steps, 4),
+                     "tokens_accept": round(tok_ms / a.steps, 4)},
+        "wall_ms_per_step": round(wall / a.steps * 1e3, 4),
+        "compress_ms": round(st["comp_ms"], 4),
+        "roofline": {"bound": "hbm", "kernel": "decode_generic_kernel (quant)" if w.method == "quant"
+                     else "decode_generic_kernel (kept rows)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(per_launch), "avg_launch_us": round(dec_avg_ms * 1e3, 3)},
+    }
+    if not a.no_stage:
+        line["stage_full_kv"] = measure_stage(st)
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -272,8 +272,16 @@ def vc_accept(draft, target, accept_len, n_commit, commit, *, stream=None):
                          _stream(stream)), "vc_accept")
 
 
+def _ensure_event(ev, stream):
+    """torch creates the HIP event behind a torch.cuda.Event on its first record;
+    record it once so that a valid handle is passed to the library."""
+    if ev is not None and not ev.cuda_event:
+        ev.record(torch.cuda.current_stream() if stream is None else stream)
+
+
 def vc_stage_full_kv(host_k, host_v, dev_k, dev_v, tok_begin, tok_end, *, copy_stream=None, done=None):
     B, Hkv, host_rows, d = host_k.shape
+    _ensure_event(done, copy_stream)
     _check(lib.vc_stage_full_kv(_ptr(host_k), _ptr(host_v), _ptr(dev_k), _ptr(dev_v), B, Hkv, d,
                                 host_k.element_size(), host_rows, dev_k.shape[2], tok_begin, tok_end,
                                 _stream(copy_stream), None if done is None else done.cuda_event),
@@ -282,6 +290,7 @@ def vc_stage_full_kv(host_k, host_v, dev_k, dev_v, tok_begin, tok_end, *, copy_s
 
 def vc_stage_full_kv_d2h(dev_k, dev_v, host_k, host_v, tok_begin, tok_end, *, copy_stream=None, done=None):
     B, Hkv, host_rows, d = host_k.shape
+    _ensure_event(done, copy_stream)
     _check(lib.vc_stage_full_kv_d2h(_ptr(dev_k), _ptr(dev_v), _ptr(host_k), _ptr(host_v), B, Hkv, d,
                                     host_k.element_size(), host_rows, dev_k.shape[2], tok_begin, tok_end,
                                     _stream(copy_stream), None if done is None else done.cuda_event),

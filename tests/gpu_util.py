@@ -12,6 +12,28 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}      # max-abs on attention outputs
 LSE_TOL = {"f32": 1e-4, "bf16": 2e-3}  # log-sum-exp is float32 on both storage types
 
 
+def storage_half_ulp(ref, dtype):
+    """Half a unit in the last place of the output storage type at |ref|: the bf16
+    rounding of the stored result adds up to this much on top of the arithmetic
+    error (a value of 28 in an outlier channel has a bf16 half-ulp of 0.0625)."""
+    if dtype != "bf16":
+        return 0.0
+    a = np.maximum(np.abs(ref), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 8)
+
+
+def max_excess(got, ref, dtype):
+    """max over elements of |got - ref| - (TOL + storage half-ulp); <= 0 passes."""
+    err = np.abs(np.asarray(got, np.float64) - ref)
+    return float((err - TOL[dtype] - storage_half_ulp(ref, dtype)).max())
+
+
+def assert_close(got, ref, dtype, what=""):
+    ex = max_excess(got, ref, dtype)
+    err = float(np.abs(np.asarray(got, np.float64) - ref).max())
+    assert ex <= 0, f"{what} max-abs error {err:.4g} exceeds {TOL[dtype]} + storage half-ulp"
+
+
 def tdtype(s):
     return {"f32": torch.float32, "bf16": torch.bfloat16}[s]
 

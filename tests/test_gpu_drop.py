@@ -8,7 +8,7 @@ import torch
 import lossy_kv_draft_amd as L
 from workloads import configs as C, gen as G
 from oracle import drop as OD, attention as OA
-from gpu_util import T, np32, say, TOL
+from gpu_util import assert_close, T, np32, say, TOL
 
 pytestmark = pytest.mark.gpu
 
@@ -99,7 +99,7 @@ def test_compress_drop_end_to_end_and_decode():
     torch.cuda.synchronize()
     for b in range(w.B):
         o, _ = OA.decode(Q[b], kk[b], vk[b], w.d ** -0.5)
-        assert np.abs(np32(out[b]) - o).max() <= TOL["bf16"]
+        assert_close(np32(out[b]), o, 'bf16')
 
 
 def test_keep_all_decode_equals_dense_decode():

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 def test_head_mean_matches_oracle():
     w = C.small(C.LLAMA8B)
-    o = G.normal(w, ("hm",), (w.B, w.Hq, w.k, w.d), dtype="bf16")
+    o = G.normal(w, (1,), (w.B, w.Hq, w.k, w.d), dtype="bf16")
     u = torch.empty(w.B * w.k, w.d, device="cuda")
     L.vc_head_mean(T(o, torch.bfloat16), u)
     o3 = o[:, :, 0]
@@ -45,9 +45,9 @@ def test_logits_argmax_agrees_on_untied_rows(case):
         W = G.projection(w)
     else:
         w, R, Wd = C.TINY, 100, "bf16"
-        W = G.normal(w, ("W5k",), (5000, 64), dtype="bf16")
+        W = G.normal(w, (3,), (5000, 64), dtype="bf16")
     say(f"[argmax] {case}")
-    u = G.normal(w, ("u", case), (R, W.shape[1]), std=0.05)
+    u = G.normal(w, (2, len(case), R), (R, W.shape[1]), std=0.05)
     tok = torch.empty(R, dtype=torch.int32, device="cuda")
     L.vc_logits_argmax(T(u), T(W, torch.float32 if Wd == "f32" else torch.bfloat16), tok)
     torch.cuda.synchronize()
@@ -64,8 +64,8 @@ def test_logits_argmax_agrees_on_untied_rows(case):
 
 def test_logits_argmax_exact_ties_take_lowest_index():
     w = C.TINY
-    W = G.normal(w, ("ties",), (3000, 128), dtype="bf16")
-    u = G.normal(w, ("tu",), (20, 128))
+    W = G.normal(w, (4,), (3000, 128), dtype="bf16")
+    u = G.normal(w, (5,), (20, 128))
     best = OL.argmax_lowest(OL.logits(u, W))
     # duplicate each row's winner at a higher and a lower index: the lower copy must win
     for r, j in enumerate(best[:5]):

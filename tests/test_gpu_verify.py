@@ -8,7 +8,7 @@ import torch
 import lossy_kv_draft_amd as L
 from workloads import configs as C, gen as G
 from oracle import attention as OA
-from gpu_util import T, np32, tdtype, inputs, TOL, LSE_TOL, say
+from gpu_util import assert_close, T, np32, tdtype, inputs, TOL, LSE_TOL, say
 
 pytestmark = pytest.mark.gpu
 
@@ -48,8 +48,7 @@ def test_verify_matches_oracle(name, split):
     torch.cuda.synchronize()
     for b in range(w.B):
         o, l = OA.verify_masked(Q[b], K[b], V[b], Kw[b], Vw[b], w.d ** -0.5)
-        err = np.abs(np32(out[b]) - o).max()
-        assert err <= TOL[w.dtype], f"b={b} max-abs {err}"
+        assert_close(np32(out[b]), o, w.dtype, f"b={b}")
         assert np.abs(np32(lse[b]) - l).max() <= LSE_TOL[w.dtype]
 
 
@@ -87,7 +86,7 @@ def test_verify_ragged_context_lengths():
     torch.cuda.synchronize()
     for b, Lb in enumerate(lens):
         o, l = OA.verify_masked(Q[b], K[b, :, :Lb], V[b, :, :Lb], Kw[b], Vw[b], w.d ** -0.5)
-        assert np.abs(np32(out[b]) - o).max() <= TOL["bf16"]
+        assert_close(np32(out[b]), o, 'bf16')
         assert np.abs(np32(lse[b]) - l).max() <= LSE_TOL["bf16"]
 
 
@@ -130,4 +129,4 @@ def test_full_size_verify_sampled_rows():
         K, V = G.kv_slice(w, "k", b, h), G.kv_slice(w, "v", b, h)
         Kw, Vw = G.window_kv(w, "k", b, h), G.window_kv(w, "v", b, h)
         o, _ = OA.decode(Q[b, hq:hq + 1, i], K[None], V[None], w.d ** -0.5, Kw[None, :i + 1], Vw[None, :i + 1])
-        assert np.abs(np32(out[b, hq, i]) - o[0]).max() <= TOL["bf16"]
+        assert_close(np32(out[b, hq, i]), o[0], 'bf16')
