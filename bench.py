@@ -327,7 +327,7 @@ def main():
                      "tokens_accept": round(tok_ms / a.steps, 4)},
         "wall_ms_per_step": round(wall / a.steps * 1e3, 4),
         "compress_ms": round(st["comp_ms"], 4),
-        "roofline": {"bound": "hbm", "kernel": "decode_generic_kernel (quant)" if w.method == "quant"
+        "roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel (quant)" if w.method == "quant"
                      else "decode_generic_kernel (kept rows)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,

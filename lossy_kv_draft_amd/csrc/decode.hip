@@ -17,45 +17,19 @@
 //   atomic counter -- merges all splits in split order (deterministic) and writes
 //   the normalized output and the log-sum-exp, then resets its counter to zero.
 
-#include "common.h"
+#include "decode_common.h"
 
 namespace vc {
 
-constexpr int kDecThreads = 256;
 constexpr int kDecTile = 32;
 constexpr int kDecMaxAcc = 16;     // (H * d) / kDecThreads accumulators per thread
-constexpr int kDecMaxSplits = 64;
 constexpr int kDecTargetBlocks = 2048;
 
-struct DecodeArgs {
-  // compressed cache
-  const uint32_t* k_codes;
-  const uint32_t* v_codes;
-  const void* k_scale;
-  const void* k_zero;
-  const void* v_scale;
-  const void* v_zero;
-  const void* k_kept;
-  const void* v_kept;
-  const void* tail_k;
-  const void* tail_v;
-  int64_t capacity, tail_cap, n_main, tail_len;
-  const int32_t* main_lens;
-  const int32_t* tail_lens;
-  int k_bits, v_bits, G;
-  // problem
-  const void* q;
-  void* out;
-  float* lse;
-  int Hkv, H, d;
-  float qscale;  // sm_scale * log2(e)
-  int splits;
-  int64_t chunk;
-  // workspace
-  float* part_o;   // [B*Hkv][splits][H][d]
-  float* part_ml;  // [B*Hkv][splits][H][2]
-  int* counters;   // [B*Hkv]
-};
+bool decode_mfma_supported(const vc_ckv* c, int H);
+int decode_mfma_splits(const vc_ckv* c);
+void launch_decode_mfma(const vc_ckv* c, const DecodeArgs& a, dim3 grid, hipStream_t s);
+
+
 
 template <typename P>
 __device__ __forceinline__ float load_param(const void* p, int64_t i) {
@@ -83,7 +57,6 @@ __global__ void __launch_bounds__(kDecThreads) decode_generic_kernel(DecodeArgs 
   float* alpha = sc + H * kDecTile;          // [H]
   float* mrun = alpha + H;                   // [H]
   float* lrun = mrun + H;                    // [H]
-  __shared__ int is_last;
 
   const int split = blockIdx.x;
   const int bh = blockIdx.y;
@@ -200,38 +173,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_generic_kernel(DecodeArgs 
     a.part_ml[(pbase * H + h) * 2 + 0] = mrun[h];
     a.part_ml[(pbase * H + h) * 2 + 1] = lrun[h];
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    int prev = atomicAdd(a.counters + bh, 1);
-    is_last = (prev == a.splits - 1);
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-
-  // ---- merge all splits in split order
-  T* out = static_cast<T*>(a.out);
-  for (int i = tid; i < H * d; i += kDecThreads) {
-    int h = i / d;
-    float M = -INFINITY;
-    for (int s = 0; s < a.splits; ++s)
-      M = fmaxf(M, a.part_ml[((static_cast<int64_t>(bh) * a.splits + s) * H + h) * 2]);
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-      int64_t ps = static_cast<int64_t>(bh) * a.splits + s;
-      float m = a.part_ml[(ps * H + h) * 2];
-      float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-      L += a.part_ml[(ps * H + h) * 2 + 1] * w;
-      O += a.part_o[ps * H * d + i] * w;
-    }
-    float o = L > 0.f ? O / L : 0.f;
-    int64_t oi = (static_cast<int64_t>(b) * a.Hkv * H + hk * H) * d + i;
-    Elem<T>::store(out, oi, o);
-    if (a.lse && (i % d) == 0)
-      a.lse[static_cast<int64_t>(b) * a.Hkv * H + hk * H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
-  }
-  if (tid == 0) a.counters[bh] = 0;
+  decode_finish<T>(a, bh);
 }
 
 // ------------------------------------------------------------------ host side
@@ -264,7 +206,7 @@ using namespace vc;
 extern "C" size_t vc_decode_workspace_bytes(const vc_ckv* c, int32_t Hq) {
   if (!c || c->B <= 0 || c->Hkv <= 0 || c->d <= 0 || Hq <= 0) return 0;
   size_t bh = static_cast<size_t>(c->B) * c->Hkv;
-  size_t S = decode_splits(c);
+  size_t S = kDecMaxSplits;
   size_t H = Hq / c->Hkv;
   size_t bytes = align_up(bh * S * H * c->d * sizeof(float), 256);
   bytes += align_up(bh * S * H * 2 * sizeof(float), 256);
@@ -317,9 +259,16 @@ extern "C" vc_status vc_decode_attn_compressed(const vc_ckv* c, const void* q, i
   a.H = H;
   a.d = c->d;
   a.qscale = sm_scale * kLog2e;
-  int S = decode_splits(c);
-  int64_t total = c->n_main + c->tail_len;
-  a.chunk = cdiv(cdiv(total > 0 ? total : 1, S), kDecTile) * kDecTile;
+  const bool mfma = decode_mfma_supported(c, H);
+  int S;
+  if (mfma) {
+    S = decode_mfma_splits(c);  // compressed-row splits + one tail split
+    a.chunk = cdiv(cdiv(c->n_main > 0 ? c->n_main : 1, S - 1), 128) * 128;
+  } else {
+    S = decode_splits(c);
+    int64_t total = c->n_main + c->tail_len;
+    a.chunk = cdiv(cdiv(total > 0 ? total : 1, S), kDecTile) * kDecTile;
+  }
   a.splits = S;
   size_t bh = static_cast<size_t>(c->B) * c->Hkv;
   char* w = static_cast<char*>(ws);
@@ -330,9 +279,14 @@ extern "C" vc_status vc_decode_attn_compressed(const vc_ckv* c, const void* q, i
   a.counters = reinterpret_cast<int*>(w);
 
   dim3 grid(S, static_cast<unsigned>(bh));
+  hipStream_t s = as_stream(stream);
+  if (mfma) {
+    launch_decode_mfma(c, a, grid, s);
+    VC_LAUNCHED("decode_mfma_kernel");
+    return VC_OK;
+  }
   size_t lds = (static_cast<size_t>(H) * c->d + kDecTile * (c->d + 1) + kDecTile * c->d + H * kDecTile + 3 * H) *
                sizeof(float);
-  hipStream_t s = as_stream(stream);
   const bool quant = c->method == VC_QUANT_KIVI;
   const bool bf = c->kv_dtype == VC_BF16;
   const bool pbf = c->param_dtype == VC_BF16;

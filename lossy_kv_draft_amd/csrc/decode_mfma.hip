@@ -1,0 +1,522 @@
+// Draft-side decode attention over KIVI-quantized packed K/V on matrix cores.
+//
+// Summary page "VeriCache: Turning Lossy KV Cache into Lossless LLM Inference",
+// "What the paper found": drafting on the compressed cache is HBM-bandwidth-bound.
+// A scalar implementation of grouped-query decode is not: every code costs an
+// extract, a convert and an FMA per q-head, which on CDNA4 exceeds the vector ALU
+// budget long before HBM is saturated.  This kernel moves both contractions onto
+// v_mfma_f32_16x16x32_f16 and keeps the vector ALU work to turning codes into f16:
+//
+// * one wave processes 32-token blocks of one (sequence, kv-head); the q-heads that
+//   read the kv-head are the 16 columns of the B operand (zero beyond Hq/Hkv), so
+//   every packed row is read from HBM once for all of them;
+// * a code c becomes the f16 value 1024 + c by placing it under the exponent byte
+//   0x64 with one v_perm_b32 per pair of codes (the byte 0x64 is taken from a
+//   constant operand), then (x - 1024) * s + z is evaluated with packed f16 adds and
+//   FMAs, s and z being the group's scale and zero;
+// * S^T = K_hat Q^T for two 16-token tiles, online softmax per q-head in base 2 with
+//   a lazy rescale (only when the block maximum exceeds the running one by more than
+//   8, i.e. probabilities stay below 2^8), probabilities rounded to f16, then
+//   O^T += V_hat^T P^T.  The probabilities stay in the lanes that produced them: the
+//   S^T layout of two 16-token tiles is the B-operand layout of the 32-token P.V
+//   product once both operands enumerate the block's tokens in the same order;
+// * within an operand the order of the contraction index is free as long as both
+//   operands agree, so K channels and V tokens are enumerated in whatever order the
+//   byte permutes produce them (korder / vorder below);
+// * K's code row is read as 32-channel chunks (one 64/96/128-bit load per lane), V's
+//   as 8-channel fields of 8 tokens per lane; all loads of the next block are issued
+//   before the current block is computed and are only decoded when used;
+// * the 4 waves of a block cover consecutive token ranges and are merged in LDS; the
+//   block writes one partial per split, the tail rows are a split of their own, and
+//   the last block to finish merges all splits in split order.
+//
+// Precision: K_hat, V_hat, q and p are f16 (11-bit significands) with float32
+// accumulation; against float64 attention on the outlier workloads the error is
+// about 1e-4, far below the bf16 output resolution.  Values must lie within the f16
+// range (|x| < 65504).
+
+#include <type_traits>
+
+#include "decode_common.h"
+
+namespace vc {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kMagic = 0x64646464u;  // exponent byte of 1024.0 in f16, in every byte
+
+__device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
+__device__ __forceinline__ uint32_t as_u32(h2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+// pair of f16 values (1024 + c0, 1024 + c1) -> (c0 * s0 + z0, c1 * s1 + z1)
+__device__ __forceinline__ uint32_t dequant_pair(uint32_t magic, uint32_t s2, uint32_t z2) {
+  const h2_t off = {static_cast<_Float16>(-1024.f), static_cast<_Float16>(-1024.f)};
+  const h2_t c = as_h2(magic) + off;  // exact: small integers
+  return as_u32(__builtin_elementwise_fma(c, as_h2(s2), as_h2(z2)));
+}
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  h2_t h = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+  return as_u32(h);
+}
+
+// bytes [x.b_i, 0x64, x.b_j, 0x64]: the f16 pair (1024 + x.b_i, 1024 + x.b_j)
+__device__ __forceinline__ uint32_t magic_bytes(uint32_t x, uint32_t sel) { return __builtin_amdgcn_perm(kMagic, x, sel); }
+constexpr uint32_t kSel01 = 0x04010400u;  // bytes 0, 1
+constexpr uint32_t kSel23 = 0x04030402u;  // bytes 2, 3
+constexpr uint32_t kSel02 = 0x04020400u;  // bytes 0, 2
+constexpr uint32_t kSel13 = 0x04030401u;  // bytes 1, 3
+
+// Channel (within a lane's 8-channel k-step chunk) of contraction index j.
+template <int KB>
+__device__ __forceinline__ constexpr int korder(int j) {
+  if constexpr (KB == 4) return (j & 3) * 2 + (j >> 2);  // 0,2,4,6,1,3,5,7
+  else return (j & 1) ? (j >> 1) + 4 : (j >> 1);         // 0,4,1,5,2,6,3,7
+}
+
+// K: the four f16 magic pairs of k-step s from a lane's 32-channel chunk (KB words);
+// pair jj holds channels korder(2jj), korder(2jj+1).
+template <int KB>
+__device__ __forceinline__ void kpairs(const uint32_t* w, int s, uint32_t (&out)[4]) {
+  if constexpr (KB == 4) {
+    const uint32_t x = w[s];
+    const uint32_t lo = x & 0x0F0F0F0Fu;         // channels 0, 2, 4, 6
+    const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // channels 1, 3, 5, 7
+    out[0] = magic_bytes(lo, kSel01);
+    out[1] = magic_bytes(lo, kSel23);
+    out[2] = magic_bytes(hi, kSel01);
+    out[3] = magic_bytes(hi, kSel23);
+  } else if constexpr (KB == 2) {
+    const uint32_t x = w[s >> 1];
+    const uint32_t sel = (s & 1) ? kSel23 : kSel01;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t m = (x >> (2 * r)) & 0x03030303u;  // bytes: codes r, 4+r, 8+r, 12+r of the word
+      out[r] = magic_bytes(m, sel);
+    }
+  } else {  // 3 bits: 24-bit fields at bit 24 s of a 96-bit chunk
+    uint32_t f;
+    if (s == 0) f = w[0] & 0xFFFFFFu;
+    else if (s == 1) f = __builtin_amdgcn_alignbit(w[1], w[0], 24) & 0xFFFFFFu;
+    else if (s == 2) f = __builtin_amdgcn_alignbit(w[2], w[1], 16) & 0xFFFFFFu;
+    else f = w[2] >> 8;
+    const uint32_t u = (f & 0xFFFu) | ((f >> 12) << 16);  // codes 0..3 low half, 4..7 high half
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = ((u >> (3 * j)) & 0x00070007u) | 0x64006400u;
+  }
+}
+
+// Channel of V tile t for a field of VB-bit codes.
+template <int VB>
+__device__ __forceinline__ constexpr int vorder(int t) {
+  if constexpr (VB == 4) return (t & 3) * 2 + (t >> 2);  // 0,2,4,6,1,3,5,7
+  else if constexpr (VB == 2) return (t & 1) ? (t >> 1) + 4 : (t >> 1);
+  else return t;
+}
+
+// V: for two tokens' 8-code fields fa, fb, the f16 magic pair (token a, token b) of
+// each of the 8 channels, tile t holding channel vorder(t).
+template <int VB>
+__device__ __forceinline__ void vpairs(uint32_t fa, uint32_t fb, uint32_t (&out)[8]) {
+  if constexpr (VB == 4) {
+    const uint32_t la = fa & 0x0F0F0F0Fu, ha = (fa >> 4) & 0x0F0F0F0Fu;
+    const uint32_t lb = fb & 0x0F0F0F0Fu, hb = (fb >> 4) & 0x0F0F0F0Fu;
+    const uint32_t x0 = __builtin_amdgcn_perm(lb, la, 0x05010400u);  // a0 b0 a2 b2
+    const uint32_t x1 = __builtin_amdgcn_perm(lb, la, 0x07030602u);  // a4 b4 a6 b6
+    const uint32_t y0 = __builtin_amdgcn_perm(hb, ha, 0x05010400u);  // a1 b1 a3 b3
+    const uint32_t y1 = __builtin_amdgcn_perm(hb, ha, 0x07030602u);  // a5 b5 a7 b7
+    out[0] = magic_bytes(x0, kSel01);
+    out[1] = magic_bytes(x0, kSel23);
+    out[2] = magic_bytes(x1, kSel01);
+    out[3] = magic_bytes(x1, kSel23);
+    out[4] = magic_bytes(y0, kSel01);
+    out[5] = magic_bytes(y0, kSel23);
+    out[6] = magic_bytes(y1, kSel01);
+    out[7] = magic_bytes(y1, kSel23);
+  } else if constexpr (VB == 2) {
+    const uint32_t comb = (fa & 0xFFFFu) | (fb << 16);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t m = (comb >> (2 * r)) & 0x03030303u;  // a_r, a_{4+r}, b_r, b_{4+r}
+      out[2 * r] = magic_bytes(m, kSel02);
+      out[2 * r + 1] = magic_bytes(m, kSel13);
+    }
+  } else {
+    const uint32_t lo = (fa & 0xFFFu) | ((fb & 0xFFFu) << 16);
+    const uint32_t hi = ((fa >> 12) & 0xFFFu) | (((fb >> 12) & 0xFFFu) << 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      out[j] = ((lo >> (3 * j)) & 0x00070007u) | 0x64006400u;
+      out[j + 4] = ((hi >> (3 * j)) & 0x00070007u) | 0x64006400u;
+    }
+  }
+}
+
+// token of slot j (0..7) of lane group kb in a 32-token block
+__device__ __forceinline__ int slot_token(int kb, int j) { return j < 4 ? 4 * kb + j : 16 + 4 * kb + (j - 4); }
+
+template <typename P>
+__device__ __forceinline__ float param_f32(const P* p, int i) { return Elem<P>::load(p, i); }
+
+template <int KB, int VB, int NGV, typename P>
+__global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) {
+  constexpr int D = 128;
+  constexpr int G = D / NGV;                          // K: tokens per group; V: channels per group
+  constexpr int KW = D * KB / 32;                     // words per packed K row
+  constexpr int VW = D * VB / 32;
+  constexpr int VWR = VB == 3 ? 2 : 1;                // raw words per V field
+  constexpr int HW = D * static_cast<int>(sizeof(P)) / 4;  // words per K parameter row
+  constexpr int KPW = 2 * HW / 64;                    // K-parameter words per lane
+  constexpr int NKG = G >= 32 ? 1 : 2;                // K groups per 32-token block
+  __shared__ float sh_o[4][16][D];
+  __shared__ float sh_m[4][16], sh_l[4][16];
+  __shared__ uint32_t sh_kp[4][2 * HW];
+
+  const int split = blockIdx.x, bh = blockIdx.y;
+  if (split == a.splits - 1) {  // the full-precision tail rows form the last split
+    decode_tail_partial<bf16_t>(a, bh, split);
+    decode_finish<bf16_t>(a, bh);
+    return;
+  }
+  const int b = bh / a.Hkv, hk = bh % a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
+  const int n = lane & 15, kb = lane >> 4;
+  const int H = a.H;
+  const int main_len = static_cast<int>(dec_main_len(a, b));
+  const int wchunk = static_cast<int>(a.chunk / 4);
+  const int t_begin = split * static_cast<int>(a.chunk) + wave * wchunk;
+  const int t_end = min(main_len, t_begin + wchunk);
+
+  // queries as the B operand: column n = q-head n of this kv-head (0 beyond H),
+  // lane group kb holds channels 32 kb + 8 s + korder(j) for k-step s
+  h8_t bq[4];
+  {
+    const bf16_t* q = static_cast<const bf16_t*>(a.q) +
+                      (static_cast<int64_t>(b) * a.Hkv * H + hk * H + (n < H ? n : 0)) * D + 32 * kb;
+    const float qs = n < H ? a.qscale : 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 x = *reinterpret_cast<const uint4*>(q + 8 * s);
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};  // channels (0,1) (2,3) (4,5) (6,7)
+      float v[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[c] = __uint_as_float((c & 1) ? (w[c >> 1] & 0xFFFF0000u) : (w[c >> 1] << 16));
+      uint32_t pr[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) pr[jj] = pack_h2(v[korder<KB>(2 * jj)] * qs, v[korder<KB>(2 * jj + 1)] * qs);
+      bq[s] = __builtin_bit_cast(h8_t, pr);
+    }
+  }
+
+  // uniform bases of this (sequence, kv-head); per-lane 32-bit word offsets
+  const uint32_t* kcodes = a.k_codes + static_cast<int64_t>(bh) * a.capacity * KW;
+  const uint32_t* vcodes = a.v_codes + static_cast<int64_t>(bh) * a.capacity * VW;
+  const uint32_t* kscale = reinterpret_cast<const uint32_t*>(static_cast<const P*>(a.k_scale) +
+                                                             static_cast<int64_t>(bh) * (a.capacity / G) * D);
+  const uint32_t* kzero = reinterpret_cast<const uint32_t*>(static_cast<const P*>(a.k_zero) +
+                                                            static_cast<int64_t>(bh) * (a.capacity / G) * D);
+  const P* vscale = static_cast<const P*>(a.v_scale) + static_cast<int64_t>(bh) * a.capacity * NGV;
+  const P* vzero = static_cast<const P*>(a.v_zero) + static_cast<int64_t>(bh) * a.capacity * NGV;
+  const int gv = (8 * n) / G;  // V group of this lane's 8-channel field
+  const uint32_t vfw = VB == 4 ? n : (VB == 2 ? (n >> 1) : ((24 * n) >> 5));  // first word of field n
+  const uint32_t vfo = VB == 4 ? 0 : (VB == 2 ? 16 * (n & 1) : ((24 * n) & 31));  // its bit offset
+  const uint32_t vfw2 = (VB == 3 && vfw + 1 < VW) ? vfw + 1 : vfw;
+  const uint32_t k_lane = n * KW + kb * KB;
+
+  f4_t acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+  uint32_t ks2[4][4], kz2[4][4];
+  int g_cur = -1;
+
+  // Raw loads of one block, issued one block ahead of use and decoded only when used
+  // (arithmetic on a fresh load would make the wave wait for it).  This path
+  // requires the capacity to be a multiple of 32 rows, so every row of a block that
+  // starts before the end is inside the allocation; rows past the end are masked
+  // (scores -inf, V scale and zero 0), which keeps the loads branch-free.
+  struct Blk {
+    uint32_t kw[2][KB];
+    uint32_t vw[8][VWR];
+    uint32_t vs[8], vz[8];  // word holding the slot token's group-gv parameter
+    uint32_t kp[NKG][KPW];  // this lane's share of the block's K group parameters
+  };
+  auto load_blk = [&](int t0, Blk& x) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const uint32_t* src = kcodes + (static_cast<uint32_t>(t0 + 16 * tt) * KW + k_lane);
+      if constexpr (KB == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src);
+        x.kw[tt][0] = v.x; x.kw[tt][1] = v.y; x.kw[tt][2] = v.z; x.kw[tt][3] = v.w;
+      } else if constexpr (KB == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(src);
+        x.kw[tt][0] = v.x; x.kw[tt][1] = v.y;
+      } else {
+#pragma unroll
+        for (int i = 0; i < KB; ++i) x.kw[tt][i] = src[i];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t tok = static_cast<uint32_t>(t0 + slot_token(kb, j));
+      x.vw[j][0] = vcodes[tok * VW + vfw];
+      if constexpr (VB == 3) x.vw[j][1] = vcodes[tok * VW + vfw2];
+      if constexpr (sizeof(P) == 2) {
+        const uint32_t e = (tok * NGV + gv) >> 1;
+        x.vs[j] = reinterpret_cast<const uint32_t*>(vscale)[e];
+        x.vz[j] = reinterpret_cast<const uint32_t*>(vzero)[e];
+      } else {
+        x.vs[j] = reinterpret_cast<const uint32_t*>(vscale)[tok * NGV + gv];
+        x.vz[j] = reinterpret_cast<const uint32_t*>(vzero)[tok * NGV + gv];
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < NKG; ++gi) {
+      const uint32_t g = static_cast<uint32_t>((t0 + 16 * gi) / G);
+#pragma unroll
+      for (int i = 0; i < KPW; ++i) {
+        const uint32_t wi = lane * KPW + i;  // word of [scale row, zero row]
+        x.kp[gi][i] = wi < HW ? kscale[g * HW + wi] : kzero[g * HW + (wi - HW)];
+      }
+    }
+  };
+  // the (scale, zero) rows of a new K group: exchanged through LDS, then the lane's
+  // 32 channels are packed as f16 pairs in contraction order
+  auto use_kp = [&](const uint32_t* kp) {
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) sh_kp[wave][lane * KPW + i] = kp[i];
+    __builtin_amdgcn_wave_barrier();
+    const P* sp = reinterpret_cast<const P*>(&sh_kp[wave][0]) + 32 * kb;
+    const P* zp = sp + D;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float sv[8], zv[8];
+      if constexpr (sizeof(P) == 2) {
+        const uint4 xs = *reinterpret_cast<const uint4*>(sp + 8 * s);
+        const uint4 xz = *reinterpret_cast<const uint4*>(zp + 8 * s);
+        const uint32_t ws[4] = {xs.x, xs.y, xs.z, xs.w}, wz[4] = {xz.x, xz.y, xz.z, xz.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          sv[c] = __uint_as_float((c & 1) ? (ws[c >> 1] & 0xFFFF0000u) : (ws[c >> 1] << 16));
+          zv[c] = __uint_as_float((c & 1) ? (wz[c >> 1] & 0xFFFF0000u) : (wz[c >> 1] << 16));
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          sv[c] = param_f32<P>(sp, 8 * s + c);
+          zv[c] = param_f32<P>(zp, 8 * s + c);
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        ks2[s][jj] = pack_h2(sv[korder<KB>(2 * jj)], sv[korder<KB>(2 * jj + 1)]);
+        kz2[s][jj] = pack_h2(zv[korder<KB>(2 * jj)], zv[korder<KB>(2 * jj + 1)]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+  // V parameter (as float) of a slot token from its raw word
+  // (with one group per token the element parity is the slot's parity; otherwise the
+  // token index is even times NGV and the parity is the group's)
+  auto vparam = [&](uint32_t w, int j) -> float {
+    if constexpr (sizeof(P) == 2) {
+      const bool high = NGV == 1 ? (j & 1) : (gv & 1);
+      return __uint_as_float(high ? (w & 0xFFFF0000u) : (w << 16));
+    } else {
+      return __uint_as_float(w);
+    }
+  };
+
+  auto process = [&](int t0, const Blk& cur, auto full_tag) {
+    constexpr bool full = decltype(full_tag)::value;  // every row of the block is live
+    // ---- S^T = K_hat Q^T for the two 16-token tiles
+    f4_t sc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sc[tt] = f4_t{0.f, 0.f, 0.f, 0.f};
+      const int g = (t0 + 16 * tt) / G;
+      if (g != g_cur) {  // wave-uniform
+        use_kp(cur.kp[NKG == 1 ? 0 : tt]);
+        g_cur = g;
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint32_t mp[4], av[4];
+        kpairs<KB>(cur.kw[tt], s, mp);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) av[jj] = dequant_pair(mp[jj], ks2[s][jj], kz2[s][jj]);
+        sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, av), bq[s], sc[tt], 0, 0, 0);
+      }
+    }
+
+    // ---- online softmax of column n over tokens 16 tt + 4 kb + i
+    float s8[8];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s8[4 * tt + i] = (full || t0 + 16 * tt + 4 * kb + i < t_end) ? sc[tt][i] : -INFINITY;
+    float mb = fmaxf(fmaxf(fmaxf(s8[0], s8[1]), fmaxf(s8[2], s8[3])), fmaxf(fmaxf(s8[4], s8[5]), fmaxf(s8[6], s8[7])));
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    if (__any(mb > m + 8.f)) {
+      const float mn = fmaxf(m, mb);
+      const float al = __builtin_amdgcn_exp2f(m - mn);  // m = -inf on the first block: 0
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] *= al;
+      l *= al;
+      m = mn;
+    }
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[j] = __builtin_amdgcn_exp2f(s8[j] - m);  // v_exp_f32: results below 2^-126 flush to 0
+      l += p[j];
+    }
+    uint32_t pw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pw[j] = pack_h2(p[2 * j], p[2 * j + 1]);
+    const h8_t bp = __builtin_bit_cast(h8_t, pw);
+
+    // ---- O^T[8 (4 kb' + i) + vorder(t)][n] += V_hat^T P^T over the block's 32 tokens
+    uint32_t sv2[4], zv2[4], vp[4][8];
+#pragma unroll
+    for (int q2 = 0; q2 < 4; ++q2) {
+      const uint32_t ta = t0 + slot_token(kb, 2 * q2), tb = t0 + slot_token(kb, 2 * q2 + 1);
+      float sa = vparam(cur.vs[2 * q2], 2 * q2), sb = vparam(cur.vs[2 * q2 + 1], 2 * q2 + 1);
+      float za = vparam(cur.vz[2 * q2], 2 * q2), zb = vparam(cur.vz[2 * q2 + 1], 2 * q2 + 1);
+      if constexpr (!full) {  // rows past the end dequantize to exactly 0
+        const bool oka = static_cast<int>(ta) < t_end, okb = static_cast<int>(tb) < t_end;
+        sa = oka ? sa : 0.f; za = oka ? za : 0.f;
+        sb = okb ? sb : 0.f; zb = okb ? zb : 0.f;
+      }
+      sv2[q2] = pack_h2(sa, sb);
+      zv2[q2] = pack_h2(za, zb);
+      uint32_t fa, fb;
+      if constexpr (VB == 3) {
+        fa = __builtin_amdgcn_alignbit(cur.vw[2 * q2][VWR - 1], cur.vw[2 * q2][0], vfo) & 0xFFFFFFu;
+        fb = __builtin_amdgcn_alignbit(cur.vw[2 * q2 + 1][VWR - 1], cur.vw[2 * q2 + 1][0], vfo) & 0xFFFFFFu;
+      } else if constexpr (VB == 2) {
+        fa = cur.vw[2 * q2][0] >> vfo;
+        fb = cur.vw[2 * q2 + 1][0] >> vfo;
+      } else {
+        fa = cur.vw[2 * q2][0];
+        fb = cur.vw[2 * q2 + 1][0];
+      }
+      vpairs<VB>(fa, fb, vp[q2]);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint32_t av[4];
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) av[q2] = dequant_pair(vp[q2][t], sv2[q2], zv2[q2]);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, av), bp, acc[t], 0, 0, 0);
+    }
+  };
+
+  // Full blocks: two prefetch buffers in turn.  The prefetch is unconditional (the
+  // last full block re-loads itself) because a load issued on only one path makes the
+  // compiler wait for every outstanding load where the paths join.  The partial last
+  // block, if any, is loaded and processed once after the loop.
+  using Full = std::integral_constant<bool, true>;
+  using Part = std::integral_constant<bool, false>;
+  Blk bufA, bufB;
+  const int t_full = t_end > t_begin ? t_begin + ((t_end - t_begin) / 32) * 32 : t_begin;
+  if (t_full > t_begin) load_blk(t_begin, bufA);
+  for (int t0 = t_begin; t0 < t_full; t0 += 64) {
+    load_blk(t0 + 32 < t_full ? t0 + 32 : t0, bufB);
+    process(t0, bufA, Full{});
+    if (t0 + 32 >= t_full) break;
+    load_blk(t0 + 64 < t_full ? t0 + 64 : t0 + 32, bufA);
+    process(t0 + 32, bufB, Full{});
+  }
+  if (t_full < t_end) {
+    load_blk(t_full, bufA);
+    process(t_full, bufA, Part{});
+  }
+
+  // ---- merge the 4 waves in LDS, write this split's partial
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (kb == 0) {
+    sh_m[wave][n] = m;
+    sh_l[wave][n] = l;
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sh_o[wave][n][8 * (4 * kb + i) + vorder<VB>(t)] = acc[t][i];
+  __syncthreads();
+  const int64_t pbase = static_cast<int64_t>(bh) * a.splits + split;
+  for (int idx = tid; idx < H * D; idx += kDecThreads) {
+    const int h = idx / D, c = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sh_m[w][h]);
+    float O = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float wt = sh_m[w][h] == -INFINITY ? 0.f : exp2f(sh_m[w][h] - M);
+      O = fmaf(sh_o[w][h][c], wt, O);
+      L = fmaf(sh_l[w][h], wt, L);
+    }
+    a.part_o[(pbase * H + h) * D + c] = O;
+    if (c == 0) {
+      a.part_ml[(pbase * H + h) * 2] = M;
+      a.part_ml[(pbase * H + h) * 2 + 1] = L;
+    }
+  }
+  decode_finish<bf16_t>(a, bh);
+}
+
+// ------------------------------------------------------------------ dispatch
+
+bool decode_mfma_supported(const vc_ckv* c, int H) {
+  if (c->method != VC_QUANT_KIVI || c->kv_dtype != VC_BF16 || c->d != 128 || H < 1 || H > 16) return false;
+  auto ok_bits = [](int b) { return b == 2 || b == 3 || b == 4; };
+  if (!ok_bits(c->k_bits) || !ok_bits(c->v_bits)) return false;
+  if (c->capacity % 32 != 0 || c->capacity > (1ll << 26)) return false;
+  return c->group == 16 || c->group == 32 || c->group == 64 || c->group == 128;
+}
+
+int decode_mfma_splits(const vc_ckv* c) {
+  const int bh = c->B * c->Hkv;
+  int s = static_cast<int>(cdiv(512, bh));
+  if (s < 1) s = 1;
+  if (s > kDecMaxSplits - 1) s = kDecMaxSplits - 1;
+  return s + 1;  // + the tail split
+}
+
+template <int KB, int VB, typename P>
+static void launch_ngv(int ngv, dim3 grid, hipStream_t s, const DecodeArgs& a) {
+  switch (ngv) {
+    case 1: hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, 1, P>), grid, dim3(kDecThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, 2, P>), grid, dim3(kDecThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, 4, P>), grid, dim3(kDecThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, 8, P>), grid, dim3(kDecThreads), 0, s, a); break;
+  }
+}
+
+template <int KB, typename P>
+static void launch_vb(int vb, int ngv, dim3 grid, hipStream_t s, const DecodeArgs& a) {
+  if (vb == 2) launch_ngv<KB, 2, P>(ngv, grid, s, a);
+  else if (vb == 3) launch_ngv<KB, 3, P>(ngv, grid, s, a);
+  else launch_ngv<KB, 4, P>(ngv, grid, s, a);
+}
+
+void launch_decode_mfma(const vc_ckv* c, const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  const int ngv = 128 / c->group;
+  if (c->param_dtype == VC_BF16) {
+    if (c->k_bits == 2) launch_vb<2, bf16_t>(c->v_bits, ngv, grid, s, a);
+    else if (c->k_bits == 3) launch_vb<3, bf16_t>(c->v_bits, ngv, grid, s, a);
+    else launch_vb<4, bf16_t>(c->v_bits, ngv, grid, s, a);
+  } else {
+    if (c->k_bits == 2) launch_vb<2, float>(c->v_bits, ngv, grid, s, a);
+    else if (c->k_bits == 3) launch_vb<3, float>(c->v_bits, ngv, grid, s, a);
+    else launch_vb<4, float>(c->v_bits, ngv, grid, s, a);
+  }
+}
+
+}  // namespace vc
