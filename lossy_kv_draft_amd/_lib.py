@@ -62,6 +62,16 @@ _DECLS = {
     "vc_stage_full_kv_d2h": (c_i32, [c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i64, c_i64, c_i64, c_i64,
                                      c_p, c_p]),
     "vc_last_error": (ctypes.c_char_p, []),
+    # vc_model.h
+    "vc_gemm_bf16": (c_i32, [c_p, c_i64, c_p, c_i64, c_i64, c_i32, c_i32, c_p, c_i64, c_i32, c_p, c_p]),
+    "vc_rmsnorm": (c_i32, [c_p, c_p, c_i64, c_i32, c_f32, c_p, c_p]),
+    "vc_rope_qkv": (c_i32, [c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_p, c_p, c_p, c_p, c_i64, c_p, c_p]),
+    "vc_swiglu": (c_i32, [c_p, c_i64, c_i32, c_p, c_p]),
+    "vc_embed": (c_i32, [c_p, c_i32, c_i32, c_p, c_i64, c_p, c_p]),
+    "vc_heads_to_rows": (c_i32, [c_p, c_i32, c_i32, c_i32, c_i32, c_p, c_p]),
+    "vc_argmax_rows": (c_i32, [c_p, c_i64, c_i32, c_p, c_p]),
+    "vc_copy_kv_rows": (c_i32, [c_p, c_p, c_i64, c_p, c_p, c_p, c_i64, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                c_p]),
 }
 EXPORTS = tuple(_DECLS)
 for _n, (_r, _a) in _DECLS.items():
@@ -295,3 +305,50 @@ def vc_stage_full_kv_d2h(dev_k, dev_v, host_k, host_v, tok_begin, tok_end, *, co
                                     host_k.element_size(), host_rows, dev_k.shape[2], tok_begin, tok_end,
                                     _stream(copy_stream), None if done is None else done.cuda_event),
            "vc_stage_full_kv_d2h")
+
+
+# ---------------------------------------------------------------- vc_model.h
+
+def vc_gemm_bf16(A, W, C, *, R=None, stream=None):
+    """C[M, N] = A[M, K] @ W[N, K]^T (+ R); A, W bf16 2-D views with unit column stride."""
+    M, K = A.shape
+    N = W.shape[0]
+    _check(lib.vc_gemm_bf16(_ptr(A), A.stride(0), _ptr(W), W.stride(0), M, N, K, _ptr(C), C.stride(0),
+                            _dt(C.dtype), _ptr(R), _stream(stream)), "vc_gemm_bf16")
+
+
+def vc_rmsnorm(x, w, y, *, eps=1e-5, stream=None):
+    M, d = x.shape
+    _check(lib.vc_rmsnorm(_ptr(x), _ptr(w), M, d, eps, _ptr(y), _stream(stream)), "vc_rmsnorm")
+
+
+def vc_rope_qkv(qkv, B, k, Hq, Hkv, hd, pos, q_out, k_dst, v_dst, row0, *, theta=10000.0, stream=None):
+    _check(lib.vc_rope_qkv(_ptr(qkv), B, k, Hq, Hkv, hd, theta, _ptr(pos), _ptr(q_out), _ptr(k_dst), _ptr(v_dst),
+                           k_dst.shape[2], _ptr(row0), _stream(stream)), "vc_rope_qkv")
+
+
+def vc_swiglu(gu, out, *, stream=None):
+    M, F2 = gu.shape
+    _check(lib.vc_swiglu(_ptr(gu), M, F2 // 2, _ptr(out), _stream(stream)), "vc_swiglu")
+
+
+def vc_embed(E, tokens, x, *, stream=None):
+    V, d = E.shape
+    _check(lib.vc_embed(_ptr(E), V, d, _ptr(tokens), tokens.numel(), _ptr(x), _stream(stream)), "vc_embed")
+
+
+def vc_heads_to_rows(o, out, *, stream=None):
+    B, H, k, hd = o.shape
+    _check(lib.vc_heads_to_rows(_ptr(o), B, H, k, hd, _ptr(out), _stream(stream)), "vc_heads_to_rows")
+
+
+def vc_argmax_rows(logits, tokens, *, stream=None):
+    R, V = logits.shape
+    _check(lib.vc_argmax_rows(_ptr(logits), R, V, _ptr(tokens), _stream(stream)), "vc_argmax_rows")
+
+
+def vc_copy_kv_rows(src_k, src_v, src_row0, dst_k, dst_v, dst_row0, count, max_count, *, stream=None):
+    B, Hkv, src_rows, d = src_k.shape
+    _check(lib.vc_copy_kv_rows(_ptr(src_k), _ptr(src_v), src_rows, _ptr(src_row0), _ptr(dst_k), _ptr(dst_v),
+                               dst_k.shape[2], _ptr(dst_row0), _ptr(count), max_count, B, Hkv, d,
+                               src_k.element_size(), _stream(stream)), "vc_copy_kv_rows")

@@ -8,6 +8,7 @@
 #include <stdarg.h>
 
 #include "../../include/vc.h"
+#include "../../include/vc_model.h"
 
 namespace vc {
 

@@ -1,0 +1,344 @@
+// Decoder-layer kernels of the end-to-end draft-and-verify round (vc_model.h).
+//
+// The VeriCache pages ("VeriCache: Turning Lossy KV Cache into Lossless LLM
+// Inference", neuraltrendhub.com summary, "What the paper found") draft with the
+// target model on the compressed cache and verify with the same model on the full
+// cache; verified output must equal greedy full-KV decoding.  Exactness across the
+// two passes needs every kernel here to be batch invariant: an output row is a
+// function of its own input row only, computed in an order that does not depend on
+// how many rows are processed together.  This file is built without floating-point
+// contraction so that every template instantiation rounds identically.
+//
+// GEMM (weights streamed from HBM once per call): C = A W^T on
+// v_mfma_f32_16x16x32_bf16.  One 64-lane wave owns 16 output features (16 rows of
+// W, the MFMA A operand, read with 16-byte loads) and up to 8 16-row tiles of A (the
+// B operand); the k loop runs in ascending 32-wide steps for every tile size, so a
+// row's result is the same whether M is 1, 4 or 128.
+
+#include "common.h"
+
+namespace vc {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+union MP16 {
+  uint4 u;
+  bf16x8_t v;
+};
+
+template <int MT, bool CF32, bool RES>
+__global__ void __launch_bounds__(64) gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda,
+                                                       const bf16_t* __restrict__ W, int64_t ldw, int64_t M, int N,
+                                                       int K, void* __restrict__ C, int64_t ldc,
+                                                       const bf16_t* __restrict__ R) {
+  const int lane = threadIdx.x, nl = lane & 15, kb = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int64_t m_base = static_cast<int64_t>(blockIdx.y) * 16 * MT;
+  const int n = n0 + nl;
+  const bool n_ok = n < N;
+  const bf16_t* wrow = W + static_cast<int64_t>(n_ok ? n : N - 1) * ldw + 8 * kb;
+  const bf16_t* arow[MT];
+  bool m_ok[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int64_t m = m_base + 16 * t + nl;
+    m_ok[t] = m < M;
+    arow[t] = A + (m_ok[t] ? m : M - 1) * lda + 8 * kb;
+  }
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    MP16 a;
+    a.u = *reinterpret_cast<const uint4*>(wrow + k0);
+    if (!n_ok) a.u = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      MP16 b;
+      b.u = *reinterpret_cast<const uint4*>(arow[t] + k0);
+      if (!m_ok[t]) b.u = make_uint4(0, 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc[t], 0, 0, 0);
+    }
+  }
+  // acc[t][i] = C[m_base + 16 t + nl][n0 + 4 kb + i]
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    if (!m_ok[t]) continue;
+    const int64_t m = m_base + 16 * t + nl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int nn = n0 + 4 * kb + i;
+      if (nn >= N) continue;
+      float v = acc[t][i];
+      if constexpr (RES) v = v + bf16_to_f32(R[m * ldc + nn]);
+      if constexpr (CF32)
+        static_cast<float*>(C)[m * ldc + nn] = v;
+      else
+        static_cast<bf16_t*>(C)[m * ldc + nn] = f32_to_bf16(v);
+    }
+  }
+}
+
+// one block per row; fixed per-row reduction tree
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const bf16_t* x, const bf16_t* w, int d, float eps, bf16_t* y) {
+  __shared__ float part[4];
+  const int64_t r = blockIdx.x;
+  const bf16_t* xr = x + r * d;
+  float s = 0.f;
+  for (int j = threadIdx.x; j < d; j += 256) {
+    const float v = bf16_to_f32(xr[j]);
+    s = fmaf(v, v, s);
+  }
+  s = warp_sum(s);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+  const float inv = 1.0f / sqrtf(tot / static_cast<float>(d) + eps);
+  for (int j = threadIdx.x; j < d; j += 256) y[r * d + j] = f32_to_bf16(bf16_to_f32(xr[j]) * inv * bf16_to_f32(w[j]));
+}
+
+// one block per token row: rotary embedding of q and k, scatter of q, k, v
+__global__ void __launch_bounds__(256) rope_qkv_kernel(const bf16_t* qkv, int k, int Hq, int Hkv, int hd, float log2_theta,
+                                                       const int32_t* pos, bf16_t* q_out, bf16_t* k_dst, bf16_t* v_dst,
+                                                       int64_t dst_rows, const int32_t* row0) {
+  const int64_t r = blockIdx.x;
+  const int b = static_cast<int>(r / k), i = static_cast<int>(r % k);
+  const int half = hd / 2;
+  const int width = (Hq + 2 * Hkv) * hd;
+  const bf16_t* src = qkv + r * width;
+  const float p = static_cast<float>(pos[r]);
+  const int64_t krow = row0[b] + i;
+  const int rot_tasks = (Hq + Hkv) * half;
+  for (int t = threadIdx.x; t < rot_tasks + Hkv * hd; t += 256) {
+    if (t < rot_tasks) {
+      const int h = t / half, j = t % half;  // h < Hq: q head, else k head h - Hq
+      const float inv_freq = exp2f(-static_cast<float>(2 * j) / static_cast<float>(hd) * log2_theta);
+      float sn, cs;
+      sincosf(p * inv_freq, &sn, &cs);
+      const float x0 = bf16_to_f32(src[h * hd + j]), x1 = bf16_to_f32(src[h * hd + j + half]);
+      const float y0 = x0 * cs - x1 * sn;
+      const float y1 = x1 * cs + x0 * sn;
+      if (h < Hq) {
+        bf16_t* dst = q_out + ((static_cast<int64_t>(b) * Hq + h) * k + i) * hd;
+        dst[j] = f32_to_bf16(y0);
+        dst[j + half] = f32_to_bf16(y1);
+      } else {
+        bf16_t* dst = k_dst + ((static_cast<int64_t>(b) * Hkv + (h - Hq)) * dst_rows + krow) * hd;
+        dst[j] = f32_to_bf16(y0);
+        dst[j + half] = f32_to_bf16(y1);
+      }
+    } else {
+      const int e = t - rot_tasks, h = e / hd, c = e % hd;
+      v_dst[((static_cast<int64_t>(b) * Hkv + h) * dst_rows + krow) * hd + c] = src[(Hq + Hkv + h) * hd + c];
+    }
+  }
+}
+
+__global__ void swiglu_kernel(const bf16_t* gu, int64_t M, int F, bf16_t* out) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= M * F) return;
+  const int64_t m = e / F;
+  const int j = static_cast<int>(e % F);
+  const float g = bf16_to_f32(gu[m * 2 * F + j]);
+  const float u = bf16_to_f32(gu[m * 2 * F + F + j]);
+  out[e] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+}
+
+__global__ void embed_kernel(const uint4* E, int row_vecs, const int32_t* tokens, int64_t M, uint4* x) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= M * row_vecs) return;
+  const int64_t m = e / row_vecs;
+  const int c = static_cast<int>(e % row_vecs);
+  x[e] = E[static_cast<int64_t>(tokens[m]) * row_vecs + c];
+}
+
+__global__ void heads_to_rows_kernel(const bf16_t* o, int H, int k, int hd, int64_t total, bf16_t* out) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= total) return;
+  const int c = static_cast<int>(e % hd);
+  int64_t t = e / hd;
+  const int h = static_cast<int>(t % H);
+  t /= H;  // t = b * k + i
+  const int64_t b = t / k, i = t % k;
+  out[e] = o[((b * H + h) * k + i) * hd + c];
+}
+
+__device__ __forceinline__ bool better_idx(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+
+__global__ void __launch_bounds__(256) argmax_rows_kernel(const float* logits, int V, int32_t* tok) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int64_t r = blockIdx.x;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int v = threadIdx.x; v < V; v += 256) {
+    const float x = logits[r * V + v];
+    if (better_idx(x, v, bv, bi)) { bv = x; bi = v; }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    if (better_idx(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = bv; si[threadIdx.x >> 6] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (better_idx(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
+    tok[r] = bi == 0x7fffffff ? 0 : bi;
+  }
+}
+
+__global__ void copy_kv_rows_kernel(const uint4* sk, const uint4* sv, int64_t src_rows, const int32_t* src_row0,
+                                    uint4* dk, uint4* dv, int64_t dst_rows, const int32_t* dst_row0,
+                                    const int32_t* count, int Hkv, int row_vecs, int max_count) {
+  const int bh = blockIdx.y;
+  const int b = bh / Hkv;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= static_cast<int64_t>(max_count) * row_vecs) return;
+  const int j = static_cast<int>(e / row_vecs), c = static_cast<int>(e % row_vecs);
+  if (j >= count[b]) return;
+  const int64_t s = (static_cast<int64_t>(bh) * src_rows + src_row0[b] + j) * row_vecs + c;
+  const int64_t t = (static_cast<int64_t>(bh) * dst_rows + dst_row0[b] + j) * row_vecs + c;
+  dk[t] = sk[s];
+  dv[t] = sv[s];
+}
+
+}  // namespace vc
+
+using namespace vc;
+
+template <int MT>
+static void launch_gemm(bool cf32, bool res, dim3 grid, hipStream_t s, const bf16_t* A, int64_t lda, const bf16_t* W,
+                        int64_t ldw, int64_t M, int N, int K, void* C, int64_t ldc, const bf16_t* R) {
+  if (cf32)
+    hipLaunchKernelGGL((gemm_bf16_kernel<MT, true, false>), grid, dim3(64), 0, s, A, lda, W, ldw, M, N, K, C, ldc, R);
+  else if (res)
+    hipLaunchKernelGGL((gemm_bf16_kernel<MT, false, true>), grid, dim3(64), 0, s, A, lda, W, ldw, M, N, K, C, ldc, R);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<MT, false, false>), grid, dim3(64), 0, s, A, lda, W, ldw, M, N, K, C, ldc, R);
+}
+
+extern "C" vc_status vc_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, int64_t M, int32_t N,
+                                  int32_t K, void* C, int64_t ldc, int32_t c_dtype, const void* R, void* stream) {
+  clear_error();
+  VC_REQUIRE(A && W && C, "A / W / C is NULL");
+  VC_REQUIRE(M > 0 && N > 0 && K > 0, "bad shape (M %lld, N %d, K %d)", (long long)M, N, K);
+  VC_REQUIRE(K % 32 == 0, "K must be a multiple of 32 (got %d)", K);
+  VC_REQUIRE(lda >= K && ldw >= K && ldc >= N, "leading dimensions too small");
+  VC_REQUIRE(lda % 8 == 0 && ldw % 8 == 0, "lda and ldw must be multiples of 8 elements");
+  VC_REQUIRE(valid_dtype(c_dtype), "bad c_dtype");
+  VC_REQUIRE(R == nullptr || c_dtype == VC_BF16, "a residual needs a bf16 output");
+  const int64_t mt_rows = M >= 128 ? 128 : ((M + 15) / 16) * 16;
+  const int MT = static_cast<int>(mt_rows / 16);
+  dim3 grid(static_cast<unsigned>(cdiv(N, 16)), static_cast<unsigned>(cdiv(M, mt_rows)));
+  hipStream_t s = as_stream(stream);
+  const bf16_t* a = static_cast<const bf16_t*>(A);
+  const bf16_t* w = static_cast<const bf16_t*>(W);
+  const bf16_t* r = static_cast<const bf16_t*>(R);
+  const bool cf = c_dtype == VC_F32, res = R != nullptr;
+  switch (MT) {
+    case 1: launch_gemm<1>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+    case 2: launch_gemm<2>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+    case 3: launch_gemm<3>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+    case 4: launch_gemm<4>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+    case 5: launch_gemm<5>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+    case 6: launch_gemm<6>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+    case 7: launch_gemm<7>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+    default: launch_gemm<8>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+  }
+  VC_LAUNCHED("gemm_bf16_kernel");
+  return VC_OK;
+}
+
+extern "C" vc_status vc_rmsnorm(const void* x, const void* w, int64_t M, int32_t d, float eps, void* y, void* stream) {
+  clear_error();
+  VC_REQUIRE(x && w && y, "x / w / y is NULL");
+  VC_REQUIRE(M > 0 && d > 0, "bad shape");
+  VC_REQUIRE(eps > 0.f, "eps must be positive");
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(static_cast<unsigned>(M)), dim3(256), 0, as_stream(stream),
+                     static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w), d, eps, static_cast<bf16_t*>(y));
+  VC_LAUNCHED("rmsnorm_kernel");
+  return VC_OK;
+}
+
+extern "C" vc_status vc_rope_qkv(const void* qkv, int32_t B, int32_t k, int32_t Hq, int32_t Hkv, int32_t hd,
+                                 float theta, const int32_t* pos, void* q_out, void* k_dst, void* v_dst,
+                                 int64_t dst_rows, const int32_t* row0, void* stream) {
+  clear_error();
+  VC_REQUIRE(qkv && pos && q_out && k_dst && v_dst && row0, "NULL pointer argument");
+  VC_REQUIRE(B > 0 && k > 0 && Hq > 0 && Hkv > 0 && hd > 0 && hd % 2 == 0, "bad shape");
+  VC_REQUIRE(theta > 1.f, "theta must exceed 1");
+  VC_REQUIRE(dst_rows >= k, "dst_rows must hold at least k rows");
+  hipLaunchKernelGGL(rope_qkv_kernel, dim3(static_cast<unsigned>(B * k)), dim3(256), 0, as_stream(stream),
+                     static_cast<const bf16_t*>(qkv), k, Hq, Hkv, hd, log2f(theta), pos, static_cast<bf16_t*>(q_out),
+                     static_cast<bf16_t*>(k_dst), static_cast<bf16_t*>(v_dst), dst_rows, row0);
+  VC_LAUNCHED("rope_qkv_kernel");
+  return VC_OK;
+}
+
+extern "C" vc_status vc_swiglu(const void* gu, int64_t M, int32_t F, void* out, void* stream) {
+  clear_error();
+  VC_REQUIRE(gu && out, "NULL pointer argument");
+  VC_REQUIRE(M > 0 && F > 0, "bad shape");
+  hipLaunchKernelGGL(swiglu_kernel, dim3(static_cast<unsigned>(cdiv(M * F, 256))), dim3(256), 0, as_stream(stream),
+                     static_cast<const bf16_t*>(gu), M, F, static_cast<bf16_t*>(out));
+  VC_LAUNCHED("swiglu_kernel");
+  return VC_OK;
+}
+
+extern "C" vc_status vc_embed(const void* E, int32_t V, int32_t d, const int32_t* tokens, int64_t M, void* x,
+                              void* stream) {
+  clear_error();
+  VC_REQUIRE(E && tokens && x, "NULL pointer argument");
+  VC_REQUIRE(V > 0 && d > 0 && M > 0, "bad shape");
+  VC_UNSUPPORTED(d % 8 == 0, "d must be a multiple of 8");
+  const int rv = d / 8;
+  hipLaunchKernelGGL(embed_kernel, dim3(static_cast<unsigned>(cdiv(M * rv, 256))), dim3(256), 0, as_stream(stream),
+                     static_cast<const uint4*>(E), rv, tokens, M, static_cast<uint4*>(x));
+  VC_LAUNCHED("embed_kernel");
+  return VC_OK;
+}
+
+extern "C" vc_status vc_heads_to_rows(const void* o, int32_t B, int32_t H, int32_t k, int32_t hd, void* out,
+                                      void* stream) {
+  clear_error();
+  VC_REQUIRE(o && out, "NULL pointer argument");
+  VC_REQUIRE(B > 0 && H > 0 && k > 0 && hd > 0, "bad shape");
+  const int64_t total = static_cast<int64_t>(B) * H * k * hd;
+  hipLaunchKernelGGL(heads_to_rows_kernel, dim3(static_cast<unsigned>(cdiv(total, 256))), dim3(256), 0,
+                     as_stream(stream), static_cast<const bf16_t*>(o), H, k, hd, total, static_cast<bf16_t*>(out));
+  VC_LAUNCHED("heads_to_rows_kernel");
+  return VC_OK;
+}
+
+extern "C" vc_status vc_argmax_rows(const float* logits, int64_t R, int32_t V, int32_t* tokens, void* stream) {
+  clear_error();
+  VC_REQUIRE(logits && tokens, "NULL pointer argument");
+  VC_REQUIRE(R > 0 && V > 0, "bad shape");
+  hipLaunchKernelGGL(argmax_rows_kernel, dim3(static_cast<unsigned>(R)), dim3(256), 0, as_stream(stream), logits, V,
+                     tokens);
+  VC_LAUNCHED("argmax_rows_kernel");
+  return VC_OK;
+}
+
+extern "C" vc_status vc_copy_kv_rows(const void* src_k, const void* src_v, int64_t src_rows, const int32_t* src_row0,
+                                     void* dst_k, void* dst_v, int64_t dst_rows, const int32_t* dst_row0,
+                                     const int32_t* count, int32_t max_count, int32_t B, int32_t Hkv, int32_t d,
+                                     int32_t elem_bytes, void* stream) {
+  clear_error();
+  VC_REQUIRE(src_k && src_v && dst_k && dst_v && src_row0 && dst_row0 && count, "NULL pointer argument");
+  VC_REQUIRE(B > 0 && Hkv > 0 && d > 0 && max_count >= 0, "bad shape");
+  VC_REQUIRE(elem_bytes == 2 || elem_bytes == 4, "elem_bytes must be 2 or 4");
+  VC_UNSUPPORTED((static_cast<int64_t>(d) * elem_bytes) % 16 == 0, "rows must be a multiple of 16 bytes");
+  if (max_count == 0) return VC_OK;
+  const int rv = static_cast<int>(static_cast<int64_t>(d) * elem_bytes / 16);
+  dim3 grid(static_cast<unsigned>(cdiv(static_cast<int64_t>(max_count) * rv, 256)), static_cast<unsigned>(B * Hkv));
+  hipLaunchKernelGGL(copy_kv_rows_kernel, grid, dim3(256), 0, as_stream(stream), static_cast<const uint4*>(src_k),
+                     static_cast<const uint4*>(src_v), src_rows, src_row0, static_cast<uint4*>(dst_k),
+                     static_cast<uint4*>(dst_v), dst_rows, dst_row0, count, Hkv, rv, max_count);
+  VC_LAUNCHED("copy_kv_rows_kernel");
+  return VC_OK;
+}

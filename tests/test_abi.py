@@ -10,11 +10,11 @@ import torch
 
 import lossy_kv_draft_amd as L
 
-HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "vc.h")
+INC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
 
 
 def declared():
-    text = open(HDR).read()
+    text = "".join(open(os.path.join(INC, f)).read() for f in sorted(os.listdir(INC)) if f.endswith(".h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return set(re.findall(r"\b(vc_\w+)\s*\(", text))
 
