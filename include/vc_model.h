@@ -48,7 +48,8 @@ vc_status vc_rmsnorm(const void* x, const void* w, int64_t M, int32_t d, float e
  * head are rotated by pos * theta^(-2j/hd) (float32 angle, float64-accurate sin/cos
  * not required).  Outputs: q_out bf16 [B, Hq, k, hd]; the (rotated) k and the v parts
  * are written to rows row0[b] + i of k_dst, v_dst bf16 [B, Hkv, dst_rows, hd]
- * (row0 int32 [B], device).  Every row0[b] + k must be <= dst_rows. */
+ * (row0 int32 [B], device).  Every row0[b] + k must be <= dst_rows; the kernel
+ * skips key/value rows that fall outside [0, dst_rows) rather than write them. */
 vc_status vc_rope_qkv(const void* qkv, int32_t B, int32_t k, int32_t Hq, int32_t Hkv, int32_t hd, float theta,
                       const int32_t* pos, void* q_out, void* k_dst, void* v_dst, int64_t dst_rows,
                       const int32_t* row0, void* stream);
@@ -56,7 +57,8 @@ vc_status vc_rope_qkv(const void* qkv, int32_t B, int32_t k, int32_t Hq, int32_t
 /* out[m][j] = silu(gu[m][j]) * gu[m][F + j], gu bf16 [M, 2F], out bf16 [M, F]. */
 vc_status vc_swiglu(const void* gu, int64_t M, int32_t F, void* out, void* stream);
 
-/* x[m] = E[tokens[m]], E bf16 [V, d], tokens int32 [M] (each in [0, V)), x bf16 [M, d]. */
+/* x[m] = E[tokens[m]], E bf16 [V, d], tokens int32 [M] (each in [0, V); a row whose
+ * token is outside that range is written as zeros), x bf16 [M, d]. */
 vc_status vc_embed(const void* E, int32_t V, int32_t d, const int32_t* tokens, int64_t M, void* x, void* stream);
 
 /* [B, H, k, hd] -> [B*k, H*hd] (bf16): attention output rows for the next projection. */
@@ -69,8 +71,9 @@ vc_status vc_argmax_rows(const float* logits, int64_t R, int32_t V, int32_t* tok
  * per element, 16-byte multiple rows): for each sequence b, rows
  * [src_row0[b], src_row0[b] + count[b]) of src_k/src_v go to rows
  * [dst_row0[b], dst_row0[b] + count[b]) of dst_k/dst_v.  src_row0, dst_row0, count
- * int32 [B] (device); count[b] <= max_count; all rows must lie in their caches.
- * Source and destination ranges must not overlap. */
+ * int32 [B] (device); count[b] <= max_count (rows past max_count are not copied);
+ * all rows must lie in their caches (the kernel skips rows that do not).  Source
+ * and destination ranges must not overlap. */
 vc_status vc_copy_kv_rows(const void* src_k, const void* src_v, int64_t src_rows, const int32_t* src_row0,
                           void* dst_k, void* dst_v, int64_t dst_rows, const int32_t* dst_row0,
                           const int32_t* count, int32_t max_count, int32_t B, int32_t Hkv, int32_t d,

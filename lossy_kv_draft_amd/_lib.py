@@ -1,4 +1,5 @@
 """ctypes declarations of include/vc.h and thin wrappers taking torch tensors."""
+import copy
 import ctypes
 import os
 
@@ -155,6 +156,16 @@ class Ckv:
                       _ptr(self.k_codes), _ptr(self.v_codes), _ptr(self.k_scale), _ptr(self.k_zero),
                       _ptr(self.v_scale), _ptr(self.v_zero), _ptr(self.k_kept), _ptr(self.v_kept),
                       _ptr(self.kept_idx), _ptr(self.tail_k), _ptr(self.tail_v), self.tail_cap, self.tail_len)
+
+    def batch_view(self, b: int) -> "Ckv":
+        """Descriptor of sequence b alone (B = 1) over the same device storage."""
+        v = copy.copy(self)
+        v.B = 1
+        for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero", "k_kept", "v_kept", "kept_idx",
+                     "tail_k", "tail_v"):
+            t = getattr(self, name)
+            setattr(v, name, None if t is None else t[b:b + 1])
+        return v
 
     def stored_bytes(self, n_main=None) -> int:
         """Bytes of the compressed rows [0, n_main) over all sequences and heads."""

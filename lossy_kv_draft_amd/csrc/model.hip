@@ -30,8 +30,8 @@ union MP16 {
 template <int MT, bool CF32, bool RES>
 __global__ void __launch_bounds__(64) gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda,
                                                        const bf16_t* __restrict__ W, int64_t ldw, int64_t M, int N,
-                                                       int K, void* __restrict__ C, int64_t ldc,
-                                                       const bf16_t* __restrict__ R) {
+                                                       int K, void* C, int64_t ldc,
+                                                       const bf16_t* R) {  // C may alias R
   const int lane = threadIdx.x, nl = lane & 15, kb = lane >> 4;
   const int n0 = blockIdx.x * 16;
   const int64_t m_base = static_cast<int64_t>(blockIdx.y) * 16 * MT;
@@ -109,7 +109,8 @@ __global__ void __launch_bounds__(256) rope_qkv_kernel(const bf16_t* qkv, int k,
   const int width = (Hq + 2 * Hkv) * hd;
   const bf16_t* src = qkv + r * width;
   const float p = static_cast<float>(pos[r]);
-  const int64_t krow = row0[b] + i;
+  const int64_t krow = static_cast<int64_t>(row0[b]) + i;
+  const bool kv_in = krow >= 0 && krow < dst_rows;  // rows outside the cache are not written
   const int rot_tasks = (Hq + Hkv) * half;
   for (int t = threadIdx.x; t < rot_tasks + Hkv * hd; t += 256) {
     if (t < rot_tasks) {
@@ -124,12 +125,12 @@ __global__ void __launch_bounds__(256) rope_qkv_kernel(const bf16_t* qkv, int k,
         bf16_t* dst = q_out + ((static_cast<int64_t>(b) * Hq + h) * k + i) * hd;
         dst[j] = f32_to_bf16(y0);
         dst[j + half] = f32_to_bf16(y1);
-      } else {
+      } else if (kv_in) {
         bf16_t* dst = k_dst + ((static_cast<int64_t>(b) * Hkv + (h - Hq)) * dst_rows + krow) * hd;
         dst[j] = f32_to_bf16(y0);
         dst[j + half] = f32_to_bf16(y1);
       }
-    } else {
+    } else if (kv_in) {
       const int e = t - rot_tasks, h = e / hd, c = e % hd;
       v_dst[((static_cast<int64_t>(b) * Hkv + h) * dst_rows + krow) * hd + c] = src[(Hq + Hkv + h) * hd + c];
     }
@@ -146,12 +147,13 @@ __global__ void swiglu_kernel(const bf16_t* gu, int64_t M, int F, bf16_t* out) {
   out[e] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
 }
 
-__global__ void embed_kernel(const uint4* E, int row_vecs, const int32_t* tokens, int64_t M, uint4* x) {
+__global__ void embed_kernel(const uint4* E, int V, int row_vecs, const int32_t* tokens, int64_t M, uint4* x) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (e >= M * row_vecs) return;
   const int64_t m = e / row_vecs;
   const int c = static_cast<int>(e % row_vecs);
-  x[e] = E[static_cast<int64_t>(tokens[m]) * row_vecs + c];
+  const int t = tokens[m];
+  x[e] = (t >= 0 && t < V) ? E[static_cast<int64_t>(t) * row_vecs + c] : make_uint4(0, 0, 0, 0);
 }
 
 __global__ void heads_to_rows_kernel(const bf16_t* o, int H, int k, int hd, int64_t total, bf16_t* out) {
@@ -200,8 +202,10 @@ __global__ void copy_kv_rows_kernel(const uint4* sk, const uint4* sv, int64_t sr
   if (e >= static_cast<int64_t>(max_count) * row_vecs) return;
   const int j = static_cast<int>(e / row_vecs), c = static_cast<int>(e % row_vecs);
   if (j >= count[b]) return;
-  const int64_t s = (static_cast<int64_t>(bh) * src_rows + src_row0[b] + j) * row_vecs + c;
-  const int64_t t = (static_cast<int64_t>(bh) * dst_rows + dst_row0[b] + j) * row_vecs + c;
+  const int64_t sr = static_cast<int64_t>(src_row0[b]) + j, dr = static_cast<int64_t>(dst_row0[b]) + j;
+  if (sr < 0 || sr >= src_rows || dr < 0 || dr >= dst_rows) return;  // rows outside a cache are skipped
+  const int64_t s = (static_cast<int64_t>(bh) * src_rows + sr) * row_vecs + c;
+  const int64_t t = (static_cast<int64_t>(bh) * dst_rows + dr) * row_vecs + c;
   dk[t] = sk[s];
   dv[t] = sv[s];
 }
@@ -209,6 +213,8 @@ __global__ void copy_kv_rows_kernel(const uint4* sk, const uint4* sv, int64_t sr
 }  // namespace vc
 
 using namespace vc;
+
+static bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
 template <int MT>
 static void launch_gemm(bool cf32, bool res, dim3 grid, hipStream_t s, const bf16_t* A, int64_t lda, const bf16_t* W,
@@ -229,6 +235,7 @@ extern "C" vc_status vc_gemm_bf16(const void* A, int64_t lda, const void* W, int
   VC_REQUIRE(K % 32 == 0, "K must be a multiple of 32 (got %d)", K);
   VC_REQUIRE(lda >= K && ldw >= K && ldc >= N, "leading dimensions too small");
   VC_REQUIRE(lda % 8 == 0 && ldw % 8 == 0, "lda and ldw must be multiples of 8 elements");
+  VC_REQUIRE(aligned16(A) && aligned16(W), "A and W must be 16-byte aligned");
   VC_REQUIRE(valid_dtype(c_dtype), "bad c_dtype");
   VC_REQUIRE(R == nullptr || c_dtype == VC_BF16, "a residual needs a bf16 output");
   const int64_t mt_rows = M >= 128 ? 128 : ((M + 15) / 16) * 16;
@@ -295,9 +302,10 @@ extern "C" vc_status vc_embed(const void* E, int32_t V, int32_t d, const int32_t
   VC_REQUIRE(E && tokens && x, "NULL pointer argument");
   VC_REQUIRE(V > 0 && d > 0 && M > 0, "bad shape");
   VC_UNSUPPORTED(d % 8 == 0, "d must be a multiple of 8");
+  VC_REQUIRE(aligned16(E) && aligned16(x), "E and x must be 16-byte aligned");
   const int rv = d / 8;
   hipLaunchKernelGGL(embed_kernel, dim3(static_cast<unsigned>(cdiv(M * rv, 256))), dim3(256), 0, as_stream(stream),
-                     static_cast<const uint4*>(E), rv, tokens, M, static_cast<uint4*>(x));
+                     static_cast<const uint4*>(E), V, rv, tokens, M, static_cast<uint4*>(x));
   VC_LAUNCHED("embed_kernel");
   return VC_OK;
 }
@@ -333,6 +341,8 @@ extern "C" vc_status vc_copy_kv_rows(const void* src_k, const void* src_v, int64
   VC_REQUIRE(B > 0 && Hkv > 0 && d > 0 && max_count >= 0, "bad shape");
   VC_REQUIRE(elem_bytes == 2 || elem_bytes == 4, "elem_bytes must be 2 or 4");
   VC_UNSUPPORTED((static_cast<int64_t>(d) * elem_bytes) % 16 == 0, "rows must be a multiple of 16 bytes");
+  VC_REQUIRE(aligned16(src_k) && aligned16(src_v) && aligned16(dst_k) && aligned16(dst_v),
+             "caches must be 16-byte aligned");
   if (max_count == 0) return VC_OK;
   const int rv = static_cast<int>(static_cast<int64_t>(d) * elem_bytes / 16);
   dim3 grid(static_cast<unsigned>(cdiv(static_cast<int64_t>(max_count) * rv, 256)), static_cast<unsigned>(B * Hkv));

@@ -1,0 +1,369 @@
+"""End-to-end draft-and-verify rounds of a decoder on one GPU, sequencing the
+library's kernels (every arithmetic step runs in libvc.so; this module only issues
+calls, keeps lengths and owns device/pinned memory through torch).
+
+The round follows "VeriCache: Turning Lossy KV Cache into Lossless LLM Inference"
+(neuraltrendhub.com summary, "What the paper found" and "Original abstract"):
+  * the full KV cache of every layer lives in pinned host memory and is staged to the
+    device layer by layer on a side stream while the model drafts k tokens on the
+    compressed (KIVI-quantized) cache;
+  * the k-row window [last committed token, d_1 .. d_{k-1}] is verified against the
+    full cache; the longest prefix on which drafts and greedy targets agree is
+    committed, plus the target at the first disagreement;
+  * the verified rows' keys/values are appended to the host full cache and to the
+    compressed cache's tail; whole groups of the tail are quantized into the
+    compressed part.
+Greedy full-KV decoding with the same kernels is the reference the output must equal.
+"""
+from dataclasses import dataclass
+import numpy as np
+import torch
+
+from . import _lib as L
+
+BF16 = torch.bfloat16
+
+
+@dataclass
+class ModelShape:
+    layers: int
+    d_model: int
+    Hq: int
+    Hkv: int
+    hd: int
+    ffn: int
+    vocab: int
+    theta: float = 10000.0
+    eps: float = 1e-5
+
+
+class DecoderGPU:
+    """Random-initialised Llama-style decoder: bf16 weights on the device."""
+
+    def __init__(self, shape: ModelShape, weights: dict, max_rows: int, device="cuda"):
+        self.s = shape
+        self.w = weights
+        self.dev = device
+        s = shape
+        z = dict(device=device, dtype=BF16)
+        self.max_rows = max_rows
+        self.x = torch.empty(max_rows, s.d_model, **z)
+        self.h = torch.empty(max_rows, s.d_model, **z)
+        self.qkv = torch.empty(max_rows, (s.Hq + 2 * s.Hkv) * s.hd, **z)
+        self.q = torch.empty(max_rows * s.Hq * s.hd, **z)
+        self.attn = torch.empty(max_rows * s.Hq * s.hd, **z)
+        self.rows = torch.empty(max_rows, s.Hq * s.hd, **z)
+        self.gu = torch.empty(max_rows, 2 * s.ffn, **z)
+        self.act = torch.empty(max_rows, s.ffn, **z)
+        self.logits = torch.empty(max_rows, s.vocab, device=device, dtype=torch.float32)
+
+    def forward(self, tokens, B, k, attend, head=True):
+        """tokens: int32 [B*k] (row b*k + i = token i of sequence b).  attend(l, M)
+        runs layer l's attention on self.qkv[:M] and leaves its output as rows
+        [M, Hq*hd] in self.rows[:M].  Returns float32 logits [M, vocab] (a view of
+        self.logits), or None when head is False (prompt chunks)."""
+        s, w = self.s, self.w
+        M = B * k
+        x, h = self.x[:M], self.h[:M]
+        L.vc_embed(w["E"], tokens, x)
+        for l in range(s.layers):
+            L.vc_rmsnorm(x, w["n1"][l], h, eps=s.eps)
+            L.vc_gemm_bf16(h, w["wqkv"][l], self.qkv[:M])
+            attend(l, M)
+            L.vc_gemm_bf16(self.rows[:M], w["wo"][l], x, R=x)
+            L.vc_rmsnorm(x, w["n2"][l], h, eps=s.eps)
+            L.vc_gemm_bf16(h, w["wgu"][l], self.gu[:M])
+            L.vc_swiglu(self.gu[:M], self.act[:M])
+            L.vc_gemm_bf16(self.act[:M], w["wd"][l], x, R=x)
+        if not head:
+            return None
+        L.vc_rmsnorm(x, w["nf"], h, eps=s.eps)
+        L.vc_gemm_bf16(h, w["head"], self.logits[:M])
+        return self.logits[:M]
+
+
+def _i32(x, device):
+    return torch.as_tensor(np.asarray(x, dtype=np.int32), device=device)
+
+
+class FullCache:
+    """Per-layer device full KV [B, Hkv, rows, hd] (bf16)."""
+
+    def __init__(self, shape: ModelShape, B, rows, device="cuda"):
+        self.k = [torch.zeros(B, shape.Hkv, rows, shape.hd, dtype=BF16, device=device) for _ in range(shape.layers)]
+        self.v = [torch.zeros_like(t) for t in self.k]
+        self.rows = rows
+
+
+def attend_full(dec: DecoderGPU, cache: FullCache, B, k, pos, row0, ctx_len, ctx_lens, split_tokens, ws,
+                wait_events=None):
+    """Attention callback: rotary + scatter of the rows' keys/values into the full
+    cache at rows row0[b] + i, then causal verify attention over [0, row0[b] + i]."""
+    s = dec.s
+
+    def attend(l, M):
+        if wait_events is not None:
+            torch.cuda.current_stream().wait_event(wait_events[l])
+        q = dec.q[: M * s.Hq * s.hd].view(B, s.Hq, k, s.hd)
+        L.vc_rope_qkv(dec.qkv[:M], B, k, s.Hq, s.Hkv, s.hd, pos, q, cache.k[l], cache.v[l], row0, theta=s.theta)
+        out = dec.attn[: M * s.Hq * s.hd].view(B, s.Hq, k, s.hd)
+        L.vc_verify_attn_full(q, cache.k[l], cache.v[l], ctx_len, out, ctx_lens=ctx_lens, split_tokens=split_tokens,
+                              ws=ws)
+        L.vc_heads_to_rows(out, dec.rows[:M])
+    return attend
+
+
+def attend_draft(dec: DecoderGPU, ckvs, B, pos, tail_row, main_lens, tail_lens, ws):
+    """Attention callback of one draft step: rotary + append of the token's key/value
+    to the compressed cache's tail, then decode attention over compressed rows + tail."""
+    s = dec.s
+
+    def attend(l, M):
+        ckv = ckvs[l]
+        q = dec.q[: M * s.Hq * s.hd].view(B, s.Hq, 1, s.hd)
+        L.vc_rope_qkv(dec.qkv[:M], B, 1, s.Hq, s.Hkv, s.hd, pos, q, ckv.tail_k, ckv.tail_v, tail_row, theta=s.theta)
+        out = dec.rows[:M].view(B, s.Hq, s.hd)
+        L.vc_decode_attn_compressed(ckv, q.view(B, s.Hq, s.hd), out, main_lens=main_lens, tail_lens=tail_lens, ws=ws)
+    return attend
+
+
+class Session:
+    """Prompt state shared by the greedy reference and the draft-and-verify loop.
+
+    The prompt's first N0 - 1 tokens run through the verify kernel in chunks (causal
+    attention over the rows before the chunk plus the chunk itself); the last prompt
+    token then runs as a one-row step, like every later greedy step, and gives the
+    first generated token."""
+
+    def __init__(self, dec: DecoderGPU, prompt: np.ndarray, k: int, gen: int, chunk=512, group=32, bits=(2, 2),
+                 device="cuda"):
+        self.dec, self.k, self.gen, self.group, self.bits = dec, k, gen, group, bits
+        s = dec.s
+        self.B, self.N0 = prompt.shape
+        B, N0 = self.B, self.N0
+        assert N0 >= 1 and B * max(k, chunk) <= dec.max_rows
+        self.rows = _round_up(N0 + gen + 2 * k, 32)
+        self.split = L.vc_verify_split_tokens(B, s.Hkv)
+        self.device = device
+        self.ver_ws = L.workspace(L.vc_verify_workspace_bytes(B, s.Hq, s.Hkv, s.hd, max(k, chunk), self.rows,
+                                                              self.split), device)
+        self.cache = FullCache(s, B, self.rows, device)
+        tok = torch.as_tensor(prompt.astype(np.int32), device=device)
+        for c0 in range(0, N0 - 1, chunk):
+            c = min(chunk, N0 - 1 - c0)
+            toks = tok[:, c0:c0 + c].contiguous().view(-1)
+            pos = (torch.arange(c, device=device, dtype=torch.int32) + c0).repeat(B)
+            row0 = torch.full((B,), c0, dtype=torch.int32, device=device)
+            dec.forward(toks, B, c, attend_full(dec, self.cache, B, c, pos, row0, c0, None, self.split, self.ver_ws),
+                        head=False)
+        self.first = greedy_step(dec, self.cache, tok[:, N0 - 1].contiguous(), N0 - 1, self.split, self.ver_ws)
+        self.first_logits = dec.logits[:B].clone()   # of the last prompt position
+        torch.cuda.synchronize()
+
+
+def _round_up(x, m):
+    return (x + m - 1) // m * m
+
+
+def greedy_step(dec: DecoderGPU, cache: FullCache, tok, L_ctx: int, split, ws):
+    """One greedy full-KV step of every sequence (all at context length L_ctx):
+    the tokens' keys/values go to cache row L_ctx; returns the next tokens (int32 [B])."""
+    B = tok.numel()
+    pos = torch.full((B,), L_ctx, dtype=torch.int32, device=tok.device)
+    lg = dec.forward(tok, B, 1, attend_full(dec, cache, B, 1, pos, pos, L_ctx, None, split, ws))
+    nxt = torch.empty(B, dtype=torch.int32, device=tok.device)
+    L.vc_argmax_rows(lg, nxt)
+    return nxt
+
+
+class Greedy:
+    """Greedy full-KV decoding from a session's prompt, the full cache resident on
+    the device (the output reference, and the baseline of the throughput figures)."""
+
+    def __init__(self, sess: Session):
+        self.sess = sess
+        s = sess.dec.s
+        self.cache = FullCache(s, sess.B, sess.rows, sess.device)
+        for l in range(s.layers):
+            self.cache.k[l].copy_(sess.cache.k[l])
+            self.cache.v[l].copy_(sess.cache.v[l])
+        self.tok = sess.first.clone()
+        self.out = [self.tok]
+        self.L = sess.N0
+
+    def step(self):
+        sess = self.sess
+        self.tok = greedy_step(sess.dec, self.cache, self.tok, self.L, sess.split, sess.ver_ws)
+        self.out.append(self.tok)
+        self.L += 1
+
+    def run(self):
+        while len(self.out) < self.sess.gen:
+            self.step()
+        torch.cuda.synchronize()
+        return torch.stack(self.out[: self.sess.gen], 1).cpu().numpy()
+
+
+class VeriCacheLoop:
+    """Draft-and-verify decoding with the full KV in pinned host memory.
+
+    host_stage=False keeps the full cache resident on the device and skips the
+    host round trip (the same kernels; for separating PCIe time from compute)."""
+
+    def __init__(self, sess: Session, host_stage=True):
+        self.sess = sess
+        dec, s, B, dev = sess.dec, sess.dec.s, sess.B, sess.device
+        self.host_stage = host_stage
+        G, k = sess.group, sess.k
+        kb, vb = sess.bits
+        N0 = sess.N0
+        self.dev_cache = FullCache(s, B, sess.rows, dev)
+        if host_stage:
+            self.host_k = [torch.empty(sess.cache.k[l].shape, dtype=BF16, pin_memory=True) for l in range(s.layers)]
+            self.host_v = [torch.empty(sess.cache.v[l].shape, dtype=BF16, pin_memory=True) for l in range(s.layers)]
+            for l in range(s.layers):
+                self.host_k[l].copy_(sess.cache.k[l])
+                self.host_v[l].copy_(sess.cache.v[l])
+        else:
+            for l in range(s.layers):
+                self.dev_cache.k[l].copy_(sess.cache.k[l])
+                self.dev_cache.v[l].copy_(sess.cache.v[l])
+        # compressed caches: whole groups of the prompt + the rest in the tail
+        cap = _round_up(N0 + sess.gen + 2 * k + G, max(32, G))
+        self.tail_cap = G + 2 * k
+        self.ckvs = []
+        n_main = (N0 // G) * G
+        for l in range(s.layers):
+            c = L.Ckv("quant", B, s.Hkv, s.hd, cap, k_bits=kb, v_bits=vb, group=G, param_dtype="bf16", kv_dtype="bf16",
+                      tail_cap=self.tail_cap, device=dev)
+            if n_main:
+                L.vc_compress(c, sess.cache.k[l], sess.cache.v[l], n_tokens=n_main)
+            L.vc_copy_kv_rows(sess.cache.k[l], sess.cache.v[l], _i32(np.full(B, n_main), dev), c.tail_k, c.tail_v,
+                              _i32(np.zeros(B), dev), _i32(np.full(B, N0 - n_main), dev), max(N0 - n_main, 1))
+            self.ckvs.append(c)
+        self.n_main = np.full(B, n_main, np.int64)
+        self.ctail = np.full(B, N0 - n_main, np.int64)
+        self.Lb = np.full(B, N0, np.int64)
+        self.tok = sess.first.clone()
+        self.out = [[int(t)] for t in sess.first.cpu().numpy()]
+        self.dec_ws = L.workspace(L.vc_decode_workspace_bytes(self.ckvs[0], s.Hq), dev)
+        self.copy_stream = torch.cuda.Stream()
+        self.stage_ev = [torch.cuda.Event() for _ in range(s.layers)]
+        self.round_ev = torch.cuda.Event()
+        self.drafts_T = torch.empty(k, B, dtype=torch.int32, device=dev)
+        self.targets = torch.empty(B * k, dtype=torch.int32, device=dev)
+        self.acc = torch.empty(B, dtype=torch.int32, device=dev)
+        self.nc = torch.empty(B, dtype=torch.int32, device=dev)
+        self.com = torch.empty(B, k, dtype=torch.int32, device=dev)
+        self.rounds = 0
+        self.accept_lens = []
+
+    def done(self):
+        return min(len(o) for o in self.out) >= self.sess.gen
+
+    def round(self):
+        """One draft-and-verify round of every sequence; returns the tokens committed."""
+        sess, dec, s = self.sess, self.sess.dec, self.sess.dec.s
+        B, k, G, dev = sess.B, sess.k, sess.group, sess.device
+        maxL = int(self.Lb.max())
+        # ---- stage each layer's full KV on the side stream (after the previous round's
+        #      device work and host write-back, which the side stream already follows)
+        for l in range(s.layers):
+            if self.host_stage:
+                L.vc_stage_full_kv(self.host_k[l], self.host_v[l], self.dev_cache.k[l], self.dev_cache.v[l], 0, maxL,
+                                   copy_stream=self.copy_stream, done=self.stage_ev[l])
+            else:
+                self.stage_ev[l].record(self.copy_stream)
+        # ---- k draft steps on the compressed cache
+        for c in self.ckvs:
+            c.n_main = int(self.n_main.max())
+            c.tail_len = self.tail_cap
+        i_col = np.arange(k)[:, None]
+        pos_all = _i32(self.Lb[None, :] + i_col, dev)               # [k, B]
+        trow_all = _i32(self.ctail[None, :] + i_col, dev)
+        tlen_all = _i32(self.ctail[None, :] + i_col + 1, dev)
+        main_lens = _i32(self.n_main, dev)
+        cur = self.tok
+        for i in range(k):
+            attend = attend_draft(dec, self.ckvs, B, pos_all[i], trow_all[i], main_lens, tlen_all[i], self.dec_ws)
+            lg = dec.forward(cur, B, 1, attend)
+            L.vc_argmax_rows(lg, self.drafts_T[i])
+            cur = self.drafts_T[i]
+        drafts = self.drafts_T.t().contiguous()                    # [B, k]
+        # ---- verify the window [last committed, d_1 .. d_{k-1}] against the full cache;
+        #      layer l waits for its staged rows
+        window = torch.cat([self.tok.view(B, 1), drafts[:, : k - 1]], 1).contiguous().view(-1)
+        vpos = _i32(self.Lb[:, None] + np.arange(k)[None, :], dev).view(-1)
+        row0 = _i32(self.Lb, dev)
+        attend = attend_full(dec, self.dev_cache, B, k, vpos, row0, maxL, row0, sess.split, sess.ver_ws,
+                             wait_events=self.stage_ev)
+        lg = dec.forward(window, B, k, attend)
+        L.vc_argmax_rows(lg, self.targets)
+        L.vc_accept(drafts, self.targets.view(B, k), self.acc, self.nc, self.com)
+        acc, nc, com = self.acc.cpu().numpy(), self.nc.cpu().numpy(), self.com.cpu().numpy()  # the round's one sync
+        adv = np.minimum(acc + 1, k)
+        # ---- compressed tails take the verified rows; whole groups are quantized
+        src0, dst0, cnt = _i32(self.Lb, dev), _i32(self.ctail, dev), _i32(adv, dev)
+        for l in range(s.layers):
+            c = self.ckvs[l]
+            L.vc_copy_kv_rows(self.dev_cache.k[l], self.dev_cache.v[l], src0, c.tail_k, c.tail_v, dst0, cnt, k)
+        new_tail = self.ctail + adv
+        full = (new_tail // G) * G
+        if full.any():
+            rest = new_tail - full
+            for b in np.nonzero(full)[0]:
+                for l in range(s.layers):
+                    c = self.ckvs[l]
+                    L.vc_compress(c.batch_view(b), c.tail_k[b:b + 1], c.tail_v[b:b + 1], n_tokens=int(full[b]),
+                                  dst_begin=int(self.n_main[b]))
+            s0, d0, rc = _i32(full, dev), _i32(np.zeros(B), dev), _i32(rest, dev)
+            for l in range(s.layers):
+                c = self.ckvs[l]
+                L.vc_copy_kv_rows(c.tail_k, c.tail_v, s0, c.tail_k, c.tail_v, d0, rc, G)
+            self.n_main = self.n_main + full
+            new_tail = rest
+        # ---- the host full cache takes the verified rows (side stream, after this round's
+        #      device work, so the next round's staging cannot overtake a reader)
+        self.round_ev.record()
+        self.copy_stream.wait_event(self.round_ev)
+        if self.host_stage:
+            lo, hi = int(self.Lb.min()), int((self.Lb + adv).max())
+            for l in range(s.layers):
+                L.vc_stage_full_kv_d2h(self.dev_cache.k[l], self.dev_cache.v[l], self.host_k[l], self.host_v[l], lo, hi,
+                                       copy_stream=self.copy_stream)
+        self.ctail = new_tail
+        self.Lb = self.Lb + adv
+        for b in range(B):
+            self.out[b].extend(int(t) for t in com[b, : nc[b]])
+        self.tok = torch.as_tensor(np.array([self.out[b][-1] for b in range(B)], np.int32), device=dev)
+        self.rounds += 1
+        self.accept_lens.extend(int(a) for a in acc)
+        return int(nc.sum())
+
+    def run(self):
+        while not self.done():
+            self.round()
+        torch.cuda.synchronize()
+        return np.array([o[: self.sess.gen] for o in self.out], np.int32)
+
+
+def random_weights(shape: ModelShape, seed_fn, std=0.02, device="cuda"):
+    """bf16 weights of a random-initialised decoder; seed_fn(key, shape, std) returns
+    a float32 numpy draw of N(0, std^2) for an integer key tuple.  Projections are
+    stored [out_features, in_features]; wgu holds the gate rows, then the up rows."""
+    s = shape
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(BF16).to(device)
+    w = dict(E=t(seed_fn((0,), (s.vocab, s.d_model), std)),
+             head=t(seed_fn((1,), (s.vocab, s.d_model), std)),
+             nf=t(1.0 + seed_fn((2,), (s.d_model,), std)))
+    w["wqkv"] = [t(seed_fn((3, l), ((s.Hq + 2 * s.Hkv) * s.hd, s.d_model), std)) for l in range(s.layers)]
+    w["wo"] = [t(seed_fn((4, l), (s.d_model, s.Hq * s.hd), std)) for l in range(s.layers)]
+    w["wgu"] = [t(seed_fn((5, l), (2 * s.ffn, s.d_model), std)) for l in range(s.layers)]
+    w["wd"] = [t(seed_fn((6, l), (s.d_model, s.ffn), std)) for l in range(s.layers)]
+    w["n1"] = [t(1.0 + seed_fn((7, l), (s.d_model,), std)) for l in range(s.layers)]
+    w["n2"] = [t(1.0 + seed_fn((8, l), (s.d_model,), std)) for l in range(s.layers)]
+    return w
+
+
+def weights_to(w: dict, device):
+    return {k: ([x.to(device) for x in v] if isinstance(v, list) else v.to(device)) for k, v in w.items()}

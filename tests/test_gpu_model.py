@@ -1,0 +1,249 @@
+"""GPU parity of the decoder-layer kernels (vc_model.h) against the oracle decoder's
+functions, and of the end-to-end draft-and-verify round: its output must equal
+greedy full-KV decoding with the same kernels, token for token ("VeriCache: Turning
+Lossy KV Cache into Lossless LLM Inference", summary page, "Original abstract")."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import DEV, T, np32, storage_half_ulp, say
+from workloads import configs as C, gen as G
+from oracle import model as OM
+from oracle.logits import argmax_lowest
+
+pytestmark = pytest.mark.gpu
+
+L = pytest.importorskip("lossy_kv_draft_amd")
+from lossy_kv_draft_amd import round as R  # noqa: E402
+
+W = C.E2E
+
+
+def bf16(x):
+    return G.to_storage(np.asarray(x, np.float32), "bf16")
+
+
+def rnd(key, shape, std=1.0):
+    return G.normal(W, key, shape, std, "bf16")
+
+
+# ---------------------------------------------------------------- single kernels
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 32), (5, 40, 96), (37, 3072, 2048), (130, 72, 512)])
+@pytest.mark.parametrize("out", ["f32", "bf16", "bf16+res"])
+def test_gemm_matches_fp64(M, N, K, out):
+    say(f"gemm M{M} N{N} K{K} {out}")
+    a, w = rnd((1, M, K), (M, K)), rnd((2, N, K), (N, K), 0.05)
+    ref = a.astype(np.float64) @ w.astype(np.float64).T
+    bound = 2.0 ** -22 * K * (np.abs(a).astype(np.float64) @ np.abs(w).astype(np.float64).T) + 1e-30
+    A, Wt = T(a, torch.bfloat16), T(w, torch.bfloat16)
+    if out == "f32":
+        Cg = torch.empty(M, N, device=DEV)
+        L.vc_gemm_bf16(A, Wt, Cg)
+        err = np.abs(np32(Cg) - ref)
+        assert (err <= bound).all(), f"max excess {(err - bound).max():.3g}"
+        return
+    res = None
+    if out == "bf16+res":
+        r = rnd((3, M, N), (M, N))
+        ref = ref + r
+        res = T(r, torch.bfloat16)
+    Cg = torch.empty(M, N, device=DEV, dtype=torch.bfloat16)
+    L.vc_gemm_bf16(A, Wt, Cg, R=res)
+    err = np.abs(np32(Cg) - ref)
+    tol = bound + storage_half_ulp(ref, "bf16") + 2.0 ** -24 * np.abs(ref)
+    assert (err <= tol).all(), f"max excess {(err - tol).max():.3g}"
+
+
+def test_gemm_in_place_residual():
+    """x += h W^T with C and R the same buffer (the decoder's residual update)."""
+    M, N, K = 9, 48, 64
+    a, w, x = rnd((4, 0), (M, K)), rnd((4, 1), (N, K), 0.05), rnd((4, 2), (M, N))
+    X = T(x, torch.bfloat16)
+    L.vc_gemm_bf16(T(a, torch.bfloat16), T(w, torch.bfloat16), X, R=X)
+    Y = torch.empty_like(X)
+    L.vc_gemm_bf16(T(a, torch.bfloat16), T(w, torch.bfloat16), Y, R=T(x, torch.bfloat16))
+    assert torch.equal(X, Y)
+
+
+def test_gemm_rows_are_batch_invariant():
+    """A row's result does not depend on how many rows are multiplied together --
+    what makes the k-row verify pass equal to k one-row greedy steps."""
+    N, K = 200, 1024
+    a, w = rnd((5, 0), (130, K)), rnd((5, 1), (N, K), 0.05)
+    A, Wt = T(a, torch.bfloat16), T(w, torch.bfloat16)
+    full = torch.empty(130, N, device=DEV)
+    L.vc_gemm_bf16(A, Wt, full)
+    for m0, n in [(0, 1), (17, 1), (3, 4), (100, 30), (64, 66)]:
+        part = torch.empty(n, N, device=DEV)
+        L.vc_gemm_bf16(A[m0:m0 + n], Wt, part)
+        assert torch.equal(part, full[m0:m0 + n]), (m0, n)
+
+
+@pytest.mark.parametrize("M,d", [(1, 64), (7, 512), (33, 2048), (4, 4000)])
+def test_rmsnorm_matches_oracle(M, d):
+    x, w = rnd((6, M, d), (M, d), 3.0), bf16(1.0 + rnd((7, d), (d,), 0.1))
+    ref = OM.rmsnorm(x, w)
+    y = torch.empty(M, d, device=DEV, dtype=torch.bfloat16)
+    L.vc_rmsnorm(T(x, torch.bfloat16), T(w, torch.bfloat16), y)
+    err = np.abs(np32(y) - ref)
+    tol = storage_half_ulp(ref, "bf16") + 1e-5 * np.abs(ref) + 1e-6
+    assert (err <= tol).all(), f"max excess {(err - tol).max():.3g}"
+
+
+@pytest.mark.parametrize("B,k,Hq,Hkv,hd,pos_max", [(1, 1, 4, 2, 128, 10), (3, 5, 16, 4, 128, 20000),
+                                                   (2, 8, 6, 2, 64, 3000)])
+def test_rope_qkv_matches_oracle(B, k, Hq, Hkv, hd, pos_max):
+    say(f"rope B{B} k{k} Hq{Hq} Hkv{Hkv} hd{hd}")
+    width = (Hq + 2 * Hkv) * hd
+    qkv = rnd((8, B, k), (B * k, width))
+    pos = G.uniform_ints(W, (8, B, k), (B * k,), 0, pos_max)
+    rows = k + 12
+    row0 = G.uniform_ints(W, (9, B, k), (B,), 0, rows - k + 1)
+    q = torch.empty(B, Hq, k, hd, device=DEV, dtype=torch.bfloat16)
+    kd = torch.zeros(B, Hkv, rows, hd, device=DEV, dtype=torch.bfloat16)
+    vd = torch.zeros_like(kd)
+    L.vc_rope_qkv(T(qkv, torch.bfloat16), B, k, Hq, Hkv, hd, T(pos, torch.int32), q, kd, vd, T(row0, torch.int32))
+    x = qkv.reshape(B * k, Hq + 2 * Hkv, hd)
+    rq = OM.rope(x[:, :Hq], pos)
+    rk = OM.rope(x[:, Hq:Hq + Hkv], pos)
+    # float32 angle: |error| <= pos * 2^-22 radians (product and exp2 rounding), times |pair|
+    pair = np.sqrt(np.concatenate([x[..., : hd // 2] ** 2 + x[..., hd // 2:] ** 2] * 2, -1))
+    ang_tol = (pos[:, None, None] + 1) * 2.0 ** -21 * pair
+    gq = np32(q).transpose(0, 2, 1, 3).reshape(B * k, Hq, hd)
+    tq = storage_half_ulp(rq, "bf16") + ang_tol[:, :Hq] + 1e-6
+    assert (np.abs(gq - rq) <= tq).all()
+    gk, gv = np32(kd), np32(vd)
+    want_k = np.zeros_like(gk)
+    want_v = np.zeros_like(gv)
+    for b in range(B):
+        for i in range(k):
+            r = b * k + i
+            want_k[b, :, row0[b] + i] = rk[r]
+            want_v[b, :, row0[b] + i] = x[r, Hq + Hkv:]
+    tk = storage_half_ulp(want_k, "bf16") + 1e-6
+    for b in range(B):
+        for i in range(k):
+            tk[b, :, row0[b] + i] += ang_tol[b * k + i, Hq:Hq + Hkv]
+    assert (np.abs(gk - want_k) <= tk).all()
+    assert np.array_equal(gv, want_v)       # values are copied, untouched rows stay zero
+
+
+def test_swiglu_matches_oracle():
+    M, F = 5, 1000
+    gu = rnd((10,), (M, 2 * F), 4.0)
+    ref = OM.silu(gu[:, :F]) * gu[:, F:]
+    out = torch.empty(M, F, device=DEV, dtype=torch.bfloat16)
+    L.vc_swiglu(T(gu, torch.bfloat16), out)
+    err = np.abs(np32(out) - ref)
+    tol = storage_half_ulp(ref, "bf16") + 1e-5 * np.abs(ref) + 1e-6
+    assert (err <= tol).all()
+
+
+def test_embed_heads_to_rows_and_argmax_rows_exact():
+    V, d = 50, 64
+    E = rnd((11,), (V, d))
+    toks = np.array([3, 0, 49, 7, 7, -1, 50], np.int64)
+    x = torch.empty(len(toks), d, device=DEV, dtype=torch.bfloat16)
+    L.vc_embed(T(E, torch.bfloat16), T(toks, torch.int32), x)
+    want = np.where(((toks >= 0) & (toks < V))[:, None], E[np.clip(toks, 0, V - 1)], 0.0)
+    assert np.array_equal(np32(x), want)
+    o = rnd((12,), (2, 3, 4, 16))
+    rows = torch.empty(8, 48, device=DEV, dtype=torch.bfloat16)
+    L.vc_heads_to_rows(T(o, torch.bfloat16), rows)
+    assert np.array_equal(np32(rows), o.transpose(0, 2, 1, 3).reshape(8, 48))
+    lg = G.normal(W, (13,), (6, 1000), 1.0, "f32")
+    lg[1, [5, 900]] = 50.0                                   # tie: lowest index wins
+    lg[2, :] = 0.0
+    lg[3, 999] = 1e9
+    lg[4, [0, 1, 2]] = -1e9
+    tk = torch.empty(6, dtype=torch.int32, device=DEV)
+    L.vc_argmax_rows(T(lg), tk)
+    assert list(tk.cpu().numpy()) == [argmax_lowest(r) for r in lg]
+
+
+def test_copy_kv_rows_exact():
+    B, Hkv, d, sr, dr = 3, 2, 128, 40, 20
+    sk, sv = rnd((14, 0), (B, Hkv, sr, d)), rnd((14, 1), (B, Hkv, sr, d))
+    s0, d0, cnt = np.array([0, 30, 5]), np.array([2, 10, 19]), np.array([4, 0, 1])
+    dk = torch.zeros(B, Hkv, dr, d, device=DEV, dtype=torch.bfloat16)
+    dv = torch.zeros_like(dk)
+    i32 = lambda a: T(a, torch.int32)
+    L.vc_copy_kv_rows(T(sk, torch.bfloat16), T(sv, torch.bfloat16), i32(s0), dk, dv, i32(d0), i32(cnt), 4)
+    wk, wv = np.zeros((B, Hkv, dr, d)), np.zeros((B, Hkv, dr, d))
+    for b in range(B):
+        wk[b, :, d0[b]:d0[b] + cnt[b]] = sk[b, :, s0[b]:s0[b] + cnt[b]]
+        wv[b, :, d0[b]:d0[b] + cnt[b]] = sv[b, :, s0[b]:s0[b] + cnt[b]]
+    assert np.array_equal(np32(dk), wk) and np.array_equal(np32(dv), wv)
+
+
+# ---------------------------------------------------------------- end to end
+
+def _shape(w):
+    return R.ModelShape(layers=w.layers, d_model=w.d_model, Hq=w.Hq, Hkv=w.Hkv, hd=w.d, ffn=w.ffn, vocab=w.vocab)
+
+
+def _setup(w, std, chunk=512):
+    shape = _shape(w)
+    seed = lambda key, shp, s: G.normal(w, key, shp, s, "f32")
+    wcpu = R.random_weights(shape, seed, std=std, device="cpu")
+    prompt = G.tokens(w, 0, shape=(w.B, w.N), high=w.vocab)
+    dec = R.DecoderGPU(shape, R.weights_to(wcpu, DEV), max_rows=w.B * max(w.k, chunk))
+    sess = R.Session(dec, prompt, w.k, w.gen_tokens, chunk=chunk, group=w.group, bits=(w.k_bits, w.v_bits))
+    return shape, wcpu, prompt, dec, sess
+
+
+SMALL = W.with_(B=3, Hq=4, Hkv=2, N=300, k=8, layers=2, d_model=512, ffn=1024, vocab=1000, gen_tokens=40)
+
+
+def test_decoder_prefill_logits_match_oracle():
+    """The composed decoder (all kernels chained, prompt through chunked verify
+    attention) against the float64 oracle decoder on the same bf16 weights; bf16
+    activations between the kernels bound the agreement (relative L2 norm)."""
+    w = SMALL
+    shape, wcpu, prompt, dec, sess = _setup(w, std=0.08, chunk=128)
+    f = lambda t: t.double().numpy()
+    ow = OM.Weights(E=f(wcpu["E"]), wqkv=[f(x) for x in wcpu["wqkv"]], wo=[f(x) for x in wcpu["wo"]],
+                    wgu=[f(x) for x in wcpu["wgu"]], wd=[f(x) for x in wcpu["wd"]], n1=[f(x) for x in wcpu["n1"]],
+                    n2=[f(x) for x in wcpu["n2"]], nf=f(wcpu["nf"]), head=f(wcpu["head"]))
+    odec = OM.Decoder(OM.Config(shape.layers, shape.d_model, shape.Hq, shape.Hkv, shape.hd, shape.ffn, shape.vocab),
+                      ow)
+    got = np32(sess.first_logits)
+    first = sess.first.cpu().numpy()
+    empty = [(np.zeros((shape.Hkv, 0, shape.hd)), np.zeros((shape.Hkv, 0, shape.hd))) for _ in range(shape.layers)]
+    for b in range(w.B):
+        lg, _ = odec.forward_full(list(prompt[b]), 0, empty)
+        ref = lg[-1]
+        rel = np.linalg.norm(got[b] - ref) / np.linalg.norm(ref)
+        say(f"seq {b}: relative L2 error of the logits {rel:.3g}")
+        assert rel < 0.03
+        top2 = np.sort(ref)[-2:]
+        if top2[1] - top2[0] > 0.1 * np.abs(ref).max():
+            assert first[b] == argmax_lowest(ref)
+
+
+@pytest.mark.parametrize("host_stage", [True, False])
+def test_round_output_equals_greedy_small(host_stage):
+    w = SMALL
+    _, _, _, dec, sess = _setup(w, std=0.08, chunk=128)
+    ref = R.Greedy(sess).run()
+    loop = R.VeriCacheLoop(sess, host_stage=host_stage)
+    got = loop.run()
+    say(f"rounds {loop.rounds}, mean accept {np.mean(loop.accept_lens):.2f}")
+    assert np.array_equal(got, ref)
+    assert loop.rounds < w.gen_tokens          # drafts are accepted at least sometimes
+
+
+def test_round_output_equals_greedy_full_size():
+    """4 layers, d_model 2048, 16/4 heads, 16k-token prompts, k = 32, 2-bit KIVI
+    drafts, 256 generated tokens per sequence."""
+    w = W
+    say(f"e2e {w.name}: prefill")
+    _, _, _, dec, sess = _setup(w, std=0.02)
+    say("greedy")
+    ref = R.Greedy(sess).run()
+    say("draft-and-verify")
+    loop = R.VeriCacheLoop(sess, host_stage=True)
+    got = loop.run()
+    say(f"rounds {loop.rounds}, mean accept {np.mean(loop.accept_lens):.2f}")
+    assert np.array_equal(got, ref)
