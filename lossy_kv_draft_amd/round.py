@@ -6,7 +6,8 @@ The round follows "VeriCache: Turning Lossy KV Cache into Lossless LLM Inference
 (neuraltrendhub.com summary, "What the paper found" and "Original abstract"):
   * the full KV cache of every layer lives in pinned host memory and is staged to the
     device layer by layer on a side stream while the model drafts k tokens on the
-    compressed (KIVI-quantized) cache;
+    compressed (KIVI-quantized) cache; the device holds R layer slots (a ring), so
+    layers past the first R are staged while the verify pass runs the earlier ones;
   * the k-row window [last committed token, d_1 .. d_{k-1}] is verified against the
     full cache; the longest prefix on which drafts and greedy targets agree is
     committed, plus the target at the first disagreement;
@@ -86,29 +87,106 @@ def _i32(x, device):
     return torch.as_tensor(np.asarray(x, dtype=np.int32), device=device)
 
 
-class FullCache:
-    """Per-layer device full KV [B, Hkv, rows, hd] (bf16)."""
+def _round_up(x, m):
+    return (x + m - 1) // m * m
 
-    def __init__(self, shape: ModelShape, B, rows, device="cuda"):
-        self.k = [torch.zeros(B, shape.Hkv, rows, shape.hd, dtype=BF16, device=device) for _ in range(shape.layers)]
+
+class FullCache:
+    """Per-layer device full KV [B, Hkv, rows, hd] (bf16), resident."""
+
+    def __init__(self, shape: ModelShape, B, rows, device="cuda", layers=None):
+        n = shape.layers if layers is None else layers
+        self.k = [torch.zeros(B, shape.Hkv, rows, shape.hd, dtype=BF16, device=device) for _ in range(n)]
         self.v = [torch.zeros_like(t) for t in self.k]
         self.rows = rows
 
+    def clone(self):
+        c = FullCache.__new__(FullCache)
+        c.k, c.v, c.rows = [t.clone() for t in self.k], [t.clone() for t in self.v], self.rows
+        return c
 
-def attend_full(dec: DecoderGPU, cache: FullCache, B, k, pos, row0, ctx_len, ctx_lens, split_tokens, ws,
-                wait_events=None):
-    """Attention callback: rotary + scatter of the rows' keys/values into the full
-    cache at rows row0[b] + i, then causal verify attention over [0, row0[b] + i]."""
+    # the hooks of a forward pass over a resident cache
+    def begin(self, n_rows, lo, hi):
+        pass
+
+    def acquire(self, l):
+        return self.k[l], self.v[l]
+
+    def release(self, l):
+        pass
+
+
+class HostFullKV:
+    """The full KV of every layer in pinned host memory, staged into `slots` device
+    buffers (layer l uses slot l % slots) on a side stream.
+
+    A forward pass over it calls begin(n_rows, lo, hi) once, then acquire(l) before
+    and release(l) after layer l's attention:
+      begin    stages rows [0, n_rows) of layers [0, slots) (these copies overlap
+               whatever the compute stream does next, e.g. drafting);
+      acquire  makes the compute stream wait for layer l's rows;
+      release  writes rows [lo, hi) of the slot back to the host (the pass's new
+               keys/values) and stages layer l + slots into the freed slot."""
+
+    def __init__(self, src: FullCache, slots: int, device="cuda"):
+        n = len(src.k)
+        self.layers, self.slots = n, max(1, min(slots, n))
+        self.host_k = [torch.empty(t.shape, dtype=BF16, pin_memory=True) for t in src.k]
+        self.host_v = [torch.empty(t.shape, dtype=BF16, pin_memory=True) for t in src.v]
+        for l in range(n):
+            self.host_k[l].copy_(src.k[l])
+            self.host_v[l].copy_(src.v[l])
+        self.slot_k = [torch.zeros_like(src.k[0]) for _ in range(self.slots)]
+        self.slot_v = [torch.zeros_like(src.v[0]) for _ in range(self.slots)]
+        self.rows = src.rows
+        self.stream = torch.cuda.Stream()
+        self.staged = [torch.cuda.Event() for _ in range(n)]
+        self.freed = [torch.cuda.Event() for _ in range(n)]
+        self.n_rows = self.lo = self.hi = 0
+        self.bytes_staged = 0
+
+    def _stage(self, l):
+        j = l % self.slots
+        L.vc_stage_full_kv(self.host_k[l], self.host_v[l], self.slot_k[j], self.slot_v[j], 0, self.n_rows,
+                           copy_stream=self.stream, done=self.staged[l])
+        self.bytes_staged += 2 * self.host_k[l][:, :, : self.n_rows].numel() * 2
+
+    def begin(self, n_rows, lo, hi):
+        self.n_rows, self.lo, self.hi = n_rows, lo, hi
+        for l in range(self.slots):
+            self._stage(l)
+
+    def acquire(self, l):
+        torch.cuda.current_stream().wait_event(self.staged[l])
+        j = l % self.slots
+        return self.slot_k[j], self.slot_v[j]
+
+    def release(self, l):
+        j = l % self.slots
+        self.freed[l].record()
+        self.stream.wait_event(self.freed[l])
+        L.vc_stage_full_kv_d2h(self.slot_k[j], self.slot_v[j], self.host_k[l], self.host_v[l], self.lo, self.hi,
+                               copy_stream=self.stream)
+        if l + self.slots < self.layers:
+            self._stage(l + self.slots)
+
+
+def attend_full(dec: DecoderGPU, cache, B, k, pos, row0, ctx_len, ctx_lens, split_tokens, ws, after=None):
+    """Attention callback over a full cache (FullCache or HostFullKV): rotary + scatter
+    of the rows' keys/values into the cache at rows row0[b] + i, then causal verify
+    attention over rows [0, row0[b] + i].  after(l, K, V) runs before the layer's
+    cache is released."""
     s = dec.s
 
     def attend(l, M):
-        if wait_events is not None:
-            torch.cuda.current_stream().wait_event(wait_events[l])
+        K, V = cache.acquire(l)
         q = dec.q[: M * s.Hq * s.hd].view(B, s.Hq, k, s.hd)
-        L.vc_rope_qkv(dec.qkv[:M], B, k, s.Hq, s.Hkv, s.hd, pos, q, cache.k[l], cache.v[l], row0, theta=s.theta)
+        L.vc_rope_qkv(dec.qkv[:M], B, k, s.Hq, s.Hkv, s.hd, pos, q, K, V, row0, theta=s.theta)
         out = dec.attn[: M * s.Hq * s.hd].view(B, s.Hq, k, s.hd)
-        L.vc_verify_attn_full(q, cache.k[l], cache.v[l], ctx_len, out, ctx_lens=ctx_lens, split_tokens=split_tokens,
-                              ws=ws)
+        L.vc_verify_attn_full(q, K, V, ctx_len, out, ctx_lens=ctx_lens, split_tokens=split_tokens, ws=ws)
+        if after is not None:
+            after(l, K, V)
+        cache.release(l)
         L.vc_heads_to_rows(out, dec.rows[:M])
     return attend
 
@@ -161,15 +239,12 @@ class Session:
         torch.cuda.synchronize()
 
 
-def _round_up(x, m):
-    return (x + m - 1) // m * m
-
-
-def greedy_step(dec: DecoderGPU, cache: FullCache, tok, L_ctx: int, split, ws):
-    """One greedy full-KV step of every sequence (all at context length L_ctx):
-    the tokens' keys/values go to cache row L_ctx; returns the next tokens (int32 [B])."""
+def greedy_step(dec: DecoderGPU, cache, tok, L_ctx: int, split, ws):
+    """One greedy full-KV step of every sequence (all at context length L_ctx): the
+    tokens' keys/values go to cache row L_ctx; returns the next tokens (int32 [B])."""
     B = tok.numel()
     pos = torch.full((B,), L_ctx, dtype=torch.int32, device=tok.device)
+    cache.begin(L_ctx, L_ctx, L_ctx + 1)
     lg = dec.forward(tok, B, 1, attend_full(dec, cache, B, 1, pos, pos, L_ctx, None, split, ws))
     nxt = torch.empty(B, dtype=torch.int32, device=tok.device)
     L.vc_argmax_rows(lg, nxt)
@@ -177,16 +252,16 @@ def greedy_step(dec: DecoderGPU, cache: FullCache, tok, L_ctx: int, split, ws):
 
 
 class Greedy:
-    """Greedy full-KV decoding from a session's prompt, the full cache resident on
-    the device (the output reference, and the baseline of the throughput figures)."""
+    """Greedy full-KV decoding from a session's prompt: the output reference, and the
+    baselines of the throughput figures -- full KV resident on the device
+    (slots=None) or staged from pinned host memory every step (slots=R)."""
 
-    def __init__(self, sess: Session):
+    def __init__(self, sess: Session, slots=None):
         self.sess = sess
-        s = sess.dec.s
-        self.cache = FullCache(s, sess.B, sess.rows, sess.device)
-        for l in range(s.layers):
-            self.cache.k[l].copy_(sess.cache.k[l])
-            self.cache.v[l].copy_(sess.cache.v[l])
+        res = sess.cache.clone()
+        self.cache = res if slots is None else HostFullKV(res, slots, sess.device)
+        if slots is not None:
+            del res
         self.tok = sess.first.clone()
         self.out = [self.tok]
         self.L = sess.N0
@@ -197,37 +272,28 @@ class Greedy:
         self.out.append(self.tok)
         self.L += 1
 
-    def run(self):
-        while len(self.out) < self.sess.gen:
+    def run(self, n=None):
+        n = self.sess.gen if n is None else n
+        while len(self.out) < n:
             self.step()
         torch.cuda.synchronize()
-        return torch.stack(self.out[: self.sess.gen], 1).cpu().numpy()
+        return torch.stack(self.out[:n], 1).cpu().numpy()
 
 
 class VeriCacheLoop:
-    """Draft-and-verify decoding with the full KV in pinned host memory.
+    """Draft-and-verify decoding.  slots=R keeps the full KV in pinned host memory and
+    stages it through R device slots (R = layers: every layer staged during
+    drafting); slots=None keeps it resident on the device (no PCIe traffic; for
+    separating transfer time from compute)."""
 
-    host_stage=False keeps the full cache resident on the device and skips the
-    host round trip (the same kernels; for separating PCIe time from compute)."""
-
-    def __init__(self, sess: Session, host_stage=True):
+    def __init__(self, sess: Session, slots=2):
         self.sess = sess
         dec, s, B, dev = sess.dec, sess.dec.s, sess.B, sess.device
-        self.host_stage = host_stage
         G, k = sess.group, sess.k
         kb, vb = sess.bits
         N0 = sess.N0
-        self.dev_cache = FullCache(s, B, sess.rows, dev)
-        if host_stage:
-            self.host_k = [torch.empty(sess.cache.k[l].shape, dtype=BF16, pin_memory=True) for l in range(s.layers)]
-            self.host_v = [torch.empty(sess.cache.v[l].shape, dtype=BF16, pin_memory=True) for l in range(s.layers)]
-            for l in range(s.layers):
-                self.host_k[l].copy_(sess.cache.k[l])
-                self.host_v[l].copy_(sess.cache.v[l])
-        else:
-            for l in range(s.layers):
-                self.dev_cache.k[l].copy_(sess.cache.k[l])
-                self.dev_cache.v[l].copy_(sess.cache.v[l])
+        res = sess.cache.clone()
+        self.full = res if slots is None else HostFullKV(res, slots, dev)
         # compressed caches: whole groups of the prompt + the rest in the tail
         cap = _round_up(N0 + sess.gen + 2 * k + G, max(32, G))
         self.tail_cap = G + 2 * k
@@ -241,15 +307,14 @@ class VeriCacheLoop:
             L.vc_copy_kv_rows(sess.cache.k[l], sess.cache.v[l], _i32(np.full(B, n_main), dev), c.tail_k, c.tail_v,
                               _i32(np.zeros(B), dev), _i32(np.full(B, N0 - n_main), dev), max(N0 - n_main, 1))
             self.ckvs.append(c)
+        del res
+        self.win = FullCache(s, B, k, dev)          # each layer's window keys/values of the verify pass
         self.n_main = np.full(B, n_main, np.int64)
         self.ctail = np.full(B, N0 - n_main, np.int64)
         self.Lb = np.full(B, N0, np.int64)
         self.tok = sess.first.clone()
         self.out = [[int(t)] for t in sess.first.cpu().numpy()]
         self.dec_ws = L.workspace(L.vc_decode_workspace_bytes(self.ckvs[0], s.Hq), dev)
-        self.copy_stream = torch.cuda.Stream()
-        self.stage_ev = [torch.cuda.Event() for _ in range(s.layers)]
-        self.round_ev = torch.cuda.Event()
         self.drafts_T = torch.empty(k, B, dtype=torch.int32, device=dev)
         self.targets = torch.empty(B * k, dtype=torch.int32, device=dev)
         self.acc = torch.empty(B, dtype=torch.int32, device=dev)
@@ -257,23 +322,21 @@ class VeriCacheLoop:
         self.com = torch.empty(B, k, dtype=torch.int32, device=dev)
         self.rounds = 0
         self.accept_lens = []
+        self.ev = {n: torch.cuda.Event(enable_timing=True) for n in ("start", "drafted", "verified", "end")}
+        self.phase_ms = {"draft": 0.0, "verify": 0.0, "update": 0.0}
 
     def done(self):
         return min(len(o) for o in self.out) >= self.sess.gen
 
-    def round(self):
+    def round(self, timed=False):
         """One draft-and-verify round of every sequence; returns the tokens committed."""
         sess, dec, s = self.sess, self.sess.dec, self.sess.dec.s
         B, k, G, dev = sess.B, sess.k, sess.group, sess.device
         maxL = int(self.Lb.max())
-        # ---- stage each layer's full KV on the side stream (after the previous round's
-        #      device work and host write-back, which the side stream already follows)
-        for l in range(s.layers):
-            if self.host_stage:
-                L.vc_stage_full_kv(self.host_k[l], self.host_v[l], self.dev_cache.k[l], self.dev_cache.v[l], 0, maxL,
-                                   copy_stream=self.copy_stream, done=self.stage_ev[l])
-            else:
-                self.stage_ev[l].record(self.copy_stream)
+        if timed:
+            self.ev["start"].record()
+        # ---- staging of the first slots' layers starts now, overlapping the drafts
+        self.full.begin(maxL, int(self.Lb.min()), maxL + k)
         # ---- k draft steps on the compressed cache
         for c in self.ckvs:
             c.n_main = int(self.n_main.max())
@@ -289,24 +352,35 @@ class VeriCacheLoop:
             lg = dec.forward(cur, B, 1, attend)
             L.vc_argmax_rows(lg, self.drafts_T[i])
             cur = self.drafts_T[i]
+        if timed:
+            self.ev["drafted"].record()
         drafts = self.drafts_T.t().contiguous()                    # [B, k]
-        # ---- verify the window [last committed, d_1 .. d_{k-1}] against the full cache;
-        #      layer l waits for its staged rows
+        # ---- verify the window [last committed, d_1 .. d_{k-1}] against the full cache
         window = torch.cat([self.tok.view(B, 1), drafts[:, : k - 1]], 1).contiguous().view(-1)
         vpos = _i32(self.Lb[:, None] + np.arange(k)[None, :], dev).view(-1)
         row0 = _i32(self.Lb, dev)
-        attend = attend_full(dec, self.dev_cache, B, k, vpos, row0, maxL, row0, sess.split, sess.ver_ws,
-                             wait_events=self.stage_ev)
+        zeros, kk = _i32(np.zeros(B), dev), _i32(np.full(B, k), dev)
+
+        def keep_window(l, K, V):
+            L.vc_copy_kv_rows(K, V, row0, self.win.k[l], self.win.v[l], zeros, kk, k)
+
+        attend = attend_full(dec, self.full, B, k, vpos, row0, maxL, row0, sess.split, sess.ver_ws, after=keep_window)
         lg = dec.forward(window, B, k, attend)
         L.vc_argmax_rows(lg, self.targets)
         L.vc_accept(drafts, self.targets.view(B, k), self.acc, self.nc, self.com)
+        if timed:
+            self.ev["verified"].record()
         acc, nc, com = self.acc.cpu().numpy(), self.nc.cpu().numpy(), self.com.cpu().numpy()  # the round's one sync
-        adv = np.minimum(acc + 1, k)
+        # a sequence that already has its tokens stays where it is (its rows are still
+        # computed, within the cache, and discarded)
+        active = np.array([len(o) < sess.gen for o in self.out])
+        nc = np.where(active, nc, 0)
+        adv = np.where(active, np.minimum(acc + 1, k), 0)
         # ---- compressed tails take the verified rows; whole groups are quantized
-        src0, dst0, cnt = _i32(self.Lb, dev), _i32(self.ctail, dev), _i32(adv, dev)
+        dst0, cnt = _i32(self.ctail, dev), _i32(adv, dev)
         for l in range(s.layers):
             c = self.ckvs[l]
-            L.vc_copy_kv_rows(self.dev_cache.k[l], self.dev_cache.v[l], src0, c.tail_k, c.tail_v, dst0, cnt, k)
+            L.vc_copy_kv_rows(self.win.k[l], self.win.v[l], zeros, c.tail_k, c.tail_v, dst0, cnt, k)
         new_tail = self.ctail + adv
         full = (new_tail // G) * G
         if full.any():
@@ -316,33 +390,31 @@ class VeriCacheLoop:
                     c = self.ckvs[l]
                     L.vc_compress(c.batch_view(b), c.tail_k[b:b + 1], c.tail_v[b:b + 1], n_tokens=int(full[b]),
                                   dst_begin=int(self.n_main[b]))
-            s0, d0, rc = _i32(full, dev), _i32(np.zeros(B), dev), _i32(rest, dev)
+            s0, rc = _i32(full, dev), _i32(rest, dev)
             for l in range(s.layers):
                 c = self.ckvs[l]
-                L.vc_copy_kv_rows(c.tail_k, c.tail_v, s0, c.tail_k, c.tail_v, d0, rc, G)
+                L.vc_copy_kv_rows(c.tail_k, c.tail_v, s0, c.tail_k, c.tail_v, zeros, rc, G)
             self.n_main = self.n_main + full
             new_tail = rest
-        # ---- the host full cache takes the verified rows (side stream, after this round's
-        #      device work, so the next round's staging cannot overtake a reader)
-        self.round_ev.record()
-        self.copy_stream.wait_event(self.round_ev)
-        if self.host_stage:
-            lo, hi = int(self.Lb.min()), int((self.Lb + adv).max())
-            for l in range(s.layers):
-                L.vc_stage_full_kv_d2h(self.dev_cache.k[l], self.dev_cache.v[l], self.host_k[l], self.host_v[l], lo, hi,
-                                       copy_stream=self.copy_stream)
         self.ctail = new_tail
         self.Lb = self.Lb + adv
         for b in range(B):
             self.out[b].extend(int(t) for t in com[b, : nc[b]])
         self.tok = torch.as_tensor(np.array([self.out[b][-1] for b in range(B)], np.int32), device=dev)
+        if timed:
+            self.ev["end"].record()
+            self.ev["end"].synchronize()
+            e = self.ev
+            self.phase_ms["draft"] += e["start"].elapsed_time(e["drafted"])
+            self.phase_ms["verify"] += e["drafted"].elapsed_time(e["verified"])
+            self.phase_ms["update"] += e["verified"].elapsed_time(e["end"])
         self.rounds += 1
-        self.accept_lens.extend(int(a) for a in acc)
+        self.accept_lens.extend(int(a) for a in acc[active])
         return int(nc.sum())
 
-    def run(self):
+    def run(self, timed=False):
         while not self.done():
-            self.round()
+            self.round(timed)
         torch.cuda.synchronize()
         return np.array([o[: self.sess.gen] for o in self.out], np.int32)
 

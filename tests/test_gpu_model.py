@@ -8,7 +8,7 @@ import torch
 
 from gpu_util import DEV, T, np32, storage_half_ulp, say
 from workloads import configs as C, gen as G
-from oracle import model as OM
+from oracle import model as OM, quant as OQ
 from oracle.logits import argmax_lowest
 
 pytestmark = pytest.mark.gpu
@@ -202,12 +202,7 @@ def test_decoder_prefill_logits_match_oracle():
     activations between the kernels bound the agreement (relative L2 norm)."""
     w = SMALL
     shape, wcpu, prompt, dec, sess = _setup(w, std=0.08, chunk=128)
-    f = lambda t: t.double().numpy()
-    ow = OM.Weights(E=f(wcpu["E"]), wqkv=[f(x) for x in wcpu["wqkv"]], wo=[f(x) for x in wcpu["wo"]],
-                    wgu=[f(x) for x in wcpu["wgu"]], wd=[f(x) for x in wcpu["wd"]], n1=[f(x) for x in wcpu["n1"]],
-                    n2=[f(x) for x in wcpu["n2"]], nf=f(wcpu["nf"]), head=f(wcpu["head"]))
-    odec = OM.Decoder(OM.Config(shape.layers, shape.d_model, shape.Hq, shape.Hkv, shape.hd, shape.ffn, shape.vocab),
-                      ow)
+    odec = _oracle_decoder(shape, wcpu)
     got = np32(sess.first_logits)
     first = sess.first.cpu().numpy()
     empty = [(np.zeros((shape.Hkv, 0, shape.hd)), np.zeros((shape.Hkv, 0, shape.hd))) for _ in range(shape.layers)]
@@ -222,12 +217,118 @@ def test_decoder_prefill_logits_match_oracle():
             assert first[b] == argmax_lowest(ref)
 
 
-@pytest.mark.parametrize("host_stage", [True, False])
-def test_round_output_equals_greedy_small(host_stage):
+def _oracle_decoder(shape, wcpu):
+    f = lambda t: t.double().numpy()
+    ow = OM.Weights(E=f(wcpu["E"]), wqkv=[f(x) for x in wcpu["wqkv"]], wo=[f(x) for x in wcpu["wo"]],
+                    wgu=[f(x) for x in wcpu["wgu"]], wd=[f(x) for x in wcpu["wd"]], n1=[f(x) for x in wcpu["n1"]],
+                    n2=[f(x) for x in wcpu["n2"]], nf=f(wcpu["nf"]), head=f(wcpu["head"]))
+    return OM.Decoder(OM.Config(shape.layers, shape.d_model, shape.Hq, shape.Hkv, shape.hd, shape.ffn, shape.vocab),
+                      ow)
+
+
+def _small_model(std):
+    w = SMALL
+    shape = _shape(w)
+    wcpu = R.random_weights(shape, lambda key, shp, s: G.normal(w, key, shp, s, "f32"), std=std, device="cpu")
+    return w, shape, wcpu, _oracle_decoder(shape, wcpu)
+
+
+def _rel(got, ref):
+    return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
+
+@pytest.mark.parametrize("std", [0.02, 0.08])
+def test_draft_forward_matches_oracle(std):
+    """One draft step of the composed decoder (rotary at the next position, append to
+    the tail, decode attention over 2-bit groups + tail, per-sequence lengths) against
+    the oracle's draft forward on the same seeded caches."""
+    w, shape, wcpu, odec = _small_model(std)
+    B, Gs, hd, Hkv = 2, w.group, shape.hd, shape.Hkv
+    m, t = [256, 192], [5, 17]
+    cap, tcap = 256, 24
+    kv = [[G.normal(w, (20, l, b, j), (Hkv, m[b] + t[b], hd), 1.0, "bf16") for j in range(2)]
+          for l in range(shape.layers) for b in range(B)]
+    kv = [kv[l * B:(l + 1) * B] for l in range(shape.layers)]
+    tokens = np.array([17, 933])
+    dec = R.DecoderGPU(shape, R.weights_to(wcpu, DEV), max_rows=8)
+    ckvs = []
+    for l in range(shape.layers):
+        c = L.Ckv("quant", B, Hkv, hd, cap, k_bits=2, v_bits=2, group=Gs, param_dtype="bf16", kv_dtype="bf16",
+                  tail_cap=tcap, device=DEV)
+        src = [np.zeros((B, Hkv, cap, hd), np.float32) for _ in range(2)]
+        for b in range(B):
+            for j in range(2):
+                src[j][b, :, : m[b]] = kv[l][b][j][:, : m[b]]
+                getattr(c, "tail_k" if j == 0 else "tail_v")[b, :, : t[b]] = T(kv[l][b][j][:, m[b]:], torch.bfloat16)
+        L.vc_compress(c, T(src[0], torch.bfloat16), T(src[1], torch.bfloat16), n_tokens=cap)
+        c.n_main, c.tail_len = cap, tcap
+        ckvs.append(c)
+    i32 = lambda a: T(np.asarray(a), torch.int32)
+    pos = i32([m[b] + t[b] for b in range(B)])
+    ws = L.workspace(L.vc_decode_workspace_bytes(ckvs[0], shape.Hq), DEV)
+    attend = R.attend_draft(dec, ckvs, B, pos, i32(t), i32(m), i32([x + 1 for x in t]), ws)
+    got = np32(dec.forward(i32(tokens), B, 1, attend))
+    for b in range(B):
+        occ = []
+        for l in range(shape.layers):
+            K, V = kv[l][b]
+            Kh, Vh = np.zeros((Hkv, m[b], hd)), np.zeros((Hkv, m[b], hd))
+            for h in range(Hkv):
+                for g0 in range(0, m[b], Gs):
+                    cs = OQ.compress_slice(K[h, g0:g0 + Gs], V[h, g0:g0 + Gs], 2, 2, Gs, "bf16")
+                    Kh[h, g0:g0 + Gs], Vh[h, g0:g0 + Gs] = OQ.dequantize_slice(cs, hd, 2, 2, Gs)
+            occ.append((Kh, Vh, K[:, m[b]:].astype(np.float64), V[:, m[b]:].astype(np.float64)))
+        ref = odec.forward_draft(int(tokens[b]), m[b] + t[b], occ)
+        rel = _rel(got[b], ref)
+        say(f"draft seq {b}: relative L2 error {rel:.3g}")
+        assert rel < 0.03
+
+
+@pytest.mark.parametrize("std", [0.02, 0.08])
+def test_verify_forward_matches_oracle(std):
+    """The k-row verify pass of the composed decoder (rotary at positions L_b + i,
+    window keys/values written at rows L_b + i, causal attention over the full cache,
+    per-sequence context lengths) against the oracle's full forward."""
+    w, shape, wcpu, odec = _small_model(std)
+    B, k, hd, Hkv = 2, 6, shape.hd, shape.Hkv
+    Lb = [300, 131]
+    rows = 320
+    kv = [[G.normal(w, (21, l, b, j), (Hkv, Lb[b], hd), 1.0, "bf16") for j in range(2)]
+          for l in range(shape.layers) for b in range(B)]
+    kv = [kv[l * B:(l + 1) * B] for l in range(shape.layers)]
+    toks = G.uniform_ints(w, (22,), (B, k), 0, shape.vocab)
+    cache = R.FullCache(shape, B, rows, DEV)
+    for l in range(shape.layers):
+        for b in range(B):
+            cache.k[l][b, :, : Lb[b]] = T(kv[l][b][0], torch.bfloat16)
+            cache.v[l][b, :, : Lb[b]] = T(kv[l][b][1], torch.bfloat16)
+    split = L.vc_verify_split_tokens(B, Hkv)
+    ws = L.workspace(L.vc_verify_workspace_bytes(B, shape.Hq, Hkv, hd, k, rows, split), DEV)
+    dec = R.DecoderGPU(shape, R.weights_to(wcpu, DEV), max_rows=B * k)
+    i32 = lambda a: T(np.asarray(a), torch.int32)
+    vpos = i32((np.array(Lb)[:, None] + np.arange(k)[None, :]).reshape(-1))
+    row0 = i32(Lb)
+    attend = R.attend_full(dec, cache, B, k, vpos, row0, max(Lb), row0, split, ws)
+    got = np32(dec.forward(i32(toks.reshape(-1)), B, k, attend)).reshape(B, k, -1)
+    for b in range(B):
+        okv = [(kv[l][b][0].astype(np.float64), kv[l][b][1].astype(np.float64)) for l in range(shape.layers)]
+        ref, _ = odec.forward_full(list(toks[b]), Lb[b], okv)
+        for i in range(k):
+            rel = _rel(got[b, i], ref[i])
+            assert rel < 0.03, (b, i, rel)
+        say(f"verify seq {b}: max relative L2 error {max(_rel(got[b, i], ref[i]) for i in range(k)):.3g}")
+
+
+@pytest.mark.parametrize("slots", [1, 2, None])
+def test_round_output_equals_greedy_small(slots):
+    """slots: device layer slots of the staged full KV (1: a ring smaller than the
+    model, 2: every layer staged during drafting, None: full KV resident)."""
     w = SMALL
     _, _, _, dec, sess = _setup(w, std=0.08, chunk=128)
     ref = R.Greedy(sess).run()
-    loop = R.VeriCacheLoop(sess, host_stage=host_stage)
+    staged = R.Greedy(sess, slots=1).run(12)
+    assert np.array_equal(staged, ref[:, :12])
+    loop = R.VeriCacheLoop(sess, slots=slots)
     got = loop.run()
     say(f"rounds {loop.rounds}, mean accept {np.mean(loop.accept_lens):.2f}")
     assert np.array_equal(got, ref)
@@ -243,7 +344,7 @@ def test_round_output_equals_greedy_full_size():
     say("greedy")
     ref = R.Greedy(sess).run()
     say("draft-and-verify")
-    loop = R.VeriCacheLoop(sess, host_stage=True)
+    loop = R.VeriCacheLoop(sess, slots=2)
     got = loop.run()
     say(f"rounds {loop.rounds}, mean accept {np.mean(loop.accept_lens):.2f}")
     assert np.array_equal(got, ref)
