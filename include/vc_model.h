@@ -32,11 +32,22 @@ extern "C" {
 /* C[m][n] = sum_k A[m][k] * W[n][k] (+ R[m][n] if R is not NULL).
  * A bf16 [M, K] with row stride lda; W bf16 [N, K] (one row per output feature)
  * with row stride ldw; C (c_dtype VC_BF16 or VC_F32) [M, N] with row stride ldc;
- * R bf16 with the layout of C (bf16 C only).  float32 accumulation over k in
- * ascending 32-wide steps on bf16 matrix cores, the residual added in float32,
- * one rounding to the output type.  K % 32 == 0. */
+ * R bf16 with the layout of C (bf16 C only; C may be R itself).  A and W 16-byte
+ * aligned, lda and ldw multiples of 8, K % 32 == 0.
+ *
+ * Batch invariant: k is cut into 8 slices fixed by K alone; each slice is summed in
+ * float32 in ascending 32-wide steps on bf16 matrix cores and the 8 partial sums
+ * are added in a fixed tree, then the residual (float32) and one rounding to the
+ * output type -- so row m's result is the same for any M and any position of the
+ * row in A.  Built for few rows (decode and verify steps stream W once). */
 vc_status vc_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, int64_t M, int32_t N, int32_t K,
                        void* C, int64_t ldc, int32_t c_dtype, const void* R, void* stream);
+
+/* The same product for many rows (prompt processing): k summed in one ascending
+ * pass per output, so its rounding differs from vc_gemm_bf16's.  Same arguments
+ * and requirements. */
+vc_status vc_gemm_bf16_wide(const void* A, int64_t lda, const void* W, int64_t ldw, int64_t M, int32_t N, int32_t K,
+                            void* C, int64_t ldc, int32_t c_dtype, const void* R, void* stream);
 
 /* y[m] = x[m] / sqrt(mean_j x[m][j]^2 + eps) * w, x and y bf16 [M, d], w bf16 [d].
  * float32 arithmetic, fixed per-row reduction order. */

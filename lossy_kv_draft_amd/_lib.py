@@ -21,7 +21,7 @@ class VcError(RuntimeError):
 
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it first (python -m lossy_kv_draft_amd.build)")
+    raise ImportError(f"{LIB_PATH} is missing: build it first (python lossy_kv_draft_amd/build.py)")
 lib = ctypes.CDLL(LIB_PATH)
 
 c_i32, c_i64, c_f32, c_sz, c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
@@ -65,6 +65,7 @@ _DECLS = {
     "vc_last_error": (ctypes.c_char_p, []),
     # vc_model.h
     "vc_gemm_bf16": (c_i32, [c_p, c_i64, c_p, c_i64, c_i64, c_i32, c_i32, c_p, c_i64, c_i32, c_p, c_p]),
+    "vc_gemm_bf16_wide": (c_i32, [c_p, c_i64, c_p, c_i64, c_i64, c_i32, c_i32, c_p, c_i64, c_i32, c_p, c_p]),
     "vc_rmsnorm": (c_i32, [c_p, c_p, c_i64, c_i32, c_f32, c_p, c_p]),
     "vc_rope_qkv": (c_i32, [c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_p, c_p, c_p, c_p, c_i64, c_p, c_p]),
     "vc_swiglu": (c_i32, [c_p, c_i64, c_i32, c_p, c_p]),
@@ -326,6 +327,14 @@ def vc_gemm_bf16(A, W, C, *, R=None, stream=None):
     N = W.shape[0]
     _check(lib.vc_gemm_bf16(_ptr(A), A.stride(0), _ptr(W), W.stride(0), M, N, K, _ptr(C), C.stride(0),
                             _dt(C.dtype), _ptr(R), _stream(stream)), "vc_gemm_bf16")
+
+
+def vc_gemm_bf16_wide(A, W, C, *, R=None, stream=None):
+    """vc_gemm_bf16 for many rows (prompt processing; not batch invariant)."""
+    M, K = A.shape
+    N = W.shape[0]
+    _check(lib.vc_gemm_bf16_wide(_ptr(A), A.stride(0), _ptr(W), W.stride(0), M, N, K, _ptr(C), C.stride(0),
+                                 _dt(C.dtype), _ptr(R), _stream(stream)), "vc_gemm_bf16_wide")
 
 
 def vc_rmsnorm(x, w, y, *, eps=1e-5, stream=None):

@@ -46,55 +46,115 @@ __device__ __forceinline__ int64_t dec_tail_len(const DecodeArgs& a, int b) {
   return a.tail_lens ? a.tail_lens[b] : a.tail_len;
 }
 
-// Tail rows (full precision) of one (sequence, kv-head): each wave owns heads
-// wave, wave + 4, ...; lanes own channel pairs.  Writes the partial of `split`.
-template <typename T>
-__device__ void decode_tail_partial(const DecodeArgs& a, int bh, int split) {
+// Tail rows (full precision, bf16, d = 128) of one (sequence, kv-head), H <= 16
+// q-heads; writes the partial of `split`.  Rows go in chunks of 64, all in
+// parallel: one thread per (head, row) score, one wave per head for the chunk's
+// softmax (online across chunks), and for the outputs 16 lanes per head covering
+// 8 channels each, the chunk's rows strided over the remaining threads and summed
+// in a fixed order through LDS.  lds: >= 5 * 1024 floats of scratch.
+__device__ void decode_tail_partial_d128(const DecodeArgs& a, int bh, int split, float* lds) {
+  constexpr int D = 128, TC = 64;
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int d = a.d, H = a.H;
-  const int64_t tl = dec_tail_len(a, b);
-  const T* q = static_cast<const T*>(a.q);
-  const T* tk = static_cast<const T*>(a.tail_k) + static_cast<int64_t>(bh) * a.tail_cap * d;
-  const T* tv = static_cast<const T*>(a.tail_v) + static_cast<int64_t>(bh) * a.tail_cap * d;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.H;
+  const int tl = static_cast<int>(min(dec_tail_len(a, b), a.tail_cap));
+  float* s_q = lds;                    // [16][128] scaled queries
+  float* s_p = lds + 16 * D;           // [16][64] scores, then probabilities
+  float* s_red = lds + 16 * D + 16 * TC;  // [16 * RS][128] per-row-set output sums
+  float* s_st = s_red + 16 * D;        // [3][16] running max, running sum, rescale
+  const bf16_t* q = static_cast<const bf16_t*>(a.q) + (static_cast<int64_t>(b) * a.Hkv * H + hk * H) * D;
+  const bf16_t* tk = static_cast<const bf16_t*>(a.tail_k) + static_cast<int64_t>(bh) * a.tail_cap * D;
+  const bf16_t* tv = static_cast<const bf16_t*>(a.tail_v) + static_cast<int64_t>(bh) * a.tail_cap * D;
+  for (int e = tid; e < H * D; e += kDecThreads) s_q[e] = bf16_to_f32(q[e]) * a.qscale;
+  if (tid < H) {
+    s_st[tid] = -INFINITY;
+    s_st[16 + tid] = 0.f;
+  }
+  const int RS = 16 / H;  // row sets per head in the output pass
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  for (int r0 = 0; r0 < tl; r0 += TC) {
+    const int nr = min(TC, tl - r0);
+    __syncthreads();
+    // scores
+    for (int e = tid; e < H * TC; e += kDecThreads) {
+      const int hh = e / TC, r = e % TC;
+      float sc = -INFINITY;
+      if (r < nr) {
+        const uint4* kr = reinterpret_cast<const uint4*>(tk + static_cast<int64_t>(r0 + r) * D);
+        const float* qh = s_q + hh * D;
+        float x = 0.f;
+#pragma unroll
+        for (int v = 0; v < D / 8; ++v) {
+          const uint4 w = kr[v];
+          const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const float kv = __uint_as_float((c & 1) ? (ws[c >> 1] & 0xFFFF0000u) : (ws[c >> 1] << 16));
+            x = fmaf(qh[8 * v + c], kv, x);
+          }
+        }
+        sc = x;
+      }
+      s_p[hh * TC + r] = sc;
+    }
+    __syncthreads();
+    // softmax of the chunk, one wave per head
+    for (int hh = wave; hh < H; hh += kDecThreads / 64) {
+      const float v = s_p[hh * TC + lane];
+      const float mo = s_st[hh];
+      const float mn = fmaxf(mo, warp_max(v));
+      const float p = v == -INFINITY ? 0.f : exp2f(v - mn);
+      s_p[hh * TC + lane] = p;
+      const float sum = warp_sum(p);
+      if (lane == 0) {
+        const float sc = mo == -INFINITY ? 0.f : exp2f(mo - mn);
+        s_st[32 + hh] = sc;
+        s_st[16 + hh] = s_st[16 + hh] * sc + sum;
+        s_st[hh] = mn;
+      }
+    }
+    __syncthreads();
+    // weighted rows: thread (head, row set, 8-channel group)
+    if (tid < 16 * H * RS) {
+      const int c8 = tid & 15, g = tid >> 4, hh = g / RS, rs = g % RS;
+      float part[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) part[c] = 0.f;
+      for (int r = rs; r < nr; r += RS) {
+        const float p = s_p[hh * TC + r];
+        const uint4 w = *reinterpret_cast<const uint4*>(tv + static_cast<int64_t>(r0 + r) * D + 8 * c8);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          part[c] = fmaf(p, __uint_as_float((c & 1) ? (ws[c >> 1] & 0xFFFF0000u) : (ws[c >> 1] << 16)), part[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s_red[g * D + 8 * c8 + c] = part[c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = tid + kDecThreads * j;
+      if (e < H * D) {
+        const int hh = e / D, c = e % D;
+        float v = 0.f;
+        for (int rs = 0; rs < RS; ++rs) v += s_red[(hh * RS + rs) * D + c];
+        acc[j] = fmaf(acc[j], s_st[32 + hh], v);
+      }
+    }
+  }
+  __syncthreads();
   const int64_t pbase = static_cast<int64_t>(bh) * a.splits + split;
-  for (int h = wave; h < H; h += kDecThreads / 64) {
-    float qv[4], ov[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int c = lane + 64 * j;
-      qv[j] = c < d ? Elem<T>::load(q, (static_cast<int64_t>(b) * a.Hkv * H + hk * H + h) * d + c) * a.qscale : 0.f;
-      ov[j] = 0.f;
-    }
-    float m = -INFINITY, l = 0.f;
-    for (int64_t t = 0; t < tl; ++t) {
-      float x = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int c = lane + 64 * j;
-        if (c < d) x = fmaf(qv[j], Elem<T>::load(tk, t * d + c), x);
-      }
-      x = warp_sum(x);
-      float mn = fmaxf(m, x);
-      float al = exp2f(m - mn);
-      float p = exp2f(x - mn);
-      l = l * al + p;
-      m = mn;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int c = lane + 64 * j;
-        if (c < d) ov[j] = fmaf(p, Elem<T>::load(tv, t * d + c), ov[j] * al);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int c = lane + 64 * j;
-      if (c < d) a.part_o[(pbase * H + h) * d + c] = ov[j];
-    }
-    if (lane == 0) {
-      a.part_ml[(pbase * H + h) * 2] = m;
-      a.part_ml[(pbase * H + h) * 2 + 1] = l;
-    }
+  for (int j = 0; j < 8; ++j) {
+    const int e = tid + kDecThreads * j;
+    if (e < H * D) a.part_o[pbase * H * D + e] = acc[j];
+  }
+  if (tid < H) {
+    a.part_ml[(pbase * H + tid) * 2] = s_st[tid];
+    a.part_ml[(pbase * H + tid) * 2 + 1] = s_st[16 + tid];
   }
 }
 
@@ -103,7 +163,10 @@ __device__ void decode_tail_partial(const DecodeArgs& a, int bh, int split) {
 // does not depend on arrival order), writes out/lse and resets the counter.
 template <typename T>
 __device__ void decode_finish(const DecodeArgs& a, int bh) {
+  constexpr int kHG = 16;  // heads merged per pass
   __shared__ int s_last;
+  __shared__ float2 s_ml[kDecMaxSplits][kHG];  // (max, sum) per split, then (weight, sum)
+  __shared__ float2 s_fin[kHG];                // (max, sum) over all splits
   __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) s_last = (atomicAdd(a.counters + bh, 1) == a.splits - 1);
@@ -111,25 +174,54 @@ __device__ void decode_finish(const DecodeArgs& a, int bh) {
   if (!s_last) return;
   __threadfence();
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
-  const int H = a.H, d = a.d;
+  const int H = a.H, d = a.d, S = a.splits;
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + static_cast<int64_t>(bh) * S * H;
+  const float* po = a.part_o + static_cast<int64_t>(bh) * S * H * d;
   T* out = static_cast<T*>(a.out);
-  for (int i = threadIdx.x; i < H * d; i += blockDim.x) {
-    const int h = i / d;
-    float M = -INFINITY;
-    for (int s = 0; s < a.splits; ++s)
-      M = fmaxf(M, a.part_ml[((static_cast<int64_t>(bh) * a.splits + s) * H + h) * 2]);
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-      const int64_t ps = static_cast<int64_t>(bh) * a.splits + s;
-      const float m = a.part_ml[(ps * H + h) * 2];
-      const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-      L = fmaf(a.part_ml[(ps * H + h) * 2 + 1], w, L);
-      O = fmaf(a.part_o[ps * H * d + i], w, O);
+  for (int h0 = 0; h0 < H; h0 += kHG) {
+    const int hg = min(kHG, H - h0);
+    // every split's (max, sum) of these heads, loaded at once
+    for (int e = threadIdx.x; e < S * hg; e += blockDim.x) {
+      const int sp = e / hg, hh = e % hg;
+      s_ml[sp][hh] = ml[static_cast<int64_t>(sp) * H + h0 + hh];
     }
-    const int64_t oi = (static_cast<int64_t>(b) * a.Hkv * H + hk * H) * d + i;
-    Elem<T>::store(out, oi, L > 0.f ? O / L : 0.f);
-    if (a.lse && (i % d) == 0)
-      a.lse[static_cast<int64_t>(b) * a.Hkv * H + hk * H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    __syncthreads();
+    // per head: overall max, split weights and the sum, in split order
+    if (threadIdx.x < hg) {
+      const int hh = threadIdx.x;
+      float M = -INFINITY;
+      for (int sp = 0; sp < S; ++sp) M = fmaxf(M, s_ml[sp][hh].x);
+      float L = 0.f;
+      for (int sp = 0; sp < S; ++sp) {
+        const float m = s_ml[sp][hh].x;
+        const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+        L = fmaf(s_ml[sp][hh].y, w, L);
+        s_ml[sp][hh].x = w;
+      }
+      s_fin[hh] = make_float2(M, L);
+    }
+    __syncthreads();
+    // outputs: split partials weighted and summed in split order, 8 loads in flight
+    for (int i = threadIdx.x; i < hg * d; i += blockDim.x) {
+      const int hh = i / d, c = i % d;
+      const float* p = po + static_cast<int64_t>(h0 + hh) * d + c;
+      float O = 0.f;
+      for (int s0 = 0; s0 < S; s0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = p[static_cast<int64_t>(min(s0 + j, S - 1)) * H * d];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (s0 + j < S) O = fmaf(v[j], s_ml[s0 + j][hh].x, O);
+      }
+      const float L = s_fin[hh].y;
+      const int64_t oi = (static_cast<int64_t>(b) * a.Hkv * H + hk * H + h0 + hh) * d + c;
+      Elem<T>::store(out, oi, L > 0.f ? O / L : 0.f);
+      if (a.lse && c == 0)
+        a.lse[static_cast<int64_t>(b) * a.Hkv * H + hk * H + h0 + hh] =
+            L > 0.f ? (s_fin[hh].x + log2f(L)) * kLn2 : -INFINITY;
+    }
+    __syncthreads();
   }
   if (threadIdx.x == 0) a.counters[bh] = 0;
 }

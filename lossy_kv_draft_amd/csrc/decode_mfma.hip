@@ -176,7 +176,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
 
   const int split = blockIdx.x, bh = blockIdx.y;
   if (split == a.splits - 1) {  // the full-precision tail rows form the last split
-    decode_tail_partial<bf16_t>(a, bh, split);
+    decode_tail_partial_d128(a, bh, split, &sh_o[0][0][0]);
     decode_finish<bf16_t>(a, bh);
     return;
   }

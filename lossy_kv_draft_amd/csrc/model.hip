@@ -9,11 +9,19 @@
 // how many rows are processed together.  This file is built without floating-point
 // contraction so that every template instantiation rounds identically.
 //
-// GEMM (weights streamed from HBM once per call): C = A W^T on
-// v_mfma_f32_16x16x32_bf16.  One 64-lane wave owns 16 output features (16 rows of
-// W, the MFMA A operand, read with 16-byte loads) and up to 8 16-row tiles of A (the
-// B operand); the k loop runs in ascending 32-wide steps for every tile size, so a
-// row's result is the same whether M is 1, 4 or 128.
+// GEMMs C = A W^T on v_mfma_f32_16x16x32_bf16 (W rows are the MFMA A operand, read
+// with 16-byte loads; rows of A are the B operand).
+//
+// gemm_bf16_kernel -- the decode and verify passes, where M is a few rows per
+// sequence and the call streams W from HBM once: a workgroup of 8 waves owns 16
+// output features and up to 64 rows; wave w reduces its own slice of k (chunks
+// [w P, w P + P) of 32, P = ceil(K / 256), fixed by K alone) with W loads issued 8
+// chunks ahead, and the 8 partial sums are combined through LDS in a fixed tree.
+// Every row's result therefore depends on K only, never on M or the row's place in
+// the tile: the k-row verify pass reproduces k one-row greedy steps bit for bit.
+//
+// gemm_wide_kernel -- prompt processing (thousands of rows): one wave per 16
+// features x 128 rows, k ascending; its rounding differs from gemm_bf16_kernel's.
 
 #include "common.h"
 
@@ -28,7 +36,7 @@ union MP16 {
 };
 
 template <int MT, bool CF32, bool RES>
-__global__ void __launch_bounds__(64) gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda,
+__global__ void __launch_bounds__(64) gemm_wide_kernel(const bf16_t* __restrict__ A, int64_t lda,
                                                        const bf16_t* __restrict__ W, int64_t ldw, int64_t M, int N,
                                                        int K, void* C, int64_t ldc,
                                                        const bf16_t* R) {  // C may alias R
@@ -77,6 +85,89 @@ __global__ void __launch_bounds__(64) gemm_bf16_kernel(const bf16_t* __restrict_
         static_cast<float*>(C)[m * ldc + nn] = v;
       else
         static_cast<bf16_t*>(C)[m * ldc + nn] = f32_to_bf16(v);
+    }
+  }
+}
+
+constexpr int kGemmWaves = 8;  // k slices per workgroup
+constexpr int kGemmAhead = 8;  // W chunks in flight per wave
+
+template <int MT, bool CF32, bool RES>
+__global__ void __launch_bounds__(512) gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda,
+                                                        const bf16_t* __restrict__ W, int64_t ldw, int64_t M, int N,
+                                                        int K, void* C, int64_t ldc,
+                                                        const bf16_t* R) {  // C may alias R
+  __shared__ f32x4_t red[kGemmWaves][MT][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nl = lane & 15, kb = lane >> 4;
+  const int n0 = blockIdx.y * 16;
+  const int64_t m_base = static_cast<int64_t>(blockIdx.x) * 16 * MT;
+  const int nk = K >> 5;
+  const int P = (nk + kGemmWaves - 1) / kGemmWaves;
+  const int c_first = wave * P;
+  const int c_end = min(c_first + P, nk);
+  const int nblk = (P + kGemmAhead - 1) / kGemmAhead;
+  const int n = n0 + nl;
+  const bool n_ok = n < N;
+  const bf16_t* wrow = W + static_cast<int64_t>(n_ok ? n : N - 1) * ldw + 8 * kb;
+  const bf16_t* arow[MT];
+  bool m_ok[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int64_t m = m_base + 16 * t + nl;
+    m_ok[t] = m < M;
+    arow[t] = A + (m_ok[t] ? m : M - 1) * lda + 8 * kb;
+  }
+  auto chunk_off = [&](int c) { return static_cast<int64_t>(min(c, nk - 1)) * 32; };
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint4 wv[kGemmAhead];
+#pragma unroll
+  for (int u = 0; u < kGemmAhead; ++u) wv[u] = *reinterpret_cast<const uint4*>(wrow + chunk_off(c_first + u));
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int cb = c_first + blk * kGemmAhead;
+    uint4 av[kGemmAhead][MT];
+#pragma unroll
+    for (int u = 0; u < kGemmAhead; ++u)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) av[u][t] = *reinterpret_cast<const uint4*>(arow[t] + chunk_off(cb + u));
+#pragma unroll
+    for (int u = 0; u < kGemmAhead; ++u) {
+      const bool live = cb + u < c_end;  // wave-uniform: chunks past the slice add exact zeros
+      MP16 a;
+      a.u = (live && n_ok) ? wv[u] : zero;
+      wv[u] = *reinterpret_cast<const uint4*>(wrow + chunk_off(cb + u + kGemmAhead));
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        MP16 b;
+        b.u = (live && m_ok[t]) ? av[u][t] : zero;
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc[t], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
+  __syncthreads();
+  // acc[t][i] of lane ln = C[m_base + 16 t + (ln & 15)][n0 + 4 (ln >> 4) + i]
+  for (int e = tid; e < MT * 64; e += 64 * kGemmWaves) {
+    const int t = e >> 6, ln = e & 63;
+    const int64_t m = m_base + 16 * t + (ln & 15);
+    if (m >= M) continue;
+    const f32x4_t v = ((red[0][t][ln] + red[1][t][ln]) + (red[2][t][ln] + red[3][t][ln])) +
+                      ((red[4][t][ln] + red[5][t][ln]) + (red[6][t][ln] + red[7][t][ln]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int nn = n0 + 4 * (ln >> 4) + i;
+      if (nn >= N) continue;
+      float x = v[i];
+      if constexpr (RES) x = x + bf16_to_f32(R[m * ldc + nn]);
+      if constexpr (CF32)
+        static_cast<float*>(C)[m * ldc + nn] = x;
+      else
+        static_cast<bf16_t*>(C)[m * ldc + nn] = f32_to_bf16(x);
     }
   }
 }
@@ -217,18 +308,30 @@ using namespace vc;
 static bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
 template <int MT>
-static void launch_gemm(bool cf32, bool res, dim3 grid, hipStream_t s, const bf16_t* A, int64_t lda, const bf16_t* W,
+static void launch_wide(bool cf32, bool res, dim3 grid, hipStream_t s, const bf16_t* A, int64_t lda, const bf16_t* W,
                         int64_t ldw, int64_t M, int N, int K, void* C, int64_t ldc, const bf16_t* R) {
   if (cf32)
-    hipLaunchKernelGGL((gemm_bf16_kernel<MT, true, false>), grid, dim3(64), 0, s, A, lda, W, ldw, M, N, K, C, ldc, R);
+    hipLaunchKernelGGL((gemm_wide_kernel<MT, true, false>), grid, dim3(64), 0, s, A, lda, W, ldw, M, N, K, C, ldc, R);
   else if (res)
-    hipLaunchKernelGGL((gemm_bf16_kernel<MT, false, true>), grid, dim3(64), 0, s, A, lda, W, ldw, M, N, K, C, ldc, R);
+    hipLaunchKernelGGL((gemm_wide_kernel<MT, false, true>), grid, dim3(64), 0, s, A, lda, W, ldw, M, N, K, C, ldc, R);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<MT, false, false>), grid, dim3(64), 0, s, A, lda, W, ldw, M, N, K, C, ldc, R);
+    hipLaunchKernelGGL((gemm_wide_kernel<MT, false, false>), grid, dim3(64), 0, s, A, lda, W, ldw, M, N, K, C, ldc, R);
 }
 
-extern "C" vc_status vc_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, int64_t M, int32_t N,
-                                  int32_t K, void* C, int64_t ldc, int32_t c_dtype, const void* R, void* stream) {
+template <int MT>
+static void launch_inv(bool cf32, bool res, dim3 grid, hipStream_t s, const bf16_t* A, int64_t lda, const bf16_t* W,
+                       int64_t ldw, int64_t M, int N, int K, void* C, int64_t ldc, const bf16_t* R) {
+  const dim3 blk(64 * kGemmWaves);
+  if (cf32)
+    hipLaunchKernelGGL((gemm_bf16_kernel<MT, true, false>), grid, blk, 0, s, A, lda, W, ldw, M, N, K, C, ldc, R);
+  else if (res)
+    hipLaunchKernelGGL((gemm_bf16_kernel<MT, false, true>), grid, blk, 0, s, A, lda, W, ldw, M, N, K, C, ldc, R);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<MT, false, false>), grid, blk, 0, s, A, lda, W, ldw, M, N, K, C, ldc, R);
+}
+
+static vc_status gemm_common(bool wide, const void* A, int64_t lda, const void* W, int64_t ldw, int64_t M, int32_t N,
+                             int32_t K, void* C, int64_t ldc, int32_t c_dtype, const void* R, void* stream) {
   clear_error();
   VC_REQUIRE(A && W && C, "A / W / C is NULL");
   VC_REQUIRE(M > 0 && N > 0 && K > 0, "bad shape (M %lld, N %d, K %d)", (long long)M, N, K);
@@ -238,26 +341,51 @@ extern "C" vc_status vc_gemm_bf16(const void* A, int64_t lda, const void* W, int
   VC_REQUIRE(aligned16(A) && aligned16(W), "A and W must be 16-byte aligned");
   VC_REQUIRE(valid_dtype(c_dtype), "bad c_dtype");
   VC_REQUIRE(R == nullptr || c_dtype == VC_BF16, "a residual needs a bf16 output");
-  const int64_t mt_rows = M >= 128 ? 128 : ((M + 15) / 16) * 16;
+  const int64_t cap = wide ? 128 : 64;  // rows per workgroup
+  const int64_t mt_rows = M >= cap ? cap : ((M + 15) / 16) * 16;
   const int MT = static_cast<int>(mt_rows / 16);
-  dim3 grid(static_cast<unsigned>(cdiv(N, 16)), static_cast<unsigned>(cdiv(M, mt_rows)));
+  VC_REQUIRE(cdiv(M, mt_rows) <= (wide ? 65535 : 0x7fffffff) && cdiv(N, 16) <= (wide ? 0x7fffffff : 65535),
+             "grid too large");
+  const unsigned mtiles = static_cast<unsigned>(cdiv(M, mt_rows)), ntiles = static_cast<unsigned>(cdiv(N, 16));
+  // wide: feature tiles along x; batch-invariant: row tiles along x (the workgroups
+  // sharing a feature tile run together and read its W rows from L2)
+  const dim3 grid = wide ? dim3(ntiles, mtiles) : dim3(mtiles, ntiles);
   hipStream_t s = as_stream(stream);
   const bf16_t* a = static_cast<const bf16_t*>(A);
   const bf16_t* w = static_cast<const bf16_t*>(W);
   const bf16_t* r = static_cast<const bf16_t*>(R);
   const bool cf = c_dtype == VC_F32, res = R != nullptr;
-  switch (MT) {
-    case 1: launch_gemm<1>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
-    case 2: launch_gemm<2>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
-    case 3: launch_gemm<3>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
-    case 4: launch_gemm<4>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
-    case 5: launch_gemm<5>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
-    case 6: launch_gemm<6>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
-    case 7: launch_gemm<7>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
-    default: launch_gemm<8>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+  if (wide) {
+    switch (MT) {
+      case 1: launch_wide<1>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+      case 2: launch_wide<2>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+      case 3: launch_wide<3>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+      case 4: launch_wide<4>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+      case 5: launch_wide<5>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+      case 6: launch_wide<6>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+      case 7: launch_wide<7>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+      default: launch_wide<8>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+    }
+  } else {
+    switch (MT) {
+      case 1: launch_inv<1>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+      case 2: launch_inv<2>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+      case 3: launch_inv<3>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+      default: launch_inv<4>(cf, res, grid, s, a, lda, w, ldw, M, N, K, C, ldc, r); break;
+    }
   }
-  VC_LAUNCHED("gemm_bf16_kernel");
+  VC_LAUNCHED(wide ? "gemm_wide_kernel" : "gemm_bf16_kernel");
   return VC_OK;
+}
+
+extern "C" vc_status vc_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, int64_t M, int32_t N,
+                                  int32_t K, void* C, int64_t ldc, int32_t c_dtype, const void* R, void* stream) {
+  return gemm_common(false, A, lda, W, ldw, M, N, K, C, ldc, c_dtype, R, stream);
+}
+
+extern "C" vc_status vc_gemm_bf16_wide(const void* A, int64_t lda, const void* W, int64_t ldw, int64_t M, int32_t N,
+                                       int32_t K, void* C, int64_t ldc, int32_t c_dtype, const void* R, void* stream) {
+  return gemm_common(true, A, lda, W, ldw, M, N, K, C, ldc, c_dtype, R, stream);
 }
 
 extern "C" vc_status vc_rmsnorm(const void* x, const void* w, int64_t M, int32_t d, float eps, void* y, void* stream) {

@@ -313,16 +313,35 @@ __global__ void __launch_bounds__(256) verify_merge_kernel(VerifyArgs a, void* o
   if (e >= static_cast<int64_t>(M) * d) return;
   const int row = static_cast<int>(e / d), c = static_cast<int>(e % d);
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
+  const int S = a.splits;
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + static_cast<int64_t>(bh) * S * M + row;
+  const float* po = a.part_o + (static_cast<int64_t>(bh) * S * M + row) * d + c;
+  // the partials of 8 splits are loaded at once; the sums still run in split order
   float Mx = -INFINITY;
-  for (int s = 0; s < a.splits; ++s)
-    Mx = fmaxf(Mx, a.part_ml[((static_cast<int64_t>(bh) * a.splits + s) * M + row) * 2]);
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float mv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mv[j] = ml[static_cast<int64_t>(min(s0 + j, S - 1)) * M].x;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Mx = fmaxf(Mx, mv[j]);
+  }
   float Lsum = 0.f, O = 0.f;
-  for (int s = 0; s < a.splits; ++s) {
-    int64_t pr = (static_cast<int64_t>(bh) * a.splits + s) * M + row;
-    float mv = a.part_ml[pr * 2];
-    float w = mv == -INFINITY ? 0.f : exp2f(mv - Mx);
-    Lsum = fmaf(a.part_ml[pr * 2 + 1], w, Lsum);
-    O = fmaf(a.part_o[pr * d + c], w, O);
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float2 p[8];
+    float ov[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t sp = min(s0 + j, S - 1);
+      p[j] = ml[sp * M];
+      ov[j] = po[sp * M * d];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (s0 + j >= S) break;
+      const float w = p[j].x == -INFINITY ? 0.f : exp2f(p[j].x - Mx);
+      Lsum = fmaf(p[j].y, w, Lsum);
+      O = fmaf(ov[j], w, O);
+    }
   }
   int64_t orow = (static_cast<int64_t>(b) * a.Hq + hk * a.H) * a.k + row;
   Elem<T>::store(static_cast<T*>(out), orow * d + c, Lsum > 0.f ? O / Lsum : 0.f);

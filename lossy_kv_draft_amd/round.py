@@ -62,20 +62,23 @@ class DecoderGPU:
         """tokens: int32 [B*k] (row b*k + i = token i of sequence b).  attend(l, M)
         runs layer l's attention on self.qkv[:M] and leaves its output as rows
         [M, Hq*hd] in self.rows[:M].  Returns float32 logits [M, vocab] (a view of
-        self.logits), or None when head is False (prompt chunks)."""
+        self.logits), or None when head is False: prompt chunks, whose projections
+        use the many-row GEMM (the decode and verify passes use the batch-invariant
+        one, so that verify rows equal one-row greedy steps bit for bit)."""
         s, w = self.s, self.w
         M = B * k
         x, h = self.x[:M], self.h[:M]
+        mm = L.vc_gemm_bf16 if head else L.vc_gemm_bf16_wide
         L.vc_embed(w["E"], tokens, x)
         for l in range(s.layers):
             L.vc_rmsnorm(x, w["n1"][l], h, eps=s.eps)
-            L.vc_gemm_bf16(h, w["wqkv"][l], self.qkv[:M])
+            mm(h, w["wqkv"][l], self.qkv[:M])
             attend(l, M)
-            L.vc_gemm_bf16(self.rows[:M], w["wo"][l], x, R=x)
+            mm(self.rows[:M], w["wo"][l], x, R=x)
             L.vc_rmsnorm(x, w["n2"][l], h, eps=s.eps)
-            L.vc_gemm_bf16(h, w["wgu"][l], self.gu[:M])
+            mm(h, w["wgu"][l], self.gu[:M])
             L.vc_swiglu(self.gu[:M], self.act[:M])
-            L.vc_gemm_bf16(self.act[:M], w["wd"][l], x, R=x)
+            mm(self.act[:M], w["wd"][l], x, R=x)
         if not head:
             return None
         L.vc_rmsnorm(x, w["nf"], h, eps=s.eps)
@@ -254,9 +257,15 @@ def greedy_step(dec: DecoderGPU, cache, tok, L_ctx: int, split, ws):
 class Greedy:
     """Greedy full-KV decoding from a session's prompt: the output reference, and the
     baselines of the throughput figures -- full KV resident on the device
-    (slots=None) or staged from pinned host memory every step (slots=R)."""
+    (slots=None) or staged from pinned host memory every step (slots=R).
 
-    def __init__(self, sess: Session, slots=None):
+    With the cache resident and graph=True one step is captured once as a HIP graph
+    (its launches replayed without host overhead): positions come from a device
+    buffer and the attention reads per-sequence lengths, with the cache's row count
+    as the bound -- the same arithmetic as the uncaptured step (splits sit at
+    absolute positions)."""
+
+    def __init__(self, sess: Session, slots=None, graph=True):
         self.sess = sess
         res = sess.cache.clone()
         self.cache = res if slots is None else HostFullKV(res, slots, sess.device)
@@ -265,10 +274,27 @@ class Greedy:
         self.tok = sess.first.clone()
         self.out = [self.tok]
         self.L = sess.N0
+        self.graph = None
+        if graph and slots is None:
+            dec, B = sess.dec, sess.B
+            self.g_tok = self.tok.clone()
+            self.g_L = torch.full((B,), self.L, dtype=torch.int32, device=sess.device)
+            self.g_next = torch.empty(B, dtype=torch.int32, device=sess.device)
+            self.graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(self.graph):
+                lg = dec.forward(self.g_tok, B, 1, attend_full(dec, self.cache, B, 1, self.g_L, self.g_L,
+                                                               sess.rows - 1, self.g_L, sess.split, sess.ver_ws))
+                L.vc_argmax_rows(lg, self.g_next)
+                self.g_tok.copy_(self.g_next)
 
     def step(self):
         sess = self.sess
-        self.tok = greedy_step(sess.dec, self.cache, self.tok, self.L, sess.split, sess.ver_ws)
+        if self.graph is not None:
+            self.g_L.fill_(self.L)
+            self.graph.replay()
+            self.tok = self.g_next.clone()
+        else:
+            self.tok = greedy_step(sess.dec, self.cache, self.tok, self.L, sess.split, sess.ver_ws)
         self.out.append(self.tok)
         self.L += 1
 
@@ -284,9 +310,15 @@ class VeriCacheLoop:
     """Draft-and-verify decoding.  slots=R keeps the full KV in pinned host memory and
     stages it through R device slots (R = layers: every layer staged during
     drafting); slots=None keeps it resident on the device (no PCIe traffic; for
-    separating transfer time from compute)."""
+    separating transfer time from compute).
 
-    def __init__(self, sess: Session, slots=2):
+    graph=True captures the k draft steps once as a HIP graph: their inputs
+    (positions, tail rows, lengths, the first token) live in static device buffers
+    refreshed before each replay, and the compressed caches' descriptors carry fixed
+    bounds (capacity and tail capacity) while the kernels read the per-sequence
+    lengths."""
+
+    def __init__(self, sess: Session, slots=2, graph=True):
         self.sess = sess
         dec, s, B, dev = sess.dec, sess.dec.s, sess.B, sess.device
         G, k = sess.group, sess.k
@@ -324,6 +356,39 @@ class VeriCacheLoop:
         self.accept_lens = []
         self.ev = {n: torch.cuda.Event(enable_timing=True) for n in ("start", "drafted", "verified", "end")}
         self.phase_ms = {"draft": 0.0, "verify": 0.0, "update": 0.0}
+        # the draft loop's inputs, refreshed every round
+        for c in self.ckvs:
+            c.n_main, c.tail_len = cap, self.tail_cap
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.g_tok = torch.empty(B, **i32)
+        self.g_pos, self.g_trow, self.g_tlen = (torch.empty(k, B, **i32) for _ in range(3))
+        self.g_main = torch.empty(B, **i32)
+        self.graph = None
+        if graph:
+            self._set_draft_inputs()
+            self.graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(self.graph):
+                self._draft_steps()
+
+    def _set_draft_inputs(self):
+        k = self.sess.k
+        i_col = np.arange(k)[:, None]
+        cpu = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32))
+        self.g_tok.copy_(self.tok)
+        self.g_pos.copy_(cpu(self.Lb[None, :] + i_col))
+        self.g_trow.copy_(cpu(self.ctail[None, :] + i_col))
+        self.g_tlen.copy_(cpu(self.ctail[None, :] + i_col + 1))
+        self.g_main.copy_(cpu(self.n_main))
+
+    def _draft_steps(self):
+        dec, B = self.sess.dec, self.sess.B
+        cur = self.g_tok
+        for i in range(self.sess.k):
+            attend = attend_draft(dec, self.ckvs, B, self.g_pos[i], self.g_trow[i], self.g_main, self.g_tlen[i],
+                                  self.dec_ws)
+            lg = dec.forward(cur, B, 1, attend)
+            L.vc_argmax_rows(lg, self.drafts_T[i])
+            cur = self.drafts_T[i]
 
     def done(self):
         return min(len(o) for o in self.out) >= self.sess.gen
@@ -338,20 +403,11 @@ class VeriCacheLoop:
         # ---- staging of the first slots' layers starts now, overlapping the drafts
         self.full.begin(maxL, int(self.Lb.min()), maxL + k)
         # ---- k draft steps on the compressed cache
-        for c in self.ckvs:
-            c.n_main = int(self.n_main.max())
-            c.tail_len = self.tail_cap
-        i_col = np.arange(k)[:, None]
-        pos_all = _i32(self.Lb[None, :] + i_col, dev)               # [k, B]
-        trow_all = _i32(self.ctail[None, :] + i_col, dev)
-        tlen_all = _i32(self.ctail[None, :] + i_col + 1, dev)
-        main_lens = _i32(self.n_main, dev)
-        cur = self.tok
-        for i in range(k):
-            attend = attend_draft(dec, self.ckvs, B, pos_all[i], trow_all[i], main_lens, tlen_all[i], self.dec_ws)
-            lg = dec.forward(cur, B, 1, attend)
-            L.vc_argmax_rows(lg, self.drafts_T[i])
-            cur = self.drafts_T[i]
+        self._set_draft_inputs()
+        if self.graph is not None:
+            self.graph.replay()
+        else:
+            self._draft_steps()
         if timed:
             self.ev["drafted"].record()
         drafts = self.drafts_T.t().contiguous()                    # [B, k]

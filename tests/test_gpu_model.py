@@ -319,20 +319,37 @@ def test_verify_forward_matches_oracle(std):
         say(f"verify seq {b}: max relative L2 error {max(_rel(got[b, i], ref[i]) for i in range(k)):.3g}")
 
 
-@pytest.mark.parametrize("slots", [1, 2, None])
-def test_round_output_equals_greedy_small(slots):
+@pytest.mark.parametrize("slots,graph", [(1, True), (2, False), (None, True)])
+def test_round_output_equals_greedy_small(slots, graph):
     """slots: device layer slots of the staged full KV (1: a ring smaller than the
-    model, 2: every layer staged during drafting, None: full KV resident)."""
+    model, 2: every layer staged during drafting, None: full KV resident); graph:
+    draft loop captured as a HIP graph or launched step by step."""
     w = SMALL
     _, _, _, dec, sess = _setup(w, std=0.08, chunk=128)
     ref = R.Greedy(sess).run()
+    assert np.array_equal(R.Greedy(sess, graph=False).run(), ref)
     staged = R.Greedy(sess, slots=1).run(12)
     assert np.array_equal(staged, ref[:, :12])
-    loop = R.VeriCacheLoop(sess, slots=slots)
+    loop = R.VeriCacheLoop(sess, slots=slots, graph=graph)
     got = loop.run()
     say(f"rounds {loop.rounds}, mean accept {np.mean(loop.accept_lens):.2f}")
     assert np.array_equal(got, ref)
     assert loop.rounds < w.gen_tokens          # drafts are accepted at least sometimes
+
+
+def test_graph_draft_loop_matches_eager():
+    """The captured draft loop produces the same drafts as the step-by-step launches
+    (std 0.02 model: drafts are mostly accepted, so several rounds and group
+    compressions go by)."""
+    w = SMALL
+    _, _, _, dec, sess = _setup(w, std=0.02, chunk=128)
+    a, b = R.VeriCacheLoop(sess, slots=None, graph=True), R.VeriCacheLoop(sess, slots=None, graph=False)
+    for _ in range(6):
+        a.round()
+        b.round()
+        assert torch.equal(a.drafts_T, b.drafts_T)
+        assert a.out == b.out
+    say(f"accept lengths {a.accept_lens}")
 
 
 def test_round_output_equals_greedy_full_size():
