@@ -173,7 +173,6 @@ __global__ void __launch_bounds__(kDecThreads) decode_generic_kernel(DecodeArgs 
     a.part_ml[(pbase * H + h) * 2 + 0] = mrun[h];
     a.part_ml[(pbase * H + h) * 2 + 1] = lrun[h];
   }
-  decode_finish<T>(a, bh);
 }
 
 // ------------------------------------------------------------------ host side
@@ -210,7 +209,6 @@ extern "C" size_t vc_decode_workspace_bytes(const vc_ckv* c, int32_t Hq) {
   size_t H = Hq / c->Hkv;
   size_t bytes = align_up(bh * S * H * c->d * sizeof(float), 256);
   bytes += align_up(bh * S * H * 2 * sizeof(float), 256);
-  bytes += align_up(bh * sizeof(int), 256);
   return bytes;
 }
 
@@ -275,15 +273,21 @@ extern "C" vc_status vc_decode_attn_compressed(const vc_ckv* c, const void* q, i
   a.part_o = reinterpret_cast<float*>(w);
   w += align_up(bh * S * H * c->d * sizeof(float), 256);
   a.part_ml = reinterpret_cast<float*>(w);
-  w += align_up(bh * S * H * 2 * sizeof(float), 256);
-  a.counters = reinterpret_cast<int*>(w);
 
   dim3 grid(S, static_cast<unsigned>(bh));
   hipStream_t s = as_stream(stream);
+  auto merge = [&]() -> vc_status {
+    if (c->kv_dtype == VC_BF16)
+      hipLaunchKernelGGL(decode_merge_kernel<bf16_t>, dim3(static_cast<unsigned>(bh)), dim3(kDecThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL(decode_merge_kernel<float>, dim3(static_cast<unsigned>(bh)), dim3(kDecThreads), 0, s, a);
+    VC_LAUNCHED("decode_merge_kernel");
+    return VC_OK;
+  };
   if (mfma) {
     launch_decode_mfma(c, a, grid, s);
     VC_LAUNCHED("decode_mfma_kernel");
-    return VC_OK;
+    return merge();
   }
   size_t lds = (static_cast<size_t>(H) * c->d + kDecTile * (c->d + 1) + kDecTile * c->d + H * kDecTile + 3 * H) *
                sizeof(float);
@@ -306,5 +310,5 @@ extern "C" vc_status vc_decode_attn_compressed(const vc_ckv* c, const void* q, i
       hipLaunchKernelGGL((decode_generic_kernel<float, float, false>), grid, dim3(kDecThreads), lds, s, a);
   }
   VC_LAUNCHED("decode_generic_kernel");
-  return VC_OK;
+  return merge();
 }

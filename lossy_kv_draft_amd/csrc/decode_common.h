@@ -36,7 +36,6 @@ struct DecodeArgs {
   // workspace
   float* part_o;   // [B*Hkv][splits][H][d]   unnormalized outputs
   float* part_ml;  // [B*Hkv][splits][H][2]   running max (base 2) and sum
-  int* counters;   // [B*Hkv]                 splits finished (reset to 0 by the merger)
 };
 
 __device__ __forceinline__ int64_t dec_main_len(const DecodeArgs& a, int b) {
@@ -158,21 +157,17 @@ __device__ void decode_tail_partial_d128(const DecodeArgs& a, int bh, int split,
   }
 }
 
-// Called by every block after writing its partial.  The last block of a
-// (sequence, kv-head) to arrive merges all partials in split order (so the result
-// does not depend on arrival order), writes out/lse and resets the counter.
+// Merge of the split partials of one (sequence, kv-head) per workgroup, in split
+// order (the result does not depend on which split finished first).  A kernel of
+// its own: handing the partials from one workgroup to another inside the decode
+// kernel would need a device-scope release by every workgroup, which on a part
+// with several L2 caches costs a write-back of its L2 each time.
 template <typename T>
-__device__ void decode_finish(const DecodeArgs& a, int bh) {
+__global__ void __launch_bounds__(kDecThreads) decode_merge_kernel(DecodeArgs a) {
   constexpr int kHG = 16;  // heads merged per pass
-  __shared__ int s_last;
   __shared__ float2 s_ml[kDecMaxSplits][kHG];  // (max, sum) per split, then (weight, sum)
   __shared__ float2 s_fin[kHG];                // (max, sum) over all splits
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(a.counters + bh, 1) == a.splits - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  const int bh = blockIdx.x;
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int H = a.H, d = a.d, S = a.splits;
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + static_cast<int64_t>(bh) * S * H;
@@ -223,7 +218,6 @@ __device__ void decode_finish(const DecodeArgs& a, int bh) {
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) a.counters[bh] = 0;
 }
 
 }  // namespace vc

@@ -160,6 +160,11 @@ __device__ __forceinline__ int slot_token(int kb, int j) { return j < 4 ? 4 * kb
 template <typename P>
 __device__ __forceinline__ float param_f32(const P* p, int i) { return Elem<P>::load(p, i); }
 
+template <typename T>
+struct type_tag {
+  using type = T;
+};
+
 template <int KB, int VB, int NGV, typename P>
 __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) {
   constexpr int D = 128;
@@ -177,7 +182,6 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
   const int split = blockIdx.x, bh = blockIdx.y;
   if (split == a.splits - 1) {  // the full-precision tail rows form the last split
     decode_tail_partial_d128(a, bh, split, &sh_o[0][0][0]);
-    decode_finish<bf16_t>(a, bh);
     return;
   }
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
@@ -468,7 +472,6 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
       a.part_ml[(pbase * H + h) * 2 + 1] = L;
     }
   }
-  decode_finish<bf16_t>(a, bh);
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -481,42 +484,80 @@ bool decode_mfma_supported(const vc_ckv* c, int H) {
   return c->group == 16 || c->group == 32 || c->group == 64 || c->group == 128;
 }
 
+// Every instance of the kernel, chosen by (k bits, v bits, groups per V row,
+// parameter type): op.run<...>() is called for the one matching the cache.
+template <class Op>
+static void dispatch_decode_mfma(const vc_ckv* c, const Op& op) {
+  const int ngv = 128 / c->group;
+  auto by_ngv = [&](auto kb, auto vb, auto p) {
+    constexpr int KB = decltype(kb)::value, VB = decltype(vb)::value;
+    using P = typename decltype(p)::type;
+    switch (ngv) {
+      case 1: op.template run<KB, VB, 1, P>(); break;
+      case 2: op.template run<KB, VB, 2, P>(); break;
+      case 4: op.template run<KB, VB, 4, P>(); break;
+      default: op.template run<KB, VB, 8, P>(); break;
+    }
+  };
+  auto by_vb = [&](auto kb, auto p) {
+    if (c->v_bits == 2) by_ngv(kb, std::integral_constant<int, 2>{}, p);
+    else if (c->v_bits == 3) by_ngv(kb, std::integral_constant<int, 3>{}, p);
+    else by_ngv(kb, std::integral_constant<int, 4>{}, p);
+  };
+  auto by_kb = [&](auto p) {
+    if (c->k_bits == 2) by_vb(std::integral_constant<int, 2>{}, p);
+    else if (c->k_bits == 3) by_vb(std::integral_constant<int, 3>{}, p);
+    else by_vb(std::integral_constant<int, 4>{}, p);
+  };
+  if (c->param_dtype == VC_BF16) by_kb(type_tag<bf16_t>{});
+  else by_kb(type_tag<float>{});
+}
+
+// Workgroups of an instance that fit on the device at once (queried once).
+template <int KB, int VB, int NGV, typename P>
+static int decode_mfma_resident() {
+  static const int r = [] {
+    int dev = 0, cus = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 512;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 512;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_mfma_kernel<KB, VB, NGV, P>, kDecThreads, 0) !=
+        hipSuccess)
+      return 512;
+    return (per > 0 ? per : 1) * (cus > 0 ? cus : 1);
+  }();
+  return r;
+}
+
+struct ResidentOp {
+  int* out;
+  template <int KB, int VB, int NGV, typename P>
+  void run() const { *out = decode_mfma_resident<KB, VB, NGV, P>(); }
+};
+
+struct LaunchOp {
+  dim3 grid;
+  hipStream_t s;
+  const DecodeArgs* a;
+  template <int KB, int VB, int NGV, typename P>
+  void run() const {
+    hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, NGV, P>), grid, dim3(kDecThreads), 0, s, *a);
+  }
+};
+
+// Compressed-row splits sized so that they and the tail split run in one pass
+// over the device: (splits + 1) * B * Hkv workgroups <= the resident count.
 int decode_mfma_splits(const vc_ckv* c) {
   const int bh = c->B * c->Hkv;
-  int s = static_cast<int>(cdiv(512, bh));
+  int resident = 512;
+  dispatch_decode_mfma(c, ResidentOp{&resident});
+  int s = resident / bh - 1;
   if (s < 1) s = 1;
   if (s > kDecMaxSplits - 1) s = kDecMaxSplits - 1;
   return s + 1;  // + the tail split
 }
 
-template <int KB, int VB, typename P>
-static void launch_ngv(int ngv, dim3 grid, hipStream_t s, const DecodeArgs& a) {
-  switch (ngv) {
-    case 1: hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, 1, P>), grid, dim3(kDecThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, 2, P>), grid, dim3(kDecThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, 4, P>), grid, dim3(kDecThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, 8, P>), grid, dim3(kDecThreads), 0, s, a); break;
-  }
-}
-
-template <int KB, typename P>
-static void launch_vb(int vb, int ngv, dim3 grid, hipStream_t s, const DecodeArgs& a) {
-  if (vb == 2) launch_ngv<KB, 2, P>(ngv, grid, s, a);
-  else if (vb == 3) launch_ngv<KB, 3, P>(ngv, grid, s, a);
-  else launch_ngv<KB, 4, P>(ngv, grid, s, a);
-}
-
 void launch_decode_mfma(const vc_ckv* c, const DecodeArgs& a, dim3 grid, hipStream_t s) {
-  const int ngv = 128 / c->group;
-  if (c->param_dtype == VC_BF16) {
-    if (c->k_bits == 2) launch_vb<2, bf16_t>(c->v_bits, ngv, grid, s, a);
-    else if (c->k_bits == 3) launch_vb<3, bf16_t>(c->v_bits, ngv, grid, s, a);
-    else launch_vb<4, bf16_t>(c->v_bits, ngv, grid, s, a);
-  } else {
-    if (c->k_bits == 2) launch_vb<2, float>(c->v_bits, ngv, grid, s, a);
-    else if (c->k_bits == 3) launch_vb<3, float>(c->v_bits, ngv, grid, s, a);
-    else launch_vb<4, float>(c->v_bits, ngv, grid, s, a);
-  }
+  dispatch_decode_mfma(c, LaunchOp{grid, s, &a});
 }
 
 }  // namespace vc
