@@ -27,8 +27,12 @@
 //   as 8-channel fields of 8 tokens per lane; all loads of the next block are issued
 //   before the current block is computed and are only decoded when used;
 // * the 4 waves of a block cover consecutive token ranges and are merged in LDS; the
-//   block writes one partial per split, the tail rows are a split of their own, and
-//   the last block to finish merges all splits in split order.
+//   block writes one partial per split and the tail rows are a split of their own;
+//   the splits are merged in split order by decode_merge_kernel, launched next (a
+//   merge by the last block to finish would need a device-scope release by every
+//   block, i.e. an L2 write-back per block on a part with one L2 per XCD);
+// * the number of splits is chosen so that all blocks, tail included, are resident
+//   at once (occupancy times compute units, queried from the runtime).
 //
 // Precision: K_hat, V_hat, q and p are f16 (11-bit significands) with float32
 // accumulation; against float64 attention on the outlier workloads the error is
