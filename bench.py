@@ -47,7 +47,40 @@ def parse():
     p.add_argument("--e2e-ctx", type=int, default=32768, help="prompt length of the end-to-end rounds")
     p.add_argument("--e2e-gen", type=int, default=256, help="tokens generated per sequence")
     p.add_argument("--e2e-slots", type=int, default=2, help="device layer slots of the staged full KV")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="first run a plain device copy of this many MiB (3 times): the reference dispatch that "
+                        "scales hardware traffic counters to bytes")
     return p.parse_args()
+
+
+DECODE_SOURCES = ("decode_mfma.hip", "decode_common.h", "decode.hip", "common.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_llama8b_n32k_hbm_traffic.txt")
+
+
+def decode_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "lossy_kv_draft_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per decode launch from the committed counter summary, if it was
+    taken on the current decode sources and this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(line[2:].split(":", 1) for line in fh if line.startswith("# ") and ":" in line)
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_sha256") != decode_source_hash() or kv.get("workload") != workload_name:
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def decode_bytes(w, n_ctx, tail):
@@ -349,6 +382,14 @@ def main():
     import torch
     w = workload(a.workload)
     torch.cuda.set_device(0)
+    if a.copy_calibration:
+        n = a.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     st = setup(w, a.copies)
     for _ in range(a.warmup):
         run_step(st)
@@ -400,10 +441,10 @@ def main():
                      "tokens_accept": round(tok_ms / a.steps, 4)},
         "wall_ms_per_step": round(wall / a.steps * 1e3, 4),
         "compress_ms": round(st["comp_ms"], 4),
-        "roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel (quant)" if w.method == "quant"
-                     else "decode_generic_kernel (kept rows)",
+        "roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel + decode_merge_kernel (quant)" if w.method == "quant"
+                     else "decode_generic_kernel + decode_merge_kernel (kept rows)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
                      "bytes_per_launch": int(per_launch), "avg_launch_us": round(dec_avg_ms * 1e3, 3)},
     }
     if not a.no_stage:
