@@ -164,6 +164,63 @@ __device__ __forceinline__ int slot_token(int kb, int j) { return j < 4 ? 4 * kb
 template <typename P>
 __device__ __forceinline__ float param_f32(const P* p, int i) { return Elem<P>::load(p, i); }
 
+// Global -> LDS copies for the decode ring.  The copy instruction writes 16 bytes
+// per active lane at (M0 + 16 * lane); it is issued from inline assembly so that the
+// compiler does not treat every later LDS read as depending on every copy in flight
+// (which would drain the ring at each block): the kernel places the vmcnt waits
+// itself.  Loads the compiler issues are still waited for correctly, since copies
+// it does not know of can only make its own waits stricter.
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+
+// Slot layout of one 32-token block and the ring depth for one kernel instance.
+template <int KB, int VB, int NGV, typename P>
+struct DecRing {
+  static constexpr int kD = 128;
+  static constexpr int kG = kD / NGV;
+  static constexpr int kNKG = kG >= 32 ? 1 : 2;                        // K groups per block
+  static constexpr int kKC = 32 * kD * KB / 8;                         // K code bytes
+  static constexpr int kVC = 32 * kD * VB / 8;                         // V code bytes
+  static constexpr int kVP = 32 * NGV * static_cast<int>(sizeof(P));  // V scale (and zero) bytes
+  static constexpr int kKPG = kD * static_cast<int>(sizeof(P));        // one K parameter row
+  static constexpr int kOffK = 0;
+  static constexpr int kOffV = kOffK + kKC;
+  static constexpr int kOffVP = kOffV + kVC;
+  static constexpr int kOffKP = kOffVP + 2 * kVP;
+  static constexpr int kSlot = kOffKP + kNKG * 2 * kKPG;
+  static constexpr int pieces(int bytes) { return (bytes + 1023) / 1024; }
+  static constexpr int kInstr = pieces(kKC) + pieces(kVC) + pieces(2 * kVP) + kNKG * pieces(2 * kKPG);
+  // two workgroups of 4 waves per compute unit: 4 * depth * slot <= ~79 KB each
+  static constexpr int kDepthRaw = 20224 / kSlot;
+  static constexpr int kDepth = kDepthRaw < 2 ? 2 : (kDepthRaw > 8 ? 8 : kDepthRaw);
+  static_assert(kSlot % 16 == 0 && kVP % 16 == 0 && kKPG % 16 == 0, "16-byte pieces");
+  static_assert((kDepth - 1) * kInstr <= 63, "vmcnt range");
+
+  // `bytes` contiguous bytes from src into LDS at `lds`
+  static __device__ __forceinline__ void copy_span(const unsigned char* src, int bytes, uint32_t lds, int lane) {
+#pragma unroll
+    for (int c = 0; c < pieces(bytes); ++c) {
+      const int off = 1024 * c + 16 * lane;
+      if (off < bytes) lds_copy16(src + off, lds + 1024 * c);
+    }
+  }
+  // `bytes` from a, then `bytes` from b, into LDS at `lds` back to back
+  static __device__ __forceinline__ void copy_pair(const unsigned char* a, const unsigned char* b, int bytes,
+                                                   uint32_t lds, int lane) {
+#pragma unroll
+    for (int c = 0; c < pieces(2 * bytes); ++c) {
+      const int off = 1024 * c + 16 * lane;
+      if (off < 2 * bytes) lds_copy16(off < bytes ? a + off : b + (off - bytes), lds + 1024 * c);
+    }
+  }
+  static __device__ __forceinline__ void wait_ahead() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kDepth - 1) * kInstr) : "memory");
+  }
+  static __device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+  static __device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+};
+
 template <typename T>
 struct type_tag {
   using type = T;
@@ -179,13 +236,18 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
   constexpr int HW = D * static_cast<int>(sizeof(P)) / 4;  // words per K parameter row
   constexpr int KPW = 2 * HW / 64;                    // K-parameter words per lane
   constexpr int NKG = G >= 32 ? 1 : 2;                // K groups per 32-token block
-  __shared__ float sh_o[4][16][D];
+  using Ring = DecRing<KB, VB, NGV, P>;
+  // per-wave rings of block slots; after the main loop the same memory holds the
+  // waves' outputs for the merge (and, in the tail block, the tail pass's scratch)
+  __shared__ __attribute__((aligned(16))) unsigned char ring[4 * Ring::kDepth * Ring::kSlot];
+  static_assert(4 * Ring::kDepth * Ring::kSlot >= 4 * 16 * D * sizeof(float), "merge buffer does not fit");
+  static_assert(4 * Ring::kDepth * Ring::kSlot >= 5 * 1024 * sizeof(float), "tail scratch does not fit");
+  float (*sh_o)[16][D] = reinterpret_cast<float (*)[16][D]>(ring);
   __shared__ float sh_m[4][16], sh_l[4][16];
-  __shared__ uint32_t sh_kp[4][2 * HW];
 
   const int split = blockIdx.x, bh = blockIdx.y;
   if (split == a.splits - 1) {  // the full-precision tail rows form the last split
-    decode_tail_partial_d128(a, bh, split, &sh_o[0][0][0]);
+    decode_tail_partial_d128(a, bh, split, reinterpret_cast<float*>(ring));
     return;
   }
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
@@ -241,21 +303,48 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
   uint32_t ks2[4][4], kz2[4][4];
   int g_cur = -1;
 
-  // Raw loads of one block, issued one block ahead of use and decoded only when used
-  // (arithmetic on a fresh load would make the wave wait for it).  This path
-  // requires the capacity to be a multiple of 32 rows, so every row of a block that
-  // starts before the end is inside the allocation; rows past the end are masked
-  // (scores -inf, V scale and zero 0), which keeps the loads branch-free.
+  // The block's bytes (K codes, V codes, V parameters, the K parameters of its
+  // group(s)) are copied global -> LDS by the wave itself (16 bytes per lane per
+  // instruction, Ring::kInstr instructions per block) kDepth blocks ahead, into a
+  // ring of slots private to the wave; a block is read from its slot into registers
+  // only when it is processed.  Rows of a block that starts before the end are
+  // inside the allocation (capacity is a multiple of 32); rows past the end are
+  // masked (scores -inf, V scale and zero 0).
+  unsigned char* const wring = ring + wave * Ring::kDepth * Ring::kSlot;
+  const int nblk = t_end > t_begin ? (t_end - t_begin + 31) / 32 : 0;
+  const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kcodes);
+  const unsigned char* vbytes = reinterpret_cast<const unsigned char*>(vcodes);
+  const unsigned char* ksb = reinterpret_cast<const unsigned char*>(kscale);
+  const unsigned char* kzb = reinterpret_cast<const unsigned char*>(kzero);
+  const unsigned char* vsb = reinterpret_cast<const unsigned char*>(vscale);
+  const unsigned char* vzb = reinterpret_cast<const unsigned char*>(vzero);
+  auto issue = [&](int i) {  // block i of this wave's range into slot i % kDepth
+    const uint32_t t0 = static_cast<uint32_t>(t_begin + 32 * i);
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(wring + (i % Ring::kDepth) * Ring::kSlot)));
+    // codes: 32 consecutive rows of each
+    Ring::copy_span(kbytes + static_cast<size_t>(t0) * KW * 4, Ring::kKC, lds + Ring::kOffK, lane);
+    Ring::copy_span(vbytes + static_cast<size_t>(t0) * VW * 4, Ring::kVC, lds + Ring::kOffV, lane);
+    // V parameters: scales of the 32 rows, then zeros
+    Ring::copy_pair(vsb + static_cast<size_t>(t0) * NGV * sizeof(P), vzb + static_cast<size_t>(t0) * NGV * sizeof(P),
+                    Ring::kVP, lds + Ring::kOffVP, lane);
+    // K parameters of the block's group(s): [scale row, zero row] per group
+    const uint32_t g0 = t0 / G;
+#pragma unroll
+    for (int gi = 0; gi < NKG; ++gi)
+      Ring::copy_pair(ksb + static_cast<size_t>(g0 + gi) * D * sizeof(P), kzb + static_cast<size_t>(g0 + gi) * D * sizeof(P),
+                      D * sizeof(P), lds + Ring::kOffKP + gi * 2 * D * sizeof(P), lane);
+  };
+
   struct Blk {
     uint32_t kw[2][KB];
     uint32_t vw[8][VWR];
     uint32_t vs[8], vz[8];  // word holding the slot token's group-gv parameter
-    uint32_t kp[NKG][KPW];  // this lane's share of the block's K group parameters
   };
-  auto load_blk = [&](int t0, Blk& x) {
+  auto read_blk = [&](const unsigned char* slot, Blk& x) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const uint32_t* src = kcodes + (static_cast<uint32_t>(t0 + 16 * tt) * KW + k_lane);
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(slot + Ring::kOffK) + (16 * tt + n) * KW + kb * KB;
       if constexpr (KB == 4) {
         const uint4 v = *reinterpret_cast<const uint4*>(src);
         x.kw[tt][0] = v.x; x.kw[tt][1] = v.y; x.kw[tt][2] = v.z; x.kw[tt][3] = v.w;
@@ -267,37 +356,22 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
         for (int i = 0; i < KB; ++i) x.kw[tt][i] = src[i];
       }
     }
+    const uint32_t* vw = reinterpret_cast<const uint32_t*>(slot + Ring::kOffV);
+    const uint32_t* vp = reinterpret_cast<const uint32_t*>(slot + Ring::kOffVP);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t tok = static_cast<uint32_t>(t0 + slot_token(kb, j));
-      x.vw[j][0] = vcodes[tok * VW + vfw];
-      if constexpr (VB == 3) x.vw[j][1] = vcodes[tok * VW + vfw2];
-      if constexpr (sizeof(P) == 2) {
-        const uint32_t e = (tok * NGV + gv) >> 1;
-        x.vs[j] = reinterpret_cast<const uint32_t*>(vscale)[e];
-        x.vz[j] = reinterpret_cast<const uint32_t*>(vzero)[e];
-      } else {
-        x.vs[j] = reinterpret_cast<const uint32_t*>(vscale)[tok * NGV + gv];
-        x.vz[j] = reinterpret_cast<const uint32_t*>(vzero)[tok * NGV + gv];
-      }
-    }
-#pragma unroll
-    for (int gi = 0; gi < NKG; ++gi) {
-      const uint32_t g = static_cast<uint32_t>((t0 + 16 * gi) / G);
-#pragma unroll
-      for (int i = 0; i < KPW; ++i) {
-        const uint32_t wi = lane * KPW + i;  // word of [scale row, zero row]
-        x.kp[gi][i] = wi < HW ? kscale[g * HW + wi] : kzero[g * HW + (wi - HW)];
-      }
+      const uint32_t tok = static_cast<uint32_t>(slot_token(kb, j));
+      x.vw[j][0] = vw[tok * VW + vfw];
+      if constexpr (VB == 3) x.vw[j][1] = vw[tok * VW + vfw2];
+      const uint32_t e = sizeof(P) == 2 ? (tok * NGV + gv) >> 1 : tok * NGV + gv;
+      x.vs[j] = vp[e];
+      x.vz[j] = vp[Ring::kVP / 4 + e];
     }
   };
-  // the (scale, zero) rows of a new K group: exchanged through LDS, then the lane's
+  // the (scale, zero) rows of a new K group, read from the block's slot; the lane's
   // 32 channels are packed as f16 pairs in contraction order
-  auto use_kp = [&](const uint32_t* kp) {
-#pragma unroll
-    for (int i = 0; i < KPW; ++i) sh_kp[wave][lane * KPW + i] = kp[i];
-    __builtin_amdgcn_wave_barrier();
-    const P* sp = reinterpret_cast<const P*>(&sh_kp[wave][0]) + 32 * kb;
+  auto use_kp = [&](const unsigned char* kp) {
+    const P* sp = reinterpret_cast<const P*>(kp) + 32 * kb;
     const P* zp = sp + D;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -324,7 +398,6 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
         kz2[s][jj] = pack_h2(zv[korder<KB>(2 * jj)], zv[korder<KB>(2 * jj + 1)]);
       }
     }
-    __builtin_amdgcn_wave_barrier();
   };
   // V parameter (as float) of a slot token from its raw word
   // (with one group per token the element parity is the slot's parity; otherwise the
@@ -338,7 +411,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
     }
   };
 
-  auto process = [&](int t0, const Blk& cur, auto full_tag) {
+  auto process = [&](int t0, const Blk& cur, const unsigned char* slot, auto full_tag) {
     constexpr bool full = decltype(full_tag)::value;  // every row of the block is live
     // ---- S^T = K_hat Q^T for the two 16-token tiles
     f4_t sc[2];
@@ -347,7 +420,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
       sc[tt] = f4_t{0.f, 0.f, 0.f, 0.f};
       const int g = (t0 + 16 * tt) / G;
       if (g != g_cur) {  // wave-uniform
-        use_kp(cur.kp[NKG == 1 ? 0 : tt]);
+        use_kp(slot + Ring::kOffKP + (NKG == 1 ? 0 : tt) * 2 * D * sizeof(P));
         g_cur = g;
       }
 #pragma unroll
@@ -424,26 +497,38 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
     }
   };
 
-  // Full blocks: two prefetch buffers in turn.  The prefetch is unconditional (the
-  // last full block re-loads itself) because a load issued on only one path makes the
-  // compiler wait for every outstanding load where the paths join.  The partial last
-  // block, if any, is loaded and processed once after the loop.
+  // Main loop over the wave's blocks.  Before block i is read, its copies must have
+  // landed: kInstr copies are issued per block, so while blocks i+1 .. i+kDepth-1 are
+  // still in flight the wait is vmcnt((kDepth-1) kInstr); near the end, where fewer
+  // blocks follow, everything is drained.  The slot is refilled (block i + kDepth)
+  // only after block i has been processed, so its reads are complete by then.
   using Full = std::integral_constant<bool, true>;
   using Part = std::integral_constant<bool, false>;
-  Blk bufA, bufB;
-  const int t_full = t_end > t_begin ? t_begin + ((t_end - t_begin) / 32) * 32 : t_begin;
-  if (t_full > t_begin) load_blk(t_begin, bufA);
-  for (int t0 = t_begin; t0 < t_full; t0 += 64) {
-    load_blk(t0 + 32 < t_full ? t0 + 32 : t0, bufB);
-    process(t0, bufA, Full{});
-    if (t0 + 32 >= t_full) break;
-    load_blk(t0 + 64 < t_full ? t0 + 64 : t0 + 32, bufA);
-    process(t0 + 32, bufB, Full{});
+  const int nfull = t_end > t_begin ? (t_end - t_begin) / 32 : 0;  // blocks with every row live
+  // the query loads complete before the first copies are issued (a wait the compiler
+  // tracks, so it adds none behind the copies, which would drain the ring)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  for (int i = 0; i < nblk && i < Ring::kDepth; ++i) issue(i);
+  for (int i = 0; i < nfull; ++i) {
+    if (i + Ring::kDepth <= nblk) Ring::wait_ahead();
+    else Ring::wait_all();
+    const unsigned char* slot = wring + (i % Ring::kDepth) * Ring::kSlot;
+    Blk cur;
+    read_blk(slot, cur);
+    process(t_begin + 32 * i, cur, slot, Full{});
+    if (i + Ring::kDepth < nblk) {
+      Ring::lds_reads_done();
+      issue(i + Ring::kDepth);
+    }
   }
-  if (t_full < t_end) {
-    load_blk(t_full, bufA);
-    process(t_full, bufA, Part{});
+  Ring::wait_all();
+  if (nfull < nblk) {  // the partial last block (its copies were issued above)
+    const unsigned char* slot = wring + (nfull % Ring::kDepth) * Ring::kSlot;
+    Blk cur;
+    read_blk(slot, cur);
+    process(t_begin + 32 * nfull, cur, slot, Part{});
   }
+  __syncthreads();  // every wave's copies have landed before the ring is reused
 
   // ---- merge the 4 waves in LDS, write this split's partial
   l += __shfl_xor(l, 16);
