@@ -80,26 +80,34 @@ __device__ __forceinline__ constexpr int korder(int j) {
   else return (j & 1) ? (j >> 1) + 4 : (j >> 1);         // 0,4,1,5,2,6,3,7
 }
 
-// K: the four f16 magic pairs of k-step s from a lane's 32-channel chunk (KB words);
-// pair jj holds channels korder(2jj), korder(2jj+1).
+// K codes enter the score product as the f16 values 64 + c: the code sits in bits
+// 4..7 of a byte under the exponent byte 0x54 (64.0).  The scale is folded into the
+// query and the zero-point and the offset into a per-group bias (see use_kp), so K
+// needs no dequantization arithmetic; the offset is 64 rather than 1024 so that the
+// cancellation it causes in the float32 accumulation stays small.
+constexpr uint32_t kMagicK = 0x54545454u;
+__device__ __forceinline__ uint32_t kmagic(uint32_t x, uint32_t sel) { return __builtin_amdgcn_perm(kMagicK, x, sel); }
+
+// K: the four f16 pairs (64 + c) of k-step s from a lane's 32-channel chunk (KB
+// words); pair jj holds channels korder(2jj), korder(2jj+1).
 template <int KB>
 __device__ __forceinline__ void kpairs(const uint32_t* w, int s, uint32_t (&out)[4]) {
   if constexpr (KB == 4) {
     const uint32_t x = w[s];
-    const uint32_t lo = x & 0x0F0F0F0Fu;         // channels 0, 2, 4, 6
-    const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // channels 1, 3, 5, 7
-    out[0] = magic_bytes(lo, kSel01);
-    out[1] = magic_bytes(lo, kSel23);
-    out[2] = magic_bytes(hi, kSel01);
-    out[3] = magic_bytes(hi, kSel23);
+    const uint32_t lo = (x << 4) & 0xF0F0F0F0u;  // channels 0, 2, 4, 6
+    const uint32_t hi = x & 0xF0F0F0F0u;         // channels 1, 3, 5, 7
+    out[0] = kmagic(lo, kSel01);
+    out[1] = kmagic(lo, kSel23);
+    out[2] = kmagic(hi, kSel01);
+    out[3] = kmagic(hi, kSel23);
   } else if constexpr (KB == 2) {
     const uint32_t x = w[s >> 1];
     const uint32_t sel = (s & 1) ? kSel23 : kSel01;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t m = (x >> (2 * r)) & 0x03030303u;  // bytes: codes r, 4+r, 8+r, 12+r of the word
-      out[r] = magic_bytes(m, sel);
-    }
+    // bytes: codes r, 4+r, 8+r, 12+r of the word, each moved to bits 4..5
+    out[0] = kmagic((x << 4) & 0x30303030u, sel);
+    out[1] = kmagic((x << 2) & 0x30303030u, sel);
+    out[2] = kmagic(x & 0x30303030u, sel);
+    out[3] = kmagic((x >> 2) & 0x30303030u, sel);
   } else {  // 3 bits: 24-bit fields at bit 24 s of a 96-bit chunk
     uint32_t f;
     if (s == 0) f = w[0] & 0xFFFFFFu;
@@ -107,8 +115,10 @@ __device__ __forceinline__ void kpairs(const uint32_t* w, int s, uint32_t (&out)
     else if (s == 2) f = __builtin_amdgcn_alignbit(w[2], w[1], 16) & 0xFFFFFFu;
     else f = w[2] >> 8;
     const uint32_t u = (f & 0xFFFu) | ((f >> 12) << 16);  // codes 0..3 low half, 4..7 high half
-#pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = ((u >> (3 * j)) & 0x00070007u) | 0x64006400u;
+    out[0] = ((u << 4) & 0x00700070u) | 0x54005400u;       // code j of each half to bits 4..6
+    out[1] = ((u << 1) & 0x00700070u) | 0x54005400u;
+    out[2] = ((u >> 2) & 0x00700070u) | 0x54005400u;
+    out[3] = ((u >> 5) & 0x00700070u) | 0x54005400u;
   }
 }
 
@@ -300,7 +310,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = f4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
-  uint32_t ks2[4][4], kz2[4][4];
+  h8_t qt[4];  // queries times the current K group's scales (the B operand of the scores)
+  f4_t kbias;  // sum_c q_c z_c - 64 sum_c qt_c of the current group, per q-head column
   int g_cur = -1;
 
   // The block's bytes (K codes, V codes, V parameters, the K parameters of its
@@ -368,11 +379,17 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
       x.vz[j] = vp[Ring::kVP / 4 + e];
     }
   };
-  // the (scale, zero) rows of a new K group, read from the block's slot; the lane's
-  // 32 channels are packed as f16 pairs in contraction order
+  // A new K group: the lane's 32 channels of its (scale, zero) rows are read from the
+  // block's slot and packed as f16 pairs in contraction order; the query operand
+  // becomes q * s and the bias sum_c q_c z_c - 64 sum_c (q s)_c is formed on the
+  // matrix cores (every row of its A operands is the same, so every score row of a
+  // column receives its column's bias).
   auto use_kp = [&](const unsigned char* kp) {
     const P* sp = reinterpret_cast<const P*>(kp) + 32 * kb;
     const P* zp = sp + D;
+    constexpr uint32_t kNeg64 = 0xD400D400u;  // (-64, -64) in f16
+    const uint32_t neg64[4] = {kNeg64, kNeg64, kNeg64, kNeg64};
+    kbias = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       float sv[8], zv[8];
@@ -392,20 +409,29 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
           zv[c] = param_f32<P>(zp, 8 * s + c);
         }
       }
+      uint32_t s2[4], z2[4], q2[4];
+      const h8_t qs = bq[s];
+      const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qs);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        ks2[s][jj] = pack_h2(sv[korder<KB>(2 * jj)], sv[korder<KB>(2 * jj + 1)]);
-        kz2[s][jj] = pack_h2(zv[korder<KB>(2 * jj)], zv[korder<KB>(2 * jj + 1)]);
+        s2[jj] = pack_h2(sv[korder<KB>(2 * jj)], sv[korder<KB>(2 * jj + 1)]);
+        z2[jj] = pack_h2(zv[korder<KB>(2 * jj)], zv[korder<KB>(2 * jj + 1)]);
+        q2[jj] = as_u32(as_h2(qw[jj]) * as_h2(s2[jj]));
       }
+      qt[s] = __builtin_bit_cast(h8_t, q2);
+      kbias = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, z2), bq[s], kbias, 0, 0, 0);
+      kbias = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, neg64), qt[s], kbias, 0, 0, 0);
     }
   };
   // V parameter (as float) of a slot token from its raw word
   // (with one group per token the element parity is the slot's parity; otherwise the
   // token index is even times NGV and the parity is the group's)
+  // (bf16 parameters: one byte permute moves the lane's half of the word to the top)
+  const uint32_t vsel = (gv & 1) ? 0x03020C0Cu : 0x01000C0Cu;
   auto vparam = [&](uint32_t w, int j) -> float {
     if constexpr (sizeof(P) == 2) {
-      const bool high = NGV == 1 ? (j & 1) : (gv & 1);
-      return __uint_as_float(high ? (w & 0xFFFF0000u) : (w << 16));
+      if constexpr (NGV == 1) return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+      else return __uint_as_float(__builtin_amdgcn_perm(0u, w, vsel));
     } else {
       return __uint_as_float(w);
     }
@@ -417,19 +443,17 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
     f4_t sc[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      sc[tt] = f4_t{0.f, 0.f, 0.f, 0.f};
       const int g = (t0 + 16 * tt) / G;
       if (g != g_cur) {  // wave-uniform
         use_kp(slot + Ring::kOffKP + (NKG == 1 ? 0 : tt) * 2 * D * sizeof(P));
         g_cur = g;
       }
+      sc[tt] = kbias;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        uint32_t mp[4], av[4];
+        uint32_t mp[4];
         kpairs<KB>(cur.kw[tt], s, mp);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) av[jj] = dequant_pair(mp[jj], ks2[s][jj], kz2[s][jj]);
-        sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, av), bq[s], sc[tt], 0, 0, 0);
+        sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, mp), qt[s], sc[tt], 0, 0, 0);
       }
     }
 
@@ -439,10 +463,13 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) s8[4 * tt + i] = (full || t0 + 16 * tt + 4 * kb + i < t_end) ? sc[tt][i] : -INFINITY;
+    // the column maximum is only needed when some score exceeds the running maximum
+    // by more than 8 (probabilities up to 2^8 are fine in f16): a wave vote on the
+    // lanes' own maxima, then the cross-lane maximum inside the (rare) rescale
     float mb = fmaxf(fmaxf(fmaxf(s8[0], s8[1]), fmaxf(s8[2], s8[3])), fmaxf(fmaxf(s8[4], s8[5]), fmaxf(s8[6], s8[7])));
-    mb = fmaxf(mb, __shfl_xor(mb, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
     if (__any(mb > m + 8.f)) {
+      mb = fmaxf(mb, __shfl_xor(mb, 16));
+      mb = fmaxf(mb, __shfl_xor(mb, 32));
       const float mn = fmaxf(m, mb);
       const float al = __builtin_amdgcn_exp2f(m - mn);  // m = -inf on the first block: 0
 #pragma unroll
