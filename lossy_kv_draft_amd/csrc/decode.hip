@@ -277,10 +277,11 @@ extern "C" vc_status vc_decode_attn_compressed(const vc_ckv* c, const void* q, i
   dim3 grid(S, static_cast<unsigned>(bh));
   hipStream_t s = as_stream(stream);
   auto merge = [&]() -> vc_status {
+    const dim3 mgrid(static_cast<unsigned>(bh), static_cast<unsigned>(H));
     if (c->kv_dtype == VC_BF16)
-      hipLaunchKernelGGL(decode_merge_kernel<bf16_t>, dim3(static_cast<unsigned>(bh)), dim3(kDecThreads), 0, s, a);
+      hipLaunchKernelGGL(decode_merge_kernel<bf16_t>, mgrid, dim3(kDecThreads), 0, s, a);
     else
-      hipLaunchKernelGGL(decode_merge_kernel<float>, dim3(static_cast<unsigned>(bh)), dim3(kDecThreads), 0, s, a);
+      hipLaunchKernelGGL(decode_merge_kernel<float>, mgrid, dim3(kDecThreads), 0, s, a);
     VC_LAUNCHED("decode_merge_kernel");
     return VC_OK;
   };

@@ -164,59 +164,59 @@ __device__ void decode_tail_partial_d128(const DecodeArgs& a, int bh, int split,
 // with several L2 caches costs a write-back of its L2 each time.
 template <typename T>
 __global__ void __launch_bounds__(kDecThreads) decode_merge_kernel(DecodeArgs a) {
-  constexpr int kHG = 16;  // heads merged per pass
-  __shared__ float2 s_ml[kDecMaxSplits][kHG];  // (max, sum) per split, then (weight, sum)
-  __shared__ float2 s_fin[kHG];                // (max, sum) over all splits
-  const int bh = blockIdx.x;
+  // one workgroup per (sequence, kv-head) and q-head of it; splits <= 64
+  __shared__ float s_w[kDecMaxSplits];
+  __shared__ float s_fin[2];
+  __shared__ float s_part[kDecThreads];
+  const int bh = blockIdx.x, h = blockIdx.y;
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int H = a.H, d = a.d, S = a.splits;
-  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + static_cast<int64_t>(bh) * S * H;
-  const float* po = a.part_o + static_cast<int64_t>(bh) * S * H * d;
-  T* out = static_cast<T*>(a.out);
-  for (int h0 = 0; h0 < H; h0 += kHG) {
-    const int hg = min(kHG, H - h0);
-    // every split's (max, sum) of these heads, loaded at once
-    for (int e = threadIdx.x; e < S * hg; e += blockDim.x) {
-      const int sp = e / hg, hh = e % hg;
-      s_ml[sp][hh] = ml[static_cast<int64_t>(sp) * H + h0 + hh];
+  const int tid = threadIdx.x;
+  if (tid < 64) {  // split weights: a wave holds one split per lane
+    float m = -INFINITY, l = 0.f;
+    if (tid < S) {
+      const float2 v = reinterpret_cast<const float2*>(a.part_ml)[(static_cast<int64_t>(bh) * S + tid) * H + h];
+      m = v.x;
+      l = v.y;
     }
-    __syncthreads();
-    // per head: overall max, split weights and the sum, in split order
-    if (threadIdx.x < hg) {
-      const int hh = threadIdx.x;
-      float M = -INFINITY;
-      for (int sp = 0; sp < S; ++sp) M = fmaxf(M, s_ml[sp][hh].x);
-      float L = 0.f;
-      for (int sp = 0; sp < S; ++sp) {
-        const float m = s_ml[sp][hh].x;
-        const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-        L = fmaf(s_ml[sp][hh].y, w, L);
-        s_ml[sp][hh].x = w;
-      }
-      s_fin[hh] = make_float2(M, L);
+    const float M = warp_max(m);
+    const float w = m == -INFINITY ? 0.f : exp2f(m - M);
+    const float L = warp_sum(l * w);
+    if (tid < S) s_w[tid] = w;
+    if (tid == 0) {
+      s_fin[0] = M;
+      s_fin[1] = L;
     }
-    __syncthreads();
-    // outputs: split partials weighted and summed in split order, 8 loads in flight
-    for (int i = threadIdx.x; i < hg * d; i += blockDim.x) {
-      const int hh = i / d, c = i % d;
-      const float* p = po + static_cast<int64_t>(h0 + hh) * d + c;
-      float O = 0.f;
-      for (int s0 = 0; s0 < S; s0 += 8) {
-        float v[8];
+  }
+  __syncthreads();
+  // tpo threads per output channel, each summing a contiguous share of the splits
+  const int tpo = kDecThreads / d;
+  const int c = tid % d, part = tid / d;
+  const int per = (S + tpo - 1) / tpo;
+  const int s_lo = part * per, s_hi = min(S, s_lo + per);
+  float O = 0.f;
+  if (part < tpo) {
+    const float* p = a.part_o + (static_cast<int64_t>(bh) * S * H + h) * d + c;
+    const int64_t stride = static_cast<int64_t>(H) * d;
+    for (int s0 = s_lo; s0 < s_hi; s0 += 16) {
+      float v[16];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = p[static_cast<int64_t>(min(s0 + j, S - 1)) * H * d];
+      for (int j = 0; j < 16; ++j) v[j] = p[min(s0 + j, s_hi - 1) * stride];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (s0 + j < S) O = fmaf(v[j], s_ml[s0 + j][hh].x, O);
-      }
-      const float L = s_fin[hh].y;
-      const int64_t oi = (static_cast<int64_t>(b) * a.Hkv * H + hk * H + h0 + hh) * d + c;
-      Elem<T>::store(out, oi, L > 0.f ? O / L : 0.f);
-      if (a.lse && c == 0)
-        a.lse[static_cast<int64_t>(b) * a.Hkv * H + hk * H + h0 + hh] =
-            L > 0.f ? (s_fin[hh].x + log2f(L)) * kLn2 : -INFINITY;
+      for (int j = 0; j < 16; ++j)
+        if (s0 + j < s_hi) O = fmaf(v[j], s_w[s0 + j], O);
     }
-    __syncthreads();
+  }
+  s_part[tid] = O;
+  __syncthreads();
+  if (tid < d) {
+    float v = 0.f;
+    for (int q = 0; q < tpo; ++q) v += s_part[q * d + tid];
+    const float L = s_fin[1];
+    const int64_t oi = (static_cast<int64_t>(b) * a.Hkv * H + hk * H + h) * d + tid;
+    Elem<T>::store(static_cast<T*>(a.out), oi, L > 0.f ? v / L : 0.f);
+    if (a.lse && tid == 0)
+      a.lse[static_cast<int64_t>(b) * a.Hkv * H + hk * H + h] = L > 0.f ? (s_fin[0] + log2f(L)) * kLn2 : -INFINITY;
   }
 }
 
