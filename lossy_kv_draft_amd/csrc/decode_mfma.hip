@@ -10,10 +10,17 @@
 // * one wave processes 32-token blocks of one (sequence, kv-head); the q-heads that
 //   read the kv-head are the 16 columns of the B operand (zero beyond Hq/Hkv), so
 //   every packed row is read from HBM once for all of them;
-// * a code c becomes the f16 value 1024 + c by placing it under the exponent byte
-//   0x64 with one v_perm_b32 per pair of codes (the byte 0x64 is taken from a
-//   constant operand), then (x - 1024) * s + z is evaluated with packed f16 adds and
-//   FMAs, s and z being the group's scale and zero;
+// * a code c becomes the f16 value 64 + c by moving it to bits 4.. of a byte and
+//   placing it under the exponent byte 0x54 with one v_perm_b32 per pair of codes;
+// * K needs no dequantization: with per-channel scale s and zero z, q . k_hat =
+//   sum_c (q s)_c (64 + c) + [sum_c q_c z_c - 64 sum_c (q s)_c]; the query operand
+//   becomes q * s (packed f16 multiplies) and the bracket, a bias per q-head and K
+//   group, is formed on the matrix cores when the group changes and seeds the score
+//   accumulator;
+// * V (per-token scale and zero): each pair becomes c * s with one packed fused
+//   multiply-add of (64 + c) by s with addend -64 s (exact, rounded once); the
+//   zero-point term sum_t p_t z_t is one extra product per block (its A operand is
+//   the tokens' zeros) added to every channel tile at the end;
 // * S^T = K_hat Q^T for two 16-token tiles, online softmax per q-head in base 2 with
 //   a lazy rescale (only when the block maximum exceeds the running one by more than
 //   8, i.e. probabilities stay below 2^8), probabilities rounded to f16, then
@@ -34,10 +41,10 @@
 // * the number of splits is chosen so that all blocks, tail included, are resident
 //   at once (occupancy times compute units, queried from the runtime).
 //
-// Precision: K_hat, V_hat, q and p are f16 (11-bit significands) with float32
-// accumulation; against float64 attention on the outlier workloads the error is
-// about 1e-4, far below the bf16 output resolution.  Values must lie within the f16
-// range (|x| < 65504).
+// Precision: q * s, c * s, the zero-points and p are f16 (11-bit significands) with
+// float32 accumulation; against float64 attention on the outlier workloads the error
+// is about 1e-4, far below the bf16 output resolution.  Values and 64 * s must lie
+// within the f16 range (65504).
 
 #include <type_traits>
 
@@ -54,11 +61,10 @@ constexpr uint32_t kMagic = 0x64646464u;  // exponent byte of 1024.0 in f16, in 
 __device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
 __device__ __forceinline__ uint32_t as_u32(h2_t h) { return __builtin_bit_cast(uint32_t, h); }
 
-// pair of f16 values (1024 + c0, 1024 + c1) -> (c0 * s0 + z0, c1 * s1 + z1)
-__device__ __forceinline__ uint32_t dequant_pair(uint32_t magic, uint32_t s2, uint32_t z2) {
-  const h2_t off = {static_cast<_Float16>(-1024.f), static_cast<_Float16>(-1024.f)};
-  const h2_t c = as_h2(magic) + off;  // exact: small integers
-  return as_u32(__builtin_elementwise_fma(c, as_h2(s2), as_h2(z2)));
+// pair of f16 values (64 + c0, 64 + c1) -> (c0 * s0, c1 * s1): one fused multiply-add
+// with the addend -64 s (exact: a power-of-two multiple), rounded once
+__device__ __forceinline__ uint32_t scale_pair(uint32_t magic, uint32_t s2, uint32_t ns2) {
+  return as_u32(__builtin_elementwise_fma(as_h2(magic), as_h2(s2), as_h2(ns2)));
 }
 
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
@@ -130,41 +136,47 @@ __device__ __forceinline__ constexpr int vorder(int t) {
   else return t;
 }
 
-// V: for two tokens' 8-code fields fa, fb, the f16 magic pair (token a, token b) of
-// each of the 8 channels, tile t holding channel vorder(t).
+// V: for two tokens' 8-code fields fa, fb, the f16 pair (64 + a_c, 64 + b_c) of each
+// of the 8 channels, tile t holding channel vorder(t) (codes moved to bits 4.. of a
+// byte under the exponent byte 0x54, as for K).
 template <int VB>
 __device__ __forceinline__ void vpairs(uint32_t fa, uint32_t fb, uint32_t (&out)[8]) {
   if constexpr (VB == 4) {
-    const uint32_t la = fa & 0x0F0F0F0Fu, ha = (fa >> 4) & 0x0F0F0F0Fu;
-    const uint32_t lb = fb & 0x0F0F0F0Fu, hb = (fb >> 4) & 0x0F0F0F0Fu;
+    const uint32_t la = (fa << 4) & 0xF0F0F0F0u, ha = fa & 0xF0F0F0F0u;
+    const uint32_t lb = (fb << 4) & 0xF0F0F0F0u, hb = fb & 0xF0F0F0F0u;
     const uint32_t x0 = __builtin_amdgcn_perm(lb, la, 0x05010400u);  // a0 b0 a2 b2
     const uint32_t x1 = __builtin_amdgcn_perm(lb, la, 0x07030602u);  // a4 b4 a6 b6
     const uint32_t y0 = __builtin_amdgcn_perm(hb, ha, 0x05010400u);  // a1 b1 a3 b3
     const uint32_t y1 = __builtin_amdgcn_perm(hb, ha, 0x07030602u);  // a5 b5 a7 b7
-    out[0] = magic_bytes(x0, kSel01);
-    out[1] = magic_bytes(x0, kSel23);
-    out[2] = magic_bytes(x1, kSel01);
-    out[3] = magic_bytes(x1, kSel23);
-    out[4] = magic_bytes(y0, kSel01);
-    out[5] = magic_bytes(y0, kSel23);
-    out[6] = magic_bytes(y1, kSel01);
-    out[7] = magic_bytes(y1, kSel23);
+    out[0] = kmagic(x0, kSel01);
+    out[1] = kmagic(x0, kSel23);
+    out[2] = kmagic(x1, kSel01);
+    out[3] = kmagic(x1, kSel23);
+    out[4] = kmagic(y0, kSel01);
+    out[5] = kmagic(y0, kSel23);
+    out[6] = kmagic(y1, kSel01);
+    out[7] = kmagic(y1, kSel23);
   } else if constexpr (VB == 2) {
     const uint32_t comb = (fa & 0xFFFFu) | (fb << 16);
+    // bytes: a_r, a_{4+r}, b_r, b_{4+r}, each moved to bits 4..5
+    const uint32_t m[4] = {(comb << 4) & 0x30303030u, (comb << 2) & 0x30303030u, comb & 0x30303030u,
+                           (comb >> 2) & 0x30303030u};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint32_t m = (comb >> (2 * r)) & 0x03030303u;  // a_r, a_{4+r}, b_r, b_{4+r}
-      out[2 * r] = magic_bytes(m, kSel02);
-      out[2 * r + 1] = magic_bytes(m, kSel13);
+      out[2 * r] = kmagic(m[r], kSel02);
+      out[2 * r + 1] = kmagic(m[r], kSel13);
     }
   } else {
     const uint32_t lo = (fa & 0xFFFu) | ((fb & 0xFFFu) << 16);
     const uint32_t hi = ((fa >> 12) & 0xFFFu) | (((fb >> 12) & 0xFFFu) << 16);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      out[j] = ((lo >> (3 * j)) & 0x00070007u) | 0x64006400u;
-      out[j + 4] = ((hi >> (3 * j)) & 0x00070007u) | 0x64006400u;
-    }
+    out[0] = ((lo << 4) & 0x00700070u) | 0x54005400u;
+    out[1] = ((lo << 1) & 0x00700070u) | 0x54005400u;
+    out[2] = ((lo >> 2) & 0x00700070u) | 0x54005400u;
+    out[3] = ((lo >> 5) & 0x00700070u) | 0x54005400u;
+    out[4] = ((hi << 4) & 0x00700070u) | 0x54005400u;
+    out[5] = ((hi << 1) & 0x00700070u) | 0x54005400u;
+    out[6] = ((hi >> 2) & 0x00700070u) | 0x54005400u;
+    out[7] = ((hi >> 5) & 0x00700070u) | 0x54005400u;
   }
 }
 
@@ -201,8 +213,9 @@ struct DecRing {
   static constexpr int kSlot = kOffKP + kNKG * 2 * kKPG;
   static constexpr int pieces(int bytes) { return (bytes + 1023) / 1024; }
   static constexpr int kInstr = pieces(kKC) + pieces(kVC) + pieces(2 * kVP) + kNKG * pieces(2 * kKPG);
-  // two workgroups of 4 waves per compute unit: 4 * depth * slot <= ~79 KB each
-  static constexpr int kDepthRaw = 20224 / kSlot;
+  // two workgroups of 4 waves per compute unit (80 KB of LDS each, ~2.5 KB of it
+  // outside the ring): 4 * depth * slot <= 79360
+  static constexpr int kDepthRaw = 19840 / kSlot;
   static constexpr int kDepth = kDepthRaw < 2 ? 2 : (kDepthRaw > 8 ? 8 : kDepthRaw);
   static_assert(kSlot % 16 == 0 && kVP % 16 == 0 && kKPG % 16 == 0, "16-byte pieces");
   static_assert((kDepth - 1) * kInstr <= 63, "vmcnt range");
@@ -254,6 +267,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
   static_assert(4 * Ring::kDepth * Ring::kSlot >= 5 * 1024 * sizeof(float), "tail scratch does not fit");
   float (*sh_o)[16][D] = reinterpret_cast<float (*)[16][D]>(ring);
   __shared__ float sh_m[4][16], sh_l[4][16];
+  __shared__ __attribute__((aligned(16))) uint32_t sh_kq[4][2][4][16];  // per wave: K scale / zero f16 pairs
 
   const int split = blockIdx.x, bh = blockIdx.y;
   if (split == a.splits - 1) {  // the full-precision tail rows form the last split
@@ -309,6 +323,9 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
   f4_t acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = f4_t{0.f, 0.f, 0.f, 0.f};
+  // V zero-points: sum over tokens of p * z, the same for every channel of a field's
+  // group, so one product per block; added to every channel tile at the end
+  f4_t accz = f4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
   h8_t qt[4];  // queries times the current K group's scales (the B operand of the scores)
   f4_t kbias;  // sum_c q_c z_c - 64 sum_c qt_c of the current group, per q-head column
@@ -385,43 +402,37 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
   // matrix cores (every row of its A operands is the same, so every score row of a
   // column receives its column's bias).
   auto use_kp = [&](const unsigned char* kp) {
-    const P* sp = reinterpret_cast<const P*>(kp) + 32 * kb;
-    const P* zp = sp + D;
+    // the scale and zero pairs do not depend on the q-head column: each lane converts
+    // one pair of each (step n / 4, pair n % 4 of its channel chunk) and the wave
+    // shares them through LDS; only q * s is per lane
+    {
+      const int st = n >> 2, jj = n & 3;
+      const int c0 = 32 * kb + 8 * st + korder<KB>(2 * jj), c1 = 32 * kb + 8 * st + korder<KB>(2 * jj + 1);
+      const P* sp = reinterpret_cast<const P*>(kp);
+      const P* zp = sp + D;
+      sh_kq[wave][0][kb][n] = pack_h2(param_f32<P>(sp, c0), param_f32<P>(sp, c1));
+      sh_kq[wave][1][kb][n] = pack_h2(param_f32<P>(zp, c0), param_f32<P>(zp, c1));
+    }
+    __builtin_amdgcn_wave_barrier();
     constexpr uint32_t kNeg64 = 0xD400D400u;  // (-64, -64) in f16
     const uint32_t neg64[4] = {kNeg64, kNeg64, kNeg64, kNeg64};
     kbias = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      float sv[8], zv[8];
-      if constexpr (sizeof(P) == 2) {
-        const uint4 xs = *reinterpret_cast<const uint4*>(sp + 8 * s);
-        const uint4 xz = *reinterpret_cast<const uint4*>(zp + 8 * s);
-        const uint32_t ws[4] = {xs.x, xs.y, xs.z, xs.w}, wz[4] = {xz.x, xz.y, xz.z, xz.w};
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          sv[c] = __uint_as_float((c & 1) ? (ws[c >> 1] & 0xFFFF0000u) : (ws[c >> 1] << 16));
-          zv[c] = __uint_as_float((c & 1) ? (wz[c >> 1] & 0xFFFF0000u) : (wz[c >> 1] << 16));
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          sv[c] = param_f32<P>(sp, 8 * s + c);
-          zv[c] = param_f32<P>(zp, 8 * s + c);
-        }
-      }
-      uint32_t s2[4], z2[4], q2[4];
+      const uint4 sw = *reinterpret_cast<const uint4*>(&sh_kq[wave][0][kb][4 * s]);
+      const uint4 zw = *reinterpret_cast<const uint4*>(&sh_kq[wave][1][kb][4 * s]);
+      const uint32_t s2[4] = {sw.x, sw.y, sw.z, sw.w};
+      const uint32_t z2[4] = {zw.x, zw.y, zw.z, zw.w};
       const h8_t qs = bq[s];
       const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qs);
+      uint32_t q2[4];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        s2[jj] = pack_h2(sv[korder<KB>(2 * jj)], sv[korder<KB>(2 * jj + 1)]);
-        z2[jj] = pack_h2(zv[korder<KB>(2 * jj)], zv[korder<KB>(2 * jj + 1)]);
-        q2[jj] = as_u32(as_h2(qw[jj]) * as_h2(s2[jj]));
-      }
+      for (int jj = 0; jj < 4; ++jj) q2[jj] = as_u32(as_h2(qw[jj]) * as_h2(s2[jj]));
       qt[s] = __builtin_bit_cast(h8_t, q2);
       kbias = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, z2), bq[s], kbias, 0, 0, 0);
       kbias = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, neg64), qt[s], kbias, 0, 0, 0);
     }
+    __builtin_amdgcn_wave_barrier();
   };
   // V parameter (as float) of a slot token from its raw word
   // (with one group per token the element parity is the slot's parity; otherwise the
@@ -474,6 +485,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
       const float al = __builtin_amdgcn_exp2f(m - mn);  // m = -inf on the first block: 0
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] *= al;
+      accz *= al;
       l *= al;
       m = mn;
     }
@@ -489,7 +501,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
     const h8_t bp = __builtin_bit_cast(h8_t, pw);
 
     // ---- O^T[8 (4 kb' + i) + vorder(t)][n] += V_hat^T P^T over the block's 32 tokens
-    uint32_t sv2[4], zv2[4], vp[4][8];
+    uint32_t sv2[4], nsv2[4], zv2[4], vp[4][8];
 #pragma unroll
     for (int q2 = 0; q2 < 4; ++q2) {
       const uint32_t ta = t0 + slot_token(kb, 2 * q2), tb = t0 + slot_token(kb, 2 * q2 + 1);
@@ -514,12 +526,14 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
         fb = cur.vw[2 * q2 + 1][0];
       }
       vpairs<VB>(fa, fb, vp[q2]);
+      nsv2[q2] = as_u32(as_h2(sv2[q2]) * as_h2(0xD400D400u));  // -64 s, exact
     }
+    accz = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, zv2), bp, accz, 0, 0, 0);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       uint32_t av[4];
 #pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) av[q2] = dequant_pair(vp[q2][t], sv2[q2], zv2[q2]);
+      for (int q2 = 0; q2 < 4; ++q2) av[q2] = scale_pair(vp[q2][t], sv2[q2], nsv2[q2]);
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, av), bp, acc[t], 0, 0, 0);
     }
   };
@@ -567,7 +581,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sh_o[wave][n][8 * (4 * kb + i) + vorder<VB>(t)] = acc[t][i];
+    for (int i = 0; i < 4; ++i) sh_o[wave][n][8 * (4 * kb + i) + vorder<VB>(t)] = acc[t][i] + accz[i];
   __syncthreads();
   const int64_t pbase = static_cast<int64_t>(bh) * a.splits + split;
   for (int idx = tid; idx < H * D; idx += kDecThreads) {
