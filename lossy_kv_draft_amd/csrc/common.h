@@ -91,6 +91,23 @@ __device__ __forceinline__ float warp_sum(float v) {
   return v;
 }
 
+// Global -> LDS copy of 16 bytes per active lane, written at (lds + 16 * lane).  It
+// is issued from inline assembly so that the compiler does not treat every later
+// LDS read as depending on every copy in flight (it would wait for all of them
+// before each read); kernels that use it place the vmcnt waits themselves.  Loads
+// the compiler issues are still waited for correctly: copies it does not know of
+// can only make its own waits stricter.
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -186,15 +186,8 @@ __device__ __forceinline__ int slot_token(int kb, int j) { return j < 4 ? 4 * kb
 template <typename P>
 __device__ __forceinline__ float param_f32(const P* p, int i) { return Elem<P>::load(p, i); }
 
-// Global -> LDS copies for the decode ring.  The copy instruction writes 16 bytes
-// per active lane at (M0 + 16 * lane); it is issued from inline assembly so that the
-// compiler does not treat every later LDS read as depending on every copy in flight
-// (which would drain the ring at each block): the kernel places the vmcnt waits
-// itself.  Loads the compiler issues are still waited for correctly, since copies
-// it does not know of can only make its own waits stricter.
-__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
-}
+// The ring is filled with lds_copy16 (common.h): 16 bytes per lane, global -> LDS,
+// with the vmcnt waits placed by the kernel itself.
 
 // Slot layout of one 32-token block and the ring depth for one kernel instance.
 template <int KB, int VB, int NGV, typename P>

@@ -253,6 +253,216 @@ __global__ void __launch_bounds__(kVerThreads) verify_mfma_kernel(VerifyArgs a) 
   }
 }
 
+// ---------------------------------------------------------------- bf16, d = 128
+// Tiles of 64 positions of K and V (32 KB) are copied global -> LDS by all four waves
+// (16 bytes per lane per instruction, 8 instructions per wave per tile) into a
+// two-stage ring, one tile ahead of the one being computed; 16-byte chunks of a row
+// are XOR-swizzled by the row so that the matrix-core operand reads spread over the
+// banks.  K feeds S^T = K Q^T as the A operand (16-byte reads).  V stays position-
+// major: the A operand of O^T += V^T P^T (channels x positions) is read with the
+// transposing LDS load ds_read_b64_tr_b16, which within each 16-lane group returns
+// to lane j the element j & 3 of the four values addressed by lane 4e + (j >> 2) as
+// element e; so lane (4e + i) addresses position e and channels 4i .. 4i + 3.
+// Softmax per row: masking only on tiles that reach past a row's limit; the running
+// maximum and the rescale of the row's accumulators only when a tile raises it (a
+// decision of the row alone, so batch invariance holds; the row's largest
+// probability is exactly 1); exp2 of an fma; bf16 P; the row sums come from one more
+// product with an all-ones A operand.
+constexpr int kVtTile = 64;
+constexpr int kVtRow = 256;                       // bytes per position row
+constexpr int kVtTileBytes = kVtTile * kVtRow;    // one K or V tile
+typedef short s4_t __attribute__((ext_vector_type(4)));
+typedef float f2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int vt_chunk(int r, int c) { return c ^ (r & 15); }
+
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
+  typedef __attribute__((address_space(3))) s4_t lds_s4;
+  const s4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s4*)(__attribute__((address_space(3))) unsigned char*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+template <int RT>
+__global__ void __launch_bounds__(kVerThreads) verify_tile_kernel(VerifyArgs a) {
+  constexpr int D = 128, KS = D / 32, DT = D / 16;
+  __shared__ __attribute__((aligned(16))) unsigned char ring[2][2 * kVtTileBytes];
+  const int split = blockIdx.x, rblk = blockIdx.y, bh = blockIdx.z;
+  const int b = bh / a.Hkv, hk = bh % a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, kb = lane >> 4;
+  const int M = a.H * a.k;
+  const int row0 = rblk * a.rows_per_block + wave * 16 * RT;
+  const int64_t L = a.ctx_lens ? a.ctx_lens[b] : a.ctx_len;
+  const int64_t limit = L + a.k;  // readable positions [0, limit)
+  const int64_t s_begin = static_cast<int64_t>(split) * a.C;
+  const int64_t s_end = min(s_begin + a.C, limit);
+  const int ntile = s_end > s_begin ? static_cast<int>((s_end - s_begin + kVtTile - 1) / kVtTile) : 0;
+
+  const bf16_t* q = static_cast<const bf16_t*>(a.q) + (static_cast<int64_t>(b) * a.Hq + hk * a.H) * a.k * D;
+  bf16x8_t qf[RT][KS];
+  int64_t rlim[RT];  // last position the row may see (inclusive); -1 for padding rows
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = row0 + rt * 16 + l16;
+    rlim[rt] = row < M ? L + (row % a.k) : -1;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      Pack16 p;
+      p.u = make_uint4(0, 0, 0, 0);
+      if (row < M) p.u = *reinterpret_cast<const uint4*>(q + static_cast<int64_t>(row) * D + 32 * ks + 8 * kb);
+      qf[rt][ks] = p.v;
+    }
+  }
+  f32x4_t o[DT][RT], lacc[RT];
+  float m[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m[rt] = -INFINITY;
+    lacc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  Pack16 ones;
+  ones.u = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);  // bf16 1.0
+
+  // copies: wave w moves rows 16 w .. 16 w + 15 of the K and V tiles, 4 rows per
+  // instruction (lane l: row 16 w + 4 i + l / 16, LDS chunk l % 16)
+  const unsigned char* kbase = static_cast<const unsigned char*>(a.kc) + static_cast<size_t>(bh) * a.cache_rows * kVtRow;
+  const unsigned char* vbase = static_cast<const unsigned char*>(a.vc) + static_cast<size_t>(bh) * a.cache_rows * kVtRow;
+  auto issue = [&](int j) {
+    const int64_t t0 = s_begin + static_cast<int64_t>(j) * kVtTile;
+    unsigned char* st = ring[j & 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * wave + 4 * i + (lane >> 4);
+      const int c = vt_chunk(r, lane & 15);          // the global chunk that lives at LDS chunk lane % 16
+      const int64_t pos = min(t0 + r, limit - 1);   // rows past the end repeat the last readable row
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(st + (16 * wave + 4 * i) * kVtRow));
+      lds_copy16(kbase + pos * kVtRow + c * 16, dst);
+      lds_copy16(vbase + pos * kVtRow + c * 16, dst + kVtTileBytes);
+    }
+  };
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the query loads complete before the copies start
+  if (ntile > 0) issue(0);
+  if (ntile > 1) issue(1);
+  for (int j = 0; j < ntile; ++j) {
+    if (j + 1 < ntile) wait_vmcnt<8>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // every wave's copies of tile j have landed
+    const unsigned char* kt = ring[j & 1];
+    const unsigned char* vt = kt + kVtTileBytes;
+    const int64_t t0 = s_begin + static_cast<int64_t>(j) * kVtTile;
+    if (row0 < M) {  // wave-uniform; padding waves only copy
+      // ---- S^T = K Q^T: s[tt][rt][r] = score(position t0 + 16 tt + 4 kb + r, row row0 + 16 rt + l16)
+      f32x4_t s[4][RT];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) s[tt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          Pack16 ka;
+          ka.u = *reinterpret_cast<const uint4*>(kt + (16 * tt + l16) * kVtRow + ((4 * ks + kb) ^ l16) * 16);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            s[tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.v, qf[rt][ks], s[tt][rt], 0, 0, 0);
+        }
+      }
+      // ---- softmax per row
+      const bool full = t0 + kVtTile - 1 <= L;  // every row sees every position of the tile
+      bf16x8_t pb[RT][2];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        float mt = -INFINITY;
+        if (full) {
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[tt][rt][r]);
+        } else {
+          const int lr = static_cast<int>(max(min(rlim[rt] - t0, static_cast<int64_t>(kVtTile)), static_cast<int64_t>(-1)));
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float v = 16 * tt + 4 * kb + r <= lr ? s[tt][rt][r] : -INFINITY;
+              s[tt][rt][r] = v;
+              mt = fmaxf(mt, v);
+            }
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mts = mt * a.qscale;
+        if (mts > m[rt]) {  // the row's own decision (all lanes of a row agree)
+          const float al = __builtin_amdgcn_exp2f(m[rt] - mts);  // 0 on the row's first scores
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= al;
+          lacc[rt] *= al;
+          m[rt] = mts;
+        }
+        const float nm = m[rt] == -INFINITY ? 0.f : -m[rt];
+        Pack16 p0, p1;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int r = 0; r < 4; r += 2) {
+            const f2_t e = {__builtin_amdgcn_exp2f(fmaf(s[tt][rt][r], a.qscale, nm)),
+                            __builtin_amdgcn_exp2f(fmaf(s[tt][rt][r + 1], a.qscale, nm))};
+            const bf16x2_t h = __builtin_convertvector(e, bf16x2_t);
+            Pack16& dst = tt < 2 ? p0 : p1;
+            dst.v[(tt & 1) * 4 + r] = h[0];
+            dst.v[(tt & 1) * 4 + r + 1] = h[1];
+          }
+        pb[rt][0] = p0.v;
+        pb[rt][1] = p1.v;
+        lacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones.v, pb[rt][0], lacc[rt], 0, 0, 0);
+        lacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones.v, pb[rt][1], lacc[rt], 0, 0, 0);
+      }
+      // ---- O^T += V^T P^T; k-slot j of lane group kb is position 32 ks2 + 4 kb + j (j < 4),
+      //      32 ks2 + 16 + 4 kb + (j - 4) otherwise, as in P^T
+      const int e = l16 >> 2, qd = l16 & 3;
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        const int ra = 32 * ks2 + 4 * kb + e, rb = ra + 16;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int ch = 2 * dt + (qd >> 1), half = 8 * (qd & 1);
+          const uint2 lo = lds_read_tr16(vt + ra * kVtRow + vt_chunk(ra, ch) * 16 + half);
+          const uint2 hi = lds_read_tr16(vt + rb * kVtRow + vt_chunk(rb, ch) * 16 + half);
+          Pack16 va;
+          va.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pb[rt][ks2], o[dt][rt], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();  // every wave is done with stage j & 1
+    if (j + 2 < ntile) issue(j + 2);
+  }
+
+  if (row0 >= M) return;
+  // ---- partials: o[dt][rt][r] = O^T[d = 16 dt + 4 kb + r][row = row0 + 16 rt + l16]
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = row0 + rt * 16 + l16;
+    if (row >= M) continue;
+    const int64_t pr = (static_cast<int64_t>(bh) * a.splits + split) * M + row;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<f32x4_t*>(a.part_o + pr * D + dt * 16 + 4 * kb) = o[dt][rt];
+    if (kb == 0) {
+      a.part_ml[pr * 2] = m[rt];
+      a.part_ml[pr * 2 + 1] = lacc[rt][0];
+    }
+  }
+}
+
 // float32 path: one 64-lane wave per (row, split); lanes cover d (d <= 256).
 template <typename T>
 __global__ void __launch_bounds__(256) verify_f32_kernel(VerifyArgs a) {
@@ -425,7 +635,20 @@ extern "C" vc_status vc_verify_attn_full(const void* q, const void* k_cache, con
   a.part_o = static_cast<float*>(ws);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(bh * a.splits * M * d * sizeof(float), 256));
   hipStream_t s = as_stream(stream);
-  if (kv_dtype == VC_BF16) {
+  if (kv_dtype == VC_BF16 && d == 128) {
+    // at most 128 rows per workgroup: RT (1 or 2) 16-row tiles per wave
+    const int nblk = static_cast<int>(cdiv(M, 128));
+    const int RT = cdiv(cdiv(M, nblk), 64) > 1 ? 2 : 1;
+    a.rows_per_block = 64 * RT;
+    dim3 grid(a.splits, static_cast<unsigned>(cdiv(M, 64 * RT)), static_cast<unsigned>(bh));
+    if (RT == 1)
+      hipLaunchKernelGGL((verify_tile_kernel<1>), grid, dim3(kVerThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((verify_tile_kernel<2>), grid, dim3(kVerThreads), 0, s, a);
+    VC_LAUNCHED("verify_tile_kernel");
+    dim3 mgrid(static_cast<unsigned>(cdiv(static_cast<int64_t>(M) * d, 256)), static_cast<unsigned>(bh));
+    hipLaunchKernelGGL(verify_merge_kernel<bf16_t>, mgrid, dim3(256), 0, s, a, out, lse);
+  } else if (kv_dtype == VC_BF16) {
     int RT, nblk;
     verify_tiling(M, RT, nblk);
     a.rows_per_block = 64 * RT;

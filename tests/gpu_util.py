@@ -9,7 +9,10 @@ from oracle import quant as OQ
 
 DEV = "cuda"
 TOL = {"f32": 1e-4, "bf16": 2e-2}      # max-abs on attention outputs
-LSE_TOL = {"f32": 1e-4, "bf16": 2e-3}  # log-sum-exp is float32 on both storage types
+# log-sum-exp: float32 on both storage types; with bf16 KV the probabilities enter the
+# products (and their sum) rounded to bf16, 8 significant bits: the sum's relative
+# error is at most 2^-8, so ln of it is off by at most ln(1 + 2^-8) < 3.9e-3
+LSE_TOL = {"f32": 1e-4, "bf16": 4e-3}
 
 
 def storage_half_ulp(ref, dtype):
