@@ -442,7 +442,7 @@ def main():
         "wall_ms_per_step": round(wall / a.steps * 1e3, 4),
         "compress_ms": round(st["comp_ms"], 4),
         "roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel + decode_merge_kernel (quant)" if w.method == "quant"
-                     else "decode_generic_kernel + decode_merge_kernel (kept rows)",
+                     else "decode_dense_kernel + decode_merge_kernel (kept rows)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
                      "bytes_per_launch": int(per_launch), "avg_launch_us": round(dec_avg_ms * 1e3, 3)},

@@ -28,6 +28,7 @@ constexpr int kDecTargetBlocks = 2048;
 bool decode_mfma_supported(const vc_ckv* c, int H);
 int decode_mfma_splits(const vc_ckv* c);
 void launch_decode_mfma(const vc_ckv* c, const DecodeArgs& a, dim3 grid, hipStream_t s);
+vc_status launch_decode_dense(const vc_ckv* c, const DecodeArgs& a, hipStream_t s);
 
 
 
@@ -258,10 +259,20 @@ extern "C" vc_status vc_decode_attn_compressed(const vc_ckv* c, const void* q, i
   a.d = c->d;
   a.qscale = sm_scale * kLog2e;
   const bool mfma = decode_mfma_supported(c, H);
+  // kept bf16 rows, d = 128: the verification tile loop with one query row per head
+  const bool dense = !mfma && c->method == VC_DROP_TOPK && c->kv_dtype == VC_BF16 && c->d == 128 && H <= 16;
   int S;
   if (mfma) {
     S = decode_mfma_splits(c);  // compressed-row splits + one tail split
     a.chunk = cdiv(cdiv(c->n_main > 0 ? c->n_main : 1, S - 1), 128) * 128;
+  } else if (dense) {
+    // two 4-wave workgroups per compute unit (64 KB of LDS each): row splits and the
+    // tail split together fill the device once
+    const int bh = c->B * c->Hkv;
+    S = 512 / bh;
+    if (S < 2) S = 2;
+    if (S > kDecMaxSplits) S = kDecMaxSplits;
+    a.chunk = cdiv(cdiv(c->n_main > 0 ? c->n_main : 1, S - 1), 64) * 64;
   } else {
     S = decode_splits(c);
     int64_t total = c->n_main + c->tail_len;
@@ -288,6 +299,11 @@ extern "C" vc_status vc_decode_attn_compressed(const vc_ckv* c, const void* q, i
   if (mfma) {
     launch_decode_mfma(c, a, grid, s);
     VC_LAUNCHED("decode_mfma_kernel");
+    return merge();
+  }
+  if (dense) {
+    const vc_status st = launch_decode_dense(c, a, s);
+    if (st != VC_OK) return st;
     return merge();
   }
   size_t lds = (static_cast<size_t>(H) * c->d + kDecTile * (c->d + 1) + kDecTile * c->d + H * kDecTile + 3 * H) *

@@ -31,6 +31,7 @@
 // instantiation performs the same roundings.
 
 #include "common.h"
+#include "decode_common.h"
 
 namespace vc {
 
@@ -47,6 +48,7 @@ struct VerifyArgs {
   int Hq, Hkv, H, d, k;
   int64_t cache_rows, ctx_len;
   const int32_t* ctx_lens;
+  int ctx_off;    // added to ctx_lens[b] (decode over kept rows: lengths minus one)
   int64_t C;      // split size in positions
   int splits;
   int rows_per_block;
@@ -78,7 +80,7 @@ __global__ void __launch_bounds__(kVerThreads) verify_mfma_kernel(VerifyArgs a) 
   const int l16 = lane & 15, kb = lane >> 4;
   const int M = a.H * a.k;
   const int row0 = rblk * a.rows_per_block + wave * 16 * RT;
-  const int64_t L = a.ctx_lens ? a.ctx_lens[b] : a.ctx_len;
+  const int64_t L = a.ctx_lens ? a.ctx_lens[b] + a.ctx_off : a.ctx_len;
   const int64_t limit = L + a.k;  // readable positions [0, limit)
   const int64_t s_begin = static_cast<int64_t>(split) * a.C;
   const int64_t s_end = min(s_begin + a.C, limit);
@@ -285,17 +287,16 @@ __device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
 }
 
 template <int RT>
-__global__ void __launch_bounds__(kVerThreads) verify_tile_kernel(VerifyArgs a) {
+__device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int rblk, int bh,
+                                             unsigned char (*ring)[2 * kVtTileBytes]) {
   constexpr int D = 128, KS = D / 32, DT = D / 16;
-  __shared__ __attribute__((aligned(16))) unsigned char ring[2][2 * kVtTileBytes];
-  const int split = blockIdx.x, rblk = blockIdx.y, bh = blockIdx.z;
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, kb = lane >> 4;
   const int M = a.H * a.k;
   const int row0 = rblk * a.rows_per_block + wave * 16 * RT;
-  const int64_t L = a.ctx_lens ? a.ctx_lens[b] : a.ctx_len;
+  const int64_t L = a.ctx_lens ? a.ctx_lens[b] + a.ctx_off : a.ctx_len;
   const int64_t limit = L + a.k;  // readable positions [0, limit)
   const int64_t s_begin = static_cast<int64_t>(split) * a.C;
   const int64_t s_end = min(s_begin + a.C, limit);
@@ -463,6 +464,26 @@ __global__ void __launch_bounds__(kVerThreads) verify_tile_kernel(VerifyArgs a) 
   }
 }
 
+template <int RT>
+__global__ void __launch_bounds__(kVerThreads) verify_tile_kernel(VerifyArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char ring[2][2 * kVtTileBytes];
+  verify_tiles<RT>(a, blockIdx.x, blockIdx.y, blockIdx.z, ring);
+}
+
+// Draft-side decode over kept (token-dropped) bf16 rows, d = 128, at most 16 q-heads
+// per kv-head: the same tile loop with one query row per q-head, a window of one and
+// the context length set to the kept rows minus one, so that row 0 attends to every
+// kept row; splits 0 .. S-2 cover the kept rows and write the decode partials, split
+// S-1 covers the full-precision tail rows; decode_merge_kernel combines them.
+__global__ void __launch_bounds__(kVerThreads) decode_dense_kernel(VerifyArgs a, DecodeArgs d) {
+  __shared__ __attribute__((aligned(16))) unsigned char ring[2][2 * kVtTileBytes];
+  if (static_cast<int>(blockIdx.x) == d.splits - 1) {
+    decode_tail_partial_d128(d, blockIdx.z, d.splits - 1, reinterpret_cast<float*>(&ring[0][0]));
+    return;
+  }
+  verify_tiles<1>(a, blockIdx.x, 0, blockIdx.z, ring);
+}
+
 // float32 path: one 64-lane wave per (row, split); lanes cover d (d <= 256).
 template <typename T>
 __global__ void __launch_bounds__(256) verify_f32_kernel(VerifyArgs a) {
@@ -472,7 +493,7 @@ __global__ void __launch_bounds__(256) verify_f32_kernel(VerifyArgs a) {
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int M = a.H * a.k, d = a.d;
   if (row >= M) return;
-  const int64_t L = a.ctx_lens ? a.ctx_lens[b] : a.ctx_len;
+  const int64_t L = a.ctx_lens ? a.ctx_lens[b] + a.ctx_off : a.ctx_len;
   const int64_t last = L + (row % a.k);
   const int64_t s_begin = static_cast<int64_t>(split) * a.C;
   const int64_t s_end = min(s_begin + a.C, last + 1);
@@ -568,6 +589,34 @@ static void verify_tiling(int M, int& RT, int& nblk) {
   nblk = static_cast<int>(cdiv(M, 64 * RT));
 }
 
+// Dense decode over kept rows (see decode_dense_kernel): S - 1 row splits of `chunk`
+// positions (a multiple of the 64-position tile) plus the tail split.
+vc_status launch_decode_dense(const vc_ckv* c, const DecodeArgs& d, hipStream_t s) {
+  VerifyArgs a{};
+  a.q = d.q;
+  a.kc = c->k_kept;
+  a.vc = c->v_kept;
+  a.Hq = c->Hkv * d.H;
+  a.Hkv = c->Hkv;
+  a.H = d.H;
+  a.d = 128;
+  a.k = 1;
+  a.cache_rows = c->capacity;
+  a.ctx_len = c->n_main - 1;
+  a.ctx_lens = d.main_lens;
+  a.ctx_off = -1;
+  a.C = d.chunk;
+  a.splits = d.splits;
+  a.rows_per_block = 64;
+  a.qscale = d.qscale;
+  a.part_o = d.part_o;
+  a.part_ml = d.part_ml;
+  const dim3 grid(static_cast<unsigned>(d.splits), 1, static_cast<unsigned>(c->B * c->Hkv));
+  hipLaunchKernelGGL(decode_dense_kernel, grid, dim3(kVerThreads), 0, s, a, d);
+  VC_LAUNCHED("decode_dense_kernel");
+  return VC_OK;
+}
+
 }  // namespace vc
 
 using namespace vc;
@@ -627,6 +676,7 @@ extern "C" vc_status vc_verify_attn_full(const void* q, const void* k_cache, con
   a.cache_rows = cache_rows;
   a.ctx_len = ctx_len;
   a.ctx_lens = ctx_lens;
+  a.ctx_off = 0;
   a.C = C;
   a.splits = static_cast<int>(cdiv(ctx_len + k, C));
   a.qscale = sm_scale * kLog2e;
