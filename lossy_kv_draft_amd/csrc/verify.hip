@@ -6,19 +6,22 @@
 // Row i of a sequence with context length L attends to cache rows [0, L + i] (the
 // window's own keys/values are already written at rows [L, L + k)).
 //
-// bf16 path (matrix cores, v_mfma_f32_16x16x32_bf16, float32 accumulation):
-//   grid = (splits, row blocks, B*Hkv).  The rows of all Hq/Hkv q-heads that read
-//   one kv-head are stacked (M = (Hq/Hkv) * k rows) so every K/V tile is read from
-//   HBM once per row block.  Each of the 4 waves owns 16*RT rows.  Per 64-token
-//   tile: K is staged in LDS as [token][d] and V transposed as [d][token]; the
-//   wave computes S^T = K Q^T (tokens x rows), masks positions beyond each row's
-//   limit, runs an online softmax per row (base 2), rounds P to bf16 and
-//   accumulates O^T += V^T P^T.  The probabilities stay in the lanes that produced
-//   them: the S^T output layout of a pair of 16-token tiles is exactly the
-//   B-operand layout of the P.V product once the 32 token indices of that product
-//   are enumerated in the same (permuted) order on both operands.
-//   The global loads of the next tile are issued before the current tile is
-//   computed (register prefetch).
+// bf16 paths (matrix cores, v_mfma_f32_16x16x32_bf16, float32 accumulation).  The
+// rows of all Hq/Hkv q-heads that read one kv-head are stacked (M = (Hq/Hkv) * k
+// rows) so every K/V tile is read from HBM once per row block; each of the 4 waves
+// of a workgroup owns 16*RT rows.  Per tile the wave computes S^T = K Q^T (tokens x
+// rows), masks positions beyond each row's limit, runs an online softmax per row
+// (base 2), rounds P to bf16 and accumulates O^T += V^T P^T.  The probabilities stay
+// in the lanes that produced them: the S^T output layout of a pair of 16-token tiles
+// is exactly the B-operand layout of the P.V product once the 32 token indices of
+// that product are enumerated in the same (permuted) order on both operands.
+//   d = 128 (verify_tile_kernel): K and V tiles go global -> LDS through the direct
+//   LDS load, V is read transposed by the LDS transpose load; see the notes above
+//   verify_tiles.
+//   d = 64 (verify_mfma_kernel): grid = (splits, row blocks, B*Hkv); K staged in LDS
+//   as [token][d] and V transposed as [d][token] by the waves themselves, the global
+//   loads of the next tile issued before the current tile is computed (register
+//   prefetch).
 //
 // float32 path: one wave per (row, split), lanes over d, float32 throughout.
 //
@@ -256,9 +259,12 @@ __global__ void __launch_bounds__(kVerThreads) verify_mfma_kernel(VerifyArgs a) 
 }
 
 // ---------------------------------------------------------------- bf16, d = 128
-// Tiles of 64 positions of K and V (32 KB) are copied global -> LDS by all four waves
-// (16 bytes per lane per instruction, 8 instructions per wave per tile) into a
-// two-stage ring, one tile ahead of the one being computed; 16-byte chunks of a row
+// Tiles of kVtTile positions of K and V are copied global -> LDS by all waves of the
+// workgroup (16 bytes per lane per instruction) into a ring of kVtStages tiles: while
+// tile j is
+// computed, the copies of the next kVtStages - 1 tiles are in flight.  One barrier per
+// tile: after it, tile j has landed for every wave and every wave is done with tile
+// j - 1, whose stage then receives tile j + kVtStages - 1.  16-byte chunks of a row
 // are XOR-swizzled by the row so that the matrix-core operand reads spread over the
 // banks.  K feeds S^T = K Q^T as the A operand (16-byte reads).  V stays position-
 // major: the A operand of O^T += V^T P^T (channels x positions) is read with the
@@ -270,9 +276,13 @@ __global__ void __launch_bounds__(kVerThreads) verify_mfma_kernel(VerifyArgs a) 
 // decision of the row alone, so batch invariance holds; the row's largest
 // probability is exactly 1); exp2 of an fma; bf16 P; the row sums come from one more
 // product with an all-ones A operand.
-constexpr int kVtTile = 64;
+constexpr int kVtTile = 64;                       // positions per tile
+constexpr int kVtStages = 2;                      // tiles held in the LDS ring
 constexpr int kVtRow = 256;                       // bytes per position row
+constexpr int kVtPrefetch = 4;                    // K or V fragments read ahead of their product
 constexpr int kVtTileBytes = kVtTile * kVtRow;    // one K or V tile
+static_assert(kVtTile % 32 == 0 && kVtStages >= 2, "tile shape");
+typedef unsigned char VtStage[2 * kVtTileBytes];  // K tile, then V tile
 typedef short s4_t __attribute__((ext_vector_type(4)));
 typedef float f2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -286,10 +296,40 @@ __device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// Maximum over the four 16-lane groups of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48)
+// with the lane-swap instructions: given the same register twice, the 16-lane swap
+// returns the pair {x[l], x[l ^ 16]} and the 32-lane swap {x[l], x[l ^ 32]} (one in
+// each result, in an order that does not matter for the maximum).
+__device__ __forceinline__ float group4_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const unsigned w = __float_as_uint(x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
+// Wait until at most `ahead` tiles of this wave's copies (I instructions per tile)
+// are still in flight.
+template <int I, int A>
+__device__ __forceinline__ void vt_wait(int ahead) {
+  if constexpr (A == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= A) wait_vmcnt<I * A>();
+    else vt_wait<I, A - 1>(ahead);
+  }
+}
+
+// RT 16-row tiles per wave, 4 waves per workgroup (64 RT rows per workgroup).
 template <int RT>
-__device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int rblk, int bh,
-                                             unsigned char (*ring)[2 * kVtTileBytes]) {
+__device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int rblk, int bh, VtStage* ring) {
   constexpr int D = 128, KS = D / 32, DT = D / 16;
+  constexpr int kWaveRows = kVtTile / 4;   // rows each wave copies per tile
+  constexpr int kCopies = kWaveRows / 4;   // instructions per wave per tile, K and V each
+  static_assert(kWaveRows % 4 == 0, "copy shape");
+  constexpr int NT = kVtTile / 16;  // 16-position score tiles per tile
+  constexpr int KP = kVtTile / 32;  // 32-position k-steps of the P V product per tile
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -329,66 +369,88 @@ __device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int
   Pack16 ones;
   ones.u = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);  // bf16 1.0
 
-  // copies: wave w moves rows 16 w .. 16 w + 15 of the K and V tiles, 4 rows per
-  // instruction (lane l: row 16 w + 4 i + l / 16, LDS chunk l % 16)
+  // copies: wave w moves rows kWaveRows w .. kWaveRows (w + 1) - 1 of the K and V
+  // tiles, 4 rows per instruction (lane l: row base + l / 16, LDS chunk l % 16)
   const unsigned char* kbase = static_cast<const unsigned char*>(a.kc) + static_cast<size_t>(bh) * a.cache_rows * kVtRow;
   const unsigned char* vbase = static_cast<const unsigned char*>(a.vc) + static_cast<size_t>(bh) * a.cache_rows * kVtRow;
   auto issue = [&](int j) {
     const int64_t t0 = s_begin + static_cast<int64_t>(j) * kVtTile;
-    unsigned char* st = ring[j & 1];
+    unsigned char* st = ring[j % kVtStages];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * wave + 4 * i + (lane >> 4);
+    for (int i = 0; i < kCopies; ++i) {
+      const int rw = kWaveRows * wave + 4 * i;
+      const int r = rw + (lane >> 4);
       const int c = vt_chunk(r, lane & 15);          // the global chunk that lives at LDS chunk lane % 16
       const int64_t pos = min(t0 + r, limit - 1);   // rows past the end repeat the last readable row
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(st + (16 * wave + 4 * i) * kVtRow));
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(st + rw * kVtRow));
       lds_copy16(kbase + pos * kVtRow + c * 16, dst);
       lds_copy16(vbase + pos * kVtRow + c * 16, dst + kVtTileBytes);
     }
   };
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the query loads complete before the copies start
-  if (ntile > 0) issue(0);
-  if (ntile > 1) issue(1);
+  for (int t = 0; t < kVtStages - 1 && t < ntile; ++t) issue(t);
   for (int j = 0; j < ntile; ++j) {
-    if (j + 1 < ntile) wait_vmcnt<8>();
-    else wait_vmcnt<0>();
-    __syncthreads();  // every wave's copies of tile j have landed
-    const unsigned char* kt = ring[j & 1];
+    vt_wait<2 * kCopies, kVtStages - 2>(ntile - 1 - j);  // this wave's copies of tile j have landed
+    __syncthreads();  // ... and every wave's; every wave is done with tile j - 1
+    if (j + kVtStages - 1 < ntile) issue(j + kVtStages - 1);  // into the stage of tile j - 1
+    const unsigned char* kt = ring[j % kVtStages];
     const unsigned char* vt = kt + kVtTileBytes;
     const int64_t t0 = s_begin + static_cast<int64_t>(j) * kVtTile;
     if (row0 < M) {  // wave-uniform; padding waves only copy
-      // ---- S^T = K Q^T: s[tt][rt][r] = score(position t0 + 16 tt + 4 kb + r, row row0 + 16 rt + l16)
-      f32x4_t s[4][RT];
+      // ---- S^T = K Q^T: s[tt][rt][r] = score(position t0 + 16 tt + 4 kb + r, row row0 + 16 rt + l16);
+      //      K fragments are read ahead of the products that take them
+      f32x4_t s[NT][RT];
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+      for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) s[tt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // fragment i = (step i / NT, position tile i % NT); kVtPrefetch of them in flight
+      auto kload = [&](Pack16& dst, int i) {
+        const int ks = i / NT, tt = i % NT;
+        dst.u = *reinterpret_cast<const uint4*>(kt + (16 * tt + l16) * kVtRow + ((4 * ks + kb) ^ l16) * 16);
+      };
+      Pack16 kf[kVtPrefetch];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int i = 0; i < kVtPrefetch; ++i) kload(kf[i], i);
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          Pack16 ka;
-          ka.u = *reinterpret_cast<const uint4*>(kt + (16 * tt + l16) * kVtRow + ((4 * ks + kb) ^ l16) * 16);
+      for (int i = 0; i < KS * NT; ++i) {
+        const Pack16 ka = kf[i % kVtPrefetch];
+        if (i + kVtPrefetch < KS * NT) kload(kf[i % kVtPrefetch], i + kVtPrefetch);
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
-            s[tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.v, qf[rt][ks], s[tt][rt], 0, 0, 0);
-        }
+        for (int rt = 0; rt < RT; ++rt)
+          s[i % NT][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.v, qf[rt][i / NT], s[i % NT][rt], 0, 0, 0);
       }
+      // ---- V^T fragments (A operand of the P V product), kVtPrefetch of them in flight:
+      //      fragment i = (k-step i / DT, channel tile i % DT); k-slot j of lane group kb is
+      //      position 32 ks2 + 4 kb + j (j < 4), 32 ks2 + 16 + 4 kb + (j - 4) otherwise, as in P^T
+      constexpr int NV = KP * DT;
+      const int e = l16 >> 2, qd = l16 & 3;
+      auto vload = [&](Pack16& dst, int i) {
+        const int ks2 = i / DT, dt = i % DT;
+        const int ra = 32 * ks2 + 4 * kb + e, rb = ra + 16;
+        const int ch = 2 * dt + (qd >> 1), half = 8 * (qd & 1);
+        const uint2 lo = lds_read_tr16(vt + ra * kVtRow + vt_chunk(ra, ch) * 16 + half);
+        const uint2 hi = lds_read_tr16(vt + rb * kVtRow + vt_chunk(rb, ch) * 16 + half);
+        dst.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      };
+      Pack16 vf[kVtPrefetch];
+#pragma unroll
+      for (int i = 0; i < kVtPrefetch; ++i) vload(vf[i], i);  // in flight during the softmax
       // ---- softmax per row
       const bool full = t0 + kVtTile - 1 <= L;  // every row sees every position of the tile
-      bf16x8_t pb[RT][2];
+      bf16x8_t pb[RT][KP];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         float mt = -INFINITY;
         if (full) {
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt)
+          for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[tt][rt][r]);
         } else {
           const int lr = static_cast<int>(max(min(rlim[rt] - t0, static_cast<int64_t>(kVtTile)), static_cast<int64_t>(-1)));
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt)
+          for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float v = 16 * tt + 4 * kb + r <= lr ? s[tt][rt][r] : -INFINITY;
@@ -396,9 +458,7 @@ __device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int
               mt = fmaxf(mt, v);
             }
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float mts = mt * a.qscale;
+        const float mts = group4_max(mt) * a.qscale;
         if (mts > m[rt]) {  // the row's own decision (all lanes of a row agree)
           const float al = __builtin_amdgcn_exp2f(m[rt] - mts);  // 0 on the row's first scores
 #pragma unroll
@@ -407,44 +467,33 @@ __device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int
           m[rt] = mts;
         }
         const float nm = m[rt] == -INFINITY ? 0.f : -m[rt];
-        Pack16 p0, p1;
+        Pack16 pp[KP];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+        for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
           for (int r = 0; r < 4; r += 2) {
-            const f2_t e = {__builtin_amdgcn_exp2f(fmaf(s[tt][rt][r], a.qscale, nm)),
-                            __builtin_amdgcn_exp2f(fmaf(s[tt][rt][r + 1], a.qscale, nm))};
-            const bf16x2_t h = __builtin_convertvector(e, bf16x2_t);
-            Pack16& dst = tt < 2 ? p0 : p1;
-            dst.v[(tt & 1) * 4 + r] = h[0];
-            dst.v[(tt & 1) * 4 + r + 1] = h[1];
+            const f2_t ex = {__builtin_amdgcn_exp2f(fmaf(s[tt][rt][r], a.qscale, nm)),
+                             __builtin_amdgcn_exp2f(fmaf(s[tt][rt][r + 1], a.qscale, nm))};
+            const bf16x2_t h = __builtin_convertvector(ex, bf16x2_t);
+            pp[tt >> 1].v[(tt & 1) * 4 + r] = h[0];
+            pp[tt >> 1].v[(tt & 1) * 4 + r + 1] = h[1];
           }
-        pb[rt][0] = p0.v;
-        pb[rt][1] = p1.v;
-        lacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones.v, pb[rt][0], lacc[rt], 0, 0, 0);
-        lacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones.v, pb[rt][1], lacc[rt], 0, 0, 0);
-      }
-      // ---- O^T += V^T P^T; k-slot j of lane group kb is position 32 ks2 + 4 kb + j (j < 4),
-      //      32 ks2 + 16 + 4 kb + (j - 4) otherwise, as in P^T
-      const int e = l16 >> 2, qd = l16 & 3;
 #pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const int ra = 32 * ks2 + 4 * kb + e, rb = ra + 16;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int ch = 2 * dt + (qd >> 1), half = 8 * (qd & 1);
-          const uint2 lo = lds_read_tr16(vt + ra * kVtRow + vt_chunk(ra, ch) * 16 + half);
-          const uint2 hi = lds_read_tr16(vt + rb * kVtRow + vt_chunk(rb, ch) * 16 + half);
-          Pack16 va;
-          va.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
-            o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pb[rt][ks2], o[dt][rt], 0, 0, 0);
+        for (int ks2 = 0; ks2 < KP; ++ks2) {
+          pb[rt][ks2] = pp[ks2].v;
+          lacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones.v, pb[rt][ks2], lacc[rt], 0, 0, 0);
         }
       }
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const Pack16 va = vf[i % kVtPrefetch];
+        if (i + kVtPrefetch < NV) vload(vf[i % kVtPrefetch], i + kVtPrefetch);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          o[i % DT][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pb[rt][i / DT], o[i % DT][rt], 0, 0, 0);
+      }
     }
-    __syncthreads();  // every wave is done with stage j & 1
-    if (j + 2 < ntile) issue(j + 2);
   }
 
   if (row0 >= M) return;
@@ -464,10 +513,17 @@ __device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int
   }
 }
 
+// One workgroup per (split, bh, row block), from a one-dimensional grid: the row
+// blocks of one (split, bh) share their K and V tiles, so their workgroup ids are
+// congruent mod 8 (workgroups go to the eight XCDs, each with its own L2, in id
+// order) and lie within 8 * nblk of each other.  Ids past the last (split, bh) exit.
 template <int RT>
-__global__ void __launch_bounds__(kVerThreads) verify_tile_kernel(VerifyArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char ring[2][2 * kVtTileBytes];
-  verify_tiles<RT>(a, blockIdx.x, blockIdx.y, blockIdx.z, ring);
+__global__ void __launch_bounds__(kVerThreads) verify_tile_kernel(VerifyArgs a, int nblk, int units) {
+  __shared__ __attribute__((aligned(16))) VtStage ring[kVtStages];
+  const int id = blockIdx.x;
+  const int u = (id / (8 * nblk)) * 8 + (id & 7);
+  if (u >= units) return;
+  verify_tiles<RT>(a, u % a.splits, (id >> 3) % nblk, u / a.splits, ring);
 }
 
 // Draft-side decode over kept (token-dropped) bf16 rows, d = 128, at most 16 q-heads
@@ -476,7 +532,7 @@ __global__ void __launch_bounds__(kVerThreads) verify_tile_kernel(VerifyArgs a) 
 // kept row; splits 0 .. S-2 cover the kept rows and write the decode partials, split
 // S-1 covers the full-precision tail rows; decode_merge_kernel combines them.
 __global__ void __launch_bounds__(kVerThreads) decode_dense_kernel(VerifyArgs a, DecodeArgs d) {
-  __shared__ __attribute__((aligned(16))) unsigned char ring[2][2 * kVtTileBytes];
+  __shared__ __attribute__((aligned(16))) VtStage ring[kVtStages];
   if (static_cast<int>(blockIdx.x) == d.splits - 1) {
     decode_tail_partial_d128(d, blockIdx.z, d.splits - 1, reinterpret_cast<float*>(&ring[0][0]));
     return;
@@ -686,15 +742,17 @@ extern "C" vc_status vc_verify_attn_full(const void* q, const void* k_cache, con
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(bh * a.splits * M * d * sizeof(float), 256));
   hipStream_t s = as_stream(stream);
   if (kv_dtype == VC_BF16 && d == 128) {
-    // at most 128 rows per workgroup: RT (1 or 2) 16-row tiles per wave
-    const int nblk = static_cast<int>(cdiv(M, 128));
-    const int RT = cdiv(cdiv(M, nblk), 64) > 1 ? 2 : 1;
+    // 4 waves of one 16-row tile (up to 64 rows) or two (128 rows per workgroup), as
+    // many row blocks as M needs
+    const int RT = M <= 64 ? 1 : 2;
+    const int nblk = static_cast<int>(cdiv(M, 64 * RT));
     a.rows_per_block = 64 * RT;
-    dim3 grid(a.splits, static_cast<unsigned>(cdiv(M, 64 * RT)), static_cast<unsigned>(bh));
+    const int units = a.splits * static_cast<int>(bh);
+    const dim3 grid(static_cast<unsigned>(cdiv(units, 8) * 8 * nblk));
     if (RT == 1)
-      hipLaunchKernelGGL((verify_tile_kernel<1>), grid, dim3(kVerThreads), 0, s, a);
+      hipLaunchKernelGGL((verify_tile_kernel<1>), grid, dim3(kVerThreads), 0, s, a, nblk, units);
     else
-      hipLaunchKernelGGL((verify_tile_kernel<2>), grid, dim3(kVerThreads), 0, s, a);
+      hipLaunchKernelGGL((verify_tile_kernel<2>), grid, dim3(kVerThreads), 0, s, a, nblk, units);
     VC_LAUNCHED("verify_tile_kernel");
     dim3 mgrid(static_cast<unsigned>(cdiv(static_cast<int64_t>(M) * d, 256)), static_cast<unsigned>(bh));
     hipLaunchKernelGGL(verify_merge_kernel<bf16_t>, mgrid, dim3(256), 0, s, a, out, lse);
