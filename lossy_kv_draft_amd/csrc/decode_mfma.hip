@@ -320,9 +320,12 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
   // group, so one product per block; added to every channel tile at the end
   f4_t accz = f4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
-  h8_t qt[4];  // queries times the current K group's scales (the B operand of the scores)
-  f4_t kbias;  // sum_c q_c z_c - 64 sum_c qt_c of the current group, per q-head column
-  int g_cur = -1;
+  // the score operands of one K group: the queries times the group's scales (the B
+  // operand of the scores) and sum_c q_c z_c - 64 sum_c qt_c per q-head column
+  struct KQ {
+    h8_t qt[4];
+    f4_t kbias;
+  };
 
   // The block's bytes (K codes, V codes, V parameters, the K parameters of its
   // group(s)) are copied global -> LDS by the wave itself (16 bytes per lane per
@@ -394,7 +397,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
   // becomes q * s and the bias sum_c q_c z_c - 64 sum_c (q s)_c is formed on the
   // matrix cores (every row of its A operands is the same, so every score row of a
   // column receives its column's bias).
-  auto use_kp = [&](const unsigned char* kp) {
+  auto use_kp = [&](const unsigned char* kp) -> KQ {
     // the scale and zero pairs do not depend on the q-head column: each lane converts
     // one pair of each (step n / 4, pair n % 4 of its channel chunk) and the wave
     // shares them through LDS; only q * s is per lane
@@ -409,7 +412,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
     __builtin_amdgcn_wave_barrier();
     constexpr uint32_t kNeg64 = 0xD400D400u;  // (-64, -64) in f16
     const uint32_t neg64[4] = {kNeg64, kNeg64, kNeg64, kNeg64};
-    kbias = f4_t{0.f, 0.f, 0.f, 0.f};
+    KQ r;
+    r.kbias = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const uint4 sw = *reinterpret_cast<const uint4*>(&sh_kq[wave][0][kb][4 * s]);
@@ -421,11 +425,12 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
       uint32_t q2[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) q2[jj] = as_u32(as_h2(qw[jj]) * as_h2(s2[jj]));
-      qt[s] = __builtin_bit_cast(h8_t, q2);
-      kbias = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, z2), bq[s], kbias, 0, 0, 0);
-      kbias = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, neg64), qt[s], kbias, 0, 0, 0);
+      r.qt[s] = __builtin_bit_cast(h8_t, q2);
+      r.kbias = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, z2), bq[s], r.kbias, 0, 0, 0);
+      r.kbias = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, neg64), r.qt[s], r.kbias, 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
+    return r;
   };
   // V parameter (as float) of a slot token from its raw word
   // (with one group per token the element parity is the slot's parity; otherwise the
@@ -441,23 +446,23 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
     }
   };
 
-  auto process = [&](int t0, const Blk& cur, const unsigned char* slot, auto full_tag) {
+  // kq: the score operands of the block's K group when a group spans whole blocks
+  // (G >= 32); with 16-token groups each 16-token tile forms its own from the slot
+  auto process = [&](int t0, const Blk& cur, const unsigned char* slot, const KQ& kq, auto full_tag) {
     constexpr bool full = decltype(full_tag)::value;  // every row of the block is live
     // ---- S^T = K_hat Q^T for the two 16-token tiles
     f4_t sc[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const int g = (t0 + 16 * tt) / G;
-      if (g != g_cur) {  // wave-uniform
-        use_kp(slot + Ring::kOffKP + (NKG == 1 ? 0 : tt) * 2 * D * sizeof(P));
-        g_cur = g;
-      }
-      sc[tt] = kbias;
+      KQ kt;
+      if constexpr (NKG == 2) kt = use_kp(slot + Ring::kOffKP + tt * 2 * D * sizeof(P));
+      const KQ& k = NKG == 2 ? kt : kq;
+      sc[tt] = k.kbias;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         uint32_t mp[4];
         kpairs<KB>(cur.kw[tt], s, mp);
-        sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, mp), qt[s], sc[tt], 0, 0, 0);
+        sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, mp), k.qt[s], sc[tt], 0, 0, 0);
       }
     }
 
@@ -543,24 +548,41 @@ __global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) 
   // tracks, so it adds none behind the copies, which would drain the ring)
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   for (int i = 0; i < nblk && i < Ring::kDepth; ++i) issue(i);
-  for (int i = 0; i < nfull; ++i) {
+  auto wait_blk = [&](int i) {
     if (i + Ring::kDepth <= nblk) Ring::wait_ahead();
     else Ring::wait_all();
-    const unsigned char* slot = wring + (i % Ring::kDepth) * Ring::kSlot;
-    Blk cur;
-    read_blk(slot, cur);
-    process(t_begin + 32 * i, cur, slot, Full{});
-    if (i + Ring::kDepth < nblk) {
-      Ring::lds_reads_done();
-      issue(i + Ring::kDepth);
+  };
+  // one pass of the outer loop per K group (its blocks in the inner loop), so that the
+  // group's score operands are formed once and are not loop-carried
+  for (int i = 0; i < nfull;) {
+    KQ kq;
+    int nb = nfull - i;
+    if constexpr (NKG == 1) {
+      const int t0 = t_begin + 32 * i;
+      nb = min(nb, (G - t0 % G) / 32);  // blocks left in this group
+      wait_blk(i);
+      kq = use_kp(wring + (i % Ring::kDepth) * Ring::kSlot + Ring::kOffKP);
+    }
+    for (int e = i + nb; i < e; ++i) {
+      wait_blk(i);
+      const unsigned char* slot = wring + (i % Ring::kDepth) * Ring::kSlot;
+      Blk cur;
+      read_blk(slot, cur);
+      process(t_begin + 32 * i, cur, slot, kq, Full{});
+      if (i + Ring::kDepth < nblk) {
+        Ring::lds_reads_done();
+        issue(i + Ring::kDepth);
+      }
     }
   }
   Ring::wait_all();
   if (nfull < nblk) {  // the partial last block (its copies were issued above)
     const unsigned char* slot = wring + (nfull % Ring::kDepth) * Ring::kSlot;
+    KQ kq;
+    if constexpr (NKG == 1) kq = use_kp(slot + Ring::kOffKP);
     Blk cur;
     read_blk(slot, cur);
-    process(t_begin + 32 * nfull, cur, slot, Part{});
+    process(t_begin + 32 * nfull, cur, slot, kq, Part{});
   }
   __syncthreads();  // every wave's copies have landed before the ring is reused
 
