@@ -194,10 +194,19 @@ size_t vc_decode_workspace_bytes(const vc_ckv* ckv, int32_t Hq);
  * in float32.
  *
  * Batch invariance: the cache is cut into splits of split_tokens rows at absolute
- * positions (0 = the library default for this B*Hkv, see vc_verify_split_tokens)
- * and every row is reduced in the same order whatever k, its position in the
- * window or the other sequences' lengths are; so row i equals, bit for bit, the
- * 1-row call made with ctx length L + i and the same split_tokens.
+ * positions (0 = the library default for this B, Hkv and cache_rows, see
+ * vc_verify_split_tokens) and every row is reduced in the same order whatever k,
+ * its position in the window or the other sequences' lengths are; so row i equals,
+ * bit for bit, the 1-row call made with ctx length L + i and the same split_tokens.
+ * split_tokens must be a multiple of 64.
+ *
+ * vc_verify_workspace_bytes: workspace for calls with contexts up to max_len and
+ * this k and split_tokens (0: the default for a cache of max_len + k rows, which
+ * also covers the default of any larger cache).
+ * vc_verify_split_tokens: the default split, a multiple of 64 chosen so that a
+ * cache of cache_rows rows is cut into at most as many splits per (sequence,
+ * kv-head) as workgroups of the verification kernel fit on the current device
+ * for all B*Hkv of them at once (512 are assumed when no device is present).
  * ------------------------------------------------------------------------- */
 vc_status vc_verify_attn_full(const void* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
                               int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t k,
@@ -206,7 +215,7 @@ vc_status vc_verify_attn_full(const void* q, const void* k_cache, const void* v_
                               void* ws, size_t ws_bytes, void* stream);
 size_t vc_verify_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t k,
                                  int64_t max_len, int32_t split_tokens);
-int32_t vc_verify_split_tokens(int32_t B, int32_t Hkv);
+int32_t vc_verify_split_tokens(int32_t B, int32_t Hkv, int64_t cache_rows);
 
 /* ---------------------------------------------------------------------------
  * Greedy tokens (summary page: greedy-decoding output identical to full-KV

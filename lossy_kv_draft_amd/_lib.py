@@ -53,7 +53,7 @@ _DECLS = {
     "vc_verify_attn_full": (c_i32, [c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, c_i64, c_p,
                                     c_i32, c_f32, c_p, c_p, c_p, c_sz, c_p]),
     "vc_verify_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, c_i32]),
-    "vc_verify_split_tokens": (c_i32, [c_i32, c_i32]),
+    "vc_verify_split_tokens": (c_i32, [c_i32, c_i32, c_i64]),
     "vc_head_mean": (c_i32, [c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, c_i64, c_i64, c_p, c_p]),
     "vc_logits_argmax": (c_i32, [c_p, c_i32, c_i64, c_i32, c_p, c_i32, c_i32, c_p, c_p, c_sz, c_p]),
     "vc_logits_workspace_bytes": (c_sz, [c_i64, c_i32]),
@@ -243,8 +243,8 @@ def vc_decode_attn_compressed(ckv: Ckv, q, out, *, lse=None, sm_scale=None, main
                                          ws.numel(), _stream(stream)), "vc_decode_attn_compressed")
 
 
-def vc_verify_split_tokens(B: int, Hkv: int) -> int:
-    return lib.vc_verify_split_tokens(B, Hkv)
+def vc_verify_split_tokens(B: int, Hkv: int, cache_rows: int) -> int:
+    return lib.vc_verify_split_tokens(B, Hkv, cache_rows)
 
 
 def vc_verify_workspace_bytes(B, Hq, Hkv, d, k, max_len, split_tokens=0) -> int:

@@ -33,6 +33,8 @@
 // this file are compiled without floating-point contraction so that every
 // instantiation performs the same roundings.
 
+#include <algorithm>
+
 #include "common.h"
 #include "decode_common.h"
 
@@ -677,17 +679,38 @@ vc_status launch_decode_dense(const vc_ckv* c, const DecodeArgs& d, hipStream_t 
 
 using namespace vc;
 
-extern "C" int32_t vc_verify_split_tokens(int32_t B, int32_t Hkv) {
-  int64_t bh = static_cast<int64_t>(B > 0 ? B : 1) * (Hkv > 0 ? Hkv : 1);
-  int64_t c = 1024;
-  while (c < 64 * bh && c < 16384) c *= 2;
-  return static_cast<int32_t>(c);
+// Workgroups of the bf16 tile kernel that fit on the device at once (queried once;
+// 512 without a device).
+static int verify_resident() {
+  static const int r = [] {
+    int dev = 0, cus = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 512;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 512;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, verify_tile_kernel<2>, kVerThreads, 0) != hipSuccess)
+      return 512;
+    return (per > 0 ? per : 1) * (cus > 0 ? cus : 1);
+  }();
+  return r;
+}
+
+// The default split: a full cache of cache_rows rows is cut into as many splits per
+// (sequence, kv-head) as workgroups fit on the device for all of them at once, so a
+// pass over a nearly full cache is one round of workgroups with no short trailing
+// split.  It depends on the cache, not on the context length or the window, so the
+// calls that must agree bit for bit (a k-row pass and its 1-row steps) share it.
+extern "C" int32_t vc_verify_split_tokens(int32_t B, int32_t Hkv, int64_t cache_rows) {
+  const int64_t bh = static_cast<int64_t>(B > 0 ? B : 1) * (Hkv > 0 ? Hkv : 1);
+  const int64_t S = std::max<int64_t>(1, verify_resident() / bh);
+  const int64_t c = cdiv(std::max<int64_t>(cache_rows, 1), S);
+  return static_cast<int32_t>(std::min<int64_t>(cdiv(c, kVerTile) * kVerTile, 1ll << 30));
 }
 
 extern "C" size_t vc_verify_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t k,
                                             int64_t max_len, int32_t split_tokens) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || k <= 0 || max_len < 0) return 0;
-  int64_t C = split_tokens > 0 ? split_tokens : vc_verify_split_tokens(B, Hkv);
+  // the default for the smallest cache that holds max_len + k rows: a larger cache
+  // gets a larger default split, so fewer splits and less workspace
+  int64_t C = split_tokens > 0 ? split_tokens : vc_verify_split_tokens(B, Hkv, max_len + k);
   int64_t S = cdiv(max_len + k, C);
   if (S < 1) S = 1;
   size_t M = static_cast<size_t>(Hq / Hkv) * k;
@@ -714,7 +737,7 @@ extern "C" vc_status vc_verify_attn_full(const void* q, const void* k_cache, con
     VC_UNSUPPORTED(d == 64 || d == 128, "bf16 verify supports d = 64 or 128 (got %d)", d);
   else
     VC_UNSUPPORTED(d <= 256, "f32 verify supports d <= 256 (got %d)", d);
-  const int64_t C = split_tokens > 0 ? split_tokens : vc_verify_split_tokens(B, Hkv);
+  const int64_t C = split_tokens > 0 ? split_tokens : vc_verify_split_tokens(B, Hkv, cache_rows);
   size_t need = vc_verify_workspace_bytes(B, Hq, Hkv, d, k, ctx_len, static_cast<int32_t>(C));
   if (!ws || ws_bytes < need) {
     set_error("verify workspace needs %zu bytes (got %zu)", need, ws_bytes);
@@ -743,7 +766,8 @@ extern "C" vc_status vc_verify_attn_full(const void* q, const void* k_cache, con
   hipStream_t s = as_stream(stream);
   if (kv_dtype == VC_BF16 && d == 128) {
     // 4 waves of one 16-row tile (up to 64 rows) or two (128 rows per workgroup), as
-    // many row blocks as M needs
+    // many row blocks as M needs (64-row blocks for M = 160 or 320 were slower: more
+    // blocks reading the same tiles)
     const int RT = M <= 64 ? 1 : 2;
     const int nblk = static_cast<int>(cdiv(M, 64 * RT));
     a.rows_per_block = 64 * RT;

@@ -224,7 +224,7 @@ class Session:
         B, N0 = self.B, self.N0
         assert N0 >= 1 and B * max(k, chunk) <= dec.max_rows
         self.rows = _round_up(N0 + gen + 2 * k, 32)
-        self.split = L.vc_verify_split_tokens(B, s.Hkv)
+        self.split = L.vc_verify_split_tokens(B, s.Hkv, self.rows)
         self.device = device
         self.ver_ws = L.workspace(L.vc_verify_workspace_bytes(B, s.Hq, s.Hkv, s.hd, max(k, chunk), self.rows,
                                                               self.split), device)

@@ -33,9 +33,13 @@ def test_keep_count_and_split_tokens():
     assert L.vc_drop_keep_count(0.25, 131072) == 32768
     assert L.vc_drop_keep_count(0.25, 10) == 3
     assert L.vc_drop_keep_count(1.0, 7) == 7
-    for B, H in [(1, 2), (4, 4), (8, 8), (16, 4), (4, 8)]:
-        c = L.vc_verify_split_tokens(B, H)
-        assert c % 64 == 0 and 1024 <= c <= 16384
+    # without a device the library assumes 512 resident workgroups
+    for B, H, rows in [(1, 2, 32800), (4, 4, 64), (8, 8, 32800), (16, 4, 65576), (4, 8, 131112), (8, 8, 1)]:
+        c = L.vc_verify_split_tokens(B, H, rows)
+        S = max(1, 512 // (B * H))                # splits per (sequence, kv-head) that fit
+        assert c % 64 == 0 and c >= 64
+        assert -(-rows // c) <= S                 # at most S splits
+        assert c == 64 or -(-rows // (c - 64)) > S  # and the smallest such multiple of 64
 
 
 def _ckv(**kw):

@@ -302,7 +302,7 @@ def test_verify_forward_matches_oracle(std):
         for b in range(B):
             cache.k[l][b, :, : Lb[b]] = T(kv[l][b][0], torch.bfloat16)
             cache.v[l][b, :, : Lb[b]] = T(kv[l][b][1], torch.bfloat16)
-    split = L.vc_verify_split_tokens(B, Hkv)
+    split = L.vc_verify_split_tokens(B, Hkv, rows)
     ws = L.workspace(L.vc_verify_workspace_bytes(B, shape.Hq, Hkv, hd, k, rows, split), DEV)
     dec = R.DecoderGPU(shape, R.weights_to(wcpu, DEV), max_rows=B * k)
     i32 = lambda a: T(np.asarray(a), torch.int32)

@@ -61,7 +61,7 @@ def test_verify_batch_invariance(name):
     K, V, Q, Kw, Vw = inputs(w)
     dt = tdtype(w.dtype)
     kc, vc = _cache(K, V, Kw, Vw, dt)
-    split = L.vc_verify_split_tokens(w.B, w.Hkv)
+    split = L.vc_verify_split_tokens(w.B, w.Hkv, kc.shape[2])
     q = T(Q, dt)
     out, lse = _run(w, q, kc, vc, w.N, split)
     for i in [0, 1, w.k // 2, w.k - 1]:
