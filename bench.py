@@ -53,14 +53,20 @@ def parse():
     return p.parse_args()
 
 
-DECODE_SOURCES = ("decode_mfma.hip", "decode_common.h", "decode.hip", "common.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_llama8b_n32k_hbm_traffic.txt")
+# Committed counter summaries of the decode kernel per workload, and the sources whose
+# hash they record (a summary taken on other sources is not reported).
+TRAFFIC = {
+    "llama8b_n32k_4bit": ("decode_mfma_llama8b_n32k_hbm_traffic.txt",
+                          ("decode_mfma.hip", "decode_common.h", "decode.hip", "common.h")),
+    "drop25_n128k": ("decode_dense_drop25_n128k_hbm_traffic.txt",
+                     ("verify.hip", "decode_common.h", "decode.hip", "common.h")),
+}
 
 
-def decode_source_hash():
+def source_hash(files):
     import hashlib
     h = hashlib.sha256()
-    for f in DECODE_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "lossy_kv_draft_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -69,13 +75,16 @@ def decode_source_hash():
 def measured_traffic(workload_name):
     """HBM bytes per decode launch from the committed counter summary, if it was
     taken on the current decode sources and this workload; else None."""
+    if workload_name not in TRAFFIC:
+        return None
+    fname, files = TRAFFIC[workload_name]
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(os.path.join(ROOT, "profiles", fname)) as fh:
             kv = dict(line[2:].split(":", 1) for line in fh if line.startswith("# ") and ":" in line)
     except OSError:
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
-    if kv.get("source_sha256") != decode_source_hash() or kv.get("workload") != workload_name:
+    if kv.get("source_sha256") != source_hash(files) or kv.get("workload") != workload_name:
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
