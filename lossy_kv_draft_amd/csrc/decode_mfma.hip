@@ -206,9 +206,13 @@ struct DecRing {
   static constexpr int kSlot = kOffKP + kNKG * 2 * kKPG;
   static constexpr int pieces(int bytes) { return (bytes + 1023) / 1024; }
   static constexpr int kInstr = pieces(kKC) + pieces(kVC) + pieces(2 * kVP) + kNKG * pieces(2 * kKPG);
-  // two workgroups of 4 waves per compute unit (80 KB of LDS each, ~2.5 KB of it
-  // outside the ring): 4 * depth * slot <= 79360
-  static constexpr int kDepthRaw = 19840 / kSlot;
+  // kWgPerCu workgroups of 4 waves per compute unit share its 160 KB of LDS (~2.5 KB
+  // of each outside the ring): 4 * depth * slot <= 160 KB / kWgPerCu - 2.5 KB.  Three
+  // (three waves per SIMD, at most 168 registers a wave: a shallower ring, but more
+  // waves to hide the latency of the code conversion) where that measured faster and
+  // needs no register spills: bf16 parameters with 64-channel V groups; else two.
+  static constexpr int kWgPerCu = (sizeof(P) == 2 && NGV == 2) ? 3 : 2;
+  static constexpr int kDepthRaw = (163840 / kWgPerCu - 2560) / (4 * kSlot);
   static constexpr int kDepth = kDepthRaw < 2 ? 2 : (kDepthRaw > 8 ? 8 : kDepthRaw);
   static_assert(kSlot % 16 == 0 && kVP % 16 == 0 && kKPG % 16 == 0, "16-byte pieces");
   static_assert((kDepth - 1) * kInstr <= 63, "vmcnt range");
@@ -243,7 +247,9 @@ struct type_tag {
 };
 
 template <int KB, int VB, int NGV, typename P>
-__global__ void __launch_bounds__(kDecThreads) decode_mfma_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kDecThreads)
+__attribute__((amdgpu_waves_per_eu(DecRing<KB, VB, NGV, P>::kWgPerCu)))
+decode_mfma_kernel(DecodeArgs a) {
   constexpr int D = 128;
   constexpr int G = D / NGV;                          // K: tokens per group; V: channels per group
   constexpr int KW = D * KB / 32;                     // words per packed K row
