@@ -341,6 +341,28 @@ def e2e_rounds(ctx, gen, slots):
                     "synthetic model, not of a trained one"}
 
 
+def gpu_state():
+    """Clocks and socket power as amd-smi reports them (read-only query)."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        g = json.loads(r.stdout)["gpu_data"][0]
+        clk = g["clock"]
+        gfx = [clk[k]["clk"]["value"] for k in sorted(clk) if k.startswith("gfx_")]
+        return {"tool": "amd-smi metric --clock --power", "gfx_clk_mhz": gfx,
+                "gfx_max_clk_mhz": clk["gfx_0"]["max_clk"]["value"], "mem_clk_mhz": clk["mem_0"]["clk"]["value"],
+                "socket_power_w": g["power"]["socket_power"]["value"]}
+    except Exception as e:  # the tool is optional; its absence does not fail the run
+        return {"error": f"{type(e).__name__}: {e}"[:200]}
+
+
+def spread(v_us):
+    """median, p10 and p90 of a list of durations in microseconds."""
+    q = np.percentile(np.asarray(v_us, dtype=np.float64), [50, 10, 90])
+    return {"median": round(float(q[0]), 3), "p10": round(float(q[1]), 3), "p90": round(float(q[2]), 3)}
+
+
 def cpu_baseline(w, seconds):
     """The oracle (numpy, float64 attention) timed on the host for a bounded sample:
     whole (sequence, kv-head) slices of the same workload -- dequantize the slice's
@@ -413,6 +435,7 @@ def main():
         run_step(st, evs[s], dec[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    state = gpu_state()  # right after the timed region
     draft_ms = sum(e[0].elapsed_time(e[1]) for e in evs)
     verify_ms = sum(e[1].elapsed_time(e[2]) for e in evs)
     tok_ms = sum(e[2].elapsed_time(e[3]) for e in evs)
@@ -444,6 +467,17 @@ def main():
         "verify_attn_tflops": round(verify_tflops, 2),
         "verify_attn_hbm_gbs": round(verify_gbs, 1),
         "verify_mfma_frac": round(verify_tflops / BF16_PEAK_TFLOPS, 4),
+        # roofline of the verify pass: arithmetic intensity (algorithmic flops per byte of
+        # the full cache), the attainable rate min(MFMA peak, AI x HBM peak), and the
+        # fraction of it reached
+        "verify_roofline": {"ai_flop_per_byte": round(vflops / verify_bytes(w, w.N), 1),
+                            "attainable_tflops": round(min(BF16_PEAK_TFLOPS, vflops / verify_bytes(w, w.N) *
+                                                           HBM_PEAK_GBS / 1e3), 1),
+                            "frac_of_attainable": round(verify_tflops / min(BF16_PEAK_TFLOPS, vflops / verify_bytes(
+                                w, w.N) * HBM_PEAK_GBS / 1e3), 4)},
+        "decode_call_us": spread([x * 1e3 for x in dec_launch_ms]),
+        "verify_call_us": spread([e[1].elapsed_time(e[2]) * 1e3 for e in evs]),
+        "gpu_state": state,
         "kernel_round_accepted_tok_per_s": round(accepted / (step_ms * 1e-3), 1),
         "mean_accept_len": round(acc_len, 3),
         "phase_ms": {"draft": round(draft_ms / a.steps, 4), "verify": round(verify_ms / a.steps, 4),
