@@ -475,6 +475,43 @@ class VeriCacheLoop:
         return np.array([o[: self.sess.gen] for o in self.out], np.int32)
 
 
+class Staggered:
+    """Several independent batches decoded at once, each by its own VeriCacheLoop
+    (its own decoder buffers, caches and staging stream) driven by its own host thread
+    on its own compute stream, so that one batch's drafting overlaps another's full-KV
+    staging and verification (summary page, "What the paper found": the drafting,
+    staging and verification of different batches are staggered across the GPU and
+    the host link).  Each loop's HIP graph is captured when the loop is built, before
+    any thread starts; the threads share nothing but the device."""
+
+    def __init__(self, loops):
+        self.loops = list(loops)
+        self.streams = [torch.cuda.Stream() for _ in self.loops]
+
+    def run(self, timed=False):
+        import threading
+        errors = []
+
+        def drive(loop, stream):
+            try:
+                with torch.cuda.stream(stream):
+                    while not loop.done():
+                        loop.round(timed)
+                stream.synchronize()
+            except BaseException as e:  # re-raised in the calling thread
+                errors.append(e)
+
+        threads = [threading.Thread(target=drive, args=(lp, st)) for lp, st in zip(self.loops, self.streams)]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+        if errors:
+            raise errors[0]
+        torch.cuda.synchronize()
+        return [np.array([o[: lp.sess.gen] for o in lp.out], np.int32) for lp in self.loops]
+
+
 def random_weights(shape: ModelShape, seed_fn, std=0.02, device="cuda"):
     """bf16 weights of a random-initialised decoder; seed_fn(key, shape, std) returns
     a float32 numpy draw of N(0, std^2) for an integer key tuple.  Projections are

@@ -337,6 +337,29 @@ def test_round_output_equals_greedy_small(slots, graph):
     assert loop.rounds < w.gen_tokens          # drafts are accepted at least sometimes
 
 
+def test_staggered_batches_equal_greedy():
+    """Two batches decoded at once by Staggered (one host thread and compute stream
+    each, full KV staged through one device slot each): each batch's output equals its
+    own greedy output, and equals the same loop run alone."""
+    w = SMALL
+    shape = _shape(w)
+    seed = lambda key, shp, s: G.normal(w, key, shp, s, "f32")
+    weights = R.weights_to(R.random_weights(shape, seed, std=0.08, device="cpu"), DEV)
+    sessions = []
+    for i in range(2):
+        prompt = G.tokens(w, 10 + i, shape=(w.B, w.N), high=w.vocab)
+        dec = R.DecoderGPU(shape, weights, max_rows=w.B * max(w.k, 128))
+        sessions.append(R.Session(dec, prompt, w.k, w.gen_tokens, chunk=128, group=w.group, bits=(w.k_bits, w.v_bits)))
+    refs = [R.Greedy(se).run() for se in sessions]
+    alone = R.VeriCacheLoop(sessions[0], slots=1).run()
+    assert np.array_equal(alone, refs[0])
+    st = R.Staggered([R.VeriCacheLoop(se, slots=1) for se in sessions])
+    got = st.run(timed=True)
+    for b in range(2):
+        assert np.array_equal(got[b], refs[b]), b
+    say(f"rounds {[lp.rounds for lp in st.loops]}")
+
+
 def test_graph_draft_loop_matches_eager():
     """The captured draft loop produces the same drafts as the step-by-step launches
     (std 0.02 model: drafts are mostly accepted, so several rounds and group
