@@ -319,6 +319,16 @@ def e2e_rounds(ctx, gen, slots):
     loop = R.VeriCacheLoop(sess, slots=slots)
     got, t_vc = timed(lambda: loop.run(timed=True))
     ok = bool(np.array_equal(got, ref))
+    # the same batch with the draft horizon chosen per round by the cost model
+    horizons = tuple(h for h in (4, 8, 16, 32) if h <= w.k)
+    ada = R.VeriCacheLoop(sess, slots=slots, horizons=horizons)
+    got_a, t_ada = timed(lambda: ada.run())
+    adaptive = {"horizons": list(horizons), "accepted_tok_per_s": round(w.B * (gen - 1) / t_ada, 1),
+                "rounds": ada.rounds, "rounds_per_horizon": {str(k): v for k, v in ada.policy.chosen.items()},
+                "mean_round_ms_per_horizon": {str(k): round(float(np.mean(v)) * 1e3, 2)
+                                              for k, v in ada.policy.times.items() if v},
+                "output_equals_greedy": bool(np.array_equal(got_a, ref))}
+    del ada
     stag = staggered_rounds(w, shape, weights, sess, ref, slots, gen, chunk, timed)
     committed = w.B * (gen - 1)                                 # tokens produced after the prefill's first
     staged_bytes = loop.full.bytes_staged if hasattr(loop.full, "bytes_staged") else 0
@@ -338,6 +348,7 @@ def e2e_rounds(ctx, gen, slots):
             "speedup_vs_greedy_staged": round(vc_tps / st_tps, 2),
             "speedup_vs_greedy_resident": round(vc_tps / res_tps, 3),
             "output_equals_greedy": ok, "prefill_s": round(prefill_s, 2),
+            "adaptive_horizon": adaptive,
             "staggered": stag,
             "note": "random-init weights and uniform-random prompts; acceptance is a property of this "
                     "synthetic model, not of a trained one"}

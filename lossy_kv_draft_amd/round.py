@@ -17,6 +17,7 @@ The round follows "VeriCache: Turning Lossy KV Cache into Lossless LLM Inference
 Greedy full-KV decoding with the same kernels is the reference the output must equal.
 """
 from dataclasses import dataclass
+import time
 import numpy as np
 import torch
 
@@ -306,6 +307,49 @@ class Greedy:
         return torch.stack(self.out[:n], 1).cpu().numpy()
 
 
+class HorizonPolicy:
+    """Adaptive draft horizon from a cost model (summary page, "What the paper found":
+    the draft horizon is extended to exploit long acceptance runs): each round drafts
+    with the horizon k of `horizons` that maximises the estimated commits per second,
+    E[min(a + 1, k)] / T(k).  a is a sequence's accepted draft count; a round drafted
+    with horizon kr reveals min(a, kr - 1), which fixes min(a + 1, k) for every
+    k <= kr, so E[min(a + 1, k)] is the mean over the recent rounds drafted with a
+    horizon of at least k.  T(k) is the mean wall time of the recent rounds drafted with
+    k.  Every horizon is tried once, the longest first, and the longest is drafted again
+    every `explore` rounds so that its statistics stay current."""
+
+    def __init__(self, horizons, explore=8, memory=64):
+        self.h = sorted(set(int(k) for k in horizons))
+        self.explore, self.memory = explore, memory
+        self.times = {k: [] for k in self.h}
+        self.obs = []                       # (horizon, accepted counts of the active sequences)
+        self.rounds = 0
+        self.chosen = {k: 0 for k in self.h}
+
+    def choose(self):
+        untried = [k for k in reversed(self.h) if not self.times[k]]
+        if untried:
+            return untried[0]
+        if self.rounds % self.explore == 0:
+            return self.h[-1]
+        best, kb = -1.0, self.h[-1]
+        for k in self.h:
+            seen = [np.minimum(a + 1, k) for kr, a in self.obs if kr >= k and len(a)]
+            if not seen:
+                continue
+            rate = float(np.mean(np.concatenate(seen))) / float(np.mean(self.times[k][-16:]))
+            if rate > best:
+                best, kb = rate, k
+        return kb
+
+    def update(self, k, seconds, accepted):
+        self.rounds += 1
+        self.chosen[k] += 1
+        self.times[k].append(seconds)
+        self.obs.append((k, np.asarray(accepted, np.int64)))
+        del self.obs[:-self.memory]
+
+
 class VeriCacheLoop:
     """Draft-and-verify decoding.  slots=R keeps the full KV in pinned host memory and
     stages it through R device slots (R = layers: every layer staged during
@@ -318,8 +362,14 @@ class VeriCacheLoop:
     bounds (capacity and tail capacity) while the kernels read the per-sequence
     lengths."""
 
-    def __init__(self, sess: Session, slots=2, graph=True):
+    def __init__(self, sess: Session, slots=2, graph=True, horizons=None):
         self.sess = sess
+        # draft horizons: the session's k alone, or several (each at most k), one chosen
+        # per round by HorizonPolicy; buffers are sized for k
+        hs = sorted(set(int(h) for h in horizons)) if horizons else [sess.k]
+        assert 1 <= hs[0] and hs[-1] <= sess.k
+        self.policy = HorizonPolicy(hs) if len(hs) > 1 else None
+        self.horizons = hs
         dec, s, B, dev = sess.dec, sess.dec.s, sess.B, sess.device
         G, k = sess.group, sess.k
         kb, vb = sess.bits
@@ -351,7 +401,7 @@ class VeriCacheLoop:
         self.targets = torch.empty(B * k, dtype=torch.int32, device=dev)
         self.acc = torch.empty(B, dtype=torch.int32, device=dev)
         self.nc = torch.empty(B, dtype=torch.int32, device=dev)
-        self.com = torch.empty(B, k, dtype=torch.int32, device=dev)
+        self.com_flat = torch.empty(B * k, dtype=torch.int32, device=dev)
         self.rounds = 0
         self.accept_lens = []
         self.ev = {n: torch.cuda.Event(enable_timing=True) for n in ("start", "drafted", "verified", "end")}
@@ -363,12 +413,13 @@ class VeriCacheLoop:
         self.g_tok = torch.empty(B, **i32)
         self.g_pos, self.g_trow, self.g_tlen = (torch.empty(k, B, **i32) for _ in range(3))
         self.g_main = torch.empty(B, **i32)
-        self.graph = None
+        self.graphs = {}
         if graph:
             self._set_draft_inputs()
-            self.graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(self.graph):
-                self._draft_steps()
+            for h in hs:
+                self.graphs[h] = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(self.graphs[h]):
+                    self._draft_steps(h)
 
     def _set_draft_inputs(self):
         k = self.sess.k
@@ -380,10 +431,10 @@ class VeriCacheLoop:
         self.g_tlen.copy_(cpu(self.ctail[None, :] + i_col + 1))
         self.g_main.copy_(cpu(self.n_main))
 
-    def _draft_steps(self):
+    def _draft_steps(self, kr):
         dec, B = self.sess.dec, self.sess.B
         cur = self.g_tok
-        for i in range(self.sess.k):
+        for i in range(kr):
             attend = attend_draft(dec, self.ckvs, B, self.g_pos[i], self.g_trow[i], self.g_main, self.g_tlen[i],
                                   self.dec_ws)
             lg = dec.forward(cur, B, 1, attend)
@@ -396,7 +447,9 @@ class VeriCacheLoop:
     def round(self, timed=False):
         """One draft-and-verify round of every sequence; returns the tokens committed."""
         sess, dec, s = self.sess, self.sess.dec, self.sess.dec.s
-        B, k, G, dev = sess.B, sess.k, sess.group, sess.device
+        B, G, dev = sess.B, sess.group, sess.device
+        k = self.policy.choose() if self.policy else sess.k      # this round's horizon
+        t_round = time.perf_counter()
         maxL = int(self.Lb.max())
         if timed:
             self.ev["start"].record()
@@ -404,10 +457,10 @@ class VeriCacheLoop:
         self.full.begin(maxL, int(self.Lb.min()), maxL + k)
         # ---- k draft steps on the compressed cache
         self._set_draft_inputs()
-        if self.graph is not None:
-            self.graph.replay()
+        if self.graphs:
+            self.graphs[k].replay()
         else:
-            self._draft_steps()
+            self._draft_steps(k)
         if timed:
             self.ev["drafted"].record()
         drafts = self.drafts_T.t().contiguous()                    # [B, k]
@@ -422,11 +475,14 @@ class VeriCacheLoop:
 
         attend = attend_full(dec, self.full, B, k, vpos, row0, maxL, row0, sess.split, sess.ver_ws, after=keep_window)
         lg = dec.forward(window, B, k, attend)
-        L.vc_argmax_rows(lg, self.targets)
-        L.vc_accept(drafts, self.targets.view(B, k), self.acc, self.nc, self.com)
+        targets = self.targets[: B * k]
+        com = self.com_flat[: B * k].view(B, k)
+        L.vc_argmax_rows(lg, targets)
+        L.vc_accept(drafts[:, :k].contiguous(), targets.view(B, k), self.acc, self.nc, com)
         if timed:
             self.ev["verified"].record()
-        acc, nc, com = self.acc.cpu().numpy(), self.nc.cpu().numpy(), self.com.cpu().numpy()  # the round's one sync
+        acc, nc, com = self.acc.cpu().numpy(), self.nc.cpu().numpy(), com.cpu().numpy()  # the round's one sync
+        t_round = time.perf_counter() - t_round
         # a sequence that already has its tokens stays where it is (its rows are still
         # computed, within the cache, and discarded)
         active = np.array([len(o) < sess.gen for o in self.out])
@@ -466,6 +522,8 @@ class VeriCacheLoop:
             self.phase_ms["update"] += e["verified"].elapsed_time(e["end"])
         self.rounds += 1
         self.accept_lens.extend(int(a) for a in acc[active])
+        if self.policy:
+            self.policy.update(k, t_round, acc[active])
         return int(nc.sum())
 
     def run(self, timed=False):

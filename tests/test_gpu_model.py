@@ -360,6 +360,21 @@ def test_staggered_batches_equal_greedy():
     say(f"rounds {[lp.rounds for lp in st.loops]}")
 
 
+@pytest.mark.parametrize("graph", [True, False])
+def test_adaptive_horizon_equals_greedy(graph):
+    """Draft horizons chosen per round by the cost model (HorizonPolicy, horizons 2, 4
+    and 8 with buffers for 8): the output still equals greedy, and every horizon is
+    drafted at least once."""
+    w = SMALL
+    _, _, _, dec, sess = _setup(w, std=0.08, chunk=128)
+    ref = R.Greedy(sess).run()
+    loop = R.VeriCacheLoop(sess, slots=1, graph=graph, horizons=(2, 4, 8))
+    got = loop.run()
+    assert np.array_equal(got, ref)
+    assert all(v > 0 for v in loop.policy.chosen.values()), loop.policy.chosen
+    say(f"rounds {loop.rounds}, horizons chosen {loop.policy.chosen}")
+
+
 def test_graph_draft_loop_matches_eager():
     """The captured draft loop produces the same drafts as the step-by-step launches
     (std 0.02 model: drafts are mostly accepted, so several rounds and group
