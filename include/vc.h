@@ -236,6 +236,22 @@ vc_status vc_logits_argmax(const void* u, int32_t u_dtype, int64_t R, int32_t Kd
 size_t vc_logits_workspace_bytes(int64_t R, int32_t V);
 
 /* ---------------------------------------------------------------------------
+ * Channel rotation before quantization (summary page, "What the paper found":
+ * rotation-based low-bit quantizers such as RotateKV and TurboQuant behind the uniform
+ * compressor interface).
+ *
+ * vc_hadamard_rows: out[r] = x[r] H / sqrt(d) for rows r < rows, H the Sylvester
+ *   Hadamard matrix of order d (d = 64, 128 or 256).  x, out dtype (VC_BF16 or
+ *   VC_F32) [rows, d], contiguous; out may be x (in place).  float32 arithmetic, one
+ *   rounding to dtype.  The map is its own inverse and keeps dot products, so keys
+ *   and queries rotated alike give the same scores, and an attention output over
+ *   rotated values is rotated back by a second call.  A compressor with the
+ *   pre-pass rotates K and V rows before vc_compress; the drafter rotates q before
+ *   vc_decode_attn_compressed and its output after.
+ * ------------------------------------------------------------------------- */
+vc_status vc_hadamard_rows(const void* x, int32_t dtype, int64_t rows, int32_t d, void* out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Acceptance: longest prefix where draft equals target (episode page, source 2,
  * speculative decoding; summary page, greedy identity).
  *

@@ -58,6 +58,7 @@ _DECLS = {
     "vc_logits_argmax": (c_i32, [c_p, c_i32, c_i64, c_i32, c_p, c_i32, c_i32, c_p, c_p, c_sz, c_p]),
     "vc_logits_workspace_bytes": (c_sz, [c_i64, c_i32]),
     "vc_accept": (c_i32, [c_p, c_p, c_i32, c_i32, c_p, c_p, c_p, c_p]),
+    "vc_hadamard_rows": (c_i32, [c_p, c_i32, c_i64, c_i32, c_p, c_p]),
     "vc_stage_full_kv": (c_i32, [c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i64, c_i64, c_i64, c_i64,
                                  c_p, c_p]),
     "vc_stage_full_kv_d2h": (c_i32, [c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i64, c_i64, c_i64, c_i64,
@@ -261,6 +262,19 @@ def vc_verify_attn_full(q, k_cache, v_cache, ctx_len, out, *, lse=None, ctx_lens
                                    ctx_len, _ptr(ctx_lens), split_tokens,
                                    d ** -0.5 if sm_scale is None else sm_scale, _ptr(out), _ptr(lse), _ptr(ws),
                                    ws.numel(), _stream(stream)), "vc_verify_attn_full")
+
+
+def vc_hadamard_rows(x, out=None, *, stream=None):
+    """Rows of x [..., d] (contiguous, bf16 or f32) rotated by H / sqrt(d) into out
+    (default: a new tensor; out may be x).  Returns out."""
+    assert x.is_contiguous()
+    if out is None:
+        out = torch.empty_like(x)
+    assert out.is_contiguous() and out.shape == x.shape and out.dtype == x.dtype
+    d = x.shape[-1]
+    _check(lib.vc_hadamard_rows(_ptr(x), _dt(x.dtype), x.numel() // d if d else 0, d, _ptr(out), _stream(stream)),
+           "vc_hadamard_rows")
+    return out
 
 
 def vc_head_mean(o, u, *, k=None, stream=None):

@@ -107,3 +107,10 @@ def test_drop_rejects_bad_arguments():
     k = torch.zeros(1, 2, 10, 64, dtype=torch.bfloat16)
     _bad(L.vc_drop_scores, k, torch.zeros(2, 65, 64, dtype=torch.bfloat16), torch.zeros(1, 2, 10),
          ws=torch.zeros(1 << 16, dtype=torch.uint8), stream=0)
+
+
+def test_hadamard_rejects_unsupported_widths():
+    x = torch.zeros(3, 96, dtype=torch.bfloat16)
+    assert "d = 64, 128 or 256" in _bad(L.vc_hadamard_rows, x, stream=0, status=L._lib.VC_ERR_UNSUPPORTED)
+    y = torch.zeros(0, 128)
+    assert L.vc_hadamard_rows(y, stream=0).shape == (0, 128)    # no rows: nothing launched
