@@ -228,6 +228,29 @@ def run_step(st, ev=None, dec_ev=None):
         ev[3].record()
 
 
+def measure_rotation(st):
+    """The rotation pre-pass (vc_hadamard_rows) over the layer's full K: one read and
+    one write of every row; HBM-bound."""
+    import torch
+    import lossy_kv_draft_amd as L
+    x = st["kc"]
+    y = torch.empty_like(x)
+    for _ in range(2):
+        L.vc_hadamard_rows(x, y)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        L.vc_hadamard_rows(x, y)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / 5 * 1e3
+    nbytes = 2 * x.numel() * x.element_size()
+    return {"rows": int(x.numel() // x.shape[-1]), "d": int(x.shape[-1]), "us": round(us, 2),
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 /
+                                                                                   HBM_PEAK_GBS, 4)}
+
+
 def measure_stage(st):
     """Full-KV swap-in: H2D copy of the whole context of one layer from pinned host
     memory on a side stream, alone and overlapped with the k draft decodes."""
@@ -540,6 +563,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
                      "bytes_per_launch": int(per_launch), "avg_launch_us": round(dec_avg_ms * 1e3, 3)},
     }
+    line["rotation_prepass"] = measure_rotation(st)
     if not a.no_stage:
         line["stage_full_kv"] = measure_stage(st)
     if not a.no_e2e:

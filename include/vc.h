@@ -242,8 +242,9 @@ size_t vc_logits_workspace_bytes(int64_t R, int32_t V);
  *
  * vc_hadamard_rows: out[r] = x[r] H / sqrt(d) for rows r < rows, H the Sylvester
  *   Hadamard matrix of order d (d = 64, 128 or 256).  x, out dtype (VC_BF16 or
- *   VC_F32) [rows, d], contiguous; out may be x (in place).  float32 arithmetic, one
- *   rounding to dtype.  The map is its own inverse and keeps dot products, so keys
+ *   VC_F32) [rows, d], contiguous and 16-byte aligned (VC_ERR_INVALID_ARG
+ *   otherwise); out may be x (in place), but no other overlap.  float32
+ *   arithmetic, one rounding to dtype.  The map is its own inverse and keeps dot products, so keys
  *   and queries rotated alike give the same scores, and an attention output over
  *   rotated values is rotated back by a second call.  A compressor with the
  *   pre-pass rotates K and V rows before vc_compress; the drafter rotates q before

@@ -114,3 +114,5 @@ def test_hadamard_rejects_unsupported_widths():
     assert "d = 64, 128 or 256" in _bad(L.vc_hadamard_rows, x, stream=0, status=L._lib.VC_ERR_UNSUPPORTED)
     y = torch.zeros(0, 128)
     assert L.vc_hadamard_rows(y, stream=0).shape == (0, 128)    # no rows: nothing launched
+    z = torch.zeros(4 * 128 + 2, dtype=torch.bfloat16)[2:].view(4, 128)   # 4-byte offset
+    assert "aligned" in _bad(L.vc_hadamard_rows, z, stream=0)

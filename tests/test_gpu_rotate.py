@@ -35,6 +35,17 @@ def test_rotation_matches_oracle(dtype, d, rows):
     assert excess <= 0, f"max excess {excess}"
 
 
+@pytest.mark.parametrize("dtype,d,rows", [("f32", 256, 40001), ("bf16", 64, 270001)])
+def test_rotation_many_rows(dtype, d, rows):
+    """More rows than one pass of the (capped) grid holds, with a ragged last pass; the
+    oracle checks every 97th row."""
+    x = _rows(rows, d, (d, 1), dtype)
+    got = np32(L.vc_hadamard_rows(T(x, tdtype(dtype))))[::97]
+    ref = RO.rotate_rows(x[::97])
+    tol = (2.0 ** -8 if dtype == "bf16" else 1e-7) * np.abs(ref) + 1e-6 * np.abs(x[::97]).sum(-1, keepdims=True)
+    assert (np.abs(got - ref) <= tol).all()
+
+
 @pytest.mark.parametrize("d", [64, 256])
 def test_rotation_bit_exact_on_small_integers(d):
     """Small integers: every butterfly sum is exact in float32 and 1/sqrt(d) is a power of
