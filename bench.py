@@ -352,6 +352,7 @@ def e2e_rounds(ctx, gen, slots):
                                               for k, v in ada.policy.times.items() if v},
                 "output_equals_greedy": bool(np.array_equal(got_a, ref))}
     del ada
+    remote = remote_prefix_rounds(w, sess, ref, slots, gen, timed)
     stag = staggered_rounds(w, shape, weights, sess, ref, slots, gen, chunk, timed)
     committed = w.B * (gen - 1)                                 # tokens produced after the prefill's first
     staged_bytes = loop.full.bytes_staged if hasattr(loop.full, "bytes_staged") else 0
@@ -372,9 +373,48 @@ def e2e_rounds(ctx, gen, slots):
             "speedup_vs_greedy_resident": round(vc_tps / res_tps, 3),
             "output_equals_greedy": ok, "prefill_s": round(prefill_s, 2),
             "adaptive_horizon": adaptive,
+            "remote_prefix": remote,
             "staggered": stag,
             "note": "random-init weights and uniform-random prompts; acceptance is a property of this "
                     "synthetic model, not of a trained one"}
+
+
+def remote_prefix_rounds(w, sess, ref, slots, gen, timed, rates=(0.0, 25e9)):
+    """The remote-prefix-cache setting: the prompt's full KV staged every round from a
+    file (page-cached; the store's stand-in) by the library's reader threads, uncapped
+    and capped at 25 GB/s (a 200 Gb/s link); the generated rows from pinned host
+    memory.  Also the stager's raw rate: the prompt rows of the first `slots` layers
+    staged alone."""
+    import torch
+    from lossy_kv_draft_amd import round as R
+    out = []
+    for rate in rates:
+        loop = R.VeriCacheLoop(sess, slots=slots, prefix_store=dict(max_bytes_per_s=rate))
+        full = loop.full
+        full.begin(w.N, w.N, w.N)                   # warm the file's pages and the stager
+        for l in range(full.slots):
+            full.acquire(l)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        b0 = full.bytes_from_file
+        full.begin(w.N, w.N, w.N)
+        for l in range(full.slots):
+            full.acquire(l)
+        torch.cuda.synchronize()
+        t_stage = time.perf_counter() - t0
+        stage_bytes = full.bytes_from_file - b0
+        b0 = full.bytes_from_file
+        got, t = timed(lambda: loop.run())
+        out.append({"link_cap_GBps": rate / 1e9 if rate else None,
+                    "file_stage_GBps": round(stage_bytes / t_stage / 1e9, 2),
+                    "accepted_tok_per_s": round(w.B * (gen - 1) / t, 1), "rounds": loop.rounds,
+                    "round_ms": round(t / loop.rounds * 1e3, 2),
+                    "file_GB_per_round": round((full.bytes_from_file - b0) / loop.rounds / 1e9, 3),
+                    "output_equals_greedy": bool(np.array_equal(got, ref))})
+        full.close()
+        del loop, full
+        torch.cuda.empty_cache()
+    return out
 
 
 def staggered_rounds(w, shape, weights, sess0, ref0, slots, gen, chunk, timed):

@@ -15,7 +15,8 @@
  * - Pointers named host_* are host memory (pinned, from hipHostMalloc or a
  *   pinned torch tensor); every other data pointer is device memory on the
  *   current HIP device.  The caller owns all memory; the library never allocates
- *   or frees and keeps no per-call state beyond the thread-local error message.
+ *   or frees and keeps no per-call state beyond the thread-local error message,
+ *   except inside a vc_file_stager, which owns its threads and pinned buffers.
  * - Tensors are dense, row-major, with the shapes given in each comment (last
  *   index fastest).  Element types: VC_F32 = IEEE float32, VC_BF16 = bfloat16,
  *   int32/uint32 where stated.
@@ -29,7 +30,8 @@
  * - Errors: arguments are validated on the host before anything is enqueued.  A
  *   bad argument returns VC_ERR_INVALID_ARG (or VC_ERR_UNSUPPORTED for a legal but
  *   unimplemented combination, VC_ERR_WORKSPACE for a short workspace) with no
- *   side effect.  A HIP launch or copy failure returns VC_ERR_HIP.  The message of
+ *   side effect.  A HIP launch or copy failure returns VC_ERR_HIP, a failed file
+ *   read VC_ERR_IO.  The message of
  *   the last failure on the calling thread is returned by vc_last_error().  No
  *   C++ exception crosses this interface.
  */
@@ -48,7 +50,8 @@ typedef enum {
   VC_ERR_INVALID_ARG = 1,
   VC_ERR_UNSUPPORTED = 2,
   VC_ERR_WORKSPACE = 3,
-  VC_ERR_HIP = 4
+  VC_ERR_HIP = 4,
+  VC_ERR_IO = 5
 } vc_status;
 
 typedef enum { VC_F32 = 0, VC_BF16 = 1 } vc_dtype;
@@ -284,6 +287,43 @@ vc_status vc_stage_full_kv_d2h(const void* dev_k, const void* dev_v, void* host_
                                int32_t B, int32_t Hkv, int32_t d, int32_t elem_bytes, int64_t host_rows,
                                int64_t dev_rows, int64_t tok_begin, int64_t tok_end, void* copy_stream,
                                void* done);
+
+/* ---------------------------------------------------------------------------
+ * Full-KV staging from a file: the remote-prefix-cache setting (summary page, "What
+ * the paper found" and "Original abstract": the same method serves remote prefix
+ * caching, where the full KV's swap-in is network-bound rather than PCIe-bound).
+ * A file descriptor that supports pread stands in for the remote store.
+ *
+ * vc_file_stager_create: n_threads reader threads (1..64), n_buffers pinned
+ *   bounce buffers of chunk_bytes each (n_threads <= n_buffers <= 1024,
+ *   4 KiB <= chunk_bytes <= 1 GiB), reads capped at max_bytes_per_s (0 =
+ *   uncapped: the link being modelled).  Uses the current HIP device.  *out is
+ *   the stager, owned by the caller until vc_file_stager_destroy, which first
+ *   finishes every queued read and copy.
+ * vc_stage_full_kv_file: copies token rows [tok_begin, tok_end) of every
+ *   (sequence, kv-head) from the file -- K at byte k_offset and V at v_offset,
+ *   each laid out [B, Hkv, file_rows, d] of elem_bytes-sized elements -- to the
+ *   same rows of dev_k, dev_v ([B, Hkv, dev_rows, d]).  Returns at once with
+ *   *ticket; the reads and the host-to-device copies (on copy_stream) run on the
+ *   stager's threads, and `done` (a hipEvent_t as void*, or NULL) is recorded on
+ *   copy_stream once every copy of the call has been issued.  The file must not
+ *   change while the call is in flight; the device rows must not be read before
+ *   `done`.
+ * vc_file_stager_wait: blocks until every copy of the ticket's call has been
+ *   issued and `done` recorded, then returns the call's status (VC_ERR_IO with
+ *   the reason when a read failed, e.g. past the end of the file; the remaining
+ *   chunks of that call are skipped).  Every ticket is waited for exactly once;
+ *   a consumer waits for the ticket before it makes its stream wait for `done`.
+ * ------------------------------------------------------------------------- */
+typedef struct vc_file_stager vc_file_stager;
+vc_status vc_file_stager_create(int32_t n_threads, size_t chunk_bytes, int32_t n_buffers, double max_bytes_per_s,
+                                vc_file_stager** out);
+vc_status vc_file_stager_destroy(vc_file_stager* st);
+vc_status vc_stage_full_kv_file(vc_file_stager* st, int32_t fd, int64_t k_offset, int64_t v_offset, void* dev_k,
+                                void* dev_v, int32_t B, int32_t Hkv, int32_t d, int32_t elem_bytes, int64_t file_rows,
+                                int64_t dev_rows, int64_t tok_begin, int64_t tok_end, void* copy_stream, void* done,
+                                int64_t* ticket);
+vc_status vc_file_stager_wait(vc_file_stager* st, int64_t ticket);
 
 /* Message of the last failed call on this thread ("" if none).  Valid until the
  * next vc_* call on the same thread. */

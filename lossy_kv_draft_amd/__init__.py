@@ -12,6 +12,6 @@ from ._lib import (  # noqa: F401
     vc_drop_scores_workspace_bytes, vc_drop_select, vc_gather_rows, vc_decode_attn_compressed,
     vc_decode_workspace_bytes, vc_verify_attn_full, vc_verify_workspace_bytes, vc_verify_split_tokens,
     vc_head_mean, vc_logits_argmax, vc_logits_workspace_bytes, vc_accept, vc_stage_full_kv, vc_hadamard_rows,
-    vc_stage_full_kv_d2h, vc_last_error, workspace,
+    vc_stage_full_kv_d2h, vc_last_error, workspace, FileStager, VC_ERR_IO,
     vc_gemm_bf16, vc_gemm_bf16_wide, vc_rmsnorm, vc_rope_qkv, vc_swiglu, vc_embed, vc_heads_to_rows, vc_argmax_rows, vc_copy_kv_rows,
 )

@@ -7,11 +7,11 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvc.so")
 
-VC_OK, VC_ERR_INVALID_ARG, VC_ERR_UNSUPPORTED, VC_ERR_WORKSPACE, VC_ERR_HIP = range(5)
+VC_OK, VC_ERR_INVALID_ARG, VC_ERR_UNSUPPORTED, VC_ERR_WORKSPACE, VC_ERR_HIP, VC_ERR_IO = range(6)
 VC_F32, VC_BF16 = 0, 1
 VC_QUANT_KIVI, VC_DROP_TOPK = 1, 2
 
-_STATUS = {1: "VC_ERR_INVALID_ARG", 2: "VC_ERR_UNSUPPORTED", 3: "VC_ERR_WORKSPACE", 4: "VC_ERR_HIP"}
+_STATUS = {1: "VC_ERR_INVALID_ARG", 2: "VC_ERR_UNSUPPORTED", 3: "VC_ERR_WORKSPACE", 4: "VC_ERR_HIP", 5: "VC_ERR_IO"}
 
 
 class VcError(RuntimeError):
@@ -63,6 +63,11 @@ _DECLS = {
                                  c_p, c_p]),
     "vc_stage_full_kv_d2h": (c_i32, [c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i64, c_i64, c_i64, c_i64,
                                      c_p, c_p]),
+    "vc_file_stager_create": (c_i32, [c_i32, c_sz, c_i32, ctypes.c_double, ctypes.POINTER(c_p)]),
+    "vc_file_stager_destroy": (c_i32, [c_p]),
+    "vc_stage_full_kv_file": (c_i32, [c_p, c_i32, c_i64, c_i64, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i64, c_i64,
+                                      c_i64, c_i64, c_p, c_p, ctypes.POINTER(c_i64)]),
+    "vc_file_stager_wait": (c_i32, [c_p, c_i64]),
     "vc_last_error": (ctypes.c_char_p, []),
     # vc_model.h
     "vc_gemm_bf16": (c_i32, [c_p, c_i64, c_p, c_i64, c_i64, c_i32, c_i32, c_p, c_i64, c_i32, c_p, c_p]),
@@ -331,6 +336,48 @@ def vc_stage_full_kv_d2h(dev_k, dev_v, host_k, host_v, tok_begin, tok_end, *, co
                                     host_k.element_size(), host_rows, dev_k.shape[2], tok_begin, tok_end,
                                     _stream(copy_stream), None if done is None else done.cuda_event),
            "vc_stage_full_kv_d2h")
+
+
+class FileStager:
+    """vc_file_stager: reader threads and pinned bounce buffers that stage full-KV rows
+    from a file (the remote prefix cache stand-in) to the device."""
+
+    def __init__(self, n_threads=8, chunk_bytes=4 << 20, n_buffers=32, max_bytes_per_s=0.0):
+        h = c_p()
+        _check(lib.vc_file_stager_create(n_threads, chunk_bytes, n_buffers, float(max_bytes_per_s),
+                                         ctypes.byref(h)), "vc_file_stager_create")
+        self.handle = h.value
+
+    def stage(self, fd, k_offset, v_offset, dev_k, dev_v, file_rows, tok_begin, tok_end, *, copy_stream=None,
+              done=None):
+        """Rows [tok_begin, tok_end) of the [B, Hkv, file_rows, d] K and V stored at the two
+        byte offsets of fd -> the same rows of dev_k, dev_v.  Returns the ticket."""
+        B, Hkv, dev_rows, d = dev_k.shape
+        assert dev_v.shape == dev_k.shape and dev_k.is_contiguous() and dev_v.is_contiguous()
+        _ensure_event(done, copy_stream)
+        t = c_i64()
+        _check(lib.vc_stage_full_kv_file(self.handle, fd, k_offset, v_offset, _ptr(dev_k), _ptr(dev_v), B, Hkv, d,
+                                         dev_k.element_size(), file_rows, dev_rows, tok_begin, tok_end,
+                                         _stream(copy_stream), None if done is None else done.cuda_event,
+                                         ctypes.byref(t)), "vc_stage_full_kv_file")
+        return t.value
+
+    def wait(self, ticket):
+        _check(lib.vc_file_stager_wait(self.handle, ticket), "vc_file_stager_wait")
+
+    def close(self):
+        if self.handle:
+            _check(lib.vc_file_stager_destroy(self.handle), "vc_file_stager_destroy")
+            self.handle = None
+
+    def __del__(self):
+        import sys
+        if sys.is_finalizing():   # the HIP runtime may already be gone: leave it to the OS
+            return
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 # ---------------------------------------------------------------- vc_model.h

@@ -175,6 +175,82 @@ class HostFullKV:
             self._stage(l + self.slots)
 
 
+class FileFullKV(HostFullKV):
+    """The remote-prefix-cache setting (summary page, "What the paper found" and
+    "Original abstract"): the full KV of the prompt (rows [0, prefix_rows)) lives in a
+    store off the host's pinned memory -- a file here, read by the library's stager
+    threads, optionally capped at a link rate -- and is staged from there every
+    round; rows written after the prompt (the generated tokens) stay in pinned host
+    memory as in HostFullKV.  The file holds, per layer, K then V, each
+    [B, Hkv, prefix_rows, hd] bf16; it is unlinked at creation and lives as long as
+    its descriptor.  The prompt rows of the pinned copy are cleared, so every prompt
+    row a verify pass reads has come through the file."""
+
+    def __init__(self, src: FullCache, slots: int, prefix_rows: int, device="cuda", directory=None,
+                 n_threads=8, chunk_bytes=4 << 20, n_buffers=32, max_bytes_per_s=0.0):
+        import os
+        import tempfile
+        super().__init__(src, slots, device)
+        P = int(prefix_rows)
+        assert 0 < P <= src.rows
+        self.P = P
+        if directory is None:
+            directory = tempfile.gettempdir()
+        fd, path = tempfile.mkstemp(prefix="vc_prefix_", dir=directory)
+        os.unlink(path)
+        self.fd = fd
+        self.layer_bytes = 2 * src.k[0][:, :, :P].numel() * 2
+        with os.fdopen(os.dup(fd), "wb") as f:   # the prefix store, written once by the prefill
+            for l in range(self.layers):
+                for t in (self.host_k[l], self.host_v[l]):
+                    f.write(t[:, :, :P].contiguous().view(torch.int16).numpy().tobytes())
+                    t[:, :, :P].zero_()
+        self.stager = L.FileStager(n_threads, chunk_bytes, n_buffers, max_bytes_per_s)
+        self.file_done = [torch.cuda.Event() for _ in range(self.layers)]
+        self.tickets = [None] * self.layers
+        self.bytes_from_file = 0
+
+    def _stage(self, l):
+        j = l % self.slots
+        P, n = self.P, self.n_rows
+        off = l * self.layer_bytes
+        self.tickets[l] = self.stager.stage(self.fd, off, off + self.layer_bytes // 2, self.slot_k[j], self.slot_v[j],
+                                            P, 0, min(P, n), copy_stream=self.stream, done=self.file_done[l])
+        self.bytes_from_file += 2 * self.slot_k[j][:, :, : min(P, n)].numel() * 2
+        L.vc_stage_full_kv(self.host_k[l], self.host_v[l], self.slot_k[j], self.slot_v[j], min(P, n), max(P, n),
+                           copy_stream=self.stream, done=self.staged[l])
+        self.bytes_staged += 2 * self.host_k[l][:, :, : n].numel() * 2
+
+    def acquire(self, l):
+        self.stager.wait(self.tickets[l])
+        self.tickets[l] = None
+        torch.cuda.current_stream().wait_event(self.file_done[l])
+        return super().acquire(l)
+
+    def release(self, l):
+        assert self.lo >= self.P, "rows of the prompt are never rewritten"
+        super().release(l)
+
+    def close(self):
+        import os
+        for t in self.tickets:
+            if t is not None:
+                self.stager.wait(t)
+        self.tickets = [None] * self.layers
+        self.stager.close()
+        if self.fd is not None:
+            os.close(self.fd)
+            self.fd = None
+
+    def __del__(self):
+        import sys
+        if not sys.is_finalizing() and getattr(self, "fd", None) is not None:
+            try:
+                self.close()
+            except Exception:
+                pass
+
+
 def attend_full(dec: DecoderGPU, cache, B, k, pos, row0, ctx_len, ctx_lens, split_tokens, ws, after=None):
     """Attention callback over a full cache (FullCache or HostFullKV): rotary + scatter
     of the rows' keys/values into the cache at rows row0[b] + i, then causal verify
@@ -362,7 +438,10 @@ class VeriCacheLoop:
     bounds (capacity and tail capacity) while the kernels read the per-sequence
     lengths."""
 
-    def __init__(self, sess: Session, slots=2, graph=True, horizons=None):
+    def __init__(self, sess: Session, slots=2, graph=True, horizons=None, prefix_store=None):
+        """prefix_store: None, or the keyword arguments of FileFullKV (without src,
+        slots, prefix_rows) to stage the prompt's full KV from a file instead of
+        pinned host memory (needs slots)."""
         self.sess = sess
         # draft horizons: the session's k alone, or several (each at most k), one chosen
         # per round by HorizonPolicy; buffers are sized for k
@@ -375,7 +454,11 @@ class VeriCacheLoop:
         kb, vb = sess.bits
         N0 = sess.N0
         res = sess.cache.clone()
-        self.full = res if slots is None else HostFullKV(res, slots, dev)
+        if prefix_store is not None:
+            assert slots is not None, "the prefix store is staged through device slots"
+            self.full = FileFullKV(res, slots, N0, dev, **prefix_store)
+        else:
+            self.full = res if slots is None else HostFullKV(res, slots, dev)
         # compressed caches: whole groups of the prompt + the rest in the tail
         cap = _round_up(N0 + sess.gen + 2 * k + G, max(32, G))
         self.tail_cap = G + 2 * k

@@ -116,3 +116,17 @@ def test_hadamard_rejects_unsupported_widths():
     assert L.vc_hadamard_rows(y, stream=0).shape == (0, 128)    # no rows: nothing launched
     z = torch.zeros(4 * 128 + 2, dtype=torch.bfloat16)[2:].view(4, 128)   # 4-byte offset
     assert "aligned" in _bad(L.vc_hadamard_rows, z, stream=0)
+
+
+def test_file_stager_rejects_bad_arguments():
+    """Checked before any HIP call: bad sizes, a NULL stager, a bad descriptor."""
+    h = ctypes.c_void_p()
+    lib = L._lib.lib
+    for args in [(0, 1 << 20, 4, 0.0), (4, 1 << 20, 2, 0.0), (2, 100, 4, 0.0), (2, 1 << 20, 4, -1.0)]:
+        assert lib.vc_file_stager_create(*args, ctypes.byref(h)) == L._lib.VC_ERR_INVALID_ARG
+        assert h.value is None and L.vc_last_error() != ""
+    t = ctypes.c_int64()
+    assert lib.vc_stage_full_kv_file(None, 3, 0, 0, 1, 1, 1, 1, 64, 2, 10, 10, 0, 10, None, None,
+                                     ctypes.byref(t)) == L._lib.VC_ERR_INVALID_ARG
+    assert lib.vc_file_stager_wait(None, 1) == L._lib.VC_ERR_INVALID_ARG
+    assert lib.vc_file_stager_destroy(None) == L._lib.VC_OK

@@ -375,6 +375,25 @@ def test_adaptive_horizon_equals_greedy(graph):
     say(f"rounds {loop.rounds}, horizons chosen {loop.policy.chosen}")
 
 
+@pytest.mark.parametrize("rate", [0.0, 2e9])
+def test_prefix_from_file_equals_greedy(tmp_path, rate):
+    """The remote-prefix-cache setting: the prompt's full KV is staged every round from
+    a file by the library's stager threads (uncapped, and capped at 2 GB/s), the
+    generated rows from pinned host memory; the output still equals greedy, and every
+    prompt row came through the file (the pinned copy of those rows is cleared)."""
+    w = SMALL
+    _, _, _, dec, sess = _setup(w, std=0.08, chunk=128)
+    ref = R.Greedy(sess).run()
+    loop = R.VeriCacheLoop(sess, slots=1, prefix_store=dict(directory=str(tmp_path), n_threads=3,
+                                                            chunk_bytes=1 << 14, n_buffers=6, max_bytes_per_s=rate))
+    assert all(float(t[:, :, : w.N].abs().max()) == 0 for t in loop.full.host_k)
+    got = loop.run()
+    assert np.array_equal(got, ref)
+    assert loop.full.bytes_from_file > 0
+    loop.full.close()
+    say(f"rounds {loop.rounds}, {loop.full.bytes_from_file / 2 ** 20:.1f} MiB from the file")
+
+
 def test_graph_draft_loop_matches_eager():
     """The captured draft loop produces the same drafts as the step-by-step launches
     (std 0.02 model: drafts are mostly accepted, so several rounds and group
