@@ -327,6 +327,8 @@ def e2e_rounds(ctx, gen, slots):
         torch.cuda.synchronize()
         return out, time.perf_counter() - t
 
+    note = lambda m: print(f"[bench] e2e: {m}", file=sys.stderr, flush=True)
+    note(f"prefill done in {prefill_s:.1f}s; greedy baselines")
     g = R.Greedy(sess)
     g.run(4)                                                    # warm-up
     g = R.Greedy(sess)
@@ -336,6 +338,7 @@ def e2e_rounds(ctx, gen, slots):
     gs.run(2)
     _, t_st = timed(lambda: gs.run(2 + n_staged))
     del gs
+    note("draft-and-verify")
     warm = R.VeriCacheLoop(sess, slots=slots)
     warm.round()
     del warm
@@ -343,6 +346,7 @@ def e2e_rounds(ctx, gen, slots):
     got, t_vc = timed(lambda: loop.run(timed=True))
     ok = bool(np.array_equal(got, ref))
     # the same batch with the draft horizon chosen per round by the cost model
+    note("adaptive horizon")
     horizons = tuple(h for h in (4, 8, 16, 32) if h <= w.k)
     ada = R.VeriCacheLoop(sess, slots=slots, horizons=horizons)
     got_a, t_ada = timed(lambda: ada.run())
@@ -352,7 +356,9 @@ def e2e_rounds(ctx, gen, slots):
                                               for k, v in ada.policy.times.items() if v},
                 "output_equals_greedy": bool(np.array_equal(got_a, ref))}
     del ada
+    note("prefix staged from a file")
     remote = remote_prefix_rounds(w, sess, ref, slots, gen, timed)
+    note("staggered batches")
     stag = staggered_rounds(w, shape, weights, sess, ref, slots, gen, chunk, timed)
     committed = w.B * (gen - 1)                                 # tokens produced after the prefill's first
     staged_bytes = loop.full.bytes_staged if hasattr(loop.full, "bytes_staged") else 0
