@@ -24,4 +24,4 @@ so that codes can be compared bit for bit.
 
 Parity status of each function is stated in its module header.
 """
-from . import quant, attention, drop, accept, logits, rotate  # noqa: F401
+from . import quant, attention, drop, accept, logits, rotate, split  # noqa: F401
