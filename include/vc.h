@@ -289,6 +289,32 @@ vc_status vc_stage_full_kv_d2h(const void* dev_k, const void* dev_v, void* host_
                                void* done);
 
 /* ---------------------------------------------------------------------------
+ * Split-stream form of a quantized cache (thelatestinai.com listing page for
+ * 2604.15409, the Lynx abstract: an anchor stream of the most significant bits, a
+ * residual stream of the rest; decoding may start on the anchor).  The anchor is an
+ * ordinary VC_QUANT_KIVI cache that vc_decode_attn_compressed reads as it is.
+ *
+ * full, anchor: VC_QUANT_KIVI descriptors with equal B, Hkv, d (a multiple of 32),
+ *   capacity, group and param_dtype; full K/V bits b in {2, 3, 4, 8}, anchor bits a
+ *   in {2, 3, 4} with a <= b (per tensor), r = b - a.
+ * k_resid, v_resid: uint32 [B, Hkv, capacity, d * r / 32], codes packed like every
+ *   other code row (NULL allowed where r = 0).
+ * vc_split_planes: for rows [0, n_tokens) (a multiple of group) of every (sequence,
+ *   kv-head): anchor code = c >> r, residual code = c & (2^r - 1); anchor scale =
+ *   s * 2^r, anchor zero = z + s * (2^r - 1) / 2 (float32 product, then sum, then
+ *   rounding to param_dtype), i.e. each anchor level is the midpoint of the full
+ *   levels it covers.  The anchor must not share arrays with the full cache.  The
+ *   full cache's own parameters are the residual stream's.
+ * vc_join_planes: full code = (anchor code << r) | residual code for the same rows
+ *   (codes only; the full cache keeps its parameters).  Restores the split codes
+ *   exactly.
+ * ------------------------------------------------------------------------- */
+vc_status vc_split_planes(const vc_ckv* full, const vc_ckv* anchor, uint32_t* k_resid, uint32_t* v_resid,
+                          int64_t n_tokens, void* stream);
+vc_status vc_join_planes(const vc_ckv* anchor, const uint32_t* k_resid, const uint32_t* v_resid,
+                         const vc_ckv* full, int64_t n_tokens, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Full-KV staging from a file: the remote-prefix-cache setting (summary page, "What
  * the paper found" and "Original abstract": the same method serves remote prefix
  * caching, where the full KV's swap-in is network-bound rather than PCIe-bound).

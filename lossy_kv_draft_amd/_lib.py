@@ -63,6 +63,8 @@ _DECLS = {
                                  c_p, c_p]),
     "vc_stage_full_kv_d2h": (c_i32, [c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i64, c_i64, c_i64, c_i64,
                                      c_p, c_p]),
+    "vc_split_planes": (c_i32, [_P, _P, c_p, c_p, c_i64, c_p]),
+    "vc_join_planes": (c_i32, [_P, c_p, c_p, _P, c_i64, c_p]),
     "vc_file_stager_create": (c_i32, [c_i32, c_sz, c_i32, ctypes.c_double, ctypes.POINTER(c_p)]),
     "vc_file_stager_destroy": (c_i32, [c_p]),
     "vc_stage_full_kv_file": (c_i32, [c_p, c_i32, c_i64, c_i64, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i64, c_i64,
@@ -336,6 +338,28 @@ def vc_stage_full_kv_d2h(dev_k, dev_v, host_k, host_v, tok_begin, tok_end, *, co
                                     host_k.element_size(), host_rows, dev_k.shape[2], tok_begin, tok_end,
                                     _stream(copy_stream), None if done is None else done.cuda_event),
            "vc_stage_full_kv_d2h")
+
+
+def split_residuals(full: "Ckv", anchor: "Ckv"):
+    """Zeroed residual arrays (k_resid, v_resid) for splitting `full` into `anchor`
+    (None where the widths are equal)."""
+    def one(b, a):
+        r = b - a
+        if r <= 0:
+            return None
+        return torch.zeros(full.B, full.Hkv, full.capacity, full.d * r // 32, dtype=torch.int32,
+                           device=full.k_codes.device)
+    return one(full.k_bits, anchor.k_bits), one(full.v_bits, anchor.v_bits)
+
+
+def vc_split_planes(full: "Ckv", anchor: "Ckv", k_resid, v_resid, n_tokens, *, stream=None):
+    _check(lib.vc_split_planes(ctypes.byref(full.struct()), ctypes.byref(anchor.struct()), _ptr(k_resid),
+                               _ptr(v_resid), n_tokens, _stream(stream)), "vc_split_planes")
+
+
+def vc_join_planes(anchor: "Ckv", k_resid, v_resid, full: "Ckv", n_tokens, *, stream=None):
+    _check(lib.vc_join_planes(ctypes.byref(anchor.struct()), _ptr(k_resid), _ptr(v_resid),
+                              ctypes.byref(full.struct()), n_tokens, _stream(stream)), "vc_join_planes")
 
 
 class FileStager:

@@ -130,3 +130,17 @@ def test_file_stager_rejects_bad_arguments():
                                      ctypes.byref(t)) == L._lib.VC_ERR_INVALID_ARG
     assert lib.vc_file_stager_wait(None, 1) == L._lib.VC_ERR_INVALID_ARG
     assert lib.vc_file_stager_destroy(None) == L._lib.VC_OK
+
+
+def test_split_planes_rejects_bad_arguments():
+    full = _ckv(k_bits=4, v_bits=4)
+    anchor = _ckv(k_bits=2, v_bits=2)
+    r = torch.zeros(1, 2, 512, 4, dtype=torch.int32)
+    assert "exceed" in _bad(L.vc_split_planes, anchor, full, r, r, 64, stream=0)       # anchor wider than full
+    _bad(L.vc_split_planes, full, anchor, r, r, 48, stream=0)                          # not a whole group
+    _bad(L.vc_split_planes, full, anchor, None, r, 64, stream=0)                       # residual missing
+    _bad(L.vc_split_planes, full, full, r, r, 64, stream=0)                            # shares arrays
+    wide = _ckv(k_bits=16, v_bits=4)
+    _bad(L.vc_split_planes, wide, anchor, r, r, 64, stream=0, status=L._lib.VC_ERR_UNSUPPORTED)
+    other = _ckv(k_bits=2, v_bits=2, group=64)
+    _bad(L.vc_join_planes, other, r, r, full, 64, stream=0)                            # group differs
