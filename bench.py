@@ -251,6 +251,48 @@ def measure_rotation(st):
                                                                                    HBM_PEAK_GBS, 4)}
 
 
+def measure_split_stream(st, anchor_bits=2):
+    """The split-stream compressor on the layer's compressed cache: vc_split_planes
+    (anchor of the top `anchor_bits` bits plus residual), and the draft decode over the
+    anchor alone against the decode over the full-width cache (same query, same
+    tail)."""
+    import torch
+    import lossy_kv_draft_amd as L
+    w = st["w"]
+    full = st["ckvs"][0]
+    if w.method != "quant" or min(full.k_bits, full.v_bits) <= anchor_bits:
+        return None
+    anchor = L.Ckv("quant", w.B, w.Hkv, w.d, w.N, k_bits=anchor_bits, v_bits=anchor_bits, group=w.group,
+                   param_dtype=w.scale_dtype, kv_dtype=w.dtype, tail_cap=w.k)
+    anchor.tail_k, anchor.tail_v = full.tail_k, full.tail_v
+    anchor.n_main = full.n_main
+    kr, vr = L.split_residuals(full, anchor)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    split_us = timed(lambda: L.vc_split_planes(full, anchor, kr, vr, w.N), 5)
+    full.tail_len = anchor.tail_len = w.k
+    q, out = st["qrows"][w.k - 1], st["dec_out"][w.k - 1]
+    full_us = timed(lambda: L.vc_decode_attn_compressed(full, q, out, ws=st["dec_ws"]), 20)
+    anchor_us = timed(lambda: L.vc_decode_attn_compressed(anchor, q, out, ws=st["dec_ws"]), 20)
+    moved = full.stored_bytes(w.N) + anchor.stored_bytes(w.N) + sum(t.numel() * 4 for t in (kr, vr) if t is not None)
+    anchor_bytes = decode_bytes(w.with_(k_bits=anchor_bits, v_bits=anchor_bits), w.N, w.k)
+    return {"anchor_bits": anchor_bits, "split_us": round(split_us, 2),
+            "split_GBps": round(moved / (split_us * 1e-6) / 1e9, 1),
+            "decode_full_us": round(full_us, 2), "decode_anchor_us": round(anchor_us, 2),
+            "decode_anchor_GBps": round(anchor_bytes / (anchor_us * 1e-6) / 1e9, 1),
+            "anchor_speedup": round(full_us / anchor_us, 3)}
+
+
 def measure_stage(st):
     """Full-KV swap-in: H2D copy of the whole context of one layer from pinned host
     memory on a side stream, alone and overlapped with the k draft decodes."""
@@ -610,6 +652,7 @@ def main():
                      "bytes_per_launch": int(per_launch), "avg_launch_us": round(dec_avg_ms * 1e3, 3)},
     }
     line["rotation_prepass"] = measure_rotation(st)
+    line["split_stream"] = measure_split_stream(st)
     if not a.no_stage:
         line["stage_full_kv"] = measure_stage(st)
     if not a.no_e2e:
