@@ -2,6 +2,7 @@
 import copy
 import ctypes
 import os
+import sys
 
 import torch
 
@@ -366,7 +367,7 @@ class FileStager:
     """vc_file_stager: reader threads and pinned bounce buffers that stage full-KV rows
     from a file (the remote prefix cache stand-in) to the device."""
 
-    def __init__(self, n_threads=8, chunk_bytes=4 << 20, n_buffers=32, max_bytes_per_s=0.0):
+    def __init__(self, n_threads=8, chunk_bytes=16 << 20, n_buffers=16, max_bytes_per_s=0.0):
         h = c_p()
         _check(lib.vc_file_stager_create(n_threads, chunk_bytes, n_buffers, float(max_bytes_per_s),
                                          ctypes.byref(h)), "vc_file_stager_create")
@@ -394,9 +395,8 @@ class FileStager:
             _check(lib.vc_file_stager_destroy(self.handle), "vc_file_stager_destroy")
             self.handle = None
 
-    def __del__(self):
-        import sys
-        if sys.is_finalizing():   # the HIP runtime may already be gone: leave it to the OS
+    def __del__(self, _finalizing=sys.is_finalizing):
+        if _finalizing():   # the HIP runtime may already be gone: leave it to the OS
             return
         try:
             self.close()

@@ -17,6 +17,7 @@ The round follows "VeriCache: Turning Lossy KV Cache into Lossless LLM Inference
 Greedy full-KV decoding with the same kernels is the reference the output must equal.
 """
 from dataclasses import dataclass
+import sys
 import time
 import numpy as np
 import torch
@@ -187,7 +188,7 @@ class FileFullKV(HostFullKV):
     row a verify pass reads has come through the file."""
 
     def __init__(self, src: FullCache, slots: int, prefix_rows: int, device="cuda", directory=None,
-                 n_threads=8, chunk_bytes=4 << 20, n_buffers=32, max_bytes_per_s=0.0):
+                 n_threads=8, chunk_bytes=16 << 20, n_buffers=16, max_bytes_per_s=0.0):
         import os
         import tempfile
         super().__init__(src, slots, device)
@@ -242,9 +243,8 @@ class FileFullKV(HostFullKV):
             os.close(self.fd)
             self.fd = None
 
-    def __del__(self):
-        import sys
-        if not sys.is_finalizing() and getattr(self, "fd", None) is not None:
+    def __del__(self, _finalizing=sys.is_finalizing):
+        if not _finalizing() and getattr(self, "fd", None) is not None:
             try:
                 self.close()
             except Exception:
