@@ -205,7 +205,8 @@ size_t vc_decode_workspace_bytes(const vc_ckv* ckv, int32_t Hq);
  *
  * vc_verify_workspace_bytes: workspace for calls with contexts up to max_len and
  * this k and split_tokens (0: the default for a cache of max_len + k rows, which
- * also covers the default of any larger cache).
+ * also covers the default of any larger cache).  ws must be 16-byte aligned
+ * (VC_ERR_INVALID_ARG otherwise).
  * vc_verify_split_tokens: the default split, a multiple of 64 chosen so that a
  * cache of cache_rows rows is cut into at most as many splits per (sequence,
  * kv-head) as workgroups of the verification kernel fit on the current device

@@ -261,35 +261,54 @@ __global__ void __launch_bounds__(kVerThreads) verify_mfma_kernel(VerifyArgs a) 
 }
 
 // ---------------------------------------------------------------- bf16, d = 128
-// Tiles of kVtTile positions of K and V are copied global -> LDS by all waves of the
-// workgroup (16 bytes per lane per instruction) into a ring of kVtStages tiles: while
-// tile j is
-// computed, the copies of the next kVtStages - 1 tiles are in flight.  One barrier per
-// tile: after it, tile j has landed for every wave and every wave is done with tile
-// j - 1, whose stage then receives tile j + kVtStages - 1.  16-byte chunks of a row
-// are XOR-swizzled by the row so that the matrix-core operand reads spread over the
-// banks.  K feeds S^T = K Q^T as the A operand (16-byte reads).  V stays position-
-// major: the A operand of O^T += V^T P^T (channels x positions) is read with the
-// transposing LDS load ds_read_b64_tr_b16, which within each 16-lane group returns
-// to lane j the element j & 3 of the four values addressed by lane 4e + (j >> 2) as
-// element e; so lane (4e + i) addresses position e and channels 4i .. 4i + 3.
+// Tiles of kVtTile positions of K and V are copied global -> LDS by all W waves of
+// the workgroup (16 bytes per lane per instruction, buffer loads through descriptors
+// that end at the last readable row, so rows past it arrive as zeros and every wave's
+// offsets are loop invariant) into a ring of S tiles: while tile j is computed, the
+// copies of the next S - 1 tiles are in flight.  One barrier per tile: after it,
+// tile j has landed for every wave and every wave is done with tile j - 1, whose
+// stage then receives tile j + S - 1.  16-byte chunks of a row are XOR-swizzled by
+// the row so that the matrix-core operand reads spread over the banks.  K feeds
+// S^T = K Q^T as the A operand (16-byte reads).  V stays position-major: the A
+// operand of O^T += V^T P^T (channels x positions) is read with the transposing LDS
+// load ds_read_b64_tr_b16, which within each 16-lane group returns to lane j the
+// element j & 3 of the four values addressed by lane 4e + (j >> 2) as element e; so
+// lane (4e + i) addresses position e and channels 4i .. 4i + 3.
 // Softmax per row: masking only on tiles that reach past a row's limit; the running
-// maximum and the rescale of the row's accumulators only when a tile raises it (a
-// decision of the row alone, so batch invariance holds; the row's largest
-// probability is exactly 1); exp2 of an fma; bf16 P; the row sums come from one more
-// product with an all-ones A operand.
+// maximum moves, and the row's accumulators are rescaled, only when a tile's maximum
+// exceeds it by more than 8 (base 2), so probabilities stay below 2^8 and the rescale
+// is rare (a decision of the row alone, so batch invariance holds); exp2 of an fma;
+// bf16 P; the row sums come from one more product with an all-ones A operand.
 constexpr int kVtTile = 64;                       // positions per tile
-constexpr int kVtStages = 2;                      // tiles held in the LDS ring
 constexpr int kVtRow = 256;                       // bytes per position row
 constexpr int kVtPrefetch = 4;                    // K or V fragments read ahead of their product
 constexpr int kVtTileBytes = kVtTile * kVtRow;    // one K or V tile
-static_assert(kVtTile % 32 == 0 && kVtStages >= 2, "tile shape");
+static_assert(kVtTile % 32 == 0, "tile shape");
 typedef unsigned char VtStage[2 * kVtTileBytes];  // K tile, then V tile
 typedef short s4_t __attribute__((ext_vector_type(4)));
 typedef float f2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int vt_chunk(int r, int c) { return c ^ (r & 15); }
+
+// Buffer descriptor over `bytes` bytes from `base` (raw, stride 0): 16-byte loads at
+// offsets at or past `bytes` return zeros.  Every field is made wave-uniform.
+typedef int32_t vt_rsrc_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ vt_rsrc_t vt_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  vt_rsrc_t r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(p));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((p >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(bytes));
+  r.w = 0x00020000;
+  return r;
+}
+// Buffer -> LDS copy of 16 bytes per active lane at (lds + 16 * lane), from byte
+// offset voff of the descriptor's range (inline assembly for the reason given at
+// lds_copy16).
+__device__ __forceinline__ void lds_copy16_buf(vt_rsrc_t r, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "s"(lds) : "memory", "m0");
+}
 
 __device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
   typedef __attribute__((address_space(3))) s4_t lds_s4;
@@ -323,11 +342,13 @@ __device__ __forceinline__ void vt_wait(int ahead) {
   }
 }
 
-// RT 16-row tiles per wave, 4 waves per workgroup (64 RT rows per workgroup).
-template <int RT>
+// RT 16-row tiles per wave, W waves per workgroup (16 RT W rows per workgroup), a
+// ring of S tiles.
+template <int RT, int W, int S>
 __device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int rblk, int bh, VtStage* ring) {
   constexpr int D = 128, KS = D / 32, DT = D / 16;
-  constexpr int kWaveRows = kVtTile / 4;   // rows each wave copies per tile
+  static_assert(S >= 2 && kVtTile % W == 0, "ring shape");
+  constexpr int kWaveRows = kVtTile / W;   // rows each wave copies per tile
   constexpr int kCopies = kWaveRows / 4;   // instructions per wave per tile, K and V each
   static_assert(kWaveRows % 4 == 0, "copy shape");
   constexpr int NT = kVtTile / 16;  // 16-position score tiles per tile
@@ -375,27 +396,33 @@ __device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int
   // tiles, 4 rows per instruction (lane l: row base + l / 16, LDS chunk l % 16)
   const unsigned char* kbase = static_cast<const unsigned char*>(a.kc) + static_cast<size_t>(bh) * a.cache_rows * kVtRow;
   const unsigned char* vbase = static_cast<const unsigned char*>(a.vc) + static_cast<size_t>(bh) * a.cache_rows * kVtRow;
+  uint32_t voff[kCopies];  // byte offset within a tile of this lane's chunk (the global chunk at LDS chunk lane % 16)
+#pragma unroll
+  for (int i = 0; i < kCopies; ++i) {
+    const int r = kWaveRows * wave + 4 * i + (lane >> 4);
+    voff[i] = r * kVtRow + vt_chunk(r, lane & 15) * 16;
+  }
   auto issue = [&](int j) {
     const int64_t t0 = s_begin + static_cast<int64_t>(j) * kVtTile;
-    unsigned char* st = ring[j % kVtStages];
+    // descriptors over the tile's readable rows: rows at or past the end read as zeros
+    const uint32_t nb = static_cast<uint32_t>(min(limit - t0, static_cast<int64_t>(kVtTile))) * kVtRow;
+    const vt_rsrc_t kr = vt_rsrc(kbase + t0 * kVtRow, nb);
+    const vt_rsrc_t vr = vt_rsrc(vbase + t0 * kVtRow, nb);
+    unsigned char* st = ring[j % S];
 #pragma unroll
     for (int i = 0; i < kCopies; ++i) {
-      const int rw = kWaveRows * wave + 4 * i;
-      const int r = rw + (lane >> 4);
-      const int c = vt_chunk(r, lane & 15);          // the global chunk that lives at LDS chunk lane % 16
-      const int64_t pos = min(t0 + r, limit - 1);   // rows past the end repeat the last readable row
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(st + rw * kVtRow));
-      lds_copy16(kbase + pos * kVtRow + c * 16, dst);
-      lds_copy16(vbase + pos * kVtRow + c * 16, dst + kVtTileBytes);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(st + (kWaveRows * wave + 4 * i) * kVtRow));
+      lds_copy16_buf(kr, voff[i], dst);
+      lds_copy16_buf(vr, voff[i], dst + kVtTileBytes);
     }
   };
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the query loads complete before the copies start
-  for (int t = 0; t < kVtStages - 1 && t < ntile; ++t) issue(t);
+  for (int t = 0; t < S - 1 && t < ntile; ++t) issue(t);
   for (int j = 0; j < ntile; ++j) {
-    vt_wait<2 * kCopies, kVtStages - 2>(ntile - 1 - j);  // this wave's copies of tile j have landed
+    vt_wait<2 * kCopies, S - 2>(ntile - 1 - j);  // this wave's copies of tile j have landed
     __syncthreads();  // ... and every wave's; every wave is done with tile j - 1
-    if (j + kVtStages - 1 < ntile) issue(j + kVtStages - 1);  // into the stage of tile j - 1
-    const unsigned char* kt = ring[j % kVtStages];
+    if (j + S - 1 < ntile) issue(j + S - 1);  // into the stage of tile j - 1
+    const unsigned char* kt = ring[j % S];
     const unsigned char* vt = kt + kVtTileBytes;
     const int64_t t0 = s_begin + static_cast<int64_t>(j) * kVtTile;
     if (row0 < M) {  // wave-uniform; padding waves only copy
@@ -461,7 +488,7 @@ __device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int
             }
         }
         const float mts = group4_max(mt) * a.qscale;
-        if (mts > m[rt]) {  // the row's own decision (all lanes of a row agree)
+        if (mts > m[rt] + 8.f) {  // the row's own decision (all lanes of a row agree)
           const float al = __builtin_amdgcn_exp2f(m[rt] - mts);  // 0 on the row's first scores
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= al;
@@ -519,13 +546,13 @@ __device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int
 // blocks of one (split, bh) share their K and V tiles, so their workgroup ids are
 // congruent mod 8 (workgroups go to the eight XCDs, each with its own L2, in id
 // order) and lie within 8 * nblk of each other.  Ids past the last (split, bh) exit.
-template <int RT>
-__global__ void __launch_bounds__(kVerThreads) verify_tile_kernel(VerifyArgs a, int nblk, int units) {
-  __shared__ __attribute__((aligned(16))) VtStage ring[kVtStages];
+template <int RT, int W, int S>
+__global__ void __launch_bounds__(64 * W) verify_tile_kernel(VerifyArgs a, int nblk, int units) {
+  __shared__ __attribute__((aligned(16))) VtStage ring[S];
   const int id = blockIdx.x;
   const int u = (id / (8 * nblk)) * 8 + (id & 7);
   if (u >= units) return;
-  verify_tiles<RT>(a, u % a.splits, (id >> 3) % nblk, u / a.splits, ring);
+  verify_tiles<RT, W, S>(a, u % a.splits, (id >> 3) % nblk, u / a.splits, ring);
 }
 
 // Draft-side decode over kept (token-dropped) bf16 rows, d = 128, at most 16 q-heads
@@ -533,13 +560,14 @@ __global__ void __launch_bounds__(kVerThreads) verify_tile_kernel(VerifyArgs a, 
 // the context length set to the kept rows minus one, so that row 0 attends to every
 // kept row; splits 0 .. S-2 cover the kept rows and write the decode partials, split
 // S-1 covers the full-precision tail rows; decode_merge_kernel combines them.
+constexpr int kDdStages = 2;  // LDS ring of decode_dense_kernel (4 waves)
 __global__ void __launch_bounds__(kVerThreads) decode_dense_kernel(VerifyArgs a, DecodeArgs d) {
-  __shared__ __attribute__((aligned(16))) VtStage ring[kVtStages];
+  __shared__ __attribute__((aligned(16))) VtStage ring[kDdStages];
   if (static_cast<int>(blockIdx.x) == d.splits - 1) {
     decode_tail_partial_d128(d, blockIdx.z, d.splits - 1, reinterpret_cast<float*>(&ring[0][0]));
     return;
   }
-  verify_tiles<1>(a, blockIdx.x, 0, blockIdx.z, ring);
+  verify_tiles<1, 4, kDdStages>(a, blockIdx.x, 0, blockIdx.z, ring);
 }
 
 // float32 path: one 64-lane wave per (row, split); lanes cover d (d <= 256).
@@ -593,19 +621,22 @@ __global__ void __launch_bounds__(256) verify_f32_kernel(VerifyArgs a) {
   }
 }
 
-// Merge of the split partials in split order; one thread per (row, channel).
-template <typename T>
+// Merge of the split partials in split order; one thread per (row, V consecutive
+// channels).
+template <typename T, int V>
 __global__ void __launch_bounds__(256) verify_merge_kernel(VerifyArgs a, void* out, float* lse) {
+  typedef float fv_t __attribute__((ext_vector_type(V)));
   const int bh = blockIdx.y;
-  const int M = a.H * a.k, d = a.d;
+  const int M = a.H * a.k, d = a.d, dv = d / V;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (e >= static_cast<int64_t>(M) * d) return;
-  const int row = static_cast<int>(e / d), c = static_cast<int>(e % d);
+  if (e >= static_cast<int64_t>(M) * dv) return;
+  const int row = static_cast<int>(e / dv), c = static_cast<int>(e % dv) * V;
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int S = a.splits;
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + static_cast<int64_t>(bh) * S * M + row;
   const float* po = a.part_o + (static_cast<int64_t>(bh) * S * M + row) * d + c;
-  // the partials of 8 splits are loaded at once; the sums still run in split order
+  // the partials of 8 splits are loaded at once (V channels per thread); the sums
+  // still run in split order
   float Mx = -INFINITY;
   for (int s0 = 0; s0 < S; s0 += 8) {
     float mv[8];
@@ -614,26 +645,29 @@ __global__ void __launch_bounds__(256) verify_merge_kernel(VerifyArgs a, void* o
 #pragma unroll
     for (int j = 0; j < 8; ++j) Mx = fmaxf(Mx, mv[j]);
   }
-  float Lsum = 0.f, O = 0.f;
+  float Lsum = 0.f;
+  fv_t O = {};
   for (int s0 = 0; s0 < S; s0 += 8) {
     float2 p[8];
-    float ov[8];
+    fv_t ov[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int64_t sp = min(s0 + j, S - 1);
       p[j] = ml[sp * M];
-      ov[j] = po[sp * M * d];
+      ov[j] = *reinterpret_cast<const fv_t*>(po + sp * M * d);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (s0 + j >= S) break;
       const float w = p[j].x == -INFINITY ? 0.f : exp2f(p[j].x - Mx);
       Lsum = fmaf(p[j].y, w, Lsum);
-      O = fmaf(ov[j], w, O);
+#pragma unroll
+      for (int v = 0; v < V; ++v) O[v] = fmaf(ov[j][v], w, O[v]);
     }
   }
   int64_t orow = (static_cast<int64_t>(b) * a.Hq + hk * a.H) * a.k + row;
-  Elem<T>::store(static_cast<T*>(out), orow * d + c, Lsum > 0.f ? O / Lsum : 0.f);
+#pragma unroll
+  for (int v = 0; v < V; ++v) Elem<T>::store(static_cast<T*>(out), orow * d + c + v, Lsum > 0.f ? O[v] / Lsum : 0.f);
   if (lse && c == 0) lse[orow] = Lsum > 0.f ? (Mx + log2f(Lsum)) * kLn2 : -INFINITY;
 }
 
@@ -686,7 +720,7 @@ static int verify_resident() {
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 512;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 512;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, verify_tile_kernel<2>, kVerThreads, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, verify_tile_kernel<2, 4, 2>, 256, 0) != hipSuccess)
       return 512;
     return (per > 0 ? per : 1) * (cus > 0 ? cus : 1);
   }();
@@ -743,6 +777,7 @@ extern "C" vc_status vc_verify_attn_full(const void* q, const void* k_cache, con
     set_error("verify workspace needs %zu bytes (got %zu)", need, ws_bytes);
     return VC_ERR_WORKSPACE;
   }
+  VC_REQUIRE(reinterpret_cast<uintptr_t>(ws) % 16 == 0, "verify workspace must be 16-byte aligned");
   VerifyArgs a{};
   a.q = q;
   a.kc = k_cache;
@@ -765,21 +800,27 @@ extern "C" vc_status vc_verify_attn_full(const void* q, const void* k_cache, con
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(bh * a.splits * M * d * sizeof(float), 256));
   hipStream_t s = as_stream(stream);
   if (kv_dtype == VC_BF16 && d == 128) {
-    // 4 waves of one 16-row tile (up to 64 rows) or two (128 rows per workgroup), as
-    // many row blocks as M needs (64-row blocks for M = 160 or 320 were slower: more
-    // blocks reading the same tiles)
-    const int RT = M <= 64 ? 1 : 2;
-    const int nblk = static_cast<int>(cdiv(M, 64 * RT));
-    a.rows_per_block = 64 * RT;
+    // Row blocks: 4 waves of one 16-row tile (up to 64 rows) or two (128 rows per
+    // workgroup), two workgroups per CU with a 2-tile ring; for 128 < M <= 256 one
+    // block of 8 waves of two tiles each and a 4-tile ring (one workgroup per CU), so
+    // K and V are read once instead of twice.  Larger M: as many 128-row blocks as
+    // needed (64-row blocks for M = 320, or 256-row ones, were slower).  The arithmetic
+    // of a row does not depend on the block shape.
+    const int W = M > 128 && M <= 256 ? 8 : 4;
+    const int RT = M <= 16 * W ? 1 : 2;
+    const int nblk = static_cast<int>(cdiv(M, 16 * W * RT));
+    a.rows_per_block = 16 * W * RT;
     const int units = a.splits * static_cast<int>(bh);
     const dim3 grid(static_cast<unsigned>(cdiv(units, 8) * 8 * nblk));
-    if (RT == 1)
-      hipLaunchKernelGGL((verify_tile_kernel<1>), grid, dim3(kVerThreads), 0, s, a, nblk, units);
+    if (W == 8)
+      hipLaunchKernelGGL((verify_tile_kernel<2, 8, 4>), grid, dim3(512), 0, s, a, nblk, units);
+    else if (RT == 1)
+      hipLaunchKernelGGL((verify_tile_kernel<1, 4, 2>), grid, dim3(256), 0, s, a, nblk, units);
     else
-      hipLaunchKernelGGL((verify_tile_kernel<2>), grid, dim3(kVerThreads), 0, s, a, nblk, units);
+      hipLaunchKernelGGL((verify_tile_kernel<2, 4, 2>), grid, dim3(256), 0, s, a, nblk, units);
     VC_LAUNCHED("verify_tile_kernel");
-    dim3 mgrid(static_cast<unsigned>(cdiv(static_cast<int64_t>(M) * d, 256)), static_cast<unsigned>(bh));
-    hipLaunchKernelGGL(verify_merge_kernel<bf16_t>, mgrid, dim3(256), 0, s, a, out, lse);
+    dim3 mgrid(static_cast<unsigned>(cdiv(static_cast<int64_t>(M) * d / 4, 256)), static_cast<unsigned>(bh));
+    hipLaunchKernelGGL((verify_merge_kernel<bf16_t, 4>), mgrid, dim3(256), 0, s, a, out, lse);
   } else if (kv_dtype == VC_BF16) {
     int RT, nblk;
     verify_tiling(M, RT, nblk);
@@ -800,14 +841,19 @@ extern "C" vc_status vc_verify_attn_full(const void* q, const void* k_cache, con
     }
 #undef VC_VER_LAUNCH
     VC_LAUNCHED("verify_mfma_kernel");
-    dim3 mgrid(static_cast<unsigned>(cdiv(static_cast<int64_t>(M) * d, 256)), static_cast<unsigned>(bh));
-    hipLaunchKernelGGL(verify_merge_kernel<bf16_t>, mgrid, dim3(256), 0, s, a, out, lse);
+    dim3 mgrid(static_cast<unsigned>(cdiv(static_cast<int64_t>(M) * d / 4, 256)), static_cast<unsigned>(bh));
+    hipLaunchKernelGGL((verify_merge_kernel<bf16_t, 4>), mgrid, dim3(256), 0, s, a, out, lse);
   } else {
     dim3 grid(a.splits, static_cast<unsigned>(cdiv(M, 4)), static_cast<unsigned>(bh));
     hipLaunchKernelGGL(verify_f32_kernel<float>, grid, dim3(256), 0, s, a);
     VC_LAUNCHED("verify_f32_kernel");
-    dim3 mgrid(static_cast<unsigned>(cdiv(static_cast<int64_t>(M) * d, 256)), static_cast<unsigned>(bh));
-    hipLaunchKernelGGL(verify_merge_kernel<float>, mgrid, dim3(256), 0, s, a, out, lse);
+    if (d % 4 == 0) {
+      dim3 mgrid(static_cast<unsigned>(cdiv(static_cast<int64_t>(M) * d / 4, 256)), static_cast<unsigned>(bh));
+      hipLaunchKernelGGL((verify_merge_kernel<float, 4>), mgrid, dim3(256), 0, s, a, out, lse);
+    } else {
+      dim3 mgrid(static_cast<unsigned>(cdiv(static_cast<int64_t>(M) * d, 256)), static_cast<unsigned>(bh));
+      hipLaunchKernelGGL((verify_merge_kernel<float, 1>), mgrid, dim3(256), 0, s, a, out, lse);
+    }
   }
   VC_LAUNCHED("verify_merge_kernel");
   return VC_OK;
