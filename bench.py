@@ -11,7 +11,8 @@ Staging of the full KV from pinned host memory (PCIe) and compression are measur
 separately (they are not part of `value`).
 
 value = compressed decode-attention HBM GB/s (algorithmic bytes of the k decode
-calls / their time).  verify TFLOP/s is reported beside it, and "e2e" holds the
+calls / their time; the k calls are replayed from one HIP graph, as the end-to-end
+rounds do).  verify TFLOP/s is reported beside it, and "e2e" holds the
 accepted tokens/s of whole draft-and-verify rounds of a random-init 4-layer decoder
 after a 32k-token prompt (full KV staged from pinned host memory every round),
 beside greedy full-KV decoding with the KV resident and with it staged every step.
@@ -199,13 +200,11 @@ def setup(w, copies):
     return st
 
 
-def run_step(st, ev=None, dec_ev=None):
-    """One round.  ev: 4 events (start, after draft, after verify, after tokens);
-    dec_ev: list of (start, end) event pairs around each decode launch."""
+def draft_calls(st, dec_ev=None):
+    """The k draft decode calls of one round (step i sees i + 1 tail rows).  dec_ev:
+    list of (start, end) event pairs around each decode launch."""
     import lossy_kv_draft_amd as L
     w = st["w"]
-    if ev:
-        ev[0].record()
     for i in range(w.k):
         ckv = st["ckvs"][i % len(st["ckvs"])]
         ckv.tail_len = i + 1
@@ -214,6 +213,37 @@ def run_step(st, ev=None, dec_ev=None):
         L.vc_decode_attn_compressed(ckv, st["qrows"][i], st["dec_out"][i], ws=st["dec_ws"])
         if dec_ev:
             dec_ev[i][1].record()
+
+
+def capture_draft(st):
+    """The k draft calls captured once as a HIP graph (their arguments, tail lengths
+    included, are fixed per step), replayed in every timed round: host launch gaps
+    between the calls are gone."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        draft_calls(st)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        draft_calls(st)
+    torch.cuda.synchronize()
+    return g
+
+
+def run_step(st, ev=None, graph=None):
+    """One round.  ev: 4 events (start, after draft, after verify, after tokens);
+    graph: the captured draft calls (else they are launched one by one)."""
+    import lossy_kv_draft_amd as L
+    w = st["w"]
+    if ev:
+        ev[0].record()
+    if graph is not None:
+        graph.replay()
+    else:
+        draft_calls(st)
     if ev:
         ev[1].record()
     L.vc_verify_attn_full(st["q"], st["kc"], st["vc"], w.N, st["out_v"], ws=st["ver_ws"])
@@ -313,10 +343,7 @@ def measure_stage(st):
         L.vc_stage_full_kv(hk, hv, dk, dv, 0, w.N, copy_stream=side, done=done)
 
     def draft():
-        for i in range(w.k):
-            ckv = st["ckvs"][i % len(st["ckvs"])]
-            ckv.tail_len = i + 1
-            L.vc_decode_attn_compressed(ckv, st["qrows"][i], st["dec_out"][i], ws=st["dec_ws"])
+        draft_calls(st)
 
     res = {}
     for name, fn in (("stage_alone", lambda: (stage(), done.synchronize())),
@@ -583,26 +610,34 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     st = setup(w, a.copies)
+    graph = capture_draft(st)
     for _ in range(a.warmup):
-        run_step(st)
+        run_step(st, graph=graph)
     torch.cuda.synchronize()
 
     mk = lambda: torch.cuda.Event(enable_timing=True)
     evs = [[mk() for _ in range(4)] for _ in range(a.steps)]
-    dec = [[(mk(), mk()) for _ in range(w.k)] for _ in range(a.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(a.steps):
-        run_step(st, evs[s], dec[s])
+        run_step(st, evs[s], graph)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     state = gpu_state()  # right after the timed region
+    # each decode call on its own, launched eagerly between HIP events (the spread of
+    # single calls; the roofline takes the graph-replayed calls of the timed region)
+    dec = [[(mk(), mk()) for _ in range(w.k)] for _ in range(a.steps)]
+    for s in range(a.steps):
+        draft_calls(st, dec[s])
+    torch.cuda.synchronize()
     draft_ms = sum(e[0].elapsed_time(e[1]) for e in evs)
     verify_ms = sum(e[1].elapsed_time(e[2]) for e in evs)
     tok_ms = sum(e[2].elapsed_time(e[3]) for e in evs)
     step_ms = sum(e[0].elapsed_time(e[3]) for e in evs) / a.steps
     dec_launch_ms = [p[0].elapsed_time(p[1]) for d in dec for p in d]
-    dec_avg_ms = float(np.mean(dec_launch_ms))
+    # average duration of one decode call in the timed region: the draft phase (HIP
+    # events on the stream the graph is replayed on) over its k calls
+    dec_avg_ms = draft_ms / a.steps / w.k
 
     # algorithmic work: draft step i reads the compressed context plus i + 1 tail rows
     n_ctx = st["ckvs"][0].n_main
@@ -636,11 +671,13 @@ def main():
                                                            HBM_PEAK_GBS / 1e3), 1),
                             "frac_of_attainable": round(verify_tflops / min(BF16_PEAK_TFLOPS, vflops / verify_bytes(
                                 w, w.N) * HBM_PEAK_GBS / 1e3), 4)},
-        "decode_call_us": spread([x * 1e3 for x in dec_launch_ms]),
+        "decode_call_us": {"graph_replay_mean": round(dec_avg_ms * 1e3, 3),
+                           "eager": spread([x * 1e3 for x in dec_launch_ms])},
         "verify_call_us": spread([e[1].elapsed_time(e[2]) * 1e3 for e in evs]),
         "gpu_state": state,
         "kernel_round_accepted_tok_per_s": round(accepted / (step_ms * 1e-3), 1),
         "mean_accept_len": round(acc_len, 3),
+        "draft_replay": f"HIP graph of the {w.k} decode calls",
         "phase_ms": {"draft": round(draft_ms / a.steps, 4), "verify": round(verify_ms / a.steps, 4),
                      "tokens_accept": round(tok_ms / a.steps, 4)},
         "wall_ms_per_step": round(wall / a.steps * 1e3, 4),

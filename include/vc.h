@@ -230,7 +230,9 @@ int32_t vc_verify_split_tokens(int32_t B, int32_t Hkv, int64_t cache_rows);
  *   u float32 [B*k, d], u[b*k + i] = mean over the Hq heads.
  * vc_logits_argmax: u float32/bf16 (u_dtype) [R, Kdim], W w_dtype [V, Kdim] (one
  *   row per vocabulary entry) -> tokens int32 [R] = argmax_v (u_r . W_v), equal
- *   logits going to the lowest v.  Logits accumulate in float32.
+ *   logits going to the lowest v.  Logits accumulate in float32.  With bf16 W and
+ *   Kdim 64 or 128 (the matrix-core path) u and W must be 16-byte aligned
+ *   (VC_ERR_INVALID_ARG otherwise).
  * ------------------------------------------------------------------------- */
 vc_status vc_head_mean(const void* o, int32_t kv_dtype, int32_t B, int32_t Hq, int32_t k, int32_t d,
                        int64_t stride_b, int64_t stride_h, int64_t stride_i, float* u, void* stream);

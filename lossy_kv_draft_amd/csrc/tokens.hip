@@ -18,6 +18,8 @@
 //   float32 W or other shapes: one workgroup per row, float32 dot products.
 // vc_accept: one thread per sequence.
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace vc {
@@ -74,23 +76,32 @@ __global__ void __launch_bounds__(256) argmax_rowwise_kernel(const TU* u, const 
 }
 
 // ---- bf16 W on matrix cores
-constexpr int kLgVBlock = 128;
+// Each wave owns kLgWave consecutive vocabulary rows of W, held in registers as the A
+// operand (16 rows per tile), and sweeps all R rows of u in chunks of 16 (the B
+// operand): float32 u is split exactly into bf16 hi + lo, two products per step
+// (bf16 u: one).  The next chunk of u is loaded while the current one is
+// multiplied.  Per (row, wave slice) the largest logit and its lowest index go to
+// the partials, with no communication between waves; argmax_reduce_kernel combines
+// the slices of a row.
+constexpr int kLgWave = 64;                 // vocabulary rows per wave
+constexpr int kLgVBlock = 4 * kLgWave;      // per workgroup of 4 waves
 
 template <int KD, typename TU>
 __global__ void __launch_bounds__(256) argmax_mfma_kernel(const TU* u, const bf16_t* W, int64_t R, int V,
-                                                          float* part_v, int* part_i, int nvb) {
-  constexpr int KS = KD / 32;
-  __shared__ float wv[4][16];
-  __shared__ int wi[4][16];
-  const int vb = blockIdx.x;
+                                                          float* part_v, int* part_i, int nsl) {
+  constexpr int KS = KD / 32, VT = kLgWave / 16;
+  constexpr bool kF32 = std::is_same<TU, float>::value;
+  constexpr int UL = kF32 ? 2 : 1;  // 16-byte loads of u per lane per k-step
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, kb = lane >> 4;
-  const int v0 = vb * kLgVBlock + wave * 32;
+  const int slice = blockIdx.x * 4 + wave;
+  const int v0 = slice * kLgWave;
+  if (v0 >= V) return;  // wave-uniform; no barriers below
   union P16 { uint4 u; bf16x8_t v; };
-  bf16x8_t wa[2][KS];
+  bf16x8_t wa[VT][KS];
 #pragma unroll
-  for (int vt = 0; vt < 2; ++vt) {
-    int v = v0 + vt * 16 + l16;
+  for (int vt = 0; vt < VT; ++vt) {
+    const int v = v0 + vt * 16 + l16;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       P16 p;
@@ -99,52 +110,72 @@ __global__ void __launch_bounds__(256) argmax_mfma_kernel(const TU* u, const bf1
       wa[vt][ks] = p.v;
     }
   }
-  for (int64_t r0 = 0; r0 < R; r0 += 16) {
+  // u of row r0 + l16, channels 32 ks + 8 kb .. + 7: UL 16-byte pieces per k-step
+  auto load_u = [&](int64_t r0, uint4 (&x)[KS][UL]) {
     const int64_t r = r0 + l16;
-    f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int h = 0; h < UL; ++h) {
+        x[ks][h] = make_uint4(0, 0, 0, 0);
+        if (r < R) x[ks][h] = *reinterpret_cast<const uint4*>(u + r * KD + 32 * ks + 8 * kb + h * (8 / UL));
+      }
+  };
+  uint4 cur[KS][UL], nxt[KS][UL];
+  load_u(0, cur);
+  for (int64_t r0 = 0; r0 < R; r0 += 16) {
+    if (r0 + 16 < R) load_u(r0 + 16, nxt);
+    f32x4_t acc[VT];
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) acc[vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      bf16x8_t hi, lo;
+      if constexpr (kF32) {
+        const float* xf = reinterpret_cast<const float*>(&cur[ks][0]);
+        bf16x8_t hi, lo;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float x = r < R ? Elem<TU>::load(u, r * KD + 32 * ks + 8 * kb + j) : 0.f;
-        __bf16 h = static_cast<__bf16>(x);
-        hi[j] = h;
-        lo[j] = static_cast<__bf16>(x - static_cast<float>(h));
-      }
+        for (int j = 0; j < 8; ++j) {
+          const __bf16 h = static_cast<__bf16>(xf[j]);
+          hi[j] = h;
+          lo[j] = static_cast<__bf16>(xf[j] - static_cast<float>(h));
+        }
 #pragma unroll
-      for (int vt = 0; vt < 2; ++vt) {
-        acc[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[vt][ks], hi, acc[vt], 0, 0, 0);
-        acc[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[vt][ks], lo, acc[vt], 0, 0, 0);
+        for (int vt = 0; vt < VT; ++vt) {
+          acc[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[vt][ks], hi, acc[vt], 0, 0, 0);
+          acc[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[vt][ks], lo, acc[vt], 0, 0, 0);
+        }
+      } else {
+        P16 p;
+        p.u = cur[ks][0];
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt)
+          acc[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[vt][ks], p.v, acc[vt], 0, 0, 0);
       }
     }
-    // acc[vt][i] = logit(vocab v0 + 16 vt + 4 kb + i, row r)
+    // acc[vt][i] = logit(vocabulary v0 + 16 vt + 4 kb + i, row r0 + l16)
     float bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
-    for (int vt = 0; vt < 2; ++vt)
+    for (int vt = 0; vt < VT; ++vt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        int v = v0 + vt * 16 + 4 * kb + i;
+        const int v = v0 + vt * 16 + 4 * kb + i;
         if (v < V && better(acc[vt][i], v, bv, bi)) { bv = acc[vt][i]; bi = v; }
       }
 #pragma unroll
     for (int o = 16; o <= 32; o <<= 1) {
-      float ov = __shfl_xor(bv, o);
-      int oi = __shfl_xor(bi, o);
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
       if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
     }
-    if (kb == 0) { wv[wave][l16] = bv; wi[wave][l16] = bi; }
-    __syncthreads();
-    if (tid < 16 && r0 + tid < R) {
-      float b2 = wv[0][tid];
-      int i2 = wi[0][tid];
-      for (int w = 1; w < 4; ++w)
-        if (better(wv[w][tid], wi[w][tid], b2, i2)) { b2 = wv[w][tid]; i2 = wi[w][tid]; }
-      part_v[(r0 + tid) * nvb + vb] = b2;
-      part_i[(r0 + tid) * nvb + vb] = i2;
+    if (kb == 0 && r0 + l16 < R) {
+      part_v[(r0 + l16) * nsl + slice] = bv;
+      part_i[(r0 + l16) * nsl + slice] = bi;
     }
-    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int h = 0; h < UL; ++h) cur[ks][h] = nxt[ks][h];
   }
 }
 
@@ -219,8 +250,8 @@ extern "C" vc_status vc_head_mean(const void* o, int32_t kv_dtype, int32_t B, in
 
 extern "C" size_t vc_logits_workspace_bytes(int64_t R, int32_t V) {
   if (R <= 0 || V <= 0) return 0;
-  size_t nvb = static_cast<size_t>(cdiv(V, kLgVBlock));
-  return align_up(R * nvb * sizeof(float), 256) + align_up(R * nvb * sizeof(int), 256);
+  size_t nsl = static_cast<size_t>(cdiv(V, kLgWave));
+  return align_up(R * nsl * sizeof(float), 256) + align_up(R * nsl * sizeof(int), 256);
 }
 
 extern "C" vc_status vc_logits_argmax(const void* u, int32_t u_dtype, int64_t R, int32_t K, const void* W,
@@ -232,28 +263,31 @@ extern "C" vc_status vc_logits_argmax(const void* u, int32_t u_dtype, int64_t R,
   VC_REQUIRE(R > 0 && K > 0 && V > 0, "bad shape (R %lld, K %d, V %d)", (long long)R, K, V);
   hipStream_t s = as_stream(stream);
   if (use_mfma_argmax(w_dtype, K)) {
+    VC_REQUIRE(reinterpret_cast<uintptr_t>(u) % 16 == 0 && reinterpret_cast<uintptr_t>(W) % 16 == 0,
+               "u and W must be 16-byte aligned");
     size_t need = vc_logits_workspace_bytes(R, V);
     if (!ws || ws_bytes < need) {
       set_error("logits workspace needs %zu bytes (got %zu)", need, ws_bytes);
       return VC_ERR_WORKSPACE;
     }
-    int nvb = static_cast<int>(cdiv(V, kLgVBlock));
+    const int nsl = static_cast<int>(cdiv(V, kLgWave));
+    const unsigned nwg = static_cast<unsigned>(cdiv(V, kLgVBlock));
     float* pv = static_cast<float*>(ws);
-    int* pi = reinterpret_cast<int*>(static_cast<char*>(ws) + align_up(R * nvb * sizeof(float), 256));
+    int* pi = reinterpret_cast<int*>(static_cast<char*>(ws) + align_up(R * nsl * sizeof(float), 256));
     const bf16_t* w = static_cast<const bf16_t*>(W);
     if (K == 128) {
       if (u_dtype == VC_F32)
-        hipLaunchKernelGGL((argmax_mfma_kernel<128, float>), dim3(nvb), dim3(256), 0, s, static_cast<const float*>(u), w, R, V, pv, pi, nvb);
+        hipLaunchKernelGGL((argmax_mfma_kernel<128, float>), dim3(nwg), dim3(256), 0, s, static_cast<const float*>(u), w, R, V, pv, pi, nsl);
       else
-        hipLaunchKernelGGL((argmax_mfma_kernel<128, bf16_t>), dim3(nvb), dim3(256), 0, s, static_cast<const bf16_t*>(u), w, R, V, pv, pi, nvb);
+        hipLaunchKernelGGL((argmax_mfma_kernel<128, bf16_t>), dim3(nwg), dim3(256), 0, s, static_cast<const bf16_t*>(u), w, R, V, pv, pi, nsl);
     } else {
       if (u_dtype == VC_F32)
-        hipLaunchKernelGGL((argmax_mfma_kernel<64, float>), dim3(nvb), dim3(256), 0, s, static_cast<const float*>(u), w, R, V, pv, pi, nvb);
+        hipLaunchKernelGGL((argmax_mfma_kernel<64, float>), dim3(nwg), dim3(256), 0, s, static_cast<const float*>(u), w, R, V, pv, pi, nsl);
       else
-        hipLaunchKernelGGL((argmax_mfma_kernel<64, bf16_t>), dim3(nvb), dim3(256), 0, s, static_cast<const bf16_t*>(u), w, R, V, pv, pi, nvb);
+        hipLaunchKernelGGL((argmax_mfma_kernel<64, bf16_t>), dim3(nwg), dim3(256), 0, s, static_cast<const bf16_t*>(u), w, R, V, pv, pi, nsl);
     }
     VC_LAUNCHED("argmax_mfma_kernel");
-    hipLaunchKernelGGL(argmax_reduce_kernel, dim3(static_cast<unsigned>(R)), dim3(256), 0, s, pv, pi, nvb, tokens);
+    hipLaunchKernelGGL(argmax_reduce_kernel, dim3(static_cast<unsigned>(R)), dim3(256), 0, s, pv, pi, nsl, tokens);
     VC_LAUNCHED("argmax_reduce_kernel");
     return VC_OK;
   }
