@@ -530,8 +530,12 @@ def staggered_rounds(w, shape, weights, sess0, ref0, slots, gen, chunk, timed):
 
 
 def gpu_state():
-    """Clocks and socket power as amd-smi reports them (read-only query)."""
+    """Clocks and socket power as amd-smi reports them (read-only query).  Skipped
+    under a profiler: its preloaded library would initialise the GPU in the child
+    before amd-smi's interpreter replaces it."""
     import subprocess
+    if "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        return {"skipped": "run under a profiler"}
     try:
         r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"], capture_output=True,
                            text=True, timeout=20)
