@@ -77,26 +77,35 @@ __global__ void __launch_bounds__(256) argmax_rowwise_kernel(const TU* u, const 
 
 // ---- bf16 W on matrix cores
 // Each wave owns kLgWave consecutive vocabulary rows of W, held in registers as the A
-// operand (16 rows per tile), and sweeps all R rows of u in chunks of 16 (the B
-// operand): float32 u is split exactly into bf16 hi + lo, two products per step
-// (bf16 u: one).  The next chunk of u is loaded while the current one is
-// multiplied.  Per (row, wave slice) the largest logit and its lowest index go to
-// the partials, with no communication between waves; argmax_reduce_kernel combines
-// the slices of a row.
-constexpr int kLgWave = 64;                 // vocabulary rows per wave
-constexpr int kLgVBlock = 4 * kLgWave;      // per workgroup of 4 waves
+// operand (16 rows per tile); the workgroup sweeps all R rows of u in chunks of
+// kLgChunk rows (the B operand).  A chunk is loaded from global memory once per
+// workgroup, split exactly into bf16 hi + lo (float32 u; bf16 u is its own hi) and
+// staged in LDS, double-buffered; the loads of the next kLgAhead chunks are in
+// flight while the current one is multiplied, two products per step for float32 u,
+// one for bf16.  Per (row, wave slice) the largest logit and its lowest index go to
+// the partials; argmax_reduce_kernel combines the slices of a row.  At most 128
+// registers a wave, so two workgroups share a compute unit.
+constexpr int kLgWave = 64;                     // vocabulary rows per wave
+constexpr int kLgWaves = 8;                     // waves per workgroup
+constexpr int kLgVBlock = kLgWaves * kLgWave;   // vocabulary rows per workgroup
+constexpr int kLgChunk = 16;                    // rows of u staged at a time
+constexpr int kLgAhead = 1;                     // chunks of u loaded ahead of the one staged
 
 template <int KD, typename TU>
-__global__ void __launch_bounds__(256) argmax_mfma_kernel(const TU* u, const bf16_t* W, int64_t R, int V,
-                                                          float* part_v, int* part_i, int nsl) {
+__global__ void __launch_bounds__(64 * kLgWaves) __attribute__((amdgpu_waves_per_eu(4))) argmax_mfma_kernel(const TU* u, const bf16_t* W, int64_t R, int V,
+                                                                   float* part_v, int* part_i, int nsl) {
   constexpr int KS = KD / 32, VT = kLgWave / 16;
   constexpr bool kF32 = std::is_same<TU, float>::value;
-  constexpr int UL = kF32 ? 2 : 1;  // 16-byte loads of u per lane per k-step
+  constexpr int NP = kF32 ? 2 : 1;               // staged parts of u: hi (and lo)
+  constexpr int PITCH = KD + 8;                  // bf16 elements per staged row
+  constexpr int EPT = kLgChunk * KD / (64 * kLgWaves);  // chunk elements staged per thread
+  static_assert(EPT >= 1 && KD % EPT == 0, "staging shape");
+  __shared__ __attribute__((aligned(16))) bf16_t su[2][NP][kLgChunk * PITCH];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, kb = lane >> 4;
-  const int slice = blockIdx.x * 4 + wave;
+  const int slice = blockIdx.x * kLgWaves + wave;
   const int v0 = slice * kLgWave;
-  if (v0 >= V) return;  // wave-uniform; no barriers below
+  const bool active = v0 < V;  // wave-uniform; idle waves still stage u and meet the barriers
   union P16 { uint4 u; bf16x8_t v; };
   bf16x8_t wa[VT][KS];
 #pragma unroll
@@ -110,72 +119,82 @@ __global__ void __launch_bounds__(256) argmax_mfma_kernel(const TU* u, const bf1
       wa[vt][ks] = p.v;
     }
   }
-  // u of row r0 + l16, channels 32 ks + 8 kb .. + 7: UL 16-byte pieces per k-step
-  auto load_u = [&](int64_t r0, uint4 (&x)[KS][UL]) {
-    const int64_t r = r0 + l16;
+  // staging: this thread's EPT consecutive elements of a chunk
+  const int srow = (tid * EPT) / KD, scol = (tid * EPT) % KD;
+  float xq[kLgAhead][EPT];  // chunks c + 1 .. c + kLgAhead, oldest first
+  auto load = [&](int64_t r0, float (&xs)[EPT]) {
+    const int64_t r = r0 + srow;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int h = 0; h < UL; ++h) {
-        x[ks][h] = make_uint4(0, 0, 0, 0);
-        if (r < R) x[ks][h] = *reinterpret_cast<const uint4*>(u + r * KD + 32 * ks + 8 * kb + h * (8 / UL));
-      }
+    for (int j = 0; j < EPT; ++j) xs[j] = r < R ? Elem<TU>::load(u, r * KD + scol + j) : 0.f;
   };
-  uint4 cur[KS][UL], nxt[KS][UL];
-  load_u(0, cur);
-  for (int64_t r0 = 0; r0 < R; r0 += 16) {
-    if (r0 + 16 < R) load_u(r0 + 16, nxt);
-    f32x4_t acc[VT];
+  auto stage = [&](int buf, const float (&xs)[EPT]) {
 #pragma unroll
-    for (int vt = 0; vt < VT; ++vt) acc[vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < EPT; ++j) {
+      const __bf16 h = static_cast<__bf16>(xs[j]);
+      su[buf][0][srow * PITCH + scol + j] = __builtin_bit_cast(bf16_t, h);
+      if constexpr (kF32)
+        su[buf][NP - 1][srow * PITCH + scol + j] = __builtin_bit_cast(bf16_t, static_cast<__bf16>(xs[j] - static_cast<float>(h)));
+    }
+  };
+  {
+    float x0[EPT];
+    load(0, x0);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if constexpr (kF32) {
-        const float* xf = reinterpret_cast<const float*>(&cur[ks][0]);
-        bf16x8_t hi, lo;
+    for (int q = 0; q < kLgAhead; ++q) load(static_cast<int64_t>(q + 1) * kLgChunk, xq[q]);
+    stage(0, x0);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int64_t c0 = 0; c0 < R; c0 += kLgChunk) {
+    const bool more = c0 + kLgChunk < R;
+    for (int rt = 0; rt < kLgChunk / 16 && active; ++rt) {
+      const int64_t r0 = c0 + 16 * rt;
+      if (r0 >= R) break;
+      f32x4_t acc[VT];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const __bf16 h = static_cast<__bf16>(xf[j]);
-          hi[j] = h;
-          lo[j] = static_cast<__bf16>(xf[j] - static_cast<float>(h));
+      for (int vt = 0; vt < VT; ++vt) acc[vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int pt = 0; pt < NP; ++pt) {
+          P16 b;
+          b.u = *reinterpret_cast<const uint4*>(&su[buf][pt][(16 * rt + l16) * PITCH + 32 * ks + 8 * kb]);
+#pragma unroll
+          for (int vt = 0; vt < VT; ++vt)
+            acc[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[vt][ks], b.v, acc[vt], 0, 0, 0);
+        }
+      }
+      // acc[vt][i] = logit(vocabulary v0 + 16 vt + 4 kb + i, row r0 + l16)
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int v = v0 + vt * 16 + 4 * kb + i;
+          if (v < V && better(acc[vt][i], v, bv, bi)) { bv = acc[vt][i]; bi = v; }
         }
 #pragma unroll
-        for (int vt = 0; vt < VT; ++vt) {
-          acc[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[vt][ks], hi, acc[vt], 0, 0, 0);
-          acc[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[vt][ks], lo, acc[vt], 0, 0, 0);
-        }
-      } else {
-        P16 p;
-        p.u = cur[ks][0];
-#pragma unroll
-        for (int vt = 0; vt < VT; ++vt)
-          acc[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[vt][ks], p.v, acc[vt], 0, 0, 0);
+      for (int o = 16; o <= 32; o <<= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
+      if (kb == 0 && r0 + l16 < R) {
+        part_v[(r0 + l16) * nsl + slice] = bv;
+        part_i[(r0 + l16) * nsl + slice] = bi;
       }
     }
-    // acc[vt][i] = logit(vocabulary v0 + 16 vt + 4 kb + i, row r0 + l16)
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    if (more) {
+      stage(buf ^ 1, xq[0]);  // into the buffer read one chunk ago; the barrier below orders it
 #pragma unroll
-    for (int vt = 0; vt < VT; ++vt)
+      for (int q = 0; q + 1 < kLgAhead; ++q)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v = v0 + vt * 16 + 4 * kb + i;
-        if (v < V && better(acc[vt][i], v, bv, bi)) { bv = acc[vt][i]; bi = v; }
-      }
-#pragma unroll
-    for (int o = 16; o <= 32; o <<= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        for (int j = 0; j < EPT; ++j) xq[q][j] = xq[q + 1][j];
+      load(c0 + static_cast<int64_t>(kLgAhead + 1) * kLgChunk, xq[kLgAhead - 1]);
     }
-    if (kb == 0 && r0 + l16 < R) {
-      part_v[(r0 + l16) * nsl + slice] = bv;
-      part_i[(r0 + l16) * nsl + slice] = bi;
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int h = 0; h < UL; ++h) cur[ks][h] = nxt[ks][h];
+    __syncthreads();
+    buf ^= 1;
   }
 }
 
@@ -277,14 +296,14 @@ extern "C" vc_status vc_logits_argmax(const void* u, int32_t u_dtype, int64_t R,
     const bf16_t* w = static_cast<const bf16_t*>(W);
     if (K == 128) {
       if (u_dtype == VC_F32)
-        hipLaunchKernelGGL((argmax_mfma_kernel<128, float>), dim3(nwg), dim3(256), 0, s, static_cast<const float*>(u), w, R, V, pv, pi, nsl);
+        hipLaunchKernelGGL((argmax_mfma_kernel<128, float>), dim3(nwg), dim3(64 * kLgWaves), 0, s, static_cast<const float*>(u), w, R, V, pv, pi, nsl);
       else
-        hipLaunchKernelGGL((argmax_mfma_kernel<128, bf16_t>), dim3(nwg), dim3(256), 0, s, static_cast<const bf16_t*>(u), w, R, V, pv, pi, nsl);
+        hipLaunchKernelGGL((argmax_mfma_kernel<128, bf16_t>), dim3(nwg), dim3(64 * kLgWaves), 0, s, static_cast<const bf16_t*>(u), w, R, V, pv, pi, nsl);
     } else {
       if (u_dtype == VC_F32)
-        hipLaunchKernelGGL((argmax_mfma_kernel<64, float>), dim3(nwg), dim3(256), 0, s, static_cast<const float*>(u), w, R, V, pv, pi, nsl);
+        hipLaunchKernelGGL((argmax_mfma_kernel<64, float>), dim3(nwg), dim3(64 * kLgWaves), 0, s, static_cast<const float*>(u), w, R, V, pv, pi, nsl);
       else
-        hipLaunchKernelGGL((argmax_mfma_kernel<64, bf16_t>), dim3(nwg), dim3(256), 0, s, static_cast<const bf16_t*>(u), w, R, V, pv, pi, nsl);
+        hipLaunchKernelGGL((argmax_mfma_kernel<64, bf16_t>), dim3(nwg), dim3(64 * kLgWaves), 0, s, static_cast<const bf16_t*>(u), w, R, V, pv, pi, nsl);
     }
     VC_LAUNCHED("argmax_mfma_kernel");
     hipLaunchKernelGGL(argmax_reduce_kernel, dim3(static_cast<unsigned>(R)), dim3(256), 0, s, pv, pi, nsl, tokens);
