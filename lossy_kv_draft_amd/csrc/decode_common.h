@@ -172,12 +172,24 @@ __global__ void __launch_bounds__(kDecThreads) decode_merge_kernel(DecodeArgs a)
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int H = a.H, d = a.d, S = a.splits;
   const int tid = threadIdx.x;
+  // tpo threads per output channel, each summing a contiguous share of the splits;
+  // the first 16 of its partials are loaded before the weights are known, so the
+  // two rounds of global loads overlap
+  const int tpo = kDecThreads / d;
+  const int c = tid % d, part = tid / d;
+  const int per = (S + tpo - 1) / tpo;
+  const int s_lo = part < tpo ? part * per : S, s_hi = min(S, s_lo + per);
+  const float* p = a.part_o + (static_cast<int64_t>(bh) * S * H + h) * d + c;
+  const int64_t stride = static_cast<int64_t>(H) * d;
+  float v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = s_lo + j < s_hi ? p[(s_lo + j) * stride] : 0.f;
   if (tid < 64) {  // split weights: a wave holds one split per lane
     float m = -INFINITY, l = 0.f;
     if (tid < S) {
-      const float2 v = reinterpret_cast<const float2*>(a.part_ml)[(static_cast<int64_t>(bh) * S + tid) * H + h];
-      m = v.x;
-      l = v.y;
+      const float2 mv = reinterpret_cast<const float2*>(a.part_ml)[(static_cast<int64_t>(bh) * S + tid) * H + h];
+      m = mv.x;
+      l = mv.y;
     }
     const float M = warp_max(m);
     const float w = m == -INFINITY ? 0.f : exp2f(m - M);
@@ -189,32 +201,25 @@ __global__ void __launch_bounds__(kDecThreads) decode_merge_kernel(DecodeArgs a)
     }
   }
   __syncthreads();
-  // tpo threads per output channel, each summing a contiguous share of the splits
-  const int tpo = kDecThreads / d;
-  const int c = tid % d, part = tid / d;
-  const int per = (S + tpo - 1) / tpo;
-  const int s_lo = part * per, s_hi = min(S, s_lo + per);
   float O = 0.f;
-  if (part < tpo) {
-    const float* p = a.part_o + (static_cast<int64_t>(bh) * S * H + h) * d + c;
-    const int64_t stride = static_cast<int64_t>(H) * d;
-    for (int s0 = s_lo; s0 < s_hi; s0 += 16) {
-      float v[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = p[min(s0 + j, s_hi - 1) * stride];
+  for (int j = 0; j < 16; ++j)
+    if (s_lo + j < s_hi) O = fmaf(v[j], s_w[s_lo + j], O);
+  for (int s0 = s_lo + 16; s0 < s_hi; s0 += 16) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (s0 + j < s_hi) O = fmaf(v[j], s_w[s0 + j], O);
-    }
+    for (int j = 0; j < 16; ++j) v[j] = p[min(s0 + j, s_hi - 1) * stride];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (s0 + j < s_hi) O = fmaf(v[j], s_w[s0 + j], O);
   }
   s_part[tid] = O;
   __syncthreads();
   if (tid < d) {
-    float v = 0.f;
-    for (int q = 0; q < tpo; ++q) v += s_part[q * d + tid];
+    float sum = 0.f;
+    for (int q = 0; q < tpo; ++q) sum += s_part[q * d + tid];
     const float L = s_fin[1];
     const int64_t oi = (static_cast<int64_t>(b) * a.Hkv * H + hk * H + h) * d + tid;
-    Elem<T>::store(static_cast<T*>(a.out), oi, L > 0.f ? v / L : 0.f);
+    Elem<T>::store(static_cast<T*>(a.out), oi, L > 0.f ? sum / L : 0.f);
     if (a.lse && tid == 0)
       a.lse[static_cast<int64_t>(b) * a.Hkv * H + hk * H + h] = L > 0.f ? (s_fin[0] + log2f(L)) * kLn2 : -INFINITY;
   }

@@ -35,21 +35,26 @@ def _tie_eps(u, W):
     return 2 * (2.0 ** -15 + K * 2.0 ** -23) * mag.max(axis=1)
 
 
-@pytest.mark.parametrize("case", ["f32_64x1000", "bf16_128x151936", "bf16_64x5000"])
+@pytest.mark.parametrize("case", ["f32_64x1000", "bf16_128x151936", "bf16_64x5000", "bf16u_128x3001"])
 def test_logits_argmax_agrees_on_untied_rows(case):
+    u_dt = torch.float32
     if case == "f32_64x1000":
         w, R, Wd = C.TINY, 40, "f32"
         W = G.projection(w)
     elif case == "bf16_128x151936":
         w, R, Wd = C.QWEN30B, 640, "bf16"
         W = G.projection(w)
-    else:
+    elif case == "bf16_64x5000":
         w, R, Wd = C.TINY, 100, "bf16"
         W = G.normal(w, (3,), (5000, 64), dtype="bf16")
+    else:  # bf16 u (one product per step), ragged row and vocabulary counts
+        w, R, Wd = C.TINY, 37, "bf16"
+        W = G.normal(w, (6,), (3001, 128), dtype="bf16")
+        u_dt = torch.bfloat16
     say(f"[argmax] {case}")
-    u = G.normal(w, (2, len(case), R), (R, W.shape[1]), std=0.05)
+    u = G.normal(w, (2, len(case), R), (R, W.shape[1]), std=0.05, dtype="bf16" if u_dt == torch.bfloat16 else "f32")
     tok = torch.empty(R, dtype=torch.int32, device="cuda")
-    L.vc_logits_argmax(T(u), T(W, torch.float32 if Wd == "f32" else torch.bfloat16), tok)
+    L.vc_logits_argmax(T(u, u_dt), T(W, torch.float32 if Wd == "f32" else torch.bfloat16), tok)
     torch.cuda.synchronize()
     got = tok.cpu().numpy()
     lg = OL.logits(u, W)
