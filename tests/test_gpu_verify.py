@@ -71,8 +71,12 @@ def test_verify_batch_invariance(name):
         assert torch.equal(l1[:, :, 0], lse[:, :, i])
 
 
-def test_verify_ragged_context_lengths():
-    w = C.small(C.LLAMA8B, B=3, N=1500)
+@pytest.mark.parametrize("base", ["llama8b", "drop_k40"])
+def test_verify_ragged_context_lengths(base):
+    """Per-sequence context lengths (one of them empty), with 128 rows per kv-head
+    (4-wave blocks) and 160 (one 8-wave block)."""
+    w = C.small(C.LLAMA8B if base == "llama8b" else C.DROP, B=3, N=1500, **({} if base == "llama8b" else {"Hkv": 1, "Hq": 4}))
+    say(f"[verify ragged] {base}")
     K, V, Q, Kw, Vw = inputs(w)
     lens = [1500, 700, 0]
     cap = 1500 + w.k
