@@ -260,25 +260,64 @@ __global__ void heads_to_rows_kernel(const bf16_t* o, int H, int k, int hd, int6
 
 __device__ __forceinline__ bool better_idx(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
 
-__global__ void __launch_bounds__(256) argmax_rows_kernel(const float* logits, int V, int32_t* tok) {
-  __shared__ float sv[4];
-  __shared__ int si[4];
+// One workgroup of 16 waves per row: each thread keeps 8 loads (16 bytes each when
+// the rows allow it) in flight and its own (max, lowest index); a fixed-order
+// reduction over lanes, then waves.  The result is the row's largest logit with the
+// lowest index among equal ones, whatever the order of the comparisons.
+constexpr int kArgThreads = 1024;
+__global__ void __launch_bounds__(kArgThreads) argmax_rows_kernel(const float* logits, int V, int32_t* tok) {
+  __shared__ float sv[kArgThreads / 64];
+  __shared__ int si[kArgThreads / 64];
   const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* row = logits + r * V;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int v = threadIdx.x; v < V; v += 256) {
-    const float x = logits[r * V + v];
-    if (better_idx(x, v, bv, bi)) { bv = x; bi = v; }
+  if (V % 4 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0) {
+    const float4* r4 = reinterpret_cast<const float4*>(row);
+    const int n4 = V / 4;
+    for (int base = 0; base < n4; base += 8 * kArgThreads) {
+      float4 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * kArgThreads + tid;
+        x[u] = i < n4 ? r4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * kArgThreads + tid;
+        if (i < n4) {
+          if (better_idx(x[u].x, 4 * i, bv, bi)) { bv = x[u].x; bi = 4 * i; }
+          if (better_idx(x[u].y, 4 * i + 1, bv, bi)) { bv = x[u].y; bi = 4 * i + 1; }
+          if (better_idx(x[u].z, 4 * i + 2, bv, bi)) { bv = x[u].z; bi = 4 * i + 2; }
+          if (better_idx(x[u].w, 4 * i + 3, bv, bi)) { bv = x[u].w; bi = 4 * i + 3; }
+        }
+      }
+    }
+  } else {
+    for (int base = 0; base < V; base += 8 * kArgThreads) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int v = base + u * kArgThreads + tid;
+        x[u] = v < V ? row[v] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int v = base + u * kArgThreads + tid;
+        if (v < V && better_idx(x[u], v, bv, bi)) { bv = x[u]; bi = v; }
+      }
+    }
   }
   for (int o = 32; o > 0; o >>= 1) {
     const float ov = __shfl_xor(bv, o);
     const int oi = __shfl_xor(bi, o);
     if (better_idx(ov, oi, bv, bi)) { bv = ov; bi = oi; }
   }
-  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = bv; si[threadIdx.x >> 6] = bi; }
+  if ((tid & 63) == 0) { sv[tid >> 6] = bv; si[tid >> 6] = bi; }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w)
+  if (tid == 0) {
+    for (int w = 1; w < kArgThreads / 64; ++w)
       if (better_idx(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
     tok[r] = bi == 0x7fffffff ? 0 : bi;
   }
@@ -454,8 +493,8 @@ extern "C" vc_status vc_argmax_rows(const float* logits, int64_t R, int32_t V, i
   clear_error();
   VC_REQUIRE(logits && tokens, "NULL pointer argument");
   VC_REQUIRE(R > 0 && V > 0, "bad shape");
-  hipLaunchKernelGGL(argmax_rows_kernel, dim3(static_cast<unsigned>(R)), dim3(256), 0, as_stream(stream), logits, V,
-                     tokens);
+  hipLaunchKernelGGL(argmax_rows_kernel, dim3(static_cast<unsigned>(R)), dim3(kArgThreads), 0, as_stream(stream), logits,
+                     V, tokens);
   VC_LAUNCHED("argmax_rows_kernel");
   return VC_OK;
 }

@@ -162,6 +162,19 @@ def test_embed_heads_to_rows_and_argmax_rows_exact():
     assert list(tk.cpu().numpy()) == [argmax_lowest(r) for r in lg]
 
 
+@pytest.mark.parametrize("V", [32000, 40000, 32003])
+def test_argmax_rows_large_and_ragged(V):
+    """Vocabularies past one sweep of the workgroup (40000 > 8 x 1024 x 4) and a row
+    length that is not a multiple of 4 (the scalar path); planted ties far apart."""
+    lg = G.normal(W, (15, V), (5, V), 1.0, "f32")
+    lg[0, [7, V - 2]] = 40.0
+    lg[1, [V - 1]] = 40.0
+    lg[2, [4096, 4097, 30000]] = 40.0
+    tk = torch.empty(5, dtype=torch.int32, device=DEV)
+    L.vc_argmax_rows(T(lg), tk)
+    assert list(tk.cpu().numpy()) == [argmax_lowest(r) for r in lg]
+
+
 def test_copy_kv_rows_exact():
     B, Hkv, d, sr, dr = 3, 2, 128, 40, 20
     sk, sv = rnd((14, 0), (B, Hkv, sr, d)), rnd((14, 1), (B, Hkv, sr, d))
