@@ -49,8 +49,9 @@ vc_status vc_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, i
 vc_status vc_gemm_bf16_wide(const void* A, int64_t lda, const void* W, int64_t ldw, int64_t M, int32_t N, int32_t K,
                             void* C, int64_t ldc, int32_t c_dtype, const void* R, void* stream);
 
-/* y[m] = x[m] / sqrt(mean_j x[m][j]^2 + eps) * w, x and y bf16 [M, d], w bf16 [d].
- * float32 arithmetic, fixed per-row reduction order. */
+/* y[m] = x[m] / sqrt(mean_j x[m][j]^2 + eps) * w, x and y bf16 [M, d], w bf16 [d];
+ * d % 8 == 0, x, w, y 16-byte aligned (VC_ERR_INVALID_ARG otherwise).  float32
+ * arithmetic, fixed per-row reduction order. */
 vc_status vc_rmsnorm(const void* x, const void* w, int64_t M, int32_t d, float eps, void* y, void* stream);
 
 /* Rotary embedding of the q and k parts of a fused projection and scatter into the

@@ -172,22 +172,51 @@ __global__ void __launch_bounds__(512) gemm_bf16_kernel(const bf16_t* __restrict
   }
 }
 
-// one block per row; fixed per-row reduction tree
-__global__ void __launch_bounds__(256) rmsnorm_kernel(const bf16_t* x, const bf16_t* w, int d, float eps, bf16_t* y) {
-  __shared__ float part[4];
-  const int64_t r = blockIdx.x;
-  const bf16_t* xr = x + r * d;
+// Sum of squares of a row of d bf16 values (d % 8 == 0, 16-byte aligned) by one
+// wave: lane l takes the 8-value chunks l, l + 64, ... in order, then the wave's
+// fixed butterfly.  Every lane returns the total.
+__device__ __forceinline__ float row_sumsq(const bf16_t* xr, int d, int lane) {
   float s = 0.f;
-  for (int j = threadIdx.x; j < d; j += 256) {
-    const float v = bf16_to_f32(xr[j]);
-    s = fmaf(v, v, s);
+  for (int c = lane; c < d / 8; c += 64) {
+    const uint4 v = *reinterpret_cast<const uint4*>(xr + 8 * c);
+    const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = bf16_to_f32(static_cast<bf16_t>(ws[i] & 0xFFFFu));
+      const float hi = bf16_to_f32(static_cast<bf16_t>(ws[i] >> 16));
+      s = fmaf(lo, lo, s);
+      s = fmaf(hi, hi, s);
+    }
   }
-  s = warp_sum(s);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
-  __syncthreads();
-  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
-  const float inv = 1.0f / sqrtf(tot / static_cast<float>(d) + eps);
-  for (int j = threadIdx.x; j < d; j += 256) y[r * d + j] = f32_to_bf16(bf16_to_f32(xr[j]) * inv * bf16_to_f32(w[j]));
+  return warp_sum(s);
+}
+
+// 8 values x (bf16) times inv times the weights w (bf16), each rounded to bf16
+__device__ __forceinline__ uint4 scale_rms8(uint4 x, uint4 w, float inv) {
+  const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ws[4] = {w.x, w.y, w.z, w.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16_t lo = f32_to_bf16(bf16_to_f32(static_cast<bf16_t>(xs[i] & 0xFFFFu)) * inv *
+                                  bf16_to_f32(static_cast<bf16_t>(ws[i] & 0xFFFFu)));
+    const bf16_t hi = f32_to_bf16(bf16_to_f32(static_cast<bf16_t>(xs[i] >> 16)) * inv *
+                                  bf16_to_f32(static_cast<bf16_t>(ws[i] >> 16)));
+    o[i] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// one wave per row (four rows per workgroup), 16-byte loads and stores
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const bf16_t* x, const bf16_t* w, int64_t M, int d, float eps,
+                                                      bf16_t* y) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= M) return;
+  const bf16_t* xr = x + r * d;
+  const float inv = 1.0f / sqrtf(row_sumsq(xr, d, lane) / static_cast<float>(d) + eps);
+  for (int c = lane; c < d / 8; c += 64)
+    *reinterpret_cast<uint4*>(y + r * d + 8 * c) =
+        scale_rms8(*reinterpret_cast<const uint4*>(xr + 8 * c), *reinterpret_cast<const uint4*>(w + 8 * c), inv);
 }
 
 // one block per token row: rotary embedding of q and k, scatter of q, k, v
@@ -432,8 +461,10 @@ extern "C" vc_status vc_rmsnorm(const void* x, const void* w, int64_t M, int32_t
   VC_REQUIRE(x && w && y, "x / w / y is NULL");
   VC_REQUIRE(M > 0 && d > 0, "bad shape");
   VC_REQUIRE(eps > 0.f, "eps must be positive");
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(static_cast<unsigned>(M)), dim3(256), 0, as_stream(stream),
-                     static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w), d, eps, static_cast<bf16_t*>(y));
+  VC_REQUIRE(d % 8 == 0, "d must be a multiple of 8 (got %d)", d);
+  VC_REQUIRE(aligned16(x) && aligned16(w) && aligned16(y), "x, w and y must be 16-byte aligned");
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(static_cast<unsigned>(cdiv(M, 4))), dim3(256), 0, as_stream(stream),
+                     static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w), M, d, eps, static_cast<bf16_t*>(y));
   VC_LAUNCHED("rmsnorm_kernel");
   return VC_OK;
 }

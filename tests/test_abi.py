@@ -144,3 +144,11 @@ def test_split_planes_rejects_bad_arguments():
     _bad(L.vc_split_planes, wide, anchor, r, r, 64, stream=0, status=L._lib.VC_ERR_UNSUPPORTED)
     other = _ckv(k_bits=2, v_bits=2, group=64)
     _bad(L.vc_join_planes, other, r, r, full, 64, stream=0)                            # group differs
+
+
+def test_rmsnorm_rejects_bad_arguments():
+    bf = torch.bfloat16
+    _bad(L.vc_rmsnorm, torch.zeros(4, 250, dtype=bf), torch.zeros(250, dtype=bf), torch.zeros(4, 250, dtype=bf),
+         stream=0)                                                                     # d not a multiple of 8
+    _bad(L.vc_rmsnorm, torch.zeros(4, 256, dtype=bf), torch.zeros(256, dtype=bf), torch.zeros(4, 256, dtype=bf),
+         eps=0.0, stream=0)
