@@ -43,6 +43,16 @@ extern "C" {
 vc_status vc_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, int64_t M, int32_t N, int32_t K,
                        void* C, int64_t ldc, int32_t c_dtype, const void* R, void* stream);
 
+/* The gate/up projection of a SwiGLU block fused with the activation:
+ * act[m][j] = vc_swiglu of the bf16-rounded products (gate j, up j) of A[m], equal bit
+ * for bit to vc_gemm_bf16 into a [M, 2F] buffer followed by vc_swiglu, with one launch
+ * and no intermediate.  W bf16 [2F, K] holds the gate and up rows interleaved in
+ * blocks of 8: rows 16j .. 16j + 7 are gate rows 8j .. 8j + 7 and rows 16j + 8 ..
+ * 16j + 15 the up rows 8j .. 8j + 7.  act bf16 [M, F] with row stride ld_act;
+ * F % 8 == 0; other arguments and errors as vc_gemm_bf16. */
+vc_status vc_gemm_bf16_swiglu(const void* A, int64_t lda, const void* W, int64_t ldw, int64_t M, int32_t F, int32_t K,
+                              void* act, int64_t ld_act, void* stream);
+
 /* The same product for many rows (prompt processing): k summed in one ascending
  * pass per output, so its rounding differs from vc_gemm_bf16's.  Same arguments
  * and requirements. */

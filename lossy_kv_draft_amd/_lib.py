@@ -75,6 +75,7 @@ _DECLS = {
     # vc_model.h
     "vc_gemm_bf16": (c_i32, [c_p, c_i64, c_p, c_i64, c_i64, c_i32, c_i32, c_p, c_i64, c_i32, c_p, c_p]),
     "vc_gemm_bf16_wide": (c_i32, [c_p, c_i64, c_p, c_i64, c_i64, c_i32, c_i32, c_p, c_i64, c_i32, c_p, c_p]),
+    "vc_gemm_bf16_swiglu": (c_i32, [c_p, c_i64, c_p, c_i64, c_i64, c_i32, c_i32, c_p, c_i64, c_p]),
     "vc_rmsnorm": (c_i32, [c_p, c_p, c_i64, c_i32, c_f32, c_p, c_p]),
     "vc_rope_qkv": (c_i32, [c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_p, c_p, c_p, c_p, c_i64, c_p, c_p]),
     "vc_swiglu": (c_i32, [c_p, c_i64, c_i32, c_p, c_p]),
@@ -412,6 +413,22 @@ def vc_gemm_bf16(A, W, C, *, R=None, stream=None):
     N = W.shape[0]
     _check(lib.vc_gemm_bf16(_ptr(A), A.stride(0), _ptr(W), W.stride(0), M, N, K, _ptr(C), C.stride(0),
                             _dt(C.dtype), _ptr(R), _stream(stream)), "vc_gemm_bf16")
+
+
+def swiglu_interleave(wgu):
+    """[2F, K] gate-then-up rows -> the layout vc_gemm_bf16_swiglu reads (blocks of 8
+    gate rows followed by the same 8 up rows); a copy of the weights, no arithmetic."""
+    F2, K = wgu.shape
+    return wgu.view(2, F2 // 16, 8, K).transpose(0, 1).reshape(F2, K).contiguous()
+
+
+def vc_gemm_bf16_swiglu(A, Wi, act, *, stream=None):
+    """act[M, F] = swiglu(A @ Wgu^T) with Wi = swiglu_interleave(Wgu); equal bit for bit to
+    vc_gemm_bf16 into [M, 2F] followed by vc_swiglu."""
+    M, K = A.shape
+    F = Wi.shape[0] // 2
+    _check(lib.vc_gemm_bf16_swiglu(_ptr(A), A.stride(0), _ptr(Wi), Wi.stride(0), M, F, K, _ptr(act), act.stride(0),
+                                   _stream(stream)), "vc_gemm_bf16_swiglu")
 
 
 def vc_gemm_bf16_wide(A, W, C, *, R=None, stream=None):

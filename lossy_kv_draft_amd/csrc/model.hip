@@ -92,7 +92,14 @@ __global__ void __launch_bounds__(64) gemm_wide_kernel(const bf16_t* __restrict_
 constexpr int kGemmWaves = 8;  // k slices per workgroup
 constexpr int kGemmAhead = 8;  // W chunks in flight per wave
 
-template <int MT, bool CF32, bool RES>
+// Epilogue of gemm_bf16_kernel: the rounded output (plus residual), or SwiGLU of the
+// gate and up halves of an interleaved gate/up projection (each 16-row tile of W
+// holds gate rows 8j .. 8j + 7, then up rows 8j .. 8j + 7): C is then the
+// activation [M, N / 2], computed from the bf16-rounded gate and up values exactly
+// as swiglu_kernel computes it from the stored product.
+constexpr int kEpiStore = 0, kEpiSwiglu = 1;
+
+template <int MT, bool CF32, bool RES, int EPI = kEpiStore>
 __global__ void __launch_bounds__(512) gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda,
                                                         const bf16_t* __restrict__ W, int64_t ldw, int64_t M, int N,
                                                         int K, void* C, int64_t ldc,
@@ -152,12 +159,32 @@ __global__ void __launch_bounds__(512) gemm_bf16_kernel(const bf16_t* __restrict
   for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
   __syncthreads();
   // acc[t][i] of lane ln = C[m_base + 16 t + (ln & 15)][n0 + 4 (ln >> 4) + i]
+  auto total = [&](int t, int ln) {
+    return ((red[0][t][ln] + red[1][t][ln]) + (red[2][t][ln] + red[3][t][ln])) +
+           ((red[4][t][ln] + red[5][t][ln]) + (red[6][t][ln] + red[7][t][ln]));
+  };
+  if constexpr (EPI == kEpiSwiglu) {
+    // lanes 0 .. 31 hold the gate features of the tile, lanes 32 .. 63 the up ones
+    for (int e = tid; e < MT * 32; e += 64 * kGemmWaves) {
+      const int t = e >> 5, ln = e & 31;
+      const int64_t m = m_base + 16 * t + (ln & 15);
+      if (m >= M) continue;
+      const f32x4_t g = total(t, ln), u = total(t, ln + 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = (n0 >> 1) + 4 * (ln >> 4) + i;
+        if (2 * j >= N) continue;
+        const float gb = bf16_to_f32(f32_to_bf16(g[i])), ub = bf16_to_f32(f32_to_bf16(u[i]));
+        static_cast<bf16_t*>(C)[m * ldc + j] = f32_to_bf16(gb / (1.0f + expf(-gb)) * ub);
+      }
+    }
+    return;
+  }
   for (int e = tid; e < MT * 64; e += 64 * kGemmWaves) {
     const int t = e >> 6, ln = e & 63;
     const int64_t m = m_base + 16 * t + (ln & 15);
     if (m >= M) continue;
-    const f32x4_t v = ((red[0][t][ln] + red[1][t][ln]) + (red[2][t][ln] + red[3][t][ln])) +
-                      ((red[4][t][ln] + red[5][t][ln]) + (red[6][t][ln] + red[7][t][ln]));
+    const f32x4_t v = total(t, ln);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int nn = n0 + 4 * (ln >> 4) + i;
@@ -449,6 +476,39 @@ static vc_status gemm_common(bool wide, const void* A, int64_t lda, const void* 
 extern "C" vc_status vc_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, int64_t M, int32_t N,
                                   int32_t K, void* C, int64_t ldc, int32_t c_dtype, const void* R, void* stream) {
   return gemm_common(false, A, lda, W, ldw, M, N, K, C, ldc, c_dtype, R, stream);
+}
+
+extern "C" vc_status vc_gemm_bf16_swiglu(const void* A, int64_t lda, const void* W, int64_t ldw, int64_t M,
+                                         int32_t F, int32_t K, void* act, int64_t ld_act, void* stream) {
+  clear_error();
+  VC_REQUIRE(A && W && act, "A / W / act is NULL");
+  VC_REQUIRE(M > 0 && F > 0 && K > 0, "bad shape (M %lld, F %d, K %d)", (long long)M, F, K);
+  VC_REQUIRE(F % 8 == 0, "F must be a multiple of 8 (got %d)", F);
+  VC_REQUIRE(K % 32 == 0, "K must be a multiple of 32 (got %d)", K);
+  VC_REQUIRE(lda >= K && ldw >= K && ld_act >= F, "leading dimensions too small");
+  VC_REQUIRE(lda % 8 == 0 && ldw % 8 == 0, "lda and ldw must be multiples of 8 elements");
+  VC_REQUIRE(aligned16(A) && aligned16(W), "A and W must be 16-byte aligned");
+  const int64_t mt_rows = M >= 64 ? 64 : ((M + 15) / 16) * 16;
+  const int MT = static_cast<int>(mt_rows / 16);
+  const int N = 2 * F;
+  VC_REQUIRE(cdiv(N, 16) <= 65535, "grid too large");
+  const dim3 grid(static_cast<unsigned>(cdiv(M, mt_rows)), static_cast<unsigned>(cdiv(N, 16)));
+  const dim3 blk(64 * kGemmWaves);
+  hipStream_t s = as_stream(stream);
+  const bf16_t* a = static_cast<const bf16_t*>(A);
+  const bf16_t* w = static_cast<const bf16_t*>(W);
+#define VC_SWIGLU_LAUNCH(MT_)                                                                                   \
+  hipLaunchKernelGGL((gemm_bf16_kernel<MT_, false, false, kEpiSwiglu>), grid, blk, 0, s, a, lda, w, ldw, M, N, K, \
+                     act, ld_act, nullptr)
+  switch (MT) {
+    case 1: VC_SWIGLU_LAUNCH(1); break;
+    case 2: VC_SWIGLU_LAUNCH(2); break;
+    case 3: VC_SWIGLU_LAUNCH(3); break;
+    default: VC_SWIGLU_LAUNCH(4); break;
+  }
+#undef VC_SWIGLU_LAUNCH
+  VC_LAUNCHED("gemm_bf16_kernel");
+  return VC_OK;
 }
 
 extern "C" vc_status vc_gemm_bf16_wide(const void* A, int64_t lda, const void* W, int64_t ldw, int64_t M, int32_t N,

@@ -59,6 +59,8 @@ class DecoderGPU:
         self.gu = torch.empty(max_rows, 2 * s.ffn, **z)
         self.act = torch.empty(max_rows, s.ffn, **z)
         self.logits = torch.empty(max_rows, s.vocab, device=device, dtype=torch.float32)
+        # gate/up rows interleaved in blocks of 8 for the product fused with SwiGLU
+        self.wgu_i = [L.swiglu_interleave(t) for t in weights["wgu"]]
 
     def forward(self, tokens, B, k, attend, head=True):
         """tokens: int32 [B*k] (row b*k + i = token i of sequence b).  attend(l, M)
@@ -78,8 +80,11 @@ class DecoderGPU:
             attend(l, M)
             mm(self.rows[:M], w["wo"][l], x, R=x)
             L.vc_rmsnorm(x, w["n2"][l], h, eps=s.eps)
-            mm(h, w["wgu"][l], self.gu[:M])
-            L.vc_swiglu(self.gu[:M], self.act[:M])
+            if head:  # the batch-invariant product with SwiGLU in its epilogue (bit for bit the two calls)
+                L.vc_gemm_bf16_swiglu(h, self.wgu_i[l], self.act[:M])
+            else:
+                mm(h, w["wgu"][l], self.gu[:M])
+                L.vc_swiglu(self.gu[:M], self.act[:M])
             mm(self.act[:M], w["wd"][l], x, R=x)
         if not head:
             return None

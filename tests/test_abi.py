@@ -152,3 +152,12 @@ def test_rmsnorm_rejects_bad_arguments():
          stream=0)                                                                     # d not a multiple of 8
     _bad(L.vc_rmsnorm, torch.zeros(4, 256, dtype=bf), torch.zeros(256, dtype=bf), torch.zeros(4, 256, dtype=bf),
          eps=0.0, stream=0)
+
+
+def test_gemm_swiglu_rejects_bad_arguments():
+    bf = torch.bfloat16
+    x = torch.zeros(4, 256, dtype=bf)
+    act = torch.zeros(4, 60, dtype=bf)
+    _bad(L.vc_gemm_bf16_swiglu, x, torch.zeros(120, 256, dtype=bf), act, stream=0)       # F = 60 not a multiple of 8
+    _bad(L.vc_gemm_bf16_swiglu, torch.zeros(4, 250, dtype=bf), torch.zeros(128, 250, dtype=bf),
+         torch.zeros(4, 64, dtype=bf), stream=0)                                         # K not a multiple of 32

@@ -435,3 +435,21 @@ def test_round_output_equals_greedy_full_size():
     got = loop.run()
     say(f"rounds {loop.rounds}, mean accept {np.mean(loop.accept_lens):.2f}")
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("M", [1, 4, 40, 128])
+def test_gemm_swiglu_equals_separate_calls(M):
+    """The gate/up product with SwiGLU in its epilogue equals, bit for bit, the plain
+    batch-invariant product into [M, 2F] followed by the activation kernel."""
+    say(f"[gemm swiglu] M={M}")
+    d, F = 2048, 5504
+    x = T(G.normal(W, (22, M), (M, d), 1.0, "bf16"), torch.bfloat16)
+    wgu = T(G.normal(W, (23,), (2 * F, d), 0.02, "bf16"), torch.bfloat16)
+    gu = torch.empty(M, 2 * F, device=DEV, dtype=torch.bfloat16)
+    want = torch.empty(M, F, device=DEV, dtype=torch.bfloat16)
+    got = torch.empty_like(want)
+    L.vc_gemm_bf16(x, wgu, gu)
+    L.vc_swiglu(gu, want)
+    L.vc_gemm_bf16_swiglu(x, L.swiglu_interleave(wgu), got)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
