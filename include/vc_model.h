@@ -53,6 +53,18 @@ vc_status vc_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, i
 vc_status vc_gemm_bf16_swiglu(const void* A, int64_t lda, const void* W, int64_t ldw, int64_t M, int32_t F, int32_t K,
                               void* act, int64_t ld_act, void* stream);
 
+/* The QKV projection fused with vc_rope_qkv: the rows A [B*k, K] are projected by W
+ * and the result is rotated and scattered exactly as vc_rope_qkv does it with the
+ * bf16-rounded product (same outputs, same arguments, bit for bit), with one launch
+ * and no intermediate.  W bf16 [(Hq + 2 Hkv) hd, K] is the projection with the rows
+ * of each q and k head permuted in tiles of 16: rows (16 t .. 16 t + 7) of a head
+ * are its elements 8 t .. 8 t + 7 and rows 16 t + 8 .. 16 t + 15 the elements
+ * hd/2 + 8 t .. hd/2 + 8 t + 7 (the rotation partners); the v rows keep their order.
+ * hd % 16 == 0, K % 32 == 0; A and W 16-byte aligned, lda, ldw multiples of 8. */
+vc_status vc_gemm_bf16_rope(const void* A, int64_t lda, const void* W, int64_t ldw, int32_t B, int32_t k, int32_t K,
+                            int32_t Hq, int32_t Hkv, int32_t hd, float theta, const int32_t* pos, void* q_out,
+                            void* k_dst, void* v_dst, int64_t dst_rows, const int32_t* row0, void* stream);
+
 /* The same product for many rows (prompt processing): k summed in one ascending
  * pass per output, so its rounding differs from vc_gemm_bf16's.  Same arguments
  * and requirements. */

@@ -14,6 +14,6 @@ from ._lib import (  # noqa: F401
     vc_head_mean, vc_logits_argmax, vc_logits_workspace_bytes, vc_accept, vc_stage_full_kv, vc_hadamard_rows,
     vc_stage_full_kv_d2h, vc_last_error, workspace, FileStager, VC_ERR_IO,
     vc_split_planes, vc_join_planes, split_residuals,
-    vc_gemm_bf16_swiglu, swiglu_interleave,
+    vc_gemm_bf16_swiglu, swiglu_interleave, vc_gemm_bf16_rope, rope_interleave,
     vc_gemm_bf16, vc_gemm_bf16_wide, vc_rmsnorm, vc_rope_qkv, vc_swiglu, vc_embed, vc_heads_to_rows, vc_argmax_rows, vc_copy_kv_rows,
 )

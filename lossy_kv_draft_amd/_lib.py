@@ -76,6 +76,8 @@ _DECLS = {
     "vc_gemm_bf16": (c_i32, [c_p, c_i64, c_p, c_i64, c_i64, c_i32, c_i32, c_p, c_i64, c_i32, c_p, c_p]),
     "vc_gemm_bf16_wide": (c_i32, [c_p, c_i64, c_p, c_i64, c_i64, c_i32, c_i32, c_p, c_i64, c_i32, c_p, c_p]),
     "vc_gemm_bf16_swiglu": (c_i32, [c_p, c_i64, c_p, c_i64, c_i64, c_i32, c_i32, c_p, c_i64, c_p]),
+    "vc_gemm_bf16_rope": (c_i32, [c_p, c_i64, c_p, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_p, c_p, c_p,
+                                  c_p, c_i64, c_p, c_p]),
     "vc_rmsnorm": (c_i32, [c_p, c_p, c_i64, c_i32, c_f32, c_p, c_p]),
     "vc_rope_qkv": (c_i32, [c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_p, c_p, c_p, c_p, c_i64, c_p, c_p]),
     "vc_swiglu": (c_i32, [c_p, c_i64, c_i32, c_p, c_p]),
@@ -429,6 +431,24 @@ def vc_gemm_bf16_swiglu(A, Wi, act, *, stream=None):
     F = Wi.shape[0] // 2
     _check(lib.vc_gemm_bf16_swiglu(_ptr(A), A.stride(0), _ptr(Wi), Wi.stride(0), M, F, K, _ptr(act), act.stride(0),
                                    _stream(stream)), "vc_gemm_bf16_swiglu")
+
+
+def rope_interleave(wqkv, Hq, Hkv, hd):
+    """[(Hq + 2 Hkv) hd, K] QKV projection -> the layout vc_gemm_bf16_rope reads (in each
+    q and k head, tiles of 8 elements followed by their 8 rotation partners); a copy of
+    the weights, no arithmetic."""
+    K = wqkv.shape[1]
+    nqk = (Hq + Hkv) * hd
+    qk = wqkv[:nqk].view(Hq + Hkv, 2, hd // 16, 8, K).permute(0, 2, 1, 3, 4).reshape(nqk, K)
+    return torch.cat([qk, wqkv[nqk:]]).contiguous()
+
+
+def vc_gemm_bf16_rope(A, Wr, B, k, Hq, Hkv, hd, pos, q_out, k_dst, v_dst, row0, *, theta=10000.0, stream=None):
+    """vc_rope_qkv(A @ Wqkv^T, ...) in one launch, Wr = rope_interleave(Wqkv, Hq, Hkv, hd)."""
+    assert k_dst.shape == v_dst.shape and k_dst.is_contiguous() and v_dst.is_contiguous() and q_out.is_contiguous()
+    _check(lib.vc_gemm_bf16_rope(_ptr(A), A.stride(0), _ptr(Wr), Wr.stride(0), B, k, A.shape[1], Hq, Hkv, hd, theta,
+                                 _ptr(pos), _ptr(q_out), _ptr(k_dst), _ptr(v_dst), k_dst.shape[2], _ptr(row0),
+                                 _stream(stream)), "vc_gemm_bf16_rope")
 
 
 def vc_gemm_bf16_wide(A, W, C, *, R=None, stream=None):

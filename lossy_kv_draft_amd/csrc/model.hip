@@ -97,13 +97,39 @@ constexpr int kGemmAhead = 8;  // W chunks in flight per wave
 // holds gate rows 8j .. 8j + 7, then up rows 8j .. 8j + 7): C is then the
 // activation [M, N / 2], computed from the bf16-rounded gate and up values exactly
 // as swiglu_kernel computes it from the stored product.
-constexpr int kEpiStore = 0, kEpiSwiglu = 1;
+// kEpiRope: the QKV projection with the rotary embedding and the scatter of
+// rope_qkv_kernel in its epilogue; W's q and k rows are permuted so that each 16-row
+// tile holds the rotation pairs (j0 .. j0 + 7, j0 + hd/2 .. j0 + hd/2 + 7) of one
+// head, the v rows are in their order.
+constexpr int kEpiStore = 0, kEpiSwiglu = 1, kEpiRope = 2;
+
+struct RopeArgs {
+  int k, Hq, Hkv, hd;
+  float log2_theta;
+  const int32_t* pos;
+  bf16_t* q_out;
+  bf16_t* k_dst;
+  bf16_t* v_dst;
+  int64_t dst_rows;
+  const int32_t* row0;
+};
+
+// rotation of the pair (x0, x1) of element j at position p, as rope_qkv_kernel does it
+__device__ __forceinline__ void rope_pair(float x0, float x1, int j, int hd, float log2_theta, float p, float& y0,
+                                          float& y1) {
+  const float inv_freq = exp2f(-static_cast<float>(2 * j) / static_cast<float>(hd) * log2_theta);
+  float sn, cs;
+  sincosf(p * inv_freq, &sn, &cs);
+  y0 = x0 * cs - x1 * sn;
+  y1 = x1 * cs + x0 * sn;
+}
 
 template <int MT, bool CF32, bool RES, int EPI = kEpiStore>
 __global__ void __launch_bounds__(512) gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda,
                                                         const bf16_t* __restrict__ W, int64_t ldw, int64_t M, int N,
                                                         int K, void* C, int64_t ldc,
-                                                        const bf16_t* R) {  // C may alias R
+                                                        const bf16_t* R,  // C may alias R
+                                                        RopeArgs ra = RopeArgs{}) {
   __shared__ f32x4_t red[kGemmWaves][MT][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -176,6 +202,55 @@ __global__ void __launch_bounds__(512) gemm_bf16_kernel(const bf16_t* __restrict
         if (2 * j >= N) continue;
         const float gb = bf16_to_f32(f32_to_bf16(g[i])), ub = bf16_to_f32(f32_to_bf16(u[i]));
         static_cast<bf16_t*>(C)[m * ldc + j] = f32_to_bf16(gb / (1.0f + expf(-gb)) * ub);
+      }
+    }
+    return;
+  }
+  if constexpr (EPI == kEpiRope) {
+    const int half = ra.hd / 2;
+    const int qk_width = (ra.Hq + ra.Hkv) * ra.hd;
+    if (n0 < qk_width) {  // a tile of rotation pairs: lanes 0 .. 31 first halves, 32 .. 63 second
+      const int tpb = half / 8;  // tiles per head
+      const int h = (n0 / 16) / tpb, j0 = 8 * ((n0 / 16) % tpb);
+      for (int e = tid; e < MT * 32; e += 64 * kGemmWaves) {
+        const int t = e >> 5, ln = e & 31;
+        const int64_t m = m_base + 16 * t + (ln & 15);
+        if (m >= M) continue;
+        const int b = static_cast<int>(m / ra.k), i = static_cast<int>(m % ra.k);
+        const float p = static_cast<float>(ra.pos[m]);
+        const int64_t krow = static_cast<int64_t>(ra.row0[b]) + i;
+        const bool kv_in = krow >= 0 && krow < ra.dst_rows;
+        const f32x4_t x0v = total(t, ln), x1v = total(t, ln + 32);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = j0 + 4 * (ln >> 4) + q;
+          float y0, y1;
+          rope_pair(bf16_to_f32(f32_to_bf16(x0v[q])), bf16_to_f32(f32_to_bf16(x1v[q])), j, ra.hd, ra.log2_theta, p,
+                    y0, y1);
+          bf16_t* dst;
+          if (h < ra.Hq) dst = ra.q_out + ((static_cast<int64_t>(b) * ra.Hq + h) * ra.k + i) * ra.hd;
+          else if (kv_in) dst = ra.k_dst + ((static_cast<int64_t>(b) * ra.Hkv + (h - ra.Hq)) * ra.dst_rows + krow) * ra.hd;
+          else continue;
+          dst[j] = f32_to_bf16(y0);
+          dst[j + half] = f32_to_bf16(y1);
+        }
+      }
+    } else {  // value rows: scattered as they are
+      for (int e = tid; e < MT * 64; e += 64 * kGemmWaves) {
+        const int t = e >> 6, ln = e & 63;
+        const int64_t m = m_base + 16 * t + (ln & 15);
+        if (m >= M) continue;
+        const int b = static_cast<int>(m / ra.k), i = static_cast<int>(m % ra.k);
+        const int64_t krow = static_cast<int64_t>(ra.row0[b]) + i;
+        if (krow < 0 || krow >= ra.dst_rows) continue;
+        const f32x4_t v = total(t, ln);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nn = n0 + 4 * (ln >> 4) + q;
+          if (nn >= N) continue;
+          const int hv = (nn - qk_width) / ra.hd, c = (nn - qk_width) % ra.hd;
+          ra.v_dst[((static_cast<int64_t>(b) * ra.Hkv + hv) * ra.dst_rows + krow) * ra.hd + c] = f32_to_bf16(v[q]);
+        }
       }
     }
     return;
@@ -262,12 +337,8 @@ __global__ void __launch_bounds__(256) rope_qkv_kernel(const bf16_t* qkv, int k,
   for (int t = threadIdx.x; t < rot_tasks + Hkv * hd; t += 256) {
     if (t < rot_tasks) {
       const int h = t / half, j = t % half;  // h < Hq: q head, else k head h - Hq
-      const float inv_freq = exp2f(-static_cast<float>(2 * j) / static_cast<float>(hd) * log2_theta);
-      float sn, cs;
-      sincosf(p * inv_freq, &sn, &cs);
-      const float x0 = bf16_to_f32(src[h * hd + j]), x1 = bf16_to_f32(src[h * hd + j + half]);
-      const float y0 = x0 * cs - x1 * sn;
-      const float y1 = x1 * cs + x0 * sn;
+      float y0, y1;
+      rope_pair(bf16_to_f32(src[h * hd + j]), bf16_to_f32(src[h * hd + j + half]), j, hd, log2_theta, p, y0, y1);
       if (h < Hq) {
         bf16_t* dst = q_out + ((static_cast<int64_t>(b) * Hq + h) * k + i) * hd;
         dst[j] = f32_to_bf16(y0);
@@ -507,6 +578,45 @@ extern "C" vc_status vc_gemm_bf16_swiglu(const void* A, int64_t lda, const void*
     default: VC_SWIGLU_LAUNCH(4); break;
   }
 #undef VC_SWIGLU_LAUNCH
+  VC_LAUNCHED("gemm_bf16_kernel");
+  return VC_OK;
+}
+
+extern "C" vc_status vc_gemm_bf16_rope(const void* A, int64_t lda, const void* W, int64_t ldw, int32_t B, int32_t k,
+                                       int32_t K, int32_t Hq, int32_t Hkv, int32_t hd, float theta, const int32_t* pos,
+                                       void* q_out, void* k_dst, void* v_dst, int64_t dst_rows, const int32_t* row0,
+                                       void* stream) {
+  clear_error();
+  VC_REQUIRE(A && W && pos && q_out && k_dst && v_dst && row0, "NULL pointer argument");
+  VC_REQUIRE(B > 0 && k > 0 && K > 0 && Hq > 0 && Hkv > 0 && hd > 0, "bad shape");
+  VC_REQUIRE(hd % 16 == 0, "hd must be a multiple of 16 (got %d)", hd);
+  VC_REQUIRE(K % 32 == 0, "K must be a multiple of 32 (got %d)", K);
+  VC_REQUIRE(theta > 1.f, "theta must exceed 1");
+  VC_REQUIRE(dst_rows >= k, "dst_rows must hold at least k rows");
+  VC_REQUIRE(lda >= K && ldw >= K && lda % 8 == 0 && ldw % 8 == 0, "bad leading dimensions");
+  VC_REQUIRE(aligned16(A) && aligned16(W), "A and W must be 16-byte aligned");
+  const int64_t M = static_cast<int64_t>(B) * k;
+  const int N = (Hq + 2 * Hkv) * hd;
+  const int64_t mt_rows = M >= 64 ? 64 : ((M + 15) / 16) * 16;
+  const int MT = static_cast<int>(mt_rows / 16);
+  VC_REQUIRE(cdiv(N, 16) <= 65535, "grid too large");
+  const dim3 grid(static_cast<unsigned>(cdiv(M, mt_rows)), static_cast<unsigned>(cdiv(N, 16)));
+  const dim3 blk(64 * kGemmWaves);
+  const RopeArgs ra{k, Hq, Hkv, hd, log2f(theta), pos, static_cast<bf16_t*>(q_out), static_cast<bf16_t*>(k_dst),
+                    static_cast<bf16_t*>(v_dst), dst_rows, row0};
+  hipStream_t s = as_stream(stream);
+  const bf16_t* a = static_cast<const bf16_t*>(A);
+  const bf16_t* w = static_cast<const bf16_t*>(W);
+#define VC_ROPE_LAUNCH(MT_)                                                                                           \
+  hipLaunchKernelGGL((gemm_bf16_kernel<MT_, false, false, kEpiRope>), grid, blk, 0, s, a, lda, w, ldw, M, N, K, nullptr, \
+                     0, nullptr, ra)
+  switch (MT) {
+    case 1: VC_ROPE_LAUNCH(1); break;
+    case 2: VC_ROPE_LAUNCH(2); break;
+    case 3: VC_ROPE_LAUNCH(3); break;
+    default: VC_ROPE_LAUNCH(4); break;
+  }
+#undef VC_ROPE_LAUNCH
   VC_LAUNCHED("gemm_bf16_kernel");
   return VC_OK;
 }

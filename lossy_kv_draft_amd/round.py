@@ -59,8 +59,11 @@ class DecoderGPU:
         self.gu = torch.empty(max_rows, 2 * s.ffn, **z)
         self.act = torch.empty(max_rows, s.ffn, **z)
         self.logits = torch.empty(max_rows, s.vocab, device=device, dtype=torch.float32)
-        # gate/up rows interleaved in blocks of 8 for the product fused with SwiGLU
+        # gate/up rows interleaved in blocks of 8 for the product fused with SwiGLU, and
+        # the q/k rows of each head with their rotation partners for the product fused
+        # with the rotary embedding (copies of the weights in the layouts those read)
         self.wgu_i = [L.swiglu_interleave(t) for t in weights["wgu"]]
+        self.wqkv_r = [L.rope_interleave(t, s.Hq, s.Hkv, s.hd) for t in weights["wqkv"]]
 
     def forward(self, tokens, B, k, attend, head=True):
         """tokens: int32 [B*k] (row b*k + i = token i of sequence b).  attend(l, M)
@@ -76,7 +79,16 @@ class DecoderGPU:
         L.vc_embed(w["E"], tokens, x)
         for l in range(s.layers):
             L.vc_rmsnorm(x, w["n1"][l], h, eps=s.eps)
-            mm(h, w["wqkv"][l], self.qkv[:M])
+            # steps of up to 32 rows: the batch-invariant product with the rotary scatter in
+            # its epilogue (bit for bit the two calls; the verify pass keeps them apart,
+            # where the layer's full cache is waited for after the projection)
+            rope = getattr(attend, "rope", None) if head and M <= 32 else None
+            if rope is not None:
+                t = rope(l, M)
+                L.vc_gemm_bf16_rope(h, self.wqkv_r[l], t["B"], t["k"], s.Hq, s.Hkv, s.hd, t["pos"], t["q"], t["K"],
+                                    t["V"], t["row0"], theta=s.theta)
+            else:
+                mm(h, w["wqkv"][l], self.qkv[:M])
             attend(l, M)
             mm(self.rows[:M], w["wo"][l], x, R=x)
             L.vc_rmsnorm(x, w["n2"][l], h, eps=s.eps)
@@ -262,17 +274,30 @@ def attend_full(dec: DecoderGPU, cache, B, k, pos, row0, ctx_len, ctx_lens, spli
     attention over rows [0, row0[b] + i].  after(l, K, V) runs before the layer's
     cache is released."""
     s = dec.s
+    roped = {}
 
-    def attend(l, M):
+    def rope(l, M):
+        """The rotary scatter's destinations, for a projection that applies it (the
+        layer's cache is acquired here, before the projection writes into it)."""
         K, V = cache.acquire(l)
         q = dec.q[: M * s.Hq * s.hd].view(B, s.Hq, k, s.hd)
-        L.vc_rope_qkv(dec.qkv[:M], B, k, s.Hq, s.Hkv, s.hd, pos, q, K, V, row0, theta=s.theta)
+        roped[l] = (q, K, V)
+        return dict(B=B, k=k, pos=pos, q=q, K=K, V=V, row0=row0)
+
+    def attend(l, M):
+        if l in roped:
+            q, K, V = roped.pop(l)
+        else:
+            K, V = cache.acquire(l)
+            q = dec.q[: M * s.Hq * s.hd].view(B, s.Hq, k, s.hd)
+            L.vc_rope_qkv(dec.qkv[:M], B, k, s.Hq, s.Hkv, s.hd, pos, q, K, V, row0, theta=s.theta)
         out = dec.attn[: M * s.Hq * s.hd].view(B, s.Hq, k, s.hd)
         L.vc_verify_attn_full(q, K, V, ctx_len, out, ctx_lens=ctx_lens, split_tokens=split_tokens, ws=ws)
         if after is not None:
             after(l, K, V)
         cache.release(l)
         L.vc_heads_to_rows(out, dec.rows[:M])
+    attend.rope = rope
     return attend
 
 
@@ -280,13 +305,27 @@ def attend_draft(dec: DecoderGPU, ckvs, B, pos, tail_row, main_lens, tail_lens, 
     """Attention callback of one draft step: rotary + append of the token's key/value
     to the compressed cache's tail, then decode attention over compressed rows + tail."""
     s = dec.s
+    roped = set()
+
+    def rope(l, M):
+        """The rotary scatter's destinations (the compressed cache's tail), for a
+        projection that applies it."""
+        ckv = ckvs[l]
+        roped.add(l)
+        q = dec.q[: M * s.Hq * s.hd].view(B, s.Hq, 1, s.hd)
+        return dict(B=B, k=1, pos=pos, q=q, K=ckv.tail_k, V=ckv.tail_v, row0=tail_row)
 
     def attend(l, M):
         ckv = ckvs[l]
         q = dec.q[: M * s.Hq * s.hd].view(B, s.Hq, 1, s.hd)
-        L.vc_rope_qkv(dec.qkv[:M], B, 1, s.Hq, s.Hkv, s.hd, pos, q, ckv.tail_k, ckv.tail_v, tail_row, theta=s.theta)
+        if l in roped:
+            roped.discard(l)
+        else:
+            L.vc_rope_qkv(dec.qkv[:M], B, 1, s.Hq, s.Hkv, s.hd, pos, q, ckv.tail_k, ckv.tail_v, tail_row,
+                          theta=s.theta)
         out = dec.rows[:M].view(B, s.Hq, s.hd)
         L.vc_decode_attn_compressed(ckv, q.view(B, s.Hq, s.hd), out, main_lens=main_lens, tail_lens=tail_lens, ws=ws)
+    attend.rope = rope
     return attend
 
 

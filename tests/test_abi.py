@@ -161,3 +161,14 @@ def test_gemm_swiglu_rejects_bad_arguments():
     _bad(L.vc_gemm_bf16_swiglu, x, torch.zeros(120, 256, dtype=bf), act, stream=0)       # F = 60 not a multiple of 8
     _bad(L.vc_gemm_bf16_swiglu, torch.zeros(4, 250, dtype=bf), torch.zeros(128, 250, dtype=bf),
          torch.zeros(4, 64, dtype=bf), stream=0)                                         # K not a multiple of 32
+
+
+def test_gemm_rope_rejects_bad_arguments():
+    bf = torch.bfloat16
+    x = torch.zeros(4, 256, dtype=bf)
+    w = torch.zeros(24 * 8, 256, dtype=bf)
+    q = torch.zeros(4, 16, 1, 8, dtype=bf)
+    kv = torch.zeros(4, 4, 10, 8, dtype=bf)
+    i32 = torch.zeros(4, dtype=torch.int32)
+    _bad(L.vc_gemm_bf16_rope, x, w, 4, 1, 16, 4, 8, i32, q, kv, kv, i32, stream=0)          # hd not a multiple of 16
+    _bad(L.vc_gemm_bf16_rope, x, w, 4, 1, 16, 4, 16, i32, q, kv, kv, i32, theta=1.0, stream=0)

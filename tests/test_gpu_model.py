@@ -453,3 +453,36 @@ def test_gemm_swiglu_equals_separate_calls(M):
     L.vc_gemm_bf16_swiglu(x, L.swiglu_interleave(wgu), got)
     torch.cuda.synchronize()
     assert torch.equal(got, want)
+
+
+@pytest.mark.parametrize("B,k", [(4, 1), (3, 5), (4, 32)])
+def test_gemm_rope_equals_separate_calls(B, k):
+    """The QKV product with the rotary scatter in its epilogue writes, bit for bit,
+    what the plain batch-invariant product followed by the rotary kernel writes
+    (queries, and key/value rows including ones that fall outside the cache)."""
+    say(f"[gemm rope] B={B} k={k}")
+    Hq, Hkv, hd, d = 16, 4, 128, 2048
+    M = B * k
+    width = (Hq + 2 * Hkv) * hd
+    x = T(G.normal(W, (24, B, k), (M, d), 1.0, "bf16"), torch.bfloat16)
+    wqkv = T(G.normal(W, (25,), (width, d), 0.02, "bf16"), torch.bfloat16)
+    pos = T(G.uniform_ints(W, (26, B, k), (M,), 0, 40000), torch.int32)
+    rows = k + 6
+    r0 = np.array([(b * 3) % (rows - k + 1) for b in range(B)], np.int64)
+    r0[-1] = rows - k + 3                      # the last sequence's last rows fall outside the cache
+    row0 = T(r0, torch.int32)
+    qkv = torch.empty(M, width, device=DEV, dtype=torch.bfloat16)
+    L.vc_gemm_bf16(x, wqkv, qkv)
+    outs = []
+    for fused in (False, True):
+        q = torch.zeros(B, Hq, k, hd, device=DEV, dtype=torch.bfloat16)
+        kd = torch.zeros(B, Hkv, rows, hd, device=DEV, dtype=torch.bfloat16)
+        vd = torch.zeros_like(kd)
+        if fused:
+            L.vc_gemm_bf16_rope(x, L.rope_interleave(wqkv, Hq, Hkv, hd), B, k, Hq, Hkv, hd, pos, q, kd, vd, row0)
+        else:
+            L.vc_rope_qkv(qkv, B, k, Hq, Hkv, hd, pos, q, kd, vd, row0)
+        outs.append((q, kd, vd))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
