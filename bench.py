@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--no-stage", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-e2e", action="store_true", help="skip the end-to-end decoder rounds")
+    p.add_argument("--no-remote-prefix", action="store_true",
+                   help="skip the end-to-end rounds with the prompt's full KV staged from a file")
     p.add_argument("--e2e-ctx", type=int, default=32768, help="prompt length of the end-to-end rounds")
     p.add_argument("--e2e-gen", type=int, default=256, help="tokens generated per sequence")
     p.add_argument("--e2e-slots", type=int, default=2, help="device layer slots of the staged full KV")
@@ -367,7 +369,7 @@ def measure_stage(st):
             "copy_exact": bool(ok)}
 
 
-def e2e_rounds(ctx, gen, slots):
+def e2e_rounds(ctx, gen, slots, remote=True):
     """Draft-and-verify decoding of the random-init 4-layer decoder (d_model 2048,
     16/4 heads, SwiGLU 5504, vocab 32000, batch 4, 2-bit KIVI drafts, k = 32) after a
     prompt of `ctx` tokens: accepted tokens/s with the full KV staged from pinned host
@@ -425,8 +427,11 @@ def e2e_rounds(ctx, gen, slots):
                                               for k, v in ada.policy.times.items() if v},
                 "output_equals_greedy": bool(np.array_equal(got_a, ref))}
     del ada
-    note("prefix staged from a file")
-    remote = remote_prefix_rounds(w, sess, ref, slots, gen, timed)
+    if remote:
+        note("prefix staged from a file")
+        remote = remote_prefix_rounds(w, sess, ref, slots, gen, timed)
+    else:
+        remote = None
     note("staggered batches")
     stag = staggered_rounds(w, shape, weights, sess, ref, slots, gen, chunk, timed)
     committed = w.B * (gen - 1)                                 # tokens produced after the prefill's first
@@ -699,7 +704,7 @@ def main():
     if not a.no_e2e:
         del st
         torch.cuda.empty_cache()
-        line["e2e"] = e2e_rounds(a.e2e_ctx, a.e2e_gen, a.e2e_slots)
+        line["e2e"] = e2e_rounds(a.e2e_ctx, a.e2e_gen, a.e2e_slots, remote=not a.no_remote_prefix)
         line["accepted_tok_per_s"] = line["e2e"]["accepted_tok_per_s"]
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
