@@ -105,15 +105,18 @@ def test_verify_deterministic():
     assert torch.equal(a, b)
 
 
-def test_full_size_verify_sampled_rows():
-    """Llama-3-8B-shaped layer at 32k context, k = 32, in the launch configuration
-    the benchmark times; sampled rows against the oracle."""
-    w = C.LLAMA8B
+@pytest.mark.parametrize("name", ["llama8b", "drop", "qwen30b"])
+def test_full_size_verify_sampled_rows(name):
+    """The benchmark's verify shapes at full size, in the launch configuration it
+    times (Llama-3-8B-shaped 32k, k 32: 128 rows per kv-head; token-dropping 131k,
+    k 40: 160 rows, one 8-wave block; Qwen-shaped 64k, k 40: 320 rows, three
+    blocks); sampled rows against the oracle."""
+    w = {"llama8b": C.LLAMA8B, "drop": C.DROP, "qwen30b": C.QWEN30B}[name]
     dt = torch.bfloat16
     rows = w.N + w.k
     kc = torch.empty(w.B, w.Hkv, rows, w.d, dtype=dt, device="cuda")
     vc = torch.empty_like(kc)
-    say("[full verify] generating inputs")
+    say(f"[full verify] {name}: generating inputs")
     for b in range(w.B):
         for h in range(w.Hkv):
             kc[b, h, :w.N] = T(G.kv_slice(w, "k", b, h), dt)
@@ -129,7 +132,7 @@ def test_full_size_verify_sampled_rows():
     for _ in range(4):
         b, hq, i = int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(w.k))
         h = hq // grp
-        say(f"[full verify] b={b} hq={hq} row={i}")
+        say(f"[full verify] {name} b={b} hq={hq} row={i}")
         K, V = G.kv_slice(w, "k", b, h), G.kv_slice(w, "v", b, h)
         Kw, Vw = G.window_kv(w, "k", b, h), G.window_kv(w, "v", b, h)
         o, _ = OA.decode(Q[b, hq:hq + 1, i], K[None], V[None], w.d ** -0.5, Kw[None, :i + 1], Vw[None, :i + 1])
