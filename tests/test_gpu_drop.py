@@ -112,3 +112,41 @@ def test_keep_all_decode_equals_dense_decode():
     torch.cuda.synchronize()
     assert np.array_equal(ckv.kept_idx.cpu().numpy(), np.broadcast_to(np.arange(w.N), (w.B, w.Hkv, w.N)))
     assert torch.equal(ckv.k_kept, T(K, torch.bfloat16))
+
+
+def test_full_size_kept_row_decode_sampled():
+    """Decode over kept rows at the token-dropping workload's full size (B4, 32/8
+    heads, 32768 kept rows of 131072, d 128) plus a ragged tail, in the launch
+    configuration the benchmark times; sampled (sequence, q-head) outputs against
+    the oracle.  The kept rows are seeded rows of the layer (the decode reads the
+    gathered rows only; selection is checked on the reduced shapes above)."""
+    w = C.DROP
+    keep = L.vc_drop_keep_count(w.keep_ratio, w.N)
+    tl = 17
+    ckv = L.Ckv("drop", w.B, w.Hkv, w.d, keep, keep_ratio=w.keep_ratio, kv_dtype="bf16", tail_cap=w.k)
+    say("[full drop decode] generating inputs")
+    kept = {}
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            K, V = G.kv_slice(w, "k", b, h)[:keep], G.kv_slice(w, "v", b, h)[:keep]
+            ckv.k_kept[b, h] = T(K, torch.bfloat16)
+            ckv.v_kept[b, h] = T(V, torch.bfloat16)
+            kept[b, h] = (np32(ckv.k_kept[b, h]), np32(ckv.v_kept[b, h]))
+            ckv.tail_k[b, h] = T(G.window_kv(w, "k", b, h), torch.bfloat16)
+            ckv.tail_v[b, h] = T(G.window_kv(w, "v", b, h), torch.bfloat16)
+    ckv.n_main = keep
+    ckv.tail_len = tl
+    Q = G.full_window_q(w)[:, :, tl - 1]
+    out = torch.empty(w.B, w.Hq, w.d, device="cuda", dtype=torch.bfloat16)
+    L.vc_decode_attn_compressed(ckv, T(Q, torch.bfloat16), out)
+    torch.cuda.synchronize()
+    tk, tv = np32(ckv.tail_k), np32(ckv.tail_v)
+    rng = np.random.default_rng(5)
+    grp = w.Hq // w.Hkv
+    for _ in range(4):
+        b, hq = int(rng.integers(w.B)), int(rng.integers(w.Hq))
+        h = hq // grp
+        say(f"[full drop decode] b={b} hq={hq}")
+        K, V = kept[b, h]
+        o, _ = OA.decode(Q[b, hq:hq + 1], K[None], V[None], w.d ** -0.5, tk[b, h][None, :tl], tv[b, h][None, :tl])
+        assert_close(np32(out[b, hq]), o[0], 'bf16')
