@@ -35,8 +35,18 @@ __global__ void head_mean_kernel(const T* o, int B, int Hq, int k, int d, int64_
   int c = static_cast<int>(e % d);
   int64_t r = e / d;
   int b = static_cast<int>(r / k), i = static_cast<int>(r % k);
+  const int64_t base = b * sb + i * si + c;
+  // eight loads in flight, summed in head order
   float s = 0.f;
-  for (int h = 0; h < Hq; ++h) s += Elem<T>::load(o, b * sb + h * sh + i * si + c);
+  int h = 0;
+  for (; h + 8 <= Hq; h += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = Elem<T>::load(o, base + (h + j) * sh);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += v[j];
+  }
+  for (; h < Hq; ++h) s += Elem<T>::load(o, base + h * sh);
   u[e] = s / static_cast<float>(Hq);
 }
 
