@@ -24,7 +24,8 @@
 // * S^T = K_hat Q^T for two 16-token tiles, online softmax per q-head in base 2 with
 //   a lazy rescale (only when the block maximum exceeds the running one by more than
 //   8, i.e. probabilities stay below 2^8), probabilities rounded to f16, then
-//   O^T += V_hat^T P^T.  The probabilities stay in the lanes that produced them: the
+//   O^T += V_hat^T P^T; the denominators are the sums of the same rounded
+//   probabilities, formed on the matrix cores.  The probabilities stay in the lanes that produced them: the
 //   S^T layout of two 16-token tiles is the B-operand layout of the 32-token P.V
 //   product once both operands enumerate the block's tokens in the same order;
 // * within an operand the order of the contraction index is free as long as both
@@ -142,12 +143,12 @@ __device__ __forceinline__ constexpr int vorder(int t) {
 template <int VB>
 __device__ __forceinline__ void vpairs(uint32_t fa, uint32_t fb, uint32_t (&out)[8]) {
   if constexpr (VB == 4) {
-    const uint32_t la = (fa << 4) & 0xF0F0F0F0u, ha = fa & 0xF0F0F0F0u;
-    const uint32_t lb = (fb << 4) & 0xF0F0F0F0u, hb = fb & 0xF0F0F0F0u;
-    const uint32_t x0 = __builtin_amdgcn_perm(lb, la, 0x05010400u);  // a0 b0 a2 b2
-    const uint32_t x1 = __builtin_amdgcn_perm(lb, la, 0x07030602u);  // a4 b4 a6 b6
-    const uint32_t y0 = __builtin_amdgcn_perm(hb, ha, 0x05010400u);  // a1 b1 a3 b3
-    const uint32_t y1 = __builtin_amdgcn_perm(hb, ha, 0x07030602u);  // a5 b5 a7 b7
+    const uint32_t w0 = __builtin_amdgcn_perm(fb, fa, 0x05010400u);  // bytes a.0 b.0 a.1 b.1
+    const uint32_t w1 = __builtin_amdgcn_perm(fb, fa, 0x07030602u);  // bytes a.2 b.2 a.3 b.3
+    const uint32_t x0 = (w0 << 4) & 0xF0F0F0F0u;  // a0 b0 a2 b2
+    const uint32_t x1 = (w1 << 4) & 0xF0F0F0F0u;  // a4 b4 a6 b6
+    const uint32_t y0 = w0 & 0xF0F0F0F0u;         // a1 b1 a3 b3
+    const uint32_t y1 = w1 & 0xF0F0F0F0u;         // a5 b5 a7 b7
     out[0] = kmagic(x0, kSel01);
     out[1] = kmagic(x0, kSel23);
     out[2] = kmagic(x1, kSel01);
@@ -325,7 +326,11 @@ decode_mfma_kernel(DecodeArgs a) {
   // V zero-points: sum over tokens of p * z, the same for every channel of a field's
   // group, so one product per block; added to every channel tile at the end
   f4_t accz = f4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  // softmax denominators: the column sums of the f16 probabilities that enter the
+  // P.V product (one more product with an all-ones A operand, so every row of a
+  // column holds the column's sum)
+  f4_t accl = f4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;
   // the score operands of one K group: the queries times the group's scales (the B
   // operand of the scores) and sum_c q_c z_c - 64 sum_c qt_c per q-head column
   struct KQ {
@@ -490,19 +495,22 @@ decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] *= al;
       accz *= al;
-      l *= al;
+      accl *= al;
       m = mn;
     }
     float p[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       p[j] = __builtin_amdgcn_exp2f(s8[j] - m);  // v_exp_f32: results below 2^-126 flush to 0
-      l += p[j];
     }
     uint32_t pw[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) pw[j] = pack_h2(p[2 * j], p[2 * j + 1]);
     const h8_t bp = __builtin_bit_cast(h8_t, pw);
+    {
+      const uint32_t one2[4] = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};  // f16 1.0
+      accl = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, one2), bp, accl, 0, 0, 0);
+    }
 
     // ---- O^T[8 (4 kb' + i) + vorder(t)][n] += V_hat^T P^T over the block's 32 tokens
     uint32_t sv2[4], nsv2[4], zv2[4], vp[4][8];
@@ -593,8 +601,7 @@ decode_mfma_kernel(DecodeArgs a) {
   __syncthreads();  // every wave's copies have landed before the ring is reused
 
   // ---- merge the 4 waves in LDS, write this split's partial
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  const float l = accl[0];
   if (kb == 0) {
     sh_m[wave][n] = m;
     sh_l[wave][n] = l;
