@@ -803,10 +803,9 @@ extern "C" vc_status vc_verify_attn_full(const void* q, const void* k_cache, con
     // Row blocks: 4 waves of one 16-row tile (up to 64 rows) or two (128 rows per
     // workgroup), two workgroups per CU with a 2-tile ring; for 128 < M <= 256 one
     // block of 8 waves of two tiles each and a 4-tile ring (one workgroup per CU), so
-    // K and V are read once instead of twice (three 64-row blocks for M = 160 were
-    // ~15% slower).  Larger M: as many 128-row blocks as needed (64-row blocks for
-    // M = 320, or 256-row ones, were slower).  The arithmetic of a row does not depend
-    // on the block shape.
+    // K and V are read once instead of twice.  Larger M: as many 128-row blocks as
+    // needed (64-row blocks for M = 320, or 256-row ones, were slower).  The arithmetic
+    // of a row does not depend on the block shape.
     const int W = M > 128 && M <= 256 ? 8 : 4;
     const int RT = M <= 16 * W ? 1 : 2;
     const int nblk = static_cast<int>(cdiv(M, 16 * W * RT));
