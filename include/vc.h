@@ -114,7 +114,44 @@ typedef struct {
   void* tail_v;
   int64_t tail_cap;
   int64_t tail_len;     /* live tail rows (or their maximum) */
+  int32_t flags;        /* VC_CKV_* bits below, 0 for the defaults */
 } vc_ckv;
+
+/* vc_ckv.flags.
+ * VC_CKV_DECODE_F32: vc_decode_attn_compressed keeps every operand in float32 (the
+ *   generic kernel) instead of the f16 matrix-core operands of the fast path.  Set
+ *   it for a quantized cache outside the f16 domain stated at that call. */
+enum { VC_CKV_DECODE_F32 = 1 };
+
+/* Arrays of a vc_ckv, in the order vc_ckv_sizes reports them. */
+typedef enum {
+  VC_CKV_K_CODES = 0,
+  VC_CKV_V_CODES,
+  VC_CKV_K_SCALE,
+  VC_CKV_K_ZERO,
+  VC_CKV_V_SCALE,
+  VC_CKV_V_ZERO,
+  VC_CKV_K_KEPT,
+  VC_CKV_V_KEPT,
+  VC_CKV_KEPT_IDX,
+  VC_CKV_TAIL_K,
+  VC_CKV_TAIL_V,
+  VC_CKV_NARRAYS
+} vc_ckv_array;
+
+/* Byte size of every device array a vc_ckv descriptor points to, from its method,
+ * bits, group, param_dtype, kv_dtype, B, Hkv, d, capacity and tail_cap (the layouts
+ * above; the pointers and live lengths are not read).  out_bytes[VC_CKV_NARRAYS]
+ * receives the sizes indexed by vc_ckv_array; arrays the method does not use are
+ * 0 (the codes and parameters for VC_DROP_TOPK, the kept rows and positions for
+ * VC_QUANT_KIVI), and so are the tail arrays when tail_cap is 0.  A caller
+ * allocates each array with exactly this many bytes.  The uniform compressor
+ * interface of the summary page ("What the paper found"): one call sizes the
+ * storage of either family.  VC_ERR_INVALID_ARG for an invalid descriptor (bits
+ * outside {2, 3, 4, 8, 16}, a group that does not divide d, d * bits not a
+ * multiple of 32, a capacity that is not a multiple of the group, negative sizes);
+ * out_bytes is then left unchanged. */
+vc_status vc_ckv_sizes(const vc_ckv* ckv, size_t* out_bytes);
 
 /* ---------------------------------------------------------------------------
  * Compression (summary page, "What the paper found": one compressor interface
@@ -148,7 +185,9 @@ int64_t vc_drop_keep_count(float keep_ratio, int64_t N);
  * vc_drop_scores: k bf16/f32 (kv_dtype) [B, Hkv, N, d], probes bf16 [Hkv, P, d]
  *   -> scores float32 [B, Hkv, N].
  * vc_drop_select: scores float32 [B, Hkv, N] -> kept_idx int32 [B, Hkv, n_keep]
- *   (top n_keep, ties to the lower position, ascending).  n_keep <= N.
+ *   (top n_keep, ties to the lower position, ascending).  n_keep <= N.  Scores
+ *   are ranked as numbers: negative scores are allowed, -0.0 equals +0.0, and a NaN
+ *   ranks below every other score (NaNs among themselves by position).
  * vc_gather_rows: src kv_dtype [B, Hkv, src_rows, d], idx int32 [B, Hkv, n]
  *   -> dst [B, Hkv, dst_rows, d] rows [0, n).  Every idx must be < src_rows. */
 vc_status vc_drop_scores(const void* k, int32_t kv_dtype, const void* probes, int32_t B, int32_t Hkv,
@@ -172,11 +211,26 @@ vc_status vc_gather_rows(const void* src, int32_t kv_dtype, int32_t B, int32_t H
  * kept rows -- followed by tail rows [0, tail_len):
  *   s_n = (q . k_n) * sm_scale, o = sum_n softmax(s)_n v_n, lse = ln sum_n exp(s_n).
  * main_lens / tail_lens: device int32 [B] per-sequence lengths, or NULL to use
- * ckv->n_main / ckv->tail_len for every sequence (when given, every entry must be
- * at most ckv->n_main / ckv->tail_len; for quantization main lengths are
- * multiples of the group).  A sequence with no rows at all gets o = 0 and
+ * ckv->n_main / ckv->tail_len for every sequence (when given, ckv->n_main and
+ * ckv->tail_len are the largest lengths of the call, and every entry is clamped
+ * to [0, ckv->n_main] / [0, ckv->tail_len] on the device; for quantization main
+ * lengths are multiples of the group).  A sequence with no rows at all gets o = 0 and
  * lse = -inf.  out kv_dtype [B, Hq, d]; lse float32 [B, Hq] or NULL.
  * Accumulation is float32.
+ *
+ * Precision.  A quantized bf16 cache with d = 128, Hq/Hkv <= 16, 2/3/4-bit K and V
+ * codes, group 16, 32, 64 or 128 and a capacity that is a multiple of 32 runs on f16
+ * matrix cores unless ckv->flags has VC_CKV_DECODE_F32: the operands q_c * sm_scale *
+ * log2(e) (and its products with the K scales), the zero-points, the V scales times
+ * 64 and the probabilities are rounded to f16 (11 significant bits) and the products
+ * accumulate in float32.  Range: every |z| and 64 * s_V must be at most 65504.
+ * Accuracy: each score carries an error of about 2^-10 * sm_scale * sum_c |q_c k_c|
+ * (the f16 rounding of its terms) and the output that error times the spread of the
+ * values, plus about 2^-11 |v|.  For keys, values and queries of unit scale (N(0,1)
+ * entries, x10 on a few outlier channels) that is ~1e-4, inside the 2e-2 bar; it
+ * grows with the square of the scale and leaves the bar near twice it.  For larger
+ * activations set VC_CKV_DECODE_F32 (float32 operands throughout, the generic
+ * kernel); every other cache runs in float32 as well.
  * ------------------------------------------------------------------------- */
 vc_status vc_decode_attn_compressed(const vc_ckv* ckv, const void* q, int32_t Hq, float sm_scale,
                                     const int32_t* main_lens, const int32_t* tail_lens,
@@ -190,7 +244,10 @@ size_t vc_decode_workspace_bytes(const vc_ckv* ckv, int32_t Hq);
  *
  * k_cache, v_cache kv_dtype [B, Hkv, cache_rows, d] hold the full cache with the
  * window's own keys/values already written at rows [L, L + k), L = the sequence's
- * context length (ctx_lens[b], or ctx_len for all when ctx_lens is NULL).  q
+ * context length (ctx_lens[b], or ctx_len for all when ctx_lens is NULL).  With
+ * ctx_lens, ctx_len is the longest context of the call: it sizes the splits and the
+ * workspace, and every entry is clamped to [0, ctx_len] on the device (an entry
+ * above ctx_len is read as ctx_len).  q
  * kv_dtype [B, Hq, k, d]; row i of sequence b attends to cache rows [0, L + i].
  * out kv_dtype [B, Hq, k, d]; lse float32 [B, Hq, k] or NULL.  L + k <= cache_rows.
  * bf16 inputs run on bf16 matrix cores with float32 accumulation; f32 inputs run
@@ -353,6 +410,28 @@ vc_status vc_stage_full_kv_file(vc_file_stager* st, int32_t fd, int64_t k_offset
                                 int64_t dev_rows, int64_t tok_begin, int64_t tok_end, void* copy_stream, void* done,
                                 int64_t* ticket);
 vc_status vc_file_stager_wait(vc_file_stager* st, int64_t ticket);
+
+/* ---------------------------------------------------------------------------
+ * One workspace query for the calls that take a workspace (the boundary's single
+ * size query; the per-call *_workspace_bytes functions return the same numbers).
+ * VC_OP_COMPRESS reads ckv, n_tokens, n_probes; VC_OP_DECODE reads ckv, Hq;
+ * VC_OP_VERIFY reads B, Hq, Hkv, d, k, max_len, split_tokens; VC_OP_LOGITS reads
+ * rows, vocab.  Returns 0 for an unknown op, a NULL query or shapes the matching
+ * call would reject.
+ * ------------------------------------------------------------------------- */
+typedef enum { VC_OP_COMPRESS = 1, VC_OP_DECODE = 2, VC_OP_VERIFY = 3, VC_OP_LOGITS = 4 } vc_op;
+typedef struct {
+  const vc_ckv* ckv;
+  int64_t n_tokens;
+  int32_t n_probes;
+  int32_t Hq;
+  int32_t B, Hkv, d, k;
+  int64_t max_len;
+  int32_t split_tokens;
+  int64_t rows;
+  int32_t vocab;
+} vc_ws_query;
+size_t vc_workspace_size(int32_t op, const vc_ws_query* query);
 
 /* Message of the last failed call on this thread ("" if none).  Valid until the
  * next vc_* call on the same thread. */

@@ -1,8 +1,10 @@
 """ctypes declarations of include/vc.h and thin wrappers taking torch tensors."""
+import atexit
 import copy
 import ctypes
 import os
 import sys
+import weakref
 
 import torch
 
@@ -35,12 +37,27 @@ class vc_ckv(ctypes.Structure):
                 ("k_codes", c_p), ("v_codes", c_p), ("k_scale", c_p), ("k_zero", c_p),
                 ("v_scale", c_p), ("v_zero", c_p), ("k_kept", c_p), ("v_kept", c_p),
                 ("kept_idx", c_p), ("tail_k", c_p), ("tail_v", c_p),
-                ("tail_cap", c_i64), ("tail_len", c_i64)]
+                ("tail_cap", c_i64), ("tail_len", c_i64), ("flags", c_i32)]
+
+
+VC_CKV_DECODE_F32 = 1
+# vc_ckv_array: order of the sizes vc_ckv_sizes reports
+CKV_ARRAYS = ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero", "k_kept", "v_kept", "kept_idx",
+              "tail_k", "tail_v")
+VC_OP_COMPRESS, VC_OP_DECODE, VC_OP_VERIFY, VC_OP_LOGITS = 1, 2, 3, 4
+
+
+class vc_ws_query(ctypes.Structure):
+    _fields_ = [("ckv", ctypes.POINTER(vc_ckv)), ("n_tokens", c_i64), ("n_probes", c_i32), ("Hq", c_i32),
+                ("B", c_i32), ("Hkv", c_i32), ("d", c_i32), ("k", c_i32), ("max_len", c_i64),
+                ("split_tokens", c_i32), ("rows", c_i64), ("vocab", c_i32)]
 
 
 _P = ctypes.POINTER(vc_ckv)
 # name -> (restype, argtypes); every symbol declared in include/vc.h
 _DECLS = {
+    "vc_ckv_sizes": (c_i32, [_P, ctypes.POINTER(c_sz)]),
+    "vc_workspace_size": (c_sz, [c_i32, ctypes.POINTER(vc_ws_query)]),
     "vc_compress": (c_i32, [_P, c_p, c_p, c_i64, c_i64, c_i64, c_i64, c_p, c_i32, c_f32, c_p, c_sz, c_p]),
     "vc_compress_workspace_bytes": (c_sz, [_P, c_i64, c_i32]),
     "vc_drop_keep_count": (c_i64, [c_f32, c_i64]),
@@ -135,31 +152,35 @@ class Ckv:
     their source positions.  Both carry a full-precision tail of tail_cap rows."""
 
     def __init__(self, method, B, Hkv, d, capacity, *, k_bits=4, v_bits=4, group=32, param_dtype="bf16",
-                 kv_dtype="bf16", keep_ratio=1.0, tail_cap=0, device="cuda"):
+                 kv_dtype="bf16", keep_ratio=1.0, tail_cap=0, flags=0, device="cuda"):
         self.method = {"quant": VC_QUANT_KIVI, "drop": VC_DROP_TOPK}[method]
         self.B, self.Hkv, self.d, self.capacity = B, Hkv, d, capacity
         self.k_bits, self.v_bits, self.group = k_bits, v_bits, group
         self.param_dtype, self.kv_dtype, self.keep_ratio = param_dtype, kv_dtype, keep_ratio
         self.tail_cap = tail_cap
+        self.flags = flags
         self.n_main = 0
         self.tail_len = 0
+        for name in CKV_ARRAYS:
+            setattr(self, name, None)
+        # byte sizes from the library (vc_ckv_sizes); the shapes below are the views
+        # the header's layouts give those bytes
+        sizes = vc_ckv_sizes(self)
         kvt, pt = _TORCH[kv_dtype], _TORCH[param_dtype]
-        z = dict(device=device)
-        self.k_codes = self.v_codes = self.k_scale = self.k_zero = self.v_scale = self.v_zero = None
-        self.k_kept = self.v_kept = self.kept_idx = None
-        if self.method == VC_QUANT_KIVI:
-            self.k_codes = torch.zeros(B, Hkv, capacity, d * k_bits // 32, dtype=torch.int32, **z)
-            self.v_codes = torch.zeros(B, Hkv, capacity, d * v_bits // 32, dtype=torch.int32, **z)
-            self.k_scale = torch.zeros(B, Hkv, capacity // group, d, dtype=pt, **z)
-            self.k_zero = torch.zeros(B, Hkv, capacity // group, d, dtype=pt, **z)
-            self.v_scale = torch.zeros(B, Hkv, capacity, d // group, dtype=pt, **z)
-            self.v_zero = torch.zeros(B, Hkv, capacity, d // group, dtype=pt, **z)
-        else:
-            self.k_kept = torch.zeros(B, Hkv, capacity, d, dtype=kvt, **z)
-            self.v_kept = torch.zeros(B, Hkv, capacity, d, dtype=kvt, **z)
-            self.kept_idx = torch.zeros(B, Hkv, capacity, dtype=torch.int32, **z)
-        self.tail_k = torch.zeros(B, Hkv, tail_cap, d, dtype=kvt, **z) if tail_cap else None
-        self.tail_v = torch.zeros(B, Hkv, tail_cap, d, dtype=kvt, **z) if tail_cap else None
+        shapes = {
+            "k_codes": (torch.int32, (B, Hkv, capacity, d * k_bits // 32)),
+            "v_codes": (torch.int32, (B, Hkv, capacity, d * v_bits // 32)),
+            "k_scale": (pt, (B, Hkv, capacity // group, d)), "k_zero": (pt, (B, Hkv, capacity // group, d)),
+            "v_scale": (pt, (B, Hkv, capacity, d // group)), "v_zero": (pt, (B, Hkv, capacity, d // group)),
+            "k_kept": (kvt, (B, Hkv, capacity, d)), "v_kept": (kvt, (B, Hkv, capacity, d)),
+            "kept_idx": (torch.int32, (B, Hkv, capacity)),
+            "tail_k": (kvt, (B, Hkv, tail_cap, d)), "tail_v": (kvt, (B, Hkv, tail_cap, d)),
+        }
+        for name in CKV_ARRAYS:
+            nbytes = sizes[name]
+            if nbytes:
+                dt, shape = shapes[name]
+                setattr(self, name, torch.zeros(nbytes, dtype=torch.uint8, device=device).view(dt).view(shape))
 
     def struct(self) -> vc_ckv:
         return vc_ckv(self.method, self.k_bits, self.v_bits, self.group,
@@ -168,7 +189,8 @@ class Ckv:
                       self.B, self.Hkv, self.d, self.capacity, self.n_main,
                       _ptr(self.k_codes), _ptr(self.v_codes), _ptr(self.k_scale), _ptr(self.k_zero),
                       _ptr(self.v_scale), _ptr(self.v_zero), _ptr(self.k_kept), _ptr(self.v_kept),
-                      _ptr(self.kept_idx), _ptr(self.tail_k), _ptr(self.tail_v), self.tail_cap, self.tail_len)
+                      _ptr(self.kept_idx), _ptr(self.tail_k), _ptr(self.tail_v), self.tail_cap, self.tail_len,
+                      self.flags)
 
     def batch_view(self, b: int) -> "Ckv":
         """Descriptor of sequence b alone (B = 1) over the same device storage."""
@@ -191,6 +213,21 @@ class Ckv:
             return codes + params
         eb = 4 if self.kv_dtype == "f32" else 2
         return bh * n * self.d * 2 * eb
+
+
+def vc_ckv_sizes(ckv: "Ckv") -> dict:
+    """Byte size of every array of the descriptor (vc_ckv_sizes), by array name."""
+    out = (c_sz * len(CKV_ARRAYS))()
+    _check(lib.vc_ckv_sizes(ctypes.byref(ckv.struct()), out), "vc_ckv_sizes")
+    return dict(zip(CKV_ARRAYS, (int(x) for x in out)))
+
+
+def vc_workspace_size(op: int, *, ckv=None, n_tokens=0, n_probes=0, Hq=0, B=0, Hkv=0, d=0, k=0, max_len=0,
+                      split_tokens=0, rows=0, vocab=0) -> int:
+    c = ckv.struct() if ckv is not None else None
+    q = vc_ws_query(ctypes.pointer(c) if c is not None else None, n_tokens, n_probes, Hq, B, Hkv, d, k, max_len,
+                    split_tokens, rows, vocab)
+    return lib.vc_workspace_size(op, ctypes.byref(q))
 
 
 def vc_compress_workspace_bytes(ckv: Ckv, n_tokens: int, n_probes: int) -> int:
@@ -366,15 +403,31 @@ def vc_join_planes(anchor: "Ckv", k_resid, v_resid, full: "Ckv", n_tokens, *, st
                               ctypes.byref(full.struct()), n_tokens, _stream(stream)), "vc_join_planes")
 
 
+_LIVE_STAGERS = weakref.WeakSet()
+
+
+@atexit.register
+def _close_live_stagers():
+    """Joins the reader threads of every stager still open before the interpreter and
+    the HIP runtime shut down (a worker must not be inside a HIP call then)."""
+    for st in list(_LIVE_STAGERS):
+        try:
+            st.close()
+        except Exception:
+            pass
+
+
 class FileStager:
     """vc_file_stager: reader threads and pinned bounce buffers that stage full-KV rows
-    from a file (the remote prefix cache stand-in) to the device."""
+    from a file (the remote prefix cache stand-in) to the device.  Closed by close(),
+    by the garbage collector, or at interpreter exit, whichever comes first."""
 
     def __init__(self, n_threads=8, chunk_bytes=16 << 20, n_buffers=16, max_bytes_per_s=0.0):
         h = c_p()
         _check(lib.vc_file_stager_create(n_threads, chunk_bytes, n_buffers, float(max_bytes_per_s),
                                          ctypes.byref(h)), "vc_file_stager_create")
         self.handle = h.value
+        _LIVE_STAGERS.add(self)
 
     def stage(self, fd, k_offset, v_offset, dev_k, dev_v, file_rows, tok_begin, tok_end, *, copy_stream=None,
               done=None):
@@ -395,8 +448,9 @@ class FileStager:
 
     def close(self):
         if self.handle:
-            _check(lib.vc_file_stager_destroy(self.handle), "vc_file_stager_destroy")
-            self.handle = None
+            h, self.handle = self.handle, None
+            _LIVE_STAGERS.discard(self)
+            _check(lib.vc_file_stager_destroy(h), "vc_file_stager_destroy")
 
     def __del__(self, _finalizing=sys.is_finalizing):
         if _finalizing():   # the HIP runtime may already be gone: leave it to the OS

@@ -67,6 +67,51 @@ using namespace vc;
 
 extern "C" const char* vc_last_error(void) { return g_err; }
 
+extern "C" vc_status vc_ckv_sizes(const vc_ckv* c, size_t* out_bytes) {
+  clear_error();
+  VC_REQUIRE(c && out_bytes, "ckv / out_bytes is NULL");
+  VC_REQUIRE(c->B > 0 && c->Hkv > 0 && c->d > 0, "bad B/Hkv/d (%d, %d, %d)", c->B, c->Hkv, c->d);
+  VC_REQUIRE(c->capacity >= 0 && c->tail_cap >= 0, "capacity / tail_cap must be non-negative");
+  VC_REQUIRE(valid_dtype(c->kv_dtype), "bad kv_dtype %d", c->kv_dtype);
+  size_t sz[VC_CKV_NARRAYS] = {};
+  const size_t bh = static_cast<size_t>(c->B) * c->Hkv, d = static_cast<size_t>(c->d);
+  const size_t cap = static_cast<size_t>(c->capacity), eb = dtype_bytes(c->kv_dtype);
+  if (c->method == VC_QUANT_KIVI) {
+    auto ok_bits = [](int b) { return b == 2 || b == 3 || b == 4 || b == 8 || b == 16; };
+    VC_REQUIRE(ok_bits(c->k_bits) && ok_bits(c->v_bits), "bits must be one of 2,3,4,8,16 (got K %d, V %d)",
+               c->k_bits, c->v_bits);
+    VC_REQUIRE(c->group > 0 && c->d % c->group == 0, "group %d must divide d %d", c->group, c->d);
+    VC_REQUIRE((c->d * c->k_bits) % 32 == 0 && (c->d * c->v_bits) % 32 == 0, "d*bits must be a multiple of 32");
+    VC_REQUIRE(c->capacity % c->group == 0, "capacity %lld must be a multiple of group %d", (long long)c->capacity,
+               c->group);
+    VC_REQUIRE(valid_dtype(c->param_dtype), "bad param_dtype %d", c->param_dtype);
+    const size_t pb = dtype_bytes(c->param_dtype), G = static_cast<size_t>(c->group);
+    sz[VC_CKV_K_CODES] = bh * cap * (d * c->k_bits / 32) * 4;
+    sz[VC_CKV_V_CODES] = bh * cap * (d * c->v_bits / 32) * 4;
+    sz[VC_CKV_K_SCALE] = sz[VC_CKV_K_ZERO] = bh * (cap / G) * d * pb;
+    sz[VC_CKV_V_SCALE] = sz[VC_CKV_V_ZERO] = bh * cap * (d / G) * pb;
+  } else {
+    VC_REQUIRE(c->method == VC_DROP_TOPK, "unknown ckv.method %d", c->method);
+    sz[VC_CKV_K_KEPT] = sz[VC_CKV_V_KEPT] = bh * cap * d * eb;
+    sz[VC_CKV_KEPT_IDX] = bh * cap * sizeof(int32_t);
+  }
+  sz[VC_CKV_TAIL_K] = sz[VC_CKV_TAIL_V] = bh * static_cast<size_t>(c->tail_cap) * d * eb;
+  memcpy(out_bytes, sz, sizeof(sz));
+  return VC_OK;
+}
+
+extern "C" size_t vc_workspace_size(int32_t op, const vc_ws_query* q) {
+  if (!q) return 0;
+  switch (op) {
+    case VC_OP_COMPRESS: return q->ckv ? vc_compress_workspace_bytes(q->ckv, q->n_tokens, q->n_probes) : 0;
+    case VC_OP_DECODE: return q->ckv ? vc_decode_workspace_bytes(q->ckv, q->Hq) : 0;
+    case VC_OP_VERIFY:
+      return vc_verify_workspace_bytes(q->B, q->Hq, q->Hkv, q->d, q->k, q->max_len, q->split_tokens);
+    case VC_OP_LOGITS: return q->rows > 0 && q->vocab > 0 ? vc_logits_workspace_bytes(q->rows, q->vocab) : 0;
+    default: return 0;
+  }
+}
+
 extern "C" size_t vc_compress_workspace_bytes(const vc_ckv* c, int64_t n_tokens, int32_t n_probes) {
   if (!c || c->method != VC_DROP_TOPK || n_tokens <= 0 || n_probes <= 0 || c->B <= 0 || c->Hkv <= 0) return 0;
   size_t scores = align_up(static_cast<size_t>(c->B) * c->Hkv * n_tokens * sizeof(float), 256);

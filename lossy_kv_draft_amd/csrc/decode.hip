@@ -65,8 +65,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_generic_kernel(DecodeArgs 
   const int hk = bh % a.Hkv;
   const int tid = threadIdx.x;
 
-  const int64_t main_len = a.main_lens ? a.main_lens[b] : a.n_main;
-  const int64_t tail_len = a.tail_lens ? a.tail_lens[b] : a.tail_len;
+  const int64_t main_len = dec_main_len(a, b);
+  const int64_t tail_len = dec_tail_len(a, b);
   const int64_t total = main_len + tail_len;
   const int64_t start = static_cast<int64_t>(split) * a.chunk;
   const int64_t end = min(total, start + a.chunk);

@@ -38,11 +38,13 @@ struct DecodeArgs {
   float* part_ml;  // [B*Hkv][splits][H][2]   running max (base 2) and sum
 };
 
+// per-sequence lengths, clamped to [0, n_main] and [0, tail_len]
 __device__ __forceinline__ int64_t dec_main_len(const DecodeArgs& a, int b) {
-  return a.main_lens ? a.main_lens[b] : a.n_main;
+  return a.main_lens ? min(max(static_cast<int64_t>(a.main_lens[b]), static_cast<int64_t>(0)), a.n_main) : a.n_main;
 }
 __device__ __forceinline__ int64_t dec_tail_len(const DecodeArgs& a, int b) {
-  return a.tail_lens ? a.tail_lens[b] : a.tail_len;
+  return a.tail_lens ? min(max(static_cast<int64_t>(a.tail_lens[b]), static_cast<int64_t>(0)), a.tail_len)
+                     : a.tail_len;
 }
 
 // Tail rows (full precision, bf16, d = 128) of one (sequence, kv-head), H <= 16

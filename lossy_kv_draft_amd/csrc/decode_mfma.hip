@@ -635,6 +635,7 @@ decode_mfma_kernel(DecodeArgs a) {
 // ------------------------------------------------------------------ dispatch
 
 bool decode_mfma_supported(const vc_ckv* c, int H) {
+  if (c->flags & VC_CKV_DECODE_F32) return false;  // the caller asked for float32 operands
   if (c->method != VC_QUANT_KIVI || c->kv_dtype != VC_BF16 || c->d != 128 || H < 1 || H > 16) return false;
   auto ok_bits = [](int b) { return b == 2 || b == 3 || b == 4; };
   if (!ok_bits(c->k_bits) || !ok_bits(c->v_bits)) return false;

@@ -204,6 +204,16 @@ __global__ void __launch_bounds__(256) drop_scores_kernel(const T* k, const bf16
 // ---- top-k selection: one block per (sequence, kv-head)
 constexpr int kSelThreads = 1024;
 
+// Unsigned key whose order is the numeric order of the score: a negative float's
+// bits are flipped, a non-negative one gets its sign bit set; -0.0 is read as +0.0
+// (equal scores) and every NaN as key 0, below -inf.
+__device__ __forceinline__ uint32_t select_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0u;
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 __global__ void __launch_bounds__(kSelThreads) drop_select_kernel(const float* scores, int64_t N, int64_t n_keep,
                                                                   int32_t* kept, int64_t kept_pitch) {
   __shared__ unsigned hist[256];
@@ -227,7 +237,7 @@ __global__ void __launch_bounds__(kSelThreads) drop_select_kernel(const float* s
     const uint32_t prefix = s_prefix;
     const uint32_t pmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
     for (int64_t n = tid; n < N; n += kSelThreads) {
-      uint32_t key = __float_as_uint(sc[n]);
+      uint32_t key = select_key(sc[n]);
       if ((key & pmask) == (prefix & pmask)) atomicAdd(&hist[(key >> shift) & 0xFF], 1u);
     }
     __syncthreads();
@@ -251,7 +261,7 @@ __global__ void __launch_bounds__(kSelThreads) drop_select_kernel(const float* s
   const int lane = tid & 63, wave = tid >> 6;
   for (int64_t n0 = 0; n0 < N; n0 += kSelThreads) {
     int64_t n = n0 + tid;
-    uint32_t key = n < N ? __float_as_uint(sc[n]) : 0u;
+    uint32_t key = n < N ? select_key(sc[n]) : 0u;
     bool gt = n < N && key > thr;
     bool eq = n < N && key == thr;
     unsigned long long bgt = __ballot(gt), beq = __ballot(eq);

@@ -31,7 +31,7 @@
 
 #include <unistd.h>
 
-#include "common.h"
+#include "host_common.h"
 
 namespace vc {
 

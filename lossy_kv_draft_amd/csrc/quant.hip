@@ -14,7 +14,8 @@
 // bit for bit.
 //
 // One workgroup quantizes one tile of G tokens x d channels of one (sequence,
-// kv-head): the tile is staged in LDS as float32, parameters are computed by one
+// kv-head): the tile is staged in LDS in the source type (bf16 values convert to
+// float32 exactly when read), parameters are computed by one
 // thread per K channel / per (token, V group), then each thread builds whole
 // 32-bit words of packed codes (a word may hold a code that straddles into the
 // next word; both words compute that code).  HBM-bound: each input element is
@@ -25,7 +26,7 @@
 namespace vc {
 
 constexpr int kQuantThreads = 256;
-constexpr int kQuantMaxTile = 8192;  // G * d floats per tile (32 KiB of LDS)
+constexpr int kQuantMaxTileBytes = 32768;  // G * d source elements per tile (32 KiB of LDS)
 
 template <typename T>
 __device__ __forceinline__ void group_params(float mn, float mx, int bits, int param_f32,
@@ -81,9 +82,9 @@ quant_pack_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src, int6
                   int64_t capacity, int64_t dst_begin, uint32_t* __restrict__ k_codes,
                   uint32_t* __restrict__ v_codes, void* k_scale, void* k_zero, void* v_scale,
                   void* v_zero) {
-  extern __shared__ float smem[];
-  float* tile = smem;                 // [G][d]
-  float* ks = tile + G * d;           // [d]
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  T* tile = reinterpret_cast<T*>(smem_raw);                                  // [G][d]
+  float* ks = reinterpret_cast<float*>(smem_raw + static_cast<size_t>(G) * d * sizeof(T));  // [d]
   float* kz = ks + d;                 // [d]
   float* vs = kz + d;                 // [G][d/G]
   float* vz = vs + d;                 // [G][d/G]  (G * d/G == d)
@@ -98,14 +99,14 @@ quant_pack_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src, int6
 
   for (int pass = 0; pass < 2; ++pass) {
     const T* src = pass == 0 ? k_src : v_src;
-    for (int i = tid; i < n; i += kQuantThreads) tile[i] = Elem<T>::load(src, src_base + i);
+    for (int i = tid; i < n; i += kQuantThreads) tile[i] = src[src_base + i];
     __syncthreads();
     if (pass == 0) {
       // K: one group per channel over the tile's G tokens.
       for (int c = tid; c < d; c += kQuantThreads) {
-        float mn = tile[c], mx = tile[c];
+        float mn = Elem<T>::load(tile, c), mx = mn;
         for (int t = 1; t < G; ++t) {
-          float x = tile[t * d + c];
+          float x = Elem<T>::load(tile, t * d + c);
           mn = fminf(mn, x);
           mx = fmaxf(mx, x);
         }
@@ -121,11 +122,12 @@ quant_pack_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src, int6
       // V: one group per (token, G consecutive channels).
       for (int j = tid; j < G * vgroups; j += kQuantThreads) {
         int t = j / vgroups, g = j % vgroups;
-        const float* row = tile + t * d + g * G;
-        float mn = row[0], mx = row[0];
+        const T* row = tile + t * d + g * G;
+        float mn = Elem<T>::load(row, 0), mx = mn;
         for (int c = 1; c < G; ++c) {
-          mn = fminf(mn, row[c]);
-          mx = fmaxf(mx, row[c]);
+          const float x = Elem<T>::load(row, c);
+          mn = fminf(mn, x);
+          mx = fmaxf(mx, x);
         }
         float s, z;
         group_params<T>(mn, mx, v_bits, param_f32, s, z);
@@ -142,14 +144,14 @@ quant_pack_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src, int6
     uint32_t* codes = pass == 0 ? k_codes : v_codes;
     for (int j = tid; j < G * wpr; j += kQuantThreads) {
       int t = j / wpr, w = j % wpr;
-      const float* row = tile + t * d;
+      const T* row = tile + t * d;
       uint32_t word;
       if (pass == 0)
-        word = pack_word(w, bits, [&](int c) { return quant_code(row[c], ks[c], kz[c], bits); });
+        word = pack_word(w, bits, [&](int c) { return quant_code(Elem<T>::load(row, c), ks[c], kz[c], bits); });
       else
         word = pack_word(w, bits, [&](int c) {
           int g = c / G;
-          return quant_code(row[c], vs[t * vgroups + g], vz[t * vgroups + g], bits);
+          return quant_code(Elem<T>::load(row, c), vs[t * vgroups + g], vz[t * vgroups + g], bits);
         });
       codes[(static_cast<int64_t>(bh) * capacity + dst_tok0 + t) * wpr + w] = word;
     }
@@ -192,10 +194,12 @@ vc_status compress_quant(const vc_ckv* c, const void* k_src, const void* v_src, 
   VC_REQUIRE(dst_begin >= 0 && dst_begin % G == 0 && dst_begin + n_tokens <= c->capacity,
              "destination rows [%lld, %lld) exceed capacity %lld or are not group-aligned", (long long)dst_begin,
              (long long)(dst_begin + n_tokens), (long long)c->capacity);
-  VC_UNSUPPORTED(G * c->d <= kQuantMaxTile, "group*d = %d exceeds %d", G * c->d, kQuantMaxTile);
+  const size_t tile_bytes = static_cast<size_t>(G) * c->d * dtype_bytes(c->kv_dtype);
+  VC_UNSUPPORTED(tile_bytes <= kQuantMaxTileBytes, "group*d*element size = %zu bytes exceeds %d", tile_bytes,
+                 kQuantMaxTileBytes);
   if (n_tokens == 0) return VC_OK;
   dim3 grid(static_cast<unsigned>(n_tokens / G), static_cast<unsigned>(c->B * c->Hkv));
-  size_t lds = (static_cast<size_t>(G) * c->d + 4 * c->d) * sizeof(float);
+  size_t lds = tile_bytes + 4 * static_cast<size_t>(c->d) * sizeof(float);
   int pf32 = c->param_dtype == VC_F32;
   if (c->kv_dtype == VC_F32)
     hipLaunchKernelGGL(quant_pack_kernel<float>, grid, dim3(kQuantThreads), lds, stream,

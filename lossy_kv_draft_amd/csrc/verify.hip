@@ -62,6 +62,14 @@ struct VerifyArgs {
   float* part_ml; // [B*Hkv][splits][M][2]
 };
 
+// Context length of sequence b: ctx_lens[b] clamped to [0, ctx_len - ctx_off], plus
+// ctx_off (decode over kept rows passes row counts and ctx_off = -1); else ctx_len.
+__device__ __forceinline__ int64_t ver_ctx_len(const VerifyArgs& a, int b) {
+  if (!a.ctx_lens) return a.ctx_len;
+  const int64_t x = a.ctx_lens[b];
+  return min(max(x, static_cast<int64_t>(0)), a.ctx_len - a.ctx_off) + a.ctx_off;
+}
+
 union Pack16 {
   uint4 u;
   bf16x8_t v;
@@ -85,7 +93,7 @@ __global__ void __launch_bounds__(kVerThreads) verify_mfma_kernel(VerifyArgs a) 
   const int l16 = lane & 15, kb = lane >> 4;
   const int M = a.H * a.k;
   const int row0 = rblk * a.rows_per_block + wave * 16 * RT;
-  const int64_t L = a.ctx_lens ? a.ctx_lens[b] + a.ctx_off : a.ctx_len;
+  const int64_t L = ver_ctx_len(a, b);
   const int64_t limit = L + a.k;  // readable positions [0, limit)
   const int64_t s_begin = static_cast<int64_t>(split) * a.C;
   const int64_t s_end = min(s_begin + a.C, limit);
@@ -359,7 +367,7 @@ __device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int
   const int l16 = lane & 15, kb = lane >> 4;
   const int M = a.H * a.k;
   const int row0 = rblk * a.rows_per_block + wave * 16 * RT;
-  const int64_t L = a.ctx_lens ? a.ctx_lens[b] + a.ctx_off : a.ctx_len;
+  const int64_t L = ver_ctx_len(a, b);
   const int64_t limit = L + a.k;  // readable positions [0, limit)
   const int64_t s_begin = static_cast<int64_t>(split) * a.C;
   const int64_t s_end = min(s_begin + a.C, limit);
@@ -579,7 +587,7 @@ __global__ void __launch_bounds__(256) verify_f32_kernel(VerifyArgs a) {
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int M = a.H * a.k, d = a.d;
   if (row >= M) return;
-  const int64_t L = a.ctx_lens ? a.ctx_lens[b] + a.ctx_off : a.ctx_len;
+  const int64_t L = ver_ctx_len(a, b);
   const int64_t last = L + (row % a.k);
   const int64_t s_begin = static_cast<int64_t>(split) * a.C;
   const int64_t s_end = min(s_begin + a.C, last + 1);

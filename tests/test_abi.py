@@ -60,7 +60,8 @@ def test_decode_rejects_bad_arguments():
     q = torch.zeros(1, 8, 64)
     out = torch.zeros(1, 8, 64)
     ws = torch.zeros(1 << 20, dtype=torch.uint8)
-    c = _ckv(k_bits=5)
+    c = _ckv()
+    c.k_bits = 5
     assert "bits" in _bad(L.vc_decode_attn_compressed, c, q, out, ws=ws, stream=0)
     c = _ckv()
     c.n_main = 100  # not a multiple of the group
@@ -172,3 +173,74 @@ def test_gemm_rope_rejects_bad_arguments():
     i32 = torch.zeros(4, dtype=torch.int32)
     _bad(L.vc_gemm_bf16_rope, x, w, 4, 1, 16, 4, 8, i32, q, kv, kv, i32, stream=0)          # hd not a multiple of 16
     _bad(L.vc_gemm_bf16_rope, x, w, 4, 1, 16, 4, 16, i32, q, kv, kv, i32, theta=1.0, stream=0)
+
+
+def _layout_bytes(method, B, Hkv, d, cap, kb, vb, G, pdt, kvdt, tail_cap):
+    """The array sizes the header's layouts give, written out per array."""
+    pb = {"f32": 4, "bf16": 2}[pdt]
+    eb = {"f32": 4, "bf16": 2}[kvdt]
+    z = dict.fromkeys(L.CKV_ARRAYS, 0)
+    if method == "quant":
+        z["k_codes"] = B * Hkv * cap * (d * kb // 32) * 4
+        z["v_codes"] = B * Hkv * cap * (d * vb // 32) * 4
+        z["k_scale"] = z["k_zero"] = B * Hkv * (cap // G) * d * pb
+        z["v_scale"] = z["v_zero"] = B * Hkv * cap * (d // G) * pb
+    else:
+        z["k_kept"] = z["v_kept"] = B * Hkv * cap * d * eb
+        z["kept_idx"] = B * Hkv * cap * 4
+    z["tail_k"] = z["tail_v"] = B * Hkv * tail_cap * d * eb
+    return z
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8, 16])
+@pytest.mark.parametrize("pdt", ["f32", "bf16"])
+def test_ckv_sizes_match_the_layouts(bits, pdt):
+    for G, d, cap, tail in [(32, 128, 1024, 70), (64, 128, 32768, 0), (16, 64, 48, 5), (128, 128, 256, 1)]:
+        kb, vb = bits, {2: 3, 3: 2, 4: 8, 8: 4, 16: 2}[bits]
+        c = L.Ckv("quant", 3, 2, d, cap, k_bits=kb, v_bits=vb, group=G, param_dtype=pdt, kv_dtype="bf16",
+                  tail_cap=tail, device="cpu")
+        want = _layout_bytes("quant", 3, 2, d, cap, kb, vb, G, pdt, "bf16", tail)
+        assert L.vc_ckv_sizes(c) == want
+        for name in L.CKV_ARRAYS:  # the binding allocates exactly those bytes
+            t = getattr(c, name)
+            assert (0 if t is None else t.numel() * t.element_size()) == want[name], name
+
+
+@pytest.mark.parametrize("kvdt", ["f32", "bf16"])
+def test_ckv_sizes_drop(kvdt):
+    c = L.Ckv("drop", 4, 8, 128, 32768, keep_ratio=0.25, kv_dtype=kvdt, tail_cap=40, device="cpu")
+    want = _layout_bytes("drop", 4, 8, 128, 32768, 0, 0, 1, "f32", kvdt, 40)
+    assert L.vc_ckv_sizes(c) == want
+    assert c.k_codes is None and c.k_kept.shape == (4, 8, 32768, 128) and c.kept_idx.dtype == torch.int32
+
+
+def test_ckv_sizes_reject_invalid_descriptors():
+    c = _ckv()
+    for field, value in [("k_bits", 5), ("group", 48), ("capacity", 500), ("B", 0), ("tail_cap", -1),
+                         ("param_dtype", "f16")]:
+        bad = _ckv()
+        setattr(bad, field, value)
+        if field == "param_dtype":
+            st = bad.struct()
+            st.param_dtype = 7
+            out = (ctypes.c_size_t * len(L.CKV_ARRAYS))()
+            assert L._lib.lib.vc_ckv_sizes(ctypes.byref(st), out) == L._lib.VC_ERR_INVALID_ARG
+            continue
+        _bad(L.vc_ckv_sizes, bad)
+    assert L.vc_ckv_sizes(c)["k_codes"] == 2 * 512 * 4 * 4
+
+
+def test_workspace_size_query_equals_the_per_call_sizes():
+    c = _ckv(kv_dtype="bf16", param_dtype="bf16")
+    assert L.vc_workspace_size(L.VC_OP_DECODE, ckv=c, Hq=8) == L.vc_decode_workspace_bytes(c, 8) > 0
+    for args in [(8, 32, 8, 128, 32, 32768, 0), (16, 32, 4, 128, 40, 65536, 0), (1, 8, 2, 64, 8, 512, 256)]:
+        B, Hq, Hkv, d, k, n, sp = args
+        got = L.vc_workspace_size(L.VC_OP_VERIFY, B=B, Hq=Hq, Hkv=Hkv, d=d, k=k, max_len=n, split_tokens=sp)
+        assert got == L.vc_verify_workspace_bytes(B, Hq, Hkv, d, k, n, sp) > 0
+    assert L.vc_workspace_size(L.VC_OP_LOGITS, rows=640, vocab=151936) == L.vc_logits_workspace_bytes(640, 151936)
+    dr = L.Ckv("drop", 2, 2, 128, 1024, keep_ratio=0.25, tail_cap=0, device="cpu")
+    assert (L.vc_workspace_size(L.VC_OP_COMPRESS, ckv=dr, n_tokens=4096, n_probes=64)
+            == L.vc_compress_workspace_bytes(dr, 4096, 64) > 0)
+    assert L.vc_workspace_size(99, rows=1, vocab=1) == 0
+    assert L.vc_workspace_size(L.VC_OP_DECODE) == 0           # no descriptor
+

@@ -78,11 +78,24 @@ def test_verify_bytes_llama8b(bench):
     assert bench.verify_bytes(w, 32768) == kv + q_o
 
 
+def _recorded_hash(bench, name):
+    with open(os.path.join(bench.ROOT, "profiles", bench.TRAFFIC[name][0])) as fh:
+        for line in fh:
+            if line.startswith("# source_sha256:"):
+                return line.split(":", 1)[1].strip()
+    return None
+
+
 def test_traffic_reported_only_for_matching_sources(bench, monkeypatch):
+    # sources hashed as the summary recorded: the figure is reported
     for name in bench.TRAFFIC:
+        rec = _recorded_hash(bench, name)
+        assert rec, name
+        monkeypatch.setattr(bench, "source_hash", lambda files, rec=rec: rec)
         t = bench.measured_traffic(name)
         assert t is not None and t > 0, name
     assert bench.measured_traffic("no_such_workload") is None
+    # any other sources: not reported
     monkeypatch.setattr(bench, "source_hash", lambda files: "0" * 16)
     for name in bench.TRAFFIC:
         assert bench.measured_traffic(name) is None, name

@@ -50,6 +50,26 @@ def test_drop_select_bit_exact_on_same_scores(N, keep):
             assert np.array_equal(got[b, h], OD.select(s[b, h], keep)), (b, h)
 
 
+@pytest.mark.parametrize("keep", [1, 700, 1999])
+def test_drop_select_mixed_sign_zeros_and_nan(keep):
+    """Scores of either sign with many ties, -0.0 next to +0.0 (equal scores), -inf and
+    NaNs (ranked below every other score): the kept set equals the oracle's."""
+    w = SMALL.with_(N=2000)
+    rng = np.random.default_rng(keep)
+    s = (np.round(rng.standard_normal((w.B, w.Hkv, w.N)) * 4) / 4).astype(np.float32)
+    s[..., 10], s[..., 11], s[..., 12], s[..., 13] = -0.0, 0.0, np.nan, -np.inf
+    s[..., 14] = np.float32(-np.nan)
+    s[..., 1500:1520] = 0.0
+    s[..., 1520:1540] = -0.0
+    kept = torch.empty(w.B, w.Hkv, keep, dtype=torch.int32, device="cuda")
+    L.vc_drop_select(T(s), keep, kept)
+    torch.cuda.synchronize()
+    got = kept.cpu().numpy()
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            assert np.array_equal(got[b, h], OD.select(s[b, h], keep)), (b, h)
+
+
 def test_gather_rows_bit_exact():
     w = SMALL
     K = G.full_kv(w, "k")

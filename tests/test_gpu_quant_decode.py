@@ -20,8 +20,24 @@ SMALL = {
     "e2e_2bit": C.small(C.E2E, N=32 * 41),
     "k8v16_f32": C.TINY.with_(name="k8v16", k_bits=8, v_bits=16, N=32 * 9),
     "k16v8_bf16": C.small(C.LLAMA8B, N=64 * 5, k_bits=16, v_bits=8, scale_dtype="f32"),
-    "k3v2_g16": C.small(C.E2E, N=16 * 13, k_bits=3, v_bits=2, group=16),
+    # group 16 on the matrix-core kernel (capacity a multiple of 32) ...
+    "k3v2_g16": C.small(C.E2E, N=32 * 13, k_bits=3, v_bits=2, group=16),
+    # ... and on the generic kernel (a capacity of 208 rows is not a multiple of 32)
+    "k3v2_g16_generic": C.small(C.E2E, N=16 * 13, k_bits=3, v_bits=2, group=16),
 }
+
+# Groups 16 and 128 on the matrix-core kernel: every K and V bit width, both
+# parameter types, 4 (Llama-shaped, with outlier channels) and 8 (Qwen-shaped)
+# q-heads per kv-head.  Group 16 puts two K groups in each 32-token block; group 128
+# has one V group per token row.
+MFMA_GROUPS = {}
+for _G, _N in ((16, 32 * 41), (128, 128 * 11)):
+    for _kb, _vb, _p, _base in ((2, 2, "bf16", C.LLAMA8B), (3, 3, "f32", C.QWEN30B), (4, 4, "bf16", C.QWEN30B),
+                                (2, 4, "f32", C.LLAMA8B), (4, 2, "bf16", C.LLAMA8B), (3, 4, "bf16", C.QWEN30B),
+                                (4, 3, "f32", C.LLAMA8B)):
+        MFMA_GROUPS[f"g{_G}_k{_kb}v{_vb}_{_p}_h{_base.group_size}"] = C.small(
+            _base, N=_N, k_bits=_kb, v_bits=_vb, group=_G, scale_dtype=_p)
+ALL_CASES = {**SMALL, **MFMA_GROUPS}
 
 
 def _ckv(w, N, tail_cap=0):
@@ -29,9 +45,9 @@ def _ckv(w, N, tail_cap=0):
                  param_dtype=w.scale_dtype, kv_dtype=w.dtype, tail_cap=tail_cap)
 
 
-@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("name", list(ALL_CASES))
 def test_compress_quant_bit_exact(name):
-    w = SMALL[name]
+    w = ALL_CASES[name]
     say(f"[quant] {name} B{w.B} Hkv{w.Hkv} N{w.N} d{w.d} k{w.k_bits} v{w.v_bits} G{w.group}")
     K, V = G.full_kv(w, "k"), G.full_kv(w, "v")
     ckv = _ckv(w, w.N)
@@ -71,13 +87,21 @@ def test_compress_constant_groups_give_zero_scale():
     assert torch.all(ckv.k_zero.float() == 1.5)
 
 
-def _decode_case(w, tail, seed_row=None):
+def _scaled(x, scale, dtype):
+    """x * scale rounded to the storage type (both sides get the rounded values)."""
+    return x if scale == 1.0 else G.to_storage(x * np.float32(scale), dtype)
+
+
+def _decode_case(w, tail, scale=1.0, flags=0):
     """Decode each sequence's window query `tail-1` over the compressed context plus
-    window rows [0, tail) (the draft step of that row)."""
+    window rows [0, tail) (the draft step of that row); keys and values (context and
+    window) multiplied by `scale`."""
     K, V, Q, Kw, Vw = inputs(w)
+    K, V, Kw, Vw = (_scaled(x, scale, w.dtype) for x in (K, V, Kw, Vw))
     comp = oracle_compress(w, K, V)
     dt = tdtype(w.dtype)
     ckv = _ckv(w, w.N, tail_cap=max(tail, 1))
+    ckv.flags = flags
     upload_quant(ckv, comp, w.N)
     ckv.n_main = w.N
     ckv.tail_len = tail
@@ -100,12 +124,85 @@ def _decode_case(w, tail, seed_row=None):
     return ckv, out
 
 
-@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("name", list(ALL_CASES))
 @pytest.mark.parametrize("tail", [0, 5])
 def test_decode_quant_matches_oracle(name, tail):
-    w = SMALL[name]
+    w = ALL_CASES[name]
     say(f"[decode] {name} tail={tail}")
     _decode_case(w, tail)
+
+
+@pytest.mark.parametrize("name, scale", [("qwen30b_k4v3", 1e-3), ("llama8b_4bit", 1e-3), ("g16_k2v2_bf16_h4", 1e-3),
+                                         ("g128_k3v3_f32_h8", 1e-3), ("llama8b_4bit", 2.0)])
+def test_decode_range_edges_on_the_matrix_cores(name, scale):
+    """Inside the f16 path's stated domain: small keys and values whose operands are
+    f16 subnormals (x1e-3), and the outlier workload at twice its unit scale."""
+    w = ALL_CASES[name]
+    say(f"[decode range] {name} x{scale}")
+    _decode_case(w, 5, scale=scale)
+
+
+@pytest.mark.parametrize("name, scale", [("qwen30b_k4v3", 300.0), ("llama8b_4bit", 300.0), ("llama8b_4bit", 500.0),
+                                         ("g128_k3v3_f32_h8", 300.0), ("e2e_2bit", 40.0), ("g16_k2v2_bf16_h4", 300.0)])
+def test_decode_large_magnitudes_with_the_float32_flag(name, scale):
+    """Keys and values far above unit scale (|K|, |V| up to ~10^4 with the outlier
+    channels): outside the f16 path's accuracy domain (scores of magnitude ~10^3) and,
+    for the outlier workload at x500, outside f16's range (64 s_V > 65504).  With
+    VC_CKV_DECODE_F32 the float32 kernel decodes them within the bar."""
+    w = ALL_CASES[name]
+    say(f"[decode f32] {name} x{scale}")
+    if scale == 500.0:
+        V = _scaled(inputs(w)[1], scale, w.dtype)
+        assert 64 * float(np.max(oracle_compress(w, V, V)["v_scale"])) > 65504
+    _decode_case(w, 5, scale=scale, flags=L.VC_CKV_DECODE_F32)
+
+
+def test_decode_group16_ragged_lengths_mid_block():
+    """Group 16 on the matrix-core kernel with per-sequence lengths that end half-way
+    into a 32-token block (16 mod 32) and in the middle of a split."""
+    w = MFMA_GROUPS["g16_k4v4_bf16_h8"].with_(B=3)
+    K, V, Q, Kw, Vw = inputs(w)
+    comp = oracle_compress(w, K, V)
+    ckv = _ckv(w, w.N, tail_cap=8)
+    upload_quant(ckv, comp, w.N)
+    ckv.n_main, ckv.tail_len = w.N, 8
+    ckv.tail_k[:] = T(Kw[:, :, :8], torch.bfloat16)
+    ckv.tail_v[:] = T(Vw[:, :, :8], torch.bfloat16)
+    main = [w.N - 16, 32 * 17 + 16, 16]
+    tl = [8, 1, 0]
+    out = torch.empty(w.B, w.Hq, w.d, device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty(w.B, w.Hq, device="cuda")
+    L.vc_decode_attn_compressed(ckv, T(Q[:, :, 0], torch.bfloat16), out, lse=lse,
+                                main_lens=torch.tensor(main, dtype=torch.int32, device="cuda"),
+                                tail_lens=torch.tensor(tl, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    kh, vh = oracle_dequant(w, comp)
+    for b in range(w.B):
+        o, l = OA.decode(Q[b, :, 0], kh[b, :, :main[b]], vh[b, :, :main[b]], w.d ** -0.5,
+                         Kw[b, :, :tl[b]], Vw[b, :, :tl[b]])
+        assert_close(np32(out[b]), o, 'bf16', f"b={b}")
+        assert np.abs(np32(lse[b]) - l).max() <= LSE_TOL["bf16"]
+
+
+def test_decode_lengths_above_the_maximum_are_clamped():
+    """main_lens / tail_lens entries above n_main / tail_len read as n_main / tail_len."""
+    w = SMALL["llama8b_4bit"]
+    K, V, Q, Kw, Vw = inputs(w)
+    comp = oracle_compress(w, K, V)
+    ckv = _ckv(w, w.N, tail_cap=8)
+    upload_quant(ckv, comp, w.N)
+    ckv.n_main, ckv.tail_len = w.N - 64, 4
+    ckv.tail_k[:] = T(Kw[:, :, :8], torch.bfloat16)
+    ckv.tail_v[:] = T(Vw[:, :, :8], torch.bfloat16)
+    q = T(Q[:, :, 0], torch.bfloat16)
+    outs = []
+    for main, tl in (([w.N, w.N - 64], [8, 4]), ([w.N - 64, w.N - 64], [4, 4])):
+        o = torch.empty(w.B, w.Hq, w.d, device="cuda", dtype=torch.bfloat16)
+        L.vc_decode_attn_compressed(ckv, q, o, main_lens=torch.tensor(main, dtype=torch.int32, device="cuda"),
+                                    tail_lens=torch.tensor(tl, dtype=torch.int32, device="cuda"))
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
 
 
 def test_decode_ragged_lengths_and_empty_sequence():

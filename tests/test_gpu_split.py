@@ -80,7 +80,7 @@ def test_join_restores_the_full_codes(name):
     assert torch.equal(back.k_codes, full.k_codes) and torch.equal(back.v_codes, full.v_codes)
 
 
-@pytest.mark.parametrize("name", ["llama8b_4to2", "qwen30b_k4v3_to2", "k4v4_to3v2_f32"])
+@pytest.mark.parametrize("name", list(CASES))
 def test_decode_on_the_anchor_matches_oracle(name):
     """The drafter's decode over the anchor alone (plus tail rows) against the oracle's
     float64 attention over the anchor's dequantized keys and values."""

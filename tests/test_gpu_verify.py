@@ -94,6 +94,34 @@ def test_verify_ragged_context_lengths(base):
         assert np.abs(np32(lse[b]) - l).max() <= LSE_TOL["bf16"]
 
 
+def test_verify_ctx_lens_above_ctx_len_are_clamped():
+    """ctx_len is the call's longest context (it sizes the splits and the workspace);
+    an entry of ctx_lens above it reads as ctx_len: the output equals the call with
+    that entry lowered to ctx_len, bit for bit, and the oracle at that length."""
+    w = C.small(C.LLAMA8B, B=2, N=1500)
+    K, V, Q, Kw, Vw = inputs(w)
+    Lc = 1000
+    rows = w.N + w.k + 600
+    rng = np.random.default_rng(11)
+    kc = rng.standard_normal((w.B, w.Hkv, rows, w.d)).astype(np.float32)   # rows past the window: noise
+    vc = rng.standard_normal((w.B, w.Hkv, rows, w.d)).astype(np.float32)
+    kc[:, :, :Lc], vc[:, :, :Lc] = K[:, :, :Lc], V[:, :, :Lc]
+    kc[:, :, Lc:Lc + w.k], vc[:, :, Lc:Lc + w.k] = Kw, Vw
+    kc, vc = G.to_storage(kc, "bf16"), G.to_storage(vc, "bf16")
+    q = T(Q, torch.bfloat16)
+    kd, vd = T(kc, torch.bfloat16), T(vc, torch.bfloat16)
+    lens = lambda x: torch.tensor(x, dtype=torch.int32, device="cuda")
+    a, la = _run(w, q, kd, vd, Lc, ctx_lens=lens([Lc + 700, Lc]))
+    b, lb = _run(w, q, kd, vd, Lc, ctx_lens=lens([Lc, Lc]))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    for bb in range(w.B):
+        o, l = OA.verify_masked(Q[bb], kc[bb, :, :Lc], vc[bb, :, :Lc], kc[bb, :, Lc:Lc + w.k], vc[bb, :, Lc:Lc + w.k],
+                                w.d ** -0.5)
+        assert_close(np32(a[bb]), o, 'bf16')
+        assert np.abs(np32(la[bb]) - l).max() <= LSE_TOL["bf16"]
+
+
 def test_verify_deterministic():
     w = SMALL["llama8b"]
     K, V, Q, Kw, Vw = inputs(w)
