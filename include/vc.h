@@ -237,6 +237,23 @@ vc_status vc_decode_attn_compressed(const vc_ckv* ckv, const void* q, int32_t Hq
                                     void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 size_t vc_decode_workspace_bytes(const vc_ckv* ckv, int32_t Hq);
 
+/* vc_decode_attn_compressed without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, serving loops and harnesses that forbid
+ * hipMalloc.  The same kernels and splits as vc_decode_attn_compressed, so the same
+ * results bit for bit; the split partials go to a device array of
+ * VC_DECODE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on,
+ * from the first call on that GPU until the process ends.  The call allocates
+ * nothing.  A call whose partials exceed the array -- B*Hkv*S*(Hq/Hkv)*(d + 2)*4
+ * bytes plus alignment, S the call's split count (at most 64; e.g. B 8, Hkv 8, d 128,
+ * 4 q-heads per kv-head and 12 splits need 1.6 MB) -- returns VC_ERR_WORKSPACE with
+ * nothing enqueued.  Every call on a GPU uses the same array and nothing in it has to
+ * start at zero: calls that overlap in time on one GPU (other streams, other host
+ * threads) race on it and must not be issued; calls in one stream's order are fine. */
+#define VC_DECODE_NOALLOC_SCRATCH_BYTES (8u << 20)
+vc_status vc_decode_attn_compressed_noalloc(const vc_ckv* ckv, const void* q, int32_t Hq, float sm_scale,
+                                            const int32_t* main_lens, const int32_t* tail_lens, void* out,
+                                            float* lse, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Verification: causal attention of the k-row draft window over the full KV
  * (summary page, "What the paper found": verification against the full KV cache;

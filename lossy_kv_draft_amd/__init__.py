@@ -11,7 +11,8 @@ from ._lib import (  # noqa: F401
     Ckv, vc_ckv_sizes, vc_workspace_size, CKV_ARRAYS, VC_CKV_DECODE_F32, VC_OP_COMPRESS, VC_OP_DECODE,
     VC_OP_VERIFY, VC_OP_LOGITS, vc_compress, vc_compress_workspace_bytes, vc_drop_keep_count, vc_drop_scores,
     vc_drop_scores_workspace_bytes, vc_drop_select, vc_gather_rows, vc_decode_attn_compressed,
-    vc_decode_workspace_bytes, vc_verify_attn_full, vc_verify_workspace_bytes, vc_verify_split_tokens,
+    vc_decode_workspace_bytes, vc_decode_attn_compressed_noalloc, VC_DECODE_NOALLOC_SCRATCH_BYTES,
+    vc_verify_attn_full, vc_verify_workspace_bytes, vc_verify_split_tokens,
     vc_head_mean, vc_logits_argmax, vc_logits_workspace_bytes, vc_accept, vc_stage_full_kv, vc_hadamard_rows,
     vc_stage_full_kv_d2h, vc_last_error, workspace, FileStager, VC_ERR_IO,
     vc_split_planes, vc_join_planes, split_residuals,

@@ -68,6 +68,7 @@ _DECLS = {
     "vc_gather_rows": (c_i32, [c_p, c_i32, c_i32, c_i32, c_i64, c_i32, c_p, c_i64, c_p, c_i64, c_p]),
     "vc_decode_attn_compressed": (c_i32, [_P, c_p, c_i32, c_f32, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
     "vc_decode_workspace_bytes": (c_sz, [_P, c_i32]),
+    "vc_decode_attn_compressed_noalloc": (c_i32, [_P, c_p, c_i32, c_f32, c_p, c_p, c_p, c_p, c_p]),
     "vc_verify_attn_full": (c_i32, [c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, c_i64, c_p,
                                     c_i32, c_f32, c_p, c_p, c_p, c_sz, c_p]),
     "vc_verify_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, c_i32]),
@@ -290,6 +291,20 @@ def vc_decode_attn_compressed(ckv: Ckv, q, out, *, lse=None, sm_scale=None, main
     _check(lib.vc_decode_attn_compressed(ctypes.byref(c), _ptr(q), Hq, d ** -0.5 if sm_scale is None else sm_scale,
                                          _ptr(main_lens), _ptr(tail_lens), _ptr(out), _ptr(lse), _ptr(ws),
                                          ws.numel(), _stream(stream)), "vc_decode_attn_compressed")
+
+
+VC_DECODE_NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def vc_decode_attn_compressed_noalloc(ckv: Ckv, q, out, *, lse=None, sm_scale=None, main_lens=None, tail_lens=None,
+                                      stream=None):
+    """vc_decode_attn_compressed with the split partials in the library's own device
+    array (no workspace argument, nothing allocated)."""
+    B, Hq, d = q.shape
+    _check(lib.vc_decode_attn_compressed_noalloc(ctypes.byref(ckv.struct()), _ptr(q), Hq,
+                                                 d ** -0.5 if sm_scale is None else sm_scale, _ptr(main_lens),
+                                                 _ptr(tail_lens), _ptr(out), _ptr(lse), _stream(stream)),
+           "vc_decode_attn_compressed_noalloc")
 
 
 def vc_verify_split_tokens(B: int, Hkv: int, cache_rows: int) -> int:

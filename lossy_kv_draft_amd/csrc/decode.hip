@@ -17,6 +17,8 @@
 //   atomic counter -- merges all splits in split order (deterministic) and writes
 //   the normalized output and the log-sum-exp, then resets its counter to zero.
 
+#include <mutex>
+
 #include "decode_common.h"
 
 namespace vc {
@@ -213,10 +215,47 @@ extern "C" size_t vc_decode_workspace_bytes(const vc_ckv* c, int32_t Hq) {
   return bytes;
 }
 
-extern "C" vc_status vc_decode_attn_compressed(const vc_ckv* c, const void* q, int32_t Hq, float sm_scale,
-                                               const int32_t* main_lens, const int32_t* tail_lens, void* out,
-                                               float* lse, void* ws, size_t ws_bytes, void* stream) {
-  clear_error();
+namespace vc {
+
+// Splits of one decode call and the compressed rows each covers: the kernel is chosen
+// by the cache (matrix-core quantized, kept bf16 rows, generic), and so is the split.
+struct DecodePlan {
+  bool mfma, dense;
+  int S;
+  int64_t chunk;
+};
+
+static DecodePlan plan_decode(const vc_ckv* c, int H) {
+  DecodePlan p{};
+  p.mfma = decode_mfma_supported(c, H);
+  // kept bf16 rows, d = 128: the verification tile loop with one query row per head
+  p.dense = !p.mfma && c->method == VC_DROP_TOPK && c->kv_dtype == VC_BF16 && c->d == 128 && H <= 16;
+  if (p.mfma) {
+    p.S = decode_mfma_splits(c);  // compressed-row splits + one tail split
+    p.chunk = cdiv(cdiv(c->n_main > 0 ? c->n_main : 1, p.S - 1), 128) * 128;
+  } else if (p.dense) {
+    // two 4-wave workgroups per compute unit (64 KB of LDS each): row splits and the
+    // tail split together fill the device once
+    const int bh = c->B * c->Hkv;
+    p.S = 512 / bh;
+    if (p.S < 2) p.S = 2;
+    if (p.S > kDecMaxSplits) p.S = kDecMaxSplits;
+    p.chunk = cdiv(cdiv(c->n_main > 0 ? c->n_main : 1, p.S - 1), 64) * 64;
+  } else {
+    p.S = decode_splits(c);
+    const int64_t total = c->n_main + c->tail_len;
+    p.chunk = cdiv(cdiv(total > 0 ? total : 1, p.S), kDecTile) * kDecTile;
+  }
+  return p;
+}
+
+// Bytes of the split partials a call with S splits writes: outputs, then (max, sum).
+static size_t decode_partials_bytes(const vc_ckv* c, int H, int S) {
+  const size_t bh = static_cast<size_t>(c->B) * c->Hkv;
+  return align_up(bh * S * H * c->d * sizeof(float), 256) + align_up(bh * S * H * 2 * sizeof(float), 256);
+}
+
+static vc_status validate_decode_call(const vc_ckv* c, const void* q, int32_t Hq, float sm_scale, const void* out) {
   vc_status st = validate_decode_ckv(c);
   if (st != VC_OK) return st;
   VC_REQUIRE(q && out, "q / out is NULL");
@@ -226,11 +265,13 @@ extern "C" vc_status vc_decode_attn_compressed(const vc_ckv* c, const void* q, i
   VC_UNSUPPORTED(c->d % 32 == 0 && c->d <= 256, "d must be a multiple of 32 and at most 256 (got %d)", c->d);
   VC_UNSUPPORTED(H * c->d <= kDecMaxAcc * kDecThreads, "Hq/Hkv * d = %d exceeds %d", H * c->d,
                  kDecMaxAcc * kDecThreads);
-  size_t need = vc_decode_workspace_bytes(c, Hq);
-  if (!ws || ws_bytes < need) {
-    set_error("decode workspace needs %zu bytes (got %zu)", need, ws_bytes);
-    return VC_ERR_WORKSPACE;
-  }
+  return VC_OK;
+}
+
+// The decode kernel and the merge of its partials, with the partials at ws.
+static vc_status decode_launch(const vc_ckv* c, const void* q, int H, float sm_scale, const int32_t* main_lens,
+                               const int32_t* tail_lens, void* out, float* lse, const DecodePlan& p, void* ws,
+                               hipStream_t s) {
   DecodeArgs a{};
   a.k_codes = c->k_codes;
   a.v_codes = c->v_codes;
@@ -258,35 +299,15 @@ extern "C" vc_status vc_decode_attn_compressed(const vc_ckv* c, const void* q, i
   a.H = H;
   a.d = c->d;
   a.qscale = sm_scale * kLog2e;
-  const bool mfma = decode_mfma_supported(c, H);
-  // kept bf16 rows, d = 128: the verification tile loop with one query row per head
-  const bool dense = !mfma && c->method == VC_DROP_TOPK && c->kv_dtype == VC_BF16 && c->d == 128 && H <= 16;
-  int S;
-  if (mfma) {
-    S = decode_mfma_splits(c);  // compressed-row splits + one tail split
-    a.chunk = cdiv(cdiv(c->n_main > 0 ? c->n_main : 1, S - 1), 128) * 128;
-  } else if (dense) {
-    // two 4-wave workgroups per compute unit (64 KB of LDS each): row splits and the
-    // tail split together fill the device once
-    const int bh = c->B * c->Hkv;
-    S = 512 / bh;
-    if (S < 2) S = 2;
-    if (S > kDecMaxSplits) S = kDecMaxSplits;
-    a.chunk = cdiv(cdiv(c->n_main > 0 ? c->n_main : 1, S - 1), 64) * 64;
-  } else {
-    S = decode_splits(c);
-    int64_t total = c->n_main + c->tail_len;
-    a.chunk = cdiv(cdiv(total > 0 ? total : 1, S), kDecTile) * kDecTile;
-  }
-  a.splits = S;
-  size_t bh = static_cast<size_t>(c->B) * c->Hkv;
+  a.splits = p.S;
+  a.chunk = p.chunk;
+  const size_t bh = static_cast<size_t>(c->B) * c->Hkv;
   char* w = static_cast<char*>(ws);
   a.part_o = reinterpret_cast<float*>(w);
-  w += align_up(bh * S * H * c->d * sizeof(float), 256);
+  w += align_up(bh * p.S * H * c->d * sizeof(float), 256);
   a.part_ml = reinterpret_cast<float*>(w);
 
-  dim3 grid(S, static_cast<unsigned>(bh));
-  hipStream_t s = as_stream(stream);
+  const dim3 grid(p.S, static_cast<unsigned>(bh));
   auto merge = [&]() -> vc_status {
     const dim3 mgrid(static_cast<unsigned>(bh), static_cast<unsigned>(H));
     if (c->kv_dtype == VC_BF16)
@@ -296,12 +317,12 @@ extern "C" vc_status vc_decode_attn_compressed(const vc_ckv* c, const void* q, i
     VC_LAUNCHED("decode_merge_kernel");
     return VC_OK;
   };
-  if (mfma) {
+  if (p.mfma) {
     launch_decode_mfma(c, a, grid, s);
     VC_LAUNCHED("decode_mfma_kernel");
     return merge();
   }
-  if (dense) {
+  if (p.dense) {
     const vc_status st = launch_decode_dense(c, a, s);
     if (st != VC_OK) return st;
     return merge();
@@ -328,4 +349,66 @@ extern "C" vc_status vc_decode_attn_compressed(const vc_ckv* c, const void* q, i
   }
   VC_LAUNCHED("decode_generic_kernel");
   return merge();
+}
+
+// ---- the entry point that allocates nothing: its split partials live in `scratch`,
+// a file-scope device array (one copy per GPU, held until the process ends).  In host
+// code the array's name is only a host-side stand-in: the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+constexpr int kScratchMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[VC_DECODE_NOALLOC_SCRATCH_BYTES];
+
+static vc_status scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[kScratchMaxDevices] = {};
+  int dev = -1;
+  VC_HIP(hipGetDevice(&dev));
+  VC_REQUIRE(dev >= 0 && dev < kScratchMaxDevices, "device %d beyond the %d the library tracks", dev,
+             kScratchMaxDevices);
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    VC_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    VC_REQUIRE(p != nullptr, "no device address for the decode scratch array");
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return VC_OK;
+}
+
+}  // namespace vc
+
+extern "C" vc_status vc_decode_attn_compressed(const vc_ckv* c, const void* q, int32_t Hq, float sm_scale,
+                                               const int32_t* main_lens, const int32_t* tail_lens, void* out,
+                                               float* lse, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  vc_status st = validate_decode_call(c, q, Hq, sm_scale, out);
+  if (st != VC_OK) return st;
+  const size_t need = vc_decode_workspace_bytes(c, Hq);
+  if (!ws || ws_bytes < need) {
+    set_error("decode workspace needs %zu bytes (got %zu)", need, ws_bytes);
+    return VC_ERR_WORKSPACE;
+  }
+  const int H = Hq / c->Hkv;
+  return decode_launch(c, q, H, sm_scale, main_lens, tail_lens, out, lse, plan_decode(c, H), ws, as_stream(stream));
+}
+
+extern "C" vc_status vc_decode_attn_compressed_noalloc(const vc_ckv* c, const void* q, int32_t Hq, float sm_scale,
+                                                       const int32_t* main_lens, const int32_t* tail_lens, void* out,
+                                                       float* lse, void* stream) {
+  clear_error();
+  vc_status st = validate_decode_call(c, q, Hq, sm_scale, out);
+  if (st != VC_OK) return st;
+  const int H = Hq / c->Hkv;
+  const DecodePlan p = plan_decode(c, H);
+  const size_t need = decode_partials_bytes(c, H, p.S);
+  if (need > VC_DECODE_NOALLOC_SCRATCH_BYTES) {
+    set_error("decode partials need %zu bytes, beyond the %zu of the library's scratch array", need,
+              static_cast<size_t>(VC_DECODE_NOALLOC_SCRATCH_BYTES));
+    return VC_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != VC_OK) return st;
+  return decode_launch(c, q, H, sm_scale, main_lens, tail_lens, out, lse, p, ws, as_stream(stream));
 }
