@@ -352,8 +352,8 @@ __device__ __forceinline__ void vt_wait(int ahead) {
 
 // RT 16-row tiles per wave, W waves per workgroup (16 RT W rows per workgroup), a
 // ring of S tiles.
-template <int RT, int W, int S>
-__device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int rblk, int bh, VtStage* ring) {
+template <int RT, int W, int S, int PF = kVtPrefetch>
+__device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int row0, int bh, VtStage* ring) {
   constexpr int D = 128, KS = D / 32, DT = D / 16;
   static_assert(S >= 2 && kVtTile % W == 0, "ring shape");
   constexpr int kWaveRows = kVtTile / W;   // rows each wave copies per tile
@@ -366,7 +366,6 @@ __device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, kb = lane >> 4;
   const int M = a.H * a.k;
-  const int row0 = rblk * a.rows_per_block + wave * 16 * RT;
   const int64_t L = ver_ctx_len(a, b);
   const int64_t limit = L + a.k;  // readable positions [0, limit)
   const int64_t s_begin = static_cast<int64_t>(split) * a.C;
@@ -424,6 +423,18 @@ __device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int
       lds_copy16_buf(vr, voff[i], dst + kVtTileBytes);
     }
   };
+  // per-lane LDS byte offsets of the operand reads within a stage: K fragment (k-step
+  // ks) of position tile 0, V fragment (channel tile dt) of position 4 kb + e; the other
+  // tiles and halves are constant offsets from these (16-position tiles 4096 bytes
+  // apart, halves 8192), which the LDS reads take as immediates
+  uint32_t kofs[KS], vofs[DT];
+  {
+    const int e = l16 >> 2, qd = l16 & 3, ra = 4 * kb + e;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kofs[ks] = l16 * kVtRow + ((4 * ks + kb) ^ l16) * 16;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vofs[dt] = ra * kVtRow + vt_chunk(ra, 2 * dt + (qd >> 1)) * 16 + 8 * (qd & 1);
+  }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the query loads complete before the copies start
   for (int t = 0; t < S - 1 && t < ntile; ++t) issue(t);
   for (int j = 0; j < ntile; ++j) {
@@ -434,101 +445,118 @@ __device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int
     const unsigned char* vt = kt + kVtTileBytes;
     const int64_t t0 = s_begin + static_cast<int64_t>(j) * kVtTile;
     if (row0 < M) {  // wave-uniform; padding waves only copy
-      // ---- S^T = K Q^T: s[tt][rt][r] = score(position t0 + 16 tt + 4 kb + r, row row0 + 16 rt + l16);
-      //      K fragments are read ahead of the products that take them
-      f32x4_t s[NT][RT];
+      // the offsets as values of this iteration, so that their sums with the constant
+      // tile and half offsets are not hoisted out of the loop as registers of their own
+      uint32_t ko[KS], vo[DT];
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) s[tt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      // fragment i = (step i / NT, position tile i % NT); kVtPrefetch of them in flight
-      auto kload = [&](Pack16& dst, int i) {
-        const int ks = i / NT, tt = i % NT;
-        dst.u = *reinterpret_cast<const uint4*>(kt + (16 * tt + l16) * kVtRow + ((4 * ks + kb) ^ l16) * 16);
-      };
-      Pack16 kf[kVtPrefetch];
-#pragma unroll
-      for (int i = 0; i < kVtPrefetch; ++i) kload(kf[i], i);
-#pragma unroll
-      for (int i = 0; i < KS * NT; ++i) {
-        const Pack16 ka = kf[i % kVtPrefetch];
-        if (i + kVtPrefetch < KS * NT) kload(kf[i % kVtPrefetch], i + kVtPrefetch);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          s[i % NT][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.v, qf[rt][i / NT], s[i % NT][rt], 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        ko[ks] = kofs[ks];
+        asm volatile("" : "+v"(ko[ks]));
       }
-      // ---- V^T fragments (A operand of the P V product), kVtPrefetch of them in flight:
-      //      fragment i = (k-step i / DT, channel tile i % DT); k-slot j of lane group kb is
-      //      position 32 ks2 + 4 kb + j (j < 4), 32 ks2 + 16 + 4 kb + (j - 4) otherwise, as in P^T
-      constexpr int NV = KP * DT;
-      const int e = l16 >> 2, qd = l16 & 3;
-      auto vload = [&](Pack16& dst, int i) {
-        const int ks2 = i / DT, dt = i % DT;
-        const int ra = 32 * ks2 + 4 * kb + e, rb = ra + 16;
-        const int ch = 2 * dt + (qd >> 1), half = 8 * (qd & 1);
-        const uint2 lo = lds_read_tr16(vt + ra * kVtRow + vt_chunk(ra, ch) * 16 + half);
-        const uint2 hi = lds_read_tr16(vt + rb * kVtRow + vt_chunk(rb, ch) * 16 + half);
-        dst.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      };
-      Pack16 vf[kVtPrefetch];
 #pragma unroll
-      for (int i = 0; i < kVtPrefetch; ++i) vload(vf[i], i);  // in flight during the softmax
-      // ---- softmax per row
-      const bool full = t0 + kVtTile - 1 <= L;  // every row sees every position of the tile
-      bf16x8_t pb[RT][KP];
+      for (int dt = 0; dt < DT; ++dt) {
+        vo[dt] = vofs[dt];
+        asm volatile("" : "+v"(vo[dt]));
+      }
+      // The tile in 32-position halves (scores, softmax and both products of one half
+      // before the next), so that a wave holds the scores of half a tile
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        float mt = -INFINITY;
-        if (full) {
+      for (int hh = 0; hh < KP; ++hh) {
+        const int64_t h0 = t0 + 32 * hh;
+        // ---- S^T = K Q^T: s[tt][rt][r] = score(position h0 + 16 tt + 4 kb + r, row row0 + 16 rt + l16);
+        //      K fragments are read ahead of the products that take them
+        f32x4_t s[2][RT];
 #pragma unroll
-          for (int tt = 0; tt < NT; ++tt)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[tt][rt][r]);
-        } else {
-          const int lr = static_cast<int>(max(min(rlim[rt] - t0, static_cast<int64_t>(kVtTile)), static_cast<int64_t>(-1)));
+          for (int rt = 0; rt < RT; ++rt) s[tt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // fragment i = (step i / 2, position tile 2 hh + i % 2); PF of them in flight
+        auto kload = [&](Pack16& dst, int i) {
+          const int ks = i / 2, tt = 2 * hh + i % 2;
+          dst.u = *reinterpret_cast<const uint4*>(kt + ko[ks] + 16 * tt * kVtRow);
+        };
+        Pack16 kf[PF];
 #pragma unroll
-          for (int tt = 0; tt < NT; ++tt)
+        for (int i = 0; i < PF; ++i) kload(kf[i], i);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float v = 16 * tt + 4 * kb + r <= lr ? s[tt][rt][r] : -INFINITY;
-              s[tt][rt][r] = v;
-              mt = fmaxf(mt, v);
-            }
+        for (int i = 0; i < KS * 2; ++i) {
+          const Pack16 ka = kf[i % PF];
+          if (i + PF < KS * 2) kload(kf[i % PF], i + PF);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            s[i % 2][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.v, qf[rt][i / 2], s[i % 2][rt], 0, 0, 0);
         }
-        const float mts = group4_max(mt) * a.qscale;
-        if (mts > m[rt] + 8.f) {  // the row's own decision (all lanes of a row agree)
-          const float al = __builtin_amdgcn_exp2f(m[rt] - mts);  // 0 on the row's first scores
+        // ---- V^T fragments (A operand of the P V product), PF of them in flight:
+        //      fragment dt = channel tile; k-slot j of lane group kb is position
+        //      32 hh + 4 kb + j (j < 4), 32 hh + 16 + 4 kb + (j - 4) otherwise, as in P^T
+        auto vload = [&](Pack16& dst, int dt) {  // rows 32 hh + 4 kb + e and 16 further: same swizzle
+          const uint2 lo = lds_read_tr16(vt + vo[dt] + 32 * hh * kVtRow);
+          const uint2 hi = lds_read_tr16(vt + vo[dt] + (32 * hh + 16) * kVtRow);
+          dst.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        };
+        Pack16 vf[PF];
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= al;
-          lacc[rt] *= al;
-          m[rt] = mts;
-        }
-        const float nm = m[rt] == -INFINITY ? 0.f : -m[rt];
-        Pack16 pp[KP];
+        for (int i = 0; i < PF; ++i) vload(vf[i], i);  // in flight during the softmax
+        // ---- softmax per row over the half
+        const bool full = h0 + 31 <= L;  // every row sees every position of the half
+        bf16x8_t pb[RT];
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
+        for (int rt = 0; rt < RT; ++rt) {
+          float mt = -INFINITY;
+          if (full) {
 #pragma unroll
-          for (int r = 0; r < 4; r += 2) {
-            const f2_t ex = {__builtin_amdgcn_exp2f(fmaf(s[tt][rt][r], a.qscale, nm)),
-                             __builtin_amdgcn_exp2f(fmaf(s[tt][rt][r + 1], a.qscale, nm))};
-            const bf16x2_t h = __builtin_convertvector(ex, bf16x2_t);
-            pp[tt >> 1].v[(tt & 1) * 4 + r] = h[0];
-            pp[tt >> 1].v[(tt & 1) * 4 + r + 1] = h[1];
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[tt][rt][r]);
+          } else {
+            const int lr = static_cast<int>(max(min(rlim[rt] - h0, static_cast<int64_t>(32)), static_cast<int64_t>(-1)));
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float v = 16 * tt + 4 * kb + r <= lr ? s[tt][rt][r] : -INFINITY;
+                s[tt][rt][r] = v;
+                mt = fmaxf(mt, v);
+              }
           }
+          // The running maximum moves only when a score exceeds it by more than 8: a lane
+          // tests its own scores (rounding is monotone, so fl(max x * q) > m + 8 exactly
+          // when some fl(x * q) > m + 8), a wave vote gates the row maxima, and each row
+          // still decides alone
+          if (__any(mt * a.qscale > m[rt] + 8.f)) {
+            const float mts = group4_max(mt) * a.qscale;
+            if (mts > m[rt] + 8.f) {  // the row's own decision (all lanes of a row agree)
+              const float al = __builtin_amdgcn_exp2f(m[rt] - mts);  // 0 on the row's first scores
 #pragma unroll
-        for (int ks2 = 0; ks2 < KP; ++ks2) {
-          pb[rt][ks2] = pp[ks2].v;
-          lacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones.v, pb[rt][ks2], lacc[rt], 0, 0, 0);
+              for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= al;
+              lacc[rt] *= al;
+              m[rt] = mts;
+            }
+          }
+          const float nm = m[rt] == -INFINITY ? 0.f : -m[rt];
+          Pack16 pp;
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+              const f2_t ex = {__builtin_amdgcn_exp2f(fmaf(s[tt][rt][r], a.qscale, nm)),
+                               __builtin_amdgcn_exp2f(fmaf(s[tt][rt][r + 1], a.qscale, nm))};
+              const bf16x2_t h = __builtin_convertvector(ex, bf16x2_t);
+              pp.v[tt * 4 + r] = h[0];
+              pp.v[tt * 4 + r + 1] = h[1];
+            }
+          pb[rt] = pp.v;
+          lacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones.v, pb[rt], lacc[rt], 0, 0, 0);
         }
-      }
-      // ---- O^T += V^T P^T
+        // ---- O^T += V^T P^T over the half
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const Pack16 va = vf[i % kVtPrefetch];
-        if (i + kVtPrefetch < NV) vload(vf[i % kVtPrefetch], i + kVtPrefetch);
+        for (int dt = 0; dt < DT; ++dt) {
+          const Pack16 va = vf[dt % PF];
+          if (dt + PF < DT) vload(vf[dt % PF], dt + PF);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          o[i % DT][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pb[rt][i / DT], o[i % DT][rt], 0, 0, 0);
+          for (int rt = 0; rt < RT; ++rt)
+            o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pb[rt], o[dt][rt], 0, 0, 0);
+        }
       }
     }
   }
@@ -560,7 +588,40 @@ __global__ void __launch_bounds__(64 * W) verify_tile_kernel(VerifyArgs a, int n
   const int id = blockIdx.x;
   const int u = (id / (8 * nblk)) * 8 + (id & 7);
   if (u >= units) return;
-  verify_tiles<RT, W, S>(a, u % a.splits, (id >> 3) % nblk, u / a.splits, ring);
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  verify_tiles<RT, W, S>(a, u % a.splits, ((id >> 3) % nblk) * a.rows_per_block + wave * 16 * RT, u / a.splits, ring);
+}
+
+// Rows of one kv-head in two independent 4-wave workgroups, one with RTA row tiles
+// per wave, one with RTB (64 (RTA + RTB) rows, e.g. 320 as 3 + 2): each reads every
+// K/V tile, and two such workgroups on a compute unit keep every SIMD at RTA + RTB
+// tiles without sharing a barrier.  Workgroup 2u + r of the one-dimensional grid is
+// role r of unit u = (split, sequence, kv-head).
+template <int RTA, int RTB, int S>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) verify_roles_kernel(VerifyArgs a) {
+  __shared__ __attribute__((aligned(16))) VtStage ring[S];
+  const int u = blockIdx.x >> 1;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  if ((blockIdx.x & 1) == 0)
+    verify_tiles<RTA, 4, S, 2>(a, u % a.splits, wave * 16 * RTA, u / a.splits, ring);
+  else
+    verify_tiles<RTB, 4, S, 2>(a, u % a.splits, 64 * RTA + wave * 16 * RTB, u / a.splits, ring);
+}
+
+// Rows of one kv-head in 8 waves with unequal row tiles: waves 0-3 hold RTA 16-row
+// tiles each, waves 4-7 RTB, so every SIMD (waves w and w + 4) carries RTA + RTB
+// tiles: 64 (RTA + RTB) rows in one workgroup that reads each K/V tile once (320 rows,
+// i.e. 8 q-heads x 40 window rows, as 3 + 2).  One workgroup per (split, sequence,
+// kv-head).
+template <int RTA, int RTB, int S>
+__global__ void __launch_bounds__(512) verify_mixed_kernel(VerifyArgs a) {
+  __shared__ __attribute__((aligned(16))) VtStage ring[S];
+  const int u = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  if (wave < 4)
+    verify_tiles<RTA, 8, S, 2>(a, u % a.splits, wave * 16 * RTA, u / a.splits, ring);
+  else
+    verify_tiles<RTB, 8, S, 2>(a, u % a.splits, 64 * RTA + (wave - 4) * 16 * RTB, u / a.splits, ring);
 }
 
 // Draft-side decode over kept (token-dropped) bf16 rows, d = 128, at most 16 q-heads
@@ -575,7 +636,8 @@ __global__ void __launch_bounds__(kVerThreads) decode_dense_kernel(VerifyArgs a,
     decode_tail_partial_d128(d, blockIdx.z, d.splits - 1, reinterpret_cast<float*>(&ring[0][0]));
     return;
   }
-  verify_tiles<1, 4, kDdStages>(a, blockIdx.x, 0, blockIdx.z, ring);
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  verify_tiles<1, 4, kDdStages>(a, blockIdx.x, 16 * wave, blockIdx.z, ring);
 }
 
 // float32 path: one 64-lane wave per (row, split); lanes cover d (d <= 256).
@@ -820,7 +882,11 @@ extern "C" vc_status vc_verify_attn_full(const void* q, const void* k_cache, con
     a.rows_per_block = 16 * W * RT;
     const int units = a.splits * static_cast<int>(bh);
     const dim3 grid(static_cast<unsigned>(cdiv(units, 8) * 8 * nblk));
-    if (W == 8)
+    if (M > 256 && M <= 320) {
+      // one 8-wave block per (split, kv-head): 3 row tiles in waves 0-3, 2 in waves 4-7
+      a.rows_per_block = 320;
+      hipLaunchKernelGGL((verify_mixed_kernel<3, 2, 4>), dim3(static_cast<unsigned>(units)), dim3(512), 0, s, a);
+    } else if (W == 8)
       hipLaunchKernelGGL((verify_tile_kernel<2, 8, 4>), grid, dim3(512), 0, s, a, nblk, units);
     else if (RT == 1)
       hipLaunchKernelGGL((verify_tile_kernel<1, 4, 2>), grid, dim3(256), 0, s, a, nblk, units);
