@@ -416,6 +416,8 @@ def e2e_rounds(ctx, gen, slots, remote=True):
     loop = R.VeriCacheLoop(sess, slots=slots)
     got, t_vc = timed(lambda: loop.run(timed=True))
     ok = bool(np.array_equal(got, ref))
+    note("cost model calibration")
+    calib = cost_calibration(R, sess, w, timed)
     # the same batch with the draft horizon chosen per round by the cost model
     note("adaptive horizon")
     horizons = tuple(h for h in (4, 8, 16, 32) if h <= w.k)
@@ -432,6 +434,16 @@ def e2e_rounds(ctx, gen, slots, remote=True):
         remote = remote_prefix_rounds(w, sess, ref, slots, gen, timed)
     else:
         remote = None
+    # the same batch with every layer's slot on the device (all staging under the drafts)
+    note(f"{w.layers} device slots")
+    loop4 = R.VeriCacheLoop(sess, slots=w.layers)
+    got4, t_4 = timed(lambda: loop4.run())
+    all_slots = {"device_kv_slots": w.layers, "accepted_tok_per_s": round(w.B * (gen - 1) / t_4, 1),
+                 "rounds": loop4.rounds, "round_ms": round(t_4 / loop4.rounds * 1e3, 3),
+                 "output_equals_greedy": bool(np.array_equal(got4, ref))}
+    del loop4
+    cost = cost_model_points(w, calib, slots, t_vc / loop.rounds, t_4 / all_slots["rounds"], adaptive, remote,
+                             commits=(gen - 1) / loop.rounds)
     note("staggered batches")
     stag = staggered_rounds(w, shape, weights, sess, ref, slots, gen, chunk, timed)
     committed = w.B * (gen - 1)                                 # tokens produced after the prefill's first
@@ -453,10 +465,110 @@ def e2e_rounds(ctx, gen, slots, remote=True):
             "speedup_vs_greedy_resident": round(vc_tps / res_tps, 3),
             "output_equals_greedy": ok, "prefill_s": round(prefill_s, 2),
             "adaptive_horizon": adaptive,
+            "all_slots": all_slots,
+            "cost_model": cost,
             "remote_prefix": remote,
             "staggered": stag,
             "note": "random-init weights and uniform-random prompts; acceptance is a property of this "
                     "synthetic model, not of a trained one"}
+
+
+def cost_calibration(R, sess, w, timed, horizons=(4, 8, 16, 32), rounds=3):
+    """Component times of a round, measured apart from the rounds the model predicts:
+    loops over the resident full KV (no staging) at each horizon give the draft step,
+    the verify pass per layer and what follows it (tokens, acceptance, cache update,
+    sync); staging the full KV through the slot ring with nothing else running gives
+    the link's time per layer."""
+    import torch
+    out = {"horizons": {}}
+    for k in horizons:
+        lp = R.VeriCacheLoop(sess, slots=None, horizons=[k])
+        lp.round()                                              # warm
+        lp.phase_ms = {n: 0.0 for n in lp.phase_ms}
+        r0 = lp.rounds
+        _, t = timed(lambda: [lp.round(timed=True) for _ in range(rounds)])
+        n = lp.rounds - r0
+        draft, verify = lp.phase_ms["draft"] / n / 1e3, lp.phase_ms["verify"] / n / 1e3
+        out["horizons"][k] = {"t_step": draft / k, "t_layer": verify / w.layers, "t_tail": t / n - draft - verify}
+        del lp
+        torch.cuda.empty_cache()
+    # the link: every layer staged through the slots of a staged loop, back to back
+    lp = R.VeriCacheLoop(sess, slots=2, horizons=[horizons[0]])
+    full, n_rows = lp.full, int(lp.Lb.max())
+    t_best = None
+    for _ in range(3):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        b0 = full.bytes_staged
+        full.begin(n_rows, n_rows, n_rows)
+        for l in range(full.layers):
+            full.acquire(l)
+            full.release(l)
+        torch.cuda.synchronize()
+        t = time.perf_counter() - t0
+        t_best = t if t_best is None else min(t_best, t)
+        nbytes = full.bytes_staged - b0
+    out["layer_bytes"] = nbytes / full.layers
+    out["link_Bps"] = nbytes / t_best
+    del lp
+    torch.cuda.empty_cache()
+    return out
+
+
+def cost_model_points(w, calib, slots, t_fixed, t_all_slots, adaptive, remote, commits):
+    """Round times the cost model predicts from the calibration, beside the measured
+    rounds: the fixed horizon over `slots` slots and over one slot per layer, each
+    horizon of the adaptive loop, and the prefix staged from a file (its link rate
+    from the file stager's measured rate).  Also the speedup over greedy with the full
+    KV staged every token on a grid of acceptance lengths and link rates."""
+    from lossy_kv_draft_amd import costmodel as CM
+    hz = calib["horizons"]
+    lb, link = calib["layer_bytes"], calib["link_Bps"]
+
+    def costs(k, n_slots, rate=link):
+        c = hz[k]
+        return CM.RoundCosts(layers=w.layers, slots=n_slots, t_step=c["t_step"], t_layer=c["t_layer"],
+                             t_stage=lb / rate, t_tail=c["t_tail"])
+
+    pts = []
+
+    def add(name, k, n_slots, measured_s, rate=link):
+        pred = CM.round_time(k, costs(k, n_slots, rate))
+        pts.append({"setting": name, "predicted_round_ms": round(pred * 1e3, 2),
+                    "measured_round_ms": round(measured_s * 1e3, 2),
+                    "rel_err": round(pred / measured_s - 1.0, 3)})
+
+    add(f"fixed k={w.k}, {slots} slots", w.k, slots, t_fixed)
+    add(f"fixed k={w.k}, {w.layers} slots", w.k, w.layers, t_all_slots)
+    for k, ms in adaptive.get("mean_round_ms_per_horizon", {}).items():
+        if int(k) in hz and adaptive["rounds_per_horizon"].get(k, 0) >= 3:
+            add(f"adaptive, horizon {k}", int(k), slots, ms / 1e3)
+    for r in remote or []:
+        file_rate = r["file_stage_GBps"] * 1e9
+        # per layer: the prompt rows from the file, the generated rows from pinned memory
+        p_frac = w.N / (w.N + w.gen_tokens / 2)
+        rate = 1.0 / (p_frac / file_rate + (1.0 - p_frac) / link)
+        cap = r["link_cap_GBps"]
+        add(f"prefix from a file, {'uncapped' if cap is None else f'{cap} GB/s cap'}", w.k, slots,
+            r["round_ms"] / 1e3, rate)
+    errs = [abs(p["rel_err"]) for p in pts]
+    p_acc = CM.accept_p_from_commits(commits, w.k)
+    surf = CM.speedup_surface(w.B, w.k, costs(w.k, slots), lb, hz[min(hz)]["t_layer"] * w.layers,
+                              accepted_lens=(0.5, 4.0, 10.0, 25.0, 40.0),
+                              link_rates=(8e9, 16e9, 32e9, link, 128e9))
+    best = {str(a): CM.best_horizon(w.B, sorted(hz), CM.accept_p_from_commits(min(a + 1.0, w.k), w.k),
+                                    lambda k: costs(k, slots))
+            for a in (0.5, 4.0, 25.0)}
+    return {"calibration": {"t_step_ms": {str(k): round(v["t_step"] * 1e3, 3) for k, v in hz.items()},
+                            "t_layer_ms": {str(k): round(v["t_layer"] * 1e3, 3) for k, v in hz.items()},
+                            "t_tail_ms": {str(k): round(v["t_tail"] * 1e3, 3) for k, v in hz.items()},
+                            "layer_MB": round(lb / 1e6, 1), "link_GBps": round(link / 1e9, 2)},
+            "points": pts, "max_abs_rel_err": round(max(errs), 3) if errs else None,
+            "accept_p": round(p_acc, 3),
+            "predicted_accepted_tok_per_s": round(CM.tokens_per_s(w.B, w.k, p_acc, costs(w.k, slots)), 1),
+            "best_horizon_by_accepted_drafts": best,
+            "speedup_vs_staged_greedy": [{"accepted": a, "link_GBps": round(r / 1e9, 1), "speedup": round(x, 2)}
+                                         for a, r, _, x in surf]}
 
 
 def remote_prefix_rounds(w, sess, ref, slots, gen, timed, rates=(0.0, 25e9)):
@@ -534,24 +646,80 @@ def staggered_rounds(w, shape, weights, sess0, ref0, slots, gen, chunk, timed):
     return out
 
 
+def verify_mfma_shape(steps=20, warmup=5):
+    """Verification at the Qwen3-30B-A3B-shaped layer (B16, 32/4 heads, d 128, N 65536,
+    window 40: AI 320 flop per byte, where the matrix cores and not HBM bound it):
+    seeded N(0, 1) bf16 inputs made on the device, each call timed between HIP events."""
+    import torch
+    import lossy_kv_draft_amd as L
+    w = workload("qwen30b")
+    rows = w.N + w.k
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1000 + w.index)
+    kc = torch.randn(w.B, w.Hkv, rows, w.d, device="cuda", dtype=torch.bfloat16, generator=g)
+    vc = torch.randn(w.B, w.Hkv, rows, w.d, device="cuda", dtype=torch.bfloat16, generator=g)
+    q = torch.randn(w.B, w.Hq, w.k, w.d, device="cuda", dtype=torch.bfloat16, generator=g)
+    out = torch.empty_like(q)
+    ws = L.workspace(L.vc_verify_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, w.k, w.N))
+    call = lambda: L.vc_verify_attn_full(q, kc, vc, w.N, out, ws=ws)
+    for _ in range(warmup):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+    med = float(np.median(us))
+    flops, nbytes = verify_flops(w, w.N), verify_bytes(w, w.N)
+    tflops = flops / (med * 1e-6) / 1e12
+    attain = min(BF16_PEAK_TFLOPS, flops / nbytes * HBM_PEAK_GBS / 1e3)
+    del kc, vc, q, out, ws
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "seq_len": w.N, "window": w.k,
+            "call_us": spread(us), "tflops": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+            "ai_flop_per_byte": round(flops / nbytes, 1), "attainable_tflops": round(attain, 1),
+            "frac_of_attainable": round(tflops / attain, 4), "hbm_gbs": round(nbytes / (med * 1e-6) / 1e9, 1)}
+
+
 def gpu_state():
-    """Clocks and socket power as amd-smi reports them (read-only query).  Skipped
-    under a profiler: its preloaded library would initialise the GPU in the child
-    before amd-smi's interpreter replaces it."""
-    import subprocess
-    if "rocprof" in os.environ.get("LD_PRELOAD", ""):
-        return {"skipped": "run under a profiler"}
-    try:
-        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"], capture_output=True,
-                           text=True, timeout=20)
-        g = json.loads(r.stdout)["gpu_data"][0]
-        clk = g["clock"]
-        gfx = [clk[k]["clk"]["value"] for k in sorted(clk) if k.startswith("gfx_")]
-        return {"tool": "amd-smi metric --clock --power", "gfx_clk_mhz": gfx,
-                "gfx_max_clk_mhz": clk["gfx_0"]["max_clk"]["value"], "mem_clk_mhz": clk["mem_0"]["clk"]["value"],
-                "socket_power_w": g["power"]["socket_power"]["value"]}
-    except Exception as e:  # the tool is optional; its absence does not fail the run
-        return {"error": f"{type(e).__name__}: {e}"[:200]}
+    """Clocks and power of the GPU from the amdgpu driver's files in sysfs (read-only;
+    no child process is started, so nothing inherits a profiler's preloaded library):
+    the current levels of pp_dpm_sclk / pp_dpm_mclk and the hwmon power reading."""
+    import glob
+    import re
+    out = {"source": "sysfs (amdgpu)"}
+
+    def read(path):
+        try:
+            with open(path) as fh:
+                return fh.read()
+        except OSError:
+            return None
+
+    for dev in sorted(glob.glob("/sys/class/drm/card[0-9]*/device")):
+        if (read(dev + "/vendor") or "").strip() != "0x1002":
+            continue
+        for name, key in (("pp_dpm_sclk", "gfx_clk_mhz"), ("pp_dpm_mclk", "mem_clk_mhz")):
+            txt = read(f"{dev}/{name}")
+            if txt:
+                levels = [int(m) for m in re.findall(r"(\d+)\s*[Mm][Hh]z", txt)]
+                cur = re.search(r"(\d+)\s*[Mm][Hh]z\s*\*", txt)
+                if cur:
+                    out[key] = int(cur.group(1))
+                if levels and key == "gfx_clk_mhz":
+                    out["gfx_max_clk_mhz"] = max(levels)
+        for hw in sorted(glob.glob(dev + "/hwmon/hwmon*")):
+            for f in ("power1_average", "power1_input"):
+                v = read(f"{hw}/{f}")
+                if v and v.strip().isdigit():
+                    out["socket_power_w"] = round(int(v) / 1e6, 1)
+                    break
+        if len(out) > 1:
+            return out
+    out["unavailable"] = "no amdgpu clock or power files visible"
+    return out
 
 
 def spread(v_us):
@@ -560,28 +728,56 @@ def spread(v_us):
     return {"median": round(float(q[0]), 3), "p10": round(float(q[1]), 3), "p90": round(float(q[2]), 3)}
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, seconds):
-    """The oracle (numpy, float64 attention) timed on the host for a bounded sample:
-    whole (sequence, kv-head) slices of the same workload -- dequantize the slice's
-    compressed rows and decode one draft query of each of its q-heads -- repeated
-    until about `seconds` of work; scaled to GB/s of the same algorithmic bytes."""
-    from workloads import gen as G
-    from oracle import quant as OQ, attention as OA, drop as OD
+    """The oracle (numpy; float64 attention, float32 quantization arithmetic) timed on
+    the host, BLAS threads pinned to the visible cores, on bounded samples of the
+    same workload.  The headline leg: whole (sequence, kv-head) slices -- dequantize
+    the slice's compressed rows and decode one draft query of each of its q-heads --
+    repeated until about `seconds` of work, scaled to GB/s of the same algorithmic
+    bytes.  Beside it: compressing slices (quantize + pack), verifying one slice's
+    window over its full context, acceptance of the batch's window, and one
+    draft-and-verify round of the end-to-end decoder at a reduced prompt."""
+    from workloads import gen as G, configs as Cfg
+    from oracle import quant as OQ, attention as OA, drop as OD, accept as OC, model as OM
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=cores)
+    except Exception:
+        limit = None
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = 1
     grp = w.Hq // w.Hkv
-    per_slice = decode_bytes(w, w.N, 1) / (w.B * w.Hkv)
+    n_slices = w.B * w.Hkv
+    per_slice = decode_bytes(w, w.N, 1) / n_slices
     done, t_total, b, h = 0, 0.0, 0, 0
+    legs = {}
     # inputs and their compression are prepared outside the timed region
-    while t_total < seconds and done < w.B * w.Hkv:
+    comp_t, comp_n = 0.0, 0
+    while t_total < seconds and done < n_slices:
         k, v = G.kv_slice(w, "k", b, h), G.kv_slice(w, "v", b, h)
         q = np.stack([G.window_q(w, b, h * grp + j)[0] for j in range(grp)])
         kw, vw = G.window_kv(w, "k", b, h)[:1], G.window_kv(w, "v", b, h)[:1]
         if w.method == "quant":
+            t0 = time.perf_counter()
             c = OQ.compress_slice(k, v, w.k_bits, w.v_bits, w.group, w.scale_dtype)
+            if comp_n < 2:                                   # the compress leg: two slices
+                comp_t += time.perf_counter() - t0
+                comp_n += 1
             t0 = time.perf_counter()
             kh, vh = OQ.dequantize_slice(c, w.d, w.k_bits, w.v_bits, w.group)
             OA.decode(q, kh[None], vh[None], w.d ** -0.5, kw[None], vw[None])
@@ -594,11 +790,63 @@ def cpu_baseline(w, seconds):
         h += 1
         if h == w.Hkv:
             h, b = 0, b + 1
+    if comp_n:
+        in_bytes = 2 * w.N * w.d * (4 if w.dtype == "f32" else 2)
+        legs["compress"] = {"GBps": round(comp_n * in_bytes / comp_t / 1e9, 4),
+                            "whole_workload_s": round(comp_t / comp_n * n_slices, 2),
+                            "sample": f"quantize + pack {comp_n} of {n_slices} slices ({w.N} tokens each); "
+                                      f"whole workload extrapolated"}
+    # verify: the window of one (sequence, kv-head) over its full context, every q-head
+    k, v = G.kv_slice(w, "k", 0, 0), G.kv_slice(w, "v", 0, 0)
+    qw = np.stack([G.window_q(w, 0, j) for j in range(grp)])
+    kw, vw = G.window_kv(w, "k", 0, 0), G.window_kv(w, "v", 0, 0)
+    t0 = time.perf_counter()
+    OA.verify_masked(qw, k[None], v[None], kw[None], vw[None], w.d ** -0.5)
+    t_v = time.perf_counter() - t0
+    slice_flops = verify_flops(w, w.N) / n_slices
+    legs["verify"] = {"TFLOPs": round(slice_flops / t_v / 1e12, 5), "whole_workload_s": round(t_v * n_slices, 2),
+                      "sample": f"1 of {n_slices} slices: {grp} q-heads x {w.k} window rows over {w.N} + {w.k} "
+                                f"positions; whole workload extrapolated"}
+    # accept: the batch's drafts against targets
+    rng = np.random.default_rng(5)
+    dr = rng.integers(0, 3, size=(w.B, w.k))
+    tg = rng.integers(0, 3, size=(w.B, w.k))
+    t0 = time.perf_counter()
+    reps = 200
+    for _ in range(reps):
+        for bb in range(w.B):
+            OC.accept_row(list(dr[bb]), list(tg[bb]))
+    legs["accept"] = {"us_per_call": round((time.perf_counter() - t0) / reps * 1e6, 2),
+                      "sample": f"{w.B} sequences x window {w.k}, {reps} calls"}
+    # one draft-and-verify round of the end-to-end decoder (float64) at a reduced prompt
+    e = Cfg.E2E
+    P = 256
+    cfg = OM.Config(layers=e.layers, d_model=e.d_model, Hq=e.Hq, Hkv=e.Hkv, hd=e.d, ffn=e.ffn, vocab=e.vocab)
+    dec = OM.Decoder(cfg, OM.random_weights(cfg, np.random.default_rng(7)))
+    prompt = G.tokens(e, 0, shape=(P,), high=e.vocab)
+    run = lambda T, st=None: OM.vericache(dec, prompt, T, e.k, bits=(e.k_bits, e.v_bits), group=e.group,
+                                          scale_dtype="f32", stats=st)
+    run(1)                                                  # warm: the prefill and prompt compression only
+    t0 = time.perf_counter()
+    run(1)
+    t_pre = time.perf_counter() - t0
+    st = OM.RoundStats()
+    t0 = time.perf_counter()
+    run(2, st)                                              # the same, then one round
+    t_round = time.perf_counter() - t0 - t_pre
+    legs["round"] = {"round_s": round(t_round, 2), "rounds": st.rounds,
+                     "sample": f"decoder {e.layers}L d_model {e.d_model}, 1 sequence, prompt {P} tokens "
+                               f"(reduced from the end-to-end workload's), k {e.k}: {e.k} draft steps on the "
+                               f"compressed cache, the verify pass, acceptance and the cache update (a run to "
+                               f"two tokens minus a run to one)"}
+    if limit is not None:
+        limit.restore_original_limits()
     return {"value": round(done * per_slice / t_total / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{done} of {w.B * w.Hkv} (sequence, kv-head) slices: {'dequantize + ' if w.method == 'quant' else ''}decode of "
-                      f"{grp} q-heads over {w.N} tokens, {t_total:.1f}s of CPU time, "
-                      f"{len(os.sched_getaffinity(0))} cores visible"}
+            "kind": "oracle", "cpu_model": _cpu_model(), "cores_visible": cores,
+            "sample": f"{done} of {n_slices} (sequence, kv-head) slices: {'dequantize + ' if w.method == 'quant' else ''}"
+                      f"decode of {grp} q-heads over {w.N} tokens, {t_total:.1f}s of CPU time; "
+                      f"{'extrapolated to the whole workload' if done < n_slices else 'the whole workload'}",
+            "legs": legs}
 
 
 def main():
@@ -697,6 +945,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
                      "bytes_per_launch": int(per_launch), "avg_launch_us": round(dec_avg_ms * 1e3, 3)},
     }
+    line["verify_mfma_shape"] = verify_mfma_shape() if w.name != workload("qwen30b").name else None
     line["rotation_prepass"] = measure_rotation(st)
     line["split_stream"] = measure_split_stream(st)
     if not a.no_stage:

@@ -491,7 +491,7 @@ class VeriCacheLoop:
         # per round by HorizonPolicy; buffers are sized for k
         hs = sorted(set(int(h) for h in horizons)) if horizons else [sess.k]
         assert 1 <= hs[0] and hs[-1] <= sess.k
-        self.policy = HorizonPolicy(hs) if len(hs) > 1 else None
+        self.policy = HorizonPolicy(hs) if len(hs) > 1 else None   # one horizon: drafted every round
         self.horizons = hs
         dec, s, B, dev = sess.dec, sess.dec.s, sess.B, sess.device
         G, k = sess.group, sess.k
@@ -575,15 +575,17 @@ class VeriCacheLoop:
         """One draft-and-verify round of every sequence; returns the tokens committed."""
         sess, dec, s = self.sess, self.sess.dec, self.sess.dec.s
         B, G, dev = sess.B, sess.group, sess.device
-        k = self.policy.choose() if self.policy else sess.k      # this round's horizon
+        k = self.policy.choose() if self.policy else self.horizons[-1]    # this round's horizon
         t_round = time.perf_counter()
         maxL = int(self.Lb.max())
         if timed:
             self.ev["start"].record()
+        # the draft steps' inputs first: their small host-to-device copies must not queue
+        # behind the staging copies
+        self._set_draft_inputs()
         # ---- staging of the first slots' layers starts now, overlapping the drafts
         self.full.begin(maxL, int(self.Lb.min()), maxL + k)
         # ---- k draft steps on the compressed cache
-        self._set_draft_inputs()
         if self.graphs:
             self.graphs[k].replay()
         else:
@@ -609,7 +611,6 @@ class VeriCacheLoop:
         if timed:
             self.ev["verified"].record()
         acc, nc, com = self.acc.cpu().numpy(), self.nc.cpu().numpy(), com.cpu().numpy()  # the round's one sync
-        t_round = time.perf_counter() - t_round
         # a sequence that already has its tokens stays where it is (its rows are still
         # computed, within the cache, and discarded)
         active = np.array([len(o) < sess.gen for o in self.out])
@@ -650,7 +651,10 @@ class VeriCacheLoop:
         self.rounds += 1
         self.accept_lens.extend(int(a) for a in acc[active])
         if self.policy:
-            self.policy.update(k, t_round, acc[active])
+            # the round's whole cost, its cache update included, is charged to its own
+            # horizon: wait for the update's device work before reading the clock
+            torch.cuda.current_stream().synchronize()
+            self.policy.update(k, time.perf_counter() - t_round, acc[active])
         return int(nc.sum())
 
     def run(self, timed=False):
