@@ -16,7 +16,7 @@ SMALL = {
     "tiny_fp32": C.TINY,
     "llama8b": C.small(C.LLAMA8B, N=3000),                 # H=4, k=32: M=128
     "drop_k40": C.small(C.DROP, N=2500, Hkv=1, Hq=4),      # H=4, k=40: M=160 (one 8-wave block)
-    "qwen30b_k40": C.small(C.QWEN30B, N=1100, Hkv=1, Hq=8),  # H=8, k=40: M=320 (two row blocks)
+    "qwen30b_k40": C.small(C.QWEN30B, N=1100, Hkv=1, Hq=8),  # H=8, k=40: M=320 (one mixed 8-wave block)
     "d64_k7": C.small(C.LLAMA8B, N=700, d=64, k=7),
 }
 
@@ -137,8 +137,8 @@ def test_verify_deterministic():
 def test_full_size_verify_sampled_rows(name):
     """The benchmark's verify shapes at full size, in the launch configuration it
     times (Llama-3-8B-shaped 32k, k 32: 128 rows per kv-head; token-dropping 131k,
-    k 40: 160 rows, one 8-wave block; Qwen-shaped 64k, k 40: 320 rows, three
-    blocks); sampled rows against the oracle."""
+    k 40: 160 rows, one 8-wave block; Qwen-shaped 64k, k 40: 320 rows, one mixed
+    8-wave block of 3- and 2-tile waves); sampled rows against the oracle."""
     w = {"llama8b": C.LLAMA8B, "drop": C.DROP, "qwen30b": C.QWEN30B}[name]
     dt = torch.bfloat16
     rows = w.N + w.k
