@@ -48,6 +48,27 @@ __device__ __forceinline__ float warp_sum(float v) {
 __device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
+// Buffer descriptor over `bytes` bytes from `base` (raw, stride 0): 16-byte loads at
+// offsets at or past `bytes` return zeros.  Every field is made wave-uniform.
+typedef int32_t buf_rsrc_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ buf_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  buf_rsrc_t r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(p));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((p >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(bytes));
+  r.w = 0x00020000;
+  return r;
+}
+// Buffer -> LDS copy of 16 bytes per active lane at (lds + 16 * lane), from byte
+// offset soff + voff of the descriptor's range: the per-lane part voff stays in a
+// register, the wave-uniform part soff is a scalar, so that moving the copy along
+// the buffer costs no vector instruction (inline assembly for the reason given at
+// lds_copy16).
+__device__ __forceinline__ void lds_copy16_buf_so(buf_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "s"(lds)
+               : "memory", "m0");
+}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");

@@ -13,9 +13,10 @@
 //   dequantize K and V into LDS (float32), scores per (head, token), online
 //   softmax per head (base-2, scale folded into q), then P.V accumulated in
 //   registers per (head, channel).  Each split writes (m, l, o) partials to the
-//   workspace; the last split of a (sequence, kv-head) to finish -- found with an
-//   atomic counter -- merges all splits in split order (deterministic) and writes
-//   the normalized output and the log-sum-exp, then resets its counter to zero.
+//   workspace; decode_merge_kernel, launched next, merges the splits of each
+//   (sequence, kv-head) in split order (deterministic) and writes the normalized
+//   output and the log-sum-exp.  The matrix-core and kept-row kernels cover only
+//   the compressed rows; their merge adds the full-precision tail rows itself.
 
 #include <mutex>
 
@@ -231,16 +232,18 @@ static DecodePlan plan_decode(const vc_ckv* c, int H) {
   // kept bf16 rows, d = 128: the verification tile loop with one query row per head
   p.dense = !p.mfma && c->method == VC_DROP_TOPK && c->kv_dtype == VC_BF16 && c->d == 128 && H <= 16;
   if (p.mfma) {
-    p.S = decode_mfma_splits(c);  // compressed-row splits + one tail split
-    p.chunk = cdiv(cdiv(c->n_main > 0 ? c->n_main : 1, p.S - 1), 128) * 128;
+    // compressed-row splits (the kernel deals the rows out itself); the tail rows are
+    // merged by decode_merge_kernel
+    p.S = decode_mfma_splits(c);
+    p.chunk = 0;
   } else if (p.dense) {
-    // two 4-wave workgroups per compute unit (64 KB of LDS each): row splits and the
-    // tail split together fill the device once
+    // two 4-wave workgroups per compute unit (64 KB of LDS each): the row splits
+    // fill the device once; the tail rows are merged by decode_merge_kernel
     const int bh = c->B * c->Hkv;
     p.S = 512 / bh;
-    if (p.S < 2) p.S = 2;
-    if (p.S > kDecMaxSplits) p.S = kDecMaxSplits;
-    p.chunk = cdiv(cdiv(c->n_main > 0 ? c->n_main : 1, p.S - 1), 64) * 64;
+    if (p.S < 1) p.S = 1;
+    if (p.S > kDecMaxSplits - 1) p.S = kDecMaxSplits - 1;
+    p.chunk = cdiv(cdiv(c->n_main > 0 ? c->n_main : 1, p.S), 64) * 64;
   } else {
     p.S = decode_splits(c);
     const int64_t total = c->n_main + c->tail_len;
@@ -308,12 +311,16 @@ static vc_status decode_launch(const vc_ckv* c, const void* q, int H, float sm_s
   a.part_ml = reinterpret_cast<float*>(w);
 
   const dim3 grid(p.S, static_cast<unsigned>(bh));
+  // the matrix-core and kept-row kernels leave the tail rows (bf16, d = 128) to the
+  // merge; the generic kernel's splits cover them
   auto merge = [&]() -> vc_status {
     const dim3 mgrid(static_cast<unsigned>(bh), static_cast<unsigned>(H));
-    if (c->kv_dtype == VC_BF16)
-      hipLaunchKernelGGL(decode_merge_kernel<bf16_t>, mgrid, dim3(kDecThreads), 0, s, a);
+    if (p.mfma || p.dense)
+      hipLaunchKernelGGL((decode_merge_kernel<bf16_t, true>), mgrid, dim3(kDecThreads), 0, s, a);
+    else if (c->kv_dtype == VC_BF16)
+      hipLaunchKernelGGL((decode_merge_kernel<bf16_t, false>), mgrid, dim3(kDecThreads), 0, s, a);
     else
-      hipLaunchKernelGGL(decode_merge_kernel<float>, mgrid, dim3(kDecThreads), 0, s, a);
+      hipLaunchKernelGGL((decode_merge_kernel<float, false>), mgrid, dim3(kDecThreads), 0, s, a);
     VC_LAUNCHED("decode_merge_kernel");
     return VC_OK;
   };

@@ -47,126 +47,100 @@ __device__ __forceinline__ int64_t dec_tail_len(const DecodeArgs& a, int b) {
                      : a.tail_len;
 }
 
-// Tail rows (full precision, bf16, d = 128) of one (sequence, kv-head), H <= 16
-// q-heads; writes the partial of `split`.  Rows go in chunks of 64, all in
-// parallel: one thread per (head, row) score, one wave per head for the chunk's
-// softmax (online across chunks), and for the outputs 16 lanes per head covering
-// 8 channels each, the chunk's rows strided over the remaining threads and summed
-// in a fixed order through LDS.  lds: >= 5 * 1024 floats of scratch.
-__device__ void decode_tail_partial_d128(const DecodeArgs& a, int bh, int split, float* lds) {
-  constexpr int D = 128, TC = 64;
+// Partial of the full-precision tail rows (bf16, d = 128) for q-head h of one
+// (sequence, kv-head), by the 256 threads of a merge workgroup, float32 throughout.
+// Rows go in chunks of 64 with an online softmax across chunks.  The partial is on
+// the path of every decode call after the decode kernel, so the work is spread to
+// keep the chain of dependent steps short: the query slice, a chunk's K rows and
+// its V values are loaded at once (tail_load, issued before the merge's own loads),
+// then (tail_chunk)
+// * scores: four threads per row, 32 channels each, summed over the quad;
+// * every wave takes the chunk's maximum and the sum of its probabilities itself
+//   (one row per lane), so all threads know them;
+// * outputs: thread (c, part) sums channel c over the rows of parity `part`.
+// The running maximum and sum end in every thread, the output share of channel c
+// in thread (c, part).
+struct TailPartial {
+  float m, l, o;
+};
+constexpr int kTailChunk = 64;
+struct TailRegs {
+  uint4 qw[4], kw[4];             // the query's and a K row's channels 32 quarter .. + 31
+  uint32_t vr[kTailChunk / 2];    // V channel c of the rows of parity part (bf16 bits)
+};
+// Loads of rows [r0, r0 + nr) (0 <= nr <= 64); rows past the end read the last row,
+// or with no rows at all the first 256 bytes of the partials (no branch around a
+// load, so they issue back to back and ahead of the merge's own loads): their
+// scores are dropped and their probabilities are 0.
+__device__ __forceinline__ void tail_load(TailRegs& x, const DecodeArgs& a, int bh, int h, int r0, int nr) {
+  constexpr int D = 128;
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int H = a.H;
-  const int tl = static_cast<int>(min(dec_tail_len(a, b), a.tail_cap));
-  float* s_q = lds;                    // [16][128] scaled queries
-  float* s_p = lds + 16 * D;           // [16][64] scores, then probabilities
-  float* s_red = lds + 16 * D + 16 * TC;  // [16 * RS][128] per-row-set output sums
-  float* s_st = s_red + 16 * D;        // [3][16] running max, running sum, rescale
-  const bf16_t* q = static_cast<const bf16_t*>(a.q) + (static_cast<int64_t>(b) * a.Hkv * H + hk * H) * D;
-  const bf16_t* tk = static_cast<const bf16_t*>(a.tail_k) + static_cast<int64_t>(bh) * a.tail_cap * D;
-  const bf16_t* tv = static_cast<const bf16_t*>(a.tail_v) + static_cast<int64_t>(bh) * a.tail_cap * D;
-  for (int e = tid; e < H * D; e += kDecThreads) s_q[e] = bf16_to_f32(q[e]) * a.qscale;
-  if (tid < H) {
-    s_st[tid] = -INFINITY;
-    s_st[16 + tid] = 0.f;
+  const int tid = threadIdx.x, c = tid % D, part = tid / D, rr = tid >> 2, quarter = tid & 3;
+  const bf16_t* q = static_cast<const bf16_t*>(a.q) + (static_cast<int64_t>(b) * a.Hkv * a.H + hk * a.H + h) * D;
+  const bool rows = nr > 0;
+  const bf16_t* tk = rows ? static_cast<const bf16_t*>(a.tail_k) + static_cast<int64_t>(bh) * a.tail_cap * D
+                          : reinterpret_cast<const bf16_t*>(a.part_o);
+  const uint16_t* tv = rows ? reinterpret_cast<const uint16_t*>(a.tail_v) + static_cast<int64_t>(bh) * a.tail_cap * D
+                            : reinterpret_cast<const uint16_t*>(a.part_o);
+  if (!rows) r0 = 0, nr = 1;
+  const int kr = min(rr, nr - 1);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    x.qw[u] = reinterpret_cast<const uint4*>(q + 32 * quarter)[u];
+    x.kw[u] = reinterpret_cast<const uint4*>(tk + static_cast<int64_t>(r0 + kr) * D + 32 * quarter)[u];
   }
-  const int RS = 16 / H;  // row sets per head in the output pass
-  float acc[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-  for (int r0 = 0; r0 < tl; r0 += TC) {
-    const int nr = min(TC, tl - r0);
-    __syncthreads();
-    // scores
-    for (int e = tid; e < H * TC; e += kDecThreads) {
-      const int hh = e / TC, r = e % TC;
-      float sc = -INFINITY;
-      if (r < nr) {
-        const uint4* kr = reinterpret_cast<const uint4*>(tk + static_cast<int64_t>(r0 + r) * D);
-        const float* qh = s_q + hh * D;
-        float x = 0.f;
+  for (int j = 0; j < kTailChunk / 2; ++j) x.vr[j] = tv[static_cast<int64_t>(r0 + min(part + 2 * j, nr - 1)) * D + c];
+}
+__device__ __forceinline__ void tail_chunk(TailPartial& t, const TailRegs& x, float qscale, int nr, float* s_s) {
+  const int tid = threadIdx.x, lane = tid & 63, part = tid / 128, rr = tid >> 2, quarter = tid & 3;
+  auto f32_lo = [](uint32_t w) { return __uint_as_float(w << 16); };
+  auto f32_hi = [](uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); };
+  float y = 0.f;
 #pragma unroll
-        for (int v = 0; v < D / 8; ++v) {
-          const uint4 w = kr[v];
-          const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t qs[4] = {x.qw[u].x, x.qw[u].y, x.qw[u].z, x.qw[u].w};
+    const uint32_t ks[4] = {x.kw[u].x, x.kw[u].y, x.kw[u].z, x.kw[u].w};
 #pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const float kv = __uint_as_float((c & 1) ? (ws[c >> 1] & 0xFFFF0000u) : (ws[c >> 1] << 16));
-            x = fmaf(qh[8 * v + c], kv, x);
-          }
-        }
-        sc = x;
-      }
-      s_p[hh * TC + r] = sc;
-    }
-    __syncthreads();
-    // softmax of the chunk, one wave per head
-    for (int hh = wave; hh < H; hh += kDecThreads / 64) {
-      const float v = s_p[hh * TC + lane];
-      const float mo = s_st[hh];
-      const float mn = fmaxf(mo, warp_max(v));
-      const float p = v == -INFINITY ? 0.f : exp2f(v - mn);
-      s_p[hh * TC + lane] = p;
-      const float sum = warp_sum(p);
-      if (lane == 0) {
-        const float sc = mo == -INFINITY ? 0.f : exp2f(mo - mn);
-        s_st[32 + hh] = sc;
-        s_st[16 + hh] = s_st[16 + hh] * sc + sum;
-        s_st[hh] = mn;
-      }
-    }
-    __syncthreads();
-    // weighted rows: thread (head, row set, 8-channel group)
-    if (tid < 16 * H * RS) {
-      const int c8 = tid & 15, g = tid >> 4, hh = g / RS, rs = g % RS;
-      float part[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) part[c] = 0.f;
-      for (int r = rs; r < nr; r += RS) {
-        const float p = s_p[hh * TC + r];
-        const uint4 w = *reinterpret_cast<const uint4*>(tv + static_cast<int64_t>(r0 + r) * D + 8 * c8);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          part[c] = fmaf(p, __uint_as_float((c & 1) ? (ws[c >> 1] & 0xFFFF0000u) : (ws[c >> 1] << 16)), part[c]);
-      }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) s_red[g * D + 8 * c8 + c] = part[c];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = tid + kDecThreads * j;
-      if (e < H * D) {
-        const int hh = e / D, c = e % D;
-        float v = 0.f;
-        for (int rs = 0; rs < RS; ++rs) v += s_red[(hh * RS + rs) * D + c];
-        acc[j] = fmaf(acc[j], s_st[32 + hh], v);
-      }
+    for (int e = 0; e < 4; ++e) {
+      y = fmaf(f32_lo(qs[e]), f32_lo(ks[e]), y);
+      y = fmaf(f32_hi(qs[e]), f32_hi(ks[e]), y);
     }
   }
+  y += __shfl_xor(y, 1);
+  y += __shfl_xor(y, 2);
+  if (quarter == 0) s_s[rr] = y * qscale;
   __syncthreads();
-  const int64_t pbase = static_cast<int64_t>(bh) * a.splits + split;
+  const float sr = lane < nr ? s_s[lane] : -INFINITY;
+  const float mn = fmaxf(t.m, warp_max(sr));
+  const float pr = lane < nr ? exp2f(sr - mn) : 0.f;
+  const float lc = warp_sum(pr);
+  __syncthreads();  // every wave has read the scores
+  if (tid < 64) s_s[lane] = pr;
+  __syncthreads();
+  const float sc = t.m == -INFINITY ? 0.f : exp2f(t.m - mn);
+  float o = t.o * sc;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int e = tid + kDecThreads * j;
-    if (e < H * D) a.part_o[pbase * H * D + e] = acc[j];
-  }
-  if (tid < H) {
-    a.part_ml[(pbase * H + tid) * 2] = s_st[tid];
-    a.part_ml[(pbase * H + tid) * 2 + 1] = s_st[16 + tid];
-  }
+  for (int j = 0; j < kTailChunk / 2; ++j)
+    o = fmaf(s_s[part + 2 * j], __uint_as_float(x.vr[j] << 16), o);
+  t.o = o;
+  t.l = t.l * sc + lc;
+  t.m = mn;
+  __syncthreads();  // s_s is rewritten by the next chunk
 }
 
 // Merge of the split partials of one (sequence, kv-head) per workgroup, in split
 // order (the result does not depend on which split finished first).  A kernel of
 // its own: handing the partials from one workgroup to another inside the decode
 // kernel would need a device-scope release by every workgroup, which on a part
-// with several L2 caches costs a write-back of its L2 each time.
-template <typename T>
+// with several L2 caches costs a write-back of its L2 each time.  TAIL: the
+// full-precision tail rows (bf16, d = 128) are not in the splits; the workgroup
+// computes their partial itself (while its loads of the split partials are in
+// flight) and merges it after the splits.
+template <typename T, bool TAIL>
 __global__ void __launch_bounds__(kDecThreads) decode_merge_kernel(DecodeArgs a) {
-  // one workgroup per (sequence, kv-head) and q-head of it; splits <= 64
+  // one workgroup per (sequence, kv-head) and q-head of it; splits (and the tail)
+  // <= 64
   __shared__ float s_w[kDecMaxSplits];
   __shared__ float s_fin[2];
   __shared__ float s_part[kDecThreads];
@@ -183,20 +157,37 @@ __global__ void __launch_bounds__(kDecThreads) decode_merge_kernel(DecodeArgs a)
   const int s_lo = part < tpo ? part * per : S, s_hi = min(S, s_lo + per);
   const float* p = a.part_o + (static_cast<int64_t>(bh) * S * H + h) * d + c;
   const int64_t stride = static_cast<int64_t>(H) * d;
+  TailPartial t{-INFINITY, 0.f, 0.f};
+  TailRegs tr;
+  const int tl = TAIL ? static_cast<int>(min(dec_tail_len(a, b), a.tail_cap)) : 0;
+  if (TAIL) tail_load(tr, a, bh, h, 0, min(tl, kTailChunk));
   float v[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) v[j] = s_lo + j < s_hi ? p[(s_lo + j) * stride] : 0.f;
-  if (tid < 64) {  // split weights: a wave holds one split per lane
+  if constexpr (TAIL) {
+    __shared__ float s_s[kTailChunk];
+    if (tl > 0) {
+      tail_chunk(t, tr, a.qscale, min(tl, kTailChunk), s_s);
+      for (int r0 = kTailChunk; r0 < tl; r0 += kTailChunk) {
+        tail_load(tr, a, bh, h, r0, min(tl - r0, kTailChunk));
+        tail_chunk(t, tr, a.qscale, min(tl - r0, kTailChunk), s_s);
+      }
+    }
+  }
+  if (tid < 64) {  // split weights: a wave holds one split per lane (the tail after them)
     float m = -INFINITY, l = 0.f;
     if (tid < S) {
       const float2 mv = reinterpret_cast<const float2*>(a.part_ml)[(static_cast<int64_t>(bh) * S + tid) * H + h];
       m = mv.x;
       l = mv.y;
+    } else if (TAIL && tid == S) {
+      m = t.m;
+      l = t.l;
     }
     const float M = warp_max(m);
     const float w = m == -INFINITY ? 0.f : exp2f(m - M);
     const float L = warp_sum(l * w);
-    if (tid < S) s_w[tid] = w;
+    if (tid < S + (TAIL ? 1 : 0)) s_w[tid] = w;
     if (tid == 0) {
       s_fin[0] = M;
       s_fin[1] = L;
@@ -214,6 +205,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_merge_kernel(DecodeArgs a)
     for (int j = 0; j < 16; ++j)
       if (s0 + j < s_hi) O = fmaf(v[j], s_w[s0 + j], O);
   }
+  if (TAIL && part < 2) O = fmaf(t.o, s_w[S], O);
   s_part[tid] = O;
   __syncthreads();
   if (tid < d) {

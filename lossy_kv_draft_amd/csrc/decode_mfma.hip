@@ -10,13 +10,15 @@
 // * one wave processes 32-token blocks of one (sequence, kv-head); the q-heads that
 //   read the kv-head are the 16 columns of the B operand (zero beyond Hq/Hkv), so
 //   every packed row is read from HBM once for all of them;
-// * a code c becomes the f16 value 64 + c by moving it to bits 4.. of a byte and
-//   placing it under the exponent byte 0x54 with one v_perm_b32 per pair of codes;
+// * a code c becomes an f16 value of a fixed binade, off + w c, by placing it under
+//   the exponent bits of off: 4-bit K codes as 1024 + c or 1024 + 16 c (one AND-OR
+//   per pair of codes), other codes as 64 + c (one v_perm_b32 per pair);
 // * K needs no dequantization: with per-channel scale s and zero z, q . k_hat =
-//   sum_c (q s)_c (64 + c) + [sum_c q_c z_c - 64 sum_c (q s)_c]; the query operand
-//   becomes q * s (packed f16 multiplies) and the bracket, a bias per q-head and K
-//   group, is formed on the matrix cores when the group changes and seeds the score
-//   accumulator;
+//   sum_c (q s / w)_c (off + w c) + [sum_c q_c z_c - off sum_c (q s / w)_c]; the
+//   query operand becomes q * s / w (packed f16 multiplies) and the bracket, a bias
+//   per q-head and K group, is formed on the matrix cores when the group changes;
+//   minus the running maximum it seeds the score accumulator, so the scores come
+//   out relative to the maximum;
 // * V (per-token scale and zero): each pair becomes c * s with one packed fused
 //   multiply-add of (64 + c) by s with addend -64 s (exact, rounded once); the
 //   zero-point term sum_t p_t z_t is one extra product per block (its A operand is
@@ -34,13 +36,15 @@
 // * K's code row is read as 32-channel chunks (one 64/96/128-bit load per lane), V's
 //   as 8-channel fields of 8 tokens per lane; all loads of the next block are issued
 //   before the current block is computed and are only decoded when used;
-// * the 4 waves of a block cover consecutive token ranges and are merged in LDS; the
-//   block writes one partial per split and the tail rows are a split of their own;
-//   the splits are merged in split order by decode_merge_kernel, launched next (a
-//   merge by the last block to finish would need a device-scope release by every
-//   block, i.e. an L2 write-back per block on a part with one L2 per XCD);
-// * the number of splits is chosen so that all blocks, tail included, are resident
-//   at once (occupancy times compute units, queried from the runtime).
+// * a sequence's 32-token blocks are dealt out evenly over the waves of its
+//   workgroups (in order: wave loads differ by at most one block); the 4 waves of a
+//   workgroup are merged in LDS and the workgroup writes one partial per split;
+//   decode_merge_kernel, launched next, adds the full-precision tail rows and merges
+//   the splits in split order (a merge by the last workgroup to finish would need a
+//   device-scope release by every workgroup, i.e. an L2 write-back per workgroup on
+//   a part with one L2 per XCD);
+// * the number of splits is chosen so that all workgroups are resident at once
+//   (occupancy times compute units, queried from the runtime).
 //
 // Precision: q * s, c * s, the zero-points and p are f16 (11-bit significands) with
 // float32 accumulation; against float64 attention on the outlier workloads the error
@@ -83,30 +87,53 @@ constexpr uint32_t kSel13 = 0x04030401u;  // bytes 1, 3
 // Channel (within a lane's 8-channel k-step chunk) of contraction index j.
 template <int KB>
 __device__ __forceinline__ constexpr int korder(int j) {
-  if constexpr (KB == 4) return (j & 3) * 2 + (j >> 2);  // 0,2,4,6,1,3,5,7
-  else return (j & 1) ? (j >> 1) + 4 : (j >> 1);         // 0,4,1,5,2,6,3,7
+  return (j & 1) ? (j >> 1) + 4 : (j >> 1);  // 0,4,1,5,2,6,3,7
 }
 
-// K codes enter the score product as the f16 values 64 + c: the code sits in bits
-// 4..7 of a byte under the exponent byte 0x54 (64.0).  The scale is folded into the
-// query and the zero-point and the offset into a per-group bias (see use_kp), so K
-// needs no dequantization arithmetic; the offset is 64 rather than 1024 so that the
-// cancellation it causes in the float32 accumulation stays small.
+// K codes enter the score product as f16 values of one binade, so that the scale
+// can be folded into the query and the zero-point and the offset into a per-group
+// bias (see use_kp) and K needs no dequantization arithmetic:
+// * 4-bit codes: 1024 + c for the even channels of a word (code in bits 0..3 of a
+//   16-bit half under the exponent bits of 1024) and 1024 + 16 c for the odd ones
+//   (code in bits 4..7), each pair made by one AND-OR of the word or of the word
+//   shifted by a byte; the factor 16 of the odd channels is taken out of their
+//   query operand (q s / 16).  The cancellation of the offset in the float32
+//   accumulation, about 2^-14 of sum |q s|, stays well below the f16 rounding of
+//   q s itself (2^-11 of sum |q s c|);
+// * 2- and 3-bit codes: 64 + c (code in bits 4.. of a byte under the exponent byte
+//   0x54) by one byte permute per pair.
 constexpr uint32_t kMagicK = 0x54545454u;
 __device__ __forceinline__ uint32_t kmagic(uint32_t x, uint32_t sel) { return __builtin_amdgcn_perm(kMagicK, x, sel); }
-
-// K: the four f16 pairs (64 + c) of k-step s from a lane's 32-channel chunk (KB
-// words); pair jj holds channels korder(2jj), korder(2jj+1).
+constexpr uint32_t kMagic1024 = 0x64006400u;  // (1024, 1024) in f16
+// the offset of the K code values (negated, an f16 pair) and the factor of channel c
 template <int KB>
-__device__ __forceinline__ void kpairs(const uint32_t* w, int s, uint32_t (&out)[4]) {
+__device__ __forceinline__ constexpr uint32_t kneg_offset() { return KB == 4 ? 0xE400E400u : 0xD400D400u; }
+template <int KB>
+__device__ __forceinline__ constexpr float kweight(int c) { return (KB == 4 && (c & 1)) ? 0.0625f : 1.f; }
+
+// The constants of the 4-bit K pairs, held in registers the compiler cannot see
+// through: with two literal operands it would split each AND-OR into two
+// instructions (a VOP3 instruction takes no literal here); with the masks in scalar
+// registers and the exponent pattern in a vector register it is one v_and_or_b32.
+struct KConst {
+  uint32_t lo, hi, magic;
+  __device__ __forceinline__ KConst() : lo(0x000F000Fu), hi(0x00F000F0u), magic(kMagic1024) {
+    asm("" : "+s"(lo));
+    asm("" : "+s"(hi));
+    asm("" : "+v"(magic));
+  }
+};
+
+// K: the four f16 pairs of code values of k-step s from a lane's 32-channel chunk
+// (KB words); pair jj holds channels korder(2jj), korder(2jj+1).
+template <int KB>
+__device__ __forceinline__ void kpairs(const uint32_t* w, int s, uint32_t (&out)[4], const KConst& kc) {
   if constexpr (KB == 4) {
-    const uint32_t x = w[s];
-    const uint32_t lo = (x << 4) & 0xF0F0F0F0u;  // channels 0, 2, 4, 6
-    const uint32_t hi = x & 0xF0F0F0F0u;         // channels 1, 3, 5, 7
-    out[0] = kmagic(lo, kSel01);
-    out[1] = kmagic(lo, kSel23);
-    out[2] = kmagic(hi, kSel01);
-    out[3] = kmagic(hi, kSel23);
+    const uint32_t x = w[s], y = x >> 8;
+    out[0] = (x & kc.lo) | kc.magic;  // channels 0, 4: 1024 + c
+    out[1] = (x & kc.hi) | kc.magic;  // channels 1, 5: 1024 + 16 c
+    out[2] = (y & kc.lo) | kc.magic;  // channels 2, 6
+    out[3] = (y & kc.hi) | kc.magic;  // channels 3, 7
   } else if constexpr (KB == 2) {
     const uint32_t x = w[s >> 1];
     const uint32_t sel = (s & 1) ? kSel23 : kSel01;
@@ -187,8 +214,8 @@ __device__ __forceinline__ int slot_token(int kb, int j) { return j < 4 ? 4 * kb
 template <typename P>
 __device__ __forceinline__ float param_f32(const P* p, int i) { return Elem<P>::load(p, i); }
 
-// The ring is filled with lds_copy16 (common.h): 16 bytes per lane, global -> LDS,
-// with the vmcnt waits placed by the kernel itself.
+// The ring is filled with lds_copy16_buf_so (common.h): 16 bytes per lane, global ->
+// LDS, with the vmcnt waits placed by the kernel itself.
 
 // Slot layout of one 32-token block and the ring depth for one kernel instance.
 template <int KB, int VB, int NGV, typename P>
@@ -206,7 +233,7 @@ struct DecRing {
   static constexpr int kOffKP = kOffVP + 2 * kVP;
   static constexpr int kSlot = kOffKP + kNKG * 2 * kKPG;
   static constexpr int pieces(int bytes) { return (bytes + 1023) / 1024; }
-  static constexpr int kInstr = pieces(kKC) + pieces(kVC) + pieces(2 * kVP) + kNKG * pieces(2 * kKPG);
+  static constexpr int kInstr = pieces(kKC) + pieces(kVC) + 2 * pieces(kVP) + kNKG * 2 * pieces(kKPG);
   // kWgPerCu workgroups of 4 waves per compute unit share its 160 KB of LDS (~2.5 KB
   // of each outside the ring): 4 * depth * slot <= 160 KB / kWgPerCu - 2.5 KB.  Three
   // (three waves per SIMD, at most 168 registers a wave: a shallower ring, but more
@@ -218,22 +245,13 @@ struct DecRing {
   static_assert(kSlot % 16 == 0 && kVP % 16 == 0 && kKPG % 16 == 0, "16-byte pieces");
   static_assert((kDepth - 1) * kInstr <= 63, "vmcnt range");
 
-  // `bytes` contiguous bytes from src into LDS at `lds`
-  static __device__ __forceinline__ void copy_span(const unsigned char* src, int bytes, uint32_t lds, int lane) {
+  // `bytes` contiguous bytes at byte soff of buffer r into LDS at `lds`, 16 bytes per
+  // lane and instruction (voff = 16 * lane)
+  static __device__ __forceinline__ void copy_buf(buf_rsrc_t r, uint32_t soff, int bytes, uint32_t lds, uint32_t voff,
+                                                  int lane) {
 #pragma unroll
-    for (int c = 0; c < pieces(bytes); ++c) {
-      const int off = 1024 * c + 16 * lane;
-      if (off < bytes) lds_copy16(src + off, lds + 1024 * c);
-    }
-  }
-  // `bytes` from a, then `bytes` from b, into LDS at `lds` back to back
-  static __device__ __forceinline__ void copy_pair(const unsigned char* a, const unsigned char* b, int bytes,
-                                                   uint32_t lds, int lane) {
-#pragma unroll
-    for (int c = 0; c < pieces(2 * bytes); ++c) {
-      const int off = 1024 * c + 16 * lane;
-      if (off < 2 * bytes) lds_copy16(off < bytes ? a + off : b + (off - bytes), lds + 1024 * c);
-    }
+    for (int c = 0; c < pieces(bytes); ++c)
+      if (1024 * c + 16 * lane < bytes) lds_copy16_buf_so(r, voff, soff + 1024 * c, lds + 1024 * c);
   }
   static __device__ __forceinline__ void wait_ahead() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kDepth - 1) * kInstr) : "memory");
@@ -264,25 +282,22 @@ decode_mfma_kernel(DecodeArgs a) {
   // waves' outputs for the merge (and, in the tail block, the tail pass's scratch)
   __shared__ __attribute__((aligned(16))) unsigned char ring[4 * Ring::kDepth * Ring::kSlot];
   static_assert(4 * Ring::kDepth * Ring::kSlot >= 4 * 16 * D * sizeof(float), "merge buffer does not fit");
-  static_assert(4 * Ring::kDepth * Ring::kSlot >= 5 * 1024 * sizeof(float), "tail scratch does not fit");
   float (*sh_o)[16][D] = reinterpret_cast<float (*)[16][D]>(ring);
   __shared__ float sh_m[4][16], sh_l[4][16];
   __shared__ __attribute__((aligned(16))) uint32_t sh_kq[4][2][4][16];  // per wave: K scale / zero f16 pairs
 
   const int split = blockIdx.x, bh = blockIdx.y;
-  if (split == a.splits - 1) {  // the full-precision tail rows form the last split
-    decode_tail_partial_d128(a, bh, split, reinterpret_cast<float*>(ring));
-    return;
-  }
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
   const int n = lane & 15, kb = lane >> 4;
   const int H = a.H;
   const int main_len = static_cast<int>(dec_main_len(a, b));
-  const int wchunk = static_cast<int>(a.chunk / 4);
-  const int t_begin = split * static_cast<int>(a.chunk) + wave * wchunk;
-  const int t_end = min(main_len, t_begin + wchunk);
+  // the sequence's 32-row blocks dealt out evenly over the 4 * splits waves of its
+  // workgroups, in order (so the wave loads differ by at most one block)
+  const int nb_all = (main_len + 31) / 32, nwaves = 4 * a.splits, wv = 4 * split + wave;
+  const int t_begin = 32 * static_cast<int>(static_cast<int64_t>(wv) * nb_all / nwaves);
+  const int t_end = min(main_len, 32 * static_cast<int>(static_cast<int64_t>(wv + 1) * nb_all / nwaves));
 
   // queries as the B operand: column n = q-head n of this kv-head (0 beyond H),
   // lane group kb holds channels 32 kb + 8 s + korder(j) for k-step s
@@ -330,7 +345,13 @@ decode_mfma_kernel(DecodeArgs a) {
   // P.V product (one more product with an all-ones A operand, so every row of a
   // column holds the column's sum)
   f4_t accl = f4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;
+  // The running column maximum m is a reference that the scores are taken relative
+  // to: the score accumulators are seeded with (bias - m), so the exponent needs no
+  // subtraction.  Until the first block sets it, m is 0 and every block rescales
+  // (thr = -inf); afterwards a block rescales when a score exceeds m by more than 8.
+  float m = 0.f;
+  float thr = -INFINITY;
+  f4_t seed = f4_t{0.f, 0.f, 0.f, 0.f};  // the current K group's bias minus m
   // the score operands of one K group: the queries times the group's scales (the B
   // operand of the scores) and sum_c q_c z_c - 64 sum_c qt_c per q-head column
   struct KQ {
@@ -353,22 +374,36 @@ decode_mfma_kernel(DecodeArgs a) {
   const unsigned char* kzb = reinterpret_cast<const unsigned char*>(kzero);
   const unsigned char* vsb = reinterpret_cast<const unsigned char*>(vscale);
   const unsigned char* vzb = reinterpret_cast<const unsigned char*>(vzero);
+  // buffer descriptors over this wave's rows of each array (whole 32-row blocks) and
+  // the K groups they touch: the copies move along them by scalar offsets
+  const uint32_t wrows = 32u * static_cast<uint32_t>(nblk);
+  const int g_first = t_begin / G;
+  const uint32_t g_count = nblk > 0 ? static_cast<uint32_t>((t_begin + static_cast<int>(wrows) - 1) / G - g_first + 1) : 0u;
+  const buf_rsrc_t rk = buf_rsrc(kbytes + static_cast<size_t>(t_begin) * KW * 4, wrows * KW * 4);
+  const buf_rsrc_t rv = buf_rsrc(vbytes + static_cast<size_t>(t_begin) * VW * 4, wrows * VW * 4);
+  const buf_rsrc_t rvs = buf_rsrc(vsb + static_cast<size_t>(t_begin) * NGV * sizeof(P), wrows * NGV * sizeof(P));
+  const buf_rsrc_t rvz = buf_rsrc(vzb + static_cast<size_t>(t_begin) * NGV * sizeof(P), wrows * NGV * sizeof(P));
+  const buf_rsrc_t rks = buf_rsrc(ksb + static_cast<size_t>(g_first) * Ring::kKPG, g_count * Ring::kKPG);
+  const buf_rsrc_t rkz = buf_rsrc(kzb + static_cast<size_t>(g_first) * Ring::kKPG, g_count * Ring::kKPG);
+  const uint32_t voff = 16u * static_cast<uint32_t>(lane);
   auto issue = [&](int i) {  // block i of this wave's range into slot i % kDepth
-    const uint32_t t0 = static_cast<uint32_t>(t_begin + 32 * i);
+    const uint32_t r0 = 32u * static_cast<uint32_t>(i);  // its first row within the range
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
         static_cast<uint32_t>(reinterpret_cast<uintptr_t>(wring + (i % Ring::kDepth) * Ring::kSlot)));
     // codes: 32 consecutive rows of each
-    Ring::copy_span(kbytes + static_cast<size_t>(t0) * KW * 4, Ring::kKC, lds + Ring::kOffK, lane);
-    Ring::copy_span(vbytes + static_cast<size_t>(t0) * VW * 4, Ring::kVC, lds + Ring::kOffV, lane);
+    Ring::copy_buf(rk, r0 * KW * 4, Ring::kKC, lds + Ring::kOffK, voff, lane);
+    Ring::copy_buf(rv, r0 * VW * 4, Ring::kVC, lds + Ring::kOffV, voff, lane);
     // V parameters: scales of the 32 rows, then zeros
-    Ring::copy_pair(vsb + static_cast<size_t>(t0) * NGV * sizeof(P), vzb + static_cast<size_t>(t0) * NGV * sizeof(P),
-                    Ring::kVP, lds + Ring::kOffVP, lane);
+    Ring::copy_buf(rvs, r0 * NGV * sizeof(P), Ring::kVP, lds + Ring::kOffVP, voff, lane);
+    Ring::copy_buf(rvz, r0 * NGV * sizeof(P), Ring::kVP, lds + Ring::kOffVP + Ring::kVP, voff, lane);
     // K parameters of the block's group(s): [scale row, zero row] per group
-    const uint32_t g0 = t0 / G;
+    const uint32_t g0 = static_cast<uint32_t>((t_begin + static_cast<int>(r0)) / G - g_first);
 #pragma unroll
-    for (int gi = 0; gi < NKG; ++gi)
-      Ring::copy_pair(ksb + static_cast<size_t>(g0 + gi) * D * sizeof(P), kzb + static_cast<size_t>(g0 + gi) * D * sizeof(P),
-                      D * sizeof(P), lds + Ring::kOffKP + gi * 2 * D * sizeof(P), lane);
+    for (int gi = 0; gi < NKG; ++gi) {
+      const uint32_t kp = lds + Ring::kOffKP + gi * 2 * Ring::kKPG;
+      Ring::copy_buf(rks, (g0 + gi) * Ring::kKPG, Ring::kKPG, kp, voff, lane);
+      Ring::copy_buf(rkz, (g0 + gi) * Ring::kKPG, Ring::kKPG, kp + Ring::kKPG, voff, lane);
+    }
   };
 
   struct Blk {
@@ -405,7 +440,8 @@ decode_mfma_kernel(DecodeArgs a) {
   };
   // A new K group: the lane's 32 channels of its (scale, zero) rows are read from the
   // block's slot and packed as f16 pairs in contraction order; the query operand
-  // becomes q * s and the bias sum_c q_c z_c - 64 sum_c (q s)_c is formed on the
+  // becomes q * s (times the channel's factor) and the bias sum_c q_c z_c minus the
+  // code offset times sum_c (q s)_c is formed on the
   // matrix cores (every row of its A operands is the same, so every score row of a
   // column receives its column's bias).
   auto use_kp = [&](const unsigned char* kp) -> KQ {
@@ -417,12 +453,12 @@ decode_mfma_kernel(DecodeArgs a) {
       const int c0 = 32 * kb + 8 * st + korder<KB>(2 * jj), c1 = 32 * kb + 8 * st + korder<KB>(2 * jj + 1);
       const P* sp = reinterpret_cast<const P*>(kp);
       const P* zp = sp + D;
-      sh_kq[wave][0][kb][n] = pack_h2(param_f32<P>(sp, c0), param_f32<P>(sp, c1));
+      sh_kq[wave][0][kb][n] = pack_h2(param_f32<P>(sp, c0) * kweight<KB>(c0), param_f32<P>(sp, c1) * kweight<KB>(c1));
       sh_kq[wave][1][kb][n] = pack_h2(param_f32<P>(zp, c0), param_f32<P>(zp, c1));
     }
     __builtin_amdgcn_wave_barrier();
-    constexpr uint32_t kNeg64 = 0xD400D400u;  // (-64, -64) in f16
-    const uint32_t neg64[4] = {kNeg64, kNeg64, kNeg64, kNeg64};
+    constexpr uint32_t kNegOff = kneg_offset<KB>();
+    const uint32_t negoff[4] = {kNegOff, kNegOff, kNegOff, kNegOff};
     KQ r;
     r.kbias = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -438,7 +474,7 @@ decode_mfma_kernel(DecodeArgs a) {
       for (int jj = 0; jj < 4; ++jj) q2[jj] = as_u32(as_h2(qw[jj]) * as_h2(s2[jj]));
       r.qt[s] = __builtin_bit_cast(h8_t, q2);
       r.kbias = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, z2), bq[s], r.kbias, 0, 0, 0);
-      r.kbias = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, neg64), r.qt[s], r.kbias, 0, 0, 0);
+      r.kbias = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, negoff), r.qt[s], r.kbias, 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
     return r;
@@ -459,6 +495,7 @@ decode_mfma_kernel(DecodeArgs a) {
 
   // kq: the score operands of the block's K group when a group spans whole blocks
   // (G >= 32); with 16-token groups each 16-token tile forms its own from the slot
+  const KConst kc;
   auto process = [&](int t0, const Blk& cur, const unsigned char* slot, const KQ& kq, auto full_tag) {
     constexpr bool full = decltype(full_tag)::value;  // every row of the block is live
     // ---- S^T = K_hat Q^T for the two 16-token tiles
@@ -468,11 +505,12 @@ decode_mfma_kernel(DecodeArgs a) {
       KQ kt;
       if constexpr (NKG == 2) kt = use_kp(slot + Ring::kOffKP + tt * 2 * D * sizeof(P));
       const KQ& k = NKG == 2 ? kt : kq;
-      sc[tt] = k.kbias;
+      if constexpr (NKG == 2) sc[tt] = k.kbias - m;
+      else sc[tt] = seed;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         uint32_t mp[4];
-        kpairs<KB>(cur.kw[tt], s, mp);
+        kpairs<KB>(cur.kw[tt], s, mp, kc);
         sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, mp), k.qt[s], sc[tt], 0, 0, 0);
       }
     }
@@ -486,22 +524,30 @@ decode_mfma_kernel(DecodeArgs a) {
     // the column maximum is only needed when some score exceeds the running maximum
     // by more than 8 (probabilities up to 2^8 are fine in f16): a wave vote on the
     // lanes' own maxima, then the cross-lane maximum inside the (rare) rescale
-    float mb = fmaxf(fmaxf(fmaxf(s8[0], s8[1]), fmaxf(s8[2], s8[3])), fmaxf(fmaxf(s8[4], s8[5]), fmaxf(s8[6], s8[7])));
-    if (__any(mb > m + 8.f)) {
+    auto vmax = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+    float mb = vmax(vmax(vmax(s8[0], s8[1]), vmax(s8[2], s8[3])), vmax(vmax(s8[4], s8[5]), vmax(s8[6], s8[7])));
+    if (__any(mb > thr)) {
       mb = fmaxf(mb, __shfl_xor(mb, 16));
       mb = fmaxf(mb, __shfl_xor(mb, 32));
-      const float mn = fmaxf(m, mb);
-      const float al = __builtin_amdgcn_exp2f(m - mn);  // m = -inf on the first block: 0
+      // the shift of the reference: the column maximum on the first block, else only
+      // upwards (thr - 8 is -inf, then 0)
+      const float dm = fmaxf(mb, thr - 8.f);
+      // accumulators are zero before the first block, so any finite factor will do
+      const float al = __builtin_amdgcn_exp2f(fminf(-dm, 0.f));
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] *= al;
       accz *= al;
       accl *= al;
-      m = mn;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s8[j] -= dm;
+      seed -= dm;
+      m += dm;
+      thr = 8.f;
     }
     float p[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      p[j] = __builtin_amdgcn_exp2f(s8[j] - m);  // v_exp_f32: results below 2^-126 flush to 0
+      p[j] = __builtin_amdgcn_exp2f(s8[j]);  // v_exp_f32: results below 2^-126 flush to 0
     }
     uint32_t pw[4];
 #pragma unroll
@@ -576,14 +622,22 @@ decode_mfma_kernel(DecodeArgs a) {
       nb = min(nb, (G - t0 % G) / 32);  // blocks left in this group
       wait_blk(i);
       kq = use_kp(wring + (i % Ring::kDepth) * Ring::kSlot + Ring::kOffKP);
+      seed = kq.kbias - m;
     }
     for (int e = i + nb; i < e; ++i) {
       wait_blk(i);
       const unsigned char* slot = wring + (i % Ring::kDepth) * Ring::kSlot;
       Blk cur;
       read_blk(slot, cur);
+      // with one K group per block every read of the slot is in cur: the slot is
+      // refilled before the block is computed, so that two blocks are in flight
+      // during the computation
+      if (NKG == 1 && i + Ring::kDepth < nblk) {
+        Ring::lds_reads_done();
+        issue(i + Ring::kDepth);
+      }
       process(t_begin + 32 * i, cur, slot, kq, Full{});
-      if (i + Ring::kDepth < nblk) {
+      if (NKG == 2 && i + Ring::kDepth < nblk) {
         Ring::lds_reads_done();
         issue(i + Ring::kDepth);
       }
@@ -593,11 +647,15 @@ decode_mfma_kernel(DecodeArgs a) {
   if (nfull < nblk) {  // the partial last block (its copies were issued above)
     const unsigned char* slot = wring + (nfull % Ring::kDepth) * Ring::kSlot;
     KQ kq;
-    if constexpr (NKG == 1) kq = use_kp(slot + Ring::kOffKP);
+    if constexpr (NKG == 1) {
+      kq = use_kp(slot + Ring::kOffKP);
+      seed = kq.kbias - m;
+    }
     Blk cur;
     read_blk(slot, cur);
     process(t_begin + 32 * nfull, cur, slot, kq, Part{});
   }
+  if (thr == -INFINITY) m = -INFINITY;  // no rows: the merge gives this wave no weight
   __syncthreads();  // every wave's copies have landed before the ring is reused
 
   // ---- merge the 4 waves in LDS, write this split's partial
@@ -703,16 +761,17 @@ struct LaunchOp {
   }
 };
 
-// Compressed-row splits sized so that they and the tail split run in one pass
-// over the device: (splits + 1) * B * Hkv workgroups <= the resident count.
+// Compressed-row splits sized so that they run in one pass over the device:
+// splits * B * Hkv workgroups <= the resident count (the tail rows are merged by
+// decode_merge_kernel, which takes one more partial).
 int decode_mfma_splits(const vc_ckv* c) {
   const int bh = c->B * c->Hkv;
   int resident = 512;
   dispatch_decode_mfma(c, ResidentOp{&resident});
-  int s = resident / bh - 1;
+  int s = resident / bh;
   if (s < 1) s = 1;
   if (s > kDecMaxSplits - 1) s = kDecMaxSplits - 1;
-  return s + 1;  // + the tail split
+  return s;
 }
 
 void launch_decode_mfma(const vc_ckv* c, const DecodeArgs& a, dim3 grid, hipStream_t s) {

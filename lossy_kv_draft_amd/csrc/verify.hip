@@ -494,15 +494,11 @@ __global__ void __launch_bounds__(512) verify_mixed_kernel(VerifyArgs a) {
 // Draft-side decode over kept (token-dropped) bf16 rows, d = 128, at most 16 q-heads
 // per kv-head: the same tile loop with one query row per q-head, a window of one and
 // the context length set to the kept rows minus one, so that row 0 attends to every
-// kept row; splits 0 .. S-2 cover the kept rows and write the decode partials, split
-// S-1 covers the full-precision tail rows; decode_merge_kernel combines them.
+// kept row; the S splits cover the kept rows and write the decode partials, and
+// decode_merge_kernel adds the full-precision tail rows and combines them.
 constexpr int kDdStages = 2;  // LDS ring of decode_dense_kernel (4 waves)
-__global__ void __launch_bounds__(kVerThreads) decode_dense_kernel(VerifyArgs a, DecodeArgs d) {
+__global__ void __launch_bounds__(kVerThreads) decode_dense_kernel(VerifyArgs a) {
   __shared__ __attribute__((aligned(16))) VtStage ring[kDdStages];
-  if (static_cast<int>(blockIdx.x) == d.splits - 1) {
-    decode_tail_partial_d128(d, blockIdx.z, d.splits - 1, reinterpret_cast<float*>(&ring[0][0]));
-    return;
-  }
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   verify_tiles<1, 4, kDdStages>(a, blockIdx.x, 16 * wave, blockIdx.z, ring);
 }
@@ -618,8 +614,8 @@ static void verify_tiling(int M, int& RT, int& nblk) {
   nblk = static_cast<int>(cdiv(M, 64 * RT));
 }
 
-// Dense decode over kept rows (see decode_dense_kernel): S - 1 row splits of `chunk`
-// positions (a multiple of the 64-position tile) plus the tail split.
+// Dense decode over kept rows (see decode_dense_kernel): S row splits of `chunk`
+// positions (a multiple of the 64-position tile).
 vc_status launch_decode_dense(const vc_ckv* c, const DecodeArgs& d, hipStream_t s) {
   VerifyArgs a{};
   a.q = d.q;
@@ -641,7 +637,7 @@ vc_status launch_decode_dense(const vc_ckv* c, const DecodeArgs& d, hipStream_t 
   a.part_o = d.part_o;
   a.part_ml = d.part_ml;
   const dim3 grid(static_cast<unsigned>(d.splits), 1, static_cast<unsigned>(c->B * c->Hkv));
-  hipLaunchKernelGGL(decode_dense_kernel, grid, dim3(kVerThreads), 0, s, a, d);
+  hipLaunchKernelGGL(decode_dense_kernel, grid, dim3(kVerThreads), 0, s, a);
   VC_LAUNCHED("decode_dense_kernel");
   return VC_OK;
 }

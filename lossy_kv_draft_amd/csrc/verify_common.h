@@ -74,18 +74,9 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int vt_chunk(int r, int c) { return c ^ (r & 15); }
 
-// Buffer descriptor over `bytes` bytes from `base` (raw, stride 0): 16-byte loads at
-// offsets at or past `bytes` return zeros.  Every field is made wave-uniform.
-typedef int32_t vt_rsrc_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ vt_rsrc_t vt_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  vt_rsrc_t r;
-  r.x = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(p));
-  r.y = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((p >> 32) & 0xFFFFu));
-  r.z = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(bytes));
-  r.w = 0x00020000;
-  return r;
-}
+// Buffer descriptors of the K/V tiles (common.h)
+typedef buf_rsrc_t vt_rsrc_t;
+__device__ __forceinline__ vt_rsrc_t vt_rsrc(const void* base, uint32_t bytes) { return buf_rsrc(base, bytes); }
 // Buffer -> LDS copy of 16 bytes per active lane at (lds + 16 * lane), from byte
 // offset voff of the descriptor's range (inline assembly for the reason given at
 // lds_copy16).

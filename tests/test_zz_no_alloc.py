@@ -64,12 +64,13 @@ def test_noalloc_decode_generic_and_ragged():
 
 
 def test_noalloc_rejects_partials_beyond_the_array():
-    """B 64 x Hkv 8 x 16 q-heads per kv-head needs more than the 8 MiB array: rejected
-    with VC_ERR_WORKSPACE, nothing written."""
-    ckv = L.Ckv("quant", 64, 8, 128, 32, k_bits=4, v_bits=4, group=32, tail_cap=1)
+    """B 128 x Hkv 8 x 16 q-heads per kv-head needs more than the 8 MiB array (one
+    split per (sequence, kv-head): 8 MiB of outputs plus their maxima and sums):
+    rejected with VC_ERR_WORKSPACE, nothing written."""
+    ckv = L.Ckv("quant", 128, 8, 128, 32, k_bits=4, v_bits=4, group=32, tail_cap=1)
     ckv.n_main = 32
-    q = torch.zeros(64, 128, 128, dtype=torch.bfloat16, device="cuda")
-    out = torch.full((64, 128, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros(128, 128, 128, dtype=torch.bfloat16, device="cuda")
+    out = torch.full((128, 128, 128), 7.0, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(L.VcError) as e:
         L.vc_decode_attn_compressed_noalloc(ckv, q, out)
     assert e.value.status == L._lib.VC_ERR_WORKSPACE and "scratch" in str(e.value)
