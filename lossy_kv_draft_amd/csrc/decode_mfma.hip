@@ -60,6 +60,8 @@ namespace vc {
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr uint32_t kMagic = 0x64646464u;  // exponent byte of 1024.0 in f16, in every byte
 
@@ -105,6 +107,7 @@ __device__ __forceinline__ constexpr int korder(int j) {
 constexpr uint32_t kMagicK = 0x54545454u;
 __device__ __forceinline__ uint32_t kmagic(uint32_t x, uint32_t sel) { return __builtin_amdgcn_perm(kMagicK, x, sel); }
 constexpr uint32_t kMagic1024 = 0x64006400u;  // (1024, 1024) in f16
+constexpr uint32_t kMagicV = 0x43004300u;     // (128, 128) in bf16
 // the offset of the K code values (negated, an f16 pair) and the factor of channel c
 template <int KB>
 __device__ __forceinline__ constexpr uint32_t kneg_offset() { return KB == 4 ? 0xE400E400u : 0xD400D400u; }
@@ -116,11 +119,14 @@ __device__ __forceinline__ constexpr float kweight(int c) { return (KB == 4 && (
 // instructions (a VOP3 instruction takes no literal here); with the masks in scalar
 // registers and the exponent pattern in a vector register it is one v_and_or_b32.
 struct KConst {
-  uint32_t lo, hi, magic;
-  __device__ __forceinline__ KConst() : lo(0x000F000Fu), hi(0x00F000F0u), magic(kMagic1024) {
+  uint32_t lo, hi, lo2, magic, vmagic;
+  __device__ __forceinline__ KConst()
+      : lo(0x000F000Fu), hi(0x00F000F0u), lo2(0x00030003u), magic(kMagic1024), vmagic(kMagicV) {
     asm("" : "+s"(lo));
     asm("" : "+s"(hi));
+    asm("" : "+s"(lo2));
     asm("" : "+v"(magic));
+    asm("" : "+v"(vmagic));
   }
 };
 
@@ -208,6 +214,22 @@ __device__ __forceinline__ void vpairs(uint32_t fa, uint32_t fb, uint32_t (&out)
   }
 }
 
+// V with the scale on the probabilities (64- and 128-channel V groups, 2- and 4-bit
+// codes): lane n holds channels 64 hf + 4 n + i of half hf (i = 0..3); comb holds the
+// lane's 4 codes of token a in its low and of token b in its high 16 bits (one byte
+// permute of the two tokens' words), and pair i becomes the bf16 values
+// (128 + a_i, 128 + b_i): code i shifted to bits 0.. of each half under the exponent
+// bits of 128, one AND-OR (after a shift for i > 0).
+template <int VB>
+__device__ __forceinline__ void vpairs_bf16(uint32_t comb, uint32_t (&out)[4], uint32_t mask, uint32_t magic) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = ((comb >> (VB * i)) & mask) | magic;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, bf16x2_t{static_cast<__bf16>(a), static_cast<__bf16>(b)});
+}
+
 // token of slot j (0..7) of lane group kb in a 32-token block
 __device__ __forceinline__ int slot_token(int kb, int j) { return j < 4 ? 4 * kb + j : 16 + 4 * kb + (j - 4); }
 
@@ -227,23 +249,45 @@ struct DecRing {
   static constexpr int kVC = 32 * kD * VB / 8;                         // V code bytes
   static constexpr int kVP = 32 * NGV * static_cast<int>(sizeof(P));  // V scale (and zero) bytes
   static constexpr int kKPG = kD * static_cast<int>(sizeof(P));        // one K parameter row
+  // The parameters go to a ring of their own, one entry per kPB = 2 blocks: the V
+  // scales of its 64 rows, their zeros, and with whole K groups per block the
+  // [scale row, zero row] of the (at most two) K groups those rows touch.  An entry
+  // is copied with its first block, by two instructions of up to 1 KB (the V
+  // parameters of a block are 128-256 bytes, too small a read to use the memory
+  // well); with two K groups per block the K parameters sit in the block's slot.
+  static constexpr bool kGroupKP = kNKG == 1;
+  static constexpr int kPB = 2;
   static constexpr int kOffK = 0;
   static constexpr int kOffV = kOffK + kKC;
-  static constexpr int kOffVP = kOffV + kVC;
-  static constexpr int kOffKP = kOffVP + 2 * kVP;
-  static constexpr int kSlot = kOffKP + kNKG * 2 * kKPG;
+  static constexpr int kOffKP = kOffV + kVC;
+  static constexpr int kSlot = kOffKP + (kGroupKP ? 0 : kNKG * 2 * kKPG);
+  static constexpr int kVPE = kPB * kVP;  // V scale (and zero) bytes of an entry
+  static constexpr int kOffEK = 2 * kVPE;
+  static constexpr int kEntry = kOffEK + (kGroupKP ? 2 * 2 * kKPG : 0);
   static constexpr int pieces(int bytes) { return (bytes + 1023) / 1024; }
-  static constexpr int kInstr = pieces(kKC) + pieces(kVC) + 2 * pieces(kVP) + kNKG * 2 * pieces(kKPG);
-  // kWgPerCu workgroups of 4 waves per compute unit share its 160 KB of LDS (~2.5 KB
-  // of each outside the ring): 4 * depth * slot <= 160 KB / kWgPerCu - 2.5 KB.  Three
-  // (three waves per SIMD, at most 168 registers a wave: a shallower ring, but more
-  // waves to hide the latency of the code conversion) where that measured faster and
-  // needs no register spills: bf16 parameters with 64-channel V groups; else two.
+  // copy instructions per block and per entry
+  static constexpr int kInstr = pieces(kKC) + pieces(kVC) + (kGroupKP ? 0 : kNKG * 2 * pieces(kKPG));
+  static constexpr int kEInstr = pieces(2 * kVPE) + (kGroupKP ? pieces(4 * kKPG) : 0);
+  // entries in the ring for a block ring of depth d: an entry is refilled when the
+  // block kPB * ring entries later is issued, i.e. while the block d before that one
+  // is processed, so every block of the entry must be at or before it
+  static constexpr int entries(int d) { return (kPB - 1 + d + kPB - 1) / kPB; }
+  // kWgPerCu workgroups of 4 waves per compute unit share its 160 KB of LDS (~3.5 KB
+  // of each outside the rings): 4 * (depth * slot + entries * entry) <= 160 KB /
+  // kWgPerCu - 3.5 KB.  Three (three waves per SIMD, at most 168 registers a wave: a
+  // shallower ring, but more waves to hide the latency of the code conversion) where
+  // that measured faster and needs no register spills: bf16 parameters with
+  // 64-channel V groups; else two.
   static constexpr int kWgPerCu = (sizeof(P) == 2 && NGV == 2) ? 3 : 2;
-  static constexpr int kDepthRaw = (163840 / kWgPerCu - 2560) / (4 * kSlot);
-  static constexpr int kDepth = kDepthRaw < 2 ? 2 : (kDepthRaw > 8 ? 8 : kDepthRaw);
-  static_assert(kSlot % 16 == 0 && kVP % 16 == 0 && kKPG % 16 == 0, "16-byte pieces");
-  static_assert((kDepth - 1) * kInstr <= 63, "vmcnt range");
+  static constexpr int depth_fit() {
+    int d = 8;
+    while (d > 2 && 4 * (d * kSlot + entries(d) * kEntry) > 163840 / kWgPerCu - 3584) --d;
+    return d;
+  }
+  static constexpr int kDepth = depth_fit();
+  static constexpr int kNE = entries(kDepth);
+  static_assert(kSlot % 16 == 0 && kVP % 16 == 0 && kKPG % 16 == 0 && kEntry % 16 == 0, "16-byte pieces");
+  static_assert((kDepth - 1) * kInstr + ((kDepth + kPB - 2) / kPB) * kEInstr <= 63, "vmcnt range");
 
   // `bytes` contiguous bytes at byte soff of buffer r into LDS at `lds`, 16 bytes per
   // lane and instruction (voff = 16 * lane)
@@ -253,8 +297,27 @@ struct DecRing {
     for (int c = 0; c < pieces(bytes); ++c)
       if (1024 * c + 16 * lane < bytes) lds_copy16_buf_so(r, voff, soff + 1024 * c, lds + 1024 * c);
   }
-  static __device__ __forceinline__ void wait_ahead() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kDepth - 1) * kInstr) : "memory");
+  // `bytes` into LDS at `lds` from the per-lane sources src[c] of pieces c
+  static __device__ __forceinline__ void copy_lanes(const unsigned char* const* src, int bytes, uint32_t lds, int lane) {
+#pragma unroll
+    for (int c = 0; c < pieces(bytes); ++c)
+      if (1024 * c + 16 * lane < bytes) lds_copy16(src[c], lds + 1024 * c);
+  }
+  template <int N>
+  static __device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  }
+  // wait for a block while the next kDepth - 1 blocks, ne of which start an entry,
+  // may still be in flight (ne wave-uniform)
+  template <int K = 0>
+  static __device__ __forceinline__ void wait_ahead(int ne) {
+    if constexpr (K < (kDepth + kPB - 2) / kPB) {
+      if (ne > K) {
+        wait_ahead<K + 1>(ne);
+        return;
+      }
+    }
+    wait_vm<(kDepth - 1) * kInstr + K * kEInstr>();
   }
   static __device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
   static __device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -279,12 +342,18 @@ decode_mfma_kernel(DecodeArgs a) {
   constexpr int NKG = G >= 32 ? 1 : 2;                // K groups per 32-token block
   using Ring = DecRing<KB, VB, NGV, P>;
   // per-wave rings of block slots; after the main loop the same memory holds the
-  // waves' outputs for the merge (and, in the tail block, the tail pass's scratch)
-  __shared__ __attribute__((aligned(16))) unsigned char ring[4 * Ring::kDepth * Ring::kSlot];
-  static_assert(4 * Ring::kDepth * Ring::kSlot >= 4 * 16 * D * sizeof(float), "merge buffer does not fit");
+  // waves' outputs for the merge
+  constexpr int kRingBytes = 4 * Ring::kDepth * Ring::kSlot > 4 * 16 * D * 4 ? 4 * Ring::kDepth * Ring::kSlot : 4 * 16 * D * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char ring[kRingBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char pring[4 * Ring::kNE * Ring::kEntry];
   float (*sh_o)[16][D] = reinterpret_cast<float (*)[16][D]>(ring);
   __shared__ float sh_m[4][16], sh_l[4][16];
   __shared__ __attribute__((aligned(16))) uint32_t sh_kq[4][2][4][16];  // per wave: K scale / zero f16 pairs
+  // V scales on the probabilities: per wave the block's V scales (float) and zeros
+  // (f16) by group, lane group and slot, converted once per block by the wave
+  constexpr bool kBS = NGV <= 2 && VB != 3;
+  __shared__ __attribute__((aligned(16))) float sh_vs[kBS ? 4 : 1][2][4][8];
+  __shared__ __attribute__((aligned(16))) _Float16 sh_vz[kBS ? 4 : 1][2][4][8];
 
   const int split = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
@@ -359,14 +428,16 @@ decode_mfma_kernel(DecodeArgs a) {
     f4_t kbias;
   };
 
-  // The block's bytes (K codes, V codes, V parameters, the K parameters of its
-  // group(s)) are copied global -> LDS by the wave itself (16 bytes per lane per
+  // The block's bytes (K codes, V codes, and with two K groups per block their K
+  // parameters) are copied global -> LDS by the wave itself (16 bytes per lane per
   // instruction, Ring::kInstr instructions per block) kDepth blocks ahead, into a
-  // ring of slots private to the wave; a block is read from its slot into registers
-  // only when it is processed.  Rows of a block that starts before the end are
-  // inside the allocation (capacity is a multiple of 32); rows past the end are
-  // masked (scores -inf, V scale and zero 0).
+  // ring of slots private to the wave; the first block of each parameter entry also
+  // copies the entry (Ring::kEInstr instructions) into the wave's parameter ring.  A
+  // block is read from its slot into registers only when it is processed.  Rows of a
+  // block that starts before the end are inside the allocation (capacity is a
+  // multiple of 32); rows past the end are masked (scores -inf, V scale and zero 0).
   unsigned char* const wring = ring + wave * Ring::kDepth * Ring::kSlot;
+  unsigned char* const wpr = pring + wave * Ring::kNE * Ring::kEntry;
   const int nblk = t_end > t_begin ? (t_end - t_begin + 31) / 32 : 0;
   const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kcodes);
   const unsigned char* vbytes = reinterpret_cast<const unsigned char*>(vcodes);
@@ -374,44 +445,117 @@ decode_mfma_kernel(DecodeArgs a) {
   const unsigned char* kzb = reinterpret_cast<const unsigned char*>(kzero);
   const unsigned char* vsb = reinterpret_cast<const unsigned char*>(vscale);
   const unsigned char* vzb = reinterpret_cast<const unsigned char*>(vzero);
-  // buffer descriptors over this wave's rows of each array (whole 32-row blocks) and
-  // the K groups they touch: the copies move along them by scalar offsets
+  // buffer descriptors over this wave's rows of the code arrays (whole 32-row
+  // blocks): the copies move along them by scalar offsets
   const uint32_t wrows = 32u * static_cast<uint32_t>(nblk);
   const int g_first = t_begin / G;
-  const uint32_t g_count = nblk > 0 ? static_cast<uint32_t>((t_begin + static_cast<int>(wrows) - 1) / G - g_first + 1) : 0u;
+  const int g_last = nblk > 0 ? (t_begin + static_cast<int>(wrows) - 1) / G : g_first;  // inside the allocation
+  const uint32_t g_count = nblk > 0 ? static_cast<uint32_t>(g_last - g_first + 1) : 0u;
   const buf_rsrc_t rk = buf_rsrc(kbytes + static_cast<size_t>(t_begin) * KW * 4, wrows * KW * 4);
   const buf_rsrc_t rv = buf_rsrc(vbytes + static_cast<size_t>(t_begin) * VW * 4, wrows * VW * 4);
-  const buf_rsrc_t rvs = buf_rsrc(vsb + static_cast<size_t>(t_begin) * NGV * sizeof(P), wrows * NGV * sizeof(P));
-  const buf_rsrc_t rvz = buf_rsrc(vzb + static_cast<size_t>(t_begin) * NGV * sizeof(P), wrows * NGV * sizeof(P));
   const buf_rsrc_t rks = buf_rsrc(ksb + static_cast<size_t>(g_first) * Ring::kKPG, g_count * Ring::kKPG);
   const buf_rsrc_t rkz = buf_rsrc(kzb + static_cast<size_t>(g_first) * Ring::kKPG, g_count * Ring::kKPG);
   const uint32_t voff = 16u * static_cast<uint32_t>(lane);
+  // Parameter entry e (blocks kPB e, kPB e + 1): each lane's 16-byte pieces.  V: piece
+  // c of the lane is byte off = 1024 c + 16 lane of [scales of the 64 rows][zeros],
+  // i.e. row off / (NGV sizeof(P)) of either; K: byte off of [scale row, zero row of
+  // the entry's first group][the same of its last group].
+  constexpr int kVPieces = Ring::pieces(2 * Ring::kVPE), kKPieces = Ring::kGroupKP ? Ring::pieces(4 * Ring::kKPG) : 1;
+  constexpr int kRowBytes = NGV * static_cast<int>(sizeof(P));  // V parameter bytes of one row
+  const unsigned char* vp_src[kVPieces];
+  int vp_row[kVPieces];  // the piece's row within the entry
+#pragma unroll
+  for (int c = 0; c < kVPieces; ++c) {
+    const int off = 1024 * c + 16 * lane;
+    const int w = off < Ring::kVPE ? off : off - Ring::kVPE;
+    vp_src[c] = (off < Ring::kVPE ? vsb : vzb) + static_cast<size_t>(t_begin) * kRowBytes + w;
+    vp_row[c] = w / kRowBytes;
+  }
+  const unsigned char* kp_src[kKPieces];
+  bool kp_last[kKPieces];  // the piece belongs to the entry's last group
+#pragma unroll
+  for (int c = 0; c < kKPieces; ++c) {
+    const int off = 1024 * c + 16 * lane, r = off / Ring::kKPG;
+    kp_src[c] = ((r & 1) ? kzb : ksb) + off % Ring::kKPG;
+    kp_last[c] = (r >> 1) != 0;
+  }
+  auto entry = [&](int i) { return wpr + ((i / Ring::kPB) % Ring::kNE) * Ring::kEntry; };  // block i's entry
+  // first group of block i's entry (absolute group index)
+  auto entry_g0 = [&](int i) { return (t_begin + 32 * Ring::kPB * (i / Ring::kPB)) / G; };
   auto issue = [&](int i) {  // block i of this wave's range into slot i % kDepth
     const uint32_t r0 = 32u * static_cast<uint32_t>(i);  // its first row within the range
+    if (i % Ring::kPB == 0) {  // the entry: V parameters of its rows, K parameters of its groups
+      const uint32_t el = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(entry(i))));
+      // rows past the range's end copy the range's first row instead (every
+      // instruction keeps its lanes, so the count the waits rely on holds); they
+      // are never read
+      const int rows = min(32 * Ring::kPB, static_cast<int>(wrows - r0));
+      const unsigned char* vs[kVPieces];
+#pragma unroll
+      for (int c = 0; c < kVPieces; ++c)
+        vs[c] = vp_row[c] < rows ? vp_src[c] + static_cast<size_t>(r0) * kRowBytes : vp_src[c] - vp_row[c] * kRowBytes;
+      Ring::copy_lanes(vs, 2 * Ring::kVPE, el, lane);
+      if constexpr (Ring::kGroupKP) {
+        const int ga = entry_g0(i), gb = min((t_begin + static_cast<int>(r0) + rows - 1) / G, g_last);
+        const unsigned char* ks[kKPieces];
+#pragma unroll
+        for (int c = 0; c < kKPieces; ++c) ks[c] = kp_src[c] + static_cast<size_t>(kp_last[c] ? gb : ga) * Ring::kKPG;
+        Ring::copy_lanes(ks, 4 * Ring::kKPG, el + Ring::kOffEK, lane);
+      }
+    }
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
         static_cast<uint32_t>(reinterpret_cast<uintptr_t>(wring + (i % Ring::kDepth) * Ring::kSlot)));
     // codes: 32 consecutive rows of each
     Ring::copy_buf(rk, r0 * KW * 4, Ring::kKC, lds + Ring::kOffK, voff, lane);
     Ring::copy_buf(rv, r0 * VW * 4, Ring::kVC, lds + Ring::kOffV, voff, lane);
-    // V parameters: scales of the 32 rows, then zeros
-    Ring::copy_buf(rvs, r0 * NGV * sizeof(P), Ring::kVP, lds + Ring::kOffVP, voff, lane);
-    Ring::copy_buf(rvz, r0 * NGV * sizeof(P), Ring::kVP, lds + Ring::kOffVP + Ring::kVP, voff, lane);
-    // K parameters of the block's group(s): [scale row, zero row] per group
-    const uint32_t g0 = static_cast<uint32_t>((t_begin + static_cast<int>(r0)) / G - g_first);
+    if constexpr (!Ring::kGroupKP) {
+      // K parameters of the block's two groups: [scale row, zero row] per group
+      const uint32_t g0 = static_cast<uint32_t>((t_begin + static_cast<int>(r0)) / G - g_first);
 #pragma unroll
-    for (int gi = 0; gi < NKG; ++gi) {
-      const uint32_t kp = lds + Ring::kOffKP + gi * 2 * Ring::kKPG;
-      Ring::copy_buf(rks, (g0 + gi) * Ring::kKPG, Ring::kKPG, kp, voff, lane);
-      Ring::copy_buf(rkz, (g0 + gi) * Ring::kKPG, Ring::kKPG, kp + Ring::kKPG, voff, lane);
+      for (int gi = 0; gi < NKG; ++gi) {
+        const uint32_t kp = lds + Ring::kOffKP + gi * 2 * Ring::kKPG;
+        Ring::copy_buf(rks, (g0 + gi) * Ring::kKPG, Ring::kKPG, kp, voff, lane);
+        Ring::copy_buf(rkz, (g0 + gi) * Ring::kKPG, Ring::kKPG, kp + Ring::kKPG, voff, lane);
+      }
     }
   };
+  // block i's V scales (zeros kVPE bytes further) and, with whole K groups per block,
+  // the K parameters of the group that starts at block i
+  auto vparams_of = [&](int i) { return entry(i) + (i % Ring::kPB) * 32 * kRowBytes; };
+  auto kparams_of = [&](int i) {
+    return entry(i) + Ring::kOffEK + ((t_begin + 32 * i) / G == entry_g0(i) ? 0 : 2 * Ring::kKPG);
+  };
 
-  struct Blk {
+  struct BlkA {  // V scaled in the A operand
     uint32_t kw[2][KB];
     uint32_t vw[8][VWR];
     uint32_t vs[8], vz[8];  // word holding the slot token's group-gv parameter
   };
-  auto read_blk = [&](const unsigned char* slot, Blk& x) {
+  struct BlkB {  // V scale on the probabilities
+    uint32_t kw[2][KB];
+    uint32_t vh[2][8];  // the word holding the lane's 4 codes of half hf, per slot token
+  };
+  using Blk = std::conditional_t<kBS, BlkB, BlkA>;
+  // word of a V row holding the lane's 4 channels of half hf, and the byte permute
+  // that puts those codes of two tokens into the two 16-bit halves
+  const uint32_t vbw0 = VB == 4 ? (n >> 1) : (n >> 2), vbw1 = vbw0 + (VB == 4 ? 8 : 4);
+  const uint32_t vbsel = VB == 4 ? ((n & 1) ? 0x07060302u : 0x05040100u)
+                                 : (0x0C000C00u | ((4u + (n & 3)) << 16) | static_cast<uint32_t>(n & 3));
+  // the block's V parameters, one (token, group) per lane, as float scales and f16
+  // zeros in the order of the lanes' k-slots; rows at or past t_end get 0
+  auto conv_vparams = [&](int i) {
+    const int g = lane >> 5, tok = lane & 31;
+    if (g < NGV) {
+      const P* vsp = reinterpret_cast<const P*>(vparams_of(i));
+      const bool ok = t_begin + 32 * i + tok < t_end;
+      const float sv = ok ? param_f32<P>(vsp, tok * NGV + g) : 0.f;
+      const float zv = ok ? param_f32<P>(vsp + Ring::kVPE / sizeof(P), tok * NGV + g) : 0.f;
+      const int kbt = (tok & 15) >> 2, j = (tok & 3) + 4 * (tok >> 4);
+      sh_vs[wave][g][kbt][j] = sv;
+      sh_vz[wave][g][kbt][j] = static_cast<_Float16>(zv);
+    }
+  };
+  auto read_blk = [&](const unsigned char* slot, Blk& x, int i) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const uint32_t* src = reinterpret_cast<const uint32_t*>(slot + Ring::kOffK) + (16 * tt + n) * KW + kb * KB;
@@ -427,15 +571,25 @@ decode_mfma_kernel(DecodeArgs a) {
       }
     }
     const uint32_t* vw = reinterpret_cast<const uint32_t*>(slot + Ring::kOffV);
-    const uint32_t* vp = reinterpret_cast<const uint32_t*>(slot + Ring::kOffVP);
+    if constexpr (kBS) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t tok = static_cast<uint32_t>(slot_token(kb, j));
-      x.vw[j][0] = vw[tok * VW + vfw];
-      if constexpr (VB == 3) x.vw[j][1] = vw[tok * VW + vfw2];
-      const uint32_t e = sizeof(P) == 2 ? (tok * NGV + gv) >> 1 : tok * NGV + gv;
-      x.vs[j] = vp[e];
-      x.vz[j] = vp[Ring::kVP / 4 + e];
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t tok = static_cast<uint32_t>(slot_token(kb, j));
+        x.vh[0][j] = vw[tok * VW + vbw0];
+        x.vh[1][j] = vw[tok * VW + vbw1];
+      }
+      conv_vparams(i);
+    } else {
+      const uint32_t* vp = reinterpret_cast<const uint32_t*>(vparams_of(i));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t tok = static_cast<uint32_t>(slot_token(kb, j));
+        x.vw[j][0] = vw[tok * VW + vfw];
+        if constexpr (VB == 3) x.vw[j][1] = vw[tok * VW + vfw2];
+        const uint32_t e = sizeof(P) == 2 ? (tok * NGV + gv) >> 1 : tok * NGV + gv;
+        x.vs[j] = vp[e];
+        x.vz[j] = vp[Ring::kVPE / 4 + e];
+      }
     }
   };
   // A new K group: the lane's 32 channels of its (scale, zero) rows are read from the
@@ -558,41 +712,89 @@ decode_mfma_kernel(DecodeArgs a) {
       accl = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, one2), bp, accl, 0, 0, 0);
     }
 
-    // ---- O^T[8 (4 kb' + i) + vorder(t)][n] += V_hat^T P^T over the block's 32 tokens
-    uint32_t sv2[4], nsv2[4], zv2[4], vp[4][8];
+    if constexpr (kBS) {
+      // ---- O^T[64 hf + 4 (4 kb' + i) + t % 4][n] += C^T (P s_hf)^T, hf = t / 4, over
+      // the block's 32 tokens: A the code values 128 + c (bf16, exact), B the
+      // probabilities times the tokens' scales of the half's group (bf16); the offset
+      // (-128 sum of B) and the zero-points (sum p z, f16) go to accz: rows 0-7 for
+      // half 0, rows 8-15 for half 1
+      __builtin_amdgcn_wave_barrier();  // the wave's parameter writes of this block
+      uint32_t bs[2][4];
 #pragma unroll
-    for (int q2 = 0; q2 < 4; ++q2) {
-      const uint32_t ta = t0 + slot_token(kb, 2 * q2), tb = t0 + slot_token(kb, 2 * q2 + 1);
-      float sa = vparam(cur.vs[2 * q2], 2 * q2), sb = vparam(cur.vs[2 * q2 + 1], 2 * q2 + 1);
-      float za = vparam(cur.vz[2 * q2], 2 * q2), zb = vparam(cur.vz[2 * q2 + 1], 2 * q2 + 1);
-      if constexpr (!full) {  // rows past the end dequantize to exactly 0
-        const bool oka = static_cast<int>(ta) < t_end, okb = static_cast<int>(tb) < t_end;
-        sa = oka ? sa : 0.f; za = oka ? za : 0.f;
-        sb = okb ? sb : 0.f; zb = okb ? zb : 0.f;
+      for (int hf = 0; hf < (NGV == 2 ? 2 : 1); ++hf) {
+        const float4 s0 = *reinterpret_cast<const float4*>(&sh_vs[wave][hf][kb][0]);
+        const float4 s1 = *reinterpret_cast<const float4*>(&sh_vs[wave][hf][kb][4]);
+        const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) bs[hf][q2] = pack_bf16(p[2 * q2] * sv[2 * q2], p[2 * q2 + 1] * sv[2 * q2 + 1]);
       }
-      sv2[q2] = pack_h2(sa, sb);
-      zv2[q2] = pack_h2(za, zb);
-      uint32_t fa, fb;
-      if constexpr (VB == 3) {
-        fa = __builtin_amdgcn_alignbit(cur.vw[2 * q2][VWR - 1], cur.vw[2 * q2][0], vfo) & 0xFFFFFFu;
-        fb = __builtin_amdgcn_alignbit(cur.vw[2 * q2 + 1][VWR - 1], cur.vw[2 * q2 + 1][0], vfo) & 0xFFFFFFu;
-      } else if constexpr (VB == 2) {
-        fa = cur.vw[2 * q2][0] >> vfo;
-        fb = cur.vw[2 * q2 + 1][0] >> vfo;
-      } else {
-        fa = cur.vw[2 * q2][0];
-        fb = cur.vw[2 * q2 + 1][0];
+      if constexpr (NGV == 1) {
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) bs[1][q2] = bs[0][q2];
       }
-      vpairs<VB>(fa, fb, vp[q2]);
-      nsv2[q2] = as_u32(as_h2(sv2[q2]) * as_h2(0xD400D400u));  // -64 s, exact
-    }
-    accz = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, zv2), bp, accz, 0, 0, 0);
+      {
+        const uint4 zw = *reinterpret_cast<const uint4*>(&sh_vz[wave][NGV == 2 ? (n >> 3) : 0][kb][0]);
+        accz = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, zw), bp, accz, 0, 0, 0);
+        const uint32_t o0 = (NGV == 1 || n < 8) ? 0xC300C300u : 0u, o1 = (NGV == 1 || n >= 8) ? 0xC300C300u : 0u;
+        const uint32_t a0[4] = {o0, o0, o0, o0}, a1[4] = {o1, o1, o1, o1};
+        accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), __builtin_bit_cast(bf16x8_t, bs[0]),
+                                                       accz, 0, 0, 0);
+        if constexpr (NGV == 2)
+          accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), __builtin_bit_cast(bf16x8_t, bs[1]),
+                                                         accz, 0, 0, 0);
+      }
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      uint32_t av[4];
+      for (int hf = 0; hf < 2; ++hf) {
+        uint32_t cv[4][4];  // [pair][channel i]
 #pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) av[q2] = scale_pair(vp[q2][t], sv2[q2], nsv2[q2]);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, av), bp, acc[t], 0, 0, 0);
+        for (int q2 = 0; q2 < 4; ++q2) {
+          const uint32_t comb = __builtin_amdgcn_perm(cur.vh[hf][2 * q2 + 1], cur.vh[hf][2 * q2], vbsel);
+          vpairs_bf16<VB>(comb, cv[q2], VB == 4 ? kc.lo : kc.lo2, kc.vmagic);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t av[4] = {cv[0][i], cv[1][i], cv[2][i], cv[3][i]};
+          acc[4 * hf + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bs[hf]), acc[4 * hf + i], 0, 0, 0);
+        }
+      }
+    } else {
+      // ---- O^T[8 (4 kb' + i) + vorder(t)][n] += V_hat^T P^T over the block's 32 tokens
+      uint32_t sv2[4], nsv2[4], zv2[4], vp[4][8];
+  #pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        const uint32_t ta = t0 + slot_token(kb, 2 * q2), tb = t0 + slot_token(kb, 2 * q2 + 1);
+        float sa = vparam(cur.vs[2 * q2], 2 * q2), sb = vparam(cur.vs[2 * q2 + 1], 2 * q2 + 1);
+        float za = vparam(cur.vz[2 * q2], 2 * q2), zb = vparam(cur.vz[2 * q2 + 1], 2 * q2 + 1);
+        if constexpr (!full) {  // rows past the end dequantize to exactly 0
+          const bool oka = static_cast<int>(ta) < t_end, okb = static_cast<int>(tb) < t_end;
+          sa = oka ? sa : 0.f; za = oka ? za : 0.f;
+          sb = okb ? sb : 0.f; zb = okb ? zb : 0.f;
+        }
+        sv2[q2] = pack_h2(sa, sb);
+        zv2[q2] = pack_h2(za, zb);
+        uint32_t fa, fb;
+        if constexpr (VB == 3) {
+          fa = __builtin_amdgcn_alignbit(cur.vw[2 * q2][VWR - 1], cur.vw[2 * q2][0], vfo) & 0xFFFFFFu;
+          fb = __builtin_amdgcn_alignbit(cur.vw[2 * q2 + 1][VWR - 1], cur.vw[2 * q2 + 1][0], vfo) & 0xFFFFFFu;
+        } else if constexpr (VB == 2) {
+          fa = cur.vw[2 * q2][0] >> vfo;
+          fb = cur.vw[2 * q2 + 1][0] >> vfo;
+        } else {
+          fa = cur.vw[2 * q2][0];
+          fb = cur.vw[2 * q2 + 1][0];
+        }
+        vpairs<VB>(fa, fb, vp[q2]);
+        nsv2[q2] = as_u32(as_h2(sv2[q2]) * as_h2(0xD400D400u));  // -64 s, exact
+      }
+      accz = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, zv2), bp, accz, 0, 0, 0);
+  #pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        uint32_t av[4];
+  #pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) av[q2] = scale_pair(vp[q2][t], sv2[q2], nsv2[q2]);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, av), bp, acc[t], 0, 0, 0);
+      }
     }
   };
 
@@ -609,8 +811,13 @@ decode_mfma_kernel(DecodeArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   for (int i = 0; i < nblk && i < Ring::kDepth; ++i) issue(i);
   auto wait_blk = [&](int i) {
-    if (i + Ring::kDepth <= nblk) Ring::wait_ahead();
-    else Ring::wait_all();
+    if (i + Ring::kDepth <= nblk) {
+      // entries started by the next kDepth - 1 blocks
+      const int ne = (i + Ring::kDepth - 1) / Ring::kPB - i / Ring::kPB;
+      Ring::wait_ahead(ne);
+    } else {
+      Ring::wait_all();
+    }
   };
   // one pass of the outer loop per K group (its blocks in the inner loop), so that the
   // group's score operands are formed once and are not loop-carried
@@ -621,14 +828,14 @@ decode_mfma_kernel(DecodeArgs a) {
       const int t0 = t_begin + 32 * i;
       nb = min(nb, (G - t0 % G) / 32);  // blocks left in this group
       wait_blk(i);
-      kq = use_kp(wring + (i % Ring::kDepth) * Ring::kSlot + Ring::kOffKP);
+      kq = use_kp(kparams_of(i));
       seed = kq.kbias - m;
     }
     for (int e = i + nb; i < e; ++i) {
       wait_blk(i);
       const unsigned char* slot = wring + (i % Ring::kDepth) * Ring::kSlot;
       Blk cur;
-      read_blk(slot, cur);
+      read_blk(slot, cur, i);
       // with one K group per block every read of the slot is in cur: the slot is
       // refilled before the block is computed, so that two blocks are in flight
       // during the computation
@@ -648,11 +855,11 @@ decode_mfma_kernel(DecodeArgs a) {
     const unsigned char* slot = wring + (nfull % Ring::kDepth) * Ring::kSlot;
     KQ kq;
     if constexpr (NKG == 1) {
-      kq = use_kp(slot + Ring::kOffKP);
+      kq = use_kp(kparams_of(nfull));
       seed = kq.kbias - m;
     }
     Blk cur;
-    read_blk(slot, cur);
+    read_blk(slot, cur, nfull);
     process(t_begin + 32 * nfull, cur, slot, kq, Part{});
   }
   if (thr == -INFINITY) m = -INFINITY;  // no rows: the merge gives this wave no weight
@@ -664,10 +871,22 @@ decode_mfma_kernel(DecodeArgs a) {
     sh_m[wave][n] = m;
     sh_l[wave][n] = l;
   }
+  if constexpr (kBS) {
+    // the rows of accz are alike within a half: this lane's is half kb / 2, the other
+    // half's is in lane ^ 32
+    const float cmine = accz[0], cother = __shfl_xor(cmine, 32);
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < 8; ++t) {
+      const float corr = (kb >> 1) == (t >> 2) ? cmine : cother;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sh_o[wave][n][8 * (4 * kb + i) + vorder<VB>(t)] = acc[t][i] + accz[i];
+      for (int i = 0; i < 4; ++i) sh_o[wave][n][64 * (t >> 2) + 4 * (4 * kb + i) + (t & 3)] = acc[t][i] + corr;
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sh_o[wave][n][8 * (4 * kb + i) + vorder<VB>(t)] = acc[t][i] + accz[i];
+  }
   __syncthreads();
   const int64_t pbase = static_cast<int64_t>(bh) * a.splits + split;
   for (int idx = tid; idx < H * D; idx += kDecThreads) {
