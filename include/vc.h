@@ -219,18 +219,21 @@ vc_status vc_gather_rows(const void* src, int32_t kv_dtype, int32_t B, int32_t H
  * Accumulation is float32.
  *
  * Precision.  A quantized bf16 cache with d = 128, Hq/Hkv <= 16, 2/3/4-bit K and V
- * codes, group 16, 32, 64 or 128 and a capacity that is a multiple of 32 runs on f16
+ * codes, group 16, 32, 64 or 128 and a capacity that is a multiple of 32 runs on
  * matrix cores unless ckv->flags has VC_CKV_DECODE_F32: the operands q_c * sm_scale *
  * log2(e) (and its products with the K scales), the zero-points, the V scales times
- * 64 and the probabilities are rounded to f16 (11 significant bits) and the products
- * accumulate in float32.  Range: every |z| and 64 * s_V must be at most 65504.
- * Accuracy: each score carries an error of about 2^-10 * sm_scale * sum_c |q_c k_c|
- * (the f16 rounding of its terms) and the output that error times the spread of the
- * values, plus about 2^-11 |v|.  For keys, values and queries of unit scale (N(0,1)
- * entries, x10 on a few outlier channels) that is ~1e-4, inside the 2e-2 bar; it
- * grows with the square of the scale and leaves the bar near twice it.  For larger
- * activations set VC_CKV_DECODE_F32 (float32 operands throughout, the generic
- * kernel); every other cache runs in float32 as well.
+ * the codes and the probabilities are rounded to f16 (11 significant bits) and the
+ * products accumulate in float32; with 2- or 4-bit V codes in 64- or 128-channel
+ * groups the V scale is applied to the probabilities instead, each product p * s_V
+ * rounded to bf16 (8 significant bits).  Range: every |z| and 64 * s_V must be at
+ * most 65504.  Accuracy: each score carries an error of about 2^-10 * sm_scale *
+ * sum_c |q_c k_c| (the f16 rounding of its terms) and the output that error times
+ * the spread of the values, plus about 2^-11 |v| (2^-9 |v| with the bf16 products).
+ * For keys, values and queries of unit scale (N(0,1) entries, x10 on a few outlier
+ * channels) that is 1e-4 to 2e-3, inside the 2e-2 bar; it grows with the square of
+ * the scale and leaves the bar near twice it.  For larger activations set
+ * VC_CKV_DECODE_F32 (float32 operands throughout, the generic kernel); every other
+ * cache runs in float32 as well.
  * ------------------------------------------------------------------------- */
 vc_status vc_decode_attn_compressed(const vc_ckv* ckv, const void* q, int32_t Hq, float sm_scale,
                                     const int32_t* main_lens, const int32_t* tail_lens,

@@ -19,10 +19,16 @@
 //   per q-head and K group, is formed on the matrix cores when the group changes;
 //   minus the running maximum it seeds the score accumulator, so the scores come
 //   out relative to the maximum;
-// * V (per-token scale and zero): each pair becomes c * s with one packed fused
-//   multiply-add of (64 + c) by s with addend -64 s (exact, rounded once); the
-//   zero-point term sum_t p_t z_t is one extra product per block (its A operand is
-//   the tokens' zeros) added to every channel tile at the end;
+// * V (per-token scale and zero), 64- and 128-channel groups with 2- or 4-bit codes:
+//   lane n holds channels 64 hf + 4 n .. + 3 of each half hf, so a channel tile lies
+//   in one V group and the scale moves to the probabilities: A = the codes as the
+//   exact bf16 values 128 + c (one AND-OR per pair), B = p * s of the tile's group
+//   (bf16); the offset (-128 sum of B, exact) and the zero-point term sum_t p_t z_t
+//   are products of their own into one correction accumulator.  The block's scales
+//   and zeros are converted once by the wave (one token and group per lane) into LDS;
+// * V otherwise: each pair becomes c * s with one packed fused multiply-add of
+//   (64 + c) by s with addend -64 s (exact, rounded once); the zero-point term is one
+//   extra product per block (its A operand the tokens' zeros);
 // * S^T = K_hat Q^T for two 16-token tiles, online softmax per q-head in base 2 with
 //   a lazy rescale (only when the block maximum exceeds the running one by more than
 //   8, i.e. probabilities stay below 2^8), probabilities rounded to f16, then
@@ -33,22 +39,27 @@
 // * within an operand the order of the contraction index is free as long as both
 //   operands agree, so K channels and V tokens are enumerated in whatever order the
 //   byte permutes produce them (korder / vorder below);
-// * K's code row is read as 32-channel chunks (one 64/96/128-bit load per lane), V's
-//   as 8-channel fields of 8 tokens per lane; all loads of the next block are issued
-//   before the current block is computed and are only decoded when used;
+// * each wave copies its blocks global -> LDS itself, kDepth blocks ahead into a ring
+//   of its own (buffer loads at scalar offsets); a slot is refilled as soon as its
+//   block is in registers, so two blocks are in flight while one is computed.  The
+//   V and K parameters of two blocks are copied as one entry of a parameter ring;
+// * K's code row is read from LDS as 32-channel chunks (one 64/96/128-bit read per
+//   lane), V's as the lane's fields of 8 tokens; they are decoded only when used;
+// * a merge by the last workgroup to finish would need a device-scope release by
+//   every workgroup (an L2 write-back each, on a part with one L2 per XCD): measured,
+//   that costs more than the separate merge kernel;
 // * a sequence's 32-token blocks are dealt out evenly over the waves of its
 //   workgroups (in order: wave loads differ by at most one block); the 4 waves of a
 //   workgroup are merged in LDS and the workgroup writes one partial per split;
 //   decode_merge_kernel, launched next, adds the full-precision tail rows and merges
-//   the splits in split order (a merge by the last workgroup to finish would need a
-//   device-scope release by every workgroup, i.e. an L2 write-back per workgroup on
-//   a part with one L2 per XCD);
+//   the splits in split order;
 // * the number of splits is chosen so that all workgroups are resident at once
 //   (occupancy times compute units, queried from the runtime).
 //
-// Precision: q * s, c * s, the zero-points and p are f16 (11-bit significands) with
-// float32 accumulation; against float64 attention on the outlier workloads the error
-// is about 1e-4, far below the bf16 output resolution.  Values and 64 * s must lie
+// Precision: q * s, c * s, the zero-points and p are f16 (11-bit significands), p * s
+// bf16 (8-bit) on the scaled-probability path, with float32 accumulation; against
+// float64 attention on the outlier workloads the error is 1e-4 to 2e-3 at unit scale,
+// below the bf16 output resolution of those outputs.  Values and 64 * s must lie
 // within the f16 range (65504).
 
 #include <type_traits>
