@@ -122,6 +122,33 @@ def test_compress_drop_end_to_end_and_decode():
         assert_close(np32(out[b]), o, 'bf16')
 
 
+@pytest.mark.parametrize("tail", [1, 64, 97])
+def test_kept_row_decode_with_tails(tail):
+    """Decode over kept rows plus a full-precision tail (merged by the decode's merge
+    kernel in chunks of 64 rows) against the oracle over the kept rows and the tail."""
+    w = SMALL.with_(k=max(tail, 1))
+    K, V = G.full_kv(w, "k"), G.full_kv(w, "v")
+    P = G.full_probes(w)
+    keep = OD.n_keep(w.N, w.keep_ratio)
+    ckv = L.Ckv("drop", w.B, w.Hkv, w.d, keep, keep_ratio=w.keep_ratio, kv_dtype="bf16", tail_cap=tail)
+    L.vc_compress(ckv, T(K, torch.bfloat16), T(V, torch.bfloat16), probes=T(P, torch.bfloat16))
+    ckv.n_main = keep
+    Kw, Vw = G.full_window_kv(w, "k"), G.full_window_kv(w, "v")
+    Kw, Vw = np32(T(Kw, torch.bfloat16)), np32(T(Vw, torch.bfloat16))  # the bf16 values the kernel reads
+    ckv.tail_len = tail
+    ckv.tail_k[:] = T(Kw[:, :, :tail], torch.bfloat16)
+    ckv.tail_v[:] = T(Vw[:, :, :tail], torch.bfloat16)
+    say(f"[drop decode tail] tail={tail}")
+    Q = G.full_window_q(w)[:, :, tail - 1]
+    out = torch.empty(w.B, w.Hq, w.d, device="cuda", dtype=torch.bfloat16)
+    L.vc_decode_attn_compressed(ckv, T(Q, torch.bfloat16), out)
+    torch.cuda.synchronize()
+    kk, vk = np32(ckv.k_kept), np32(ckv.v_kept)
+    for b in range(w.B):
+        o, _ = OA.decode(Q[b], kk[b], vk[b], w.d ** -0.5, Kw[b, :, :tail], Vw[b, :, :tail])
+        assert_close(np32(out[b]), o, 'bf16', f"b={b}")
+
+
 def test_keep_all_decode_equals_dense_decode():
     w = SMALL.with_(N=1000, keep_ratio=1.0)
     K, V = G.full_kv(w, "k"), G.full_kv(w, "v")

@@ -132,6 +132,17 @@ def test_decode_quant_matches_oracle(name, tail):
     _decode_case(w, tail)
 
 
+@pytest.mark.parametrize("name", ["llama8b_4bit", "qwen30b_k4v3", "g16_k2v2_bf16_h4"])
+@pytest.mark.parametrize("tail", [64, 65, 130])
+def test_decode_long_tails_merged_in_chunks(name, tail):
+    """Full-precision tails of 64 rows and longer: the matrix-core decode leaves the
+    tail rows to its merge, which takes them in chunks of 64 with an online softmax
+    across the chunks (one, two and three chunks)."""
+    w = ALL_CASES[name].with_(k=tail)
+    say(f"[decode long tail] {name} tail={tail}")
+    _decode_case(w, tail)
+
+
 @pytest.mark.parametrize("name, scale", [("qwen30b_k4v3", 1e-3), ("llama8b_4bit", 1e-3), ("g16_k2v2_bf16_h4", 1e-3),
                                          ("g128_k3v3_f32_h8", 1e-3), ("llama8b_4bit", 2.0)])
 def test_decode_range_edges_on_the_matrix_cores(name, scale):
