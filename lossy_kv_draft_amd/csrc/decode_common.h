@@ -161,6 +161,10 @@ __global__ void __launch_bounds__(kDecThreads) decode_merge_kernel(DecodeArgs a)
   TailRegs tr;
   const int tl = TAIL ? static_cast<int>(min(dec_tail_len(a, b), a.tail_cap)) : 0;
   if (TAIL) tail_load(tr, a, bh, h, 0, min(tl, kTailChunk));
+  // the splits' (maximum, sum), one split per lane of the first wave, loaded with the
+  // partials so that no later round of global loads waits on them
+  float2 mv = make_float2(-INFINITY, 0.f);
+  if (tid < S) mv = reinterpret_cast<const float2*>(a.part_ml)[(static_cast<int64_t>(bh) * S + tid) * H + h];
   float v[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) v[j] = s_lo + j < s_hi ? p[(s_lo + j) * stride] : 0.f;
@@ -177,7 +181,6 @@ __global__ void __launch_bounds__(kDecThreads) decode_merge_kernel(DecodeArgs a)
   if (tid < 64) {  // split weights: a wave holds one split per lane (the tail after them)
     float m = -INFINITY, l = 0.f;
     if (tid < S) {
-      const float2 mv = reinterpret_cast<const float2*>(a.part_ml)[(static_cast<int64_t>(bh) * S + tid) * H + h];
       m = mv.x;
       l = mv.y;
     } else if (TAIL && tid == S) {
