@@ -383,14 +383,16 @@ __device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int
         // ---- softmax per row over the half
         const bool full = h0 + 31 <= L;  // every row sees every position of the half
         bf16x8_t pb[RT];
+        float mt[RT];
+        bool up = false;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          float mt = -INFINITY;
+          mt[rt] = -INFINITY;
           if (full) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-              for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[tt][rt][r]);
+              for (int r = 0; r < 4; ++r) mt[rt] = fmaxf(mt[rt], s[tt][rt][r]);
           } else {
             const int lr = static_cast<int>(max(min(rlim[rt] - h0, static_cast<int64_t>(32)), static_cast<int64_t>(-1)));
 #pragma unroll
@@ -399,15 +401,19 @@ __device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int
               for (int r = 0; r < 4; ++r) {
                 const float v = 16 * tt + 4 * kb + r <= lr ? s[tt][rt][r] : -INFINITY;
                 s[tt][rt][r] = v;
-                mt = fmaxf(mt, v);
+                mt[rt] = fmaxf(mt[rt], v);
               }
           }
-          // The running maximum moves only when a score exceeds it by more than 8: a lane
-          // tests its own scores (rounding is monotone, so fl(max x * q) > m + 8 exactly
-          // when some fl(x * q) > m + 8), a wave vote gates the row maxima, and each row
-          // still decides alone
-          if (__any(mt * a.qscale > m[rt] + 8.f)) {
-            const float mts = group4_max(mt) * a.qscale;
+          up = up | (mt[rt] * a.qscale > m[rt] + 8.f);
+        }
+        // The running maximum moves only when a score exceeds it by more than 8: a lane
+        // tests its own scores (rounding is monotone, so fl(max x * q) > m + 8 exactly
+        // when some fl(x * q) > m + 8), one wave vote over all of the wave's rows gates
+        // the row maxima, and each row still decides alone
+        if (__any(up)) {
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const float mts = group4_max(mt[rt]) * a.qscale;
             if (mts > m[rt] + 8.f) {  // the row's own decision (all lanes of a row agree)
               const float al = __builtin_amdgcn_exp2f(m[rt] - mts);  // 0 on the row's first scores
 #pragma unroll
@@ -416,6 +422,9 @@ __device__ __forceinline__ void verify_tiles(const VerifyArgs& a, int split, int
               m[rt] = mts;
             }
           }
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
           const float nm = m[rt] == -INFINITY ? 0.f : -m[rt];
           Pack16 pp;
 #pragma unroll
