@@ -772,19 +772,13 @@ extern "C" vc_status vc_verify_attn_full(const void* q, const void* k_cache, con
     verify_tiling(M, RT, nblk);
     a.rows_per_block = 64 * RT;
     dim3 grid(a.splits, nblk, static_cast<unsigned>(bh));
-#define VC_VER_LAUNCH(D_, RT_) \
-  hipLaunchKernelGGL((verify_mfma_kernel<D_, RT_>), grid, dim3(kVerThreads), 0, s, a)
-    if (d == 128) {
-      if (RT == 1) VC_VER_LAUNCH(128, 1);
-      else if (RT == 2) VC_VER_LAUNCH(128, 2);
-      else if (RT == 3) VC_VER_LAUNCH(128, 3);
-      else VC_VER_LAUNCH(128, 4);
-    } else {
-      if (RT == 1) VC_VER_LAUNCH(64, 1);
-      else if (RT == 2) VC_VER_LAUNCH(64, 2);
-      else if (RT == 3) VC_VER_LAUNCH(64, 3);
-      else VC_VER_LAUNCH(64, 4);
-    }
+    // d = 64 (d = 128 took the tile kernels above)
+#define VC_VER_LAUNCH(RT_) \
+  hipLaunchKernelGGL((verify_mfma_kernel<64, RT_>), grid, dim3(kVerThreads), 0, s, a)
+    if (RT == 1) VC_VER_LAUNCH(1);
+    else if (RT == 2) VC_VER_LAUNCH(2);
+    else if (RT == 3) VC_VER_LAUNCH(3);
+    else VC_VER_LAUNCH(4);
 #undef VC_VER_LAUNCH
     VC_LAUNCHED("verify_mfma_kernel");
     dim3 mgrid(static_cast<unsigned>(cdiv(static_cast<int64_t>(M) * d / 4, 256)), static_cast<unsigned>(bh));
