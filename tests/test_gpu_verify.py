@@ -17,6 +17,8 @@ SMALL = {
     "llama8b": C.small(C.LLAMA8B, N=3000),                 # H=4, k=32: M=128
     "drop_k40": C.small(C.DROP, N=2500, Hkv=1, Hq=4),      # H=4, k=40: M=160 (one 8-wave block)
     "qwen30b_k40": C.small(C.QWEN30B, N=1100, Hkv=1, Hq=8),  # H=8, k=40: M=320 (one mixed 8-wave block)
+    "qwen30b_k33": C.small(C.QWEN30B, N=1100, Hkv=1, Hq=8, k=33),  # M=264: mixed block, padding rows, one idle wave
+    "qwen30b_k64": C.small(C.QWEN30B, N=900, Hkv=1, Hq=8, k=64),   # M=512: four 128-row 4-wave blocks
     "d64_k7": C.small(C.LLAMA8B, N=700, d=64, k=7),
 }
 
@@ -52,7 +54,7 @@ def test_verify_matches_oracle(name, split):
         assert np.abs(np32(lse[b]) - l).max() <= LSE_TOL[w.dtype]
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "llama8b", "drop_k40", "qwen30b_k40", "d64_k7"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama8b", "drop_k40", "qwen30b_k40", "qwen30b_k33", "qwen30b_k64", "d64_k7"])
 def test_verify_batch_invariance(name):
     """Row i of the k-row window == the 1-row call with context L + i (same split
     size), bit for bit; this is what makes verified output identical to greedy
