@@ -149,6 +149,38 @@ def test_kept_row_decode_with_tails(tail):
         assert_close(np32(out[b]), o, 'bf16', f"b={b}")
 
 
+@pytest.mark.parametrize("case", ["f32_d128", "bf16_d64", "bf16_h32"])
+def test_kept_row_decode_generic_kernel(case):
+    """Decode over kept rows where the tile loop does not apply and the generic kernel
+    runs: float32 caches, d = 64, or more than 16 q-heads per kv-head; with a 5-row
+    tail, against the oracle over the kept rows and the tail."""
+    base = SMALL.with_(N=2000, k=5)
+    w = {"f32_d128": base, "bf16_d64": base.with_(d=64), "bf16_h32": base.with_(Hq=32, Hkv=1)}[case]
+    kvdt = "f32" if case == "f32_d128" else "bf16"
+    tdt = torch.float32 if kvdt == "f32" else torch.bfloat16
+    tail = w.k
+    say(f"[drop decode generic] {case}")
+    K, V = G.full_kv(w, "k"), G.full_kv(w, "v")
+    P = G.full_probes(w)
+    keep = OD.n_keep(w.N, w.keep_ratio)
+    ckv = L.Ckv("drop", w.B, w.Hkv, w.d, keep, keep_ratio=w.keep_ratio, kv_dtype=kvdt, tail_cap=tail)
+    L.vc_compress(ckv, T(K, tdt), T(V, tdt), probes=T(P, torch.bfloat16))
+    ckv.n_main = keep
+    Kw, Vw = G.full_window_kv(w, "k"), G.full_window_kv(w, "v")
+    Kw, Vw = np32(T(Kw, tdt)), np32(T(Vw, tdt))  # the stored values the kernel reads
+    ckv.tail_len = tail
+    ckv.tail_k[:] = T(Kw, tdt)
+    ckv.tail_v[:] = T(Vw, tdt)
+    Q = G.full_window_q(w)[:, :, tail - 1]
+    out = torch.empty(w.B, w.Hq, w.d, device="cuda", dtype=tdt)
+    L.vc_decode_attn_compressed(ckv, T(Q, tdt), out)
+    torch.cuda.synchronize()
+    kk, vk = np32(ckv.k_kept), np32(ckv.v_kept)
+    for b in range(w.B):
+        o, _ = OA.decode(Q[b], kk[b], vk[b], w.d ** -0.5, Kw[b], Vw[b])
+        assert_close(np32(out[b]), o, kvdt, f"b={b}")
+
+
 def test_keep_all_decode_equals_dense_decode():
     w = SMALL.with_(N=1000, keep_ratio=1.0)
     K, V = G.full_kv(w, "k"), G.full_kv(w, "v")
