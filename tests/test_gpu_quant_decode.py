@@ -217,7 +217,10 @@ def test_decode_lengths_above_the_maximum_are_clamped():
 
 
 def test_decode_ragged_lengths_and_empty_sequence():
-    w = C.small(C.E2E, B=3, N=32 * 20)
+    """Per-sequence lengths: full, a shorter prefix, an empty sequence (zero output,
+    log-sum-exp -inf), and one with no compressed rows but a tail (every split
+    empty, the tail alone)."""
+    w = C.small(C.E2E, B=4, N=32 * 20)
     K, V, Q, Kw, Vw = inputs(w)
     comp = oracle_compress(w, K, V)
     ckv = _ckv(w, w.N, tail_cap=8)
@@ -225,8 +228,8 @@ def test_decode_ragged_lengths_and_empty_sequence():
     ckv.n_main, ckv.tail_len = w.N, 8
     ckv.tail_k[:] = T(Kw[:, :, :8], torch.bfloat16)
     ckv.tail_v[:] = T(Vw[:, :, :8], torch.bfloat16)
-    main = [w.N, 32 * 7, 0]
-    tl = [3, 0, 0]
+    main = [w.N, 32 * 7, 0, 0]
+    tl = [3, 0, 0, 5]
     out = torch.empty(w.B, w.Hq, w.d, device="cuda", dtype=torch.bfloat16)
     lse = torch.empty(w.B, w.Hq, device="cuda")
     L.vc_decode_attn_compressed(ckv, T(Q[:, :, 0], torch.bfloat16), out, lse=lse,
@@ -234,7 +237,7 @@ def test_decode_ragged_lengths_and_empty_sequence():
                                 tail_lens=torch.tensor(tl, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     kh, vh = oracle_dequant(w, comp)
-    for b in range(2):
+    for b in (0, 1, 3):
         o, l = OA.decode(Q[b, :, 0], kh[b, :, :main[b]], vh[b, :, :main[b]], w.d ** -0.5,
                          Kw[b, :, :tl[b]], Vw[b, :, :tl[b]])
         assert_close(np32(out[b]), o, 'bf16')
