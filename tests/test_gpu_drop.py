@@ -8,7 +8,7 @@ import torch
 import lossy_kv_draft_amd as L
 from workloads import configs as C, gen as G
 from oracle import drop as OD, attention as OA
-from gpu_util import assert_close, T, np32, say, TOL
+from gpu_util import LSE_TOL, assert_close, T, np32, say, TOL
 
 pytestmark = pytest.mark.gpu
 
@@ -179,6 +179,40 @@ def test_kept_row_decode_generic_kernel(case):
     for b in range(w.B):
         o, _ = OA.decode(Q[b], kk[b], vk[b], w.d ** -0.5, Kw[b], Vw[b])
         assert_close(np32(out[b]), o, kvdt, f"b={b}")
+
+
+def test_kept_row_decode_ragged_lengths():
+    """Per-sequence kept-row counts and tail lengths on the tile-loop decode: all kept
+    rows, a prefix ending mid-tile, an empty sequence (zero output, log-sum-exp
+    -inf) and one with no kept rows but a tail."""
+    w = SMALL.with_(B=4, N=2000, k=5)
+    K, V = G.full_kv(w, "k"), G.full_kv(w, "v")
+    P = G.full_probes(w)
+    keep = OD.n_keep(w.N, w.keep_ratio)
+    ckv = L.Ckv("drop", w.B, w.Hkv, w.d, keep, keep_ratio=w.keep_ratio, kv_dtype="bf16", tail_cap=w.k)
+    L.vc_compress(ckv, T(K, torch.bfloat16), T(V, torch.bfloat16), probes=T(P, torch.bfloat16))
+    ckv.n_main = keep
+    Kw, Vw = G.full_window_kv(w, "k"), G.full_window_kv(w, "v")
+    Kw, Vw = np32(T(Kw, torch.bfloat16)), np32(T(Vw, torch.bfloat16))
+    ckv.tail_len = w.k
+    ckv.tail_k[:] = T(Kw, torch.bfloat16)
+    ckv.tail_v[:] = T(Vw, torch.bfloat16)
+    main = [keep, keep // 3 + 7, 0, 0]
+    tl = [w.k, 2, 0, w.k]
+    say(f"[drop decode ragged] main {main} tail {tl}")
+    Q = G.full_window_q(w)[:, :, 0]
+    out = torch.empty(w.B, w.Hq, w.d, device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty(w.B, w.Hq, device="cuda")
+    L.vc_decode_attn_compressed(ckv, T(Q, torch.bfloat16), out, lse=lse,
+                                main_lens=torch.tensor(main, dtype=torch.int32, device="cuda"),
+                                tail_lens=torch.tensor(tl, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    kk, vk = np32(ckv.k_kept), np32(ckv.v_kept)
+    for b in (0, 1, 3):
+        o, l = OA.decode(Q[b], kk[b, :, :main[b]], vk[b, :, :main[b]], w.d ** -0.5, Kw[b, :, :tl[b]], Vw[b, :, :tl[b]])
+        assert_close(np32(out[b]), o, 'bf16', f"b={b}")
+        assert np.abs(np32(lse[b]) - l).max() <= LSE_TOL["bf16"]
+    assert torch.all(out[2] == 0) and torch.all(torch.isneginf(lse[2]))
 
 
 def test_keep_all_decode_equals_dense_decode():
