@@ -159,6 +159,379 @@ quant_pack_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src, int6
   }
 }
 
+// The code of x from the reciprocal r of the scale, when the product certifies it.  r
+// comes from v_rcp_f32 (within 1 ulp), so qa = fl(fl(x - z) r) differs from the correctly
+// rounded quotient fl(fl(x - z) / s) by at most 2^-22 of it.  Where |qa| <= 2^(BITS+1)
+// and qa lies further than 2^(BITS-20) from every half-integer, both round to the same
+// integer; where |qa| is larger, both clamp to the same end of [0, 2^BITS - 1].  ok is
+// cleared otherwise, and for NaN (scale_reciprocal returns NaN for a scale whose
+// reciprocal would not be accurate), and the caller then forms the code with quant_code.
+template <int BITS>
+__device__ __forceinline__ uint32_t quant_code_certified(float x, float z, float r, bool& ok) {
+  static_assert(BITS <= 8, "the margin grows with the code width");
+  const float qa = __fmul_rn(__fsub_rn(x, z), r);
+  ok = ok & (fabsf(__builtin_amdgcn_fractf(qa) - 0.5f) > static_cast<float>(1 << BITS) * 0x1p-20f);
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_fmed3f(rintf(qa), 0.0f, static_cast<float>((1 << BITS) - 1)));
+}
+
+// 1/s for a normal finite scale, else NaN (zero, subnormal and non-finite scales go to
+// quant_code).
+__device__ __forceinline__ float scale_reciprocal(float s) {
+  return (s >= 0x1p-126f && s <= 0x1.fffffep127f) ? __builtin_amdgcn_rcpf(s) : __builtin_nanf("");
+}
+
+// One word of N = 32 / BITS codes from elements x with per-code parameters (s, z) and
+// reciprocals r: certified products where the whole wave's are, else quant_code for
+// the wave (the branch is wave-uniform and rare up to 8 bits; 16-bit codes always divide).
+template <int BITS, int N, typename SZ>
+__device__ __forceinline__ uint32_t pack_word_fast(const float (&x)[N], SZ sz) {
+  uint32_t word = 0;
+  if constexpr (BITS <= 8) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) word |= quant_code_certified<BITS>(x[i], sz.z(i), sz.r(i), ok) << (i * BITS);
+    if (!__builtin_amdgcn_ballot_w64(!ok)) return word;
+    word = 0;
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) word |= quant_code(x[i], sz.s(i), sz.z(i), BITS) << (i * BITS);
+  return word;
+}
+
+// N consecutive tile elements as float32 from an LDS run that starts at a multiple of
+// N elements (so a run of 8 bf16 or 4 float32 is one 16-byte read)
+template <int N, typename T>
+__device__ __forceinline__ void load_run(const T* p, float (&x)[N]) {
+  if constexpr (sizeof(T) == 2 && N >= 2) {
+    constexpr int W = N / 2;  // 32-bit words, two bf16 each (element 2k in the low half)
+    uint32_t u[W];
+    if constexpr (W % 4 == 0) {
+#pragma unroll
+      for (int k = 0; k < W / 4; ++k) {
+        const uint4 v = reinterpret_cast<const uint4*>(p)[k];
+        u[4 * k] = v.x; u[4 * k + 1] = v.y; u[4 * k + 2] = v.z; u[4 * k + 3] = v.w;
+      }
+    } else if constexpr (W == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      u[0] = v.x; u[1] = v.y;
+    } else {
+      u[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      x[2 * k] = __uint_as_float(u[k] << 16);
+      x[2 * k + 1] = __uint_as_float(u[k] & 0xFFFF0000u);
+    }
+  } else if constexpr (sizeof(T) == 4 && N % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) {
+      const float4 v = reinterpret_cast<const float4*>(p)[k];
+      x[4 * k] = v.x; x[4 * k + 1] = v.y; x[4 * k + 2] = v.z; x[4 * k + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = Elem<T>::load(p, i);
+  }
+}
+
+template <int BITS, typename T>
+__device__ __forceinline__ void pack_k_columns(const T* tile, const float* ks, const float* kz, int d, int G,
+                                               uint32_t* codes, int64_t row0, int tid) {
+  constexpr int CPW = 32 / BITS;
+  const int wpr = d / CPW;
+  const int w = tid % wpr, rstep = kQuantThreads / wpr;
+  const int c0 = w * CPW;
+  float s[CPW], z[CPW], r[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    s[i] = ks[c0 + i];
+    z[i] = kz[c0 + i];
+    r[i] = scale_reciprocal(s[i]);
+  }
+  for (int t = tid / wpr; t < G; t += rstep) {
+    float x[CPW];
+    load_run<CPW>(tile + t * d + c0, x);
+    struct {
+      const float *s_, *z_, *r_;
+      __device__ float s(int i) const { return s_[i]; }
+      __device__ float z(int i) const { return z_[i]; }
+      __device__ float r(int i) const { return r_[i]; }
+    } sz{s, z, r};
+    codes[(row0 + t) * wpr + w] = pack_word_fast<BITS>(x, sz);
+  }
+}
+
+template <int BITS, typename T>
+__device__ __forceinline__ void pack_v_words(const T* tile, const float* vs, const float* vz, int d, int G,
+                                             uint32_t* codes, int64_t row0, int tid) {
+  constexpr int CPW = 32 / BITS;
+  const int wpr = d / CPW, vg = d / G;
+  for (int j = tid; j < G * wpr; j += kQuantThreads) {
+    const int t = j / wpr, w = j % wpr, c0 = w * CPW;
+    const float s = vs[t * vg + c0 / G], z = vz[t * vg + c0 / G];  // CPW <= 16 <= G: one group per word
+    const float r = scale_reciprocal(s);
+    float x[CPW];
+    load_run<CPW>(tile + t * d + c0, x);
+    struct {
+      float s_, z_, r_;
+      __device__ float s(int) const { return s_; }
+      __device__ float z(int) const { return z_; }
+      __device__ float r(int) const { return r_; }
+    } sz{s, z, r};
+    codes[(row0 + t) * wpr + w] = pack_word_fast<BITS>(x, sz);
+  }
+}
+
+// Two consecutive tile elements as float32 (one 4-byte LDS read for bf16, 8 for float32)
+template <typename T>
+__device__ __forceinline__ void load_pair(const T* p, float& a, float& b) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+    a = __uint_as_float(u << 16);
+    b = __uint_as_float(u & 0xFFFF0000u);
+  } else {
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    a = v.x;
+    b = v.y;
+  }
+}
+
+// Minimum and maximum of the elements of a 16-byte chunk (8 bf16 or 4 float32)
+template <typename T>
+__device__ __forceinline__ void chunk_minmax(uint4 u, float& mn, float& mx) {
+  constexpr int N = 16 / static_cast<int>(sizeof(T));
+  float x[N];
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __uint_as_float(w[k] << 16);
+      x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+  } else {
+    x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y); x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
+  }
+  mn = x[0];
+  mx = x[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) {
+    mn = fminf(mn, x[i]);
+    mx = fmaxf(mx, x[i]);
+  }
+}
+
+// Extrema of a run of M 16-byte chunks, visited from chunk (lane M / 16) mod M on
+template <typename T, int M>
+__device__ __forceinline__ void run_minmax(const uint4* run, int lane, float& mn, float& mx) {
+  const int rot = (lane * M / 16) & (M - 1);
+  chunk_minmax<T>(run[rot], mn, mx);
+#pragma unroll
+  for (int k = 1; k < M; ++k) {
+    float a, b;
+    chunk_minmax<T>(run[(rot + k) & (M - 1)], a, b);
+    mn = fminf(mn, a);
+    mx = fmaxf(mx, b);
+  }
+}
+
+// Lane l receives lane l - N of its row of 16 (bound_ctrl: lanes with no such source read
+// 0, and only lanes whose sources are all in the row use the result)
+template <int N>
+__device__ __forceinline__ float row_shr(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + N, 0xF, 0xF, true));
+}
+
+// The same computation restructured for throughput; its output is identical to
+// quant_pack_kernel's.  The min and max instructions order -0 below +0 and skip quiet
+// NaNs, so a group's extrema do not depend on the order its elements are visited in, and
+// the restructured kernel visits them in whichever order suits the hardware:
+//  - V groups: each thread takes a contiguous run of the tile (a group is 256 / d runs in
+//    adjacent lanes, joined by row shifts), reading its 16-byte chunks from a rotated
+//    start so that the lanes of a row hit different LDS banks;
+//  - K channels: two channels per thread (one 4- or 8-byte read per token) over a slice
+//    of the group's tokens, the P = 512 / d slices then combined per channel.
+// Codes: with 2-, 4- or 8-bit codes a word holds whole codes of consecutive channels, so a
+// thread keeps one K word column (its channels' parameters in registers for all its
+// rows), a V word reads one group's parameters, a word's elements come from one vector
+// LDS read and its codes from the certified reciprocal product (quant_code_certified);
+// 16-bit codes divide, and 3-bit words, which straddle, are built code by code as in
+// quant_pack_kernel.  Requires d and G powers of two with 32 <= d <= 256 and G >= 16, a
+// tile of 4 to 32 KB, at most 64 KB of LDS and 16-byte aligned sources (the launch
+// checks; other shapes take quant_pack_kernel).
+template <typename T, int M>
+__global__ void __launch_bounds__(kQuantThreads)
+quant_pack_fast_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src, int64_t src_rows,
+                       int64_t src_begin, int d, int G, int k_bits, int v_bits, int param_f32, int64_t capacity,
+                       int64_t dst_begin, uint32_t* __restrict__ k_codes,
+                       uint32_t* __restrict__ v_codes, void* k_scale, void* k_zero, void* v_scale, void* v_zero) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  constexpr int n = M * kQuantThreads * 16 / static_cast<int>(sizeof(T));  // G d elements
+  T* kt = reinterpret_cast<T*>(smem_raw);             // [G][d]
+  T* vt = kt + n;                                     // [G][d]
+  float* ks = reinterpret_cast<float*>(vt + n);       // [d]
+  float* kz = ks + d;                                 // [d]
+  float* vs = kz + d;                                 // [G][d/G]
+  float* vz = vs + d;                                 // [G][d/G]
+  float* vmn = vz + d;                                // [G][d/G] V group extrema
+  float* vmx = vmn + d;                               // [G][d/G]
+  float* kmn = vmx + d;                              // [512/d][d] K slice extrema
+  float* kmx = kmn + 2 * kQuantThreads;               // [512/d][d]
+  const int tid = threadIdx.x;
+  const int grp = blockIdx.x, bh = blockIdx.y, vg = d / G;
+  const int64_t src_base = (static_cast<int64_t>(bh) * src_rows + src_begin + static_cast<int64_t>(grp) * G) * d;
+  const int64_t dst_tok0 = dst_begin + static_cast<int64_t>(grp) * G;
+  const int64_t row0 = static_cast<int64_t>(bh) * capacity + dst_tok0;  // first destination token row
+
+  {  // both tiles, 16 bytes per load
+    const uint4* k4 = reinterpret_cast<const uint4*>(k_src + src_base);
+    const uint4* v4 = reinterpret_cast<const uint4*>(v_src + src_base);
+    uint4* kt4 = reinterpret_cast<uint4*>(kt);
+    uint4* vt4 = reinterpret_cast<uint4*>(vt);
+    uint4 a[M], b[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      a[i] = k4[i * kQuantThreads + tid];
+      b[i] = v4[i * kQuantThreads + tid];
+    }
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      kt4[i * kQuantThreads + tid] = a[i];
+      vt4[i * kQuantThreads + tid] = b[i];
+    }
+  }
+  __syncthreads();
+
+  // V: thread tid takes the run of G d / 256 elements (m = 1, 2, 4 or 8 chunks of 16
+  // bytes) that starts at element tid G d / 256; a group is 256 / d such runs, in
+  // adjacent lanes of one 16-lane row.  Each lane starts at chunk tid m / 16 of its run (mod
+  // m), so the 16 lanes of a row read 16 different 16-byte bank columns at every step.
+  {
+    float mn, mx;
+    run_minmax<T, M>(reinterpret_cast<const uint4*>(vt) + tid * M, tid, mn, mx);
+    const int pv = kQuantThreads / d;  // runs per group: 1, 2, 4 or 8
+    if (pv > 1) {
+      mn = fminf(mn, row_shr<1>(mn));
+      mx = fmaxf(mx, row_shr<1>(mx));
+    }
+    if (pv > 2) {
+      mn = fminf(mn, row_shr<2>(mn));
+      mx = fmaxf(mx, row_shr<2>(mx));
+    }
+    if (pv > 4) {
+      mn = fminf(mn, row_shr<4>(mn));
+      mx = fmaxf(mx, row_shr<4>(mx));
+    }
+    if ((tid & (pv - 1)) == pv - 1) {
+      vmn[tid / pv] = mn;
+      vmx[tid / pv] = mx;
+    }
+  }
+
+  // K: thread (pair cp, slice p) takes channels 2 cp, 2 cp + 1 over tokens [p span, (p + 1) span)
+  const int P = 2 * kQuantThreads / d, span = G / P;
+  {
+    const int cp = tid % (d / 2), p = tid / (d / 2);
+    const T* col = kt + 2 * cp + static_cast<int64_t>(p * span) * d;
+    float mn0, mn1;
+    load_pair(col, mn0, mn1);
+    float mx0 = mn0, mx1 = mn1;
+#pragma unroll 4
+    for (int t = 1; t < span; ++t) {
+      float a, b;
+      load_pair(col + t * d, a, b);
+      mn0 = fminf(mn0, a);
+      mx0 = fmaxf(mx0, a);
+      mn1 = fminf(mn1, b);
+      mx1 = fmaxf(mx1, b);
+    }
+    reinterpret_cast<float2*>(kmn)[tid] = make_float2(mn0, mn1);  // kmn[p d + 2 cp + {0, 1}]
+    reinterpret_cast<float2*>(kmx)[tid] = make_float2(mx0, mx1);
+  }
+  __syncthreads();
+  for (int q = tid; q < 2 * d; q += kQuantThreads) {  // K channel q, or V group q - d: the parameters
+    float s, z;
+    if (q < d) {
+      float mn = kmn[q], mx = kmx[q];
+      for (int p = 1; p < P; ++p) {
+        mn = fminf(mn, kmn[p * d + q]);
+        mx = fmaxf(mx, kmx[p * d + q]);
+      }
+      group_params<T>(mn, mx, k_bits, param_f32, s, z);
+      ks[q] = s;
+      kz[q] = z;
+      const int64_t pi = (static_cast<int64_t>(bh) * (capacity / G) + dst_tok0 / G) * d + q;
+      store_param(k_scale, param_f32, pi, s);
+      store_param(k_zero, param_f32, pi, z);
+    } else {
+      const int j = q - d;
+      group_params<T>(vmn[j], vmx[j], v_bits, param_f32, s, z);
+      vs[j] = s;
+      vz[j] = z;
+      const int64_t pi = (row0 + j / vg) * vg + j % vg;
+      store_param(v_scale, param_f32, pi, s);
+      store_param(v_zero, param_f32, pi, z);
+    }
+  }
+  __syncthreads();
+
+  switch (k_bits) {  // wave-uniform
+    case 2: pack_k_columns<2>(kt, ks, kz, d, G, k_codes, row0, tid); break;
+    case 4: pack_k_columns<4>(kt, ks, kz, d, G, k_codes, row0, tid); break;
+    case 8: pack_k_columns<8>(kt, ks, kz, d, G, k_codes, row0, tid); break;
+    case 16: pack_k_columns<16>(kt, ks, kz, d, G, k_codes, row0, tid); break;
+    default: {
+      const int wpr = d * k_bits / 32;
+      for (int j = tid; j < G * wpr; j += kQuantThreads) {
+        const int t = j / wpr, w = j % wpr;
+        const T* row = kt + t * d;
+        k_codes[(row0 + t) * wpr + w] =
+            pack_word(w, k_bits, [&](int c) { return quant_code(Elem<T>::load(row, c), ks[c], kz[c], k_bits); });
+      }
+    }
+  }
+  switch (v_bits) {
+    case 2: pack_v_words<2>(vt, vs, vz, d, G, v_codes, row0, tid); break;
+    case 4: pack_v_words<4>(vt, vs, vz, d, G, v_codes, row0, tid); break;
+    case 8: pack_v_words<8>(vt, vs, vz, d, G, v_codes, row0, tid); break;
+    case 16: pack_v_words<16>(vt, vs, vz, d, G, v_codes, row0, tid); break;
+    default: {
+      const int wpr = d * v_bits / 32;
+      for (int j = tid; j < G * wpr; j += kQuantThreads) {
+        const int t = j / wpr, w = j % wpr;
+        const T* row = vt + t * d;
+        v_codes[(row0 + t) * wpr + w] = pack_word(w, v_bits, [&](int c) {
+          const int g = c / G;
+          return quant_code(Elem<T>::load(row, c), vs[t * vg + g], vz[t * vg + g], v_bits);
+        });
+      }
+    }
+  }
+}
+
+// quant_pack_fast_kernel<T, M> for M = chunks: one workgroup per tile
+template <typename T, int M>
+static vc_status launch_quant_fast_m(const T* k_src, const T* v_src, int64_t src_rows, int64_t src_begin, int d,
+                                     int G, const vc_ckv* c, int pf32, int64_t dst_begin, dim3 grid, size_t flds,
+                                     hipStream_t stream) {
+  hipLaunchKernelGGL((quant_pack_fast_kernel<T, M>), grid, dim3(kQuantThreads), flds, stream, k_src, v_src, src_rows,
+                     src_begin, d, G, c->k_bits, c->v_bits, pf32, c->capacity, dst_begin, c->k_codes, c->v_codes,
+                     c->k_scale, c->k_zero, c->v_scale, c->v_zero);
+  return VC_OK;
+}
+
+template <typename T>
+static vc_status launch_quant_fast(int chunks, const T* k_src, const T* v_src, int64_t src_rows, int64_t src_begin,
+                                   int d, int G, const vc_ckv* c, int pf32, int64_t dst_begin, dim3 grid, size_t flds,
+                                   hipStream_t stream) {
+  switch (chunks) {
+    case 1: return launch_quant_fast_m<T, 1>(k_src, v_src, src_rows, src_begin, d, G, c, pf32, dst_begin, grid, flds, stream);
+    case 2: return launch_quant_fast_m<T, 2>(k_src, v_src, src_rows, src_begin, d, G, c, pf32, dst_begin, grid, flds, stream);
+    case 4: return launch_quant_fast_m<T, 4>(k_src, v_src, src_rows, src_begin, d, G, c, pf32, dst_begin, grid, flds, stream);
+    default: return launch_quant_fast_m<T, 8>(k_src, v_src, src_rows, src_begin, d, G, c, pf32, dst_begin, grid, flds, stream);
+  }
+}
+
 static bool valid_bits(int b) { return b == 2 || b == 3 || b == 4 || b == 8 || b == 16; }
 
 vc_status validate_quant_ckv(const vc_ckv* c) {
@@ -201,6 +574,26 @@ vc_status compress_quant(const vc_ckv* c, const void* k_src, const void* v_src, 
   dim3 grid(static_cast<unsigned>(n_tokens / G), static_cast<unsigned>(c->B * c->Hkv));
   size_t lds = tile_bytes + 4 * static_cast<size_t>(c->d) * sizeof(float);
   int pf32 = c->param_dtype == VC_F32;
+  const int d = c->d;
+  const size_t flds = 2 * tile_bytes + 6 * static_cast<size_t>(d) * sizeof(float) + 4 * kQuantThreads * sizeof(float);
+  const bool pow2_d = d >= 32 && d <= kQuantThreads && (d & (d - 1)) == 0;
+  const bool pow2_g = G >= 16 && (G & (G - 1)) == 0;
+  const bool fast = pow2_d && pow2_g && tile_bytes >= 16 * kQuantThreads && flds <= 65536 &&
+                    reinterpret_cast<uintptr_t>(k_src) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(v_src) % 16 == 0 &&
+                    (c->k_bits == 3 || kQuantThreads % (d * c->k_bits / 32) == 0);
+  if (fast) {
+    const int chunks = static_cast<int>(tile_bytes / (16 * kQuantThreads));  // 1, 2, 4 or 8
+    st = c->kv_dtype == VC_F32
+             ? launch_quant_fast<float>(chunks, static_cast<const float*>(k_src), static_cast<const float*>(v_src),
+                                        src_rows, src_begin, d, G, c, pf32, dst_begin, grid, flds, stream)
+             : launch_quant_fast<bf16_t>(chunks, static_cast<const bf16_t*>(k_src),
+                                         static_cast<const bf16_t*>(v_src), src_rows, src_begin, d, G, c, pf32,
+                                         dst_begin, grid, flds, stream);
+    if (st != VC_OK) return st;
+    VC_LAUNCHED("quant_pack_fast_kernel");
+    return VC_OK;
+  }
   if (c->kv_dtype == VC_F32)
     hipLaunchKernelGGL(quant_pack_kernel<float>, grid, dim3(kQuantThreads), lds, stream,
                        static_cast<const float*>(k_src), static_cast<const float*>(v_src), src_rows, src_begin,
