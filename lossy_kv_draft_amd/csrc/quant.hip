@@ -283,6 +283,51 @@ __device__ __forceinline__ void pack_v_words(const T* tile, const float* vs, con
   }
 }
 
+// 3-bit V codes: the 32 codes of channels [32 u, 32 u + 32) of a token fill exactly words
+// 3 u .. 3 u + 2 of its row.  A thread forms 16 of them (48 bits, channels of one group);
+// the threads of a pair (adjacent lanes, the even one holding the first 16) swap the low
+// half of the odd one's bits, then the even thread stores words 3 u and 3 u + 1 and the odd
+// thread word 3 u + 2.
+template <typename T>
+__device__ __forceinline__ void pack_v_3bit(const T* tile, const float* vs, const float* vz, int d, int G,
+                                            uint32_t* codes, int64_t row0, int tid) {
+  const int hpr = d / 16, wpr = d * 3 / 32, vg = d / G;  // 16-code halves and words per row
+  for (int j = tid; j < G * hpr; j += kQuantThreads) {   // G hpr is even: pairs stay together
+    const int t = j / hpr, h = j % hpr, c0 = 16 * h;
+    const int gi = t * vg + c0 / G;
+    const float s = vs[gi], z = vz[gi], r = scale_reciprocal(s);
+    float x[16];
+    load_run<16>(tile + t * d + c0, x);
+    uint32_t q[16];
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = quant_code_certified<3>(x[i], z, r, ok);
+    if (__builtin_amdgcn_ballot_w64(!ok)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) q[i] = quant_code(x[i], s, z, 3);
+    }
+    uint32_t lo = 0, hi = 0;  // bits [0, 32) and [32, 48) of this half
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (3 * i + 3 <= 32) lo |= q[i] << (3 * i);
+      else if (3 * i >= 32) hi |= q[i] << (3 * i - 32);
+      else {
+        lo |= q[i] << (3 * i);
+        hi |= q[i] >> (32 - 3 * i);
+      }
+    }
+    const uint32_t other = static_cast<uint32_t>(
+        __builtin_amdgcn_mov_dpp(static_cast<int>(lo), 0xB1, 0xF, 0xF, false));  // quad_perm [1, 0, 3, 2]
+    uint32_t* w = codes + (row0 + t) * wpr + 3 * (h >> 1);
+    if ((h & 1) == 0) {
+      w[0] = lo;
+      w[1] = (hi & 0xFFFFu) | (other << 16);
+    } else {
+      w[2] = (lo >> 16) | (hi << 16);
+    }
+  }
+}
+
 // Two consecutive tile elements as float32 (one 4-byte LDS read for bf16, 8 for float32)
 template <typename T>
 __device__ __forceinline__ void load_pair(const T* p, float& a, float& b) {
@@ -355,8 +400,8 @@ __device__ __forceinline__ float row_shr(float v) {
 // thread keeps one K word column (its channels' parameters in registers for all its
 // rows), a V word reads one group's parameters, a word's elements come from one vector
 // LDS read and its codes from the certified reciprocal product (quant_code_certified);
-// 16-bit codes divide, and 3-bit words, which straddle, are built code by code as in
-// quant_pack_kernel.  Requires d and G powers of two with 32 <= d <= 256 and G >= 16, a
+// 16-bit codes divide; 3-bit V codes are formed 16 per thread (pack_v_3bit), and 3-bit K
+// words, which straddle, are built code by code as in quant_pack_kernel.  Requires d and G powers of two with 32 <= d <= 256 and G >= 16, a
 // tile of 4 to 32 KB, at most 64 KB of LDS and 16-byte aligned sources (the launch
 // checks; other shapes take quant_pack_kernel).
 template <typename T, int M>
@@ -495,6 +540,7 @@ quant_pack_fast_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src,
     case 4: pack_v_words<4>(vt, vs, vz, d, G, v_codes, row0, tid); break;
     case 8: pack_v_words<8>(vt, vs, vz, d, G, v_codes, row0, tid); break;
     case 16: pack_v_words<16>(vt, vs, vz, d, G, v_codes, row0, tid); break;
+    case 3: pack_v_3bit(vt, vs, vz, d, G, v_codes, row0, tid); break;
     default: {
       const int wpr = d * v_bits / 32;
       for (int j = tid; j < G * wpr; j += kQuantThreads) {

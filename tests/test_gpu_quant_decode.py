@@ -87,6 +87,65 @@ def test_compress_constant_groups_give_zero_scale():
     assert torch.all(ckv.k_zero.float() == 1.5)
 
 
+# Codes on and beside half-integers.  Every group holds the extremes 0 and 2^b - 1 (so
+# its scale is 1 and its zero 0 in either parameter type) and otherwise multiples of 1/2,
+# a third of them moved one unit of the storage type up and a third down, all times a
+# power of two per (sequence, kv-head): the quotients are exact half-integers (ties,
+# which round to even) or lie within an ulp of one.
+TIE_CASES = {
+    "bf16_k2v2_g64": C.small(C.LLAMA8B, k_bits=2, v_bits=2),
+    "bf16_k4v4_g64": C.small(C.LLAMA8B, k_bits=4, v_bits=4),
+    "bf16_k3v3_g64": C.small(C.LLAMA8B, k_bits=3, v_bits=3),
+    "bf16_k8v8_g64": C.small(C.LLAMA8B, k_bits=8, v_bits=8, scale_dtype="f32"),
+    "bf16_k4v3_g32": C.small(C.QWEN30B),
+    "f32_k2v3_g32": C.TINY.with_(v_bits=3),
+    "f32_k8v4_g32": C.TINY.with_(k_bits=8, v_bits=4),
+}
+
+
+def _lattice(w, N, axis, seed):
+    rng = np.random.default_rng(seed)
+    hi = 2 ** (w.k_bits if axis == 2 else w.v_bits) - 1
+    shape = (w.B, w.Hkv, N, w.d)
+    x = (rng.integers(0, 2 * hi + 1, size=shape) / 2).astype(np.float32)
+    x = G.to_storage(x, w.dtype)
+    step = rng.integers(-1, 2, size=shape)
+    if w.dtype == "bf16":
+        u = x.view(np.uint32).astype(np.int64) + step * 0x10000
+        x = np.where(x > 0, u, x.view(np.uint32)).astype(np.uint32).view(np.float32)
+    else:
+        x = np.where(step > 0, np.nextafter(x, np.float32(np.inf)),
+                     np.where(step < 0, np.nextafter(x, np.float32(0)), x)).astype(np.float32)
+    x = np.clip(x, 0, hi).astype(np.float32)
+    idx = [slice(None)] * 4
+    for g0 in range(0, x.shape[axis], w.group):
+        idx[axis] = g0
+        x[tuple(idx)] = 0.0
+        idx[axis] = g0 + 1
+        x[tuple(idx)] = hi
+    e = rng.integers(-4, 5, size=(w.B, w.Hkv, 1, 1)).astype(np.float32)
+    return (x * np.exp2(e)).astype(np.float32)
+
+
+@pytest.mark.parametrize("name", list(TIE_CASES))
+def test_compress_ties_and_near_ties_bit_exact(name):
+    w = TIE_CASES[name]
+    N = 4 * w.group
+    say(f"[quant ties] {name} d{w.d} k{w.k_bits} v{w.v_bits} G{w.group}")
+    K, V = _lattice(w, N, 2, 5), _lattice(w, N, 3, 6)
+    for X, bits in ((K, w.k_bits), (V, w.v_bits)):  # the case does exercise exact ties
+        s = X.max(axis=(2, 3), keepdims=True) / (2 ** bits - 1)
+        assert np.mean((X / s) % 1 == 0.5) > 0.05
+    ckv = _ckv(w, N)
+    L.vc_compress(ckv, T(K, tdtype(w.dtype)), T(V, tdtype(w.dtype)))
+    torch.cuda.synchronize()
+    ref = oracle_compress(w, K, V)
+    assert np.array_equal(ckv.k_codes.cpu().numpy().view(np.uint32), ref["k_codes"])
+    assert np.array_equal(ckv.v_codes.cpu().numpy().view(np.uint32), ref["v_codes"])
+    for key in ("k_scale", "k_zero", "v_scale", "v_zero"):
+        assert np.array_equal(np32(getattr(ckv, key)), ref[key]), key
+
+
 def _scaled(x, scale, dtype):
     """x * scale rounded to the storage type (both sides get the rounded values)."""
     return x if scale == 1.0 else G.to_storage(x * np.float32(scale), dtype)
