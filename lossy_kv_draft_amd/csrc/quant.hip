@@ -15,11 +15,13 @@
 //
 // One workgroup quantizes one tile of G tokens x d channels of one (sequence,
 // kv-head): the tile is staged in LDS in the source type (bf16 values convert to
-// float32 exactly when read), parameters are computed by one
-// thread per K channel / per (token, V group), then each thread builds whole
-// 32-bit words of packed codes (a word may hold a code that straddles into the
-// next word; both words compute that code).  HBM-bound: each input element is
-// read once and each output word written once.
+// float32 exactly when read), the group parameters are computed, then threads build
+// whole 32-bit words of packed codes.  Each input element is read from HBM once and
+// each output word written once; at the measured shapes the vector instructions per
+// element, not HBM, set the time.  quant_pack_kernel is the direct form (one thread
+// per K channel / per (token, V group) for the parameters, a code that straddles two
+// words computed by both); quant_pack_fast_kernel, further down, the restructured one
+// used wherever its shape limits allow.
 
 #include "common.h"
 
