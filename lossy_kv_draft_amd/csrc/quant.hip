@@ -168,13 +168,25 @@ quant_pack_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src, int6
 // integer; where |qa| is larger, both clamp to the same end of [0, 2^BITS - 1].  ok is
 // cleared otherwise, and for NaN (scale_reciprocal returns NaN for a scale whose
 // reciprocal would not be accurate), and the caller then forms the code with quant_code.
+// The code is returned in biased form: the bits of fl(clamp(qa, 0, 2^BITS - 1) + 1.5 2^23),
+// which are kCodeBias plus the code (the addition rounds half to even to an integer, and
+// rounding after the clamp equals clamping after it).
+constexpr uint32_t kCodeBias = 0x4B400000u;  // bits of 1.5 2^23
 template <int BITS>
-__device__ __forceinline__ uint32_t quant_code_certified(float x, float z, float r, bool& ok) {
+__device__ __forceinline__ uint32_t quant_biased_certified(float x, float z, float r, bool& ok) {
   static_assert(BITS <= 8, "the margin grows with the code width");
   const float qa = __fmul_rn(__fsub_rn(x, z), r);
   ok = ok & (fabsf(__builtin_amdgcn_fractf(qa) - 0.5f) > static_cast<float>(1 << BITS) * 0x1p-20f);
-  return static_cast<uint32_t>(
-      __builtin_amdgcn_fmed3f(rintf(qa), 0.0f, static_cast<float>((1 << BITS) - 1)));
+  return __float_as_uint(
+      __fadd_rn(__builtin_amdgcn_fmed3f(qa, 0.0f, static_cast<float>((1 << BITS) - 1)), 0x1.8p23f));
+}
+
+// sum over the N codes of a word of kCodeBias << (i BITS), modulo 2^32
+template <int BITS, int N>
+constexpr uint32_t word_bias() {
+  uint32_t b = 0;
+  for (int i = 0; i < N; ++i) b += kCodeBias << (i * BITS);
+  return b;
 }
 
 // 1/s for a normal finite scale, else NaN (zero, subnormal and non-finite scales go to
@@ -184,21 +196,35 @@ __device__ __forceinline__ float scale_reciprocal(float s) {
 }
 
 // One word of N = 32 / BITS codes from elements x with per-code parameters (s, z) and
-// reciprocals r: certified products where the whole wave's are, else quant_code for
-// the wave (the branch is wave-uniform and rare up to 8 bits; 16-bit codes always divide).
+// reciprocals r: each code from the certified product, and a code that some lane of the
+// wave could not certify from the division (quant_code) in those lanes.  The branch per
+// code is wave-uniform: with bf16 data and parameters about 0.2% of the quotients are
+// exact half-integers (never certified), so a code position needs the division in
+// about one wave in eight, a whole word in most.  16-bit codes always divide.
 template <int BITS, int N, typename SZ>
 __device__ __forceinline__ uint32_t pack_word_fast(const float (&x)[N], SZ sz) {
-  uint32_t word = 0;
   if constexpr (BITS <= 8) {
-    bool ok = true;
+    uint32_t b[N];
+    bool ok[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) word |= quant_code_certified<BITS>(x[i], sz.z(i), sz.r(i), ok) << (i * BITS);
-    if (!__builtin_amdgcn_ballot_w64(!ok)) return word;
-    word = 0;
+    for (int i = 0; i < N; ++i) {
+      ok[i] = true;
+      b[i] = quant_biased_certified<BITS>(x[i], sz.z(i), sz.r(i), ok[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (__builtin_amdgcn_ballot_w64(!ok[i]))
+        if (!ok[i]) b[i] = kCodeBias + quant_code(x[i], sz.s(i), sz.z(i), BITS);
+    uint32_t acc = 0;  // the biased codes, each shifted to its field: the biases sum to word_bias
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc += b[i] << (i * BITS);
+    return acc - word_bias<BITS, N>();
+  } else {
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) word |= quant_code(x[i], sz.s(i), sz.z(i), BITS) << (i * BITS);
+    return word;
   }
-#pragma unroll
-  for (int i = 0; i < N; ++i) word |= quant_code(x[i], sz.s(i), sz.z(i), BITS) << (i * BITS);
-  return word;
 }
 
 // N consecutive tile elements as float32 from an LDS run that starts at a multiple of
@@ -238,50 +264,50 @@ __device__ __forceinline__ void load_run(const T* p, float (&x)[N]) {
 }
 
 template <int BITS, typename T>
-__device__ __forceinline__ void pack_k_columns(const T* tile, const float* ks, const float* kz, int d, int G,
+__device__ __forceinline__ void pack_k_columns(const T* tile, const float* ks, const float* kz, int d, int G, int ld,
                                                uint32_t* codes, int64_t row0, int tid) {
-  constexpr int CPW = 32 / BITS;
-  const int wpr = d / CPW;
-  const int w = tid % wpr, rstep = kQuantThreads / wpr;
+  constexpr int CPW = 32 / BITS, LCPW = BITS == 2 ? 4 : BITS == 4 ? 3 : BITS == 8 ? 2 : 1;
+  const int lw = ld - LCPW, wpr = 1 << lw;  // words per row (d and CPW are powers of two)
+  const int w = tid & (wpr - 1), rstep = kQuantThreads >> lw;
   const int c0 = w * CPW;
-  float s[CPW], z[CPW], r[CPW];
+  float z[CPW], r[CPW];  // the scales themselves are read from LDS on the division path only
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
-    s[i] = ks[c0 + i];
     z[i] = kz[c0 + i];
-    r[i] = scale_reciprocal(s[i]);
+    r[i] = scale_reciprocal(ks[c0 + i]);
   }
-  for (int t = tid / wpr; t < G; t += rstep) {
+  for (int t = tid >> lw; t < G; t += rstep) {
     float x[CPW];
-    load_run<CPW>(tile + t * d + c0, x);
+    load_run<CPW>(tile + (t << ld) + c0, x);
     struct {
       const float *s_, *z_, *r_;
       __device__ float s(int i) const { return s_[i]; }
       __device__ float z(int i) const { return z_[i]; }
       __device__ float r(int i) const { return r_[i]; }
-    } sz{s, z, r};
-    codes[(row0 + t) * wpr + w] = pack_word_fast<BITS>(x, sz);
+    } sz{ks + c0, z, r};
+    codes[((row0 + t) << lw) + w] = pack_word_fast<BITS>(x, sz);
   }
 }
 
 template <int BITS, typename T>
-__device__ __forceinline__ void pack_v_words(const T* tile, const float* vs, const float* vz, int d, int G,
-                                             uint32_t* codes, int64_t row0, int tid) {
-  constexpr int CPW = 32 / BITS;
-  const int wpr = d / CPW, vg = d / G;
-  for (int j = tid; j < G * wpr; j += kQuantThreads) {
-    const int t = j / wpr, w = j % wpr, c0 = w * CPW;
-    const float s = vs[t * vg + c0 / G], z = vz[t * vg + c0 / G];  // CPW <= 16 <= G: one group per word
+__device__ __forceinline__ void pack_v_words(const T* tile, const float* vs, const float* vz, int d, int G, int ld,
+                                             int lg, uint32_t* codes, int64_t row0, int tid) {
+  constexpr int CPW = 32 / BITS, LCPW = BITS == 2 ? 4 : BITS == 4 ? 3 : BITS == 8 ? 2 : 1;
+  const int lw = ld - LCPW, wpr = 1 << lw;
+  for (int j = tid; j < (G << lw); j += kQuantThreads) {
+    const int t = j >> lw, c0 = (j & (wpr - 1)) * CPW;
+    const int gi = (t << (ld - lg)) + (c0 >> lg);  // CPW <= 16 <= G: one group per word
+    const float s = vs[gi], z = vz[gi];
     const float r = scale_reciprocal(s);
     float x[CPW];
-    load_run<CPW>(tile + t * d + c0, x);
+    load_run<CPW>(tile + (t << ld) + c0, x);
     struct {
       float s_, z_, r_;
       __device__ float s(int) const { return s_; }
       __device__ float z(int) const { return z_; }
       __device__ float r(int) const { return r_; }
     } sz{s, z, r};
-    codes[(row0 + t) * wpr + w] = pack_word_fast<BITS>(x, sz);
+    codes[((row0 + t) << lw) + (j & (wpr - 1))] = pack_word_fast<BITS>(x, sz);
   }
 }
 
@@ -291,23 +317,26 @@ __device__ __forceinline__ void pack_v_words(const T* tile, const float* vs, con
 // half of the odd one's bits, then the even thread stores words 3 u and 3 u + 1 and the odd
 // thread word 3 u + 2.
 template <typename T>
-__device__ __forceinline__ void pack_v_3bit(const T* tile, const float* vs, const float* vz, int d, int G,
-                                            uint32_t* codes, int64_t row0, int tid) {
-  const int hpr = d / 16, wpr = d * 3 / 32, vg = d / G;  // 16-code halves and words per row
-  for (int j = tid; j < G * hpr; j += kQuantThreads) {   // G hpr is even: pairs stay together
-    const int t = j / hpr, h = j % hpr, c0 = 16 * h;
-    const int gi = t * vg + c0 / G;
+__device__ __forceinline__ void pack_v_3bit(const T* tile, const float* vs, const float* vz, int d, int G, int ld,
+                                            int lg, uint32_t* codes, int64_t row0, int tid) {
+  const int lh = ld - 4, wpr = d * 3 / 32;               // 16-code halves (a power of two) and words per row
+  for (int j = tid; j < (G << lh); j += kQuantThreads) {  // G d / 16 is even: pairs stay together
+    const int t = j >> lh, h = j & ((1 << lh) - 1), c0 = 16 * h;
+    const int gi = (t << (ld - lg)) + (c0 >> lg);
     const float s = vs[gi], z = vz[gi], r = scale_reciprocal(s);
     float x[16];
-    load_run<16>(tile + t * d + c0, x);
+    load_run<16>(tile + (t << ld) + c0, x);
     uint32_t q[16];
-    bool ok = true;
+    bool ok[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) q[i] = quant_code_certified<3>(x[i], z, r, ok);
-    if (__builtin_amdgcn_ballot_w64(!ok)) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) q[i] = quant_code(x[i], s, z, 3);
+    for (int i = 0; i < 16; ++i) {
+      ok[i] = true;
+      q[i] = quant_biased_certified<3>(x[i], z, r, ok[i]) & 7u;
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)  // the division where a lane could not certify (wave-uniform test)
+      if (__builtin_amdgcn_ballot_w64(!ok[i]))
+        if (!ok[i]) q[i] = quant_code(x[i], s, z, 3);
     uint32_t lo = 0, hi = 0;  // bits [0, 32) and [32, 48) of this half
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -401,7 +430,7 @@ __device__ __forceinline__ float row_shr(float v) {
 // Codes: with 2-, 4- or 8-bit codes a word holds whole codes of consecutive channels, so a
 // thread keeps one K word column (its channels' parameters in registers for all its
 // rows), a V word reads one group's parameters, a word's elements come from one vector
-// LDS read and its codes from the certified reciprocal product (quant_code_certified);
+// LDS read and its codes from the certified reciprocal product (quant_biased_certified);
 // 16-bit codes divide; 3-bit V codes are formed 16 per thread (pack_v_3bit), and 3-bit K
 // words, which straddle, are built code by code as in quant_pack_kernel.  Requires d and G powers of two with 32 <= d <= 256 and G >= 16, a
 // tile of 4 to 32 KB, at most 64 KB of LDS and 16-byte aligned sources (the launch
@@ -425,7 +454,8 @@ quant_pack_fast_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src,
   float* kmn = vmx + d;                              // [512/d][d] K slice extrema
   float* kmx = kmn + 2 * kQuantThreads;               // [512/d][d]
   const int tid = threadIdx.x;
-  const int grp = blockIdx.x, bh = blockIdx.y, vg = d / G;
+  const int grp = blockIdx.x, bh = blockIdx.y;
+  const int ld = __builtin_ctz(d), lg = __builtin_ctz(G);  // d and G are powers of two
   const int64_t src_base = (static_cast<int64_t>(bh) * src_rows + src_begin + static_cast<int64_t>(grp) * G) * d;
   const int64_t dst_tok0 = dst_begin + static_cast<int64_t>(grp) * G;
   const int64_t row0 = static_cast<int64_t>(bh) * capacity + dst_tok0;  // first destination token row
@@ -456,7 +486,7 @@ quant_pack_fast_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src,
   {
     float mn, mx;
     run_minmax<T, M>(reinterpret_cast<const uint4*>(vt) + tid * M, tid, mn, mx);
-    const int pv = kQuantThreads / d;  // runs per group: 1, 2, 4 or 8
+    const int pv = kQuantThreads >> ld;  // runs per group: 1, 2, 4 or 8
     if (pv > 1) {
       mn = fminf(mn, row_shr<1>(mn));
       mx = fmaxf(mx, row_shr<1>(mx));
@@ -470,23 +500,23 @@ quant_pack_fast_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src,
       mx = fmaxf(mx, row_shr<4>(mx));
     }
     if ((tid & (pv - 1)) == pv - 1) {
-      vmn[tid / pv] = mn;
-      vmx[tid / pv] = mx;
+      vmn[tid >> (8 - ld)] = mn;
+      vmx[tid >> (8 - ld)] = mx;
     }
   }
 
   // K: thread (pair cp, slice p) takes channels 2 cp, 2 cp + 1 over tokens [p span, (p + 1) span)
-  const int P = 2 * kQuantThreads / d, span = G / P;
+  const int P = 2 * kQuantThreads >> ld, span = G >> (9 - ld);
   {
-    const int cp = tid % (d / 2), p = tid / (d / 2);
-    const T* col = kt + 2 * cp + static_cast<int64_t>(p * span) * d;
+    const int cp = tid & ((d >> 1) - 1), p = tid >> (ld - 1);
+    const T* col = kt + 2 * cp + ((p * span) << ld);
     float mn0, mn1;
     load_pair(col, mn0, mn1);
     float mx0 = mn0, mx1 = mn1;
 #pragma unroll 4
     for (int t = 1; t < span; ++t) {
       float a, b;
-      load_pair(col + t * d, a, b);
+      load_pair(col + (t << ld), a, b);
       mn0 = fminf(mn0, a);
       mx0 = fmaxf(mx0, a);
       mn1 = fminf(mn1, b);
@@ -501,13 +531,13 @@ quant_pack_fast_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src,
     if (q < d) {
       float mn = kmn[q], mx = kmx[q];
       for (int p = 1; p < P; ++p) {
-        mn = fminf(mn, kmn[p * d + q]);
-        mx = fmaxf(mx, kmx[p * d + q]);
+        mn = fminf(mn, kmn[(p << ld) + q]);
+        mx = fmaxf(mx, kmx[(p << ld) + q]);
       }
       group_params<T>(mn, mx, k_bits, param_f32, s, z);
       ks[q] = s;
       kz[q] = z;
-      const int64_t pi = (static_cast<int64_t>(bh) * (capacity / G) + dst_tok0 / G) * d + q;
+      const int64_t pi = ((static_cast<int64_t>(bh) * (capacity >> lg) + (dst_tok0 >> lg)) << ld) + q;
       store_param(k_scale, param_f32, pi, s);
       store_param(k_zero, param_f32, pi, z);
     } else {
@@ -515,7 +545,7 @@ quant_pack_fast_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src,
       group_params<T>(vmn[j], vmx[j], v_bits, param_f32, s, z);
       vs[j] = s;
       vz[j] = z;
-      const int64_t pi = (row0 + j / vg) * vg + j % vg;
+      const int64_t pi = (row0 << (ld - lg)) + j;  // (row0 + j / vg) vg + j mod vg, vg = d / G
       store_param(v_scale, param_f32, pi, s);
       store_param(v_zero, param_f32, pi, z);
     }
@@ -523,10 +553,10 @@ quant_pack_fast_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src,
   __syncthreads();
 
   switch (k_bits) {  // wave-uniform
-    case 2: pack_k_columns<2>(kt, ks, kz, d, G, k_codes, row0, tid); break;
-    case 4: pack_k_columns<4>(kt, ks, kz, d, G, k_codes, row0, tid); break;
-    case 8: pack_k_columns<8>(kt, ks, kz, d, G, k_codes, row0, tid); break;
-    case 16: pack_k_columns<16>(kt, ks, kz, d, G, k_codes, row0, tid); break;
+    case 2: pack_k_columns<2>(kt, ks, kz, d, G, ld, k_codes, row0, tid); break;
+    case 4: pack_k_columns<4>(kt, ks, kz, d, G, ld, k_codes, row0, tid); break;
+    case 8: pack_k_columns<8>(kt, ks, kz, d, G, ld, k_codes, row0, tid); break;
+    case 16: pack_k_columns<16>(kt, ks, kz, d, G, ld, k_codes, row0, tid); break;
     default: {
       const int wpr = d * k_bits / 32;
       for (int j = tid; j < G * wpr; j += kQuantThreads) {
@@ -538,13 +568,13 @@ quant_pack_fast_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src,
     }
   }
   switch (v_bits) {
-    case 2: pack_v_words<2>(vt, vs, vz, d, G, v_codes, row0, tid); break;
-    case 4: pack_v_words<4>(vt, vs, vz, d, G, v_codes, row0, tid); break;
-    case 8: pack_v_words<8>(vt, vs, vz, d, G, v_codes, row0, tid); break;
-    case 16: pack_v_words<16>(vt, vs, vz, d, G, v_codes, row0, tid); break;
-    case 3: pack_v_3bit(vt, vs, vz, d, G, v_codes, row0, tid); break;
+    case 2: pack_v_words<2>(vt, vs, vz, d, G, ld, lg, v_codes, row0, tid); break;
+    case 4: pack_v_words<4>(vt, vs, vz, d, G, ld, lg, v_codes, row0, tid); break;
+    case 8: pack_v_words<8>(vt, vs, vz, d, G, ld, lg, v_codes, row0, tid); break;
+    case 16: pack_v_words<16>(vt, vs, vz, d, G, ld, lg, v_codes, row0, tid); break;
+    case 3: pack_v_3bit(vt, vs, vz, d, G, ld, lg, v_codes, row0, tid); break;
     default: {
-      const int wpr = d * v_bits / 32;
+      const int wpr = d * v_bits / 32, vg = d / G;
       for (int j = tid; j < G * wpr; j += kQuantThreads) {
         const int t = j / wpr, w = j % wpr;
         const T* row = vt + t * d;
