@@ -432,8 +432,9 @@ __device__ __forceinline__ float row_shr(float v) {
 // rows), a V word reads one group's parameters, a word's elements come from one vector
 // LDS read and its codes from the certified reciprocal product (quant_biased_certified);
 // 16-bit codes divide; 3-bit V codes are formed 16 per thread (pack_v_3bit), and 3-bit K
-// words, which straddle, are built code by code as in quant_pack_kernel.  Requires d and G powers of two with 32 <= d <= 256 and G >= 16, a
-// tile of 4 to 32 KB, at most 64 KB of LDS and 16-byte aligned sources (the launch
+// words, which straddle, are built code by code as in quant_pack_kernel.  Requires d and G
+// powers of two with 32 <= d <= 256 and G >= 16, a tile of 4 to 32 KB, no more LDS than a
+// workgroup may allocate (160 KB on gfx950) and 16-byte aligned sources (the launch
 // checks; other shapes take quant_pack_kernel).
 template <typename T, int M>
 __global__ void __launch_bounds__(kQuantThreads)
@@ -610,6 +611,19 @@ static vc_status launch_quant_fast(int chunks, const T* k_src, const T* v_src, i
   }
 }
 
+// LDS a workgroup may allocate on the current device (queried once per device)
+static size_t max_lds_per_block() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) v = 65536;
+    cached[dev] = v;
+  }
+  return static_cast<size_t>(cached[dev]);
+}
+
 static bool valid_bits(int b) { return b == 2 || b == 3 || b == 4 || b == 8 || b == 16; }
 
 vc_status validate_quant_ckv(const vc_ckv* c) {
@@ -656,7 +670,7 @@ vc_status compress_quant(const vc_ckv* c, const void* k_src, const void* v_src, 
   const size_t flds = 2 * tile_bytes + 6 * static_cast<size_t>(d) * sizeof(float) + 4 * kQuantThreads * sizeof(float);
   const bool pow2_d = d >= 32 && d <= kQuantThreads && (d & (d - 1)) == 0;
   const bool pow2_g = G >= 16 && (G & (G - 1)) == 0;
-  const bool fast = pow2_d && pow2_g && tile_bytes >= 16 * kQuantThreads && flds <= 65536 &&
+  const bool fast = pow2_d && pow2_g && tile_bytes >= 16 * kQuantThreads && flds <= max_lds_per_block() &&
                     reinterpret_cast<uintptr_t>(k_src) % 16 == 0 &&
                     reinterpret_cast<uintptr_t>(v_src) % 16 == 0 &&
                     (c->k_bits == 3 || kQuantThreads % (d * c->k_bits / 32) == 0);
