@@ -311,11 +311,66 @@ __device__ __forceinline__ void pack_v_words(const T* tile, const float* vs, con
   }
 }
 
-// 3-bit V codes: the 32 codes of channels [32 u, 32 u + 32) of a token fill exactly words
-// 3 u .. 3 u + 2 of its row.  A thread forms 16 of them (48 bits, channels of one group);
-// the threads of a pair (adjacent lanes, the even one holding the first 16) swap the low
-// half of the odd one's bits, then the even thread stores words 3 u and 3 u + 1 and the odd
-// thread word 3 u + 2.
+// 16 3-bit codes q (channels 16 h .. 16 h + 15 of a row) into the row's words: the 32
+// codes of channels [32 u, 32 u + 32) fill exactly words 3 u .. 3 u + 2.  The threads of a
+// pair (adjacent lanes, h even in the first) swap the low half of the odd one's 48 bits,
+// then the even thread stores words 3 u and 3 u + 1 and the odd thread word 3 u + 2.
+// Both lanes of every pair must execute this together.
+__device__ __forceinline__ void store_3bit_half(const uint32_t (&q)[16], int h, uint32_t* row_words) {
+  uint32_t lo = 0, hi = 0;  // bits [0, 32) and [32, 48) of this half
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (3 * i + 3 <= 32) lo |= q[i] << (3 * i);
+    else if (3 * i >= 32) hi |= q[i] << (3 * i - 32);
+    else {
+      lo |= q[i] << (3 * i);
+      hi |= q[i] >> (32 - 3 * i);
+    }
+  }
+  const uint32_t other = static_cast<uint32_t>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(lo), 0xB1, 0xF, 0xF, false));  // quad_perm [1, 0, 3, 2]
+  uint32_t* w = row_words + 3 * (h >> 1);
+  if ((h & 1) == 0) {
+    w[0] = lo;
+    w[1] = (hi & 0xFFFFu) | (other << 16);
+  } else {
+    w[2] = (lo >> 16) | (hi << 16);
+  }
+}
+
+// 3-bit K codes: a thread keeps the column of 16 channels 16 h .. (its zeros and
+// reciprocals in registers) over rows t = tid / (d / 16), + 256 / (d / 16), ...
+template <typename T>
+__device__ __forceinline__ void pack_k_3bit(const T* tile, const float* ks, const float* kz, int d, int G, int ld,
+                                            uint32_t* codes, int64_t row0, int tid) {
+  const int lh = ld - 4, wpr = d * 3 / 32;  // 16-code halves per row (a power of two), words per row
+  const int h = tid & ((1 << lh) - 1), c0 = 16 * h, rstep = kQuantThreads >> lh;
+  float z[16], r[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    z[i] = kz[c0 + i];
+    r[i] = scale_reciprocal(ks[c0 + i]);
+  }
+  for (int t = tid >> lh; t < G; t += rstep) {  // the lanes of a pair share t
+    float x[16];
+    load_run<16>(tile + (t << ld) + c0, x);
+    uint32_t q[16];
+    bool ok[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      ok[i] = true;
+      q[i] = quant_biased_certified<3>(x[i], z[i], r[i], ok[i]) & 7u;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)  // the division where a lane could not certify (wave-uniform test)
+      if (__builtin_amdgcn_ballot_w64(!ok[i]))
+        if (!ok[i]) q[i] = quant_code(x[i], ks[c0 + i], z[i], 3);
+    store_3bit_half(q, h, codes + (row0 + t) * wpr);
+  }
+}
+
+// 3-bit V codes: a thread forms the 16 codes of channels 16 h .. 16 h + 15 of one token
+// (one group's parameters, since G >= 16) and stores them with store_3bit_half.
 template <typename T>
 __device__ __forceinline__ void pack_v_3bit(const T* tile, const float* vs, const float* vz, int d, int G, int ld,
                                             int lg, uint32_t* codes, int64_t row0, int tid) {
@@ -337,25 +392,7 @@ __device__ __forceinline__ void pack_v_3bit(const T* tile, const float* vs, cons
     for (int i = 0; i < 16; ++i)  // the division where a lane could not certify (wave-uniform test)
       if (__builtin_amdgcn_ballot_w64(!ok[i]))
         if (!ok[i]) q[i] = quant_code(x[i], s, z, 3);
-    uint32_t lo = 0, hi = 0;  // bits [0, 32) and [32, 48) of this half
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (3 * i + 3 <= 32) lo |= q[i] << (3 * i);
-      else if (3 * i >= 32) hi |= q[i] << (3 * i - 32);
-      else {
-        lo |= q[i] << (3 * i);
-        hi |= q[i] >> (32 - 3 * i);
-      }
-    }
-    const uint32_t other = static_cast<uint32_t>(
-        __builtin_amdgcn_mov_dpp(static_cast<int>(lo), 0xB1, 0xF, 0xF, false));  // quad_perm [1, 0, 3, 2]
-    uint32_t* w = codes + (row0 + t) * wpr + 3 * (h >> 1);
-    if ((h & 1) == 0) {
-      w[0] = lo;
-      w[1] = (hi & 0xFFFFu) | (other << 16);
-    } else {
-      w[2] = (lo >> 16) | (hi << 16);
-    }
+    store_3bit_half(q, h, codes + (row0 + t) * wpr);
   }
 }
 
@@ -431,12 +468,12 @@ __device__ __forceinline__ float row_shr(float v) {
 // thread keeps one K word column (its channels' parameters in registers for all its
 // rows), a V word reads one group's parameters, a word's elements come from one vector
 // LDS read and its codes from the certified reciprocal product (quant_biased_certified);
-// 16-bit codes divide; 3-bit V codes are formed 16 per thread (pack_v_3bit), and 3-bit K
-// words, which straddle, are built code by code as in quant_pack_kernel.  Requires d and G
+// 16-bit codes divide; 3-bit codes (whose words straddle) are formed 16 per thread, the
+// lanes of a pair completing each other's words (pack_k_3bit, pack_v_3bit).  Requires d and G
 // powers of two with 32 <= d <= 256 and G >= 16, a tile of 4 to 32 KB, no more LDS than a
 // workgroup may allocate (160 KB on gfx950) and 16-byte aligned sources (the launch
 // checks; other shapes take quant_pack_kernel).
-template <typename T, int M>
+template <typename T, int M, bool K3>
 __global__ void __launch_bounds__(kQuantThreads)
 quant_pack_fast_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src, int64_t src_rows,
                        int64_t src_begin, int d, int G, int k_bits, int v_bits, int param_f32, int64_t capacity,
@@ -553,49 +590,37 @@ quant_pack_fast_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src,
   }
   __syncthreads();
 
-  switch (k_bits) {  // wave-uniform
+  // 3-bit K codes (K3, an instance of its own: its 16-channel columns need more
+  // registers than every other width) or the word columns of the other widths
+  if constexpr (K3) pack_k_3bit(kt, ks, kz, d, G, ld, k_codes, row0, tid);
+  else switch (k_bits) {  // wave-uniform; the bit widths are validated
     case 2: pack_k_columns<2>(kt, ks, kz, d, G, ld, k_codes, row0, tid); break;
     case 4: pack_k_columns<4>(kt, ks, kz, d, G, ld, k_codes, row0, tid); break;
     case 8: pack_k_columns<8>(kt, ks, kz, d, G, ld, k_codes, row0, tid); break;
-    case 16: pack_k_columns<16>(kt, ks, kz, d, G, ld, k_codes, row0, tid); break;
-    default: {
-      const int wpr = d * k_bits / 32;
-      for (int j = tid; j < G * wpr; j += kQuantThreads) {
-        const int t = j / wpr, w = j % wpr;
-        const T* row = kt + t * d;
-        k_codes[(row0 + t) * wpr + w] =
-            pack_word(w, k_bits, [&](int c) { return quant_code(Elem<T>::load(row, c), ks[c], kz[c], k_bits); });
-      }
-    }
+    default: pack_k_columns<16>(kt, ks, kz, d, G, ld, k_codes, row0, tid); break;
   }
   switch (v_bits) {
     case 2: pack_v_words<2>(vt, vs, vz, d, G, ld, lg, v_codes, row0, tid); break;
+    case 3: pack_v_3bit(vt, vs, vz, d, G, ld, lg, v_codes, row0, tid); break;
     case 4: pack_v_words<4>(vt, vs, vz, d, G, ld, lg, v_codes, row0, tid); break;
     case 8: pack_v_words<8>(vt, vs, vz, d, G, ld, lg, v_codes, row0, tid); break;
-    case 16: pack_v_words<16>(vt, vs, vz, d, G, ld, lg, v_codes, row0, tid); break;
-    case 3: pack_v_3bit(vt, vs, vz, d, G, ld, lg, v_codes, row0, tid); break;
-    default: {
-      const int wpr = d * v_bits / 32, vg = d / G;
-      for (int j = tid; j < G * wpr; j += kQuantThreads) {
-        const int t = j / wpr, w = j % wpr;
-        const T* row = vt + t * d;
-        v_codes[(row0 + t) * wpr + w] = pack_word(w, v_bits, [&](int c) {
-          const int g = c / G;
-          return quant_code(Elem<T>::load(row, c), vs[t * vg + g], vz[t * vg + g], v_bits);
-        });
-      }
-    }
+    default: pack_v_words<16>(vt, vs, vz, d, G, ld, lg, v_codes, row0, tid); break;
   }
 }
 
-// quant_pack_fast_kernel<T, M> for M = chunks: one workgroup per tile
+// quant_pack_fast_kernel<T, M, K3> for M = chunks: one workgroup per tile
 template <typename T, int M>
 static vc_status launch_quant_fast_m(const T* k_src, const T* v_src, int64_t src_rows, int64_t src_begin, int d,
                                      int G, const vc_ckv* c, int pf32, int64_t dst_begin, dim3 grid, size_t flds,
                                      hipStream_t stream) {
-  hipLaunchKernelGGL((quant_pack_fast_kernel<T, M>), grid, dim3(kQuantThreads), flds, stream, k_src, v_src, src_rows,
-                     src_begin, d, G, c->k_bits, c->v_bits, pf32, c->capacity, dst_begin, c->k_codes, c->v_codes,
-                     c->k_scale, c->k_zero, c->v_scale, c->v_zero);
+  if (c->k_bits == 3)
+    hipLaunchKernelGGL((quant_pack_fast_kernel<T, M, true>), grid, dim3(kQuantThreads), flds, stream, k_src, v_src,
+                       src_rows, src_begin, d, G, c->k_bits, c->v_bits, pf32, c->capacity, dst_begin, c->k_codes,
+                       c->v_codes, c->k_scale, c->k_zero, c->v_scale, c->v_zero);
+  else
+    hipLaunchKernelGGL((quant_pack_fast_kernel<T, M, false>), grid, dim3(kQuantThreads), flds, stream, k_src, v_src,
+                       src_rows, src_begin, d, G, c->k_bits, c->v_bits, pf32, c->capacity, dst_begin, c->k_codes,
+                       c->v_codes, c->k_scale, c->k_zero, c->v_scale, c->v_zero);
   return VC_OK;
 }
 
@@ -672,8 +697,7 @@ vc_status compress_quant(const vc_ckv* c, const void* k_src, const void* v_src, 
   const bool pow2_g = G >= 16 && (G & (G - 1)) == 0;
   const bool fast = pow2_d && pow2_g && tile_bytes >= 16 * kQuantThreads && flds <= max_lds_per_block() &&
                     reinterpret_cast<uintptr_t>(k_src) % 16 == 0 &&
-                    reinterpret_cast<uintptr_t>(v_src) % 16 == 0 &&
-                    (c->k_bits == 3 || kQuantThreads % (d * c->k_bits / 32) == 0);
+                    reinterpret_cast<uintptr_t>(v_src) % 16 == 0;
   if (fast) {
     const int chunks = static_cast<int>(tile_bytes / (16 * kQuantThreads));  // 1, 2, 4 or 8
     st = c->kv_dtype == VC_F32
