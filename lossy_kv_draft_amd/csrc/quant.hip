@@ -469,16 +469,16 @@ __device__ __forceinline__ float row_shr(float v) {
 // rows), a V word reads one group's parameters, a word's elements come from one vector
 // LDS read and its codes from the certified reciprocal product (quant_biased_certified);
 // 16-bit codes divide; 3-bit codes (whose words straddle) are formed 16 per thread, the
-// lanes of a pair completing each other's words (pack_k_3bit, pack_v_3bit).  Requires d and G
-// powers of two with 32 <= d <= 256 and G >= 16, a tile of 4 to 32 KB, no more LDS than a
-// workgroup may allocate (160 KB on gfx950) and 16-byte aligned sources (the launch
-// checks; other shapes take quant_pack_kernel).
+// lanes of a pair completing each other's words (pack_k_3bit, pack_v_3bit).  Requires d
+// and G powers of two with 32 <= d <= 256 and G >= 16, a tile of 4 to 32 KB, no more LDS
+// than a workgroup may allocate (160 KB on gfx950) and 16-byte aligned sources (the
+// launch checks; other shapes take quant_pack_kernel).
 template <typename T, int M, bool K3>
 __global__ void __launch_bounds__(kQuantThreads)
 quant_pack_fast_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src, int64_t src_rows,
                        int64_t src_begin, int d, int G, int k_bits, int v_bits, int param_f32, int64_t capacity,
-                       int64_t dst_begin, uint32_t* __restrict__ k_codes,
-                       uint32_t* __restrict__ v_codes, void* k_scale, void* k_zero, void* v_scale, void* v_zero) {
+                       int64_t dst_begin, uint32_t* __restrict__ k_codes, uint32_t* __restrict__ v_codes,
+                       void* k_scale, void* k_zero, void* v_scale, void* v_zero) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   constexpr int n = M * kQuantThreads * 16 / static_cast<int>(sizeof(T));  // G d elements
   T* kt = reinterpret_cast<T*>(smem_raw);             // [G][d]
@@ -489,7 +489,7 @@ quant_pack_fast_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src,
   float* vz = vs + d;                                 // [G][d/G]
   float* vmn = vz + d;                                // [G][d/G] V group extrema
   float* vmx = vmn + d;                               // [G][d/G]
-  float* kmn = vmx + d;                              // [512/d][d] K slice extrema
+  float* kmn = vmx + d;                               // [512/d][d] K slice extrema
   float* kmx = kmn + 2 * kQuantThreads;               // [512/d][d]
   const int tid = threadIdx.x;
   const int grp = blockIdx.x, bh = blockIdx.y;
@@ -517,10 +517,10 @@ quant_pack_fast_kernel(const T* __restrict__ k_src, const T* __restrict__ v_src,
   }
   __syncthreads();
 
-  // V: thread tid takes the run of G d / 256 elements (m = 1, 2, 4 or 8 chunks of 16
+  // V: thread tid takes the run of G d / 256 elements (M = 1, 2, 4 or 8 chunks of 16
   // bytes) that starts at element tid G d / 256; a group is 256 / d such runs, in
-  // adjacent lanes of one 16-lane row.  Each lane starts at chunk tid m / 16 of its run (mod
-  // m), so the 16 lanes of a row read 16 different 16-byte bank columns at every step.
+  // adjacent lanes of one 16-lane row.  Each lane starts at chunk tid M / 16 of its run
+  // (mod M), so the 16 lanes of a row read 16 different 16-byte bank columns at every step.
   {
     float mn, mx;
     run_minmax<T, M>(reinterpret_cast<const uint4*>(vt) + tid * M, tid, mn, mx);
