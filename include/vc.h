@@ -187,7 +187,10 @@ int64_t vc_drop_keep_count(float keep_ratio, int64_t N);
  * vc_drop_select: scores float32 [B, Hkv, N] -> kept_idx int32 [B, Hkv, n_keep]
  *   (top n_keep, ties to the lower position, ascending).  n_keep <= N.  Scores
  *   are ranked as numbers: negative scores are allowed, -0.0 equals +0.0, and a NaN
- *   ranks below every other score (NaNs among themselves by position).
+ *   ranks below every other score (NaNs among themselves by position).  ws: device
+ *   memory of vc_drop_select_workspace_bytes(B, Hkv, N) bytes, any contents (the call
+ *   clears what it needs; calls sharing one workspace must not overlap);
+ *   VC_ERR_WORKSPACE if ws is NULL or smaller.
  * vc_gather_rows: src kv_dtype [B, Hkv, src_rows, d], idx int32 [B, Hkv, n]
  *   -> dst [B, Hkv, dst_rows, d] rows [0, n).  Every idx must be < src_rows. */
 vc_status vc_drop_scores(const void* k, int32_t kv_dtype, const void* probes, int32_t B, int32_t Hkv,

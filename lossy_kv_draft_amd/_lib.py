@@ -266,10 +266,12 @@ def vc_drop_scores(k, probes, scores, *, sm_scale=None, ws=None, stream=None):
                               _stream(stream)), "vc_drop_scores")
 
 
-def vc_drop_select(scores, n_keep, kept_idx, *, stream=None):
+def vc_drop_select(scores, n_keep, kept_idx, *, ws=None, stream=None):
     B, Hkv, N = scores.shape
-    _check(lib.vc_drop_select(_ptr(scores), B, Hkv, N, n_keep, _ptr(kept_idx), None, 0, _stream(stream)),
-           "vc_drop_select")
+    if ws is None:
+        ws = workspace(lib.vc_drop_select_workspace_bytes(B, Hkv, N), scores.device)
+    _check(lib.vc_drop_select(_ptr(scores), B, Hkv, N, n_keep, _ptr(kept_idx), _ptr(ws), ws.numel(),
+                              _stream(stream)), "vc_drop_select")
 
 
 def vc_gather_rows(src, idx, n, dst, *, stream=None):

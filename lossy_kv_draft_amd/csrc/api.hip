@@ -30,7 +30,8 @@ vc_status drop_scores_impl(const void* k, int32_t kv_dtype, const void* probes, 
                            int32_t d, int32_t P, float sm_scale, float* scores, void* ws, size_t ws_bytes,
                            hipStream_t s);
 vc_status drop_select_impl(const float* scores, int32_t B, int32_t Hkv, int64_t N, int64_t n_keep, int32_t* kept,
-                           int64_t kept_pitch, hipStream_t s);
+                           int64_t kept_pitch, void* ws, size_t ws_bytes, hipStream_t s);
+size_t drop_select_ws_bytes(int32_t B, int32_t Hkv, int64_t N);
 vc_status gather_impl(const void* src, int32_t kv_dtype, int32_t B, int32_t Hkv, int64_t src_rows, int32_t d,
                       const int32_t* idx, int64_t n, int64_t idx_pitch, void* dst, int64_t dst_rows, hipStream_t s);
 
@@ -115,7 +116,10 @@ extern "C" size_t vc_workspace_size(int32_t op, const vc_ws_query* q) {
 extern "C" size_t vc_compress_workspace_bytes(const vc_ckv* c, int64_t n_tokens, int32_t n_probes) {
   if (!c || c->method != VC_DROP_TOPK || n_tokens <= 0 || n_probes <= 0 || c->B <= 0 || c->Hkv <= 0) return 0;
   size_t scores = align_up(static_cast<size_t>(c->B) * c->Hkv * n_tokens * sizeof(float), 256);
-  return scores + vc_drop_scores_workspace_bytes(c->B, c->Hkv, n_tokens, n_probes);
+  // after the scores array: the scoring statistics, then (reusing the same bytes) the selection's histograms
+  const size_t stats = vc_drop_scores_workspace_bytes(c->B, c->Hkv, n_tokens, n_probes);
+  const size_t sel = drop_select_ws_bytes(c->B, c->Hkv, n_tokens);
+  return scores + (stats > sel ? stats : sel);
 }
 
 extern "C" vc_status vc_compress(const vc_ckv* c, const void* k_src, const void* v_src, int64_t src_rows,
@@ -149,7 +153,8 @@ extern "C" vc_status vc_compress(const vc_ckv* c, const void* k_src, const void*
   vc_status st = drop_scores_impl(k_src, c->kv_dtype, probes, c->B, c->Hkv, n_tokens, c->d, n_probes, sm_scale,
                                   scores, static_cast<char*>(ws) + sb, ws_bytes - sb, s);
   if (st != VC_OK) return st;
-  st = drop_select_impl(scores, c->B, c->Hkv, n_tokens, keep, c->kept_idx, c->capacity, s);
+  st = drop_select_impl(scores, c->B, c->Hkv, n_tokens, keep, c->kept_idx, c->capacity, static_cast<char*>(ws) + sb,
+                        ws_bytes - sb, s);
   if (st != VC_OK) return st;
   st = gather_impl(k_src, c->kv_dtype, c->B, c->Hkv, src_rows, c->d, c->kept_idx, keep, c->capacity, c->k_kept,
                    c->capacity, s);

@@ -16,10 +16,10 @@
 //   pass 2: every block merges the per-chunk statistics of its (sequence, head)
 //           in chunk order, recomputes the scores of its chunk and sums the
 //           probabilities over the probes (fixed butterfly order).
-// Selection: one workgroup per (sequence, kv-head) finds the n_keep-th largest
-// score by a 4 x 8-bit radix select on the float bits (scores are >= 0, so their
-// bit patterns order like their values), then compacts in position order the
-// positions with a larger score plus the lowest-positioned equal ones.
+// Selection: a 4 x 8-bit radix select over order-preserving keys of the scores finds
+// the n_keep-th largest, workgroups over slices of every (sequence, kv-head) adding
+// into global digit histograms; then the positions with a larger score plus the
+// lowest-positioned equal ones are written in position order (sel_* below).
 
 #include "common.h"
 
@@ -201,8 +201,20 @@ __global__ void __launch_bounds__(256) drop_scores_kernel(const T* k, const bf16
   }
 }
 
-// ---- top-k selection: one block per (sequence, kv-head)
-constexpr int kSelThreads = 1024;
+// ---- top-k selection
+// The n_keep-th largest key is found by a radix select on 8-bit digits, most significant
+// first, over the whole grid: N / kSelSlice workgroups per (sequence, kv-head) each add the
+// digit histogram of their slice (keys that share the digits fixed so far) into a global
+// one, and every workgroup of the next launch re-derives the digits fixed so far from
+// those histograms (a one-wave scan each, identical in every workgroup).  Then each slice
+// counts its keys above and equal to the threshold, and the last launch writes the kept
+// positions in ascending order: a position's slot is the number of kept positions below
+// it, from the counts of the earlier slices and a scan inside the slice.  The kept set is
+// fixed by the order (key descending, position ascending), so it does not depend on the
+// split; the histogram sums are integer atomics, so nothing depends on their order.
+constexpr int kSelSlice = 8192;  // scores per workgroup
+constexpr int kSelT = 256;       // threads per workgroup
+constexpr int kSelRun = kSelSlice / kSelT;  // consecutive positions per thread in the write
 
 // Unsigned key whose order is the numeric order of the score: a negative float's
 // bits are flipped, a non-negative one gets its sign bit set; -0.0 is read as +0.0
@@ -214,80 +226,200 @@ __device__ __forceinline__ uint32_t select_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__global__ void __launch_bounds__(kSelThreads) drop_select_kernel(const float* scores, int64_t N, int64_t n_keep,
-                                                                  int32_t* kept, int64_t kept_pitch) {
-  __shared__ unsigned hist[256];
-  __shared__ uint32_t s_prefix;
-  __shared__ int64_t s_remain;
-  __shared__ int64_t s_need_eq;
-  __shared__ int64_t s_base;
-  __shared__ int64_t s_eqbase;
-  __shared__ unsigned wsum[kSelThreads / 64][2];
-  const int bh = blockIdx.x;
-  const float* sc = scores + static_cast<int64_t>(bh) * N;
-  int32_t* out = kept + static_cast<int64_t>(bh) * kept_pitch;
-  const int tid = threadIdx.x;
+static int sel_slices(int64_t N) { return static_cast<int>(cdiv(N, kSelSlice)); }
+static size_t sel_hist_bytes(int32_t B, int32_t Hkv) {
+  return align_up(4 * static_cast<size_t>(B) * Hkv * 256 * sizeof(uint32_t), 256);
+}
+static size_t sel_ws_bytes(int32_t B, int32_t Hkv, int64_t N) {
+  return sel_hist_bytes(B, Hkv) + align_up(static_cast<size_t>(B) * Hkv * sel_slices(N) * 2 * sizeof(uint32_t), 256);
+}
 
-  if (tid == 0) { s_prefix = 0; s_remain = n_keep; }
-  __syncthreads();
-  // radix select of the n_keep-th largest key, most significant digit first
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
-    __syncthreads();
-    const uint32_t prefix = s_prefix;
-    const uint32_t pmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    for (int64_t n = tid; n < N; n += kSelThreads) {
-      uint32_t key = select_key(sc[n]);
-      if ((key & pmask) == (prefix & pmask)) atomicAdd(&hist[(key >> shift) & 0xFF], 1u);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int64_t rem = s_remain;
-      int bin = 255;
-      for (; bin > 0; --bin) {
-        if (static_cast<int64_t>(hist[bin]) >= rem) break;
-        rem -= hist[bin];
-      }
-      s_prefix = prefix | (static_cast<uint32_t>(bin) << shift);
-      s_remain = rem;
-    }
-    __syncthreads();
+// One digit of the select, by one whole wave: h[256] counts the keys that share the digits
+// fixed so far, remain (>= 1) is the rank from the top of the wanted key among them.
+// Returns the wanted key's digit; remain becomes its rank among the keys with that digit.
+__device__ __forceinline__ uint32_t sel_digit(const uint32_t* h, int64_t& remain, int lane) {
+  uint32_t c[4], sum = 0;  // lane l: bins 255 - 4 l down to 252 - 4 l
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c[j] = h[255 - 4 * lane - j];
+    sum += c[j];
   }
-  const uint32_t thr = s_prefix;  // key of the n_keep-th largest score
-  if (tid == 0) { s_need_eq = s_remain; s_base = 0; s_eqbase = 0; }
+  int64_t incl = sum;  // inclusive sum over the lanes up to this one (descending bins)
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  const int64_t excl = incl - sum;
+  const int L = __ffsll(static_cast<unsigned long long>(__ballot(excl < remain && remain <= incl))) - 1;
+  uint32_t digit = 0;
+  int64_t r = remain - excl;
+  if (lane == L) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (r <= c[j]) {
+        digit = 255u - 4u * lane - j;
+        break;
+      }
+      r -= c[j];
+    }
+  }
+  remain = __shfl(r, L);
+  return static_cast<uint32_t>(__shfl(static_cast<int>(digit), L));
+}
+
+// The digits fixed by passes [0, npass) as a key prefix, and the rank that goes with it
+__device__ __forceinline__ uint32_t sel_prefix(const uint32_t* hist, int BH, int bh, int npass, int64_t n_keep,
+                                               int64_t& remain, int lane) {
+  uint32_t prefix = 0;
+  remain = n_keep;
+  for (int q = 0; q < npass; ++q)
+    prefix |= sel_digit(hist + (static_cast<size_t>(q) * BH + bh) * 256, remain, lane) << (24 - 8 * q);
+  return prefix;
+}
+
+__global__ void __launch_bounds__(256) sel_zero_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+__global__ void __launch_bounds__(kSelT) sel_hist_kernel(const float* scores, int64_t N, int64_t n_keep,
+                                                         uint32_t* hist, int BH, int pass) {
+  __shared__ uint32_t lh[kSelT / 64][256];
+  __shared__ uint32_t s_prefix;
+  const int slice = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (wave == 0) {
+    int64_t remain;
+    const uint32_t prefix = sel_prefix(hist, BH, bh, pass, n_keep, remain, lane);
+    if (lane == 0) s_prefix = prefix;
+  }
+  for (int i = tid; i < (kSelT / 64) * 256; i += kSelT) (&lh[0][0])[i] = 0u;
   __syncthreads();
-  const int64_t need_eq = s_need_eq;
-  // compaction in position order
-  const int lane = tid & 63, wave = tid >> 6;
-  for (int64_t n0 = 0; n0 < N; n0 += kSelThreads) {
-    int64_t n = n0 + tid;
-    uint32_t key = n < N ? select_key(sc[n]) : 0u;
-    bool gt = n < N && key > thr;
-    bool eq = n < N && key == thr;
-    unsigned long long bgt = __ballot(gt), beq = __ballot(eq);
-    unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    unsigned gt_before = __popcll(bgt & below), eq_before = __popcll(beq & below);
-    if (lane == 0) { wsum[wave][0] = __popcll(bgt); wsum[wave][1] = __popcll(beq); }
-    __syncthreads();
-    unsigned wgt = 0, weq = 0, tgt = 0, teq = 0;
-    for (int w = 0; w < kSelThreads / 64; ++w) {
-      if (w < wave) { wgt += wsum[w][0]; weq += wsum[w][1]; }
-      tgt += wsum[w][0];
-      teq += wsum[w][1];
+  const uint32_t prefix = s_prefix;
+  const int shift = 24 - 8 * pass;
+  const uint32_t pmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+  const float* sc = scores + static_cast<int64_t>(bh) * N;
+  const int64_t n0 = static_cast<int64_t>(slice) * kSelSlice, n1 = min(N, n0 + kSelSlice);
+  for (int64_t n = n0 + tid; n < n1; n += kSelT) {
+    const uint32_t key = select_key(sc[n]);
+    if ((key & pmask) == (prefix & pmask)) atomicAdd(&lh[wave][(key >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  uint32_t v = 0;  // kSelT == 256: one bin per thread
+#pragma unroll
+  for (int w = 0; w < kSelT / 64; ++w) v += lh[w][tid];
+  if (v) atomicAdd(&hist[(static_cast<size_t>(pass) * BH + bh) * 256 + tid], v);
+}
+
+// Block-wide exclusive sum of x (kSelT threads); total in *tot
+__device__ __forceinline__ int64_t sel_block_scan(int64_t x, int64_t* wsum, int lane, int wave, int64_t* tot) {
+  int64_t incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int64_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kSelT / 64; ++w) {
+    before += w < wave ? wsum[w] : 0;
+    all += wsum[w];
+  }
+  __syncthreads();
+  *tot = all;
+  return before + incl - x;
+}
+
+// Keys above the threshold and equal to it in each slice: cnt[bh][slice] = {gt, eq}
+__global__ void __launch_bounds__(kSelT) sel_count_kernel(const float* scores, int64_t N, int64_t n_keep,
+                                                          const uint32_t* hist, int BH, uint32_t* cnt, int S) {
+  __shared__ uint32_t s_thr;
+  __shared__ int64_t wsum[kSelT / 64];
+  const int slice = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (wave == 0) {
+    int64_t remain;
+    const uint32_t thr = sel_prefix(hist, BH, bh, 4, n_keep, remain, lane);
+    if (lane == 0) s_thr = thr;
+  }
+  __syncthreads();
+  const uint32_t thr = s_thr;
+  const float* sc = scores + static_cast<int64_t>(bh) * N;
+  const int64_t n0 = static_cast<int64_t>(slice) * kSelSlice, n1 = min(N, n0 + kSelSlice);
+  int64_t gt = 0, eq = 0;
+  for (int64_t n = n0 + tid; n < n1; n += kSelT) {
+    const uint32_t key = select_key(sc[n]);
+    gt += key > thr;
+    eq += key == thr;
+  }
+  int64_t tg, te;
+  sel_block_scan(gt, wsum, lane, wave, &tg);
+  sel_block_scan(eq, wsum, lane, wave, &te);
+  if (tid == 0) {
+    cnt[(static_cast<size_t>(bh) * S + slice) * 2] = static_cast<uint32_t>(tg);
+    cnt[(static_cast<size_t>(bh) * S + slice) * 2 + 1] = static_cast<uint32_t>(te);
+  }
+}
+
+// The kept positions of each slice, in ascending order: thread t takes the kSelRun
+// consecutive positions from n0 + kSelRun t
+__global__ void __launch_bounds__(kSelT) sel_write_kernel(const float* scores, int64_t N, int64_t n_keep,
+                                                          const uint32_t* hist, int BH, const uint32_t* cnt, int S,
+                                                          int32_t* kept, int64_t kept_pitch) {
+  __shared__ uint32_t s_thr;
+  __shared__ int64_t s_need, s_g0, s_e0;
+  __shared__ int64_t wsum[kSelT / 64];
+  const int slice = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (wave == 0) {
+    int64_t remain;  // after all four digits: how many keys equal to the threshold are kept
+    const uint32_t thr = sel_prefix(hist, BH, bh, 4, n_keep, remain, lane);
+    int64_t g = 0, e = 0;  // kept-above and equal keys in the earlier slices
+    for (int q = lane; q < slice; q += 64) {
+      g += cnt[(static_cast<size_t>(bh) * S + q) * 2];
+      e += cnt[(static_cast<size_t>(bh) * S + q) * 2 + 1];
     }
-    int64_t eq_rank = s_eqbase + weq + eq_before;
-    bool take_eq = eq && eq_rank < need_eq;
-    // positions taken before this thread: all gt before + equal ones before (capped)
-    int64_t eq_taken_before = min<int64_t>(eq_rank, need_eq);
-    int64_t slot = s_base + wgt + gt_before + (eq_taken_before - min<int64_t>(s_eqbase, need_eq));
-    if ((gt || take_eq) && slot < n_keep) out[slot] = static_cast<int32_t>(n);
-    __syncthreads();
-    if (tid == 0) {
-      int64_t eq_taken = min<int64_t>(s_eqbase + teq, need_eq) - min<int64_t>(s_eqbase, need_eq);
-      s_base += tgt + eq_taken;
-      s_eqbase += teq;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      g += __shfl_xor(g, o);
+      e += __shfl_xor(e, o);
     }
-    __syncthreads();
+    if (lane == 0) {
+      s_thr = thr;
+      s_need = remain;
+      s_g0 = g;
+      s_e0 = e;
+    }
+  }
+  __syncthreads();
+  const uint32_t thr = s_thr;
+  const int64_t need = s_need;
+  const float* sc = scores + static_cast<int64_t>(bh) * N;
+  const int64_t p0 = static_cast<int64_t>(slice) * kSelSlice + static_cast<int64_t>(tid) * kSelRun;
+  uint32_t key[kSelRun];
+  int64_t gt = 0, eq = 0;
+#pragma unroll
+  for (int i = 0; i < kSelRun; ++i) {
+    key[i] = p0 + i < N ? select_key(sc[p0 + i]) : 0u;
+    const bool in = p0 + i < N;
+    gt += in && key[i] > thr;
+    eq += in && key[i] == thr;
+  }
+  int64_t tg, te;
+  int64_t g = s_g0 + sel_block_scan(gt, wsum, lane, wave, &tg);  // above the threshold, before this run
+  int64_t e = s_e0 + sel_block_scan(eq, wsum, lane, wave, &te);  // equal to it, before this run
+  int32_t* out = kept + static_cast<int64_t>(bh) * kept_pitch;
+#pragma unroll
+  for (int i = 0; i < kSelRun; ++i) {
+    if (p0 + i >= N) break;
+    if (key[i] > thr) {
+      const int64_t slot = g + min(e, need);
+      if (slot < n_keep) out[slot] = static_cast<int32_t>(p0 + i);
+      ++g;
+    } else if (key[i] == thr) {
+      if (e < need && g + e < n_keep) out[g + e] = static_cast<int32_t>(p0 + i);
+      ++e;
+    }
   }
 }
 
@@ -303,6 +435,21 @@ __global__ void __launch_bounds__(256) gather_rows_kernel(const uint4* src, int6
   const int64_t s = idx[static_cast<int64_t>(bh) * idx_pitch + j];
   if (s < 0 || s >= src_rows) return;  // out-of-range index: row left untouched
   dst[(static_cast<int64_t>(bh) * dst_rows + j) * row_vecs + c] = src[(static_cast<int64_t>(bh) * src_rows + s) * row_vecs + c];
+}
+
+// The same copy for rows of 2^lrv 16-byte pieces: indices by shifts instead of a 64-bit
+// division per piece (which has no instruction and costs on the order of a hundred)
+__global__ void __launch_bounds__(256) gather_rows_pow2_kernel(const uint4* src, int64_t src_rows, int lrv,
+                                                               const int32_t* idx, int64_t n, int64_t idx_pitch,
+                                                               uint4* dst, int64_t dst_rows) {
+  const int bh = blockIdx.y;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= (n << lrv)) return;
+  const int64_t j = e >> lrv;
+  const int64_t c = e & ((int64_t{1} << lrv) - 1);
+  const int64_t s = idx[static_cast<int64_t>(bh) * idx_pitch + j];
+  if (s < 0 || s >= src_rows) return;  // out-of-range index: row left untouched
+  dst[((static_cast<int64_t>(bh) * dst_rows + j) << lrv) + c] = src[((static_cast<int64_t>(bh) * src_rows + s) << lrv) + c];
 }
 
 static int drop_chunks(int64_t N) { return static_cast<int>(cdiv(N, kDropChunk)); }
@@ -350,16 +497,32 @@ vc_status drop_scores_impl(const void* k, int32_t kv_dtype, const void* probes, 
   return VC_OK;
 }
 
+size_t drop_select_ws_bytes(int32_t B, int32_t Hkv, int64_t N) { return sel_ws_bytes(B, Hkv, N); }
+
 vc_status drop_select_impl(const float* scores, int32_t B, int32_t Hkv, int64_t N, int64_t n_keep, int32_t* kept,
-                           int64_t kept_pitch, hipStream_t s) {
+                           int64_t kept_pitch, void* ws, size_t ws_bytes, hipStream_t s) {
   VC_REQUIRE(scores && kept, "scores / kept_idx is NULL");
   VC_REQUIRE(B > 0 && Hkv > 0 && N > 0, "bad shape");
   VC_REQUIRE(n_keep >= 1 && n_keep <= N, "n_keep must be in [1, N] (got %lld, N %lld)", (long long)n_keep,
              (long long)N);
   VC_REQUIRE(N <= 0x7fffffffLL, "N too large for int32 indices");
-  hipLaunchKernelGGL(drop_select_kernel, dim3(static_cast<unsigned>(B * Hkv)), dim3(kSelThreads), 0, s, scores, N,
-                     n_keep, kept, kept_pitch);
-  VC_LAUNCHED("drop_select_kernel");
+  const size_t need = sel_ws_bytes(B, Hkv, N);
+  if (!ws || ws_bytes < need) {
+    set_error("drop-select workspace needs %zu bytes (got %zu)", need, ws_bytes);
+    return VC_ERR_WORKSPACE;
+  }
+  const int BH = B * Hkv, S = sel_slices(N);
+  uint32_t* hist = static_cast<uint32_t*>(ws);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sel_hist_bytes(B, Hkv));
+  const int64_t nh = 4 * static_cast<int64_t>(BH) * 256;
+  hipLaunchKernelGGL(sel_zero_kernel, dim3(static_cast<unsigned>(cdiv(nh, 256))), dim3(256), 0, s, hist, nh);
+  const dim3 grid(static_cast<unsigned>(S), static_cast<unsigned>(BH));
+  for (int pass = 0; pass < 4; ++pass)
+    hipLaunchKernelGGL(sel_hist_kernel, grid, dim3(kSelT), 0, s, scores, N, n_keep, hist, BH, pass);
+  hipLaunchKernelGGL(sel_count_kernel, grid, dim3(kSelT), 0, s, scores, N, n_keep, hist, BH, cnt, S);
+  hipLaunchKernelGGL(sel_write_kernel, grid, dim3(kSelT), 0, s, scores, N, n_keep, hist, BH, cnt, S, kept,
+                     kept_pitch);
+  VC_LAUNCHED("sel_write_kernel");
   return VC_OK;
 }
 
@@ -373,6 +536,13 @@ vc_status gather_impl(const void* src, int32_t kv_dtype, int32_t B, int32_t Hkv,
   if (n == 0) return VC_OK;
   int rv = static_cast<int>(row_bytes / 16);
   dim3 grid(static_cast<unsigned>(cdiv(n * rv, 256)), static_cast<unsigned>(B * Hkv));
+  if ((rv & (rv - 1)) == 0) {
+    hipLaunchKernelGGL(gather_rows_pow2_kernel, grid, dim3(256), 0, s, static_cast<const uint4*>(src), src_rows,
+                       __builtin_ctz(static_cast<unsigned>(rv)), idx, n, idx_pitch, static_cast<uint4*>(dst),
+                       dst_rows);
+    VC_LAUNCHED("gather_rows_pow2_kernel");
+    return VC_OK;
+  }
   hipLaunchKernelGGL(gather_rows_kernel<1>, grid, dim3(256), 0, s, static_cast<const uint4*>(src), src_rows, rv, idx, n,
                      idx_pitch, static_cast<uint4*>(dst), dst_rows);
   VC_LAUNCHED("gather_rows_kernel");
@@ -405,12 +575,15 @@ extern "C" vc_status vc_drop_scores(const void* k, int32_t kv_dtype, const void*
                           as_stream(stream));
 }
 
-extern "C" size_t vc_drop_select_workspace_bytes(int32_t, int32_t, int64_t) { return 0; }
+extern "C" size_t vc_drop_select_workspace_bytes(int32_t B, int32_t Hkv, int64_t N) {
+  if (B <= 0 || Hkv <= 0 || N <= 0) return 0;
+  return sel_ws_bytes(B, Hkv, N);
+}
 
 extern "C" vc_status vc_drop_select(const float* scores, int32_t B, int32_t Hkv, int64_t N, int64_t n_keep,
-                                    int32_t* kept_idx, void*, size_t, void* stream) {
+                                    int32_t* kept_idx, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
-  return drop_select_impl(scores, B, Hkv, N, n_keep, kept_idx, n_keep, as_stream(stream));
+  return drop_select_impl(scores, B, Hkv, N, n_keep, kept_idx, n_keep, ws, ws_bytes, as_stream(stream));
 }
 
 extern "C" vc_status vc_gather_rows(const void* src, int32_t kv_dtype, int32_t B, int32_t Hkv, int64_t src_rows,

@@ -32,14 +32,19 @@ def test_drop_scores_match_oracle():
     assert np.allclose(got.sum(axis=-1), w.n_probes, rtol=1e-4)
 
 
-@pytest.mark.parametrize("N,keep", [(5000, 1250), (4096, 1024), (777, 1), (777, 777), (300, 299)])
-def test_drop_select_bit_exact_on_same_scores(N, keep):
+# single-slice and multi-slice (8192 scores per selecting workgroup; 25093 ends in a
+# ragged slice) sizes; step 0.5 leaves a handful of distinct scores, so the threshold's
+# equal scores span several slices and are cut part-way through one
+@pytest.mark.parametrize("N,keep,step", [(5000, 1250, 8), (4096, 1024, 8), (777, 1, 8), (777, 777, 8),
+                                         (300, 299, 8), (25093, 6274, 8), (25093, 1, 8), (25093, 25093, 8),
+                                         (25093, 25092, 8), (16384, 4096, 8), (25093, 9001, 0.5)])
+def test_drop_select_bit_exact_on_same_scores(N, keep, step):
     """The oracle's scores, rounded to float32 and coarsened to force many exact ties,
     are the input of both selections."""
     w = SMALL.with_(N=N)
     rng = np.random.default_rng(N + keep)
     s = rng.gamma(2.0, 1.0, size=(w.B, w.Hkv, N)).astype(np.float32)
-    s = np.round(s * 8) / 8                     # many ties
+    s = np.round(s * step) / step               # many ties
     s = s.astype(np.float32)
     kept = torch.empty(w.B, w.Hkv, keep, dtype=torch.int32, device="cuda")
     L.vc_drop_select(T(s), keep, kept)
@@ -70,11 +75,12 @@ def test_drop_select_mixed_sign_zeros_and_nan(keep):
             assert np.array_equal(got[b, h], OD.select(s[b, h], keep)), (b, h)
 
 
-def test_gather_rows_bit_exact():
+@pytest.mark.parametrize("d", [128, 48])  # rows of 16 (a power of two) and of 6 16-byte pieces
+def test_gather_rows_bit_exact(d):
     w = SMALL
-    K = G.full_kv(w, "k")
+    K = G.full_kv(w, "k")[..., :d]
     idx = np.sort(np.random.default_rng(1).choice(w.N, size=(w.B, w.Hkv, 100), replace=True), axis=-1)
-    dst = torch.zeros(w.B, w.Hkv, 128, w.d, dtype=torch.bfloat16, device="cuda")
+    dst = torch.zeros(w.B, w.Hkv, 128, d, dtype=torch.bfloat16, device="cuda")
     L.vc_gather_rows(T(K, torch.bfloat16), T(idx, torch.int32), 100, dst)
     torch.cuda.synchronize()
     got = np32(dst)
