@@ -53,30 +53,66 @@ __device__ __forceinline__ void load_probes(const bf16_t* probes, int hk, int P,
   }
 }
 
-// s[ct][r] = score(token tok0 + 4 kb + r, probe 16 ct + l16), unscaled
+// The 16 x D tile of K rows tok0 .. tok0 + 15 as matrix-core operands: lane (l16, kb)
+// holds row tok0 + l16, channels 32 ks + 8 kb .. + 7 for each k-step ks (float32 rows
+// are rounded to bf16 when the operand is formed).  A row at or past N reads row N - 1:
+// the scores it yields are masked by the callers (no zeroing after the loads, which
+// would have to wait for them).
 template <int D, typename T>
-__device__ __forceinline__ void tile_scores(const T* krows, int64_t tok0, int64_t N, int l16, int kb,
-                                            const bf16x8_t (&pf)[4][D / 32], f32x4_t (&s)[4]) {
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) s[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  int64_t tok = tok0 + l16;
+struct KTile {
+  static constexpr int kVecs = (sizeof(T) == 2 ? 1 : 2) * (D / 32);
+  uint4 v[kVecs];
+};
+
+template <int D, typename T>
+__device__ __forceinline__ void ktile_load(const T* krows, int64_t tok, int64_t N, int kb, KTile<D, T>& t) {
+  const int64_t row = tok < N ? tok : N - 1;
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
-    DP16 a;
-    a.u = make_uint4(0, 0, 0, 0);
-    if (tok < N) {
-      if constexpr (sizeof(T) == 2) {
-        a.u = *reinterpret_cast<const uint4*>(krows + tok * D + 32 * ks + 8 * kb);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) a.v[j] = static_cast<__bf16>(krows[tok * D + 32 * ks + 8 * kb + j]);
-      }
+    const uint4* p = reinterpret_cast<const uint4*>(krows + row * D + 32 * ks + 8 * kb);
+    if constexpr (sizeof(T) == 2) {
+      t.v[ks] = p[0];
+    } else {
+      t.v[2 * ks] = p[0];
+      t.v[2 * ks + 1] = p[1];
     }
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) s[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, pf[ct][ks], s[ct], 0, 0, 0);
   }
 }
 
+template <int D, typename T>
+__device__ __forceinline__ bf16x8_t ktile_op(const KTile<D, T>& t, int ks) {
+  if constexpr (sizeof(T) == 2) {
+    DP16 a;
+    a.u = t.v[ks];
+    return a.v;
+  } else {
+    const uint4 u0 = t.v[2 * ks], u1 = t.v[2 * ks + 1];
+    const float f[8] = {__uint_as_float(u0.x), __uint_as_float(u0.y), __uint_as_float(u0.z), __uint_as_float(u0.w),
+                        __uint_as_float(u1.x), __uint_as_float(u1.y), __uint_as_float(u1.z), __uint_as_float(u1.w)};
+    bf16x8_t a;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = static_cast<__bf16>(f[j]);
+    return a;
+  }
+}
+
+// Sum over the four 16-lane groups of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48), left in
+// every lane of the four: the lane-swap instructions pair each lane with its partner,
+// and each step adds the pair (two operands: the same sum in both lanes).
+__device__ __forceinline__ float group4_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const unsigned w = __float_as_uint(x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
+// Pass 1: per chunk and probe, a reference m and the sum of exp2 of the scaled scores
+// minus m.  Lane (l16, kb) of a wave keeps probes 16 ct + l16 over tokens 4 kb .. + 3 of
+// each 16-token step (S = K P^T: K rows are the A operand); the reference moves only when
+// a score exceeds it by more than 8 (so every term is below 2^8), and the rows of the
+// next two steps are loaded while the current one is multiplied.
 template <int D, typename T>
 __global__ void __launch_bounds__(256) drop_stats_kernel(const T* k, const bf16_t* probes, int Hkv, int64_t N, int P,
                                                          float qscale, int nchunks, float* stat_m, float* stat_l) {
@@ -88,41 +124,68 @@ __global__ void __launch_bounds__(256) drop_stats_kernel(const T* k, const bf16_
   const T* krows = k + static_cast<int64_t>(bh) * N * D;
   float m[4], l[4];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) { m[ct] = -INFINITY; l[ct] = 0.f; }
+  for (int ct = 0; ct < 4; ++ct) { m[ct] = -1e30f; l[ct] = 0.f; }  // finite: a masked -inf term adds exp2(-inf) = 0
   const int64_t c0 = static_cast<int64_t>(chunk) * kDropChunk;
   const int64_t c1 = min(N, c0 + kDropChunk);
-  for (int64_t t0 = c0 + wave * 16; t0 < c1; t0 += 64) {
+  auto step = [&](const KTile<D, T>& cur, int64_t t0) {
     f32x4_t s[4];
-    tile_scores<D, T>(krows, t0, N, l16, kb, pf, s);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) s[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const bf16x8_t a = ktile_op<D, T>(cur, ks);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) s[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[ct][ks], s[ct], 0, 0, 0);
+    }
+    if (t0 + 64 > c1) {  // the chunk's last steps (wave-uniform): tokens at or past c1 drop out
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (t0 + 4 * kb + r >= c1) s[ct][r] = -INFINITY;
+    }
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      float mt = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = (t0 + 4 * kb + r < c1) ? s[ct][r] * qscale : -INFINITY;
-        s[ct][r] = v;
-        mt = fmaxf(mt, v);
+      // the maximum of the raw scores (the scale is positive), scaled once
+      const float mt = fmaxf(fmaxf(s[ct][0], s[ct][1]), fmaxf(s[ct][2], s[ct][3])) * qscale;
+      if (mt > m[ct] + 8.f) {
+        l[ct] *= exp2f(m[ct] - mt);
+        m[ct] = mt;
       }
-      float mn = fmaxf(m[ct], mt);
-      if (mn == -INFINITY) continue;
-      float acc = l[ct] * exp2f(m[ct] - mn);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc += exp2f(s[ct][r] - mn);
-      l[ct] = acc;
-      m[ct] = mn;
+      for (int r = 0; r < 4; ++r)  // results below 2^-126 read as 0
+        l[ct] += __builtin_amdgcn_exp2f(__builtin_fmaf(s[ct][r], qscale, -m[ct]));
     }
+  };
+  KTile<D, T> tl[3];  // a ring of three tiles: loads two steps ahead of the products
+  int64_t t0 = c0 + wave * 16;
+  ktile_load<D, T>(krows, t0 + l16, N, kb, tl[0]);
+  ktile_load<D, T>(krows, t0 + 64 + l16, N, kb, tl[1]);
+  while (t0 < c1) {
+    ktile_load<D, T>(krows, t0 + 128 + l16, N, kb, tl[2]);  // unconditional (rows clamped): exact waits
+    __builtin_amdgcn_sched_barrier(0);                      // and issued here, not next to their first use
+    step(tl[0], t0);
+    t0 += 64;
+    if (t0 >= c1) break;
+    ktile_load<D, T>(krows, t0 + 128 + l16, N, kb, tl[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    step(tl[1], t0);
+    t0 += 64;
+    if (t0 >= c1) break;
+    ktile_load<D, T>(krows, t0 + 128 + l16, N, kb, tl[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    step(tl[2], t0);
+    t0 += 64;
   }
   // combine the 4 lane groups (same probe), then the 4 waves
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
     for (int o = 16; o <= 32; o <<= 1) {
-      float om = __shfl_xor(m[ct], o), ol = __shfl_xor(l[ct], o);
-      float mn = fmaxf(m[ct], om);
-      if (mn != -INFINITY) {
-        l[ct] = l[ct] * exp2f(m[ct] - mn) + ol * exp2f(om - mn);
-        m[ct] = mn;
-      }
+      const float om = __shfl_xor(m[ct], o), ol = __shfl_xor(l[ct], o);
+      const float mn = fmaxf(m[ct], om);
+      l[ct] = l[ct] * exp2f(m[ct] - mn) + ol * exp2f(om - mn);
+      m[ct] = mn;
     }
     if (kb == 0) { sm[wave][ct * 16 + l16] = m[ct]; sl[wave][ct * 16 + l16] = l[ct]; }
   }
@@ -130,74 +193,104 @@ __global__ void __launch_bounds__(256) drop_stats_kernel(const T* k, const bf16_
   if (tid < P) {
     float mm = sm[0][tid], ll = sl[0][tid];
     for (int w = 1; w < 4; ++w) {
-      float om = sm[w][tid], ol = sl[w][tid];
-      float mn = fmaxf(mm, om);
-      if (mn != -INFINITY) {
-        ll = ll * exp2f(mm - mn) + ol * exp2f(om - mn);
-        mm = mn;
-      }
+      const float om = sm[w][tid], ol = sl[w][tid];
+      const float mn = fmaxf(mm, om);
+      ll = ll * exp2f(mm - mn) + ol * exp2f(om - mn);
+      mm = mn;
     }
     stat_m[(static_cast<int64_t>(bh) * nchunks + chunk) * P + tid] = mm;
     stat_l[(static_cast<int64_t>(bh) * nchunks + chunk) * P + tid] = ll;
   }
 }
 
+// The chunks' statistics of each (sequence, kv-head) merged once: off[bh][p] = M + log2 L
+// for the probe's softmax over all N tokens (M its reference, L the sum of exp2(s - M)),
+// so that a token's probability under probe p is exp2(s - off).  Thread (p, g) merges
+// chunks g, g + 4, ... in order; the four partial results are then merged in order of g.
+__global__ void __launch_bounds__(256) drop_stats_merge_kernel(const float* stat_m, const float* stat_l, int nchunks,
+                                                               int P, float* off) {
+  __shared__ float pm[4][kDropMaxProbes], pl[4][kDropMaxProbes];
+  const int bh = blockIdx.x, p = threadIdx.x & 63, g = threadIdx.x >> 6;
+  float mm = -1e30f, ll = 0.f;
+  if (p < P) {
+    for (int c = g; c < nchunks; c += 4) {
+      const float om = stat_m[(static_cast<int64_t>(bh) * nchunks + c) * P + p];
+      const float ol = stat_l[(static_cast<int64_t>(bh) * nchunks + c) * P + p];
+      const float mn = fmaxf(mm, om);
+      ll = ll * exp2f(mm - mn) + ol * exp2f(om - mn);
+      mm = mn;
+    }
+  }
+  pm[g][p] = mm;
+  pl[g][p] = ll;
+  __syncthreads();
+  if (g == 0) {
+    for (int h = 1; h < 4; ++h) {
+      const float om = pm[h][p], ol = pl[h][p];
+      const float mn = fmaxf(mm, om);
+      ll = ll * exp2f(mm - mn) + ol * exp2f(om - mn);
+      mm = mn;
+    }
+    off[bh * kDropMaxProbes + p] = p < P ? mm + log2f(ll) : INFINITY;  // no probe: probability 0
+  }
+}
+
+// Pass 2: every token's probabilities summed over the probes.  Here the probes are the A
+// operand (P K^T), so lane (l16, kb) holds token l16 of the step under probes
+// 16 ct + 4 kb + r: its 16 probabilities are summed in the lane, then over the four lane
+// groups; the rows of the next two steps are loaded while the current one is multiplied.
 template <int D, typename T>
 __global__ void __launch_bounds__(256) drop_scores_kernel(const T* k, const bf16_t* probes, int Hkv, int64_t N, int P,
-                                                          float qscale, int nchunks, const float* stat_m,
-                                                          const float* stat_l, float* scores) {
-  __shared__ float gm[kDropMaxProbes], ginv[kDropMaxProbes];
+                                                          float qscale, const float* off, float* scores) {
   const int chunk = blockIdx.x, bh = blockIdx.y, hk = bh % Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, kb = lane >> 4;
-  if (tid < P) {
-    float mm = -INFINITY, ll = 0.f;
-    for (int c = 0; c < nchunks; ++c) {
-      float om = stat_m[(static_cast<int64_t>(bh) * nchunks + c) * P + tid];
-      float ol = stat_l[(static_cast<int64_t>(bh) * nchunks + c) * P + tid];
-      float mn = fmaxf(mm, om);
-      if (mn != -INFINITY) {
-        ll = ll * exp2f(mm - mn) + ol * exp2f(om - mn);
-        mm = mn;
-      }
-    }
-    gm[tid] = mm;
-    ginv[tid] = 1.f / ll;
-  }
-  __syncthreads();
   bf16x8_t pf[4][D / 32];
   load_probes<D>(probes, hk, P, l16, kb, pf);
-  float pm[4], pinv[4];
+  float po[4][4];  // off of probe 16 ct + 4 kb + r (+inf for p >= P)
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    int p = ct * 16 + l16;
-    pm[ct] = p < P ? gm[p] : 0.f;
-    pinv[ct] = p < P ? ginv[p] : 0.f;
-  }
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) po[ct][r] = off[bh * kDropMaxProbes + 16 * ct + 4 * kb + r];
   const T* krows = k + static_cast<int64_t>(bh) * N * D;
   const int64_t c0 = static_cast<int64_t>(chunk) * kDropChunk;
   const int64_t c1 = min(N, c0 + kDropChunk);
-  for (int64_t t0 = c0 + wave * 16; t0 < c1; t0 += 64) {
+  auto step = [&](const KTile<D, T>& cur, int64_t t0) {
     f32x4_t s[4];
-    tile_scores<D, T>(krows, t0, N, l16, kb, pf, s);
-    float acc[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float x = 0.f;
+    for (int ct = 0; ct < 4; ++ct) s[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) x += exp2f(s[ct][r] * qscale - pm[ct]) * pinv[ct];
-      acc[r] = x;
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const bf16x8_t a = ktile_op<D, T>(cur, ks);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) s[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[ct][ks], a, s[ct], 0, 0, 0);
     }
+    float acc = 0.f;
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1)
+    for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] += __shfl_xor(acc[r], o);
-    if (l16 == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int64_t tok = t0 + 4 * kb + r;
-        if (tok < c1) scores[static_cast<int64_t>(bh) * N + tok] = acc[r];
-      }
-    }
+      for (int r = 0; r < 4; ++r) acc += __builtin_amdgcn_exp2f(__builtin_fmaf(s[ct][r], qscale, -po[ct][r]));
+    acc = group4_sum(acc);
+    if (kb == 0 && t0 + l16 < c1) scores[static_cast<int64_t>(bh) * N + t0 + l16] = acc;
+  };
+  KTile<D, T> tl[3];  // a ring of three tiles: loads two steps ahead of the products
+  int64_t t0 = c0 + wave * 16;
+  ktile_load<D, T>(krows, t0 + l16, N, kb, tl[0]);
+  ktile_load<D, T>(krows, t0 + 64 + l16, N, kb, tl[1]);
+  while (t0 < c1) {
+    ktile_load<D, T>(krows, t0 + 128 + l16, N, kb, tl[2]);  // unconditional (rows clamped): exact waits
+    __builtin_amdgcn_sched_barrier(0);                      // and issued here, not next to their first use
+    step(tl[0], t0);
+    t0 += 64;
+    if (t0 >= c1) break;
+    ktile_load<D, T>(krows, t0 + 128 + l16, N, kb, tl[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    step(tl[1], t0);
+    t0 += 64;
+    if (t0 >= c1) break;
+    ktile_load<D, T>(krows, t0 + 128 + l16, N, kb, tl[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    step(tl[2], t0);
+    t0 += 64;
   }
 }
 
@@ -456,7 +549,7 @@ static int drop_chunks(int64_t N) { return static_cast<int>(cdiv(N, kDropChunk))
 
 static size_t scores_ws_bytes(int32_t B, int32_t Hkv, int64_t N, int32_t P) {
   size_t n = static_cast<size_t>(B) * Hkv * drop_chunks(N) * P;
-  return 2 * align_up(n * sizeof(float), 256);
+  return 2 * align_up(n * sizeof(float), 256) + align_up(static_cast<size_t>(B) * Hkv * kDropMaxProbes * sizeof(float), 256);
 }
 
 vc_status drop_scores_impl(const void* k, int32_t kv_dtype, const void* probes, int32_t B, int32_t Hkv, int64_t N,
@@ -477,6 +570,7 @@ vc_status drop_scores_impl(const void* k, int32_t kv_dtype, const void* probes, 
   size_t n = static_cast<size_t>(B) * Hkv * nch * P;
   float* sm = static_cast<float*>(ws);
   float* sl = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(n * sizeof(float), 256));
+  float* off = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * align_up(n * sizeof(float), 256));
   dim3 grid(nch, static_cast<unsigned>(B * Hkv));
   float qs = sm_scale * kLog2e;
   const bf16_t* pr = static_cast<const bf16_t*>(probes);
@@ -484,8 +578,10 @@ vc_status drop_scores_impl(const void* k, int32_t kv_dtype, const void* probes, 
   do {                                                                                                              \
     hipLaunchKernelGGL((drop_stats_kernel<D_, T_>), grid, dim3(256), 0, s, static_cast<const T_*>(k), pr, Hkv, N, P, \
                        qs, nch, sm, sl);                                                                            \
+    hipLaunchKernelGGL(drop_stats_merge_kernel, dim3(static_cast<unsigned>(B * Hkv)), dim3(256), 0, s, sm, sl, nch, P, \
+                       off);                                                                                        \
     hipLaunchKernelGGL((drop_scores_kernel<D_, T_>), grid, dim3(256), 0, s, static_cast<const T_*>(k), pr, Hkv, N,  \
-                       P, qs, nch, sm, sl, scores);                                                                 \
+                       P, qs, off, scores);                                                                         \
   } while (0)
   if (kv_dtype == VC_BF16) {
     if (d == 128) VC_DS(128, bf16_t); else VC_DS(64, bf16_t);
