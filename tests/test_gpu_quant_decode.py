@@ -146,6 +146,33 @@ def test_compress_ties_and_near_ties_bit_exact(name):
         assert np.array_equal(np32(getattr(ckv, key)), ref[key]), key
 
 
+# Head sizes at the ends of the fast compression kernel's range (compression only): d 32
+# in float32 (16 token slices per K channel, V groups of 8 runs joined by three row
+# shifts, two 3-bit halves per row; in bf16 a d-32 tile is under 4 KB for every valid
+# group), d 64 in bf16 (4 runs per group) and d 256 (one V run per group, no shifts).
+EDGE_D_CASES = {
+    "d64_g64_k3v2_bf16": C.small(C.LLAMA8B, d=64, N=64 * 5, k_bits=3, v_bits=2, group=64),
+    "d32_g32_k4v3_f32": C.TINY.with_(d=32, N=32 * 7, k_bits=4, v_bits=3, group=32),
+    "d256_g16_k2v4_bf16": C.small(C.LLAMA8B, d=256, N=16 * 9, k_bits=2, v_bits=4, group=16),
+    "d256_g32_k8v3_bf16": C.small(C.LLAMA8B, d=256, N=32 * 5, k_bits=8, v_bits=3, group=32, scale_dtype="f32"),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE_D_CASES))
+def test_compress_quant_head_size_edges_bit_exact(name):
+    w = EDGE_D_CASES[name]
+    say(f"[quant edge d] {name} d{w.d} k{w.k_bits} v{w.v_bits} G{w.group}")
+    K, V = G.full_kv(w, "k"), G.full_kv(w, "v")
+    ckv = _ckv(w, w.N)
+    L.vc_compress(ckv, T(K, tdtype(w.dtype)), T(V, tdtype(w.dtype)))
+    torch.cuda.synchronize()
+    ref = oracle_compress(w, K, V)
+    assert np.array_equal(ckv.k_codes.cpu().numpy().view(np.uint32), ref["k_codes"])
+    assert np.array_equal(ckv.v_codes.cpu().numpy().view(np.uint32), ref["v_codes"])
+    for key in ("k_scale", "k_zero", "v_scale", "v_zero"):
+        assert np.array_equal(np32(getattr(ckv, key)), ref[key]), key
+
+
 def _scaled(x, scale, dtype):
     """x * scale rounded to the storage type (both sides get the rounded values)."""
     return x if scale == 1.0 else G.to_storage(x * np.float32(scale), dtype)
