@@ -60,6 +60,34 @@ __device__ __forceinline__ int64_t dec_tail_len(const DecodeArgs& a, int b) {
 // * outputs: thread (c, part) sums channel c over the rows of parity `part`.
 // The running maximum and sum end in every thread, the output share of channel c
 // in thread (c, part).
+// Max and sum over the 64 lanes of a wave without LDS round trips: DPP exchanges within
+// each row of 16 lanes (xor 1, xor 2, the mirrors of 8 and of 16), then the lane-swap
+// instructions across rows.  Every step combines two equal-ranked values (a op b in one
+// lane, b op a in its partner), so all 64 lanes end with the same result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <typename Op>
+__device__ __forceinline__ float wave_reduce_dpp(float v, Op op) {
+  v = op(v, dpp_mov<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = op(v, dpp_mov<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = op(v, dpp_mov<0x141>(v));  // row_half_mirror
+  v = op(v, dpp_mov<0x140>(v));  // row_mirror
+  const unsigned u = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const unsigned w = __float_as_uint(v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return op(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  return wave_reduce_dpp(v, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  return wave_reduce_dpp(v, [](float a, float b) { return a + b; });
+}
+
 struct TailPartial {
   float m, l, o;
 };
@@ -107,14 +135,14 @@ __device__ __forceinline__ void tail_chunk(TailPartial& t, const TailRegs& x, fl
       y = fmaf(f32_hi(qs[e]), f32_hi(ks[e]), y);
     }
   }
-  y += __shfl_xor(y, 1);
-  y += __shfl_xor(y, 2);
+  y += dpp_mov<0xB1>(y);  // the quad's four quarters: xor 1, then xor 2
+  y += dpp_mov<0x4E>(y);
   if (quarter == 0) s_s[rr] = y * qscale;
   __syncthreads();
   const float sr = lane < nr ? s_s[lane] : -INFINITY;
-  const float mn = fmaxf(t.m, warp_max(sr));
+  const float mn = fmaxf(t.m, wave_max_dpp(sr));
   const float pr = lane < nr ? exp2f(sr - mn) : 0.f;
-  const float lc = warp_sum(pr);
+  const float lc = wave_sum_dpp(pr);
   __syncthreads();  // every wave has read the scores
   if (tid < 64) s_s[lane] = pr;
   __syncthreads();
@@ -187,9 +215,9 @@ __global__ void __launch_bounds__(kDecThreads) decode_merge_kernel(DecodeArgs a)
       m = t.m;
       l = t.l;
     }
-    const float M = warp_max(m);
+    const float M = wave_max_dpp(m);
     const float w = m == -INFINITY ? 0.f : exp2f(m - M);
-    const float L = warp_sum(l * w);
+    const float L = wave_sum_dpp(l * w);
     if (tid < S + (TAIL ? 1 : 0)) s_w[tid] = w;
     if (tid == 0) {
       s_fin[0] = M;
