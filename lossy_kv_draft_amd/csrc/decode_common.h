@@ -120,7 +120,11 @@ __device__ __forceinline__ void tail_load(TailRegs& x, const DecodeArgs& a, int 
 #pragma unroll
   for (int j = 0; j < kTailChunk / 2; ++j) x.vr[j] = tv[static_cast<int64_t>(r0 + min(part + 2 * j, nr - 1)) * D + c];
 }
-__device__ __forceinline__ void tail_chunk(TailPartial& t, const TailRegs& x, float qscale, int nr, float* s_s) {
+// s_s holds the chunk's scores and s_p its probabilities (two arrays, so that no barrier
+// has to separate the reads of the one from the writes of the other); a caller running a
+// further chunk places a barrier before it (both arrays are rewritten).
+__device__ __forceinline__ void tail_chunk(TailPartial& t, const TailRegs& x, float qscale, int nr, float* s_s,
+                                           float* s_p) {
   const int tid = threadIdx.x, lane = tid & 63, part = tid / 128, rr = tid >> 2, quarter = tid & 3;
   auto f32_lo = [](uint32_t w) { return __uint_as_float(w << 16); };
   auto f32_hi = [](uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); };
@@ -143,18 +147,16 @@ __device__ __forceinline__ void tail_chunk(TailPartial& t, const TailRegs& x, fl
   const float mn = fmaxf(t.m, wave_max_dpp(sr));
   const float pr = lane < nr ? exp2f(sr - mn) : 0.f;
   const float lc = wave_sum_dpp(pr);
-  __syncthreads();  // every wave has read the scores
-  if (tid < 64) s_s[lane] = pr;
+  if (tid < 64) s_p[lane] = pr;
   __syncthreads();
   const float sc = t.m == -INFINITY ? 0.f : exp2f(t.m - mn);
   float o = t.o * sc;
 #pragma unroll
   for (int j = 0; j < kTailChunk / 2; ++j)
-    o = fmaf(s_s[part + 2 * j], __uint_as_float(x.vr[j] << 16), o);
+    o = fmaf(s_p[part + 2 * j], __uint_as_float(x.vr[j] << 16), o);
   t.o = o;
   t.l = t.l * sc + lc;
   t.m = mn;
-  __syncthreads();  // s_s is rewritten by the next chunk
 }
 
 // Merge of the split partials of one (sequence, kv-head) per workgroup, in split
@@ -197,12 +199,13 @@ __global__ void __launch_bounds__(kDecThreads) decode_merge_kernel(DecodeArgs a)
 #pragma unroll
   for (int j = 0; j < 16; ++j) v[j] = s_lo + j < s_hi ? p[(s_lo + j) * stride] : 0.f;
   if constexpr (TAIL) {
-    __shared__ float s_s[kTailChunk];
+    __shared__ float s_s[kTailChunk], s_p[kTailChunk];
     if (tl > 0) {
-      tail_chunk(t, tr, a.qscale, min(tl, kTailChunk), s_s);
+      tail_chunk(t, tr, a.qscale, min(tl, kTailChunk), s_s, s_p);
       for (int r0 = kTailChunk; r0 < tl; r0 += kTailChunk) {
         tail_load(tr, a, bh, h, r0, min(tl - r0, kTailChunk));
-        tail_chunk(t, tr, a.qscale, min(tl - r0, kTailChunk), s_s);
+        __syncthreads();  // every wave is done with the previous chunk's scores and probabilities
+        tail_chunk(t, tr, a.qscale, min(tl - r0, kTailChunk), s_s, s_p);
       }
     }
   }
