@@ -570,9 +570,9 @@ __global__ void __launch_bounds__(256) verify_merge_kernel(VerifyArgs a, void* o
   typedef float fv_t __attribute__((ext_vector_type(V)));
   const int bh = blockIdx.y;
   const int M = a.H * a.k, d = a.d, dv = d / V;
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (e >= static_cast<int64_t>(M) * dv) return;
-  const int row = static_cast<int>(e / dv), c = static_cast<int>(e % dv) * V;
+  const int e = static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x);  // M * dv < 2^31 (host check)
+  if (e >= M * dv) return;
+  const int row = e / dv, c = (e - row * dv) * V;
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int S = a.splits;
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + static_cast<int64_t>(bh) * S * M + row;
@@ -580,24 +580,19 @@ __global__ void __launch_bounds__(256) verify_merge_kernel(VerifyArgs a, void* o
   // the partials of 8 splits are loaded at once (V channels per thread); the sums
   // still run in split order
   float Mx = -INFINITY;
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    float mv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) mv[j] = ml[static_cast<int64_t>(min(s0 + j, S - 1)) * M].x;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) Mx = fmaxf(Mx, mv[j]);
-  }
   float Lsum = 0.f;
   fv_t O = {};
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    float2 p[8];
-    fv_t ov[8];
+  float2 p[8];
+  fv_t ov[8];
+  auto load8 = [&](int s0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int64_t sp = min(s0 + j, S - 1);
       p[j] = ml[sp * M];
       ov[j] = *reinterpret_cast<const fv_t*>(po + sp * M * d);
     }
+  };
+  auto add8 = [&](int s0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (s0 + j >= S) break;
@@ -605,6 +600,24 @@ __global__ void __launch_bounds__(256) verify_merge_kernel(VerifyArgs a, void* o
       Lsum = fmaf(p[j].y, w, Lsum);
 #pragma unroll
       for (int v = 0; v < V; ++v) O[v] = fmaf(ov[j][v], w, O[v]);
+    }
+  };
+  if (S <= 8) {  // one round of loads: the maximum from the same (maximum, sum) pairs
+    load8(0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Mx = fmaxf(Mx, p[j].x);
+    add8(0);
+  } else {
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      float mv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mv[j] = ml[static_cast<int64_t>(min(s0 + j, S - 1)) * M].x;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) Mx = fmaxf(Mx, mv[j]);
+    }
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      load8(s0);
+      add8(s0);
     }
   }
   int64_t orow = (static_cast<int64_t>(b) * a.Hq + hk * a.H) * a.k + row;
@@ -713,6 +726,7 @@ extern "C" vc_status vc_verify_attn_full(const void* q, const void* k_cache, con
     VC_UNSUPPORTED(d == 64 || d == 128, "bf16 verify supports d = 64 or 128 (got %d)", d);
   else
     VC_UNSUPPORTED(d <= 256, "f32 verify supports d <= 256 (got %d)", d);
+  VC_REQUIRE(static_cast<int64_t>(Hq / Hkv) * k * d <= 0x7fffffffLL, "q-heads per kv-head * k * d must be below 2^31");
   const int64_t C = split_tokens > 0 ? split_tokens : vc_verify_split_tokens(B, Hkv, cache_rows);
   size_t need = vc_verify_workspace_bytes(B, Hq, Hkv, d, k, ctx_len, static_cast<int32_t>(C));
   if (!ws || ws_bytes < need) {
