@@ -74,11 +74,14 @@ def test_verify_batch_invariance(name):
 
 
 @pytest.mark.parametrize("base", ["llama8b", "drop_k40"])
-def test_verify_ragged_context_lengths(base):
+@pytest.mark.parametrize("split", [0, 256])
+def test_verify_ragged_context_lengths(base, split):
     """Per-sequence context lengths (one of them empty), with 128 rows per kv-head
-    (4-wave blocks) and 160 (one 8-wave block)."""
+    (4-wave blocks) and 160 (one 8-wave block); the default split and 256-row splits
+    (6 of them: the merge's one-round path, with the splits past a short sequence's end
+    empty)."""
     w = C.small(C.LLAMA8B if base == "llama8b" else C.DROP, B=3, N=1500, **({} if base == "llama8b" else {"Hkv": 1, "Hq": 4}))
-    say(f"[verify ragged] {base}")
+    say(f"[verify ragged] {base} split={split}")
     K, V, Q, Kw, Vw = inputs(w)
     lens = [1500, 700, 0]
     cap = 1500 + w.k
@@ -87,7 +90,7 @@ def test_verify_ragged_context_lengths(base):
     for b, Lb in enumerate(lens):
         kc[b, :, :Lb], vc[b, :, :Lb] = K[b, :, :Lb], V[b, :, :Lb]
         kc[b, :, Lb:Lb + w.k], vc[b, :, Lb:Lb + w.k] = Kw[b], Vw[b]
-    out, lse = _run(w, T(Q, torch.bfloat16), T(kc, torch.bfloat16), T(vc, torch.bfloat16), 1500,
+    out, lse = _run(w, T(Q, torch.bfloat16), T(kc, torch.bfloat16), T(vc, torch.bfloat16), 1500, split,
                     ctx_lens=torch.tensor(lens, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     for b, Lb in enumerate(lens):
